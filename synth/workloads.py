@@ -1,0 +1,85 @@
+"""Input recipes for the benchmarked workloads of the three row reductions.
+
+Shapes follow the QuACK article (无需CUDA代码，给H100加速33%-50%), sections
+"NCU 性能分析（Softmax 内核）" (softmax, 16K x 131K fp32) and "内存吞吐量"
+(batch 8k-32k, reduction dim 256-262k, fp32 and bf16).  The pages give no
+value distributions; the ones here are the library's own stated recipe:
+x ~ N(0,1) (cross-entropy logits ~ N(0, sigma=2) in the vocab-like case),
+RMSNorm weight ~ U(0.5, 1.5), labels uniform in [0, N), and in the spiky
+softmax case each entry independently set to +20 with probability 1 %.
+bf16 inputs are the fp32 draw rounded to nearest even.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import SEED, STREAM_LABELS, STREAM_SPIKES, STREAM_W, STREAM_X, labels, normal, spikes_, uniform
+
+RMSNORM_EPS = 1e-6
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    op: str          # "softmax" | "rmsnorm" | "xent"
+    dtype: str       # "f32" | "bf16"
+    M: int
+    N: int
+    sigma: float = 1.0
+    spiky: bool = False
+    eps: float = RMSNORM_EPS
+    extra: dict = field(default_factory=dict)
+
+
+# The four fixed workloads, smallest first.
+SOFTMAX_SMALL = Workload("softmax_f32_256x1024", "softmax", "f32", 256, 1024)
+RMSNORM_MAIN = Workload("rmsnorm_bf16_16384x4096", "rmsnorm", "bf16", 16384, 4096)
+XENT_VOCAB = Workload("xent_f32_8192x131072", "xent", "f32", 8192, 131072, sigma=2.0)
+SOFTMAX_SPIKY = Workload("softmax_f32_16384x131072_spiky", "softmax", "f32", 16384, 131072,
+                         spiky=True)
+FIXED = [SOFTMAX_SMALL, RMSNORM_MAIN, XENT_VOCAB, SOFTMAX_SPIKY]
+
+SWEEP_M = (8192, 16384, 32768)
+SWEEP_N = (256, 1024, 4096, 16384, 65536, 262144)
+
+
+def sweep():
+    """All (op, dtype, M, N) points of the 3-op x 2-dtype sweep, x ~ N(0,1)."""
+    out = []
+    for op in ("softmax", "rmsnorm", "xent"):
+        for dtype in ("f32", "bf16"):
+            for M in SWEEP_M:
+                for N in SWEEP_N:
+                    out.append(Workload(f"{op}_{dtype}_{M}x{N}", op, dtype, M, N))
+    return out
+
+
+def by_name(name: str) -> Workload:
+    for w in FIXED + sweep():
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def x_rows(w: Workload, *, seed=SEED, rows=None, row0=0, nrows=None, nthreads=0, out=None):
+    """The input matrix (or the listed rows of it) for workload ``w``."""
+    M = w.M if nrows is None else nrows
+    x = normal(M, w.N, sigma=w.sigma, dtype=w.dtype, seed=seed, stream=STREAM_X, rows=rows,
+               row0=row0, nthreads=nthreads, out=out)
+    if w.spiky:
+        spikes_(x, p=0.01, value=20.0, dtype=w.dtype, seed=seed, stream=STREAM_SPIKES, rows=rows,
+                row0=row0, nthreads=nthreads)
+    return x
+
+
+def weight(w: Workload, *, seed=SEED) -> np.ndarray:
+    """RMSNorm weight[N] ~ U(0.5, 1.5) in the input dtype."""
+    return uniform(1, w.N, lo=0.5, hi=1.5, dtype=w.dtype, seed=seed, stream=STREAM_W).reshape(w.N)
+
+
+def label_rows(w: Workload, *, seed=SEED, rows=None, row0=0, nrows=None) -> np.ndarray:
+    """Cross-entropy labels, uniform in [0, N)."""
+    M = w.M if nrows is None else nrows
+    return labels(M, w.N, seed=seed, stream=STREAM_LABELS, rows=rows, row0=row0)

@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Throughput of the row-reduction kernels on one MI355X, as effective HBM GB/s.
+
+A step is one call of the op over one batch of seeded synthetic input (the whole
+path: plan, 128-bit loads, register / wave / LDS (/ grid) reductions, epilogue,
+stores).  Inputs are resident in HBM before timing starts; several input/output
+sets (at least 2 GiB together) rotate so that every step reads cold data rather
+than the 256 MB last-level cache.
+
+Printed: one JSON line with
+  value      whole-job effective GB/s = algorithmic bytes per step x steps / wall time
+  roofline   the kernel's algorithmic bytes / its mean launch time (HIP events on the
+             launch stream), against the MI355X HBM peak of 8 TB/s, and the HBM bytes
+             the hardware counters measured per launch (null if the kernel sources
+             changed since the counters were taken)
+  cpu_baseline  the double-precision CPU oracle on a bounded sample of the same workload
+  copy_ceiling  a 128-bit streaming copy of the same bytes in the same run
+Algorithmic bytes: softmax M*N*(s_in + s_out); RMSNorm M*N*(s_in + s_out) + N*s;
+cross-entropy M*N*s + 12*M (labels in, loss and lse out).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--sweep]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective HBM GB/s (1 read+1 write) and % of MI355X peak, per op/N/dtype"
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "rmsnorm_bf16_16384x4096"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = os.path.join(ROOT, "memory_bound_row_softmax_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_SOURCES)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def esize(dtype: str) -> int:
+    return 4 if dtype == "f32" else 2
+
+
+def algorithmic_bytes(w) -> int:
+    s = esize(w.dtype)
+    if w.op == "softmax":
+        return w.M * w.N * 2 * s
+    if w.op == "rmsnorm":
+        return w.M * w.N * 2 * s + w.N * s
+    return w.M * w.N * s + 12 * w.M
+
+
+def traffic_for(name: str):
+    """Counter-measured HBM bytes per launch, if taken on the current kernel sources."""
+    try:
+        data = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None, None
+    rec = data.get(name)
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None, rec
+    return rec["fetch_bytes"] + rec["write_bytes"], rec
+
+
+class Runner:
+    """Device buffers for one workload and a launcher for step k."""
+
+    def __init__(self, w, min_rotation_bytes: float, device="cuda:0"):
+        import numpy as np
+        import torch
+
+        import memory_bound_row_softmax_amd as rr
+        from synth import workloads as W
+
+        self.w, self.rr, self.torch = w, rr, torch
+        self.dev = device
+        self.dt = rr.RR_F32 if w.dtype == "f32" else rr.RR_BF16
+        s = esize(w.dtype)
+        in_bytes = w.M * w.N * s
+        out_bytes = in_bytes if w.op != "xent" else 8 * w.M
+        self.sets = max(1, min(16, math.ceil(min_rotation_bytes / (in_bytes + out_bytes))))
+        tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+
+        x_np = W.x_rows(w)
+        host = torch.from_numpy(x_np if w.dtype == "f32" else x_np.view(np.int16))
+        x0 = host.to(device)
+        del host, x_np
+        x0 = x0.view(tdt) if w.dtype == "bf16" else x0
+        self.x = [x0] + [x0.clone() for _ in range(self.sets - 1)]
+        if w.op == "xent":
+            lab = torch.from_numpy(W.label_rows(w)).to(device)
+            self.labels = lab
+            self.loss = [torch.empty(w.M, dtype=torch.float32, device=device) for _ in range(self.sets)]
+            self.lse = [torch.empty(w.M, dtype=torch.float32, device=device) for _ in range(self.sets)]
+        else:
+            self.y = [torch.empty_like(x0) for _ in range(self.sets)]
+        if w.op == "rmsnorm":
+            wn = W.weight(w)
+            wt = torch.from_numpy(wn if w.dtype == "f32" else wn.view(np.int16)).to(device)
+            self.weight = wt.view(tdt) if w.dtype == "bf16" else wt
+        op = {"softmax": rr.RR_OP_SOFTMAX, "rmsnorm": rr.RR_OP_RMSNORM, "xent": rr.RR_OP_XENT}[w.op]
+        self.op = op
+        self.ws = rr.workspace(op, w.M, w.N, self.dt, device)
+        self.wsp = self.ws.data_ptr() if self.ws is not None else 0
+        self.wsb = self.ws.numel() if self.ws is not None else 0
+        self.plan = rr.rr_plan_query(op, w.M, w.N, self.dt)
+        self.stream = torch.cuda.Stream(device=device)
+        self.sp = self.stream.cuda_stream
+        self.xp = [t.data_ptr() for t in self.x]
+        if w.op == "xent":
+            self.lp, self.ep = [t.data_ptr() for t in self.loss], [t.data_ptr() for t in self.lse]
+            self.labp = self.labels.data_ptr()
+        else:
+            self.yp = [t.data_ptr() for t in self.y]
+        self.wp = self.weight.data_ptr() if w.op == "rmsnorm" else 0
+        self.copy_dst = None
+
+    def launch(self, k: int) -> int:
+        w, rr, i = self.w, self.rr, k % self.sets
+        if w.op == "softmax":
+            return rr.softmax_fwd_raw(self.xp[i], self.yp[i], w.M, w.N, self.dt, self.wsp, self.wsb,
+                                      self.sp)
+        if w.op == "rmsnorm":
+            return rr.rmsnorm_fwd_raw(self.xp[i], self.wp, self.yp[i], 0, w.M, w.N, self.dt, w.eps,
+                                      self.wsp, self.wsb, self.sp)
+        return rr.cross_entropy_fwd_raw(self.xp[i], self.labp, self.lp[i], self.ep[i], w.M, w.N,
+                                        self.dt, self.wsp, self.wsb, self.sp)
+
+    def copy_launch(self, k: int) -> int:
+        i = k % self.sets
+        src = self.x[i]
+        nbytes = src.numel() * src.element_size()
+        if self.w.op == "xent":
+            if self.copy_dst is None:
+                self.copy_dst = self.torch.empty_like(self.x[0])
+            dst = self.copy_dst
+        else:
+            dst = self.y[i]
+        return self.rr.stream_copy_raw(src.data_ptr(), dst.data_ptr(), nbytes, self.sp)
+
+    def time(self, fn, steps: int, warmup: int):
+        """Wall time of `steps` launches and the mean per-launch time from events."""
+        torch = self.torch
+        with torch.cuda.stream(self.stream):
+            for k in range(warmup):
+                st = fn(k)
+                if st != 0:
+                    raise RuntimeError(f"launch failed: {self.rr.status_string(st)}")
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for k in range(steps):
+                ev[k][0].record(self.stream)
+                fn(warmup + k)
+                ev[k][1].record(self.stream)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+        per_launch = [a.elapsed_time(b) for a, b in ev]
+        return t1 - t0, sum(per_launch) / len(per_launch), min(per_launch)
+
+
+def cpu_baseline(w, seconds: float):
+    """The oracle, single-threaded, on the first rows of the same workload."""
+    import oracle
+    from synth import workloads as W
+
+    per_row = algorithmic_bytes(w) / w.M
+
+    def run(rows):
+        x = W.x_rows(w, nrows=rows)
+        t0 = time.perf_counter()
+        if w.op == "softmax":
+            oracle.softmax(x)
+        elif w.op == "rmsnorm":
+            oracle.rmsnorm(x, W.weight(w), w.eps)
+        else:
+            oracle.cross_entropy(x, W.label_rows(w, nrows=rows))
+        return time.perf_counter() - t0
+
+    probe = max(1, min(w.M, (1 << 20) // w.N))
+    t = run(probe)
+    rows = max(1, min(w.M, int(probe * seconds / max(t, 1e-6))))
+    t = run(rows)
+    return {"value": round(per_row * rows / t / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"first {rows} of {w.M} rows, one pass, single-threaded double-precision "
+                      f"oracle ({t:.1f} s)"}
+
+
+def measure(w, steps: int, warmup: int, min_rotation_bytes: float, with_cpu: bool,
+            cpu_seconds: float):
+    r = Runner(w, min_rotation_bytes)
+    nbytes = algorithmic_bytes(w)
+    wall, mean_ms, min_ms = r.time(r.launch, steps, warmup)
+    copy_wall, copy_mean_ms, _ = r.time(r.copy_launch, steps, warmup)
+    copy_bytes = 2 * r.x[0].numel() * r.x[0].element_size()
+    achieved = nbytes / (mean_ms * 1e-3) / 1e9
+    traffic, rec = traffic_for(w.name)
+    copy_gbps = copy_bytes / (copy_mean_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(nbytes * steps / wall / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(wall / steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": w.op, "io_dtype": w.dtype, "M": w.M, "N": w.N,
+                   "plan": {k: r.plan[k] for k in ("path", "vals_per_lane", "lanes_per_row",
+                                                    "groups_per_row", "block_threads")},
+                   "rotating_sets": r.sets},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "launch_ms_mean": round(mean_ms, 5),
+                     "launch_ms_min": round(min_ms, 5), "algorithmic_bytes": nbytes},
+        "copy_ceiling": {"value": round(copy_gbps, 2), "unit": "GB/s",
+                         "frac": round(copy_gbps / HBM_PEAK_GBPS, 4),
+                         "kernel_vs_copy": round(achieved / copy_gbps, 4)},
+    }
+    if rec is not None:
+        line["roofline"]["traffic_source"] = rec.get("summary")
+    if with_cpu:
+        line["cpu_baseline"] = cpu_baseline(w, cpu_seconds)
+    del r
+    import torch
+
+    torch.cuda.empty_cache()
+    return line
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--sweep", action="store_true",
+                    help="run every fixed and sweep workload; one JSON line each to --out")
+    ap.add_argument("--out", default=os.path.join("gpurun_out", "bench_sweep.jsonl"))
+    ap.add_argument("--rotate-bytes", type=float, default=float(1 << 31))
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(rows shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        return 2
+
+    from synth import workloads as W
+
+    if args.sweep:
+        os.makedirs(os.path.dirname(args.out) or ".", exist_ok=True)
+        done = set()
+        if os.path.exists(args.out):
+            for l in open(args.out):
+                try:
+                    done.add(json.loads(l)["config"]["workload"])
+                except (ValueError, KeyError):
+                    pass
+        for w in W.FIXED + W.sweep():
+            if w.name in done:
+                continue
+            line = measure(w, args.steps, args.warmup, args.rotate_bytes, False, 0)
+            with open(args.out, "a") as f:
+                f.write(json.dumps(line) + "\n")
+            print(f"{w.name:34s} {line['roofline']['achieved']:9.1f} GB/s "
+                  f"({line['roofline']['frac'] * 100:5.1f}% of peak, copy "
+                  f"{line['copy_ceiling']['value']:7.1f})", flush=True)
+        return 0
+
+    line = measure(W.by_name(args.workload), args.steps, args.warmup, args.rotate_bytes,
+                   not args.no_cpu_baseline, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

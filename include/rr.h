@@ -1,0 +1,144 @@
+/*
+ * rr.h -- C ABI of librr: memory-bound row reductions on AMD Instinct MI355X
+ * (gfx950).  Softmax, RMSNorm and cross-entropy forward over a row-major
+ * M x N matrix, each reading every input element from HBM once and (softmax,
+ * RMSNorm) writing every output element once.
+ *
+ * Source pages.  [QuACK] is the QbitAI article "无需CUDA代码，给H100加速33%-50%",
+ * a summary of the QuACK tutorial on speed-of-light memory-bound kernels.
+ * Its section 让内存密集型内核达到"光速" names the three operators (RMSNorm,
+ * softmax, cross-entropy loss) over a (batch x reduction dimension) input;
+ * its section 内存吞吐量 gives the shapes (batch 8k-32k, reduction dimension
+ * 256-262k, fp32 and bf16).  The pages print no formula; the definitions
+ * stated at each function below are the textbook ones.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers, owned by the caller.  The library keeps
+ *    no per-call state and allocates nothing.
+ *  - Matrices are contiguous and row-major: element (i, j) is at i * N + j.
+ *    x, y and w have the element type `dt`; cross-entropy outputs are fp32.
+ *  - Calls are stream-ordered and asynchronous: RR_OK means the work was
+ *    enqueued on `stream`.  Faults during execution surface at the caller's
+ *    next synchronisation.  No call aborts or throws.
+ *  - M == 0 is a no-op returning RR_OK.
+ *  - 16-byte aligned pointers with (N * element size) % 16 == 0 take the
+ *    vectorised path (128-bit loads and stores); anything else takes a
+ *    per-element path that gives the same results more slowly.
+ *  - `ws` is a workspace that only rows split over several workgroups need:
+ *    when rr_workspace_bytes(...) returns 0 it may be NULL.  Otherwise it
+ *    must hold at least that many bytes, be zero-filled once when allocated,
+ *    and must not be shared by launches that may run at the same time.  Every
+ *    launch that completes normally leaves it zero-filled again.
+ */
+#ifndef RR_H
+#define RR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RR_OK = 0,
+    RR_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, M < 0, N < 1 with M > 0, bad dtype,
+                                    eps < 0 or not finite, partial overlap of x and y, N too
+                                    large for an int32 label (cross-entropy) */
+    RR_ERR_UNSUPPORTED = 2,      /* N above the largest row the on-chip plan can hold, or the
+                                    co-resident grid does not fit on the device */
+    RR_ERR_WORKSPACE = 3,        /* ws is NULL or smaller than rr_workspace_bytes() */
+    RR_ERR_HIP = 4,              /* a HIP call failed; see rr_last_hip_error() */
+    RR_ERR_GRID_TIMEOUT = 5      /* reported by rr_workspace_check(): a split row waited for
+                                    its peer workgroups longer than the spin limit */
+} rr_status;
+
+typedef enum { RR_F32 = 0, RR_BF16 = 1 } rr_dtype;
+
+typedef enum { RR_OP_SOFTMAX = 0, RR_OP_RMSNORM = 1, RR_OP_XENT = 2 } rr_op;
+
+/*
+ * Softmax forward, per row i:  m = max_j x_ij,  y_ij = exp(x_ij - m) / sum_k exp(x_ik - m).
+ * [QuACK] section NCU 性能分析（Softmax 内核） (row max, exponential sum, final values)
+ * and the closing paragraph of 内存吞吐量 (the conventional three-pass softmax over
+ * on-chip data).  Arithmetic in fp32; y has the input type (bf16: round to nearest
+ * even).  y == x (exact aliasing) is allowed; any other overlap is rejected.
+ */
+rr_status rr_softmax_fwd(const void *x, void *y, int64_t M, int64_t N, rr_dtype dt, void *ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/*
+ * RMSNorm forward, per row i:  r_i = 1 / sqrt(sum_j x_ij^2 / N + eps),  y_ij = x_ij * r_i * w_j.
+ * [QuACK] section 让内存密集型内核达到"光速" (RMSNorm among the three kernels) and
+ * 总结 (RMSNorm's layout, loads/stores and reduction helpers reused for softmax).
+ * eps sits inside the root; there is no bias and no mean subtraction.  w has N
+ * elements of type dt.  rstd (may be NULL) receives r_i as fp32.  Arithmetic in
+ * fp32; y has the input type.  y == x is allowed.
+ */
+rr_status rr_rmsnorm_fwd(const void *x, const void *w, void *y, float *rstd, int64_t M,
+                         int64_t N, rr_dtype dt, float eps, void *ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/*
+ * Cross-entropy forward, per row i:  lse_i = log sum_j exp(x_ij),  loss_i = lse_i - x_i[label_i].
+ * [QuACK] section 让内存密集型内核达到"光速" (the cross-entropy loss kernel).  One loss
+ * per row, no reduction over rows, no label smoothing and no ignored index.  A label
+ * outside [0, N) gives loss_i = NaN (lse_i is still written) and is never used as an
+ * address.  labels: int32[M]; loss: fp32[M]; lse: fp32[M] or NULL.  N must fit int32.
+ */
+rr_status rr_cross_entropy_fwd(const void *logits, const int32_t *labels, float *loss,
+                               float *lse, int64_t M, int64_t N, rr_dtype dt, void *ws,
+                               size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Bytes of workspace the call with these arguments needs (0 when it needs none).
+ * The value depends only on (op, M, N, dt); `device` is accepted for callers that
+ * size per device and is otherwise unused (pass -1).
+ */
+size_t rr_workspace_bytes(rr_op op, int64_t M, int64_t N, rr_dtype dt, int device);
+
+/*
+ * Reads (and clears) the error word of a workspace after the work on `stream`
+ * has finished (this call synchronises the stream).  Returns RR_OK, or
+ * RR_ERR_GRID_TIMEOUT if some split row gave up waiting for its peers, in which
+ * case that launch's outputs are not valid.
+ */
+rr_status rr_workspace_check(void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Plan chosen for a call, for inspection and tests.  Needs no GPU. */
+typedef struct {
+    int path;           /* 0: row held in registers by one lane group or workgroup,
+                           1: row split over `groups_per_row` workgroups (grid path),
+                           2: streaming (cross-entropy) */
+    int vectorized;     /* 1: 128-bit path, 0: per-element path */
+    int vals_per_lane;  /* fp32 values each lane holds (row paths) or loads per step (streaming) */
+    int lanes_per_row;  /* lanes that share one row inside a workgroup */
+    int groups_per_row; /* workgroups per row (1 except on the grid path) */
+    int block_threads;  /* threads per workgroup */
+    int rows_per_block; /* rows one workgroup processes at once */
+    int64_t max_n;      /* largest N this configuration holds (row paths) */
+    size_t ws_bytes;    /* workspace bytes the call needs */
+} rr_plan_info;
+
+rr_status rr_plan_query(rr_op op, int64_t M, int64_t N, rr_dtype dt, int vectorized,
+                        rr_plan_info *out);
+
+/*
+ * 128-bit streaming copy of `bytes` bytes (a multiple of 16, 16-byte aligned pointers):
+ * the same-run HBM ceiling the three kernels are compared with.  Not one of the pages'
+ * operators; a measurement aid.
+ */
+rr_status rr_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
+
+const char *rr_status_string(rr_status status);
+
+/* hipError_t of the most recent RR_ERR_HIP in the calling thread (0 if none). */
+int rr_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RR_H */

@@ -1,0 +1,228 @@
+"""Python binding of librr (memory-bound row reductions for MI355X / gfx950).
+
+Argument marshalling only: every entry point forwards device pointers, sizes and
+the current HIP stream to the C ABI declared in ``include/rr.h``; all arithmetic
+runs in the library's HIP kernels.  PyTorch supplies device memory and streams.
+
+The library is loaded from ``librr.so`` next to this file.  If it has not been
+built, every call raises: there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librr.so")
+
+RR_OK = 0
+RR_ERR_INVALID_ARGUMENT = 1
+RR_ERR_UNSUPPORTED = 2
+RR_ERR_WORKSPACE = 3
+RR_ERR_HIP = 4
+RR_ERR_GRID_TIMEOUT = 5
+
+RR_F32, RR_BF16 = 0, 1
+RR_OP_SOFTMAX, RR_OP_RMSNORM, RR_OP_XENT = 0, 1, 2
+
+EXPORTS = ("rr_softmax_fwd", "rr_rmsnorm_fwd", "rr_cross_entropy_fwd", "rr_workspace_bytes",
+           "rr_workspace_check", "rr_plan_query", "rr_stream_copy", "rr_status_string",
+           "rr_last_hip_error")
+
+
+class RRError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)}")
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("vectorized", ctypes.c_int),
+                ("vals_per_lane", ctypes.c_int), ("lanes_per_row", ctypes.c_int),
+                ("groups_per_row", ctypes.c_int), ("block_threads", ctypes.c_int),
+                ("rows_per_block", ctypes.c_int), ("max_n", ctypes.c_int64),
+                ("ws_bytes", ctypes.c_size_t)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib():
+    """The loaded librr (raises if it is not built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is not built; run "
+                                   "`python -m memory_bound_row_softmax_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            vp, i64, sz, ci, st = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t,
+                                   ctypes.c_int, ctypes.c_int)
+            L.rr_softmax_fwd.argtypes = [vp, vp, i64, i64, ci, vp, sz, vp]
+            L.rr_rmsnorm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, ci, ctypes.c_float, vp, sz, vp]
+            L.rr_cross_entropy_fwd.argtypes = [vp, vp, vp, vp, i64, i64, ci, vp, sz, vp]
+            L.rr_workspace_bytes.argtypes = [ci, i64, i64, ci, ci]
+            L.rr_workspace_bytes.restype = sz
+            L.rr_workspace_check.argtypes = [vp, sz, vp]
+            L.rr_plan_query.argtypes = [ci, i64, i64, ci, ci, ctypes.POINTER(PlanInfo)]
+            L.rr_stream_copy.argtypes = [vp, vp, sz, vp]
+            L.rr_status_string.argtypes = [ci]
+            L.rr_status_string.restype = ctypes.c_char_p
+            L.rr_last_hip_error.argtypes = []
+            for f in (L.rr_softmax_fwd, L.rr_rmsnorm_fwd, L.rr_cross_entropy_fwd,
+                      L.rr_workspace_check, L.rr_plan_query, L.rr_stream_copy,
+                      L.rr_last_hip_error):
+                f.restype = st
+            _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().rr_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != RR_OK:
+        raise RRError(status, what)
+
+
+# --------------------------------------------------------------- raw pointers
+# The same entry points with plain integers (device addresses, stream handle),
+# for callers that manage memory themselves (the bench).
+
+def softmax_fwd_raw(x, y, M, N, dt, ws=0, ws_bytes=0, stream=0) -> int:
+    return lib().rr_softmax_fwd(x, y, M, N, dt, ws or None, ws_bytes, stream or None)
+
+
+def rmsnorm_fwd_raw(x, w, y, rstd, M, N, dt, eps, ws=0, ws_bytes=0, stream=0) -> int:
+    return lib().rr_rmsnorm_fwd(x, w, y, rstd or None, M, N, dt, eps, ws or None, ws_bytes,
+                                stream or None)
+
+
+def cross_entropy_fwd_raw(x, labels, loss, lse, M, N, dt, ws=0, ws_bytes=0, stream=0) -> int:
+    return lib().rr_cross_entropy_fwd(x, labels, loss, lse or None, M, N, dt, ws or None,
+                                      ws_bytes, stream or None)
+
+
+def stream_copy_raw(src, dst, nbytes, stream=0) -> int:
+    return lib().rr_stream_copy(src, dst, nbytes, stream or None)
+
+
+# --------------------------------------------------------------- torch tensors
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return RR_F32
+    if t.dtype == torch.bfloat16:
+        return RR_BF16
+    raise TypeError(f"librr takes float32 or bfloat16 tensors, got {t.dtype}")
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return int(stream)
+    return _torch().cuda.current_stream(t.device).cuda_stream
+
+
+def _matrix(x):
+    if x.dim() != 2 or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("expected a contiguous 2-D CUDA tensor [M, N]")
+    return x.shape[0], x.shape[1]
+
+
+def workspace_bytes(op: int, M: int, N: int, dt: int) -> int:
+    return int(lib().rr_workspace_bytes(op, M, N, dt, -1))
+
+
+def workspace(op: int, M: int, N: int, dt: int, device):
+    """A zero-filled workspace for this call shape, or None when none is needed."""
+    n = workspace_bytes(op, M, N, dt)
+    if n == 0:
+        return None
+    return _torch().zeros(n, dtype=_torch().uint8, device=device)
+
+
+def _ws_args(ws):
+    if ws is None:
+        return 0, 0
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def rr_softmax_fwd(x, y=None, ws=None, stream=None):
+    """Row softmax of x [M, N] into y (new tensor if None; y may be x)."""
+    M, N = _matrix(x)
+    if y is None:
+        y = _torch().empty_like(x)
+    dt = dtype_code(x)
+    if ws is None:
+        ws = workspace(RR_OP_SOFTMAX, M, N, dt, x.device)
+    wp, wb = _ws_args(ws)
+    _check(softmax_fwd_raw(x.data_ptr(), y.data_ptr(), M, N, dt, wp, wb, _stream(x, stream)),
+           "rr_softmax_fwd")
+    return y
+
+
+def rr_rmsnorm_fwd(x, w, eps=1e-6, y=None, rstd=None, ws=None, stream=None):
+    """RMSNorm of x [M, N] with weight w [N]; returns y (and fills rstd [M] if given)."""
+    M, N = _matrix(x)
+    if w.dtype != x.dtype or w.numel() != N or not w.is_contiguous():
+        raise ValueError("weight must be a contiguous [N] tensor of the input's dtype")
+    if y is None:
+        y = _torch().empty_like(x)
+    dt = dtype_code(x)
+    if ws is None:
+        ws = workspace(RR_OP_RMSNORM, M, N, dt, x.device)
+    wp, wb = _ws_args(ws)
+    _check(rmsnorm_fwd_raw(x.data_ptr(), w.data_ptr(), y.data_ptr(),
+                           rstd.data_ptr() if rstd is not None else 0, M, N, dt, float(eps), wp,
+                           wb, _stream(x, stream)), "rr_rmsnorm_fwd")
+    return y
+
+
+def rr_cross_entropy_fwd(logits, labels, loss=None, lse=None, ws=None, stream=None):
+    """Per-row cross-entropy of logits [M, N] with int32 labels [M]; returns (loss, lse)."""
+    torch = _torch()
+    M, N = _matrix(logits)
+    if labels.dtype != torch.int32 or labels.numel() != M or not labels.is_contiguous():
+        raise ValueError("labels must be a contiguous int32 [M] tensor")
+    if loss is None:
+        loss = torch.empty(M, dtype=torch.float32, device=logits.device)
+    if lse is None:
+        lse = torch.empty(M, dtype=torch.float32, device=logits.device)
+    dt = dtype_code(logits)
+    wp, wb = _ws_args(ws)
+    _check(cross_entropy_fwd_raw(logits.data_ptr(), labels.data_ptr(), loss.data_ptr(),
+                                 lse.data_ptr(), M, N, dt, wp, wb, _stream(logits, stream)),
+           "rr_cross_entropy_fwd")
+    return loss, lse
+
+
+def rr_workspace_check(ws, stream=None) -> int:
+    """Synchronises the stream and returns (and clears) the workspace's status."""
+    wp, wb = _ws_args(ws)
+    return lib().rr_workspace_check(wp, wb, _stream(ws, stream))
+
+
+def rr_stream_copy(src, dst, stream=None):
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("destination too small")
+    _check(stream_copy_raw(src.data_ptr(), dst.data_ptr(), nbytes, _stream(src, stream)),
+           "rr_stream_copy")
+    return dst
+
+
+def rr_plan_query(op: int, M: int, N: int, dt: int, vectorized: bool = True) -> dict:
+    info = PlanInfo()
+    _check(lib().rr_plan_query(op, M, N, dt, 1 if vectorized else 0, ctypes.byref(info)),
+           "rr_plan_query")
+    return {k: getattr(info, k) for k, _ in PlanInfo._fields_}

@@ -1,0 +1,224 @@
+// api.cpp -- the C ABI of librr: argument validation, planning, launch.
+//
+// Declarations and the meaning of every argument are in include/rr.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "launch.hpp"
+#include "plan.hpp"
+#include "rr.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_num_cus[kMaxDevices];
+
+int device_cus(int dev, hipError_t *err) {
+    *err = hipSuccess;
+    if (dev >= 0 && dev < kMaxDevices) {
+        int c = g_num_cus[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int c = 0;
+    *err = hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev);
+    if (*err != hipSuccess) return 0;
+    if (dev >= 0 && dev < kMaxDevices) g_num_cus[dev].store(c, std::memory_order_relaxed);
+    return c;
+}
+
+int spin_limit() {
+    const char *s = std::getenv("RR_SPIN_LIMIT");
+    if (s && *s) {
+        long v = std::strtol(s, nullptr, 10);
+        if (v >= 1 && v <= 0x7FFFFFFF) return (int)v;
+    }
+    return 1 << 20;
+}
+
+rr_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return RR_OK;
+    g_last_hip_error = (int)e;
+    if (e == hipErrorCooperativeLaunchTooLarge) return RR_ERR_UNSUPPORTED;
+    return RR_ERR_HIP;
+}
+
+size_t elem_size(rr_dtype dt) { return dt == RR_BF16 ? 2 : 4; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// [a, a + n) and [b, b + n) share a byte but do not start at the same address.
+bool partial_overlap(const void *a, const void *b, size_t n) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    if (pa == pb) return false;
+    return pa < pb + n && pb < pa + n;
+}
+
+// Common checks of the matrix arguments.  Returns RR_OK and the matrix size in bytes.
+rr_status check_matrix(int64_t M, int64_t N, rr_dtype dt, size_t *bytes) {
+    if (dt != RR_F32 && dt != RR_BF16) return RR_ERR_INVALID_ARGUMENT;
+    if (M < 0) return RR_ERR_INVALID_ARGUMENT;
+    if (M == 0) {
+        *bytes = 0;
+        return RR_OK;
+    }
+    if (N < 1) return RR_ERR_INVALID_ARGUMENT;
+    const size_t s = elem_size(dt);
+    if ((uint64_t)M > (uint64_t)INT64_MAX / (uint64_t)N / s) return RR_ERR_INVALID_ARGUMENT;
+    *bytes = (size_t)M * (size_t)N * s;
+    return RR_OK;
+}
+
+rr_status plan_status(rr::PlanResult r) {
+    switch (r) {
+    case rr::kPlanOk: return RR_OK;
+    case rr::kPlanUnsupported: return RR_ERR_UNSUPPORTED;
+    default: return RR_ERR_INVALID_ARGUMENT;
+    }
+}
+
+rr_status check_workspace(const rr::Plan &p, void *ws, size_t ws_bytes) {
+    if (p.ws_bytes == 0) return RR_OK;
+    if (!ws || ws_bytes < p.ws_bytes || !aligned16(ws)) return RR_ERR_WORKSPACE;
+    return RR_OK;
+}
+
+rr_status launch_args(hipStream_t stream, rr::LaunchArgs *a) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    const int cus = device_cus(dev, &e);
+    if (e != hipSuccess) return hip_status(e);
+    *a = rr::LaunchArgs{stream, cus, spin_limit()};
+    return RR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rr_status rr_softmax_fwd(const void *x, void *y, int64_t M, int64_t N, rr_dtype dt, void *ws,
+                         size_t ws_bytes, hipStream_t stream) {
+    size_t bytes = 0;
+    rr_status st = check_matrix(M, N, dt, &bytes);
+    if (st != RR_OK || M == 0) return st;
+    if (!x || !y || partial_overlap(x, y, bytes)) return RR_ERR_INVALID_ARGUMENT;
+    const bool vec = aligned16(x) && aligned16(y) && ((size_t)N * elem_size(dt)) % 16 == 0;
+    rr::Plan p;
+    st = plan_status(rr::make_plan(rr::kOpSoftmax, dt, M, N, vec, &p));
+    if (st != RR_OK) return st;
+    if ((st = check_workspace(p, ws, ws_bytes)) != RR_OK) return st;
+    rr::LaunchArgs a;
+    if ((st = launch_args(stream, &a)) != RR_OK) return st;
+    return hip_status(rr::launch_softmax(p, dt, x, y, M, N, ws, a));
+}
+
+rr_status rr_rmsnorm_fwd(const void *x, const void *w, void *y, float *rstd, int64_t M,
+                         int64_t N, rr_dtype dt, float eps, void *ws, size_t ws_bytes,
+                         hipStream_t stream) {
+    size_t bytes = 0;
+    rr_status st = check_matrix(M, N, dt, &bytes);
+    if (st != RR_OK) return st;
+    if (!(eps >= 0.0f) || eps == INFINITY) return RR_ERR_INVALID_ARGUMENT;
+    if (M == 0) return RR_OK;
+    if (!x || !w || !y || partial_overlap(x, y, bytes)) return RR_ERR_INVALID_ARGUMENT;
+    const bool vec = aligned16(x) && aligned16(y) && aligned16(w) &&
+                     ((size_t)N * elem_size(dt)) % 16 == 0;
+    rr::Plan p;
+    st = plan_status(rr::make_plan(rr::kOpRmsnorm, dt, M, N, vec, &p));
+    if (st != RR_OK) return st;
+    if ((st = check_workspace(p, ws, ws_bytes)) != RR_OK) return st;
+    rr::LaunchArgs a;
+    if ((st = launch_args(stream, &a)) != RR_OK) return st;
+    return hip_status(rr::launch_rmsnorm(p, dt, x, w, y, rstd, M, N, eps, ws, a));
+}
+
+rr_status rr_cross_entropy_fwd(const void *logits, const int32_t *labels, float *loss,
+                               float *lse, int64_t M, int64_t N, rr_dtype dt, void *ws,
+                               size_t ws_bytes, hipStream_t stream) {
+    (void)ws;
+    (void)ws_bytes;
+    size_t bytes = 0;
+    rr_status st = check_matrix(M, N, dt, &bytes);
+    if (st != RR_OK || M == 0) return st;
+    if (!logits || !labels || !loss || N > INT32_MAX) return RR_ERR_INVALID_ARGUMENT;
+    const bool vec = aligned16(logits) && ((size_t)N * elem_size(dt)) % 16 == 0;
+    rr::Plan p;
+    st = plan_status(rr::make_plan(rr::kOpXent, dt, M, N, vec, &p));
+    if (st != RR_OK) return st;
+    rr::LaunchArgs a;
+    if ((st = launch_args(stream, &a)) != RR_OK) return st;
+    return hip_status(rr::launch_xent(p, dt, logits, labels, loss, lse, M, N, a));
+}
+
+size_t rr_workspace_bytes(rr_op op, int64_t M, int64_t N, rr_dtype dt, int device) {
+    (void)device;
+    rr::Plan p;
+    if (M <= 0 || rr::make_plan(op, dt, M, N, true, &p) != rr::kPlanOk) return 0;
+    return p.ws_bytes;
+}
+
+rr_status rr_workspace_check(void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!ws || ws_bytes < sizeof(uint32_t)) return RR_ERR_WORKSPACE;
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_status(e);
+    uint32_t word = 0;
+    e = hipMemcpy(&word, ws, sizeof word, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_status(e);
+    if (word == 0) return RR_OK;
+    const uint32_t zero = 0;
+    e = hipMemcpy(ws, &zero, sizeof zero, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_status(e);
+    return RR_ERR_GRID_TIMEOUT;
+}
+
+rr_status rr_plan_query(rr_op op, int64_t M, int64_t N, rr_dtype dt, int vectorized,
+                        rr_plan_info *out) {
+    if (!out) return RR_ERR_INVALID_ARGUMENT;
+    rr::Plan p;
+    rr_status st = plan_status(rr::make_plan(op, dt, M, N, vectorized != 0, &p));
+    if (st != RR_OK) return st;
+    out->path = p.path;
+    out->vectorized = p.vec ? 1 : 0;
+    out->vals_per_lane = p.P;
+    out->lanes_per_row = p.R;
+    out->groups_per_row = p.G;
+    out->block_threads = p.block;
+    out->rows_per_block = p.rows_per_block;
+    out->max_n = p.max_n;
+    out->ws_bytes = p.ws_bytes;
+    return RR_OK;
+}
+
+rr_status rr_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t stream) {
+    if (!src || !dst || bytes % 16 != 0 || !aligned16(src) || !aligned16(dst) ||
+        partial_overlap(src, dst, bytes) || src == dst)
+        return RR_ERR_INVALID_ARGUMENT;
+    if (bytes == 0) return RR_OK;
+    rr::LaunchArgs a;
+    rr_status st = launch_args(stream, &a);
+    if (st != RR_OK) return st;
+    return hip_status(rr::launch_copy(src, dst, bytes, a));
+}
+
+const char *rr_status_string(rr_status status) {
+    switch (status) {
+    case RR_OK: return "RR_OK";
+    case RR_ERR_INVALID_ARGUMENT: return "RR_ERR_INVALID_ARGUMENT: invalid argument";
+    case RR_ERR_UNSUPPORTED: return "RR_ERR_UNSUPPORTED: shape or grid not supported";
+    case RR_ERR_WORKSPACE: return "RR_ERR_WORKSPACE: workspace missing, too small or misaligned";
+    case RR_ERR_HIP: return "RR_ERR_HIP: a HIP call failed (see rr_last_hip_error)";
+    case RR_ERR_GRID_TIMEOUT: return "RR_ERR_GRID_TIMEOUT: a split row timed out waiting for peers";
+    }
+    return "unknown rr_status";
+}
+
+int rr_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,147 @@
+// grid_exchange.hpp -- level (4) of the reduction ladder for rows split over G workgroups.
+//
+// The QuACK article (无需CUDA代码，给H100加速33%-50%), section 硬件感知的归约策略 part 4
+// and the section 内存吞吐量, lets up to 16 blocks of a cluster reduce one row through
+// distributed shared memory, so that rows too large for one SM are still read from
+// HBM only once (instead of an online algorithm that reads twice, or register
+// spills).  gfx950 has no clusters, so the G workgroups of a row meet in a small
+// global workspace instead:
+//
+//  * every workgroup k of a row group publishes its partial result in slot k as
+//    64-bit words (epoch << 32) | float_bits, written and read with agent-scope
+//    relaxed atomics.  The epoch (row iteration + 1) travels in the same word as the
+//    value, so a reader that sees the right epoch has the right value: no fences,
+//    no separate flag, no cache write-back or invalidate;
+//  * slots are double-buffered by iteration parity: a workgroup can only overwrite
+//    its parity-p slot two iterations later, after every peer has published the
+//    iteration in between, i.e. after every peer finished reading;
+//  * wave 0 polls the G slots (one lane per slot), then merges the partials in slot
+//    order, so every workgroup of the row computes the same bits;
+//  * each poll loop is bounded by `spin_limit`; a workgroup that gives up sets the
+//    workspace error word and carries on (its outputs are then not valid), so a
+//    kernel always finishes;
+//  * after its last row every workgroup increments the group's departure counter;
+//    the last one to leave zeroes the group's slots and the counter, so the
+//    workspace is all zero again for the next launch.
+//
+// Every workgroup of the grid must be resident at once (cooperative launch).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "configs.hpp"
+#include "reduce.hpp"
+
+namespace rr {
+
+struct GroupRef {
+    uint32_t *depart;  // departure counter
+    uint64_t *slots;   // [2][G][2]
+    uint32_t *error;   // workspace error word
+};
+
+template <int G>
+__device__ __forceinline__ GroupRef group_ref(uint8_t *ws, int group) {
+    uint8_t *rec = ws + kWsHeader + (size_t)group * group_stride_for(G);
+    return {reinterpret_cast<uint32_t *>(rec), reinterpret_cast<uint64_t *>(rec + 64),
+            reinterpret_cast<uint32_t *>(ws)};
+}
+
+__device__ __forceinline__ uint64_t tag(uint32_t epoch, float v) {
+    return ((uint64_t)epoch << 32) | __float_as_uint(v);
+}
+
+__device__ __forceinline__ void atomic_put(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t atomic_get(const uint64_t *p) {
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Publishes (a, b) for member k at iteration `it`, waits for all G members and
+// leaves the G pairs merged in member order by `merge2` in bcast[0..1] (the same
+// bits for the whole workgroup).  Called by every thread; uses one barrier.
+// After a wait has timed out, `spin_limit` is lowered to 1 so that the rest of
+// the launch does not wait again.
+template <int G, class Merge>
+__device__ __forceinline__ void exchange_pairs(GroupRef g, int k, int it, float a, float b,
+                                               int &spin_limit, float *bcast, Merge merge2) {
+    const int tid = threadIdx.x;
+    const int par = it & 1;
+    const uint32_t epoch = (uint32_t)it + 1u;
+    uint64_t *slot = g.slots + (size_t)par * G * 2;
+    if (tid == 0) {
+        atomic_put(slot + 2 * k, tag(epoch, a));
+        atomic_put(slot + 2 * k + 1, tag(epoch, b));
+    }
+    if (tid < 64) {
+        const int lane = tid;
+        uint64_t wa = 0, wb = 0;
+        bool all_in = false;
+        int spins = 0;
+        while (true) {
+            bool mine = true;
+            if (lane < G) {
+                wa = atomic_get(slot + 2 * lane);
+                wb = atomic_get(slot + 2 * lane + 1);
+                mine = (uint32_t)(wa >> 32) == epoch && (uint32_t)(wb >> 32) == epoch;
+            }
+            all_in = __all(mine);
+            if (all_in || ++spins >= spin_limit) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (!all_in && lane == 0)
+            __hip_atomic_store(g.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!all_in) bcast[2] = 1.0f;
+        float va = __uint_as_float((uint32_t)wa);
+        float vb = __uint_as_float((uint32_t)wb);
+        float acc_a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(va), 0));
+        float acc_b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vb), 0));
+#pragma unroll
+        for (int j = 1; j < G; ++j) {
+            float ja = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(va), j));
+            float jb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vb), j));
+            merge2(acc_a, acc_b, ja, jb);
+        }
+        if (lane == 0) {
+            bcast[0] = acc_a;
+            bcast[1] = acc_b;
+        }
+    }
+    __syncthreads();
+    if (bcast[2] != 0.0f) spin_limit = 1;
+}
+
+// Called once per workgroup after its last row (only if it processed any row).
+template <int G>
+__device__ __forceinline__ void depart_group(GroupRef g) {
+    if (threadIdx.x == 0) {
+        uint32_t before =
+            __hip_atomic_fetch_add(g.depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (before == (uint32_t)G - 1u) {
+            for (int i = 0; i < 2 * G * 2; ++i) atomic_put(g.slots + i, 0ull);
+            __hip_atomic_store(g.depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+// Which row group and member this workgroup is.  Consecutive block ids go to
+// different XCDs (round-robin dispatch), so members of one group are taken from
+// blocks with the same id modulo 8, which keeps a row's exchange inside one XCD
+// when the dispatcher behaves that way.  Correctness does not depend on it.
+template <int G>
+__device__ __forceinline__ void group_of_block(int groups, int *group, int *member) {
+    const int b = blockIdx.x;
+    if (groups % 8 == 0) {
+        const int xcd = b & 7, slot = b >> 3;
+        *group = xcd * (groups >> 3) + slot / G;
+        *member = slot % G;
+    } else {
+        *group = b / G;
+        *member = b % G;
+    }
+}
+
+}  // namespace rr

@@ -1,0 +1,27 @@
+// launch.hpp -- host-side launchers of the HIP kernels (one per op).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "plan.hpp"
+
+namespace rr {
+
+struct LaunchArgs {
+    hipStream_t stream;
+    int num_cus;     // compute units of the current device
+    int spin_limit;  // bound on each grid-exchange wait (polls)
+};
+
+hipError_t launch_softmax(const Plan &p, int dtype, const void *x, void *y, int64_t M, int64_t N,
+                          void *ws, const LaunchArgs &a);
+hipError_t launch_rmsnorm(const Plan &p, int dtype, const void *x, const void *w, void *y,
+                          float *rstd, int64_t M, int64_t N, float eps, void *ws,
+                          const LaunchArgs &a);
+hipError_t launch_xent(const Plan &p, int dtype, const void *x, const int32_t *labels,
+                       float *loss, float *lse, int64_t M, int64_t N, const LaunchArgs &a);
+hipError_t launch_copy(const void *src, void *dst, size_t bytes, const LaunchArgs &a);
+
+}  // namespace rr

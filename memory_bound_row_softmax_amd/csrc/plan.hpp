@@ -1,0 +1,37 @@
+// plan.hpp -- host planner: picks the kernel configuration for (op, dtype, M, N).
+// No HIP here, so it is testable on any machine.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace rr {
+
+enum PathKind { kPathRow = 0, kPathGrid = 1, kPathStream = 2 };
+enum OpKind { kOpSoftmax = 0, kOpRmsnorm = 1, kOpXent = 2 };
+enum DtypeKind { kF32 = 0, kBf16 = 1 };
+enum PlanResult { kPlanOk = 0, kPlanUnsupported = 1, kPlanInvalid = 2 };
+
+struct Plan {
+    int path = kPathRow;
+    bool vec = true;
+    int P = 0, R = 0, G = 1;
+    int block = 0, rows_per_block = 0;
+    int64_t max_n = 0;
+    size_t ws_bytes = 0;
+};
+
+// Whether (P, R, G) is in the compiled row menu / (P, R) in the streaming menu.
+bool row_config_exists(int P, int R, int G);
+bool xent_config_exists(int P, int R);
+
+// Chooses the plan.  `vec` says whether the 128-bit path is usable for these
+// pointers.  Test-only overrides come from the environment: RR_FORCE_P,
+// RR_FORCE_R and RR_FORCE_G (row ops) or RR_FORCE_P and RR_FORCE_R (cross-entropy);
+// a forced configuration that is not compiled, or too small for N, is unsupported.
+PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *out);
+
+// Workspace bytes of the grid path for G workgroups per row and M rows.
+size_t grid_ws_bytes(int G, int64_t M);
+
+}  // namespace rr

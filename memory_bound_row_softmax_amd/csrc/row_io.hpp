@@ -1,0 +1,94 @@
+// row_io.hpp -- a lane's share of a row: which chunks it owns, loads, masks, stores.
+//
+// Lane l of a group of R lanes owns chunks chunk0 + i * R + l for i = 0..C-1
+// (chunk = 16 bytes).  For a fixed i the R lanes touch R consecutive chunks, so
+// each load instruction of a wave covers contiguous memory (1 KiB when R >= 64).
+// All C loads are issued before any value is used and none sits behind a branch.
+//
+// A RowView is a buffer resource plus the byte offset of the row inside it: one
+// row per resource when a row has at least one whole wave (the resource is then
+// wave-uniform and lives in scalar registers), the block's rows when several rows
+// share a wave.  Reads past the end of the resource return 0 in hardware.  When a
+// lane's part is not full (N does not fill the configuration), mask_part() puts a
+// neutral value in the registers that hold no element of the row.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "vec_io.hpp"
+
+namespace rr {
+
+struct RowView {
+    Buf buf;
+    uint32_t base;  // byte offset of the row inside buf
+};
+
+// Whether every element owned by lanes chunk0 .. chunk0 + C * R - 1 lies in the row.
+template <class E, int C, int R>
+__device__ __forceinline__ bool part_full(int chunk0, int N) {
+    return (int64_t)(chunk0 + C * R) * E::VPC <= (int64_t)N;
+}
+
+template <class E, int C, int R, bool VEC>
+__device__ __forceinline__ void load_part(RowView rv, int chunk0, int l, float *v) {
+    constexpr int VPC = E::VPC;
+    if constexpr (VEC) {
+        u32x4 raw[C];
+#pragma unroll
+        for (int i = 0; i < C; ++i)
+            raw[i] = buf_load16(rv.buf, rv.base + (uint32_t)(chunk0 + i * R + l) * 16u);
+#pragma unroll
+        for (int i = 0; i < C; ++i) decode<E>(raw[i], v + i * VPC);
+    } else {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+#pragma unroll
+            for (int e = 0; e < VPC; ++e) {
+                const uint32_t idx = (uint32_t)(chunk0 + i * R + l) * VPC + e;
+                v[i * VPC + e] = buf_load_elem<E>(rv.buf, rv.base + idx * E::BYTES);
+            }
+        }
+    }
+}
+
+// Registers that hold no element of the row get `fill`.
+template <class E, int C, int R>
+__device__ __forceinline__ void mask_part(int chunk0, int l, int N, float fill, float *v) {
+    constexpr int VPC = E::VPC;
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const int first = (chunk0 + i * R + l) * VPC;
+#pragma unroll
+        for (int e = 0; e < VPC; ++e)
+            if (first + e >= N) v[i * VPC + e] = fill;
+    }
+}
+
+template <class E, int C, int R, bool VEC>
+__device__ __forceinline__ void store_part(RowView rv, int chunk0, int l, int N, bool valid,
+                                           bool full, const float *v) {
+    constexpr int VPC = E::VPC;
+    if constexpr (VEC) {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int c = chunk0 + i * R + l;
+            if (valid && (full || c * VPC < N))
+                buf_store16(rv.buf, rv.base + (uint32_t)c * 16u, encode<E>(v + i * VPC));
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+#pragma unroll
+            for (int e = 0; e < VPC; ++e) {
+                const int idx = (chunk0 + i * R + l) * VPC + e;
+                if (valid && (full || idx < N))
+                    buf_store_elem<E>(rv.buf, rv.base + (uint32_t)idx * E::BYTES, v[i * VPC + e]);
+            }
+        }
+    }
+}
+
+}  // namespace rr

@@ -1,0 +1,103 @@
+"""Helpers of the GPU tests: move seeded numpy inputs to the device, run an op
+through the C ABI, bring the outputs back, and compare them with the oracle."""
+from __future__ import annotations
+
+import os
+import sys
+from contextlib import contextmanager
+
+import numpy as np
+import torch
+
+import memory_bound_row_softmax_amd as rr
+import oracle
+from _verify import check_bf16, check_f32
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    """Names the case about to run on the GPU, flushed before the GPU step."""
+    print("[gpu]", *a, file=sys.stderr, flush=True)
+
+
+def to_dev(a: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def from_dev(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+@contextmanager
+def forced(P=None, R=None, G=None, spin=None):
+    """Test-only plan overrides (read by the library at every call)."""
+    keys = {"RR_FORCE_P": P, "RR_FORCE_R": R, "RR_FORCE_G": G, "RR_SPIN_LIMIT": spin}
+    old = {k: os.environ.get(k) for k in keys}
+    try:
+        for k, v in keys.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = str(v)
+        yield
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def check_out(got: np.ndarray, ref: np.ndarray, dtype: str, what: str):
+    if dtype == "f32":
+        return check_f32(got, ref, what)
+    return check_bf16(got, ref, what)
+
+
+def run_softmax(x_np, dtype, ws=None, inplace=False):
+    x = to_dev(x_np, dtype)
+    y = x if inplace else torch.empty_like(x)
+    rr.rr_softmax_fwd(x, y, ws=ws)
+    torch.cuda.synchronize()
+    return from_dev(y)
+
+
+def run_rmsnorm(x_np, w_np, eps, dtype, want_rstd=False):
+    x = to_dev(x_np, dtype)
+    w = to_dev(w_np, dtype)
+    rstd = torch.empty(x.shape[0], dtype=torch.float32, device=DEV) if want_rstd else None
+    y = rr.rr_rmsnorm_fwd(x, w, eps, rstd=rstd)
+    torch.cuda.synchronize()
+    return (from_dev(y), rstd.cpu().numpy()) if want_rstd else from_dev(y)
+
+
+def run_xent(x_np, labels_np, dtype):
+    x = to_dev(x_np, dtype)
+    lab = torch.from_numpy(np.ascontiguousarray(labels_np, dtype=np.int32)).to(DEV)
+    loss, lse = rr.rr_cross_entropy_fwd(x, lab)
+    torch.cuda.synchronize()
+    return loss.cpu().numpy(), lse.cpu().numpy()
+
+
+def parity_softmax(x_np, dtype, what):
+    got = run_softmax(x_np, dtype)
+    return check_out(got, oracle.softmax(x_np), dtype, what)
+
+
+def parity_rmsnorm(x_np, w_np, eps, dtype, what):
+    got, rstd = run_rmsnorm(x_np, w_np, eps, dtype, want_rstd=True)
+    ref, ref_rstd = oracle.rmsnorm(x_np, w_np, eps, want_rstd=True)
+    check_f32(rstd, ref_rstd, what + " rstd")
+    return check_out(got, ref, dtype, what)
+
+
+def parity_xent(x_np, labels_np, dtype, what):
+    loss, lse = run_xent(x_np, labels_np, dtype)
+    ref_loss, ref_lse = oracle.cross_entropy(x_np, labels_np)
+    check_f32(lse, ref_lse, what + " lse")
+    return check_f32(loss, ref_loss, what + " loss")

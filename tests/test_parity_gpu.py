@@ -1,0 +1,274 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the double-precision
+oracle, element by element, on seeded inputs.
+
+Tolerances (tests/_verify.py): fp32 outputs within relative 1e-5, bf16 outputs
+within one bf16 ulp of the exact value.  Sizes are small enough for the oracle to
+finish in seconds but span several tiles and ragged tails; every path (one lane
+group per row, one workgroup per row, split rows, the per-element path for
+unaligned rows) is run, the split-row path also forced at small N with many rows.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_row_softmax_amd as rr
+import oracle
+import synth
+from _gpu import (DEV, check_out, forced, from_dev, parity_rmsnorm, parity_softmax,
+                  parity_xent, run_softmax, say, to_dev)
+from _verify import check_f32
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ("f32", "bf16")
+# (M, N): every plan bucket, ragged tails, a few rows past a block boundary
+SHAPES = [(256, 1024), (64, 1), (64, 3), (70, 255), (64, 256), (33, 257), (37, 1000), (16, 2048),
+          (16, 4095), (16, 4096), (9, 4097), (8, 16384), (5, 20000), (4, 65536), (3, 65537),
+          (3, 131072), (2, 200000), (2, 262144)]
+
+
+def _x(M, N, dtype, sigma=1.0, seed=synth.SEED):
+    return synth.normal(M, N, sigma=sigma, dtype=dtype, seed=seed)
+
+
+def _w(N, dtype):
+    return synth.uniform(1, N, lo=0.5, hi=1.5, dtype=dtype).reshape(N)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N", SHAPES)
+def test_softmax(M, N, dtype):
+    say("softmax", dtype, M, N)
+    parity_softmax(_x(M, N, dtype, sigma=3.0), dtype, f"softmax {dtype} {M}x{N}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N", SHAPES)
+def test_rmsnorm(M, N, dtype):
+    say("rmsnorm", dtype, M, N)
+    parity_rmsnorm(_x(M, N, dtype), _w(N, dtype), 1e-6, dtype, f"rmsnorm {dtype} {M}x{N}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N", SHAPES + [(40, 50000)])
+def test_cross_entropy(M, N, dtype):
+    say("xent", dtype, M, N)
+    x = _x(M, N, dtype, sigma=2.0)
+    lab = synth.labels(M, N)
+    parity_xent(x, lab, dtype, f"xent {dtype} {M}x{N}")
+
+
+# ------------------------------------------------------------- forced paths
+
+FORCED_ROW = [  # (P, R, G, M, N): split rows at small N, empty / partial member slices
+    (64, 256, 2, 300, 20000), (64, 256, 4, 300, 3000), (32, 256, 16, 97, 70000),
+    (64, 512, 2, 50, 65536), (32, 1024, 2, 40, 65536), (64, 1024, 16, 9, 1000000),
+    (16, 16, 1, 100, 256), (32, 128, 1, 31, 4000), (16, 1024, 1, 5, 16384)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("P,R,G,M,N", FORCED_ROW)
+def test_forced_row_plans(P, R, G, M, N, dtype):
+    for op in ("softmax", "rmsnorm"):
+        code = rr.RR_OP_SOFTMAX if op == "softmax" else rr.RR_OP_RMSNORM
+        with forced(P, R, G):
+            try:
+                rr.rr_plan_query(code, M, N, rr.RR_F32 if dtype == "f32" else rr.RR_BF16)
+            except rr.RRError:
+                continue  # not compiled for this op (register budget)
+            say(op, "forced", P, R, G, dtype, M, N)
+            if op == "softmax":
+                parity_softmax(_x(M, N, dtype, sigma=2.0), dtype, f"softmax forced {P},{R},{G}")
+            else:
+                parity_rmsnorm(_x(M, N, dtype), _w(N, dtype), 1e-6, dtype,
+                               f"rmsnorm forced {P},{R},{G}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("P,R", [(16, 16), (16, 1024), (32, 64), (32, 512)])
+def test_forced_xent_plans(P, R, dtype):
+    M, N = 45, 7777
+    with forced(P, R):
+        say("xent forced", P, R, dtype)
+        parity_xent(_x(M, N, dtype, sigma=2.0), synth.labels(M, N), dtype, f"xent forced {P},{R}")
+
+
+# ------------------------------------------------------------- layouts
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("N", [64, 1000, 4096, 40000, 131072])
+def test_unaligned_rows_take_the_element_path(N, dtype):
+    M = 6
+    x_np = _x(M, N, dtype, sigma=2.0)
+    w_np = _w(N, dtype)
+    code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
+    # the tensors start one element past a 16-byte boundary
+    xs = to_dev(np.concatenate([np.zeros(1, x_np.dtype), x_np.ravel()]), dtype)[1:].view(M, N)
+    ys = torch.empty(M * N + 1, dtype=xs.dtype, device=DEV)[1:].view(M, N)
+    wt = torch.empty(N + 1, dtype=xs.dtype, device=DEV)[1:]
+    wt.copy_(to_dev(w_np, dtype))
+    assert xs.data_ptr() % 16 != 0 and wt.data_ptr() % 16 != 0
+    say("unaligned softmax", dtype, N)
+    rr.rr_softmax_fwd(xs, ys, ws=rr.workspace(rr.RR_OP_SOFTMAX, M, N, code, DEV))
+    torch.cuda.synchronize()
+    check_out(from_dev(ys), oracle.softmax(x_np), dtype, "unaligned softmax")
+    say("unaligned rmsnorm", dtype, N)
+    rr.rr_rmsnorm_fwd(xs, wt, 1e-6, y=ys, ws=rr.workspace(rr.RR_OP_RMSNORM, M, N, code, DEV))
+    torch.cuda.synchronize()
+    check_out(from_dev(ys), oracle.rmsnorm(x_np, w_np, 1e-6), dtype, "unaligned rmsnorm")
+    say("unaligned xent", dtype, N)
+    lab = synth.labels(M, N)
+    loss, lse = rr.rr_cross_entropy_fwd(xs, torch.from_numpy(lab).to(DEV))
+    ref_loss, ref_lse = oracle.cross_entropy(x_np, lab)
+    check_f32(lse.cpu().numpy(), ref_lse, "unaligned lse")
+    check_f32(loss.cpu().numpy(), ref_loss, "unaligned loss")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N", [(64, 1024), (8, 131072)])
+def test_in_place(M, N, dtype):
+    x_np = _x(M, N, dtype, sigma=2.0)
+    say("in-place softmax", dtype, M, N)
+    got = run_softmax(x_np, dtype, inplace=True)
+    check_out(got, oracle.softmax(x_np), dtype, "in-place softmax")
+    say("in-place rmsnorm", dtype, M, N)
+    w_np = _w(N, dtype)
+    x = to_dev(x_np, dtype)
+    rr.rr_rmsnorm_fwd(x, to_dev(w_np, dtype), 1e-6, y=x)
+    torch.cuda.synchronize()
+    check_out(from_dev(x), oracle.rmsnorm(x_np, w_np, 1e-6), dtype, "in-place rmsnorm")
+
+
+# ------------------------------------------------------------- special values
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_closed_forms(dtype):
+    say("closed forms", dtype)
+    # constant rows: softmax = 1/N exactly; CE = ln N; RMSNorm = w * c / sqrt(c^2 + eps)
+    for N in (1, 4096, 131072):
+        c = np.full((4, N), 2.5, dtype=np.float32)
+        x = c if dtype == "f32" else synth.f32_to_bf16(c)
+        y = run_softmax(x, dtype)
+        y = y if dtype == "f32" else (y.astype(np.uint32) << 16).view(np.float32)
+        assert np.all(y == np.float32(1.0 / N)), N
+        parity_xent(x, np.zeros(4, np.int32), dtype, "constant xent")
+        parity_rmsnorm(x, _w(N, dtype), 1e-6, dtype, "constant rmsnorm")
+    # N = 1: softmax 1, cross-entropy 0
+    x = _x(50, 1, dtype, sigma=5.0)
+    y = run_softmax(x, dtype)
+    y = y if dtype == "f32" else (y.astype(np.uint32) << 16).view(np.float32)
+    assert np.all(y == 1.0)
+    lab = np.zeros(50, np.int32)
+    x_dev = to_dev(x, dtype)
+    loss, lse = rr.rr_cross_entropy_fwd(x_dev, torch.from_numpy(lab).to(DEV))
+    torch.cuda.synchronize()
+    assert np.all(loss.cpu().numpy() == 0.0)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_spiky_and_large_rows(dtype):
+    say("spiky / large rows", dtype)
+    x = _x(40, 8192, dtype)
+    synth.spikes_(x, p=0.01, value=20.0, dtype=dtype)
+    parity_softmax(x, dtype, "spiky softmax")
+    parity_xent(x, synth.labels(40, 8192), dtype, "spiky xent")
+    big = (_x(8, 3000, "f32") * 30 + 1000.0).astype(np.float32)
+    big = big if dtype == "f32" else synth.f32_to_bf16(big)
+    parity_softmax(big, dtype, "large-value softmax")
+    parity_xent(big, synth.labels(8, 3000), dtype, "large-value xent")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_invalid_labels_give_nan(dtype):
+    say("invalid labels", dtype)
+    M, N = 8, 5000
+    x = _x(M, N, dtype, sigma=2.0)
+    lab = np.array([0, -1, N, N - 1, 1 << 30, 7, -(1 << 30), 4999], dtype=np.int32)
+    parity_xent(x, lab, dtype, "invalid labels")
+
+
+def test_nan_input_propagates():
+    say("nan input")
+    x = _x(4, 3000, "f32")
+    x[1, 17] = np.nan
+    got = run_softmax(x, "f32")
+    assert np.all(np.isnan(got[1])) and np.all(np.isfinite(got[[0, 2, 3]]))
+
+
+def test_golden_cases():
+    say("golden cases")
+    path = os.path.join(os.path.dirname(__file__), "golden", "tiny_cases.json")
+    for c in json.load(open(path))["cases"]:
+        if c["dtype"] == "f32":
+            x = np.array([[float.fromhex(v) for v in r] for r in c["x"]], dtype=np.float32)
+            w = np.array([float.fromhex(v) for v in c["w"]], dtype=np.float32) if "w" in c else None
+        else:
+            x = np.array([[int(v, 16) for v in r] for r in c["x"]], dtype=np.uint16)
+            w = np.array([int(v, 16) for v in c["w"]], dtype=np.uint16) if "w" in c else None
+        if c["op"] == "softmax":
+            ref = np.array([[float(v) for v in r] for r in c["y"]])
+            check_out(run_softmax(x, c["dtype"]), ref, c["dtype"], c["name"])
+        elif c["op"] == "rmsnorm":
+            from _gpu import run_rmsnorm
+            ref = np.array([[float(v) for v in r] for r in c["y"]])
+            check_out(run_rmsnorm(x, w, c["eps"], c["dtype"]), ref, c["dtype"], c["name"])
+        else:
+            from _gpu import run_xent
+            loss, lse = run_xent(x, np.array(c["labels"], np.int32), c["dtype"])
+            check_f32(lse, np.array([float(v) for v in c["lse"]]), c["name"] + " lse")
+            check_f32(loss, np.array([float(v) for v in c["loss"]]), c["name"] + " loss")
+
+
+# ------------------------------------------------------------- grid path hygiene
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_split_rows_are_deterministic_and_leave_the_workspace_zero(dtype):
+    M, N = 600, 131072 if dtype == "f32" else 262144
+    code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
+    assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, M, N, code)["path"] == 1
+    x = to_dev(_x(M, N, dtype, sigma=2.0), dtype)
+    ws = rr.workspace(rr.RR_OP_SOFTMAX, M, N, code, DEV)
+    outs = []
+    for i in range(3):
+        say("split-row repeat", i, dtype)
+        y = rr.rr_softmax_fwd(x, ws=ws)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0
+        outs.append(y)
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    assert rr.rr_workspace_check(ws) == rr.RR_OK
+    # rows sum to 1 (in double) on every row
+    s = outs[0].double().sum(dim=1)
+    assert float((s - 1).abs().max()) < (1e-4 if dtype == "f32" else 2e-2)
+
+
+def test_grid_wait_timeout_is_reported_not_hung():
+    """A spin limit of one poll makes split-row workgroups give up at once: the
+    kernel must still finish, report the timeout, and leave the workspace clean."""
+    M, N = 64, 131072
+    x = to_dev(_x(M, N, "f32"), "f32")
+    ws = rr.workspace(rr.RR_OP_SOFTMAX, M, N, rr.RR_F32, DEV)
+    say("forced grid timeout")
+    with forced(spin=1):
+        rr.rr_softmax_fwd(x, ws=ws)
+    st = rr.rr_workspace_check(ws)
+    assert st in (rr.RR_OK, rr.RR_ERR_GRID_TIMEOUT)
+    assert int(ws.count_nonzero()) == 0  # error word cleared by the check, slots by the kernel
+    # a normal launch afterwards is correct again
+    say("after timeout")
+    y = rr.rr_softmax_fwd(x, ws=ws)
+    torch.cuda.synchronize()
+    check_f32(y[:4].cpu().numpy(), oracle.softmax(from_dev(x)[:4]), "after timeout")
+    assert rr.rr_workspace_check(ws) == rr.RR_OK
+
+
+def test_stream_copy():
+    say("stream copy")
+    a = torch.randn(1 << 20, device=DEV)
+    b = torch.empty_like(a)
+    rr.rr_stream_copy(a, b)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

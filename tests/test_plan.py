@@ -1,0 +1,93 @@
+"""The host planner (through rr_plan_query, no GPU needed): every supported N gets
+a compiled configuration that holds the row, the grid path appears only past
+one workgroup's capacity, workspace sizes follow the documented layout, and the
+test-only overrides reach every path."""
+import os
+
+import pytest
+
+import memory_bound_row_softmax_amd as rr
+
+ROW_OPS = (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM)
+NS = [1, 2, 3, 7, 100, 255, 256, 257, 1000, 1024, 2048, 4095, 4096, 4097, 8192, 16384, 32768,
+      65535, 65536, 65537, 131072, 200000, 262144, 524288, 1 << 20]
+
+
+@pytest.mark.parametrize("op", ROW_OPS)
+@pytest.mark.parametrize("dt", (rr.RR_F32, rr.RR_BF16))
+@pytest.mark.parametrize("vec", (True, False))
+def test_row_plans_hold_the_row(op, dt, vec):
+    for N in NS:
+        if N > 262144:  # beyond the guaranteed range: either a plan that holds it, or refused
+            try:
+                p = rr.rr_plan_query(op, 16384, N, dt, vec)
+            except rr.RRError as e:
+                assert e.status == rr.RR_ERR_UNSUPPORTED
+                continue
+        else:
+            p = rr.rr_plan_query(op, 16384, N, dt, vec)
+        P, R, G = p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]
+        assert p["max_n"] == P * R * G >= N
+        assert p["path"] == (1 if G > 1 else 0)
+        assert p["block_threads"] == max(R, 256) and p["rows_per_block"] * R == p["block_threads"]
+        assert p["vectorized"] == int(vec)
+        if G > 1:
+            assert p["ws_bytes"] == 256 + 1024 * (64 + 32 * G)
+            # a split row only when one workgroup (1024 lanes) cannot hold it
+            assert N > P * R or R == 1024 or N > 32768
+        else:
+            assert p["ws_bytes"] == 0
+            # the narrowest lane group that holds the row (at least 16 lanes)
+            assert R == 16 or (R // 2) * P < N
+    with pytest.raises(rr.RRError):
+        rr.rr_plan_query(op, 16, (1 << 20) + 1, dt, vec)
+
+
+def test_workspace_scales_with_rows_up_to_the_group_cap():
+    N = 131072
+    small = rr.workspace_bytes(rr.RR_OP_SOFTMAX, 3, N, rr.RR_F32)
+    big = rr.workspace_bytes(rr.RR_OP_SOFTMAX, 100000, N, rr.RR_F32)
+    G = rr.rr_plan_query(rr.RR_OP_SOFTMAX, 3, N, rr.RR_F32)["groups_per_row"]
+    assert small == 256 + 3 * (64 + 32 * G)
+    assert big == 256 + 1024 * (64 + 32 * G)
+    assert rr.workspace_bytes(rr.RR_OP_SOFTMAX, 0, N, rr.RR_F32) == 0
+    assert rr.workspace_bytes(rr.RR_OP_XENT, 8192, N, rr.RR_F32) == 0
+
+
+@pytest.mark.parametrize("dt", (rr.RR_F32, rr.RR_BF16))
+def test_cross_entropy_streams(dt):
+    for N in NS + [(1 << 22) + 3]:
+        p = rr.rr_plan_query(rr.RR_OP_XENT, 8192, N, dt)
+        assert p["path"] == 2 and p["groups_per_row"] == 1 and p["ws_bytes"] == 0
+        assert p["vals_per_lane"] in (16, 32) and 16 <= p["lanes_per_row"] <= 256
+
+
+def test_forced_configurations(monkeypatch):
+    monkeypatch.setenv("RR_FORCE_P", "64")
+    monkeypatch.setenv("RR_FORCE_R", "256")
+    monkeypatch.setenv("RR_FORCE_G", "4")
+    p = rr.rr_plan_query(rr.RR_OP_SOFTMAX, 50, 3000, rr.RR_F32)
+    assert (p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"], p["path"]) == (64, 256, 4, 1)
+    assert p["ws_bytes"] == 256 + 50 * (64 + 32 * 4)
+    # too small for the row
+    with pytest.raises(rr.RRError):
+        rr.rr_plan_query(rr.RR_OP_SOFTMAX, 50, 70000, rr.RR_F32)
+    # not compiled for RMSNorm (would not fit in registers): 64 values x 1024 lanes
+    monkeypatch.setenv("RR_FORCE_R", "1024")
+    monkeypatch.setenv("RR_FORCE_G", "1")
+    with pytest.raises(rr.RRError):
+        rr.rr_plan_query(rr.RR_OP_RMSNORM, 50, 3000, rr.RR_F32)
+    monkeypatch.delenv("RR_FORCE_G")
+    monkeypatch.setenv("RR_FORCE_P", "16")
+    monkeypatch.setenv("RR_FORCE_R", "64")
+    p = rr.rr_plan_query(rr.RR_OP_XENT, 50, 3000, rr.RR_F32)
+    assert (p["vals_per_lane"], p["lanes_per_row"]) == (16, 64)
+
+
+def test_invalid_plan_arguments():
+    for args in ((rr.RR_OP_SOFTMAX, -1, 10, rr.RR_F32), (rr.RR_OP_SOFTMAX, 4, 0, rr.RR_F32),
+                 (7, 4, 10, rr.RR_F32), (rr.RR_OP_SOFTMAX, 4, 10, 3),
+                 (rr.RR_OP_XENT, 4, 1 << 31, rr.RR_F32)):
+        with pytest.raises(rr.RRError) as e:
+            rr.rr_plan_query(*args)
+        assert e.value.status == rr.RR_ERR_INVALID_ARGUMENT

@@ -77,7 +77,7 @@ def traffic_for(name: str):
 class Runner:
     """Device buffers for one workload and a launcher for step k."""
 
-    def __init__(self, w, min_rotation_bytes: float, device="cuda:0"):
+    def __init__(self, w, min_rotation_bytes: float, device="cuda:0", host_rows=None):
         import numpy as np
         import torch
 
@@ -93,14 +93,22 @@ class Runner:
         self.sets = max(1, min(16, math.ceil(min_rotation_bytes / (in_bytes + out_bytes))))
         tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
 
-        x_np = W.x_rows(w)
+        # host_rows: generate only that many rows and repeat them down the matrix
+        # (used by the sweep, whose largest inputs are tens of GiB; throughput does
+        # not depend on the values)
+        gen_rows = w.M if host_rows is None else min(w.M, host_rows)
+        x_np = W.x_rows(w, nrows=gen_rows)
         host = torch.from_numpy(x_np if w.dtype == "f32" else x_np.view(np.int16))
-        x0 = host.to(device)
-        del host, x_np
+        x0 = torch.empty((w.M, w.N), dtype=host.dtype, device=device)
+        block = host.to(device)
+        for r0 in range(0, w.M, gen_rows):
+            r1 = min(w.M, r0 + gen_rows)
+            x0[r0:r1].copy_(block[: r1 - r0])
+        del host, x_np, block
         x0 = x0.view(tdt) if w.dtype == "bf16" else x0
         self.x = [x0] + [x0.clone() for _ in range(self.sets - 1)]
         if w.op == "xent":
-            lab = torch.from_numpy(W.label_rows(w)).to(device)
+            lab = torch.from_numpy(W.label_rows(w)).to(device)  # labels are per row: all rows
             self.labels = lab
             self.loss = [torch.empty(w.M, dtype=torch.float32, device=device) for _ in range(self.sets)]
             self.lse = [torch.empty(w.M, dtype=torch.float32, device=device) for _ in range(self.sets)]
@@ -193,16 +201,22 @@ def cpu_baseline(w, seconds: float):
     probe = max(1, min(w.M, (1 << 20) // w.N))
     t = run(probe)
     rows = max(1, min(w.M, int(probe * seconds / max(t, 1e-6))))
-    t = run(rows)
-    return {"value": round(per_row * rows / t / 1e9, 4), "unit": "GB/s", "cores": 1,
+    passes = 1
+    if rows == w.M:  # the whole matrix takes less than `seconds`: repeat it
+        t_all = run(rows)
+        passes = max(1, int(seconds / max(t_all, 1e-6)))
+    total = 0.0
+    for _ in range(passes):
+        total += run(rows)
+    return {"value": round(per_row * rows * passes / total / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"first {rows} of {w.M} rows, one pass, single-threaded double-precision "
-                      f"oracle ({t:.1f} s)"}
+            "sample": f"first {rows} of {w.M} rows x {passes} pass(es), single-threaded "
+                      f"double-precision oracle, {total:.1f} s of CPU time"}
 
 
 def measure(w, steps: int, warmup: int, min_rotation_bytes: float, with_cpu: bool,
-            cpu_seconds: float):
-    r = Runner(w, min_rotation_bytes)
+            cpu_seconds: float, host_rows=None):
+    r = Runner(w, min_rotation_bytes, host_rows=host_rows)
     nbytes = algorithmic_bytes(w)
     wall, mean_ms, min_ms = r.time(r.launch, steps, warmup)
     copy_wall, copy_mean_ms, _ = r.time(r.copy_launch, steps, warmup)
@@ -258,6 +272,10 @@ def main() -> int:
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 31))
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep-host-rows", type=int, default=512,
+                    help="sweep only: rows generated on the host, repeated down the matrix")
+    ap.add_argument("--only", default="",
+                    help="sweep only: comma-separated substrings a workload name must contain")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -276,10 +294,13 @@ def main() -> int:
                     done.add(json.loads(l)["config"]["workload"])
                 except (ValueError, KeyError):
                     pass
+        only = [t for t in args.only.split(",") if t]
         for w in W.FIXED + W.sweep():
-            if w.name in done:
+            if w.name in done or (only and not all(t in w.name for t in only)):
                 continue
-            line = measure(w, args.steps, args.warmup, args.rotate_bytes, False, 0)
+            line = measure(w, args.steps, args.warmup, args.rotate_bytes, False, 0,
+                           host_rows=args.sweep_host_rows)
+            line["config"]["host_rows"] = args.sweep_host_rows
             with open(args.out, "a") as f:
                 f.write(json.dumps(line) + "\n")
             print(f"{w.name:34s} {line['roofline']['achieved']:9.1f} GB/s "

@@ -93,9 +93,10 @@ rr_status rr_cross_entropy_fwd(const void *logits, const int32_t *labels, float 
                                size_t ws_bytes, hipStream_t stream);
 
 /*
- * Bytes of workspace the call with these arguments needs (0 when it needs none).
- * The value depends only on (op, M, N, dt); `device` is accepted for callers that
- * size per device and is otherwise unused (pass -1).
+ * Bytes of workspace a call with these arguments needs (0 when it needs none),
+ * whatever the alignment of the pointers it will get.  The value depends only on
+ * (op, M, N, dt); `device` is accepted for callers that size per device and is
+ * otherwise unused (pass -1).
  */
 size_t rr_workspace_bytes(rr_op op, int64_t M, int64_t N, rr_dtype dt, int device);
 

@@ -159,9 +159,16 @@ rr_status rr_cross_entropy_fwd(const void *logits, const int32_t *labels, float 
 
 size_t rr_workspace_bytes(rr_op op, int64_t M, int64_t N, rr_dtype dt, int device) {
     (void)device;
-    rr::Plan p;
-    if (M <= 0 || rr::make_plan(op, dt, M, N, true, &p) != rr::kPlanOk) return 0;
-    return p.ws_bytes;
+    if (M <= 0) return 0;
+    // The pointers are not known here, so cover both the 128-bit and the
+    // per-element plan (the latter holds fewer values per lane).
+    size_t need = 0;
+    for (int vec = 0; vec < 2; ++vec) {
+        rr::Plan p;
+        if (rr::make_plan(op, dt, M, N, vec != 0, &p) == rr::kPlanOk && p.ws_bytes > need)
+            need = p.ws_bytes;
+    }
+    return need;
 }
 
 rr_status rr_workspace_check(void *ws, size_t ws_bytes, hipStream_t stream) {

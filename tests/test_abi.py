@@ -94,8 +94,8 @@ def test_too_long_rows_are_unsupported():
 @needs_no_gpu
 def test_missing_or_small_workspace():
     N = 131072
-    need = rr.workspace_bytes(rr.RR_OP_SOFTMAX, 64, N, rr.RR_F32)
-    assert need > 0
+    need = rr.rr_plan_query(rr.RR_OP_SOFTMAX, 64, N, rr.RR_F32, True)["ws_bytes"]
+    assert 0 < need <= rr.workspace_bytes(rr.RR_OP_SOFTMAX, 64, N, rr.RR_F32)
     assert rr.softmax_fwd_raw(A, B, 64, N, rr.RR_F32) == rr.RR_ERR_WORKSPACE
     assert rr.softmax_fwd_raw(A, B, 64, N, rr.RR_F32, C, need - 1) == rr.RR_ERR_WORKSPACE
     assert rr.softmax_fwd_raw(A, B, 64, N, rr.RR_F32, C + 4, need) == rr.RR_ERR_WORKSPACE

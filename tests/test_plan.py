@@ -47,7 +47,9 @@ def test_workspace_scales_with_rows_up_to_the_group_cap():
     N = 131072
     small = rr.workspace_bytes(rr.RR_OP_SOFTMAX, 3, N, rr.RR_F32)
     big = rr.workspace_bytes(rr.RR_OP_SOFTMAX, 100000, N, rr.RR_F32)
-    G = rr.rr_plan_query(rr.RR_OP_SOFTMAX, 3, N, rr.RR_F32)["groups_per_row"]
+    # the larger of the 128-bit and the per-element plans
+    G = max(rr.rr_plan_query(rr.RR_OP_SOFTMAX, 3, N, rr.RR_F32, v)["groups_per_row"]
+            for v in (True, False))
     assert small == 256 + 3 * (64 + 32 * G)
     assert big == 256 + 1024 * (64 + 32 * G)
     assert rr.workspace_bytes(rr.RR_OP_SOFTMAX, 0, N, rr.RR_F32) == 0
@@ -91,3 +93,12 @@ def test_invalid_plan_arguments():
         with pytest.raises(rr.RRError) as e:
             rr.rr_plan_query(*args)
         assert e.value.status == rr.RR_ERR_INVALID_ARGUMENT
+
+
+def test_workspace_covers_the_element_path():
+    # N * 4 bytes not a multiple of 16: the per-element plan splits the row further
+    for op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
+        for N in (40000, 65537, 131072):
+            need = rr.workspace_bytes(op, 6, N, rr.RR_F32)
+            for vec in (True, False):
+                assert rr.rr_plan_query(op, 6, N, rr.RR_F32, vec)["ws_bytes"] <= need

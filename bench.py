@@ -9,10 +9,11 @@ than the 256 MB last-level cache.
 
 Printed: one JSON line with
   value      whole-job effective GB/s = algorithmic bytes per step x steps / wall time
-  roofline   the kernel's algorithmic bytes / its mean launch time (HIP events on the
-             launch stream), against the MI355X HBM peak of 8 TB/s, and the HBM bytes
-             the hardware counters measured per launch (null if the kernel sources
-             changed since the counters were taken)
+  roofline   the kernel's algorithmic bytes / its mean time per launch (two HIP events
+             on the launch stream around the timed launches, back to back), against the
+             MI355X HBM peak of 8 TB/s, and the HBM bytes the hardware counters measured
+             per launch (null if the kernel sources changed since the counters were
+             taken)
   cpu_baseline  the double-precision CPU oracle on a bounded sample of the same workload
   copy_ceiling  a 128-bit streaming copy of the same bytes in the same run
 Algorithmic bytes: softmax M*N*(s_in + s_out); RMSNorm M*N*(s_in + s_out) + N*s;
@@ -159,25 +160,25 @@ class Runner:
         return self.rr.stream_copy_raw(src.data_ptr(), dst.data_ptr(), nbytes, self.sp)
 
     def time(self, fn, steps: int, warmup: int):
-        """Wall time of `steps` launches and the mean per-launch time from events."""
+        """Wall time of `steps` back-to-back launches, and the mean time per launch
+        from a pair of HIP events on the launch stream around the same region."""
         torch = self.torch
         with torch.cuda.stream(self.stream):
             for k in range(warmup):
                 st = fn(k)
                 if st != 0:
                     raise RuntimeError(f"launch failed: {self.rr.status_string(st)}")
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(steps)]
+            start = torch.cuda.Event(enable_timing=True)
+            end = torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
+            start.record(self.stream)
             for k in range(steps):
-                ev[k][0].record(self.stream)
                 fn(warmup + k)
-                ev[k][1].record(self.stream)
+            end.record(self.stream)
             torch.cuda.synchronize()
             t1 = time.perf_counter()
-        per_launch = [a.elapsed_time(b) for a, b in ev]
-        return t1 - t0, sum(per_launch) / len(per_launch), min(per_launch)
+        return t1 - t0, start.elapsed_time(end) / steps
 
 
 def cpu_baseline(w, seconds: float):
@@ -218,8 +219,8 @@ def measure(w, steps: int, warmup: int, min_rotation_bytes: float, with_cpu: boo
             cpu_seconds: float, host_rows=None):
     r = Runner(w, min_rotation_bytes, host_rows=host_rows)
     nbytes = algorithmic_bytes(w)
-    wall, mean_ms, min_ms = r.time(r.launch, steps, warmup)
-    copy_wall, copy_mean_ms, _ = r.time(r.copy_launch, steps, warmup)
+    wall, mean_ms = r.time(r.launch, steps, warmup)
+    copy_wall, copy_mean_ms = r.time(r.copy_launch, steps, warmup)
     copy_bytes = 2 * r.x[0].numel() * r.x[0].element_size()
     achieved = nbytes / (mean_ms * 1e-3) / 1e9
     traffic, rec = traffic_for(w.name)
@@ -244,7 +245,7 @@ def measure(w, steps: int, warmup: int, min_rotation_bytes: float, with_cpu: boo
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "launch_ms_mean": round(mean_ms, 5),
-                     "launch_ms_min": round(min_ms, 5), "algorithmic_bytes": nbytes},
+                     "algorithmic_bytes": nbytes},
         "copy_ceiling": {"value": round(copy_gbps, 2), "unit": "GB/s",
                          "frac": round(copy_gbps / HBM_PEAK_GBPS, 4),
                          "kernel_vs_copy": round(achieved / copy_gbps, 4)},

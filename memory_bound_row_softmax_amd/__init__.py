@@ -14,7 +14,9 @@ import os
 import threading
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "librr.so")
+# RR_LIBRARY may name another build of the same sources (tuning runs compare
+# builds with different compile-time options); by default the in-tree library.
+LIB_PATH = os.environ.get("RR_LIBRARY") or os.path.join(_HERE, "librr.so")
 
 RR_OK = 0
 RR_ERR_INVALID_ARGUMENT = 1

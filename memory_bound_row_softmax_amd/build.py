@@ -42,9 +42,9 @@ def _flags():
             "-Wall", "-Wno-unused-command-line-argument"]
 
 
-def _compile(src: str) -> tuple[str, str]:
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [hipcc(), *_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> tuple[str, str]:
+    obj = os.path.join(build_dir, src + ".o")
+    cmd = [hipcc(), *_flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".hip"):
         cmd.append("-Rpass-analysis=kernel-resource-usage")
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -67,17 +67,20 @@ def _resources(remarks: str) -> list[dict]:
     return rows
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link ``librr.so``; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, extra_flags=()) -> str:
+    """Compile every source and link the library (``librr.so`` next to this file
+    unless `out` names another path, e.g. a variant built with `extra_flags`
+    such as -DRR_STREAM_STORE_POLICY=2 for a tuning run); returns its path."""
+    build_dir = BUILD if out == LIB else out + ".build"
+    os.makedirs(build_dir, exist_ok=True)
     jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4)), 16))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(lambda s: _compile(s, build_dir, tuple(extra_flags)), SOURCES))
     objs = [o for o, _ in results]
     kernels = []
     for _, remarks in results:
         kernels.extend(_resources(remarks))
-    with open(os.path.join(BUILD, "resources.txt"), "w") as f:
+    with open(os.path.join(build_dir, "resources.txt"), "w") as f:
         f.write("kernel\tVGPRs\tAGPRs\tSGPRs\tSGPRspill\tScratchSize\tOccupancy\tLDS\n")
         for k in kernels:
             f.write("\t".join([k["name"], k.get("VGPRs", "?"), k.get("AGPRs", "?"),
@@ -90,15 +93,15 @@ def build(verbose: bool = False) -> str:
               or int(k.get("VGPRs Spill", "0")) > 0]
     if spills:
         raise RuntimeError(f"{len(spills)} kernels spill to scratch memory, e.g. {spills[:3]}")
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     res = subprocess.run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs],
                          capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr[-4000:]}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {LIB} ({len(kernels)} kernels, none spilling)")
-    return LIB
+        print(f"built {out} ({len(kernels)} kernels, none spilling)")
+    return out
 
 
 if __name__ == "__main__":

@@ -16,15 +16,28 @@
 #include "plan.hpp"
 
 #include <cstdlib>
+#include <cstring>
 
 #include "configs.hpp"
 
 namespace rr {
 
-bool row_config_exists(int P, int R, int G) {
-#define RR_X(p, r, g) \
-    if (P == p && R == r && G == g) return true;
-    RR_ROW_CONFIGS(RR_X)
+static int cfg_op(int op) { return op == kOpSoftmax ? kCfgSoftmax : kCfgRmsnorm; }
+static int elem_bytes(int dtype) { return dtype == kBf16 ? 2 : 4; }
+
+bool block_config_ok(int op, int dtype, bool vec, int P, int R) {
+#define RR_X(p, r) \
+    if (P == p && R == r) return block_config_enabled(cfg_op(op), elem_bytes(dtype), vec, p, r);
+    RR_BLOCK_CONFIGS(RR_X)
+#undef RR_X
+    return false;
+}
+
+bool stream_config_ok(int op, int dtype, bool vec, int P, int R, int G) {
+#define RR_X(p, r, g)                    \
+    if (P == p && R == r && G == g)      \
+        return stream_config_enabled(cfg_op(op), elem_bytes(dtype), vec, p, r, g);
+    RR_STREAM_CONFIGS(RR_X)
 #undef RR_X
     return false;
 }
@@ -60,41 +73,82 @@ static void fill_geometry(Plan *p) {
     p->rows_per_block = rows_per_block_for(p->R);
 }
 
-// Default row-resident choice: the fewest workgroups per row, then the preferred
-// number of values per lane (more values per lane = more 128-bit loads in flight
-// per lane; small rows prefer fewer so that one row still spans many lanes),
-// then the narrowest lane group that holds the row.
-static bool default_row(int op, int dtype, bool vec, int64_t N, int *P, int *R, int *G) {
-    static const int kPrefSmall[3] = {16, 32, 64};
-    static const int kPrefMid[3] = {32, 64, 16};
-    static const int kPrefLarge[3] = {64, 32, 16};
-    const int *pref = N <= 1024 ? kPrefSmall : (N <= 2048 ? kPrefMid : kPrefLarge);
-    const int cfg_op = op == kOpSoftmax ? kCfgSoftmax : kCfgRmsnorm;
-    const int ebytes = dtype == kBf16 ? 2 : 4;
-    for (int g = 1; g <= 16; g *= 2) {
-        for (int k = 0; k < 3; ++k) {
-            const int p = pref[k];
-            int64_t r = next_pow2((N + (int64_t)p * g - 1) / ((int64_t)p * g));
-            if (r < 16) r = 16;
-            if (g > 1 && r < 256) r = 256;
-            if (r > 1024) continue;
-            if (!row_config_exists(p, (int)r, g) ||
-                !row_config_enabled(cfg_op, ebytes, vec, p, (int)r, g))
-                continue;
-            *P = p;
-            *R = (int)r;
-            *G = g;
-            return true;
-        }
+// Default row-resident choice: a table of the fastest configuration measured on
+// MI355X for each op, dtype and power-of-four N (16384 rows, every compiled
+// configuration timed, cold HBM reads), applied to the smallest tabulated N
+// that is >= the call's N, then narrowed to the fewest lanes (block) or
+// workgroups (stream) that still hold the row.  Patterns behind the numbers:
+// short rows prefer two 16-byte chunks per lane and many lanes (more waves,
+// fewer loads in flight per wave); long rows prefer the persistent stream
+// kernels, whose second register buffer keeps the next row's loads in flight
+// while a row is reduced, with as few workgroups per row as fit (each extra one
+// joins the exchange).  Differences between the top few configurations are a
+// few percent.
+struct Choice {
+    bool stream;
+    int P, R, G;
+};
+constexpr int kTunedN[8] = {256, 1024, 4096, 16384, 32768, 65536, 131072, 262144};
+//                      [op: softmax, rmsnorm][dtype: f32, bf16][N bucket]
+static const Choice kTuned[2][2][8] = {
+    {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {true, 64, 512, 1},
+      {true, 16, 1024, 2}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8}},
+     {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 16, 256, 1}, {false, 64, 256, 1},
+      {true, 32, 1024, 1}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8}}},
+    {{{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 16, 1024, 1},
+      {true, 16, 1024, 2}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 64, 512, 8}},
+     {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {true, 32, 1024, 1},
+      {false, 64, 512, 1}, {true, 32, 1024, 2}, {true, 64, 512, 4}, {true, 64, 512, 8}}},
+};
+
+static bool try_choice(int op, int dtype, bool vec, int64_t N, Choice c, Plan *p) {
+    if (c.stream) {
+        while (c.G > 1 && (int64_t)c.P * c.R * (c.G / 2) >= N) c.G /= 2;
+        if ((int64_t)c.P * c.R * c.G < N || !stream_config_ok(op, dtype, vec, c.P, c.R, c.G))
+            return false;
+    } else {
+        const int64_t r = next_pow2((N + c.P - 1) / c.P);
+        c.R = r < 16 ? 16 : (int)(r > 4096 ? 4096 : r);
+        if (c.R > 1024 || !block_config_ok(op, dtype, vec, c.P, c.R)) return false;
     }
+    p->stream = c.stream;
+    p->P = c.P;
+    p->R = c.R;
+    p->G = c.G;
+    return true;
+}
+
+static bool default_row(int op, int dtype, bool vec, int64_t N, Plan *p) {
+    const int o = op == kOpSoftmax ? 0 : 1, d = dtype == kBf16 ? 1 : 0;
+    int k = 0;
+    while (k < 7 && kTunedN[k] < N) ++k;
+    if (N <= kTunedN[7]) {
+        Choice c = kTuned[o][d][k];
+        // A stream workgroup that would be less than half full: the block
+        // choice of the bucket below, widened to the row.
+        if (c.stream && k > 0 && 2 * N < (int64_t)c.P * c.R) c = kTuned[o][d][k - 1];
+        if (try_choice(op, dtype, vec, N, c, p)) return true;
+    }
+    // Past the table, or a configuration the per-element path does not have:
+    // the first stream configuration that holds the row with the fewest workgroups.
+    static const int kStreamPR[4][2] = {{64, 512}, {32, 1024}, {64, 256}, {16, 1024}};
+    for (int g = 1; g <= 16; g *= 2)
+        for (int j = 0; j < 4; ++j)
+            if (try_choice(op, dtype, vec, N, Choice{true, kStreamPR[j][0], kStreamPR[j][1], g}, p))
+                return true;
     return false;
 }
 
-static void default_xent(int64_t N, int *P, int *R) {
+// Cross-entropy: 16 values per lane for short rows, else 32; as many lanes as the
+// row needs, up to 256 lanes (512 for bf16 rows of 32768 or more, which then
+// still take two or more steps): 32 KiB of the row per step, which measured best
+// for long rows.
+static void default_xent(int dtype, int64_t N, int *P, int *R) {
     *P = N <= 512 ? 16 : 32;
     int64_t r = next_pow2((N + *P - 1) / *P);
+    const int64_t rmax = (dtype == kBf16 && N >= 32768) ? 512 : 256;
     if (r < 16) r = 16;
-    if (r > 256) r = 256;
+    if (r > rmax) r = rmax;
     *R = (int)r;
 }
 
@@ -111,11 +165,11 @@ PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *ou
     if (op == kOpXent) {
         if (N > INT32_MAX) return kPlanInvalid;
         int P, R;
-        default_xent(N, &P, &R);
+        default_xent(dtype, N, &P, &R);
         if (fP) P = fP;
         if (fR) R = fR;
         if (!xent_config_exists(P, R)) return kPlanUnsupported;
-        p.path = kPathStream;
+        p.path = kPathXent;
         p.P = P;
         p.R = R;
         p.G = 1;
@@ -126,26 +180,31 @@ PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *ou
         return kPlanOk;
     }
 
-    int P = 0, R = 0, G = 1;
-    if (fP || fR || fG) {
-        P = fP ? fP : 64;
-        R = fR ? fR : 1024;
-        G = fG ? fG : 1;
-    } else if (!default_row(op, dtype, vec, N, &P, &R, &G)) {
+    const char *kind = std::getenv("RR_FORCE_KIND");
+    const bool force_stream = kind && std::strcmp(kind, "stream") == 0;
+    const bool force_block = kind && std::strcmp(kind, "block") == 0;
+    if (fP || fR || fG || force_stream || force_block) {
+        p.stream = force_stream || (!force_block && fG > 1);
+        p.P = fP ? fP : (p.stream ? 64 : 16);
+        p.R = fR ? fR : (p.stream ? 512 : 256);
+        p.G = fG ? fG : 1;
+        const bool ok = p.stream ? stream_config_ok(op, dtype, vec, p.P, p.R, p.G)
+                                 : (p.G == 1 && block_config_ok(op, dtype, vec, p.P, p.R));
+        if (!ok) return kPlanUnsupported;
+    } else if (!default_row(op, dtype, vec, N, &p)) {
         return kPlanUnsupported;
     }
-    const int cfg_op = op == kOpSoftmax ? kCfgSoftmax : kCfgRmsnorm;
-    if (!row_config_exists(P, R, G) ||
-        !row_config_enabled(cfg_op, dtype == kBf16 ? 2 : 4, vec, P, R, G))
-        return kPlanUnsupported;
-    p.P = P;
-    p.R = R;
-    p.G = G;
+    const int P = p.P, R = p.R, G = p.G;
     p.max_n = (int64_t)P * R * G;
     if (N > p.max_n) return kPlanUnsupported;
-    p.path = G > 1 ? kPathGrid : kPathRow;
+    p.path = !p.stream ? kPathRow : (G > 1 ? kPathSplit : kPathStream);
     p.ws_bytes = G > 1 ? grid_ws_bytes(G, M) : 0;
-    fill_geometry(&p);
+    if (p.stream) {
+        p.block = R;
+        p.rows_per_block = 1;
+    } else {
+        fill_geometry(&p);
+    }
     *out = p;
     return kPlanOk;
 }

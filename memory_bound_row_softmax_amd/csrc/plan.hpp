@@ -7,13 +7,16 @@
 
 namespace rr {
 
-enum PathKind { kPathRow = 0, kPathGrid = 1, kPathStream = 2 };
+// kPathRow: block kernel; kPathSplit: stream kernel with G > 1 (split rows);
+// kPathXent: cross-entropy; kPathStream: stream kernel with G = 1.
+enum PathKind { kPathRow = 0, kPathSplit = 1, kPathXent = 2, kPathStream = 3 };
 enum OpKind { kOpSoftmax = 0, kOpRmsnorm = 1, kOpXent = 2 };
 enum DtypeKind { kF32 = 0, kBf16 = 1 };
 enum PlanResult { kPlanOk = 0, kPlanUnsupported = 1, kPlanInvalid = 2 };
 
 struct Plan {
     int path = kPathRow;
+    bool stream = false;  // persistent, double-buffered stream kernel
     bool vec = true;
     int P = 0, R = 0, G = 1;
     int block = 0, rows_per_block = 0;
@@ -21,14 +24,16 @@ struct Plan {
     size_t ws_bytes = 0;
 };
 
-// Whether (P, R, G) is in the compiled row menu / (P, R) in the streaming menu.
-bool row_config_exists(int P, int R, int G);
+// Whether a configuration is compiled (and usable) for (op, dtype, vec).
+bool block_config_ok(int op, int dtype, bool vec, int P, int R);
+bool stream_config_ok(int op, int dtype, bool vec, int P, int R, int G);
 bool xent_config_exists(int P, int R);
 
 // Chooses the plan.  `vec` says whether the 128-bit path is usable for these
-// pointers.  Test-only overrides come from the environment: RR_FORCE_P,
-// RR_FORCE_R and RR_FORCE_G (row ops) or RR_FORCE_P and RR_FORCE_R (cross-entropy);
-// a forced configuration that is not compiled, or too small for N, is unsupported.
+// pointers.  Test-only overrides come from the environment: RR_FORCE_KIND
+// ("block" or "stream"), RR_FORCE_P, RR_FORCE_R and RR_FORCE_G (row ops), or
+// RR_FORCE_P and RR_FORCE_R (cross-entropy); a forced configuration that is not
+// compiled, or too small for N, is unsupported.
 PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *out);
 
 // Workspace bytes of the grid path for G workgroups per row and M rows.

@@ -49,6 +49,17 @@ __device__ __forceinline__ float tree_reduce(const float *v, Op op) {
     }
 }
 
+// Balanced pairwise sum of v[i]^2 (squares formed at the leaves).
+template <int N>
+__device__ __forceinline__ float tree_sum_squares(const float *v) {
+    if constexpr (N == 1) {
+        return v[0] * v[0];
+    } else {
+        constexpr int H = N / 2;
+        return tree_sum_squares<H>(v) + tree_sum_squares<N - H>(v + H);
+    }
+}
+
 // ---- cross-lane moves -------------------------------------------------------
 
 template <int CTRL>

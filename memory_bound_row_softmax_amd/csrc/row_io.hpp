@@ -32,14 +32,15 @@ __device__ __forceinline__ bool part_full(int chunk0, int N) {
     return (int64_t)(chunk0 + C * R) * E::VPC <= (int64_t)N;
 }
 
-template <class E, int C, int R, bool VEC>
+// POLICY: kStreamLoad for data read once, kReuseLoad for data read by every row.
+template <class E, int C, int R, bool VEC, int POLICY = kStreamLoad>
 __device__ __forceinline__ void load_part(RowView rv, int chunk0, int l, float *v) {
     constexpr int VPC = E::VPC;
     if constexpr (VEC) {
         u32x4 raw[C];
 #pragma unroll
         for (int i = 0; i < C; ++i)
-            raw[i] = buf_load16(rv.buf, rv.base + (uint32_t)(chunk0 + i * R + l) * 16u);
+            raw[i] = buf_load16<POLICY>(rv.buf, rv.base + (uint32_t)(chunk0 + i * R + l) * 16u);
 #pragma unroll
         for (int i = 0; i < C; ++i) decode<E>(raw[i], v + i * VPC);
     } else {
@@ -48,7 +49,7 @@ __device__ __forceinline__ void load_part(RowView rv, int chunk0, int l, float *
 #pragma unroll
             for (int e = 0; e < VPC; ++e) {
                 const uint32_t idx = (uint32_t)(chunk0 + i * R + l) * VPC + e;
-                v[i * VPC + e] = buf_load_elem<E>(rv.buf, rv.base + idx * E::BYTES);
+                v[i * VPC + e] = buf_load_elem<E, POLICY>(rv.buf, rv.base + idx * E::BYTES);
             }
         }
     }

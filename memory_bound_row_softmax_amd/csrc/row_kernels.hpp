@@ -7,13 +7,13 @@
 // global load costs a third of the effective bandwidth).  RMSNorm reuses the same
 // layout, load/store and reduction helpers (section 总结).
 //
-// One kernel template per op, parameterised by
-//   E  element type (F32 / BF16),  P  fp32 values per lane,  R  lanes per row,
-//   G  workgroups per row,  VEC  128-bit path or per-element path.
-// With G == 1 each workgroup handles rows_per_block_for(R) rows, one per lane
-// group, and the grid has one workgroup per such set of rows.  With G > 1 the
-// grid is cooperative and persistent: each row group of G workgroups loops over
-// rows group, group + groups, ... and meets its peers in the workspace.
+// Template parameters: E element type (F32 / BF16), P fp32 values per lane per
+// row, R lanes per row, G workgroups per row, VEC 128-bit path or per-element
+// path.  Two kernel kinds per op (see configs.hpp): block kernels (G = 1, one
+// workgroup per few rows) and stream kernels (persistent, one row per workgroup
+// at a time, the next row's loads issued before the current row is reduced;
+// with G > 1 the grid is cooperative and the G workgroups of a row meet in the
+// workspace).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -37,9 +37,9 @@ __device__ __forceinline__ int lane_group() {
     return t;
 }
 
-// The row of lane group `sub` of this block (G == 1).  Rows past M are clamped
-// (R >= 64) or lie past the end of the block's buffer (R < 64); either way they
-// are only read, never written.
+// The row of lane group `sub` of this block (block kernels).  Rows past M are
+// clamped (R >= 64) or lie past the end of the block's buffer (R < 64); either
+// way they are only read, never written.
 template <int R>
 __device__ __forceinline__ RowView block_row_view(const char *base, int64_t M, int sub,
                                                   uint32_t row_bytes) {
@@ -56,16 +56,24 @@ __device__ __forceinline__ RowView block_row_view(const char *base, int64_t M, i
     }
 }
 
+// Row `row` of a stream kernel; past the last row the buffer is empty, so its
+// loads return 0 without touching memory.
+__device__ __forceinline__ RowView stream_row_view(const char *base, int64_t row, int64_t M,
+                                                   uint32_t row_bytes) {
+    const bool ok = row < M;
+    return {make_buf(base + (ok ? row : 0) * row_bytes, ok ? row_bytes : 0u), 0u};
+}
+
 // Everything a row body needs besides the row buffers.
 struct RowCtx {
     int N;
     int l;          // lane within the row's lane group
     int member;     // workgroup index within the row (0 when G == 1)
-    int it;         // row iteration of this workgroup (grid path)
+    int it;         // row iteration of this workgroup (stream kernels)
     bool full;      // this lane group's part of the row has no padding
     float *red_a;   // LDS slots of this row, first reduction
     float *red_b;   // LDS slots of this row, second reduction
-    float *bcast;   // LDS: merged grid partials [0..1], "a wait timed out" flag [2]
+    float *bcast;   // LDS: merged split-row partials [0..1], "a wait timed out" flag [2]
     GroupRef g;
     int spin_limit;
 };
@@ -80,12 +88,11 @@ struct MergeMaxSum {
     }
 };
 
+// Passes 1-3 on a lane's loaded part v of the row, then the store.
 template <class E, int P, int R, int G, bool VEC>
-__device__ __forceinline__ void softmax_row(RowView xv, RowView yv, bool valid, RowCtx &c) {
+__device__ __forceinline__ void softmax_finish(float *v, RowView yv, bool valid, RowCtx &c) {
     constexpr int C = P / E::VPC;
     const int chunk0 = c.member * C * R;
-    float v[P];
-    load_part<E, C, R, VEC>(xv, chunk0, c.l, v);
     if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.N, -INFINITY, v);
 
     // pass 1: row max
@@ -113,38 +120,62 @@ __device__ __forceinline__ void softmax_row(RowView xv, RowView yv, bool valid, 
     store_part<E, C, R, VEC>(yv, chunk0, c.l, c.N, valid, c.full, v);
 }
 
-template <class E, int P, int R, int G, bool VEC>
+template <class E, int P, int R, bool VEC>
 __global__ void __launch_bounds__(block_threads_for(R))
-    softmax_kernel(const char *x, char *y, int64_t M, int N, uint8_t *ws, int groups,
-                   int spin_limit) {
+    softmax_block_kernel(const char *x, char *y, int64_t M, int N) {
     constexpr int C = P / E::VPC;
     constexpr int RPB = rows_per_block_for(R);
     constexpr int W = R > 64 ? R / 64 : 1;
     __shared__ float red_max[RPB * W];
     __shared__ float red_sum[RPB * W];
-    __shared__ float bcast[3];
     const int sub = lane_group<R>();
     const uint32_t row_bytes = (uint32_t)N * E::BYTES;
-    RowCtx c{N, (int)(threadIdx.x % R), 0, 0, true, red_max + sub * W, red_sum + sub * W, bcast,
-             GroupRef{}, spin_limit};
+    RowCtx c{N, (int)(threadIdx.x % R), 0, 0, part_full<E, C, R>(0, N), red_max + sub * W,
+             red_sum + sub * W, nullptr, GroupRef{}, 0};
+    const bool valid = (int64_t)blockIdx.x * RPB + sub < M;
+    float v[P];
+    load_part<E, C, R, VEC>(block_row_view<R>(x, M, sub, row_bytes), 0, c.l, v);
+    softmax_finish<E, P, R, 1, VEC>(v, block_row_view<R>(y, M, sub, row_bytes), valid, c);
+}
 
-    if constexpr (G == 1) {
-        c.full = part_full<E, C, R>(0, N);
-        const bool valid = (int64_t)blockIdx.x * RPB + sub < M;
-        softmax_row<E, P, R, 1, VEC>(block_row_view<R>(x, M, sub, row_bytes),
-                                     block_row_view<R>(y, M, sub, row_bytes), valid, c);
-    } else {
-        static_assert(RPB == 1, "split rows use one row per workgroup");
-        int group;
+template <class E, int P, int R, int G, bool VEC>
+__global__ void __launch_bounds__(R)
+    softmax_stream_kernel(const char *x, char *y, int64_t M, int N, uint8_t *ws, int groups,
+                          int spin_limit) {
+    static_assert(R >= 64, "one row per workgroup");
+    constexpr int C = P / E::VPC;
+    constexpr int W = R / 64;
+    __shared__ float red_max[W];
+    __shared__ float red_sum[W];
+    __shared__ float bcast[3];
+    RowCtx c{N, (int)threadIdx.x, 0, 0, true, red_max, red_sum, bcast, GroupRef{}, spin_limit};
+    int group = blockIdx.x;
+    if constexpr (G > 1) {
         group_of_block<G>(groups, &group, &c.member);
         c.g = group_ref<G>(ws, group);
-        c.full = part_full<E, C, R>(c.member * C * R, N);
-        if (threadIdx.x == 0) bcast[2] = 0.0f;  // ordered before its first read by two barriers
-        for (int64_t row = group; row < M; row += groups, ++c.it) {
-            const RowView xv{make_buf(x + row * row_bytes, row_bytes), 0u};
-            const RowView yv{make_buf(y + row * row_bytes, row_bytes), 0u};
-            softmax_row<E, P, R, G, VEC>(xv, yv, true, c);
-        }
+        if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
+    }
+    const int chunk0 = c.member * C * R;
+    c.full = part_full<E, C, R>(chunk0, N);
+    const uint32_t rb = (uint32_t)N * E::BYTES;
+
+    // Two register buffers: the loads of the next row are in flight while the
+    // current row is reduced, exchanged and written.
+    float a[P], b[P];
+    int64_t row = group;
+    load_part<E, C, R, VEC>(stream_row_view(x, row, M, rb), chunk0, c.l, a);
+    while (row < M) {
+        load_part<E, C, R, VEC>(stream_row_view(x, row + groups, M, rb), chunk0, c.l, b);
+        softmax_finish<E, P, R, G, VEC>(a, stream_row_view(y, row, M, rb), true, c);
+        ++c.it;
+        row += groups;
+        if (row >= M) break;
+        load_part<E, C, R, VEC>(stream_row_view(x, row + groups, M, rb), chunk0, c.l, a);
+        softmax_finish<E, P, R, G, VEC>(b, stream_row_view(y, row, M, rb), true, c);
+        ++c.it;
+        row += groups;
+    }
+    if constexpr (G > 1) {
         if (c.it > 0) depart_group<G>(c.g);
     }
 }
@@ -158,25 +189,44 @@ struct MergeSum {
     }
 };
 
-template <class E, int P, int R, int G, bool VEC>
-__device__ __forceinline__ void rmsnorm_row(RowView xv, RowView wview, RowView yv,
-                                            float *rstd_out, float eps, bool valid,
-                                            RowCtx &c) {
+// Weight source of the block kernels: the lane's part of w, already in registers.
+template <int P>
+struct WeightRegs {
+    const float *w;
+    __device__ __forceinline__ void apply(float *v, int) const {
+#pragma unroll
+        for (int j = 0; j < P; ++j) v[j] *= w[j];
+    }
+};
+
+// Weight source of the stream kernels: the workgroup's slice of w, decoded to
+// fp32 in LDS once per launch.  Lane l keeps its values j = 4q..4q+3 at
+// slot[q * R + l], so the 16-byte LDS reads of a wave are contiguous.
+template <int P, int R>
+struct WeightLds {
+    const float4 *slot;
+    __device__ __forceinline__ void apply(float *v, int l) const {
+#pragma unroll
+        for (int q = 0; q < P / 4; ++q) {
+            const float4 w4 = slot[q * R + l];
+            v[4 * q] *= w4.x;
+            v[4 * q + 1] *= w4.y;
+            v[4 * q + 2] *= w4.z;
+            v[4 * q + 3] *= w4.w;
+        }
+    }
+};
+
+template <class E, int P, int R, int G, bool VEC, class Weight>
+__device__ __forceinline__ void rmsnorm_finish(float *v, const Weight &w, RowView yv,
+                                               float *rstd_out, float eps, bool valid, RowCtx &c) {
     constexpr int C = P / E::VPC;
     const int chunk0 = c.member * C * R;
-    float v[P];
-    load_part<E, C, R, VEC>(xv, chunk0, c.l, v);
-    float wv[P];
-    load_part<E, C, R, VEC>(wview, chunk0, c.l, wv);
     if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.N, 0.0f, v);
 
     // sum of squares, then t = x * w in place; y = t * r once r is known
-    float sq[P];
-#pragma unroll
-    for (int j = 0; j < P; ++j) sq[j] = v[j] * v[j];
-    float q = tree_reduce<P>(sq, OpSum{});
-#pragma unroll
-    for (int j = 0; j < P; ++j) v[j] *= wv[j];
+    float q = tree_sum_squares<P>(v);
+    w.apply(v, c.l);
     q = row_reduce<R>(q, c.red_a, c.l, OpSum{});
     if constexpr (G > 1) {
         exchange_pairs<G>(c.g, c.member, c.it, q, 0.0f, c.spin_limit, c.bcast, MergeSum{});
@@ -189,42 +239,77 @@ __device__ __forceinline__ void rmsnorm_row(RowView xv, RowView wview, RowView y
     if (rstd_out && valid && c.l == 0 && c.member == 0) *rstd_out = r;
 }
 
-template <class E, int P, int R, int G, bool VEC>
+template <class E, int P, int R, bool VEC>
 __global__ void __launch_bounds__(block_threads_for(R))
-    rmsnorm_kernel(const char *x, const char *w, char *y, float *rstd, int64_t M, int N,
-                   float eps, uint8_t *ws, int groups, int spin_limit) {
+    rmsnorm_block_kernel(const char *x, const char *w, char *y, float *rstd, int64_t M, int N,
+                         float eps) {
     constexpr int C = P / E::VPC;
     constexpr int RPB = rows_per_block_for(R);
     constexpr int W = R > 64 ? R / 64 : 1;
     __shared__ float red[RPB * W];
-    __shared__ float bcast[3];
     const int sub = lane_group<R>();
     const uint32_t row_bytes = (uint32_t)N * E::BYTES;
-    const RowView wview{make_buf(w, row_bytes), 0u};
-    RowCtx c{N, (int)(threadIdx.x % R), 0, 0, true, red + sub * W, nullptr, bcast, GroupRef{},
-             spin_limit};
+    RowCtx c{N, (int)(threadIdx.x % R), 0, 0, part_full<E, C, R>(0, N), red + sub * W, nullptr,
+             nullptr, GroupRef{}, 0};
+    const int64_t row = (int64_t)blockIdx.x * RPB + sub;
+    const bool valid = row < M;
+    float v[P];
+    load_part<E, C, R, VEC>(block_row_view<R>(x, M, sub, row_bytes), 0, c.l, v);
+    float wv[P];
+    load_part<E, C, R, VEC, kReuseLoad>(RowView{make_buf(w, row_bytes), 0u}, 0, c.l, wv);
+    rmsnorm_finish<E, P, R, 1, VEC>(v, WeightRegs<P>{wv}, block_row_view<R>(y, M, sub, row_bytes),
+                                    rstd ? rstd + row : nullptr, eps, valid, c);
+}
 
-    if constexpr (G == 1) {
-        c.full = part_full<E, C, R>(0, N);
-        const int64_t row = (int64_t)blockIdx.x * RPB + sub;
-        const bool valid = row < M;
-        rmsnorm_row<E, P, R, 1, VEC>(block_row_view<R>(x, M, sub, row_bytes), wview,
-                                     block_row_view<R>(y, M, sub, row_bytes),
-                                     rstd ? rstd + row : nullptr, eps, valid, c);
-    } else {
-        static_assert(RPB == 1, "split rows use one row per workgroup");
-        int group;
+template <class E, int P, int R, int G, bool VEC>
+__global__ void __launch_bounds__(R)
+    rmsnorm_stream_kernel(const char *x, const char *w, char *y, float *rstd, int64_t M, int N,
+                          float eps, uint8_t *ws, int groups, int spin_limit) {
+    static_assert(R >= 64, "one row per workgroup");
+    constexpr int C = P / E::VPC;
+    constexpr int W = R / 64;
+    __shared__ float red[W];
+    __shared__ float bcast[3];
+    __shared__ float4 wslot[(P / 4) * R];
+    RowCtx c{N, (int)threadIdx.x, 0, 0, true, red, nullptr, bcast, GroupRef{}, spin_limit};
+    int group = blockIdx.x;
+    if constexpr (G > 1) {
         group_of_block<G>(groups, &group, &c.member);
         c.g = group_ref<G>(ws, group);
-        c.full = part_full<E, C, R>(c.member * C * R, N);
-        if (threadIdx.x == 0) bcast[2] = 0.0f;  // ordered before its first read by a barrier
-        // `red` and `bcast` are rewritten every row; each write comes after a
-        // barrier that all readers of the previous row have passed.
-        for (int64_t row = group; row < M; row += groups, ++c.it) {
-            const RowView xv{make_buf(x + row * row_bytes, row_bytes), 0u};
-            const RowView yv{make_buf(y + row * row_bytes, row_bytes), 0u};
-            rmsnorm_row<E, P, R, G, VEC>(xv, wview, yv, rstd ? rstd + row : nullptr, eps, true, c);
-        }
+        if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
+    }
+    const int chunk0 = c.member * C * R;
+    c.full = part_full<E, C, R>(chunk0, N);
+    const uint32_t rb = (uint32_t)N * E::BYTES;
+
+    // This workgroup's slice of w, once; each lane later reads back only the
+    // slots it wrote, so no barrier is needed.
+    {
+        float t[P];
+        load_part<E, C, R, VEC, kReuseLoad>(RowView{make_buf(w, rb), 0u}, chunk0, c.l, t);
+#pragma unroll
+        for (int q = 0; q < P / 4; ++q)
+            wslot[q * R + c.l] = make_float4(t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]);
+    }
+    const WeightLds<P, R> wsrc{wslot};
+
+    float a[P], b[P];
+    int64_t row = group;
+    load_part<E, C, R, VEC>(stream_row_view(x, row, M, rb), chunk0, c.l, a);
+    while (row < M) {
+        load_part<E, C, R, VEC>(stream_row_view(x, row + groups, M, rb), chunk0, c.l, b);
+        rmsnorm_finish<E, P, R, G, VEC>(a, wsrc, stream_row_view(y, row, M, rb),
+                                        rstd ? rstd + row : nullptr, eps, true, c);
+        ++c.it;
+        row += groups;
+        if (row >= M) break;
+        load_part<E, C, R, VEC>(stream_row_view(x, row + groups, M, rb), chunk0, c.l, a);
+        rmsnorm_finish<E, P, R, G, VEC>(b, wsrc, stream_row_view(y, row, M, rb),
+                                        rstd ? rstd + row : nullptr, eps, true, c);
+        ++c.it;
+        row += groups;
+    }
+    if constexpr (G > 1) {
         if (c.it > 0) depart_group<G>(c.g);
     }
 }

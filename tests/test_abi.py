@@ -87,8 +87,8 @@ def test_invalid_arguments_are_rejected(case):
 
 @needs_no_gpu
 def test_too_long_rows_are_unsupported():
-    # one row held on chip holds at most 16 workgroups x 1024 lanes x 64 values
-    assert rr.softmax_fwd_raw(A, B, 2, (1 << 20) + 4, rr.RR_F32) == rr.RR_ERR_UNSUPPORTED
+    # one row held on chip holds at most 16 workgroups x 512 lanes x 64 values
+    assert rr.softmax_fwd_raw(A, B, 2, (1 << 19) + 4, rr.RR_F32) == rr.RR_ERR_UNSUPPORTED
 
 
 @needs_no_gpu

@@ -63,28 +63,37 @@ def test_cross_entropy(M, N, dtype):
 
 # ------------------------------------------------------------- forced paths
 
-FORCED_ROW = [  # (P, R, G, M, N): split rows at small N, empty / partial member slices
-    (64, 256, 2, 300, 20000), (64, 256, 4, 300, 3000), (32, 256, 16, 97, 70000),
-    (64, 512, 2, 50, 65536), (32, 1024, 2, 40, 65536), (64, 1024, 16, 9, 1000000),
-    (16, 16, 1, 100, 256), (32, 128, 1, 31, 4000), (16, 1024, 1, 5, 16384)]
+FORCED_ROW = [  # (kind, P, R, G, M, N): split rows at small N, empty / partial member
+    # slices, many rows per persistent workgroup, block kernels off their default sizes
+    ("stream", 64, 256, 2, 300, 20000), ("stream", 64, 256, 4, 300, 3000),
+    ("stream", 32, 512, 16, 97, 70000), ("stream", 64, 512, 2, 50, 65536),
+    ("stream", 32, 1024, 2, 40, 65536), ("stream", 64, 512, 16, 9, 500000),
+    ("stream", 16, 1024, 1, 700, 16000), ("stream", 64, 256, 1, 1000, 5000),
+    ("stream", 32, 512, 1, 3, 16384), ("stream", 16, 1024, 8, 200, 100000),
+    ("block", 16, 16, 1, 100, 256), ("block", 32, 128, 1, 31, 4000),
+    ("block", 16, 1024, 1, 5, 16384), ("block", 8, 512, 1, 77, 3000),
+    ("block", 64, 1024, 1, 6, 65536)]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("P,R,G,M,N", FORCED_ROW)
-def test_forced_row_plans(P, R, G, M, N, dtype):
+@pytest.mark.parametrize("kind,P,R,G,M,N", FORCED_ROW)
+def test_forced_row_plans(kind, P, R, G, M, N, dtype):
+    ran = 0
     for op in ("softmax", "rmsnorm"):
         code = rr.RR_OP_SOFTMAX if op == "softmax" else rr.RR_OP_RMSNORM
-        with forced(P, R, G):
+        with forced(P, R, G, kind=kind):
             try:
                 rr.rr_plan_query(code, M, N, rr.RR_F32 if dtype == "f32" else rr.RR_BF16)
             except rr.RRError:
                 continue  # not compiled for this op (register budget)
-            say(op, "forced", P, R, G, dtype, M, N)
+            say(op, "forced", kind, P, R, G, dtype, M, N)
+            ran += 1
             if op == "softmax":
-                parity_softmax(_x(M, N, dtype, sigma=2.0), dtype, f"softmax forced {P},{R},{G}")
+                parity_softmax(_x(M, N, dtype, sigma=2.0), dtype, f"softmax {kind} {P},{R},{G}")
             else:
                 parity_rmsnorm(_x(M, N, dtype), _w(N, dtype), 1e-6, dtype,
-                               f"rmsnorm forced {P},{R},{G}")
+                               f"rmsnorm {kind} {P},{R},{G}")
+    assert ran > 0
 
 
 @pytest.mark.parametrize("dtype", DTYPES)

@@ -28,17 +28,20 @@ def test_row_plans_hold_the_row(op, dt, vec):
             p = rr.rr_plan_query(op, 16384, N, dt, vec)
         P, R, G = p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]
         assert p["max_n"] == P * R * G >= N
-        assert p["path"] == (1 if G > 1 else 0)
-        assert p["block_threads"] == max(R, 256) and p["rows_per_block"] * R == p["block_threads"]
         assert p["vectorized"] == int(vec)
-        if G > 1:
-            assert p["ws_bytes"] == 256 + 1024 * (64 + 32 * G)
-            # a split row only when one workgroup (1024 lanes) cannot hold it
-            assert N > P * R or R == 1024 or N > 32768
-        else:
-            assert p["ws_bytes"] == 0
+        if p["path"] == 0:  # block kernel: a few rows per workgroup, one workgroup per row
+            assert G == 1 and N <= 65536
+            assert p["block_threads"] == max(R, 256) and p["rows_per_block"] * R == p["block_threads"]
             # the narrowest lane group that holds the row (at least 16 lanes)
             assert R == 16 or (R // 2) * P < N
+            assert p["ws_bytes"] == 0
+        else:  # stream kernel: one row per workgroup at a time, at least half full
+            assert p["path"] == (1 if G > 1 else 3) and N >= 2048
+            assert 2 * N >= P * R or not vec
+            assert p["block_threads"] == R and p["rows_per_block"] == 1
+            # a row is split only over as many workgroups as it needs
+            assert G == 1 or (G // 2) * P * R < N
+            assert p["ws_bytes"] == (256 + 1024 * (64 + 32 * G) if G > 1 else 0)
     with pytest.raises(rr.RRError):
         rr.rr_plan_query(op, 16, (1 << 20) + 1, dt, vec)
 
@@ -61,7 +64,7 @@ def test_cross_entropy_streams(dt):
     for N in NS + [(1 << 22) + 3]:
         p = rr.rr_plan_query(rr.RR_OP_XENT, 8192, N, dt)
         assert p["path"] == 2 and p["groups_per_row"] == 1 and p["ws_bytes"] == 0
-        assert p["vals_per_lane"] in (16, 32) and 16 <= p["lanes_per_row"] <= 256
+        assert p["vals_per_lane"] in (16, 32) and 16 <= p["lanes_per_row"] <= (512 if dt else 256)
 
 
 def test_forced_configurations(monkeypatch):
@@ -74,11 +77,21 @@ def test_forced_configurations(monkeypatch):
     # too small for the row
     with pytest.raises(rr.RRError):
         rr.rr_plan_query(rr.RR_OP_SOFTMAX, 50, 70000, rr.RR_F32)
-    # not compiled for RMSNorm (would not fit in registers): 64 values x 1024 lanes
-    monkeypatch.setenv("RR_FORCE_R", "1024")
+    # a stream kernel with one workgroup per row
+    monkeypatch.setenv("RR_FORCE_KIND", "stream")
     monkeypatch.setenv("RR_FORCE_G", "1")
+    p = rr.rr_plan_query(rr.RR_OP_RMSNORM, 50, 3000, rr.RR_BF16)
+    assert (p["path"], p["groups_per_row"], p["block_threads"], p["ws_bytes"]) == (3, 1, 256, 0)
+    # not compiled for RMSNorm (would not fit in registers): 64 values x 1024 lanes
+    monkeypatch.setenv("RR_FORCE_KIND", "block")
+    monkeypatch.setenv("RR_FORCE_R", "1024")
     with pytest.raises(rr.RRError):
         rr.rr_plan_query(rr.RR_OP_RMSNORM, 50, 3000, rr.RR_F32)
+    # no block kernel splits a row
+    monkeypatch.setenv("RR_FORCE_G", "2")
+    with pytest.raises(rr.RRError):
+        rr.rr_plan_query(rr.RR_OP_SOFTMAX, 50, 3000, rr.RR_F32)
+    monkeypatch.delenv("RR_FORCE_KIND")
     monkeypatch.delenv("RR_FORCE_G")
     monkeypatch.setenv("RR_FORCE_P", "16")
     monkeypatch.setenv("RR_FORCE_R", "64")

@@ -110,13 +110,15 @@ rr_status rr_workspace_check(void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Plan chosen for a call, for inspection and tests.  Needs no GPU. */
 typedef struct {
-    int path;           /* 0: row held in registers by one lane group or workgroup,
-                           1: row split over `groups_per_row` workgroups (grid path),
-                           2: streaming (cross-entropy) */
+    int path;           /* 0: block kernel, one row per lane group or workgroup,
+                           1: persistent stream kernel with each row split over
+                              `groups_per_row` workgroups (split rows, workspace),
+                           2: cross-entropy (streaming online max and sum),
+                           3: persistent stream kernel, one workgroup per row */
     int vectorized;     /* 1: 128-bit path, 0: per-element path */
     int vals_per_lane;  /* fp32 values each lane holds (row paths) or loads per step (streaming) */
     int lanes_per_row;  /* lanes that share one row inside a workgroup */
-    int groups_per_row; /* workgroups per row (1 except on the grid path) */
+    int groups_per_row; /* workgroups per row (1 except on path 1) */
     int block_threads;  /* threads per workgroup */
     int rows_per_block; /* rows one workgroup processes at once */
     int64_t max_n;      /* largest N this configuration holds (row paths) */

@@ -44,7 +44,12 @@ def bind(path: str):
     lib.oracle_softmax.argtypes = [vp, ci, i64, i64, vp]
     lib.oracle_rmsnorm.argtypes = [vp, vp, ci, i64, i64, ctypes.c_float, vp, vp]
     lib.oracle_cross_entropy.argtypes = [vp, vp, ci, i64, i64, vp, vp]
-    for f in (lib.oracle_softmax, lib.oracle_rmsnorm, lib.oracle_cross_entropy):
+    lib.oracle_cross_entropy_grad.argtypes = [vp, vp, vp, ci, i64, i64, vp, vp, vp]
+    lib.oracle_softmax_backward.argtypes = [vp, vp, ci, i64, i64, vp]
+    lib.oracle_rmsnorm_backward.argtypes = [vp, vp, vp, vp, ci, i64, i64, vp, vp]
+    for f in (lib.oracle_softmax, lib.oracle_rmsnorm, lib.oracle_cross_entropy,
+              lib.oracle_cross_entropy_grad, lib.oracle_softmax_backward,
+              lib.oracle_rmsnorm_backward):
         f.restype = ci
     return lib
 
@@ -68,7 +73,7 @@ def _dtype_of(x: np.ndarray) -> str:
 
 
 class Oracle:
-    """The three reference functions, bound to one compiled oracle library."""
+    """The reference functions, bound to one compiled oracle library."""
 
     def __init__(self, lib=None):
         self.lib = lib if lib is not None else _load()
@@ -112,6 +117,58 @@ class Oracle:
             raise ValueError("oracle_cross_entropy rejected its arguments")
         return loss, lse
 
+    def cross_entropy_grad(self, x: np.ndarray, labels: np.ndarray, dloss: np.ndarray):
+        """Returns (loss[M], lse[M], dx[M, N]) in float64; dloss is float32[M]."""
+        x = np.ascontiguousarray(x)
+        labels = np.ascontiguousarray(labels, dtype=np.int32)
+        dloss = np.ascontiguousarray(dloss, dtype=np.float32)
+        M, N = x.shape
+        if labels.shape != (M,) or dloss.shape != (M,):
+            raise ValueError("labels and dloss must have shape (M,)")
+        loss = np.empty(M, dtype=np.float64)
+        lse = np.empty(M, dtype=np.float64)
+        dx = np.empty((M, N), dtype=np.float64)
+        rc = self.lib.oracle_cross_entropy_grad(x.ctypes.data, labels.ctypes.data,
+                                                dloss.ctypes.data, _CODES[_dtype_of(x)], M, N,
+                                                loss.ctypes.data, lse.ctypes.data, dx.ctypes.data)
+        if rc:
+            raise ValueError("oracle_cross_entropy_grad rejected its arguments")
+        return loss, lse, dx
+
+    def softmax_backward(self, y: np.ndarray, dy: np.ndarray) -> np.ndarray:
+        """dx[M, N] in float64 from the forward output y and the gradient dy."""
+        y = np.ascontiguousarray(y)
+        dy = np.ascontiguousarray(dy)
+        M, N = y.shape
+        if dy.dtype != y.dtype or dy.shape != (M, N):
+            raise ValueError("dy must have the shape and dtype of y")
+        dx = np.empty((M, N), dtype=np.float64)
+        rc = self.lib.oracle_softmax_backward(y.ctypes.data, dy.ctypes.data, _CODES[_dtype_of(y)],
+                                              M, N, dx.ctypes.data)
+        if rc:
+            raise ValueError("oracle_softmax_backward rejected its arguments")
+        return dx
+
+    def rmsnorm_backward(self, x: np.ndarray, w: np.ndarray, dy: np.ndarray, rstd: np.ndarray):
+        """(dx[M, N], dw[N]) in float64; rstd is the forward's float32[M]."""
+        x = np.ascontiguousarray(x)
+        w = np.ascontiguousarray(w)
+        dy = np.ascontiguousarray(dy)
+        rstd = np.ascontiguousarray(rstd, dtype=np.float32)
+        M, N = x.shape
+        if w.dtype != x.dtype or w.shape != (N,) or dy.dtype != x.dtype or dy.shape != (M, N):
+            raise ValueError("w must be (N,) and dy (M, N), both of the input's dtype")
+        if rstd.shape != (M,):
+            raise ValueError("rstd must have shape (M,)")
+        dx = np.empty((M, N), dtype=np.float64)
+        dw = np.empty(N, dtype=np.float64)
+        rc = self.lib.oracle_rmsnorm_backward(x.ctypes.data, w.ctypes.data, dy.ctypes.data,
+                                              rstd.ctypes.data, _CODES[_dtype_of(x)], M, N,
+                                              dx.ctypes.data, dw.ctypes.data)
+        if rc:
+            raise ValueError("oracle_rmsnorm_backward rejected its arguments")
+        return dx, dw
+
 
 _default = None
 
@@ -133,3 +190,15 @@ def rmsnorm(x, w, eps, want_rstd=False):
 
 def cross_entropy(x, labels):
     return default().cross_entropy(x, labels)
+
+
+def cross_entropy_grad(x, labels, dloss):
+    return default().cross_entropy_grad(x, labels, dloss)
+
+
+def softmax_backward(y, dy):
+    return default().softmax_backward(y, dy)
+
+
+def rmsnorm_backward(x, w, dy, rstd):
+    return default().rmsnorm_backward(x, w, dy, rstd)

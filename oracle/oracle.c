@@ -25,6 +25,21 @@
  *                   (per row, no reduction over rows; a label outside
  *                   [0, N) gives loss = NaN)
  *
+ * The same pages present these kernels as building blocks of training as well
+ * as inference (section 让内存密集型内核达到"光速").  The backward passes are
+ * again textbook calculus on the definitions above, written out directly:
+ *
+ *   cross-entropy gradient (fused with the forward): with p_j = e_j / S the
+ *                   softmax of the row and g the row's upstream gradient
+ *                   dloss, dx_j = (p_j - [j == label]) * g; a label outside
+ *                   [0, N) makes the whole row of dx NaN, like its loss
+ *   softmax backward, from the forward output y and the upstream gradient dy:
+ *                   c = sum_k y_k * dy_k,  dx_j = y_j * (dy_j - c)
+ *   RMSNorm backward, from x, w, dy and the forward's fp32 rstd r:
+ *                   c = sum_k dy_k * w_k * x_k,
+ *                   dx_j = r * w_j * dy_j - r^3 * x_j * c / N,
+ *                   dw_j = sum_i dy_ij * x_ij * r_i   (over all rows)
+ *
  * Arithmetic: every input decodes exactly to double (fp32 by conversion,
  * bf16 as its 16 bits placed in the top half of an fp32); all sums run
  * left to right in double; exp, log and sqrt are the C library's double
@@ -113,6 +128,79 @@ int oracle_cross_entropy(const void *x, const int32_t *labels, int dtype, int64_
         if (lse) lse[i] = l;
         int32_t t = labels[i];
         loss[i] = (t >= 0 && (int64_t)t < N) ? l - load_elem(x, dtype, row + t) : NAN;
+    }
+    return 0;
+}
+
+/* Cross-entropy forward and its gradient with respect to the logits, per row:
+ * loss and lse as oracle_cross_entropy, dx_j = (p_j - [j == label]) * dloss_i
+ * with p the row's softmax.  dloss is fp32 per row (the upstream gradient of
+ * each row's loss).  A label outside [0, N) gives loss = NaN and a NaN row of
+ * dx.  dx is M x N double. */
+int oracle_cross_entropy_grad(const void *x, const int32_t *labels, const float *dloss, int dtype,
+                              int64_t M, int64_t N, double *loss, double *lse, double *dx) {
+    if (bad_args(dtype, M, N)) return -1;
+    for (int64_t i = 0; i < M; ++i) {
+        int64_t row = i * N;
+        double m = -INFINITY;
+        for (int64_t j = 0; j < N; ++j) {
+            double v = load_elem(x, dtype, row + j);
+            if (v > m || isnan(v)) m = v;
+        }
+        double S = 0.0;
+        for (int64_t j = 0; j < N; ++j) S += exp(load_elem(x, dtype, row + j) - m);
+        double l = m + log(S);
+        if (lse) lse[i] = l;
+        int32_t t = labels[i];
+        int ok = t >= 0 && (int64_t)t < N;
+        loss[i] = ok ? l - load_elem(x, dtype, row + t) : NAN;
+        double g = (double)dloss[i];
+        for (int64_t j = 0; j < N; ++j) {
+            double p = exp(load_elem(x, dtype, row + j) - m) / S;
+            double onehot = (j == (int64_t)t) ? 1.0 : 0.0;
+            dx[row + j] = ok ? (p - onehot) * g : NAN;
+        }
+    }
+    return 0;
+}
+
+/* Softmax backward per row from the forward output y and the upstream
+ * gradient dy (both of the input dtype): c = sum_k y_k dy_k,
+ * dx_j = y_j * (dy_j - c).  dx is M x N double. */
+int oracle_softmax_backward(const void *y, const void *dy, int dtype, int64_t M, int64_t N,
+                            double *dx) {
+    if (bad_args(dtype, M, N)) return -1;
+    for (int64_t i = 0; i < M; ++i) {
+        int64_t row = i * N;
+        double c = 0.0;
+        for (int64_t k = 0; k < N; ++k)
+            c += load_elem(y, dtype, row + k) * load_elem(dy, dtype, row + k);
+        for (int64_t j = 0; j < N; ++j)
+            dx[row + j] = load_elem(y, dtype, row + j) * (load_elem(dy, dtype, row + j) - c);
+    }
+    return 0;
+}
+
+/* RMSNorm backward from x, w, the upstream gradient dy (all of the input
+ * dtype) and the forward's per-row rstd (fp32): per row c = sum_k dy_k w_k x_k,
+ * dx_j = r w_j dy_j - r^3 x_j c / N; over all rows dw_j = sum_i dy_ij x_ij r_i.
+ * dx is M x N double, dw is N double. */
+int oracle_rmsnorm_backward(const void *x, const void *w, const void *dy, const float *rstd,
+                            int dtype, int64_t M, int64_t N, double *dx, double *dw) {
+    if (bad_args(dtype, M, N)) return -1;
+    for (int64_t j = 0; j < N; ++j) dw[j] = 0.0;
+    for (int64_t i = 0; i < M; ++i) {
+        int64_t row = i * N;
+        double r = (double)rstd[i];
+        double c = 0.0;
+        for (int64_t k = 0; k < N; ++k)
+            c += load_elem(dy, dtype, row + k) * load_elem(w, dtype, k) * load_elem(x, dtype, row + k);
+        for (int64_t j = 0; j < N; ++j) {
+            double xj = load_elem(x, dtype, row + j);
+            double gj = load_elem(dy, dtype, row + j);
+            dx[row + j] = r * load_elem(w, dtype, j) * gj - r * r * r * xj * c / (double)N;
+            dw[j] += gj * xj * r;
+        }
     }
     return 0;
 }

@@ -21,6 +21,8 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 
 SEED = 0x5EED
 STREAM_X, STREAM_W, STREAM_LABELS, STREAM_SPIKES = 0, 1, 2, 3
+# upstream gradients of the backward passes: dy (per element), dloss (per row)
+STREAM_DY, STREAM_DLOSS = 4, 5
 DTYPES = {"f32": 0, "bf16": 1}
 
 _lock = threading.Lock()

@@ -16,6 +16,19 @@ The facts:
 - brute force: the exact definition at 60 digits on tiny rows;
 - a library routine: torch's float64 CPU softmax, rms_norm, logsumexp and
   cross_entropy(reduction='none') on small rows.
+
+The backward functions (cross-entropy gradient, softmax backward, RMSNorm
+backward) are pinned to the forward functions by calculus, not by their own
+formulas:
+- central differences of the (already pinned) forward functions, Richardson
+  extrapolated over steps 2^-10 and 2^-9 taken on inputs that are multiples of
+  2^-10, so every perturbed input is exact in fp32 and the remaining error is
+  of order h^4;
+- torch's float64 autograd (and its softmax backward from the output);
+- invariants: a cross-entropy gradient row sums to zero, the RMSNorm input
+  gradient satisfies sum_j x_j dx_j = r c (1 - r^2 Q / N), dw is additive
+  over rows;
+- closed forms: constant rows, one-hot and uniform softmax outputs.
 """
 from __future__ import annotations
 
@@ -304,6 +317,252 @@ def pin_xent_bf16_decodes_exactly(o):
     dec = (xb.astype(np.uint32) << 16).view(np.float32)
     a = o.cross_entropy(xb, lab)
     b = o.cross_entropy(dec, lab)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ------------------------------------------------------- backward passes
+
+_H = 2.0**-10
+
+
+def _richardson(f, x, i, j, h=_H):
+    """d f / d x[i, j] by central differences at h and 2h, extrapolated."""
+    def d(step):
+        xp = x.copy()
+        xm = x.copy()
+        xp[i, j] += np.float32(step)
+        xm[i, j] -= np.float32(step)
+        assert float(xp[i, j]) - float(x[i, j]) == step  # exact perturbation
+        return (f(xp) - f(xm)) / (2.0 * step)
+    return (4.0 * d(h) - d(2.0 * h)) / 3.0
+
+
+def _dloss(M, seed_row=0):
+    return synth.uniform(1, M, lo=0.5, hi=1.5, stream=synth.STREAM_DLOSS, row0=seed_row)[0]
+
+
+def pin_xent_grad_forward_part_equals_forward(o):
+    x = synth.normal(6, 777, sigma=2.0)
+    lab = synth.labels(6, 777)
+    loss, lse, _ = o.cross_entropy_grad(x, lab, _dloss(6))
+    l2, s2 = o.cross_entropy(x, lab)
+    assert np.array_equal(loss, l2) and np.array_equal(lse, s2)
+
+
+def pin_xent_grad_finite_difference(o):
+    rng = np.random.default_rng(11)
+    x = _quantised_rows(rng, 3, 40, lim=4.0)
+    lab = np.array([0, 17, 39], dtype=np.int32)
+    g = np.array([1.0, 0.75, -2.5], dtype=np.float32)
+    _, _, dx = o.cross_entropy_grad(x, lab, g)
+    for i in range(3):
+        for j in (0, 5, 17, 39, int(lab[i])):
+            fd = _richardson(lambda z: o.cross_entropy(z, lab)[0][i], x, i, j)
+            assert abs(dx[i, j] - float(g[i]) * fd) <= 1e-9, (i, j)
+
+
+def pin_xent_grad_rows_sum_to_zero(o):
+    for N in (1, 2, 1000):
+        x = synth.normal(5, N, sigma=2.0)
+        lab = synth.labels(5, N)
+        g = _dloss(5)
+        _, _, dx = o.cross_entropy_grad(x, lab, g)
+        assert np.all(np.abs(dx.sum(axis=1)) <= 1e-14 * N), N
+        # the label entry is the only non-positive one (for a positive dloss)
+        assert np.all(dx[np.arange(5), lab] <= 0.0)
+        off = dx.copy()
+        off[np.arange(5), lab] = 0.0
+        assert np.all(off >= 0.0)
+
+
+def pin_xent_grad_constant_row(o):
+    for N in (1, 4, 1000):
+        x = np.full((2, N), 3.25, dtype=np.float32)
+        lab = np.array([0, N - 1], dtype=np.int32)
+        g = np.array([1.0, 0.5], dtype=np.float32)
+        _, _, dx = o.cross_entropy_grad(x, lab, g)
+        for i in range(2):
+            want = np.full(N, 1.0 / N)
+            want[lab[i]] -= 1.0
+            assert np.max(np.abs(dx[i] - want * float(g[i]))) <= 1e-15, N
+
+
+def pin_xent_grad_matches_torch_f64(o):
+    import torch
+
+    x = synth.normal(8, 2000, sigma=2.0)
+    lab = synth.labels(8, 2000)
+    g = _dloss(8)
+    t = torch.from_numpy(x).double().requires_grad_(True)
+    loss = torch.nn.functional.cross_entropy(t, torch.from_numpy(lab).long(), reduction="none")
+    loss.backward(torch.from_numpy(g).double())
+    _, _, dx = o.cross_entropy_grad(x, lab, g)
+    assert np.max(np.abs(dx - t.grad.numpy())) <= 1e-15
+
+
+def pin_xent_grad_invalid_label_row_is_nan(o):
+    x = synth.normal(3, 64)
+    lab = np.array([-1, 64, 5], dtype=np.int32)
+    loss, lse, dx = o.cross_entropy_grad(x, lab, _dloss(3))
+    assert np.all(np.isnan(loss[:2])) and np.isfinite(loss[2])
+    assert np.all(np.isnan(dx[:2])) and np.all(np.isfinite(dx[2]))
+    assert np.all(np.isfinite(lse))
+
+
+def pin_xent_grad_bf16_decodes_exactly(o):
+    xb = synth.normal(3, 300, dtype="bf16", sigma=2.0)
+    lab = synth.labels(3, 300)
+    dec = (xb.astype(np.uint32) << 16).view(np.float32)
+    g = _dloss(3)
+    a = o.cross_entropy_grad(xb, lab, g)
+    b = o.cross_entropy_grad(dec, lab, g)
+    assert all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
+def pin_softmax_bwd_matches_torch_f64(o):
+    import torch
+
+    for dt in ("f32", "bf16"):
+        y = o.softmax(synth.normal(6, 1500, sigma=2.0, dtype=dt))
+        y = y.astype(np.float32) if dt == "f32" else synth.f32_to_bf16(y.astype(np.float32))
+        dy = synth.normal(6, 1500, dtype=dt, stream=synth.STREAM_DY)
+        dec = (lambda a: a.astype(np.float64) if dt == "f32"
+               else (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+        ref = torch._softmax_backward_data(torch.from_numpy(dec(dy)), torch.from_numpy(dec(y)), 1,
+                                           torch.float64).numpy()
+        dx = o.softmax_backward(y, dy)
+        scale = np.abs(dec(y)) * (np.abs(dec(dy)) + np.abs(dec(y) * dec(dy)).sum(1, keepdims=True))
+        assert np.all(np.abs(dx - ref) <= 1e-13 * scale + 1e-300), dt
+
+
+def pin_softmax_bwd_finite_difference(o):
+    rng = np.random.default_rng(12)
+    x = _quantised_rows(rng, 2, 30, lim=4.0)
+    dy = (rng.standard_normal((2, 30))).astype(np.float32)
+    y = o.softmax(x).astype(np.float32)
+    dx = o.softmax_backward(y, dy)
+    for i in range(2):
+        for j in (0, 7, 29):
+            fd = _richardson(lambda z: float(np.dot(o.softmax(z)[i], dy[i].astype(np.float64))),
+                             x, i, j)
+            # y enters the backward rounded to fp32: about 2^-24 of each term
+            tol = 1e-6 * float(y[i, j]) * (abs(float(dy[i, j])) + float(np.abs(y[i] * dy[i]).sum()))
+            assert abs(dx[i, j] - fd) <= tol + 1e-12, (i, j)
+
+
+def pin_softmax_bwd_closed_forms(o):
+    # one-hot output: no gradient at all
+    y = np.zeros((1, 50), dtype=np.float32)
+    y[0, 13] = 1.0
+    dy = synth.normal(1, 50, stream=synth.STREAM_DY)
+    assert np.all(o.softmax_backward(y, dy) == 0.0)
+    # uniform output 1/N (N a power of two, exact): dx_j = (dy_j - mean(dy)) / N
+    N = 64
+    y = np.full((1, N), 1.0 / N, dtype=np.float32)
+    dy = synth.normal(1, N, stream=synth.STREAM_DY)
+    want = (dy[0].astype(np.float64) - dy[0].astype(np.float64).mean()) / N
+    assert np.max(np.abs(o.softmax_backward(y, dy)[0] - want)) <= 1e-17
+    # a constant upstream gradient has no effect on a normalised output
+    y = o.softmax(synth.normal(2, 200)).astype(np.float32)
+    dx = o.softmax_backward(y, np.full((2, 200), 0.75, dtype=np.float32))
+    s = y.astype(np.float64).sum(axis=1, keepdims=True)
+    assert np.max(np.abs(dx - 0.75 * y * (1.0 - s))) <= 1e-16
+
+
+def pin_softmax_bwd_bf16_decodes_exactly(o):
+    yb = synth.uniform(3, 256, lo=0.0, hi=0.01, dtype="bf16")
+    db = synth.normal(3, 256, dtype="bf16", stream=synth.STREAM_DY)
+    dec = lambda a: (a.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(o.softmax_backward(yb, db), o.softmax_backward(dec(yb), dec(db)))
+
+
+def _rms_case(M, N, dtype="f32"):
+    x = synth.normal(M, N, dtype=dtype)
+    w = synth.uniform(1, N, lo=0.5, hi=1.5, dtype=dtype)[0]
+    dy = synth.normal(M, N, dtype=dtype, stream=synth.STREAM_DY)
+    return x, w, dy
+
+
+def pin_rmsnorm_bwd_finite_difference(o):
+    rng = np.random.default_rng(13)
+    x = _quantised_rows(rng, 2, 24, lim=4.0)
+    w = _quantised_rows(rng, 1, 24, lim=2.0)[0]
+    dy = rng.standard_normal((2, 24)).astype(np.float32)
+    eps = 1e-3
+    _, r = o.rmsnorm(x, w, eps, want_rstd=True)
+    dx, dw = o.rmsnorm_backward(x, w, dy, r.astype(np.float32))
+    for i in range(2):
+        for j in (0, 11, 23):
+            fd = _richardson(lambda z: float(np.dot(o.rmsnorm(z, w, eps)[i],
+                                                    dy[i].astype(np.float64))), x, i, j)
+            # rstd enters the backward rounded to fp32
+            assert abs(dx[i, j] - fd) <= 2e-6 * (abs(fd) + 1e-3), (i, j)
+    wm = w[None, :].copy()
+    for j in (0, 9, 23):
+        fd = _richardson(lambda z: float(np.sum(o.rmsnorm(x, z[0], eps) * dy.astype(np.float64))),
+                         wm, 0, j)
+        assert abs(dw[j] - fd) <= 2e-6 * (abs(fd) + 1e-3), j
+
+
+def pin_rmsnorm_bwd_matches_torch_f64_exact_rstd(o):
+    """eps is chosen per row so that the exact r is an fp32 value: the backward
+    then sees exactly the r of the forward torch differentiates."""
+    import torch
+
+    M, N = 4, 500
+    x, w, dy = _rms_case(M, N)
+    q = (x.astype(np.float64) ** 2).mean(axis=1)
+    for i in range(M):
+        r = np.float32(0.9 / math.sqrt(q[i]))
+        eps_i = 1.0 / float(r) ** 2 - q[i]
+        assert eps_i > 0
+        t = torch.from_numpy(x[i:i + 1].astype(np.float64)).requires_grad_(True)
+        tw = torch.from_numpy(w.astype(np.float64)).requires_grad_(True)
+        y = torch.nn.functional.rms_norm(t, (N,), tw, eps=eps_i)
+        y.backward(torch.from_numpy(dy[i:i + 1].astype(np.float64)))
+        dx, dw = o.rmsnorm_backward(x[i:i + 1], w, dy[i:i + 1], np.array([r], dtype=np.float32))
+        assert np.max(np.abs(dx - t.grad.numpy())) <= 1e-12 * np.max(np.abs(dx)), i
+        assert np.max(np.abs(dw - tw.grad.numpy())) <= 1e-12 * np.max(np.abs(dw)), i
+
+
+def pin_rmsnorm_bwd_orthogonality_identity(o):
+    """sum_j x_j dx_j = r c (1 - r^2 Q / N) for any r; with the exact forward r
+    the bracket is r^2 eps, and with eps = 0 the gradient is orthogonal to x."""
+    x, w, dy = _rms_case(5, 3000)
+    _, r = o.rmsnorm(x, w, 0.0, want_rstd=True)
+    r32 = r.astype(np.float32)
+    dx, _ = o.rmsnorm_backward(x, w, dy, r32)
+    xd = x.astype(np.float64)
+    c = (dy.astype(np.float64) * w.astype(np.float64) * xd).sum(axis=1)
+    q = (xd * xd).sum(axis=1)
+    rr = r32.astype(np.float64)
+    lhs = (xd * dx).sum(axis=1)
+    rhs = rr * c * (1.0 - rr * rr * q / 3000)
+    scale = np.abs(xd * dx).sum(axis=1) + np.abs(rr * c)
+    assert np.all(np.abs(lhs - rhs) <= 1e-13 * scale)
+
+
+def pin_rmsnorm_bwd_dw_adds_over_rows(o):
+    x, w, dy = _rms_case(6, 700)
+    _, r = o.rmsnorm(x, w, 1e-6, want_rstd=True)
+    r32 = r.astype(np.float32)
+    _, dw = o.rmsnorm_backward(x, w, dy, r32)
+    parts = sum(o.rmsnorm_backward(x[i:i + 1], w, dy[i:i + 1], r32[i:i + 1])[1] for i in range(6))
+    assert np.max(np.abs(dw - parts)) <= 1e-13 * np.max(np.abs(dw))
+    # and doubling a row's upstream gradient doubles its share
+    dy2 = dy.copy()
+    dy2[0] *= 2
+    _, dw2 = o.rmsnorm_backward(x, w, dy2, r32)
+    one = o.rmsnorm_backward(x[:1], w, dy[:1], r32[:1])[1]
+    assert np.max(np.abs(dw2 - dw - one)) <= 1e-12 * np.max(np.abs(dw))
+
+
+def pin_rmsnorm_bwd_bf16_decodes_exactly(o):
+    x, w, dy = _rms_case(3, 256, "bf16")
+    dec = lambda a: (a.astype(np.uint32) << 16).view(np.float32)
+    r = np.array([0.5, 1.0, 0.75], dtype=np.float32)
+    a = o.rmsnorm_backward(x, w, dy, r)
+    b = o.rmsnorm_backward(dec(x), dec(w), dec(dy), r)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 

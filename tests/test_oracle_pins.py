@@ -59,6 +59,47 @@ MUTANTS = [
      "load_elem(x, dtype, row + (t + 1) % N)"),
     ("xent_no_range_check", "oracle_cross_entropy", "(t >= 0 && (int64_t)t < N) ?",
      "(t >= 0) ?"),
+    ("xent_grad_onehot_sign", "oracle_cross_entropy_grad", "(p - onehot) * g", "(p + onehot) * g"),
+    ("xent_grad_no_dloss", "oracle_cross_entropy_grad", "(p - onehot) * g", "(p - onehot)"),
+    ("xent_grad_onehot_index", "oracle_cross_entropy_grad", "(j == (int64_t)t)",
+     "(j == (int64_t)t + 1)"),
+    ("xent_grad_p_missing_max", "oracle_cross_entropy_grad",
+     "double p = exp(load_elem(x, dtype, row + j) - m) / S;",
+     "double p = exp(load_elem(x, dtype, row + j)) / S;"),
+    ("xent_grad_p_not_normalised", "oracle_cross_entropy_grad",
+     "double p = exp(load_elem(x, dtype, row + j) - m) / S;",
+     "double p = exp(load_elem(x, dtype, row + j) - m);"),
+    ("xent_grad_lse_missing_max", "oracle_cross_entropy_grad", "double l = m + log(S);",
+     "double l = log(S);"),
+    ("xent_grad_invalid_label_not_nan", "oracle_cross_entropy_grad",
+     "dx[row + j] = ok ? (p - onehot) * g : NAN;", "dx[row + j] = (p - onehot) * g;"),
+    ("xent_grad_dloss_of_wrong_row", "oracle_cross_entropy_grad", "double g = (double)dloss[i];",
+     "double g = (double)dloss[0];"),
+    ("softmax_bwd_no_c", "oracle_softmax_backward", "* (load_elem(dy, dtype, row + j) - c)",
+     "* load_elem(dy, dtype, row + j)"),
+    ("softmax_bwd_c_sign", "oracle_softmax_backward", "(load_elem(dy, dtype, row + j) - c)",
+     "(load_elem(dy, dtype, row + j) + c)"),
+    ("softmax_bwd_c_without_y", "oracle_softmax_backward",
+     "c += load_elem(y, dtype, row + k) * load_elem(dy, dtype, row + k);",
+     "c += load_elem(dy, dtype, row + k);"),
+    ("softmax_bwd_y_index", "oracle_softmax_backward", "dx[row + j] = load_elem(y, dtype, row + j)",
+     "dx[row + j] = load_elem(y, dtype, row + (j + 1) % N)"),
+    ("softmax_bwd_c_skips_last", "oracle_softmax_backward", "for (int64_t k = 0; k < N; ++k)",
+     "for (int64_t k = 0; k < N - 1; ++k)"),
+    ("rmsnorm_bwd_r_squared", "oracle_rmsnorm_backward", "r * r * r * xj", "r * r * xj"),
+    ("rmsnorm_bwd_N_minus_1", "oracle_rmsnorm_backward", "c / (double)N", "c / (double)(N - 1)"),
+    ("rmsnorm_bwd_c_without_weight", "oracle_rmsnorm_backward",
+     "load_elem(dy, dtype, row + k) * load_elem(w, dtype, k) * load_elem(x, dtype, row + k)",
+     "load_elem(dy, dtype, row + k) * load_elem(x, dtype, row + k)"),
+    ("rmsnorm_bwd_sign", "oracle_rmsnorm_backward", "* gj - r * r * r", "* gj + r * r * r"),
+    ("rmsnorm_bwd_dx_without_weight", "oracle_rmsnorm_backward", "r * load_elem(w, dtype, j) * gj",
+     "r * gj"),
+    ("rmsnorm_bwd_dw_without_r", "oracle_rmsnorm_backward", "dw[j] += gj * xj * r;",
+     "dw[j] += gj * xj;"),
+    ("rmsnorm_bwd_dw_overwritten", "oracle_rmsnorm_backward", "dw[j] += gj * xj * r;",
+     "dw[j] = gj * xj * r;"),
+    ("rmsnorm_bwd_dw_uses_weight", "oracle_rmsnorm_backward", "dw[j] += gj * xj * r;",
+     "dw[j] += gj * xj * r * load_elem(w, dtype, j);"),
     ("bf16_decode_shift", "load_elem", "<< 16", "<< 15"),
     ("bf16_decoded_as_f32_path", "load_elem", "if (dtype == ORACLE_F32)", "if (dtype != ORACLE_F32)"),
 ]
@@ -140,7 +181,21 @@ def test_oracle_matches_golden_cases(orc):
             got = orc.rmsnorm(x, w, c["eps"])
             exp = np.array([[float(v) for v in row] for row in c["y"]])
             assert np.max(np.abs(got - exp) / np.abs(exp)) <= 1e-14, c["name"]
-        else:
+        elif c["op"] == "xent":
             loss, lse = orc.cross_entropy(x, np.array(c["labels"], dtype=np.int32))
             assert np.max(np.abs(lse - np.array([float(v) for v in c["lse"]]))) <= 1e-13, c["name"]
             assert np.max(np.abs(loss - np.array([float(v) for v in c["loss"]]))) <= 1e-13, c["name"]
+        elif c["op"] == "xent_grad":
+            g = np.array([float.fromhex(v) for v in c["dloss"]], dtype=np.float32)
+            loss, lse, dx = orc.cross_entropy_grad(x, np.array(c["labels"], dtype=np.int32), g)
+            assert np.max(np.abs(loss - np.array([float(v) for v in c["loss"]]))) <= 1e-13, c["name"]
+            exp = np.array([[float(v) for v in row] for row in c["dx"]])
+            assert np.max(np.abs(dx - exp)) <= 1e-15, c["name"]
+        else:
+            dy = np.array([[float.fromhex(v) for v in row] for row in c["dy"]], dtype=np.float32)
+            r = np.array([float.fromhex(v) for v in c["rstd"]], dtype=np.float32)
+            dx, dw = orc.rmsnorm_backward(x, w, dy, r)
+            exp_dx = np.array([[float(v) for v in row] for row in c["dx"]])
+            exp_dw = np.array([float(v) for v in c["dw"]])
+            assert np.max(np.abs(dx - exp_dx)) <= 1e-14 * np.max(np.abs(exp_dx)), c["name"]
+            assert np.max(np.abs(dw - exp_dw)) <= 1e-14 * np.max(np.abs(exp_dw)), c["name"]

@@ -57,7 +57,12 @@ typedef enum {
 
 typedef enum { RR_F32 = 0, RR_BF16 = 1 } rr_dtype;
 
-typedef enum { RR_OP_SOFTMAX = 0, RR_OP_RMSNORM = 1, RR_OP_XENT = 2 } rr_op;
+typedef enum {
+    RR_OP_SOFTMAX = 0,
+    RR_OP_RMSNORM = 1,
+    RR_OP_XENT = 2,
+    RR_OP_XENT_GRAD = 3 /* rr_cross_entropy_fwd_bwd */
+} rr_op;
 
 /*
  * Softmax forward, per row i:  m = max_j x_ij,  y_ij = exp(x_ij - m) / sum_k exp(x_ik - m).
@@ -93,6 +98,25 @@ rr_status rr_cross_entropy_fwd(const void *logits, const int32_t *labels, float 
                                size_t ws_bytes, hipStream_t stream);
 
 /*
+ * Cross-entropy forward fused with its gradient with respect to the logits, per row i
+ * (p_i = softmax of row i, g_i = dloss_i, the upstream gradient of loss_i):
+ *     lse_i = log sum_j exp(x_ij),   loss_i = lse_i - x_i[label_i],
+ *     dlogits_ij = (p_ij - [j == label_i]) * g_i.
+ * [QuACK] section 让内存密集型内核达到"光速" (the cross-entropy loss kernel, and these
+ * kernels as building blocks of training); the gradient is the textbook derivative of
+ * the per-row loss.  The row is read from HBM once and the gradient written once.
+ * labels: int32[M]; dloss: fp32[M] (e.g. 1/M everywhere for a mean over rows);
+ * loss: fp32[M]; lse: fp32[M] or NULL; dlogits: M x N of type dt (bf16: round to
+ * nearest even).  dlogits == logits (exact aliasing) is allowed; any other overlap is
+ * rejected.  A label outside [0, N) gives loss_i = NaN and a NaN row of dlogits (lse_i
+ * is still written); it is never used as an address.  Same plans, limits and workspace
+ * as rr_softmax_fwd (query with RR_OP_XENT_GRAD).  N must fit int32 and M be below 2^30.
+ */
+rr_status rr_cross_entropy_fwd_bwd(const void *logits, const int32_t *labels, const float *dloss,
+                                   float *loss, float *lse, void *dlogits, int64_t M, int64_t N,
+                                   rr_dtype dt, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * Bytes of workspace a call with these arguments needs (0 when it needs none),
  * whatever the alignment of the pointers it will get.  The value depends only on
  * (op, M, N, dt); `device` is accepted for callers that size per device and is
@@ -113,7 +137,7 @@ typedef struct {
     int path;           /* 0: block kernel, one row per lane group or workgroup,
                            1: persistent stream kernel with each row split over
                               `groups_per_row` workgroups (split rows, workspace),
-                           2: cross-entropy (streaming online max and sum),
+                           2: cross-entropy forward (streaming online max and sum),
                            3: persistent stream kernel, one workgroup per row */
     int vectorized;     /* 1: 128-bit path, 0: per-element path */
     int vals_per_lane;  /* fp32 values each lane holds (row paths) or loads per step (streaming) */

@@ -26,9 +26,10 @@ RR_ERR_HIP = 4
 RR_ERR_GRID_TIMEOUT = 5
 
 RR_F32, RR_BF16 = 0, 1
-RR_OP_SOFTMAX, RR_OP_RMSNORM, RR_OP_XENT = 0, 1, 2
+RR_OP_SOFTMAX, RR_OP_RMSNORM, RR_OP_XENT, RR_OP_XENT_GRAD = 0, 1, 2, 3
 
-EXPORTS = ("rr_softmax_fwd", "rr_rmsnorm_fwd", "rr_cross_entropy_fwd", "rr_workspace_bytes",
+EXPORTS = ("rr_softmax_fwd", "rr_rmsnorm_fwd", "rr_cross_entropy_fwd",
+           "rr_cross_entropy_fwd_bwd", "rr_workspace_bytes",
            "rr_workspace_check", "rr_plan_query", "rr_stream_copy", "rr_status_string",
            "rr_last_hip_error")
 
@@ -65,6 +66,8 @@ def lib():
             L.rr_softmax_fwd.argtypes = [vp, vp, i64, i64, ci, vp, sz, vp]
             L.rr_rmsnorm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, ci, ctypes.c_float, vp, sz, vp]
             L.rr_cross_entropy_fwd.argtypes = [vp, vp, vp, vp, i64, i64, ci, vp, sz, vp]
+            L.rr_cross_entropy_fwd_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, ci, vp, sz,
+                                                   vp]
             L.rr_workspace_bytes.argtypes = [ci, i64, i64, ci, ci]
             L.rr_workspace_bytes.restype = sz
             L.rr_workspace_check.argtypes = [vp, sz, vp]
@@ -74,7 +77,7 @@ def lib():
             L.rr_status_string.restype = ctypes.c_char_p
             L.rr_last_hip_error.argtypes = []
             for f in (L.rr_softmax_fwd, L.rr_rmsnorm_fwd, L.rr_cross_entropy_fwd,
-                      L.rr_workspace_check, L.rr_plan_query, L.rr_stream_copy,
+                      L.rr_cross_entropy_fwd_bwd, L.rr_workspace_check, L.rr_plan_query, L.rr_stream_copy,
                       L.rr_last_hip_error):
                 f.restype = st
             _lib = L
@@ -106,6 +109,12 @@ def rmsnorm_fwd_raw(x, w, y, rstd, M, N, dt, eps, ws=0, ws_bytes=0, stream=0) ->
 def cross_entropy_fwd_raw(x, labels, loss, lse, M, N, dt, ws=0, ws_bytes=0, stream=0) -> int:
     return lib().rr_cross_entropy_fwd(x, labels, loss, lse or None, M, N, dt, ws or None,
                                       ws_bytes, stream or None)
+
+
+def cross_entropy_fwd_bwd_raw(x, labels, dloss, loss, lse, dx, M, N, dt, ws=0, ws_bytes=0,
+                              stream=0) -> int:
+    return lib().rr_cross_entropy_fwd_bwd(x, labels, dloss, loss, lse or None, dx, M, N, dt,
+                                          ws or None, ws_bytes, stream or None)
 
 
 def stream_copy_raw(src, dst, nbytes, stream=0) -> int:
@@ -206,6 +215,34 @@ def rr_cross_entropy_fwd(logits, labels, loss=None, lse=None, ws=None, stream=No
                                  lse.data_ptr(), M, N, dt, wp, wb, _stream(logits, stream)),
            "rr_cross_entropy_fwd")
     return loss, lse
+
+
+def rr_cross_entropy_fwd_bwd(logits, labels, dloss, dlogits=None, loss=None, lse=None, ws=None,
+                             stream=None):
+    """Per-row cross-entropy of logits [M, N] (int32 labels [M]) and its gradient
+    dlogits = (softmax - onehot) * dloss[:, None] (fp32 dloss [M]); dlogits may be
+    logits itself.  Returns (loss, lse, dlogits)."""
+    torch = _torch()
+    M, N = _matrix(logits)
+    if labels.dtype != torch.int32 or labels.numel() != M or not labels.is_contiguous():
+        raise ValueError("labels must be a contiguous int32 [M] tensor")
+    if dloss.dtype != torch.float32 or dloss.numel() != M or not dloss.is_contiguous():
+        raise ValueError("dloss must be a contiguous float32 [M] tensor")
+    if dlogits is None:
+        dlogits = torch.empty_like(logits)
+    if loss is None:
+        loss = torch.empty(M, dtype=torch.float32, device=logits.device)
+    if lse is None:
+        lse = torch.empty(M, dtype=torch.float32, device=logits.device)
+    dt = dtype_code(logits)
+    if ws is None:
+        ws = workspace(RR_OP_XENT_GRAD, M, N, dt, logits.device)
+    wp, wb = _ws_args(ws)
+    _check(cross_entropy_fwd_bwd_raw(logits.data_ptr(), labels.data_ptr(), dloss.data_ptr(),
+                                     loss.data_ptr(), lse.data_ptr(), dlogits.data_ptr(), M, N,
+                                     dt, wp, wb, _stream(logits, stream)),
+           "rr_cross_entropy_fwd_bwd")
+    return loss, lse, dlogits
 
 
 def rr_workspace_check(ws, stream=None) -> int:

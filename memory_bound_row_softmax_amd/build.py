@@ -24,7 +24,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librr.so")
 
-SOURCES = ["api.cpp", "plan.cpp", "softmax.hip", "rmsnorm.hip", "xent.hip", "copy.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "softmax.hip", "rmsnorm.hip", "xent.hip", "xent_grad.hip",
+           "copy.hip"]
 ARCH = "gfx950"
 
 

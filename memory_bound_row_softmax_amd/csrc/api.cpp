@@ -157,6 +157,26 @@ rr_status rr_cross_entropy_fwd(const void *logits, const int32_t *labels, float 
     return hip_status(rr::launch_xent(p, dt, logits, labels, loss, lse, M, N, a));
 }
 
+rr_status rr_cross_entropy_fwd_bwd(const void *logits, const int32_t *labels, const float *dloss,
+                                   float *loss, float *lse, void *dlogits, int64_t M, int64_t N,
+                                   rr_dtype dt, void *ws, size_t ws_bytes, hipStream_t stream) {
+    size_t bytes = 0;
+    rr_status st = check_matrix(M, N, dt, &bytes);
+    if (st != RR_OK || M == 0) return st;
+    if (!logits || !labels || !dloss || !loss || !dlogits || N > INT32_MAX || M >= (1ll << 30) ||
+        partial_overlap(logits, dlogits, bytes))
+        return RR_ERR_INVALID_ARGUMENT;
+    const bool vec = aligned16(logits) && aligned16(dlogits) && ((size_t)N * elem_size(dt)) % 16 == 0;
+    rr::Plan p;
+    st = plan_status(rr::make_plan(rr::kOpXentGrad, dt, M, N, vec, &p));
+    if (st != RR_OK) return st;
+    if ((st = check_workspace(p, ws, ws_bytes)) != RR_OK) return st;
+    rr::LaunchArgs a;
+    if ((st = launch_args(stream, &a)) != RR_OK) return st;
+    return hip_status(rr::launch_xent_grad(p, dt, logits, labels, dloss, loss, lse, dlogits, M, N,
+                                           ws, a));
+}
+
 size_t rr_workspace_bytes(rr_op op, int64_t M, int64_t N, rr_dtype dt, int device) {
     (void)device;
     if (M <= 0) return 0;

@@ -47,6 +47,7 @@ namespace rr {
 // Op codes shared by the planner and the kernels.
 constexpr int kCfgSoftmax = 0;
 constexpr int kCfgRmsnorm = 1;
+constexpr int kCfgXentGrad = 2;  // softmax kernels with the cross-entropy gradient epilogue
 
 // Which block configurations are compiled for (op, element bytes, vectorised
 // path).  Excluded are those that would need more than the 128 VGPRs a lane of a
@@ -70,10 +71,25 @@ constexpr bool block_config_enabled(int op, int elem_bytes, bool vec, int P, int
 // of a workgroup lives in LDS as fp32 (4 * P * R bytes, at most 128 KiB).  The
 // per-element path keeps P <= 16.  RMSNorm fp32 with 32 values on 1024 lanes
 // would need scratch when the row is split.
+// The cross-entropy gradient epilogue keeps the label, dloss and the label's logit
+// per row: fp32 with 32 values on 1024 lanes no longer fits in 128 VGPRs.
 constexpr bool stream_config_enabled(int op, int elem_bytes, bool vec, int P, int R, int G) {
     if (!vec && P > 16) return false;
+    if (op == kCfgXentGrad && elem_bytes == 4 && P == 32 && R == 1024) return false;
     if (op == kCfgRmsnorm && elem_bytes == 4 && P == 32 && R == 1024 && G > 1) return false;
     return true;
+}
+
+// Register buffers of a stream kernel (rows held at once: one being reduced,
+// the others' loads in flight).  A workgroup of 1024 lanes leaves each lane 128
+// VGPRs, enough for a third buffer only when P <= 16; RMSNorm, which also
+// reads its weight back from LDS, fits a third buffer only when P <= 32.
+#ifndef RR_STREAM_DEPTH
+#define RR_STREAM_DEPTH 2
+#endif
+constexpr int stream_depth(int op, int P, int R) {
+    const bool fits = (R < 1024 || P <= 16) && (op != 1 || P <= 32);
+    return (RR_STREAM_DEPTH > 2 && fits) ? RR_STREAM_DEPTH : 2;
 }
 
 // Threads per workgroup and rows per workgroup for a lane-group width R (block

@@ -22,7 +22,9 @@
 
 namespace rr {
 
-static int cfg_op(int op) { return op == kOpSoftmax ? kCfgSoftmax : kCfgRmsnorm; }
+static int cfg_op(int op) {
+    return op == kOpSoftmax ? kCfgSoftmax : op == kOpXentGrad ? kCfgXentGrad : kCfgRmsnorm;
+}
 static int elem_bytes(int dtype) { return dtype == kBf16 ? 2 : 4; }
 
 bool block_config_ok(int op, int dtype, bool vec, int P, int R) {
@@ -119,7 +121,8 @@ static bool try_choice(int op, int dtype, bool vec, int64_t N, Choice c, Plan *p
 }
 
 static bool default_row(int op, int dtype, bool vec, int64_t N, Plan *p) {
-    const int o = op == kOpSoftmax ? 0 : 1, d = dtype == kBf16 ? 1 : 0;
+    // the cross-entropy gradient runs the softmax kernels: softmax's measurements
+    const int o = op == kOpRmsnorm ? 1 : 0, d = dtype == kBf16 ? 1 : 0;
     int k = 0;
     while (k < 7 && kTunedN[k] < N) ++k;
     if (N <= kTunedN[7]) {
@@ -154,9 +157,10 @@ static void default_xent(int dtype, int64_t N, int *P, int *R) {
 
 PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *out) {
     if (!out) return kPlanInvalid;
-    if ((op != kOpSoftmax && op != kOpRmsnorm && op != kOpXent) ||
+    if ((op != kOpSoftmax && op != kOpRmsnorm && op != kOpXent && op != kOpXentGrad) ||
         (dtype != kF32 && dtype != kBf16) || M < 0 || (M > 0 && N < 1))
         return kPlanInvalid;
+    if (op == kOpXentGrad && N > INT32_MAX) return kPlanInvalid;
     if (N < 1) N = 1;  // M == 0: any plan will do, nothing is launched
     Plan p;
     p.vec = vec;

@@ -10,7 +10,9 @@ namespace rr {
 // kPathRow: block kernel; kPathSplit: stream kernel with G > 1 (split rows);
 // kPathXent: cross-entropy; kPathStream: stream kernel with G = 1.
 enum PathKind { kPathRow = 0, kPathSplit = 1, kPathXent = 2, kPathStream = 3 };
-enum OpKind { kOpSoftmax = 0, kOpRmsnorm = 1, kOpXent = 2 };
+// kOpXentGrad (cross-entropy forward fused with its gradient) runs the softmax
+// kernels with another epilogue and takes the softmax plan.
+enum OpKind { kOpSoftmax = 0, kOpRmsnorm = 1, kOpXent = 2, kOpXentGrad = 3 };
 enum DtypeKind { kF32 = 0, kBf16 = 1 };
 enum PlanResult { kPlanOk = 0, kPlanUnsupported = 1, kPlanInvalid = 2 };
 

@@ -19,6 +19,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "configs.hpp"
 #include "grid_exchange.hpp"
@@ -64,6 +65,40 @@ __device__ __forceinline__ RowView stream_row_view(const char *base, int64_t row
     return {make_buf(base + (ok ? row : 0) * row_bytes, ok ? row_bytes : 0u), 0u};
 }
 
+// Row loop of the stream kernels with D register buffers.  Rows group,
+// group + groups, ... < M are processed in order; buffer k % D holds the k-th of
+// them.  Before row k is finished, the loads of row k + D - 1 are issued, so
+// D - 1 rows are in flight while one is reduced and written.  Loads past the
+// last row read an empty buffer (no memory traffic).  `row` is the same for the
+// whole workgroup, so every branch here is uniform.
+template <int K, int D, class Step>
+__device__ __forceinline__ bool stream_steps(Step &step) {
+    if constexpr (K == D) {
+        return true;
+    } else {
+        if (!step(std::integral_constant<int, K>{})) return false;
+        return stream_steps<K + 1, D>(step);
+    }
+}
+
+template <int D, int P, class Load, class Finish>
+__device__ __forceinline__ void stream_rows(int64_t row, int64_t M, int groups, float (&buf)[D][P],
+                                            Load load, Finish finish) {
+    static_assert(D >= 2, "at least one row in flight");
+#pragma unroll
+    for (int k = 0; k < D - 1; ++k) load(buf[k], row + (int64_t)k * groups);
+    auto step = [&](auto K) -> bool {
+        constexpr int k = decltype(K)::value;
+        if (row >= M) return false;
+        load(buf[(k + D - 1) % D], row + (int64_t)(D - 1) * groups);
+        finish(buf[k], row);
+        row += groups;
+        return true;
+    };
+    while (stream_steps<0, D>(step)) {
+    }
+}
+
 // Everything a row body needs besides the row buffers.
 struct RowCtx {
     int N;
@@ -88,11 +123,42 @@ struct MergeMaxSum {
     }
 };
 
+// What a softmax kernel writes for a row, given e_j = exp(x_j - mu) in registers
+// and the factor `scale` that turns e_j into the softmax p_j.  An output policy
+// `Out` (a kernel argument) hands out one Epi per row:
+//   capture<E, C, R>(v, chunk0, l)  sees the lane's raw values before the exp;
+//   apply<E, C, R>(v, scale, M, S, chunk0, ctx, valid)  turns e into the values
+//                                   to store and writes any per-row outputs
+//                                   (M, S: the row's max and sum of exp(x - M)).
+// A stream kernel keeps kExtra more registers per row buffer for the row's own
+// inputs: stash(extra, r) fills them when the row's loads are issued (so they
+// arrive with the row), and epi(extra, r) builds the Epi when the row is
+// finished.  Plain softmax stores p_j and has no per-row inputs.
+struct SoftmaxOut {
+    static constexpr int kCfg = kCfgSoftmax;  // configuration menu predicates
+    static constexpr int kExtra = 0;
+    struct Epi {
+        template <class E, int C, int R>
+        __device__ __forceinline__ void capture(const float *, int, int) {}
+        template <class E, int C, int R>
+        __device__ __forceinline__ void apply(float *v, float scale, float, float, int,
+                                              const RowCtx &, bool) {
+#pragma unroll
+            for (int j = 0; j < C * E::VPC; ++j) v[j] *= scale;
+        }
+    };
+    __device__ __forceinline__ Epi row(int64_t) const { return {}; }
+    __device__ __forceinline__ void stash(float *, int64_t) const {}
+    __device__ __forceinline__ Epi epi(const float *, int64_t) const { return {}; }
+};
+
 // Passes 1-3 on a lane's loaded part v of the row, then the store.
-template <class E, int P, int R, int G, bool VEC>
-__device__ __forceinline__ void softmax_finish(float *v, RowView yv, bool valid, RowCtx &c) {
+template <class E, int P, int R, int G, bool VEC, class Epi>
+__device__ __forceinline__ void softmax_finish(float *v, RowView yv, bool valid, RowCtx &c,
+                                               Epi &epi) {
     constexpr int C = P / E::VPC;
     const int chunk0 = c.member * C * R;
+    epi.template capture<E, C, R>(v, chunk0, c.l);
     if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.N, -INFINITY, v);
 
     // pass 1: row max
@@ -107,22 +173,24 @@ __device__ __forceinline__ void softmax_finish(float *v, RowView yv, bool valid,
     s = row_reduce<R>(s, c.red_b, c.l, OpSum{});
 
     // pass 3: normalise (a split row first merges the G partial (max, sum) pairs)
-    float scale;
+    float scale, Mrow, Srow;
     if constexpr (G == 1) {
         scale = __builtin_amdgcn_rcpf(s);
+        Mrow = m;
+        Srow = s;
     } else {
         exchange_pairs<G>(c.g, c.member, c.it, m, s, c.spin_limit, c.bcast, MergeMaxSum{});
-        const float M = c.bcast[0], S = c.bcast[1];
-        scale = exp_shift(m, safe_max(M)) * __builtin_amdgcn_rcpf(S);
+        Mrow = c.bcast[0];
+        Srow = c.bcast[1];
+        scale = exp_shift(m, safe_max(Mrow)) * __builtin_amdgcn_rcpf(Srow);
     }
-#pragma unroll
-    for (int j = 0; j < P; ++j) v[j] *= scale;
+    epi.template apply<E, C, R>(v, scale, Mrow, Srow, chunk0, c, valid);
     store_part<E, C, R, VEC>(yv, chunk0, c.l, c.N, valid, c.full, v);
 }
 
-template <class E, int P, int R, bool VEC>
+template <class E, int P, int R, bool VEC, class Out = SoftmaxOut>
 __global__ void __launch_bounds__(block_threads_for(R))
-    softmax_block_kernel(const char *x, char *y, int64_t M, int N) {
+    softmax_block_kernel(const char *x, char *y, int64_t M, int N, Out out) {
     constexpr int C = P / E::VPC;
     constexpr int RPB = rows_per_block_for(R);
     constexpr int W = R > 64 ? R / 64 : 1;
@@ -132,16 +200,19 @@ __global__ void __launch_bounds__(block_threads_for(R))
     const uint32_t row_bytes = (uint32_t)N * E::BYTES;
     RowCtx c{N, (int)(threadIdx.x % R), 0, 0, part_full<E, C, R>(0, N), red_max + sub * W,
              red_sum + sub * W, nullptr, GroupRef{}, 0};
-    const bool valid = (int64_t)blockIdx.x * RPB + sub < M;
+    const int64_t row = (int64_t)blockIdx.x * RPB + sub;
+    const bool valid = row < M;
     float v[P];
     load_part<E, C, R, VEC>(block_row_view<R>(x, M, sub, row_bytes), 0, c.l, v);
-    softmax_finish<E, P, R, 1, VEC>(v, block_row_view<R>(y, M, sub, row_bytes), valid, c);
+    auto epi = out.row(valid ? row : M - 1);
+    softmax_finish<E, P, R, 1, VEC>(v, block_row_view<R>(y, M, sub, row_bytes), valid, c, epi);
 }
 
-template <class E, int P, int R, int G, bool VEC>
+template <class E, int P, int R, int G, bool VEC, class Out = SoftmaxOut,
+          int D = stream_depth(kCfgSoftmax, P, R)>
 __global__ void __launch_bounds__(R)
     softmax_stream_kernel(const char *x, char *y, int64_t M, int N, uint8_t *ws, int groups,
-                          int spin_limit) {
+                          int spin_limit, Out out) {
     static_assert(R >= 64, "one row per workgroup");
     constexpr int C = P / E::VPC;
     constexpr int W = R / 64;
@@ -159,22 +230,22 @@ __global__ void __launch_bounds__(R)
     c.full = part_full<E, C, R>(chunk0, N);
     const uint32_t rb = (uint32_t)N * E::BYTES;
 
-    // Two register buffers: the loads of the next row are in flight while the
-    // current row is reduced, exchanged and written.
-    float a[P], b[P];
-    int64_t row = group;
-    load_part<E, C, R, VEC>(stream_row_view(x, row, M, rb), chunk0, c.l, a);
-    while (row < M) {
-        load_part<E, C, R, VEC>(stream_row_view(x, row + groups, M, rb), chunk0, c.l, b);
-        softmax_finish<E, P, R, G, VEC>(a, stream_row_view(y, row, M, rb), true, c);
-        ++c.it;
-        row += groups;
-        if (row >= M) break;
-        load_part<E, C, R, VEC>(stream_row_view(x, row + groups, M, rb), chunk0, c.l, a);
-        softmax_finish<E, P, R, G, VEC>(b, stream_row_view(y, row, M, rb), true, c);
-        ++c.it;
-        row += groups;
-    }
+    // D register buffers: the loads of the next D - 1 rows are in flight while
+    // the current row is reduced, exchanged and written.  A row's per-row inputs
+    // (if the output policy has any) sit after its values and are loaded with it.
+    constexpr int X = Out::kExtra;
+    float buf[D][P + X];
+    stream_rows<D>(
+        (int64_t)group, M, groups, buf,
+        [&](float *v, int64_t r) {
+            load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
+            if (r < M) out.stash(v + P, r);
+        },
+        [&](float *v, int64_t r) {
+            auto epi = out.epi(v + P, r);
+            softmax_finish<E, P, R, G, VEC>(v, stream_row_view(y, r, M, rb), true, c, epi);
+            ++c.it;
+        });
     if constexpr (G > 1) {
         if (c.it > 0) depart_group<G>(c.g);
     }
@@ -261,7 +332,7 @@ __global__ void __launch_bounds__(block_threads_for(R))
                                     rstd ? rstd + row : nullptr, eps, valid, c);
 }
 
-template <class E, int P, int R, int G, bool VEC>
+template <class E, int P, int R, int G, bool VEC, int D = stream_depth(kCfgRmsnorm, P, R)>
 __global__ void __launch_bounds__(R)
     rmsnorm_stream_kernel(const char *x, const char *w, char *y, float *rstd, int64_t M, int N,
                           float eps, uint8_t *ws, int groups, int spin_limit) {
@@ -293,22 +364,17 @@ __global__ void __launch_bounds__(R)
     }
     const WeightLds<P, R> wsrc{wslot};
 
-    float a[P], b[P];
-    int64_t row = group;
-    load_part<E, C, R, VEC>(stream_row_view(x, row, M, rb), chunk0, c.l, a);
-    while (row < M) {
-        load_part<E, C, R, VEC>(stream_row_view(x, row + groups, M, rb), chunk0, c.l, b);
-        rmsnorm_finish<E, P, R, G, VEC>(a, wsrc, stream_row_view(y, row, M, rb),
-                                        rstd ? rstd + row : nullptr, eps, true, c);
-        ++c.it;
-        row += groups;
-        if (row >= M) break;
-        load_part<E, C, R, VEC>(stream_row_view(x, row + groups, M, rb), chunk0, c.l, a);
-        rmsnorm_finish<E, P, R, G, VEC>(b, wsrc, stream_row_view(y, row, M, rb),
-                                        rstd ? rstd + row : nullptr, eps, true, c);
-        ++c.it;
-        row += groups;
-    }
+    float buf[D][P];
+    stream_rows<D>(
+        (int64_t)group, M, groups, buf,
+        [&](float *v, int64_t r) {
+            load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
+        },
+        [&](float *v, int64_t r) {
+            rmsnorm_finish<E, P, R, G, VEC>(v, wsrc, stream_row_view(y, r, M, rb),
+                                            rstd ? rstd + r : nullptr, eps, true, c);
+            ++c.it;
+        });
     if constexpr (G > 1) {
         if (c.it > 0) depart_group<G>(c.g);
     }

@@ -1,75 +1,12 @@
 // softmax.hip -- instantiates the softmax kernels of the configuration menu and
 // launches the one the plan names.
-#include "launch_util.hpp"
-#include "row_kernels.hpp"
+#include "softmax_launch.hpp"
 
 namespace rr {
-namespace {
-
-template <class E, int P, int R, bool VEC>
-hipError_t launch_block(const void *x, void *y, int64_t M, int64_t N, const LaunchArgs &a) {
-    unsigned blocks;
-    hipError_t e = blocks_for_rows(M, rows_per_block_for(R), &blocks);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((softmax_block_kernel<E, P, R, VEC>), dim3(blocks),
-                       dim3(block_threads_for(R)), 0, a.stream, static_cast<const char *>(x),
-                       static_cast<char *>(y), M, (int)N);
-    return hipGetLastError();
-}
-
-template <class E, int P, int R, int G, bool VEC>
-hipError_t launch_stream(const void *x, void *y, int64_t M, int64_t N, void *ws,
-                         const LaunchArgs &a) {
-    auto kernel = softmax_stream_kernel<E, P, R, G, VEC>;
-    int groups;
-    hipError_t e = cooperative_groups(kernel, R, G, M, a, &groups);
-    if (e != hipSuccess) return e;
-    const char *xp = static_cast<const char *>(x);
-    char *yp = static_cast<char *>(y);
-    uint8_t *wsp = static_cast<uint8_t *>(ws);
-    int n = (int)N;
-    int spin = a.spin_limit;
-    if constexpr (G == 1) {
-        // no workgroup waits for another: an ordinary launch
-        hipLaunchKernelGGL(kernel, dim3(groups), dim3(R), 0, a.stream, xp, yp, M, n, wsp, groups,
-                           spin);
-        return hipGetLastError();
-    } else {
-        void *args[] = {&xp, &yp, &M, &n, &wsp, &groups, &spin};
-        return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(kernel),
-                                          dim3(groups * G), dim3(R), args, 0, a.stream);
-    }
-}
-
-template <class E, bool VEC>
-hipError_t dispatch(const Plan &p, const void *x, void *y, int64_t M, int64_t N, void *ws,
-                    const LaunchArgs &a) {
-    if (!p.stream) {
-#define RR_X(P_, R_)                                                               \
-    if constexpr (block_config_enabled(kCfgSoftmax, E::BYTES, VEC, P_, R_))        \
-        if (p.P == P_ && p.R == R_) return launch_block<E, P_, R_, VEC>(x, y, M, N, a);
-        RR_BLOCK_CONFIGS(RR_X)
-#undef RR_X
-    } else {
-#define RR_X(P_, R_, G_)                                                                \
-    if constexpr (stream_config_enabled(kCfgSoftmax, E::BYTES, VEC, P_, R_, G_))        \
-        if (p.P == P_ && p.R == R_ && p.G == G_)                                        \
-            return launch_stream<E, P_, R_, G_, VEC>(x, y, M, N, ws, a);
-        RR_STREAM_CONFIGS(RR_X)
-#undef RR_X
-    }
-    return hipErrorInvalidValue;
-}
-
-}  // namespace
 
 hipError_t launch_softmax(const Plan &p, int dtype, const void *x, void *y, int64_t M, int64_t N,
                           void *ws, const LaunchArgs &a) {
-    if (dtype == kF32)
-        return p.vec ? dispatch<F32, true>(p, x, y, M, N, ws, a)
-                     : dispatch<F32, false>(p, x, y, M, N, ws, a);
-    return p.vec ? dispatch<BF16, true>(p, x, y, M, N, ws, a)
-                 : dispatch<BF16, false>(p, x, y, M, N, ws, a);
+    return softmax_launch::launch(p, dtype, x, y, M, N, ws, SoftmaxOut{}, a);
 }
 
 }  // namespace rr

@@ -11,7 +11,7 @@ import torch
 
 import memory_bound_row_softmax_amd as rr
 import oracle
-from _verify import check_bf16, check_f32
+from _verify import check_bf16, check_f32, check_grad
 
 DEV = "cuda:0"
 
@@ -102,3 +102,30 @@ def parity_xent(x_np, labels_np, dtype, what):
     ref_loss, ref_lse = oracle.cross_entropy(x_np, labels_np)
     check_f32(lse, ref_lse, what + " lse")
     return check_f32(loss, ref_loss, what + " loss")
+
+
+def run_xent_grad(x_np, labels_np, dloss_np, dtype, inplace=False):
+    x = to_dev(x_np, dtype)
+    lab = torch.from_numpy(np.ascontiguousarray(labels_np, dtype=np.int32)).to(DEV)
+    g = torch.from_numpy(np.ascontiguousarray(dloss_np, dtype=np.float32)).to(DEV)
+    loss, lse, dx = rr.rr_cross_entropy_fwd_bwd(x, lab, g, dlogits=x if inplace else None)
+    torch.cuda.synchronize()
+    return loss.cpu().numpy(), lse.cpu().numpy(), from_dev(dx)
+
+
+def xent_grad_scale(x_np, labels_np, dloss_np):
+    """Per-element size of the gradient's terms: (p + onehot) * |dloss|."""
+    p = oracle.softmax(x_np)
+    M, N = p.shape
+    lab = np.asarray(labels_np)
+    ok = (lab >= 0) & (lab < N)
+    p[np.flatnonzero(ok), lab[ok]] += 1.0
+    return p * np.abs(np.asarray(dloss_np, dtype=np.float64))[:, None]
+
+
+def parity_xent_grad(x_np, labels_np, dloss_np, dtype, what, inplace=False):
+    loss, lse, dx = run_xent_grad(x_np, labels_np, dloss_np, dtype, inplace=inplace)
+    ref_loss, ref_lse, ref_dx = oracle.cross_entropy_grad(x_np, labels_np, dloss_np)
+    check_f32(lse, ref_lse, what + " lse")
+    check_f32(loss, ref_loss, what + " loss")
+    return check_grad(dx, ref_dx, xent_grad_scale(x_np, labels_np, dloss_np), dtype, what + " dx")

@@ -58,6 +58,7 @@ def test_zero_rows_is_a_no_op():
     assert rr.softmax_fwd_raw(0, 0, 0, 5, rr.RR_F32) == rr.RR_OK
     assert rr.rmsnorm_fwd_raw(0, 0, 0, 0, 0, 5, rr.RR_BF16, 1e-6) == rr.RR_OK
     assert rr.cross_entropy_fwd_raw(0, 0, 0, 0, 0, 5, rr.RR_F32) == rr.RR_OK
+    assert rr.cross_entropy_fwd_bwd_raw(0, 0, 0, 0, 0, 0, 0, 5, rr.RR_BF16) == rr.RR_OK
 
 
 @needs_no_gpu
@@ -76,6 +77,17 @@ def test_zero_rows_is_a_no_op():
     ("xent null labels", lambda: rr.cross_entropy_fwd_raw(A, 0, B, 0, 4, 8, rr.RR_F32)),
     ("xent null loss", lambda: rr.cross_entropy_fwd_raw(A, C, 0, 0, 4, 8, rr.RR_F32)),
     ("xent N > int32", lambda: rr.cross_entropy_fwd_raw(A, C, B, 0, 1, 1 << 31, rr.RR_BF16)),
+    ("xgrad null labels", lambda: rr.cross_entropy_fwd_bwd_raw(A, 0, C, C + 64, 0, B, 4, 8, rr.RR_F32)),
+    ("xgrad null dloss", lambda: rr.cross_entropy_fwd_bwd_raw(A, C, 0, C + 64, 0, B, 4, 8, rr.RR_F32)),
+    ("xgrad null loss", lambda: rr.cross_entropy_fwd_bwd_raw(A, C, C + 64, 0, 0, B, 4, 8, rr.RR_F32)),
+    ("xgrad null dlogits", lambda: rr.cross_entropy_fwd_bwd_raw(A, C, C + 64, C + 128, 0, 0, 4, 8,
+                                                                rr.RR_F32)),
+    ("xgrad overlap", lambda: rr.cross_entropy_fwd_bwd_raw(A, C, C + 64, C + 128, 0, A + 4, 4, 8,
+                                                           rr.RR_F32)),
+    ("xgrad N > int32", lambda: rr.cross_entropy_fwd_bwd_raw(A, C, C + 64, C + 128, 0, B, 1,
+                                                             1 << 31, rr.RR_BF16)),
+    ("xgrad M >= 2^30", lambda: rr.cross_entropy_fwd_bwd_raw(A, C, C + 64, C + 128, 0, B, 1 << 30,
+                                                             8, rr.RR_BF16)),
     ("size overflow", lambda: rr.softmax_fwd_raw(A, B, 1 << 62, 1 << 20, rr.RR_F32)),
     ("copy misaligned", lambda: rr.stream_copy_raw(A + 4, B, 64)),
     ("copy odd size", lambda: rr.stream_copy_raw(A, B, 40)),

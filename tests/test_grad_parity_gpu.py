@@ -1,0 +1,159 @@
+"""GPU parity of the backward passes: the HIP kernels (through the C ABI) against
+the double-precision oracle, element by element, on seeded inputs.
+
+Cross-entropy forward fused with its gradient: loss and lse within relative 1e-5,
+the gradient within the cancellation-aware bound of tests/_verify.py.  The fused
+kernel is the softmax kernel with another epilogue, so every softmax path (lane
+group, workgroup, persistent stream, split rows, per-element) is run.
+"""
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_row_softmax_amd as rr
+import oracle
+import synth
+from _gpu import DEV, forced, from_dev, parity_xent_grad, run_xent_grad, say, to_dev, xent_grad_scale
+from _verify import check_f32, check_grad
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = ("f32", "bf16")
+SHAPES = [(256, 1024), (64, 1), (64, 3), (70, 255), (33, 257), (37, 1000), (16, 4095),
+          (16, 4096), (9, 4097), (8, 16384), (5, 20000), (4, 65536), (3, 65537), (3, 131072),
+          (2, 200000), (2, 262144)]
+
+
+def _dloss(M, row0=0):
+    return synth.uniform(1, M, lo=0.5, hi=1.5, stream=synth.STREAM_DLOSS, row0=row0)[0]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N", SHAPES)
+def test_xent_grad(M, N, dtype):
+    say("xent grad", dtype, M, N)
+    x = synth.normal(M, N, sigma=2.0, dtype=dtype)
+    parity_xent_grad(x, synth.labels(M, N), _dloss(M), dtype, f"xent grad {dtype} {M}x{N}")
+
+
+FORCED = [("stream", 64, 256, 2, 300, 20000), ("stream", 32, 512, 16, 97, 70000),
+          ("stream", 64, 512, 2, 50, 65536), ("stream", 64, 512, 16, 9, 500000),
+          ("stream", 16, 1024, 1, 700, 16000), ("stream", 32, 512, 1, 3, 16384),
+          ("stream", 16, 1024, 8, 200, 100000), ("block", 16, 16, 1, 100, 256),
+          ("block", 32, 128, 1, 31, 4000), ("block", 16, 1024, 1, 5, 16384),
+          ("block", 64, 1024, 1, 6, 65536)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("kind,P,R,G,M,N", FORCED)
+def test_xent_grad_forced_plans(kind, P, R, G, M, N, dtype):
+    with forced(P, R, G, kind=kind):
+        try:
+            rr.rr_plan_query(rr.RR_OP_XENT_GRAD, M, N, rr.RR_F32 if dtype == "f32" else rr.RR_BF16)
+        except rr.RRError:
+            pytest.skip("not compiled for this dtype (register budget)")
+        say("xent grad forced", kind, P, R, G, dtype, M, N)
+        x = synth.normal(M, N, sigma=2.0, dtype=dtype)
+        parity_xent_grad(x, synth.labels(M, N), _dloss(M), dtype, f"xent grad {kind} {P},{R},{G}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N", [(64, 1024), (8, 131072)])
+def test_xent_grad_in_place(M, N, dtype):
+    say("xent grad in place", dtype, M, N)
+    x = synth.normal(M, N, sigma=2.0, dtype=dtype)
+    parity_xent_grad(x, synth.labels(M, N), _dloss(M), dtype, "in-place xent grad", inplace=True)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("N", [64, 1000, 4096, 40000, 131072])
+def test_xent_grad_unaligned(N, dtype):
+    M = 6
+    x_np = synth.normal(M, N, sigma=2.0, dtype=dtype)
+    lab, g = synth.labels(M, N), _dloss(M)
+    xs = to_dev(np.concatenate([np.zeros(1, x_np.dtype), x_np.ravel()]), dtype)[1:].view(M, N)
+    dx = torch.empty(M * N + 1, dtype=xs.dtype, device=DEV)[1:].view(M, N)
+    assert xs.data_ptr() % 16 != 0
+    say("xent grad unaligned", dtype, N)
+    loss, lse, dx = rr.rr_cross_entropy_fwd_bwd(xs, torch.from_numpy(lab).to(DEV),
+                                                torch.from_numpy(g).to(DEV), dlogits=dx)
+    torch.cuda.synchronize()
+    ref_loss, ref_lse, ref_dx = oracle.cross_entropy_grad(x_np, lab, g)
+    check_f32(loss.cpu().numpy(), ref_loss, "unaligned loss")
+    check_f32(lse.cpu().numpy(), ref_lse, "unaligned lse")
+    check_grad(from_dev(dx), ref_dx, xent_grad_scale(x_np, lab, g), dtype, "unaligned dx")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_xent_grad_special_rows(dtype):
+    say("xent grad special rows", dtype)
+    # invalid labels: NaN loss and a NaN gradient row; valid rows untouched
+    M, N = 8, 5000
+    x = synth.normal(M, N, sigma=2.0, dtype=dtype)
+    lab = np.array([0, -1, N, N - 1, 1 << 30, 7, -(1 << 30), 4999], dtype=np.int32)
+    parity_xent_grad(x, lab, _dloss(M), dtype, "invalid labels")
+    # spiky rows (many exact maxima) and large values
+    x = synth.normal(40, 8192, dtype=dtype)
+    synth.spikes_(x, p=0.01, value=20.0, dtype=dtype)
+    parity_xent_grad(x, synth.labels(40, 8192), _dloss(40), dtype, "spiky xent grad")
+    big = (synth.normal(8, 3000) * 30 + 1000.0).astype(np.float32)
+    big = big if dtype == "f32" else synth.f32_to_bf16(big)
+    parity_xent_grad(big, synth.labels(8, 3000), _dloss(8), dtype, "large-value xent grad")
+    # N = 1: loss 0, gradient 0; constant rows: gradient (1/N - onehot) * dloss
+    x = synth.normal(50, 1, sigma=5.0, dtype=dtype)
+    loss, _, dx = run_xent_grad(x, np.zeros(50, np.int32), _dloss(50), dtype)
+    assert np.all(loss == 0.0)
+    assert np.all((dx if dtype == "f32" else (dx.astype(np.uint32) << 16).view(np.float32)) == 0.0)
+    c = np.full((4, 4096), 2.5, dtype=np.float32)
+    c = c if dtype == "f32" else synth.f32_to_bf16(c)
+    parity_xent_grad(c, np.array([0, 5, 4095, 17], np.int32), _dloss(4), dtype, "constant rows")
+
+
+def test_xent_grad_negative_and_zero_dloss():
+    say("xent grad signed dloss")
+    M, N = 16, 3000
+    x = synth.normal(M, N, sigma=2.0)
+    g = np.linspace(-2.0, 2.0, M).astype(np.float32)
+    g[3] = 0.0
+    parity_xent_grad(x, synth.labels(M, N), g, "f32", "signed dloss")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_xent_grad_split_rows_are_deterministic(dtype):
+    M, N = 300, 131072 if dtype == "f32" else 262144
+    code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
+    assert rr.rr_plan_query(rr.RR_OP_XENT_GRAD, M, N, code)["path"] == 1
+    x = to_dev(synth.normal(M, N, sigma=2.0, dtype=dtype), dtype)
+    lab = torch.from_numpy(synth.labels(M, N)).to(DEV)
+    g = torch.from_numpy(_dloss(M)).to(DEV)
+    ws = rr.workspace(rr.RR_OP_XENT_GRAD, M, N, code, DEV)
+    outs = []
+    for i in range(3):
+        say("xent grad split-row repeat", i, dtype)
+        outs.append(rr.rr_cross_entropy_fwd_bwd(x, lab, g, ws=ws))
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0
+    for o in outs[1:]:
+        assert all(torch.equal(a, b) for a, b in zip(outs[0], o))
+    assert rr.rr_workspace_check(ws) == rr.RR_OK
+    # gradient rows sum to zero up to the rounding of their entries
+    s = outs[0][2].double().sum(dim=1).abs().max()
+    assert float(s) < (1e-3 if dtype == "f32" else 0.1)
+
+
+def test_xent_grad_golden_cases():
+    import json
+    import os
+    say("xent grad golden")
+    path = os.path.join(os.path.dirname(__file__), "golden", "tiny_cases.json")
+    for c in json.load(open(path))["cases"]:
+        if c["op"] != "xent_grad":
+            continue
+        x = np.array([[float.fromhex(v) for v in r] for r in c["x"]], dtype=np.float32)
+        lab = np.array(c["labels"], np.int32)
+        g = np.array([float.fromhex(v) for v in c["dloss"]], dtype=np.float32)
+        loss, lse, dx = run_xent_grad(x, lab, g, "f32")
+        check_f32(loss, np.array([float(v) for v in c["loss"]]), c["name"] + " loss")
+        check_f32(lse, np.array([float(v) for v in c["lse"]]), c["name"] + " lse")
+        ref = np.array([[float(v) for v in r] for r in c["dx"]])
+        check_grad(dx, ref, xent_grad_scale(x, lab, g), "f32", c["name"] + " dx")

@@ -8,7 +8,7 @@ import pytest
 
 import memory_bound_row_softmax_amd as rr
 
-ROW_OPS = (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM)
+ROW_OPS = (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM, rr.RR_OP_XENT_GRAD)
 NS = [1, 2, 3, 7, 100, 255, 256, 257, 1000, 1024, 2048, 4095, 4096, 4097, 8192, 16384, 32768,
       65535, 65536, 65537, 131072, 200000, 262144, 524288, 1 << 20]
 
@@ -44,6 +44,21 @@ def test_row_plans_hold_the_row(op, dt, vec):
             assert p["ws_bytes"] == (256 + 1024 * (64 + 32 * G) if G > 1 else 0)
     with pytest.raises(rr.RRError):
         rr.rr_plan_query(op, 16, (1 << 20) + 1, dt, vec)
+
+
+@pytest.mark.parametrize("dt", (rr.RR_F32, rr.RR_BF16))
+def test_cross_entropy_gradient_takes_the_softmax_plan(dt):
+    """The fused gradient runs the softmax kernels; only fp32 with 32 values on
+    1024 lanes is missing from its menu (it would not fit the registers)."""
+    for N in NS[:-2]:
+        for vec in (True, False):
+            a = rr.rr_plan_query(rr.RR_OP_SOFTMAX, 8192, N, dt, vec)
+            b = rr.rr_plan_query(rr.RR_OP_XENT_GRAD, 8192, N, dt, vec)
+            if dt == rr.RR_F32 and a["path"] in (1, 3) and (a["vals_per_lane"], a["lanes_per_row"]) == (32, 1024):
+                assert (b["vals_per_lane"], b["lanes_per_row"]) != (32, 1024)
+                assert b["max_n"] >= N
+            else:
+                assert a == b, N
 
 
 def test_workspace_scales_with_rows_up_to_the_group_cap():

@@ -60,6 +60,8 @@ def algorithmic_bytes(w) -> int:
         return w.M * w.N * 2 * s
     if w.op == "rmsnorm":
         return w.M * w.N * 2 * s + w.N * s
+    if w.op == "xent_grad":  # logits in, gradient out; labels, dloss in; loss, lse out
+        return w.M * w.N * 2 * s + 16 * w.M
     return w.M * w.N * s + 12 * w.M
 
 
@@ -91,6 +93,7 @@ class Runner:
         s = esize(w.dtype)
         in_bytes = w.M * w.N * s
         out_bytes = in_bytes if w.op != "xent" else 8 * w.M
+        has_rows = w.op in ("xent", "xent_grad")  # per-row labels and losses
         self.sets = max(1, min(16, math.ceil(min_rotation_bytes / (in_bytes + out_bytes))))
         tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
 
@@ -108,18 +111,21 @@ class Runner:
         del host, x_np, block
         x0 = x0.view(tdt) if w.dtype == "bf16" else x0
         self.x = [x0] + [x0.clone() for _ in range(self.sets - 1)]
-        if w.op == "xent":
+        if has_rows:
             lab = torch.from_numpy(W.label_rows(w)).to(device)  # labels are per row: all rows
             self.labels = lab
             self.loss = [torch.empty(w.M, dtype=torch.float32, device=device) for _ in range(self.sets)]
             self.lse = [torch.empty(w.M, dtype=torch.float32, device=device) for _ in range(self.sets)]
-        else:
+        if w.op == "xent_grad":
+            self.dloss = torch.from_numpy(W.dloss_rows(w)).to(device)
+        if w.op != "xent":
             self.y = [torch.empty_like(x0) for _ in range(self.sets)]
         if w.op == "rmsnorm":
             wn = W.weight(w)
             wt = torch.from_numpy(wn if w.dtype == "f32" else wn.view(np.int16)).to(device)
             self.weight = wt.view(tdt) if w.dtype == "bf16" else wt
-        op = {"softmax": rr.RR_OP_SOFTMAX, "rmsnorm": rr.RR_OP_RMSNORM, "xent": rr.RR_OP_XENT}[w.op]
+        op = {"softmax": rr.RR_OP_SOFTMAX, "rmsnorm": rr.RR_OP_RMSNORM, "xent": rr.RR_OP_XENT,
+              "xent_grad": rr.RR_OP_XENT_GRAD}[w.op]
         self.op = op
         self.ws = rr.workspace(op, w.M, w.N, self.dt, device)
         self.wsp = self.ws.data_ptr() if self.ws is not None else 0
@@ -128,10 +134,12 @@ class Runner:
         self.stream = torch.cuda.Stream(device=device)
         self.sp = self.stream.cuda_stream
         self.xp = [t.data_ptr() for t in self.x]
-        if w.op == "xent":
+        if has_rows:
             self.lp, self.ep = [t.data_ptr() for t in self.loss], [t.data_ptr() for t in self.lse]
             self.labp = self.labels.data_ptr()
-        else:
+        if w.op == "xent_grad":
+            self.gp = self.dloss.data_ptr()
+        if w.op != "xent":
             self.yp = [t.data_ptr() for t in self.y]
         self.wp = self.weight.data_ptr() if w.op == "rmsnorm" else 0
         self.copy_dst = None
@@ -144,6 +152,10 @@ class Runner:
         if w.op == "rmsnorm":
             return rr.rmsnorm_fwd_raw(self.xp[i], self.wp, self.yp[i], 0, w.M, w.N, self.dt, w.eps,
                                       self.wsp, self.wsb, self.sp)
+        if w.op == "xent_grad":
+            return rr.cross_entropy_fwd_bwd_raw(self.xp[i], self.labp, self.gp, self.lp[i],
+                                                self.ep[i], self.yp[i], w.M, w.N, self.dt,
+                                                self.wsp, self.wsb, self.sp)
         return rr.cross_entropy_fwd_raw(self.xp[i], self.labp, self.lp[i], self.ep[i], w.M, w.N,
                                         self.dt, self.wsp, self.wsb, self.sp)
 
@@ -195,6 +207,8 @@ def cpu_baseline(w, seconds: float):
             oracle.softmax(x)
         elif w.op == "rmsnorm":
             oracle.rmsnorm(x, W.weight(w), w.eps)
+        elif w.op == "xent_grad":
+            oracle.cross_entropy_grad(x, W.label_rows(w, nrows=rows), W.dloss_rows(w, nrows=rows))
         else:
             oracle.cross_entropy(x, W.label_rows(w, nrows=rows))
         return time.perf_counter() - t0
@@ -296,7 +310,7 @@ def main() -> int:
                 except (ValueError, KeyError):
                     pass
         only = [t for t in args.only.split(",") if t]
-        for w in W.FIXED + W.sweep():
+        for w in W.FIXED + W.sweep() + W.BACKWARD:
             if w.name in done or (only and not all(t in w.name for t in only)):
                 continue
             line = measure(w, args.steps, args.warmup, args.rotate_bytes, False, 0,

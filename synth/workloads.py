@@ -15,7 +15,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import SEED, STREAM_LABELS, STREAM_SPIKES, STREAM_W, STREAM_X, labels, normal, spikes_, uniform
+from . import (SEED, STREAM_DLOSS, STREAM_DY, STREAM_LABELS, STREAM_SPIKES, STREAM_W, STREAM_X,
+               labels, normal, spikes_, uniform)
 
 RMSNORM_EPS = 1e-6
 
@@ -23,7 +24,7 @@ RMSNORM_EPS = 1e-6
 @dataclass(frozen=True)
 class Workload:
     name: str
-    op: str          # "softmax" | "rmsnorm" | "xent"
+    op: str          # "softmax" | "rmsnorm" | "xent" | "xent_grad"
     dtype: str       # "f32" | "bf16"
     M: int
     N: int
@@ -41,6 +42,12 @@ SOFTMAX_SPIKY = Workload("softmax_f32_16384x131072_spiky", "softmax", "f32", 163
                          spiky=True)
 FIXED = [SOFTMAX_SMALL, RMSNORM_MAIN, XENT_VOCAB, SOFTMAX_SPIKY]
 
+# Backward passes (training): the cross-entropy forward fused with its gradient
+# on the vocab-like shape above and on a bf16 32K vocabulary.  Per-row upstream
+# gradients dloss ~ U(0.5, 1.5).
+BACKWARD = [Workload("xentgrad_f32_8192x131072", "xent_grad", "f32", 8192, 131072, sigma=2.0),
+            Workload("xentgrad_bf16_16384x32768", "xent_grad", "bf16", 16384, 32768, sigma=2.0)]
+
 SWEEP_M = (8192, 16384, 32768)
 SWEEP_N = (256, 1024, 4096, 16384, 65536, 262144)
 
@@ -57,7 +64,7 @@ def sweep():
 
 
 def by_name(name: str) -> Workload:
-    for w in FIXED + sweep():
+    for w in FIXED + BACKWARD + sweep():
         if w.name == name:
             return w
     raise KeyError(name)
@@ -83,3 +90,9 @@ def label_rows(w: Workload, *, seed=SEED, rows=None, row0=0, nrows=None) -> np.n
     """Cross-entropy labels, uniform in [0, N)."""
     M = w.M if nrows is None else nrows
     return labels(M, w.N, seed=seed, stream=STREAM_LABELS, rows=rows, row0=row0)
+
+
+def dloss_rows(w: Workload, *, seed=SEED, row0=0, nrows=None) -> np.ndarray:
+    """Per-row upstream gradient of the loss, U(0.5, 1.5) as float32."""
+    M = w.M if nrows is None else nrows
+    return uniform(1, M, lo=0.5, hi=1.5, seed=seed, stream=STREAM_DLOSS, row0=row0).reshape(M)

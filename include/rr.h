@@ -61,7 +61,8 @@ typedef enum {
     RR_OP_SOFTMAX = 0,
     RR_OP_RMSNORM = 1,
     RR_OP_XENT = 2,
-    RR_OP_XENT_GRAD = 3 /* rr_cross_entropy_fwd_bwd */
+    RR_OP_XENT_GRAD = 3,   /* rr_cross_entropy_fwd_bwd */
+    RR_OP_SOFTMAX_BWD = 4  /* rr_softmax_bwd */
 } rr_op;
 
 /*
@@ -115,6 +116,19 @@ rr_status rr_cross_entropy_fwd(const void *logits, const int32_t *labels, float 
 rr_status rr_cross_entropy_fwd_bwd(const void *logits, const int32_t *labels, const float *dloss,
                                    float *loss, float *lse, void *dlogits, int64_t M, int64_t N,
                                    rr_dtype dt, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Softmax backward from the forward output y and the upstream gradient dy, per row i:
+ *     c_i = sum_k y_ik * dy_ik,   dx_ij = y_ij * (dy_ij - c_i).
+ * [QuACK] sections NCU 性能分析（Softmax 内核） and 内存吞吐量 (the softmax) and
+ * 让内存密集型内核达到"光速" (these kernels as building blocks of training); the formula
+ * is the textbook derivative of the softmax.  y, dy and dx are M x N of type dt; y and
+ * dy are each read once and dx written once.  dx may be y or dy itself (exact aliasing);
+ * any other overlap among the three is rejected.  Arithmetic in fp32.  Rows of more than
+ * 32768 elements are split over workgroups and need a workspace (RR_OP_SOFTMAX_BWD).
+ */
+rr_status rr_softmax_bwd(const void *y, const void *dy, void *dx, int64_t M, int64_t N,
+                         rr_dtype dt, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * Bytes of workspace a call with these arguments needs (0 when it needs none),

@@ -26,10 +26,10 @@ RR_ERR_HIP = 4
 RR_ERR_GRID_TIMEOUT = 5
 
 RR_F32, RR_BF16 = 0, 1
-RR_OP_SOFTMAX, RR_OP_RMSNORM, RR_OP_XENT, RR_OP_XENT_GRAD = 0, 1, 2, 3
+RR_OP_SOFTMAX, RR_OP_RMSNORM, RR_OP_XENT, RR_OP_XENT_GRAD, RR_OP_SOFTMAX_BWD = 0, 1, 2, 3, 4
 
 EXPORTS = ("rr_softmax_fwd", "rr_rmsnorm_fwd", "rr_cross_entropy_fwd",
-           "rr_cross_entropy_fwd_bwd", "rr_workspace_bytes",
+           "rr_cross_entropy_fwd_bwd", "rr_softmax_bwd", "rr_workspace_bytes",
            "rr_workspace_check", "rr_plan_query", "rr_stream_copy", "rr_status_string",
            "rr_last_hip_error")
 
@@ -68,6 +68,7 @@ def lib():
             L.rr_cross_entropy_fwd.argtypes = [vp, vp, vp, vp, i64, i64, ci, vp, sz, vp]
             L.rr_cross_entropy_fwd_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, ci, vp, sz,
                                                    vp]
+            L.rr_softmax_bwd.argtypes = [vp, vp, vp, i64, i64, ci, vp, sz, vp]
             L.rr_workspace_bytes.argtypes = [ci, i64, i64, ci, ci]
             L.rr_workspace_bytes.restype = sz
             L.rr_workspace_check.argtypes = [vp, sz, vp]
@@ -77,7 +78,7 @@ def lib():
             L.rr_status_string.restype = ctypes.c_char_p
             L.rr_last_hip_error.argtypes = []
             for f in (L.rr_softmax_fwd, L.rr_rmsnorm_fwd, L.rr_cross_entropy_fwd,
-                      L.rr_cross_entropy_fwd_bwd, L.rr_workspace_check, L.rr_plan_query, L.rr_stream_copy,
+                      L.rr_cross_entropy_fwd_bwd, L.rr_softmax_bwd, L.rr_workspace_check, L.rr_plan_query, L.rr_stream_copy,
                       L.rr_last_hip_error):
                 f.restype = st
             _lib = L
@@ -115,6 +116,10 @@ def cross_entropy_fwd_bwd_raw(x, labels, dloss, loss, lse, dx, M, N, dt, ws=0, w
                               stream=0) -> int:
     return lib().rr_cross_entropy_fwd_bwd(x, labels, dloss, loss, lse or None, dx, M, N, dt,
                                           ws or None, ws_bytes, stream or None)
+
+
+def softmax_bwd_raw(y, dy, dx, M, N, dt, ws=0, ws_bytes=0, stream=0) -> int:
+    return lib().rr_softmax_bwd(y, dy, dx, M, N, dt, ws or None, ws_bytes, stream or None)
 
 
 def stream_copy_raw(src, dst, nbytes, stream=0) -> int:
@@ -243,6 +248,23 @@ def rr_cross_entropy_fwd_bwd(logits, labels, dloss, dlogits=None, loss=None, lse
                                      dt, wp, wb, _stream(logits, stream)),
            "rr_cross_entropy_fwd_bwd")
     return loss, lse, dlogits
+
+
+def rr_softmax_bwd(y, dy, dx=None, ws=None, stream=None):
+    """Softmax backward from the forward output y [M, N] and the gradient dy [M, N]:
+    dx = y * (dy - rowsum(y * dy)); dx may be y or dy itself."""
+    M, N = _matrix(y)
+    if dy.shape != y.shape or dy.dtype != y.dtype or not dy.is_contiguous():
+        raise ValueError("dy must be a contiguous tensor of y's shape and dtype")
+    if dx is None:
+        dx = _torch().empty_like(y)
+    dt = dtype_code(y)
+    if ws is None:
+        ws = workspace(RR_OP_SOFTMAX_BWD, M, N, dt, y.device)
+    wp, wb = _ws_args(ws)
+    _check(softmax_bwd_raw(y.data_ptr(), dy.data_ptr(), dx.data_ptr(), M, N, dt, wp, wb,
+                           _stream(y, stream)), "rr_softmax_bwd")
+    return dx
 
 
 def rr_workspace_check(ws, stream=None) -> int:

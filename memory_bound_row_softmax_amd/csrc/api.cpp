@@ -177,6 +177,24 @@ rr_status rr_cross_entropy_fwd_bwd(const void *logits, const int32_t *labels, co
                                            ws, a));
 }
 
+rr_status rr_softmax_bwd(const void *y, const void *dy, void *dx, int64_t M, int64_t N,
+                         rr_dtype dt, void *ws, size_t ws_bytes, hipStream_t stream) {
+    size_t bytes = 0;
+    rr_status st = check_matrix(M, N, dt, &bytes);
+    if (st != RR_OK || M == 0) return st;
+    if (!y || !dy || !dx || partial_overlap(y, dx, bytes) || partial_overlap(dy, dx, bytes))
+        return RR_ERR_INVALID_ARGUMENT;
+    const bool vec = aligned16(y) && aligned16(dy) && aligned16(dx) &&
+                     ((size_t)N * elem_size(dt)) % 16 == 0;
+    rr::Plan p;
+    st = plan_status(rr::make_plan(rr::kOpSoftmaxBwd, dt, M, N, vec, &p));
+    if (st != RR_OK) return st;
+    if ((st = check_workspace(p, ws, ws_bytes)) != RR_OK) return st;
+    rr::LaunchArgs a;
+    if ((st = launch_args(stream, &a)) != RR_OK) return st;
+    return hip_status(rr::launch_softmax_bwd(p, dt, y, dy, dx, M, N, ws, a));
+}
+
 size_t rr_workspace_bytes(rr_op op, int64_t M, int64_t N, rr_dtype dt, int device) {
     (void)device;
     if (M <= 0) return 0;

@@ -48,6 +48,7 @@ namespace rr {
 constexpr int kCfgSoftmax = 0;
 constexpr int kCfgRmsnorm = 1;
 constexpr int kCfgXentGrad = 2;  // softmax kernels with the cross-entropy gradient epilogue
+constexpr int kCfgSoftmaxBwd = 3;
 
 // Which block configurations are compiled for (op, element bytes, vectorised
 // path).  Excluded are those that would need more than the 128 VGPRs a lane of a
@@ -58,8 +59,10 @@ constexpr int kCfgXentGrad = 2;  // softmax kernels with the cross-entropy gradi
 //   RMSNorm:                       about 2P + 40 (row and weight both in registers)
 //   per-element path:              grows with the per-element offsets, so P <= 32
 //                                  (P <= 16 for RMSNorm with 1024 lanes)
+//   softmax backward:              about 2P + 30 (y and dy both in registers)
 constexpr bool block_config_enabled(int op, int elem_bytes, bool vec, int P, int R) {
     (void)elem_bytes;
+    if (op == kCfgSoftmaxBwd) return (vec ? P : 2 * P) * (R == 1024 ? 2 : 1) <= 64;
     if (!vec && P > 32) return false;
     if (!vec && op == kCfgRmsnorm && R == 1024 && P > 16) return false;
     if (op == kCfgRmsnorm && R == 1024 && P == 64) return false;
@@ -76,6 +79,8 @@ constexpr bool block_config_enabled(int op, int elem_bytes, bool vec, int P, int
 constexpr bool stream_config_enabled(int op, int elem_bytes, bool vec, int P, int R, int G) {
     if (!vec && P > 16) return false;
     if (op == kCfgXentGrad && elem_bytes == 4 && P == 32 && R == 1024) return false;
+    // softmax backward keeps two rows (y, dy) per buffer: about 4P + 40 VGPRs
+    if (op == kCfgSoftmaxBwd) return vec ? (R == 1024 ? P <= 16 : P <= 32) : P <= 16;
     if (op == kCfgRmsnorm && elem_bytes == 4 && P == 32 && R == 1024 && G > 1) return false;
     return true;
 }

@@ -25,6 +25,8 @@ hipError_t launch_xent(const Plan &p, int dtype, const void *x, const int32_t *l
 hipError_t launch_xent_grad(const Plan &p, int dtype, const void *x, const int32_t *labels,
                             const float *dloss, float *loss, float *lse, void *dx, int64_t M,
                             int64_t N, void *ws, const LaunchArgs &a);
+hipError_t launch_softmax_bwd(const Plan &p, int dtype, const void *y, const void *dy, void *dx,
+                              int64_t M, int64_t N, void *ws, const LaunchArgs &a);
 hipError_t launch_copy(const void *src, void *dst, size_t bytes, const LaunchArgs &a);
 
 }  // namespace rr

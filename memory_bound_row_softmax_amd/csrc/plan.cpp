@@ -23,7 +23,12 @@
 namespace rr {
 
 static int cfg_op(int op) {
-    return op == kOpSoftmax ? kCfgSoftmax : op == kOpXentGrad ? kCfgXentGrad : kCfgRmsnorm;
+    switch (op) {
+    case kOpSoftmax: return kCfgSoftmax;
+    case kOpXentGrad: return kCfgXentGrad;
+    case kOpSoftmaxBwd: return kCfgSoftmaxBwd;
+    default: return kCfgRmsnorm;
+    }
 }
 static int elem_bytes(int dtype) { return dtype == kBf16 ? 2 : 4; }
 
@@ -91,8 +96,8 @@ struct Choice {
     int P, R, G;
 };
 constexpr int kTunedN[8] = {256, 1024, 4096, 16384, 32768, 65536, 131072, 262144};
-//                      [op: softmax, rmsnorm][dtype: f32, bf16][N bucket]
-static const Choice kTuned[2][2][8] = {
+//                      [op: softmax, rmsnorm, softmax backward][dtype: f32, bf16][N bucket]
+static const Choice kTuned[3][2][8] = {
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {true, 64, 512, 1},
       {true, 16, 1024, 2}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 16, 256, 1}, {false, 64, 256, 1},
@@ -101,6 +106,11 @@ static const Choice kTuned[2][2][8] = {
       {true, 16, 1024, 2}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 64, 512, 8}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {true, 32, 1024, 1},
       {false, 64, 512, 1}, {true, 32, 1024, 2}, {true, 64, 512, 4}, {true, 64, 512, 8}}},
+    // softmax backward (y and dy both held: at most 32 values per lane in a stream kernel)
+    {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 16, 1024, 1},
+      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16}},
+     {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 16, 256, 1}, {false, 16, 1024, 1},
+      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16}}},
 };
 
 static bool try_choice(int op, int dtype, bool vec, int64_t N, Choice c, Plan *p) {
@@ -122,7 +132,7 @@ static bool try_choice(int op, int dtype, bool vec, int64_t N, Choice c, Plan *p
 
 static bool default_row(int op, int dtype, bool vec, int64_t N, Plan *p) {
     // the cross-entropy gradient runs the softmax kernels: softmax's measurements
-    const int o = op == kOpRmsnorm ? 1 : 0, d = dtype == kBf16 ? 1 : 0;
+    const int o = op == kOpRmsnorm ? 1 : op == kOpSoftmaxBwd ? 2 : 0, d = dtype == kBf16 ? 1 : 0;
     int k = 0;
     while (k < 7 && kTunedN[k] < N) ++k;
     if (N <= kTunedN[7]) {
@@ -134,9 +144,9 @@ static bool default_row(int op, int dtype, bool vec, int64_t N, Plan *p) {
     }
     // Past the table, or a configuration the per-element path does not have:
     // the first stream configuration that holds the row with the fewest workgroups.
-    static const int kStreamPR[4][2] = {{64, 512}, {32, 1024}, {64, 256}, {16, 1024}};
+    static const int kStreamPR[5][2] = {{64, 512}, {32, 1024}, {64, 256}, {32, 512}, {16, 1024}};
     for (int g = 1; g <= 16; g *= 2)
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 5; ++j)
             if (try_choice(op, dtype, vec, N, Choice{true, kStreamPR[j][0], kStreamPR[j][1], g}, p))
                 return true;
     return false;
@@ -157,7 +167,8 @@ static void default_xent(int dtype, int64_t N, int *P, int *R) {
 
 PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *out) {
     if (!out) return kPlanInvalid;
-    if ((op != kOpSoftmax && op != kOpRmsnorm && op != kOpXent && op != kOpXentGrad) ||
+    if ((op != kOpSoftmax && op != kOpRmsnorm && op != kOpXent && op != kOpXentGrad &&
+         op != kOpSoftmaxBwd) ||
         (dtype != kF32 && dtype != kBf16) || M < 0 || (M > 0 && N < 1))
         return kPlanInvalid;
     if (op == kOpXentGrad && N > INT32_MAX) return kPlanInvalid;

@@ -12,7 +12,8 @@ namespace rr {
 enum PathKind { kPathRow = 0, kPathSplit = 1, kPathXent = 2, kPathStream = 3 };
 // kOpXentGrad (cross-entropy forward fused with its gradient) runs the softmax
 // kernels with another epilogue and takes the softmax plan.
-enum OpKind { kOpSoftmax = 0, kOpRmsnorm = 1, kOpXent = 2, kOpXentGrad = 3 };
+// kOpSoftmaxBwd: softmax backward from the forward output (two input rows).
+enum OpKind { kOpSoftmax = 0, kOpRmsnorm = 1, kOpXent = 2, kOpXentGrad = 3, kOpSoftmaxBwd = 4 };
 enum DtypeKind { kF32 = 0, kBf16 = 1 };
 enum PlanResult { kPlanOk = 0, kPlanUnsupported = 1, kPlanInvalid = 2 };
 

@@ -60,6 +60,17 @@ __device__ __forceinline__ float tree_sum_squares(const float *v) {
     }
 }
 
+// Balanced pairwise sum of a[i] * b[i] (products formed at the leaves).
+template <int N>
+__device__ __forceinline__ float tree_dot(const float *a, const float *b) {
+    if constexpr (N == 1) {
+        return a[0] * b[0];
+    } else {
+        constexpr int H = N / 2;
+        return tree_dot<H>(a, b) + tree_dot<N - H>(a + H, b + H);
+    }
+}
+
 // ---- cross-lane moves -------------------------------------------------------
 
 template <int CTRL>

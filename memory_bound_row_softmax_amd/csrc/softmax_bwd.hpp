@@ -1,0 +1,102 @@
+// softmax_bwd.hpp -- softmax backward from the forward output: per row
+//     c = sum_k y_k * dy_k,   dx_j = y_j * (dy_j - c).
+//
+// The QuACK article (无需CUDA代码，给H100加速33%-50%), section 让内存密集型内核达到"光速",
+// presents its memory-bound kernels as building blocks of training as well as
+// inference; the softmax backward is the textbook derivative of the softmax it
+// describes (sections NCU 性能分析（Softmax 内核） and 内存吞吐量).  It is again one
+// row reduction between a load and a store: y and dy are read once, dx written once
+// (two reads and one write per element).  Each lane keeps its part of both input
+// rows, so a lane holds 2P values and the menu is narrower than the forward's.
+// Rows split over G workgroups exchange the partial dot product like RMSNorm's sum
+// of squares.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "configs.hpp"
+#include "grid_exchange.hpp"
+#include "reduce.hpp"
+#include "row_io.hpp"
+#include "row_kernels.hpp"
+#include "vec_io.hpp"
+
+namespace rr {
+
+// a: the lane's part of y, b: of dy; a becomes dx.
+template <class E, int P, int R, int G, bool VEC>
+__device__ __forceinline__ void softmax_bwd_finish(float *a, float *b, RowView dxv, bool valid,
+                                                   RowCtx &c) {
+    constexpr int C = P / E::VPC;
+    const int chunk0 = c.member * C * R;
+    if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.N, 0.0f, a);
+    float t = tree_dot<P>(a, b);
+    t = row_reduce<R>(t, c.red_a, c.l, OpSum{});
+    if constexpr (G > 1) {
+        exchange_pairs<G>(c.g, c.member, c.it, t, 0.0f, c.spin_limit, c.bcast, MergeSum{});
+        t = c.bcast[0];
+    }
+#pragma unroll
+    for (int j = 0; j < P; ++j) a[j] = a[j] * (b[j] - t);
+    store_part<E, C, R, VEC>(dxv, chunk0, c.l, c.N, valid, c.full, a);
+}
+
+template <class E, int P, int R, bool VEC>
+__global__ void __launch_bounds__(block_threads_for(R))
+    softmax_bwd_block_kernel(const char *y, const char *dy, char *dx, int64_t M, int N) {
+    constexpr int C = P / E::VPC;
+    constexpr int RPB = rows_per_block_for(R);
+    constexpr int W = R > 64 ? R / 64 : 1;
+    __shared__ float red[RPB * W];
+    const int sub = lane_group<R>();
+    const uint32_t row_bytes = (uint32_t)N * E::BYTES;
+    RowCtx c{N, (int)(threadIdx.x % R), 0, 0, part_full<E, C, R>(0, N), red + sub * W, nullptr,
+             nullptr, GroupRef{}, 0};
+    const bool valid = (int64_t)blockIdx.x * RPB + sub < M;
+    float a[P], b[P];
+    load_part<E, C, R, VEC>(block_row_view<R>(y, M, sub, row_bytes), 0, c.l, a);
+    load_part<E, C, R, VEC>(block_row_view<R>(dy, M, sub, row_bytes), 0, c.l, b);
+    softmax_bwd_finish<E, P, R, 1, VEC>(a, b, block_row_view<R>(dx, M, sub, row_bytes), valid, c);
+}
+
+// Persistent stream kernel: each buffer holds a row of y (first P values) and of
+// dy (next P), the next row's loads in flight while the current one is finished.
+template <class E, int P, int R, int G, bool VEC>
+__global__ void __launch_bounds__(R)
+    softmax_bwd_stream_kernel(const char *y, const char *dy, char *dx, int64_t M, int N,
+                              uint8_t *ws, int groups, int spin_limit) {
+    static_assert(R >= 64, "one row per workgroup");
+    constexpr int C = P / E::VPC;
+    constexpr int W = R / 64;
+    __shared__ float red[W];
+    __shared__ float bcast[3];
+    RowCtx c{N, (int)threadIdx.x, 0, 0, true, red, nullptr, bcast, GroupRef{}, spin_limit};
+    int group = blockIdx.x;
+    if constexpr (G > 1) {
+        group_of_block<G>(groups, &group, &c.member);
+        c.g = group_ref<G>(ws, group);
+        if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
+    }
+    const int chunk0 = c.member * C * R;
+    c.full = part_full<E, C, R>(chunk0, N);
+    const uint32_t rb = (uint32_t)N * E::BYTES;
+
+    float buf[2][2 * P];
+    stream_rows<2>(
+        (int64_t)group, M, groups, buf,
+        [&](float *v, int64_t r) {
+            load_part<E, C, R, VEC>(stream_row_view(y, r, M, rb), chunk0, c.l, v);
+            load_part<E, C, R, VEC>(stream_row_view(dy, r, M, rb), chunk0, c.l, v + P);
+        },
+        [&](float *v, int64_t r) {
+            softmax_bwd_finish<E, P, R, G, VEC>(v, v + P, stream_row_view(dx, r, M, rb), true, c);
+            ++c.it;
+        });
+    if constexpr (G > 1) {
+        if (c.it > 0) depart_group<G>(c.g);
+    }
+}
+
+}  // namespace rr

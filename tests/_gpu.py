@@ -129,3 +129,32 @@ def parity_xent_grad(x_np, labels_np, dloss_np, dtype, what, inplace=False):
     check_f32(lse, ref_lse, what + " lse")
     check_f32(loss, ref_loss, what + " loss")
     return check_grad(dx, ref_dx, xent_grad_scale(x_np, labels_np, dloss_np), dtype, what + " dx")
+
+
+def softmax_bwd_inputs(M, N, dtype, sigma=2.0):
+    """y = the softmax of a seeded row (oracle, rounded to the dtype), dy ~ N(0, 1)."""
+    import synth
+
+    y64 = oracle.softmax(synth.normal(M, N, sigma=sigma))
+    y = y64.astype(np.float32) if dtype == "f32" else synth.f32_to_bf16(y64.astype(np.float32))
+    dy = synth.normal(M, N, dtype=dtype, stream=synth.STREAM_DY)
+    return y, dy
+
+
+def _dec(a, dtype):
+    return (a.astype(np.float64) if dtype == "f32"
+            else (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+
+
+def softmax_bwd_scale(y_np, dy_np, dtype):
+    y, dy = _dec(y_np, dtype), _dec(dy_np, dtype)
+    return np.abs(y) * (np.abs(dy) + np.abs(y * dy).sum(axis=1, keepdims=True))
+
+
+def parity_softmax_bwd(y_np, dy_np, dtype, what, inplace=None):
+    y, dy = to_dev(y_np, dtype), to_dev(dy_np, dtype)
+    dx = {"y": y, "dy": dy}.get(inplace)
+    dx = rr.rr_softmax_bwd(y, dy, dx=dx)
+    torch.cuda.synchronize()
+    ref = oracle.softmax_backward(y_np, dy_np)
+    return check_grad(from_dev(dx), ref, softmax_bwd_scale(y_np, dy_np, dtype), dtype, what)

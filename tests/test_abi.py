@@ -59,6 +59,7 @@ def test_zero_rows_is_a_no_op():
     assert rr.rmsnorm_fwd_raw(0, 0, 0, 0, 0, 5, rr.RR_BF16, 1e-6) == rr.RR_OK
     assert rr.cross_entropy_fwd_raw(0, 0, 0, 0, 0, 5, rr.RR_F32) == rr.RR_OK
     assert rr.cross_entropy_fwd_bwd_raw(0, 0, 0, 0, 0, 0, 0, 5, rr.RR_BF16) == rr.RR_OK
+    assert rr.softmax_bwd_raw(0, 0, 0, 0, 5, rr.RR_F32) == rr.RR_OK
 
 
 @needs_no_gpu
@@ -88,6 +89,10 @@ def test_zero_rows_is_a_no_op():
                                                              1 << 31, rr.RR_BF16)),
     ("xgrad M >= 2^30", lambda: rr.cross_entropy_fwd_bwd_raw(A, C, C + 64, C + 128, 0, B, 1 << 30,
                                                              8, rr.RR_BF16)),
+    ("smbwd null dy", lambda: rr.softmax_bwd_raw(A, 0, B, 4, 8, rr.RR_F32)),
+    ("smbwd null dx", lambda: rr.softmax_bwd_raw(A, C, 0, 4, 8, rr.RR_F32)),
+    ("smbwd overlap y", lambda: rr.softmax_bwd_raw(A, C, A + 16, 4, 8, rr.RR_F32)),
+    ("smbwd overlap dy", lambda: rr.softmax_bwd_raw(A, C, C - 16, 4, 8, rr.RR_F32)),
     ("size overflow", lambda: rr.softmax_fwd_raw(A, B, 1 << 62, 1 << 20, rr.RR_F32)),
     ("copy misaligned", lambda: rr.stream_copy_raw(A + 4, B, 64)),
     ("copy odd size", lambda: rr.stream_copy_raw(A, B, 40)),

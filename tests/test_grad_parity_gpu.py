@@ -1,6 +1,10 @@
 """GPU parity of the backward passes: the HIP kernels (through the C ABI) against
 the double-precision oracle, element by element, on seeded inputs.
 
+Softmax backward: dx from the forward output y (the oracle's softmax of a seeded
+row, rounded to the dtype) and dy ~ N(0, 1), within the cancellation-aware bound
+with scale y_j * (|dy_j| + sum_k |y_k dy_k|).
+
 Cross-entropy forward fused with its gradient: loss and lse within relative 1e-5,
 the gradient within the cancellation-aware bound of tests/_verify.py.  The fused
 kernel is the softmax kernel with another epilogue, so every softmax path (lane
@@ -13,7 +17,8 @@ import torch
 import memory_bound_row_softmax_amd as rr
 import oracle
 import synth
-from _gpu import DEV, forced, from_dev, parity_xent_grad, run_xent_grad, say, to_dev, xent_grad_scale
+from _gpu import (DEV, forced, from_dev, parity_softmax_bwd, parity_xent_grad, run_xent_grad, say,
+                  softmax_bwd_inputs, softmax_bwd_scale, to_dev, xent_grad_scale)
 from _verify import check_f32, check_grad
 
 pytestmark = pytest.mark.gpu
@@ -157,3 +162,98 @@ def test_xent_grad_golden_cases():
         check_f32(lse, np.array([float(v) for v in c["lse"]]), c["name"] + " lse")
         ref = np.array([[float(v) for v in r] for r in c["dx"]])
         check_grad(dx, ref, xent_grad_scale(x, lab, g), "f32", c["name"] + " dx")
+
+
+# ------------------------------------------------------------- softmax backward
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N", SHAPES)
+def test_softmax_bwd(M, N, dtype):
+    say("softmax bwd", dtype, M, N)
+    y, dy = softmax_bwd_inputs(M, N, dtype)
+    parity_softmax_bwd(y, dy, dtype, f"softmax bwd {dtype} {M}x{N}")
+
+
+SMBWD_FORCED = [("stream", 32, 512, 2, 300, 20000), ("stream", 32, 512, 16, 97, 70000),
+                ("stream", 16, 1024, 1, 700, 16000), ("stream", 16, 1024, 16, 9, 262144),
+                ("stream", 32, 512, 1, 3, 16384), ("block", 16, 16, 1, 100, 256),
+                ("block", 32, 128, 1, 31, 4000), ("block", 64, 512, 1, 5, 32768),
+                ("block", 32, 1024, 1, 6, 30000), ("block", 8, 64, 1, 70, 300)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("kind,P,R,G,M,N", SMBWD_FORCED)
+def test_softmax_bwd_forced_plans(kind, P, R, G, M, N, dtype):
+    with forced(P, R, G, kind=kind):
+        try:
+            rr.rr_plan_query(rr.RR_OP_SOFTMAX_BWD, M, N, rr.RR_F32 if dtype == "f32" else rr.RR_BF16)
+        except rr.RRError:
+            pytest.skip("not compiled for this dtype (register budget)")
+        say("softmax bwd forced", kind, P, R, G, dtype, M, N)
+        y, dy = softmax_bwd_inputs(M, N, dtype)
+        parity_softmax_bwd(y, dy, dtype, f"softmax bwd {kind} {P},{R},{G}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("inplace", ["y", "dy"])
+def test_softmax_bwd_in_place(inplace, dtype):
+    for M, N in ((64, 1024), (8, 131072)):
+        say("softmax bwd in place", inplace, dtype, M, N)
+        y, dy = softmax_bwd_inputs(M, N, dtype)
+        parity_softmax_bwd(y, dy, dtype, f"softmax bwd in place {inplace}", inplace=inplace)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("N", [64, 1000, 4096, 40000, 131072])
+def test_softmax_bwd_unaligned(N, dtype):
+    M = 6
+    y_np, dy_np = softmax_bwd_inputs(M, N, dtype)
+    pad = lambda a: to_dev(np.concatenate([np.zeros(1, a.dtype), a.ravel()]), dtype)[1:].view(M, N)
+    y, dy = pad(y_np), pad(dy_np)
+    dx = torch.empty(M * N + 1, dtype=y.dtype, device=DEV)[1:].view(M, N)
+    assert y.data_ptr() % 16 != 0
+    say("softmax bwd unaligned", dtype, N)
+    rr.rr_softmax_bwd(y, dy, dx=dx)
+    torch.cuda.synchronize()
+    check_grad(from_dev(dx), oracle.softmax_backward(y_np, dy_np),
+               softmax_bwd_scale(y_np, dy_np, dtype), dtype, "unaligned softmax bwd")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_softmax_bwd_special_rows(dtype):
+    say("softmax bwd special rows", dtype)
+    # one-hot outputs: no gradient at all; uniform outputs: (dy - mean dy) / N
+    N = 4096
+    y = np.zeros((3, N), dtype=np.float32)
+    y[np.arange(3), [0, 17, N - 1]] = 1.0
+    yb = y if dtype == "f32" else synth.f32_to_bf16(y)
+    dy = synth.normal(3, N, dtype=dtype, stream=synth.STREAM_DY)
+    parity_softmax_bwd(yb, dy, dtype, "one-hot y")
+    u = np.full((3, N), 1.0 / N, dtype=np.float32)
+    parity_softmax_bwd(u if dtype == "f32" else synth.f32_to_bf16(u), dy, dtype, "uniform y")
+    # N = 1: y = 1, dx = 0
+    y1 = np.ones((40, 1), dtype=np.float32)
+    parity_softmax_bwd(y1 if dtype == "f32" else synth.f32_to_bf16(y1),
+                       synth.normal(40, 1, dtype=dtype, stream=synth.STREAM_DY), dtype, "N = 1")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_softmax_bwd_split_rows_are_deterministic(dtype):
+    M, N = 200, 262144
+    code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
+    assert rr.rr_plan_query(rr.RR_OP_SOFTMAX_BWD, M, N, code)["path"] == 1
+    y_np, dy_np = softmax_bwd_inputs(M, N, dtype)
+    y, dy = to_dev(y_np, dtype), to_dev(dy_np, dtype)
+    ws = rr.workspace(rr.RR_OP_SOFTMAX_BWD, M, N, code, DEV)
+    outs = []
+    for i in range(3):
+        say("softmax bwd split-row repeat", i, dtype)
+        outs.append(rr.rr_softmax_bwd(y, dy, ws=ws))
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    assert rr.rr_workspace_check(ws) == rr.RR_OK
+    rows = np.arange(0, M, 37)
+    check_grad(from_dev(outs[0][torch.from_numpy(rows).to(DEV)]),
+               oracle.softmax_backward(y_np[rows], dy_np[rows]),
+               softmax_bwd_scale(y_np[rows], dy_np[rows], dtype), dtype, "split rows sampled")

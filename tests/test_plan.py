@@ -8,7 +8,7 @@ import pytest
 
 import memory_bound_row_softmax_amd as rr
 
-ROW_OPS = (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM, rr.RR_OP_XENT_GRAD)
+ROW_OPS = (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM, rr.RR_OP_XENT_GRAD, rr.RR_OP_SOFTMAX_BWD)
 NS = [1, 2, 3, 7, 100, 255, 256, 257, 1000, 1024, 2048, 4095, 4096, 4097, 8192, 16384, 32768,
       65535, 65536, 65537, 131072, 200000, 262144, 524288, 1 << 20]
 

@@ -62,7 +62,8 @@ typedef enum {
     RR_OP_RMSNORM = 1,
     RR_OP_XENT = 2,
     RR_OP_XENT_GRAD = 3,   /* rr_cross_entropy_fwd_bwd */
-    RR_OP_SOFTMAX_BWD = 4  /* rr_softmax_bwd */
+    RR_OP_SOFTMAX_BWD = 4, /* rr_softmax_bwd */
+    RR_OP_RMSNORM_BWD = 5  /* rr_rmsnorm_bwd */
 } rr_op;
 
 /*
@@ -129,6 +130,27 @@ rr_status rr_cross_entropy_fwd_bwd(const void *logits, const int32_t *labels, co
  */
 rr_status rr_softmax_bwd(const void *y, const void *dy, void *dx, int64_t M, int64_t N,
                          rr_dtype dt, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * RMSNorm backward from x, w, the upstream gradient dy and the forward's rstd r
+ * (per row i, as written by rr_rmsnorm_fwd):
+ *     c_i = sum_k dy_ik w_k x_ik,   dx_ij = r_i (w_j dy_ij - x_ij r_i^2 c_i / N),
+ *     dw_j = sum_i dy_ij x_ij r_i.
+ * [QuACK] section 让内存密集型内核达到"光速" (RMSNorm among the memory-bound kernels,
+ * which serve training as well as inference); the formulas are the textbook
+ * derivative of the forward above (eps enters only through r).  x, dy, dx: M x N of
+ * type dt; w: N of type dt; rstd: fp32[M]; dw: fp32[N] (always written, zeros when
+ * M == 0).  x and dy are read once and dx written once; dw is reduced over the rows
+ * through fp32 partial rows in the workspace (one per workgroup), added in a fixed
+ * order, so repeated calls give the same bits.  dx may be x or dy itself (exact
+ * aliasing); any other overlap among x, dy, dx and dw is rejected.  The workspace
+ * (RR_OP_RMSNORM_BWD) is always needed when M > 0; only its first part (split rows)
+ * must start zero-filled, as for the other calls.  N up to 262144 (131072 when the
+ * rows are not 16-byte aligned).
+ */
+rr_status rr_rmsnorm_bwd(const void *x, const void *w, const void *dy, const float *rstd,
+                         void *dx, float *dw, int64_t M, int64_t N, rr_dtype dt, void *ws,
+                         size_t ws_bytes, hipStream_t stream);
 
 /*
  * Bytes of workspace a call with these arguments needs (0 when it needs none),

@@ -26,10 +26,11 @@ RR_ERR_HIP = 4
 RR_ERR_GRID_TIMEOUT = 5
 
 RR_F32, RR_BF16 = 0, 1
-RR_OP_SOFTMAX, RR_OP_RMSNORM, RR_OP_XENT, RR_OP_XENT_GRAD, RR_OP_SOFTMAX_BWD = 0, 1, 2, 3, 4
+(RR_OP_SOFTMAX, RR_OP_RMSNORM, RR_OP_XENT, RR_OP_XENT_GRAD, RR_OP_SOFTMAX_BWD,
+ RR_OP_RMSNORM_BWD) = 0, 1, 2, 3, 4, 5
 
 EXPORTS = ("rr_softmax_fwd", "rr_rmsnorm_fwd", "rr_cross_entropy_fwd",
-           "rr_cross_entropy_fwd_bwd", "rr_softmax_bwd", "rr_workspace_bytes",
+           "rr_cross_entropy_fwd_bwd", "rr_softmax_bwd", "rr_rmsnorm_bwd", "rr_workspace_bytes",
            "rr_workspace_check", "rr_plan_query", "rr_stream_copy", "rr_status_string",
            "rr_last_hip_error")
 
@@ -69,6 +70,7 @@ def lib():
             L.rr_cross_entropy_fwd_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, ci, vp, sz,
                                                    vp]
             L.rr_softmax_bwd.argtypes = [vp, vp, vp, i64, i64, ci, vp, sz, vp]
+            L.rr_rmsnorm_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, ci, vp, sz, vp]
             L.rr_workspace_bytes.argtypes = [ci, i64, i64, ci, ci]
             L.rr_workspace_bytes.restype = sz
             L.rr_workspace_check.argtypes = [vp, sz, vp]
@@ -78,7 +80,8 @@ def lib():
             L.rr_status_string.restype = ctypes.c_char_p
             L.rr_last_hip_error.argtypes = []
             for f in (L.rr_softmax_fwd, L.rr_rmsnorm_fwd, L.rr_cross_entropy_fwd,
-                      L.rr_cross_entropy_fwd_bwd, L.rr_softmax_bwd, L.rr_workspace_check, L.rr_plan_query, L.rr_stream_copy,
+                      L.rr_cross_entropy_fwd_bwd, L.rr_softmax_bwd, L.rr_rmsnorm_bwd,
+                      L.rr_workspace_check, L.rr_plan_query, L.rr_stream_copy,
                       L.rr_last_hip_error):
                 f.restype = st
             _lib = L
@@ -120,6 +123,11 @@ def cross_entropy_fwd_bwd_raw(x, labels, dloss, loss, lse, dx, M, N, dt, ws=0, w
 
 def softmax_bwd_raw(y, dy, dx, M, N, dt, ws=0, ws_bytes=0, stream=0) -> int:
     return lib().rr_softmax_bwd(y, dy, dx, M, N, dt, ws or None, ws_bytes, stream or None)
+
+
+def rmsnorm_bwd_raw(x, w, dy, rstd, dx, dw, M, N, dt, ws=0, ws_bytes=0, stream=0) -> int:
+    return lib().rr_rmsnorm_bwd(x, w, dy, rstd, dx, dw, M, N, dt, ws or None, ws_bytes,
+                                stream or None)
 
 
 def stream_copy_raw(src, dst, nbytes, stream=0) -> int:
@@ -265,6 +273,33 @@ def rr_softmax_bwd(y, dy, dx=None, ws=None, stream=None):
     _check(softmax_bwd_raw(y.data_ptr(), dy.data_ptr(), dx.data_ptr(), M, N, dt, wp, wb,
                            _stream(y, stream)), "rr_softmax_bwd")
     return dx
+
+
+def rr_rmsnorm_bwd(x, w, dy, rstd, dx=None, dw=None, ws=None, stream=None):
+    """RMSNorm backward from x [M, N], w [N], dy [M, N] and the forward's fp32 rstd [M];
+    returns (dx [M, N] of x's dtype, dw [N] fp32).  dx may be x or dy itself."""
+    torch = _torch()
+    M, N = x.shape if x.dim() == 2 else (None, None)
+    if M is None or not x.is_contiguous() or not x.is_cuda:
+        raise ValueError("expected a contiguous 2-D CUDA tensor [M, N]")
+    if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_contiguous():
+        raise ValueError("dy must be a contiguous tensor of x's shape and dtype")
+    if w.dtype != x.dtype or w.numel() != N or not w.is_contiguous():
+        raise ValueError("weight must be a contiguous [N] tensor of the input's dtype")
+    if rstd.dtype != torch.float32 or rstd.numel() != M or not rstd.is_contiguous():
+        raise ValueError("rstd must be a contiguous float32 [M] tensor")
+    if dx is None:
+        dx = torch.empty_like(x)
+    if dw is None:
+        dw = torch.empty(N, dtype=torch.float32, device=x.device)
+    dt = dtype_code(x)
+    if ws is None:
+        ws = workspace(RR_OP_RMSNORM_BWD, M, N, dt, x.device)
+    wp, wb = _ws_args(ws)
+    _check(rmsnorm_bwd_raw(x.data_ptr(), w.data_ptr(), dy.data_ptr(), rstd.data_ptr(),
+                           dx.data_ptr(), dw.data_ptr(), M, N, dt, wp, wb, _stream(x, stream)),
+           "rr_rmsnorm_bwd")
+    return dx, dw
 
 
 def rr_workspace_check(ws, stream=None) -> int:

@@ -60,6 +60,12 @@ bool partial_overlap(const void *a, const void *b, size_t n) {
     return pa < pb + n && pb < pa + n;
 }
 
+// [a, a + na) and [b, b + nb) share a byte.
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
 // Common checks of the matrix arguments.  Returns RR_OK and the matrix size in bytes.
 rr_status check_matrix(int64_t M, int64_t N, rr_dtype dt, size_t *bytes) {
     if (dt != RR_F32 && dt != RR_BF16) return RR_ERR_INVALID_ARGUMENT;
@@ -193,6 +199,31 @@ rr_status rr_softmax_bwd(const void *y, const void *dy, void *dx, int64_t M, int
     rr::LaunchArgs a;
     if ((st = launch_args(stream, &a)) != RR_OK) return st;
     return hip_status(rr::launch_softmax_bwd(p, dt, y, dy, dx, M, N, ws, a));
+}
+
+rr_status rr_rmsnorm_bwd(const void *x, const void *w, const void *dy, const float *rstd,
+                         void *dx, float *dw, int64_t M, int64_t N, rr_dtype dt, void *ws,
+                         size_t ws_bytes, hipStream_t stream) {
+    size_t bytes = 0;
+    rr_status st = check_matrix(M, N, dt, &bytes);
+    if (st != RR_OK) return st;
+    if (N < 1 || N > INT32_MAX || !dw) return RR_ERR_INVALID_ARGUMENT;
+    const size_t dw_bytes = (size_t)N * 4u;
+    if (M > 0) {
+        if (!x || !w || !dy || !rstd || !dx || partial_overlap(x, dx, bytes) ||
+            partial_overlap(dy, dx, bytes) || overlap(dw, dw_bytes, dx, bytes) ||
+            overlap(dw, dw_bytes, x, bytes) || overlap(dw, dw_bytes, dy, bytes))
+            return RR_ERR_INVALID_ARGUMENT;
+    }
+    const bool vec = M > 0 && aligned16(x) && aligned16(dy) && aligned16(dx) && aligned16(w) &&
+                     ((size_t)N * elem_size(dt)) % 16 == 0;
+    rr::Plan p;
+    st = plan_status(rr::make_plan(rr::kOpRmsnormBwd, dt, M, N, vec, &p));
+    if (st != RR_OK) return st;
+    if (M > 0 && (st = check_workspace(p, ws, ws_bytes)) != RR_OK) return st;
+    rr::LaunchArgs a;
+    if ((st = launch_args(stream, &a)) != RR_OK) return st;
+    return hip_status(rr::launch_rmsnorm_bwd(p, dt, x, w, dy, rstd, dx, dw, M, N, ws, a));
 }
 
 size_t rr_workspace_bytes(rr_op op, int64_t M, int64_t N, rr_dtype dt, int device) {

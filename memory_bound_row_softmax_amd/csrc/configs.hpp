@@ -38,6 +38,16 @@
     X(64, 256, 1) X(64, 256, 2) X(64, 256, 4) X(64, 256, 8) X(64, 256, 16)                  \
     X(64, 512, 1) X(64, 512, 2) X(64, 512, 4) X(64, 512, 8) X(64, 512, 16)
 
+// RMSNorm backward (persistent, see rmsnorm_bwd.hpp), named by (P, R, G): a lane
+// keeps x, dy (two rows in flight), its w slice and its dw partials, about 6P + 45
+// VGPRs, so P <= 32 on up to 512 lanes and P = 8 on 1024 lanes.
+#define RR_RMSBWD_CONFIGS(X)                                                                \
+    X(8, 16, 1) X(8, 32, 1) X(8, 64, 1) X(8, 128, 1) X(8, 256, 1) X(8, 512, 1) X(8, 1024, 1)  \
+    X(16, 16, 1) X(16, 32, 1) X(16, 64, 1) X(16, 128, 1) X(16, 256, 1) X(16, 512, 1)          \
+    X(32, 16, 1) X(32, 32, 1) X(32, 64, 1) X(32, 128, 1) X(32, 256, 1) X(32, 512, 1)          \
+    X(16, 512, 2) X(16, 512, 4) X(16, 512, 8) X(16, 512, 16)                                  \
+    X(32, 512, 2) X(32, 512, 4) X(32, 512, 8) X(32, 512, 16)
+
 #define RR_XENT_CONFIGS(X)                                                                  \
     X(16, 16) X(16, 32) X(16, 64) X(16, 128) X(16, 256) X(16, 512) X(16, 1024)              \
     X(32, 16) X(32, 32) X(32, 64) X(32, 128) X(32, 256) X(32, 512) X(32, 1024)
@@ -96,6 +106,15 @@ constexpr int stream_depth(int op, int P, int R) {
     const bool fits = (R < 1024 || P <= 16) && (op != 1 || P <= 32);
     return (RR_STREAM_DEPTH > 2 && fits) ? RR_STREAM_DEPTH : 2;
 }
+
+// RMSNorm backward: the per-element path keeps P <= 16.
+constexpr bool rmsbwd_config_enabled(bool vec, int P) { return vec || P <= 16; }
+
+// RMSNorm backward partial rows: at most kBwdMaxWorkgroups / G row groups, each
+// writing one fp32 partial row of dw; the column reduction first adds them in
+// slices (about kBwdReduceTarget workgroups in all), then adds the slices.
+constexpr int kBwdMaxWorkgroups = 1024;
+constexpr int kBwdReduceTarget = 512;  // workgroups of the first reduction pass
 
 // Threads per workgroup and rows per workgroup for a lane-group width R (block
 // kernels; a stream kernel's workgroup is its R lanes).

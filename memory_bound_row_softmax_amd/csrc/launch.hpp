@@ -27,6 +27,9 @@ hipError_t launch_xent_grad(const Plan &p, int dtype, const void *x, const int32
                             int64_t N, void *ws, const LaunchArgs &a);
 hipError_t launch_softmax_bwd(const Plan &p, int dtype, const void *y, const void *dy, void *dx,
                               int64_t M, int64_t N, void *ws, const LaunchArgs &a);
+hipError_t launch_rmsnorm_bwd(const Plan &p, int dtype, const void *x, const void *w,
+                              const void *dy, const float *rstd, void *dx, float *dw, int64_t M,
+                              int64_t N, void *ws, const LaunchArgs &a);
 hipError_t launch_copy(const void *src, void *dst, size_t bytes, const LaunchArgs &a);
 
 }  // namespace rr

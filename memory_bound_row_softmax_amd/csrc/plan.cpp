@@ -57,6 +57,23 @@ bool xent_config_exists(int P, int R) {
     return false;
 }
 
+bool rmsbwd_config_ok(int dtype, bool vec, int P, int R, int G) {
+    (void)dtype;
+#define RR_X(p, r, g) \
+    if (P == p && R == r && G == g) return rmsbwd_config_enabled(vec, p);
+    RR_RMSBWD_CONFIGS(RR_X)
+#undef RR_X
+    return false;
+}
+
+int rmsbwd_slices(int64_t parts, int64_t N) {
+    const int64_t tiles = (N + 1023) / 1024;  // 256 threads x 4 columns
+    int64_t s = (kBwdReduceTarget + tiles - 1) / tiles;
+    if (s > parts / 4) s = parts / 4;  // at least 4 rows per slice
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
 size_t grid_ws_bytes(int G, int64_t M) {
     int64_t groups = M < kMaxGroups ? M : kMaxGroups;
     if (groups < 1) groups = 1;
@@ -165,8 +182,63 @@ static void default_xent(int dtype, int64_t N, int *P, int *R) {
     *R = (int)r;
 }
 
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// RMSNorm backward: lanes and values per lane for the row, split over as few
+// workgroups as hold it.  Rows up to 16384 stay in one workgroup.
+static PlanResult plan_rmsnorm_bwd(int dtype, int64_t M, int64_t N, bool vec, Plan *out) {
+    const int fP = env_int("RR_FORCE_P"), fR = env_int("RR_FORCE_R"), fG = env_int("RR_FORCE_G");
+    int P, R, G = 1;
+    if (fP || fR || fG) {
+        P = fP ? fP : 16;
+        R = fR ? fR : 512;
+        G = fG ? fG : 1;
+    } else {
+        const int pmax = vec ? 32 : 16;
+        if (N <= 4096) {
+            P = 8;
+        } else if (N <= 8192 || pmax == 16) {
+            P = 16;
+        } else {
+            P = 32;
+        }
+        int64_t r = next_pow2((N + P - 1) / P);
+        if (r < 16) r = 16;
+        R = (int)(r > 512 ? 512 : r);
+        while ((int64_t)P * R * G < N && G < 16) G *= 2;
+    }
+    if (!rmsbwd_config_ok(dtype, vec, P, R, G)) return kPlanUnsupported;
+    Plan p;
+    p.vec = vec;
+    p.stream = true;
+    p.P = P;
+    p.R = R;
+    p.G = G;
+    p.max_n = (int64_t)P * R * G;
+    if (N > p.max_n) return kPlanUnsupported;
+    p.path = G > 1 ? kPathSplit : kPathStream;
+    p.block = G == 1 ? block_threads_for(R) : R;
+    p.rows_per_block = G == 1 ? rows_per_block_for(R) : 1;
+    const int64_t blocks = (M + p.rows_per_block - 1) / p.rows_per_block;
+    int64_t parts = kBwdMaxWorkgroups / G;
+    if (parts > blocks) parts = blocks;
+    if (parts < 1) parts = 1;
+    p.max_parts = (int)parts;
+    p.slices = rmsbwd_slices(parts, N);
+    const size_t exch = G > 1 ? align256(grid_ws_bytes(G, parts)) : 0;
+    p.part_off = exch;
+    p.slice_off = p.part_off + align256((size_t)parts * (size_t)N * 4u);
+    p.ws_bytes = p.slice_off + (p.slices > 1 ? align256((size_t)p.slices * (size_t)N * 4u) : 0);
+    *out = p;
+    return kPlanOk;
+}
+
 PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *out) {
     if (!out) return kPlanInvalid;
+    if (op == kOpRmsnormBwd) {
+        if ((dtype != kF32 && dtype != kBf16) || M < 0 || N < 1 || N > INT32_MAX) return kPlanInvalid;
+        return plan_rmsnorm_bwd(dtype, M, N, vec, out);
+    }
     if ((op != kOpSoftmax && op != kOpRmsnorm && op != kOpXent && op != kOpXentGrad &&
          op != kOpSoftmaxBwd) ||
         (dtype != kF32 && dtype != kBf16) || M < 0 || (M > 0 && N < 1))

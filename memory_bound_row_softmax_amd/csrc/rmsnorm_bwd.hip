@@ -1,0 +1,110 @@
+// rmsnorm_bwd.hip -- instantiates the RMSNorm backward kernels of the configuration
+// menu and launches the one the plan names, then the dw column reduction.
+#include "launch_util.hpp"
+#include "rmsnorm_bwd.hpp"
+
+namespace rr {
+namespace {
+
+template <class E, int P, int R, int G, bool VEC>
+hipError_t launch_cfg(const Plan &p, const void *x, const void *w, const void *dy,
+                      const float *rstd, void *dx, int64_t M, int64_t N, uint8_t *ws,
+                      int *parts, const LaunchArgs &a) {
+    auto kernel = rmsnorm_bwd_kernel<E, P, R, G, VEC>;
+    const int threads = bwd_threads(R, G);
+    int groups;
+    if constexpr (G == 1) {
+        // no workgroup waits for another: as many as fit at once, at most one per
+        // row block and at most the workspace's partial rows
+        int per_cu = 0;
+        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
+        if (e != hipSuccess) return e;
+        int64_t g = (int64_t)(per_cu > 0 ? per_cu : 1) * a.num_cus;
+        if (g > p.max_parts) g = p.max_parts;
+        groups = (int)g;
+    } else {
+        hipError_t e = cooperative_groups(kernel, threads, G, M, a, &groups);
+        if (e != hipSuccess) return e;
+        if (groups > p.max_parts) groups = p.max_parts - p.max_parts % (p.max_parts >= 8 ? 8 : 1);
+    }
+    *parts = groups;
+    const char *xp = static_cast<const char *>(x);
+    const char *wp = static_cast<const char *>(w);
+    const char *dyp = static_cast<const char *>(dy);
+    char *dxp = static_cast<char *>(dx);
+    float *part = reinterpret_cast<float *>(ws + p.part_off);
+    int n = (int)N;
+    int spin = a.spin_limit;
+    if constexpr (G == 1) {
+        hipLaunchKernelGGL(kernel, dim3(groups), dim3(threads), 0, a.stream, xp, wp, dyp, rstd,
+                           dxp, part, M, n, ws, groups, spin);
+        return hipGetLastError();
+    } else {
+        void *args[] = {&xp, &wp, &dyp, &rstd, &dxp, &part, &M, &n, &ws, &groups, &spin};
+        return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(kernel),
+                                          dim3(groups * G), dim3(threads), args, 0, a.stream);
+    }
+}
+
+template <class E, bool VEC>
+hipError_t dispatch(const Plan &p, const void *x, const void *w, const void *dy,
+                    const float *rstd, void *dx, int64_t M, int64_t N, uint8_t *ws, int *parts,
+                    const LaunchArgs &a) {
+#define RR_X(P_, R_, G_)                                                                 \
+    if constexpr (rmsbwd_config_enabled(VEC, P_))                                        \
+        if (p.P == P_ && p.R == R_ && p.G == G_)                                         \
+            return launch_cfg<E, P_, R_, G_, VEC>(p, x, w, dy, rstd, dx, M, N, ws, parts, a);
+    RR_RMSBWD_CONFIGS(RR_X)
+#undef RR_X
+    return hipErrorInvalidValue;
+}
+
+// dw = the sum of `parts` partial rows, in row order: first in slices (one pass
+// over all partial rows with enough workgroups to keep HBM busy), then the slices.
+hipError_t reduce_dw(const Plan &p, uint8_t *ws, int parts, int64_t N, float *dw,
+                     const LaunchArgs &a) {
+    const float *part = reinterpret_cast<const float *>(ws + p.part_off);
+    float *slice = reinterpret_cast<float *>(ws + p.slice_off);
+    const int n = (int)N;
+    const unsigned tiles = (unsigned)((N + 1023) / 1024);
+    const bool vec4 = N % 4 == 0;
+    auto pass = [&](const float *in, int rows, int per, int nslices, float *out) {
+        if (vec4)
+            hipLaunchKernelGGL(rmsnorm_dw_reduce<true>, dim3(tiles, (unsigned)nslices), dim3(256),
+                               0, a.stream, in, rows, per, n, out);
+        else
+            hipLaunchKernelGGL(rmsnorm_dw_reduce<false>, dim3(tiles, (unsigned)nslices), dim3(256),
+                               0, a.stream, in, rows, per, n, out);
+        return hipGetLastError();
+    };
+    int s = rmsbwd_slices(parts, N);
+    if (s > p.slices) s = p.slices;
+    if (s <= 1) return pass(part, parts, parts > 0 ? parts : 1, 1, dw);
+    const int per = (parts + s - 1) / s;
+    s = (parts + per - 1) / per;
+    hipError_t e = pass(part, parts, per, s, slice);
+    if (e != hipSuccess) return e;
+    return pass(slice, s, s, 1, dw);
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm_bwd(const Plan &p, int dtype, const void *x, const void *w,
+                              const void *dy, const float *rstd, void *dx, float *dw, int64_t M,
+                              int64_t N, void *ws, const LaunchArgs &a) {
+    uint8_t *wsb = static_cast<uint8_t *>(ws);
+    int parts = 0;
+    if (M > 0) {
+        hipError_t e;
+        if (dtype == kF32)
+            e = p.vec ? dispatch<F32, true>(p, x, w, dy, rstd, dx, M, N, wsb, &parts, a)
+                      : dispatch<F32, false>(p, x, w, dy, rstd, dx, M, N, wsb, &parts, a);
+        else
+            e = p.vec ? dispatch<BF16, true>(p, x, w, dy, rstd, dx, M, N, wsb, &parts, a)
+                      : dispatch<BF16, false>(p, x, w, dy, rstd, dx, M, N, wsb, &parts, a);
+        if (e != hipSuccess) return e;
+    }
+    return reduce_dw(p, wsb, parts, N, dw, a);
+}
+
+}  // namespace rr

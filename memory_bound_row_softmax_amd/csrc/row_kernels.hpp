@@ -111,6 +111,14 @@ struct RowCtx {
     float *bcast;   // LDS: merged split-row partials [0..1], "a wait timed out" flag [2]
     GroupRef g;
     int spin_limit;
+
+    // Slots for a row body with a single reduction.  A slot array may be written
+    // again only after a later barrier (waves_combine), so a persistent kernel
+    // alternates its two arrays from row to row: the barrier of row k + 1's
+    // reduction separates the last read of row k's slots from row k + 2's writes.
+    __device__ __forceinline__ float *one_reduction_slots() const {
+        return (it & 1) ? red_b : red_a;
+    }
 };
 
 // ---------------------------------------------------------------- softmax
@@ -298,7 +306,7 @@ __device__ __forceinline__ void rmsnorm_finish(float *v, const Weight &w, RowVie
     // sum of squares, then t = x * w in place; y = t * r once r is known
     float q = tree_sum_squares<P>(v);
     w.apply(v, c.l);
-    q = row_reduce<R>(q, c.red_a, c.l, OpSum{});
+    q = row_reduce<R>(q, c.one_reduction_slots(), c.l, OpSum{});
     if constexpr (G > 1) {
         exchange_pairs<G>(c.g, c.member, c.it, q, 0.0f, c.spin_limit, c.bcast, MergeSum{});
         q = c.bcast[0];
@@ -339,10 +347,10 @@ __global__ void __launch_bounds__(R)
     static_assert(R >= 64, "one row per workgroup");
     constexpr int C = P / E::VPC;
     constexpr int W = R / 64;
-    __shared__ float red[W];
+    __shared__ float red[2][W];
     __shared__ float bcast[3];
     __shared__ float4 wslot[(P / 4) * R];
-    RowCtx c{N, (int)threadIdx.x, 0, 0, true, red, nullptr, bcast, GroupRef{}, spin_limit};
+    RowCtx c{N, (int)threadIdx.x, 0, 0, true, red[0], red[1], bcast, GroupRef{}, spin_limit};
     int group = blockIdx.x;
     if constexpr (G > 1) {
         group_of_block<G>(groups, &group, &c.member);

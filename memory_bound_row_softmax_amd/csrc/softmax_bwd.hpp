@@ -33,7 +33,7 @@ __device__ __forceinline__ void softmax_bwd_finish(float *a, float *b, RowView d
     const int chunk0 = c.member * C * R;
     if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.N, 0.0f, a);
     float t = tree_dot<P>(a, b);
-    t = row_reduce<R>(t, c.red_a, c.l, OpSum{});
+    t = row_reduce<R>(t, c.one_reduction_slots(), c.l, OpSum{});
     if constexpr (G > 1) {
         exchange_pairs<G>(c.g, c.member, c.it, t, 0.0f, c.spin_limit, c.bcast, MergeSum{});
         t = c.bcast[0];
@@ -70,9 +70,9 @@ __global__ void __launch_bounds__(R)
     static_assert(R >= 64, "one row per workgroup");
     constexpr int C = P / E::VPC;
     constexpr int W = R / 64;
-    __shared__ float red[W];
+    __shared__ float red[2][W];
     __shared__ float bcast[3];
-    RowCtx c{N, (int)threadIdx.x, 0, 0, true, red, nullptr, bcast, GroupRef{}, spin_limit};
+    RowCtx c{N, (int)threadIdx.x, 0, 0, true, red[0], red[1], bcast, GroupRef{}, spin_limit};
     int group = blockIdx.x;
     if constexpr (G > 1) {
         group_of_block<G>(groups, &group, &c.member);

@@ -158,3 +158,39 @@ def parity_softmax_bwd(y_np, dy_np, dtype, what, inplace=None):
     torch.cuda.synchronize()
     ref = oracle.softmax_backward(y_np, dy_np)
     return check_grad(from_dev(dx), ref, softmax_bwd_scale(y_np, dy_np, dtype), dtype, what)
+
+
+def rmsnorm_bwd_inputs(M, N, dtype, eps=1e-6):
+    """x ~ N(0, 1), w ~ U(0.5, 1.5), dy ~ N(0, 1) in the dtype; rstd is the forward's
+    r of each row (oracle, rounded to fp32)."""
+    import synth
+
+    x = synth.normal(M, N, dtype=dtype)
+    w = synth.uniform(1, N, lo=0.5, hi=1.5, dtype=dtype).reshape(N)
+    dy = synth.normal(M, N, dtype=dtype, stream=synth.STREAM_DY)
+    _, r = oracle.rmsnorm(x, w, eps, want_rstd=True)
+    return x, w, dy, r.astype(np.float32)
+
+
+def rmsnorm_bwd_scales(x_np, w_np, dy_np, rstd, dtype):
+    """Per-element sizes of the terms of dx, and per-column of dw."""
+    x, w, dy = _dec(x_np, dtype), _dec(w_np, dtype), _dec(dy_np, dtype)
+    r = rstd.astype(np.float64)[:, None]
+    N = x.shape[1]
+    cabs = np.abs(dy * w[None, :] * x).sum(axis=1, keepdims=True)
+    sdx = r * np.abs(w[None, :] * dy) + r ** 3 * np.abs(x) * cabs / N
+    sdw = np.abs(dy * x * r).sum(axis=0)
+    return sdx, sdw
+
+
+def parity_rmsnorm_bwd(x_np, w_np, dy_np, rstd, dtype, what, inplace=None, ws=None):
+    x, w, dy = to_dev(x_np, dtype), to_dev(w_np, dtype), to_dev(dy_np, dtype)
+    r = torch.from_numpy(np.ascontiguousarray(rstd, dtype=np.float32)).to(DEV)
+    dx = {"x": x, "dy": dy}.get(inplace)
+    dx, dw = rr.rr_rmsnorm_bwd(x, w, dy, r, dx=dx, ws=ws)
+    torch.cuda.synchronize()
+    ref_dx, ref_dw = oracle.rmsnorm_backward(x_np, w_np, dy_np, rstd)
+    sdx, sdw = rmsnorm_bwd_scales(x_np, w_np, dy_np, rstd, dtype)
+    check_grad(from_dev(dx), ref_dx, sdx, dtype, what + " dx")
+    check_grad(dw.cpu().numpy(), ref_dw, sdw, "f32", what + " dw")
+    return dx, dw

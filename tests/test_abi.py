@@ -93,6 +93,12 @@ def test_zero_rows_is_a_no_op():
     ("smbwd null dx", lambda: rr.softmax_bwd_raw(A, C, 0, 4, 8, rr.RR_F32)),
     ("smbwd overlap y", lambda: rr.softmax_bwd_raw(A, C, A + 16, 4, 8, rr.RR_F32)),
     ("smbwd overlap dy", lambda: rr.softmax_bwd_raw(A, C, C - 16, 4, 8, rr.RR_F32)),
+    ("rmsbwd null rstd", lambda: rr.rmsnorm_bwd_raw(A, C, A + 512, 0, B, C + 64, 4, 8, rr.RR_F32)),
+    ("rmsbwd null dw", lambda: rr.rmsnorm_bwd_raw(A, C, A + 512, C + 64, B, 0, 4, 8, rr.RR_F32)),
+    ("rmsbwd dw on dx", lambda: rr.rmsnorm_bwd_raw(A, C, A + 512, C + 64, B, B + 8, 4, 8,
+                                                   rr.RR_F32)),
+    ("rmsbwd dx overlap", lambda: rr.rmsnorm_bwd_raw(A, C, A + 512, C + 64, A + 4, C + 256, 4, 8,
+                                                     rr.RR_F32)),
     ("size overflow", lambda: rr.softmax_fwd_raw(A, B, 1 << 62, 1 << 20, rr.RR_F32)),
     ("copy misaligned", lambda: rr.stream_copy_raw(A + 4, B, 64)),
     ("copy odd size", lambda: rr.stream_copy_raw(A, B, 40)),

@@ -1,6 +1,11 @@
 """GPU parity of the backward passes: the HIP kernels (through the C ABI) against
 the double-precision oracle, element by element, on seeded inputs.
 
+RMSNorm backward: dx and dw from x, w, dy and the forward's rstd (the oracle's,
+rounded to fp32); dx within the bound with scale r|w_j dy_j| + r^3 |x_j|
+sum_k |dy_k w_k x_k| / N, dw (fp32, summed over the rows through per-workgroup
+partial rows) within relative 1e-5 of sum_i |dy_ij x_ij r_i|.
+
 Softmax backward: dx from the forward output y (the oracle's softmax of a seeded
 row, rounded to the dtype) and dy ~ N(0, 1), within the cancellation-aware bound
 with scale y_j * (|dy_j| + sum_k |y_k dy_k|).
@@ -17,8 +22,9 @@ import torch
 import memory_bound_row_softmax_amd as rr
 import oracle
 import synth
-from _gpu import (DEV, forced, from_dev, parity_softmax_bwd, parity_xent_grad, run_xent_grad, say,
-                  softmax_bwd_inputs, softmax_bwd_scale, to_dev, xent_grad_scale)
+from _gpu import (DEV, forced, from_dev, parity_rmsnorm_bwd, parity_softmax_bwd, parity_xent_grad,
+                  rmsnorm_bwd_inputs, rmsnorm_bwd_scales, run_xent_grad, say, softmax_bwd_inputs,
+                  softmax_bwd_scale, to_dev, xent_grad_scale)
 from _verify import check_f32, check_grad
 
 pytestmark = pytest.mark.gpu
@@ -257,3 +263,117 @@ def test_softmax_bwd_split_rows_are_deterministic(dtype):
     check_grad(from_dev(outs[0][torch.from_numpy(rows).to(DEV)]),
                oracle.softmax_backward(y_np[rows], dy_np[rows]),
                softmax_bwd_scale(y_np[rows], dy_np[rows], dtype), dtype, "split rows sampled")
+
+
+# ------------------------------------------------------------- RMSNorm backward
+
+RMS_SHAPES = SHAPES + [(1000, 256), (3000, 4096), (4100, 64)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N", RMS_SHAPES)
+def test_rmsnorm_bwd(M, N, dtype):
+    say("rmsnorm bwd", dtype, M, N)
+    x, w, dy, r = rmsnorm_bwd_inputs(M, N, dtype)
+    parity_rmsnorm_bwd(x, w, dy, r, dtype, f"rmsnorm bwd {dtype} {M}x{N}")
+
+
+RMS_FORCED = [(8, 16, 1, 300, 100), (8, 1024, 1, 40, 8000), (16, 64, 1, 777, 1000),
+              (32, 128, 1, 65, 4000), (16, 512, 2, 300, 9000), (16, 512, 16, 5, 100000),
+              (32, 512, 2, 600, 20000), (32, 512, 8, 50, 131072), (32, 512, 16, 3, 200000)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("P,R,G,M,N", RMS_FORCED)
+def test_rmsnorm_bwd_forced_plans(P, R, G, M, N, dtype):
+    with forced(P, R, G):
+        say("rmsnorm bwd forced", P, R, G, dtype, M, N)
+        x, w, dy, r = rmsnorm_bwd_inputs(M, N, dtype)
+        parity_rmsnorm_bwd(x, w, dy, r, dtype, f"rmsnorm bwd forced {P},{R},{G}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("inplace", ["x", "dy"])
+def test_rmsnorm_bwd_in_place(inplace, dtype):
+    for M, N in ((64, 1024), (8, 131072)):
+        say("rmsnorm bwd in place", inplace, dtype, M, N)
+        x, w, dy, r = rmsnorm_bwd_inputs(M, N, dtype)
+        parity_rmsnorm_bwd(x, w, dy, r, dtype, f"rmsnorm bwd in place {inplace}", inplace=inplace)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("N", [64, 1000, 4096, 40000, 131072])
+def test_rmsnorm_bwd_unaligned(N, dtype):
+    M = 6
+    x_np, w_np, dy_np, r_np = rmsnorm_bwd_inputs(M, N, dtype)
+    pad = lambda a, shape: to_dev(np.concatenate([np.zeros(1, a.dtype), a.ravel()]), dtype)[1:].view(*shape)
+    x, dy, w = pad(x_np, (M, N)), pad(dy_np, (M, N)), pad(w_np, (N,))
+    dx = torch.empty(M * N + 1, dtype=x.dtype, device=DEV)[1:].view(M, N)
+    assert x.data_ptr() % 16 != 0
+    say("rmsnorm bwd unaligned", dtype, N)
+    dx, dw = rr.rr_rmsnorm_bwd(x, w, dy, torch.from_numpy(r_np).to(DEV), dx=dx)
+    torch.cuda.synchronize()
+    ref_dx, ref_dw = oracle.rmsnorm_backward(x_np, w_np, dy_np, r_np)
+    sdx, sdw = rmsnorm_bwd_scales(x_np, w_np, dy_np, r_np, dtype)
+    check_grad(from_dev(dx), ref_dx, sdx, dtype, "unaligned dx")
+    check_grad(dw.cpu().numpy(), ref_dw, sdw, "f32", "unaligned dw")
+
+
+def test_rmsnorm_bwd_no_rows_gives_zero_dw():
+    say("rmsnorm bwd M = 0")
+    dw = torch.full((777,), 5.0, device=DEV)
+    x = torch.empty((0, 777), device=DEV)
+    rr.rr_rmsnorm_bwd(x, torch.ones(777, device=DEV), x, torch.empty(0, device=DEV),
+                      dx=x, dw=dw)
+    torch.cuda.synchronize()
+    assert int(dw.count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_rmsnorm_bwd_is_deterministic(dtype):
+    code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
+    for M, N in ((5000, 4096), (300, 262144)):
+        x_np, w_np, dy_np, r_np = rmsnorm_bwd_inputs(M, N, dtype)
+        x, w, dy = to_dev(x_np, dtype), to_dev(w_np, dtype), to_dev(dy_np, dtype)
+        r = torch.from_numpy(r_np).to(DEV)
+        ws = rr.workspace(rr.RR_OP_RMSNORM_BWD, M, N, code, DEV)
+        outs = []
+        for i in range(3):
+            say("rmsnorm bwd repeat", i, dtype, M, N)
+            outs.append(rr.rr_rmsnorm_bwd(x, w, dy, r, ws=ws))
+            torch.cuda.synchronize()
+        for o in outs[1:]:
+            assert torch.equal(outs[0][0], o[0]) and torch.equal(outs[0][1], o[1])
+        p = rr.rr_plan_query(rr.RR_OP_RMSNORM_BWD, M, N, code)
+        if p["groups_per_row"] > 1:
+            assert rr.rr_workspace_check(ws) == rr.RR_OK
+        # dw against the oracle on every column, dx on sampled rows
+        rows = np.arange(0, M, max(1, M // 16))
+        ref_dx, _ = oracle.rmsnorm_backward(x_np[rows], w_np, dy_np[rows], r_np[rows])
+        _, ref_dw = oracle.rmsnorm_backward(x_np, w_np, dy_np, r_np)
+        sdx, _ = rmsnorm_bwd_scales(x_np[rows], w_np, dy_np[rows], r_np[rows], dtype)
+        _, sdw = rmsnorm_bwd_scales(x_np, w_np, dy_np, r_np, dtype)
+        check_grad(from_dev(outs[0][0][torch.from_numpy(rows).to(DEV)]), ref_dx, sdx, dtype, "dx")
+        check_grad(outs[0][1].cpu().numpy(), ref_dw, sdw, "f32", "dw")
+
+
+def test_rmsnorm_bwd_golden_cases():
+    import json
+    import os
+    say("rmsnorm bwd golden")
+    path = os.path.join(os.path.dirname(__file__), "golden", "tiny_cases.json")
+    for c in json.load(open(path))["cases"]:
+        if c["op"] != "rmsnorm_bwd":
+            continue
+        x = np.array([[float.fromhex(v) for v in r] for r in c["x"]], dtype=np.float32)
+        w = np.array([float.fromhex(v) for v in c["w"]], dtype=np.float32)
+        dy = np.array([[float.fromhex(v) for v in r] for r in c["dy"]], dtype=np.float32)
+        r = np.array([float.fromhex(v) for v in c["rstd"]], dtype=np.float32)
+        dx, dw = rr.rr_rmsnorm_bwd(to_dev(x, "f32"), to_dev(w, "f32"), to_dev(dy, "f32"),
+                                   torch.from_numpy(r).to(DEV))
+        torch.cuda.synchronize()
+        sdx, sdw = rmsnorm_bwd_scales(x, w, dy, r, "f32")
+        check_grad(dx.cpu().numpy(), np.array([[float(v) for v in q] for q in c["dx"]]), sdx,
+                   "f32", c["name"] + " dx")
+        check_grad(dw.cpu().numpy(), np.array([float(v) for v in c["dw"]]), sdw, "f32",
+                   c["name"] + " dw")

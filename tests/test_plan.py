@@ -130,3 +130,28 @@ def test_workspace_covers_the_element_path():
             need = rr.workspace_bytes(op, 6, N, rr.RR_F32)
             for vec in (True, False):
                 assert rr.rr_plan_query(op, 6, N, rr.RR_F32, vec)["ws_bytes"] <= need
+
+
+@pytest.mark.parametrize("dt", (rr.RR_F32, rr.RR_BF16))
+@pytest.mark.parametrize("vec", (True, False))
+def test_rmsnorm_bwd_plans(dt, vec):
+    """Persistent kernels: one workgroup per row up to 16384 elements, then split;
+    the workspace holds the exchange area, one fp32 partial row per row group and
+    the reduction slices."""
+    for N in NS:
+        lim = 262144 if vec else 131072
+        if N > lim:
+            with pytest.raises(rr.RRError):
+                rr.rr_plan_query(rr.RR_OP_RMSNORM_BWD, 16384, N, dt, vec)
+            continue
+        p = rr.rr_plan_query(rr.RR_OP_RMSNORM_BWD, 16384, N, dt, vec)
+        P, R, G = p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]
+        assert P * R * G == p["max_n"] >= N and P in (8, 16, 32) and (vec or P <= 16)
+        assert p["path"] == (1 if G > 1 else 3)
+        assert G == 1 or (N > 8192 and (G // 2) * P * R < N)
+        assert p["rows_per_block"] == (max(256, R) // R if G == 1 else 1)
+        parts = min(1024 // G, -(-16384 // p["rows_per_block"]))
+        assert p["ws_bytes"] >= parts * N * 4
+    # a handful of rows: as many partial rows as row blocks
+    p = rr.rr_plan_query(rr.RR_OP_RMSNORM_BWD, 3, 4096, dt, vec)
+    assert p["ws_bytes"] >= 3 * 4096 * 4 and p["ws_bytes"] < 16 * 4096 * 4

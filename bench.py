@@ -62,6 +62,10 @@ def algorithmic_bytes(w) -> int:
         return w.M * w.N * 2 * s + w.N * s
     if w.op == "xent_grad":  # logits in, gradient out; labels, dloss in; loss, lse out
         return w.M * w.N * 2 * s + 16 * w.M
+    if w.op == "softmax_bwd":  # y, dy in; dx out
+        return w.M * w.N * 3 * s
+    if w.op == "rmsnorm_bwd":  # x, dy in; dx out; w, rstd in; dw (fp32) out
+        return w.M * w.N * 3 * s + w.N * s + 4 * w.M + 4 * w.N
     return w.M * w.N * s + 12 * w.M
 
 
@@ -93,6 +97,8 @@ class Runner:
         s = esize(w.dtype)
         in_bytes = w.M * w.N * s
         out_bytes = in_bytes if w.op != "xent" else 8 * w.M
+        if w.op in ("softmax_bwd", "rmsnorm_bwd"):
+            in_bytes *= 2  # two input matrices
         has_rows = w.op in ("xent", "xent_grad")  # per-row labels and losses
         self.sets = max(1, min(16, math.ceil(min_rotation_bytes / (in_bytes + out_bytes))))
         tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
@@ -120,12 +126,36 @@ class Runner:
             self.dloss = torch.from_numpy(W.dloss_rows(w)).to(device)
         if w.op != "xent":
             self.y = [torch.empty_like(x0) for _ in range(self.sets)]
-        if w.op == "rmsnorm":
+        def tile_rows(gen):
+            """A device [M, N] matrix from `gen(nrows)` host rows repeated down it."""
+            a = gen(gen_rows)
+            h = torch.from_numpy(a if w.dtype == "f32" else a.view(np.int16)).to(device)
+            t = torch.empty((w.M, w.N), dtype=h.dtype, device=device)
+            for r0 in range(0, w.M, gen_rows):
+                r1 = min(w.M, r0 + gen_rows)
+                t[r0:r1].copy_(h[: r1 - r0])
+            return t.view(tdt) if w.dtype == "bf16" else t
+
+        if w.op in ("rmsnorm", "rmsnorm_bwd"):
             wn = W.weight(w)
             wt = torch.from_numpy(wn if w.dtype == "f32" else wn.view(np.int16)).to(device)
             self.weight = wt.view(tdt) if w.dtype == "bf16" else wt
+        if w.op in ("softmax_bwd", "rmsnorm_bwd"):
+            # the backward's second input, and the forward outputs it takes (from the
+            # library's own forward kernels: these are bench inputs, not references)
+            dy0 = tile_rows(lambda n: W.dy_rows(w, nrows=n))
+            self.dy = [dy0] + [dy0.clone() for _ in range(self.sets - 1)]
+            if w.op == "softmax_bwd":
+                for t in self.x:
+                    rr.rr_softmax_fwd(t, t)
+            else:
+                self.rstd = torch.empty(w.M, dtype=torch.float32, device=device)
+                rr.rr_rmsnorm_fwd(x0, self.weight, w.eps, y=self.y[0], rstd=self.rstd)
+                self.dw = torch.empty(w.N, dtype=torch.float32, device=device)
+            torch.cuda.synchronize()
         op = {"softmax": rr.RR_OP_SOFTMAX, "rmsnorm": rr.RR_OP_RMSNORM, "xent": rr.RR_OP_XENT,
-              "xent_grad": rr.RR_OP_XENT_GRAD}[w.op]
+              "xent_grad": rr.RR_OP_XENT_GRAD, "softmax_bwd": rr.RR_OP_SOFTMAX_BWD,
+              "rmsnorm_bwd": rr.RR_OP_RMSNORM_BWD}[w.op]
         self.op = op
         self.ws = rr.workspace(op, w.M, w.N, self.dt, device)
         self.wsp = self.ws.data_ptr() if self.ws is not None else 0
@@ -141,7 +171,9 @@ class Runner:
             self.gp = self.dloss.data_ptr()
         if w.op != "xent":
             self.yp = [t.data_ptr() for t in self.y]
-        self.wp = self.weight.data_ptr() if w.op == "rmsnorm" else 0
+        self.wp = self.weight.data_ptr() if w.op in ("rmsnorm", "rmsnorm_bwd") else 0
+        if w.op in ("softmax_bwd", "rmsnorm_bwd"):
+            self.dyp = [t.data_ptr() for t in self.dy]
         self.copy_dst = None
 
     def launch(self, k: int) -> int:
@@ -151,6 +183,13 @@ class Runner:
                                       self.sp)
         if w.op == "rmsnorm":
             return rr.rmsnorm_fwd_raw(self.xp[i], self.wp, self.yp[i], 0, w.M, w.N, self.dt, w.eps,
+                                      self.wsp, self.wsb, self.sp)
+        if w.op == "softmax_bwd":
+            return rr.softmax_bwd_raw(self.xp[i], self.dyp[i], self.yp[i], w.M, w.N, self.dt,
+                                      self.wsp, self.wsb, self.sp)
+        if w.op == "rmsnorm_bwd":
+            return rr.rmsnorm_bwd_raw(self.xp[i], self.wp, self.dyp[i], self.rstd.data_ptr(),
+                                      self.yp[i], self.dw.data_ptr(), w.M, w.N, self.dt,
                                       self.wsp, self.wsb, self.sp)
         if w.op == "xent_grad":
             return rr.cross_entropy_fwd_bwd_raw(self.xp[i], self.labp, self.gp, self.lp[i],
@@ -194,8 +233,12 @@ class Runner:
 
 
 def cpu_baseline(w, seconds: float):
-    """The oracle, single-threaded, on the first rows of the same workload."""
+    """The oracle, single-threaded, on the first rows of the same workload (for a
+    backward pass, only the backward call is timed)."""
+    import numpy as np
+
     import oracle
+    import synth
     from synth import workloads as W
 
     per_row = algorithmic_bytes(w) / w.M
@@ -209,6 +252,18 @@ def cpu_baseline(w, seconds: float):
             oracle.rmsnorm(x, W.weight(w), w.eps)
         elif w.op == "xent_grad":
             oracle.cross_entropy_grad(x, W.label_rows(w, nrows=rows), W.dloss_rows(w, nrows=rows))
+        elif w.op == "softmax_bwd":
+            y = oracle.softmax(x).astype(np.float32)
+            y = y if w.dtype == "f32" else synth.f32_to_bf16(y)
+            dy = W.dy_rows(w, nrows=rows)
+            t0 = time.perf_counter()
+            oracle.softmax_backward(y, dy)
+        elif w.op == "rmsnorm_bwd":
+            wt = W.weight(w)
+            _, r = oracle.rmsnorm(x, wt, w.eps, want_rstd=True)
+            dy = W.dy_rows(w, nrows=rows)
+            t0 = time.perf_counter()
+            oracle.rmsnorm_backward(x, wt, dy, r.astype(np.float32))
         else:
             oracle.cross_entropy(x, W.label_rows(w, nrows=rows))
         return time.perf_counter() - t0

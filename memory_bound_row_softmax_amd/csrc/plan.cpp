@@ -66,10 +66,15 @@ bool rmsbwd_config_ok(int dtype, bool vec, int P, int R, int G) {
     return false;
 }
 
+// About sqrt(parts) slices (both passes then read about sqrt(parts) rows per
+// thread), more when there are few column tiles, so that the first pass has
+// enough workgroups; at least 8 rows per slice.
 int rmsbwd_slices(int64_t parts, int64_t N) {
     const int64_t tiles = (N + 1023) / 1024;  // 256 threads x 4 columns
-    int64_t s = (kBwdReduceTarget + tiles - 1) / tiles;
-    if (s > parts / 4) s = parts / 4;  // at least 4 rows per slice
+    int64_t s = 1;
+    while (s * s < parts) s *= 2;
+    while (s * tiles < kBwdReduceTarget / 4 && s * 16 <= parts) s *= 2;
+    if (s > parts / 8) s = parts / 8;
     if (s < 1) s = 1;
     return (int)s;
 }

@@ -197,29 +197,47 @@ __global__ void __launch_bounds__(bwd_threads(R, G))
 
 // dw partial sums: out[s][j] = sum of rows s * per .. min(rows, (s + 1) * per) - 1 of
 // `in` (rows x N fp32), added in row order.  One thread per 4 columns; `in` and
-// `out` are 16-byte aligned and N is a multiple of 4 when vec4.
+// `out` are 16-byte aligned and N is a multiple of 4 when VEC4.  Eight rows are
+// loaded before they are added (still in row order), so eight loads are in flight.
+template <bool VEC4>
+__device__ __forceinline__ void dw_load4(const float *p, int col, int N, float *v) {
+    if constexpr (VEC4) {
+        const float4 u = *reinterpret_cast<const float4 *>(p);
+        v[0] = u.x;
+        v[1] = u.y;
+        v[2] = u.z;
+        v[3] = u.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (col + e < N) ? p[e] : 0.0f;
+    }
+}
+
 template <bool VEC4>
 __global__ void __launch_bounds__(256)
     rmsnorm_dw_reduce(const float *in, int rows, int per, int N, float *out) {
+    constexpr int U = 8;
     const int s = blockIdx.y;
     const int col = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (col >= N) return;
     const int r0 = s * per;
     const int r1 = (r0 + per < rows) ? r0 + per : rows;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int r = r0; r < r1; ++r) {
-        const float *p = in + (int64_t)r * N + col;
-        if constexpr (VEC4) {
-            const float4 u = *reinterpret_cast<const float4 *>(p);
-            acc[0] += u.x;
-            acc[1] += u.y;
-            acc[2] += u.z;
-            acc[3] += u.w;
-        } else {
+    int r = r0;
+    for (; r + U <= r1; r += U) {
+        float v[U][4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (col + e < N) acc[e] += p[e];
-        }
+        for (int u = 0; u < U; ++u) dw_load4<VEC4>(in + (int64_t)(r + u) * N + col, col, N, v[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] += v[u][e];
+    }
+    for (; r < r1; ++r) {
+        float v[4];
+        dw_load4<VEC4>(in + (int64_t)r * N + col, col, N, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += v[e];
     }
     float *o = out + (int64_t)s * N + col;
 #pragma unroll

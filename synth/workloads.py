@@ -24,7 +24,7 @@ RMSNORM_EPS = 1e-6
 @dataclass(frozen=True)
 class Workload:
     name: str
-    op: str          # "softmax" | "rmsnorm" | "xent" | "xent_grad"
+    op: str          # "softmax" | "rmsnorm" | "xent" | "xent_grad" | "softmax_bwd" | "rmsnorm_bwd"
     dtype: str       # "f32" | "bf16"
     M: int
     N: int
@@ -43,10 +43,18 @@ SOFTMAX_SPIKY = Workload("softmax_f32_16384x131072_spiky", "softmax", "f32", 163
 FIXED = [SOFTMAX_SMALL, RMSNORM_MAIN, XENT_VOCAB, SOFTMAX_SPIKY]
 
 # Backward passes (training): the cross-entropy forward fused with its gradient
-# on the vocab-like shape above and on a bf16 32K vocabulary.  Per-row upstream
-# gradients dloss ~ U(0.5, 1.5).
+# on the vocab-like shape above and on a bf16 32K vocabulary (per-row upstream
+# gradients dloss ~ U(0.5, 1.5)); the softmax backward from the softmax of
+# x ~ N(0, sigma=2) with dy ~ N(0, 1); the RMSNorm backward at the forward's
+# shape and a wider fp32 one, x and w as for the forward, dy ~ N(0, 1), rstd from
+# the forward.
 BACKWARD = [Workload("xentgrad_f32_8192x131072", "xent_grad", "f32", 8192, 131072, sigma=2.0),
-            Workload("xentgrad_bf16_16384x32768", "xent_grad", "bf16", 16384, 32768, sigma=2.0)]
+            Workload("xentgrad_bf16_16384x32768", "xent_grad", "bf16", 16384, 32768, sigma=2.0),
+            Workload("softmaxbwd_f32_16384x4096", "softmax_bwd", "f32", 16384, 4096, sigma=2.0),
+            Workload("softmaxbwd_bf16_16384x32768", "softmax_bwd", "bf16", 16384, 32768,
+                     sigma=2.0),
+            Workload("rmsnormbwd_bf16_16384x4096", "rmsnorm_bwd", "bf16", 16384, 4096),
+            Workload("rmsnormbwd_f32_16384x16384", "rmsnorm_bwd", "f32", 16384, 16384)]
 
 SWEEP_M = (8192, 16384, 32768)
 SWEEP_N = (256, 1024, 4096, 16384, 65536, 262144)
@@ -96,3 +104,9 @@ def dloss_rows(w: Workload, *, seed=SEED, row0=0, nrows=None) -> np.ndarray:
     """Per-row upstream gradient of the loss, U(0.5, 1.5) as float32."""
     M = w.M if nrows is None else nrows
     return uniform(1, M, lo=0.5, hi=1.5, seed=seed, stream=STREAM_DLOSS, row0=row0).reshape(M)
+
+
+def dy_rows(w: Workload, *, seed=SEED, row0=0, nrows=None) -> np.ndarray:
+    """Upstream gradient of a backward pass, N(0, 1) in the input dtype."""
+    M = w.M if nrows is None else nrows
+    return normal(M, w.N, dtype=w.dtype, seed=seed, stream=STREAM_DY, row0=row0)

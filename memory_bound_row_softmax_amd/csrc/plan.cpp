@@ -118,8 +118,8 @@ struct Choice {
     int P, R, G;
 };
 constexpr int kTunedN[8] = {256, 1024, 4096, 16384, 32768, 65536, 131072, 262144};
-//                      [op: softmax, rmsnorm, softmax backward][dtype: f32, bf16][N bucket]
-static const Choice kTuned[3][2][8] = {
+//   [op: softmax, rmsnorm, softmax backward, cross-entropy gradient][dtype: f32, bf16][N bucket]
+static const Choice kTuned[4][2][8] = {
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {true, 64, 512, 1},
       {true, 16, 1024, 2}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 16, 256, 1}, {false, 64, 256, 1},
@@ -129,10 +129,16 @@ static const Choice kTuned[3][2][8] = {
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {true, 32, 1024, 1},
       {false, 64, 512, 1}, {true, 32, 1024, 2}, {true, 64, 512, 4}, {true, 64, 512, 8}}},
     // softmax backward (y and dy both held: at most 32 values per lane in a stream kernel)
-    {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 16, 1024, 1},
-      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16}},
-     {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 16, 256, 1}, {false, 16, 1024, 1},
+    {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 16, 256, 1}, {false, 32, 1024, 1},
+      {false, 32, 1024, 1}, {true, 16, 1024, 4}, {true, 16, 1024, 8}, {true, 32, 512, 16}},
+     {{false, 8, 32, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 16, 1024, 1},
       {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16}}},
+    // cross-entropy forward fused with its gradient (the softmax kernels; block kernels
+    // hold longer rows here than for the softmax)
+    {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {true, 16, 1024, 1},
+      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 64, 512, 8}},
+     {{false, 16, 16, 1}, {false, 64, 16, 1}, {false, 16, 256, 1}, {false, 32, 512, 1},
+      {false, 64, 512, 1}, {false, 64, 1024, 1}, {true, 64, 512, 4}, {true, 32, 1024, 8}}},
 };
 
 static bool try_choice(int op, int dtype, bool vec, int64_t N, Choice c, Plan *p) {
@@ -153,8 +159,8 @@ static bool try_choice(int op, int dtype, bool vec, int64_t N, Choice c, Plan *p
 }
 
 static bool default_row(int op, int dtype, bool vec, int64_t N, Plan *p) {
-    // the cross-entropy gradient runs the softmax kernels: softmax's measurements
-    const int o = op == kOpRmsnorm ? 1 : op == kOpSoftmaxBwd ? 2 : 0, d = dtype == kBf16 ? 1 : 0;
+    const int o = op == kOpRmsnorm ? 1 : op == kOpSoftmaxBwd ? 2 : op == kOpXentGrad ? 3 : 0;
+    const int d = dtype == kBf16 ? 1 : 0;
     int k = 0;
     while (k < 7 && kTunedN[k] < N) ++k;
     if (N <= kTunedN[7]) {
@@ -163,6 +169,11 @@ static bool default_row(int op, int dtype, bool vec, int64_t N, Plan *p) {
         // choice of the bucket below, widened to the row.
         if (c.stream && k > 0 && 2 * N < (int64_t)c.P * c.R) c = kTuned[o][d][k - 1];
         if (try_choice(op, dtype, vec, N, c, p)) return true;
+        // a block choice the per-element path does not have: fewer values per lane
+        for (Choice b = c; !b.stream && b.P > 8;) {
+            b.P /= 2;
+            if (try_choice(op, dtype, vec, N, b, p)) return true;
+        }
     }
     // Past the table, or a configuration the per-element path does not have:
     // the first stream configuration that holds the row with the fewest workgroups.
@@ -189,8 +200,20 @@ static void default_xent(int dtype, int64_t N, int *P, int *R) {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// RMSNorm backward: lanes and values per lane for the row, split over as few
-// workgroups as hold it.  Rows up to 16384 stay in one workgroup.
+// RMSNorm backward: the fastest (P, R, G) measured on MI355X per dtype and N
+// bucket (16384 rows, every compiled configuration and 256, 512 or the occupancy
+// limit of persistent workgroups timed; one workgroup per CU measured best or
+// within a few percent), narrowed to the row as for the forward.
+struct BwdChoice {
+    int P, R, G;
+};
+static const BwdChoice kTunedRmsBwd[2][8] = {
+    {{8, 32, 1}, {16, 64, 1}, {16, 256, 1}, {16, 512, 2}, {16, 512, 4}, {32, 512, 4},
+     {32, 512, 8}, {32, 512, 16}},
+    {{16, 16, 1}, {16, 64, 1}, {32, 128, 1}, {32, 512, 1}, {32, 512, 2}, {32, 512, 4},
+     {32, 512, 8}, {32, 512, 16}},
+};
+
 static PlanResult plan_rmsnorm_bwd(int dtype, int64_t M, int64_t N, bool vec, Plan *out) {
     const int fP = env_int("RR_FORCE_P"), fR = env_int("RR_FORCE_R"), fG = env_int("RR_FORCE_G");
     int P, R, G = 1;
@@ -199,18 +222,23 @@ static PlanResult plan_rmsnorm_bwd(int dtype, int64_t M, int64_t N, bool vec, Pl
         R = fR ? fR : 512;
         G = fG ? fG : 1;
     } else {
-        const int pmax = vec ? 32 : 16;
-        if (N <= 4096) {
-            P = 8;
-        } else if (N <= 8192 || pmax == 16) {
-            P = 16;
-        } else {
-            P = 32;
+        int k = 0;
+        while (k < 7 && kTunedN[k] < N) ++k;
+        BwdChoice c = kTunedRmsBwd[dtype == kBf16 ? 1 : 0][k];
+        if (!vec && c.P > 16) {  // the per-element path keeps P <= 16: twice the lanes
+            c.P = 16;
+            if (c.G == 1 && c.R < 512) c.R *= 2; else c.G *= 2;
         }
-        int64_t r = next_pow2((N + P - 1) / P);
-        if (r < 16) r = 16;
-        R = (int)(r > 512 ? 512 : r);
-        while ((int64_t)P * R * G < N && G < 16) G *= 2;
+        P = c.P;
+        R = c.R;
+        G = c.G;
+        if (G == 1) {  // narrowed to the row
+            int64_t r = next_pow2((N + P - 1) / P);
+            R = (int)(r < 16 ? 16 : (r < R ? r : R));
+        } else {
+            while (G > 1 && (int64_t)P * R * (G / 2) >= N) G /= 2;
+        }
+        while ((int64_t)P * R * G < N && G < 16) G *= 2;  // past the table
     }
     if (!rmsbwd_config_ok(dtype, vec, P, R, G)) return kPlanUnsupported;
     Plan p;

@@ -1,5 +1,7 @@
 // rmsnorm_bwd.hip -- instantiates the RMSNorm backward kernels of the configuration
 // menu and launches the one the plan names, then the dw column reduction.
+#include <cstdlib>
+
 #include "launch_util.hpp"
 #include "rmsnorm_bwd.hpp"
 
@@ -14,12 +16,13 @@ hipError_t launch_cfg(const Plan &p, const void *x, const void *w, const void *d
     const int threads = bwd_threads(R, G);
     int groups;
     if constexpr (G == 1) {
-        // no workgroup waits for another: as many as fit at once, at most one per
-        // row block and at most the workspace's partial rows
-        int per_cu = 0;
-        hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
-        if (e != hipSuccess) return e;
-        int64_t g = (int64_t)(per_cu > 0 ? per_cu : 1) * a.num_cus;
+        // no workgroup waits for another: one per CU (measured best or within a few
+        // percent of two or four), at most one per row block and at most the
+        // workspace's partial rows
+        int64_t g = a.num_cus;
+        // test and tuning override of the number of persistent workgroups
+        const char *fg = std::getenv("RR_FORCE_GROUPS");
+        if (fg && *fg && std::atoi(fg) > 0) g = std::atoi(fg);
         if (g > p.max_parts) g = p.max_parts;
         groups = (int)g;
     } else {

@@ -47,18 +47,16 @@ def test_row_plans_hold_the_row(op, dt, vec):
 
 
 @pytest.mark.parametrize("dt", (rr.RR_F32, rr.RR_BF16))
-def test_cross_entropy_gradient_takes_the_softmax_plan(dt):
-    """The fused gradient runs the softmax kernels; only fp32 with 32 values on
-    1024 lanes is missing from its menu (it would not fit the registers)."""
+def test_cross_entropy_gradient_runs_the_softmax_kernels(dt):
+    """The fused gradient runs the softmax kernels with its own measured plans: the
+    same kinds of plan, never fp32 with 32 values on 1024 lanes (it would not fit
+    the registers), and the same workspace layout."""
     for N in NS[:-2]:
         for vec in (True, False):
-            a = rr.rr_plan_query(rr.RR_OP_SOFTMAX, 8192, N, dt, vec)
             b = rr.rr_plan_query(rr.RR_OP_XENT_GRAD, 8192, N, dt, vec)
-            if dt == rr.RR_F32 and a["path"] in (1, 3) and (a["vals_per_lane"], a["lanes_per_row"]) == (32, 1024):
+            assert b["max_n"] >= N and b["path"] in (0, 1, 3)
+            if dt == rr.RR_F32 and b["path"] != 0:
                 assert (b["vals_per_lane"], b["lanes_per_row"]) != (32, 1024)
-                assert b["max_n"] >= N
-            else:
-                assert a == b, N
 
 
 def test_workspace_scales_with_rows_up_to_the_group_cap():
@@ -154,4 +152,5 @@ def test_rmsnorm_bwd_plans(dt, vec):
         assert p["ws_bytes"] >= parts * N * 4
     # a handful of rows: as many partial rows as row blocks
     p = rr.rr_plan_query(rr.RR_OP_RMSNORM_BWD, 3, 4096, dt, vec)
-    assert p["ws_bytes"] >= 3 * 4096 * 4 and p["ws_bytes"] < 16 * 4096 * 4
+    blocks = -(-3 // p["rows_per_block"])
+    assert p["ws_bytes"] >= blocks * 4096 * 4 and p["ws_bytes"] < 16 * 4096 * 4

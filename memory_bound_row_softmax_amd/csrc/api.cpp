@@ -122,6 +122,9 @@ rr_status rr_softmax_fwd(const void *x, void *y, int64_t M, int64_t N, rr_dtype 
     if ((st = check_workspace(p, ws, ws_bytes)) != RR_OK) return st;
     rr::LaunchArgs a;
     if ((st = launch_args(stream, &a)) != RR_OK) return st;
+    if (p.path == rr::kPathLong)
+        return hip_status(rr::launch_long_row(p, rr::kOpSoftmax, dt, x, nullptr, y, nullptr, M, N,
+                                              0.0f, ws, a));
     return hip_status(rr::launch_softmax(p, dt, x, y, M, N, ws, a));
 }
 
@@ -142,6 +145,9 @@ rr_status rr_rmsnorm_fwd(const void *x, const void *w, void *y, float *rstd, int
     if ((st = check_workspace(p, ws, ws_bytes)) != RR_OK) return st;
     rr::LaunchArgs a;
     if ((st = launch_args(stream, &a)) != RR_OK) return st;
+    if (p.path == rr::kPathLong)
+        return hip_status(rr::launch_long_row(p, rr::kOpRmsnorm, dt, x, w, y, rstd, M, N, eps, ws,
+                                              a));
     return hip_status(rr::launch_rmsnorm(p, dt, x, w, y, rstd, M, N, eps, ws, a));
 }
 

@@ -107,6 +107,15 @@ constexpr int stream_depth(int op, int P, int R) {
     return (RR_STREAM_DEPTH > 2 && fits) ? RR_STREAM_DEPTH : 2;
 }
 
+// Two-pass long rows (softmax and RMSNorm forward past the split-row capacity):
+// tiles of kLongP * kLongR elements (kLongPElem on the per-element path), kLongG
+// workgroups per row, rows up to kLongMaxN elements (byte offsets stay 32-bit).
+constexpr int kLongP = 32;
+constexpr int kLongPElem = 16;
+constexpr int kLongR = 512;
+constexpr int kLongG = 16;
+constexpr long long kLongMaxN = 1ll << 28;
+
 // RMSNorm backward: the per-element path keeps P <= 16.
 constexpr bool rmsbwd_config_enabled(bool vec, int P) { return vec || P <= 16; }
 

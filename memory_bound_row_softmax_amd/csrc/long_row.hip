@@ -1,0 +1,47 @@
+// long_row.hip -- instantiates the two-pass long-row kernels (softmax and RMSNorm
+// forward past the on-chip capacity) and launches the one the plan names.
+#include "launch_util.hpp"
+#include "long_row.hpp"
+
+namespace rr {
+namespace {
+
+template <class E, int OP, int P, bool VEC>
+hipError_t launch_cfg(const void *x, const void *w, void *y, float *rstd, int64_t M, int64_t N,
+                      float eps, void *ws, const LaunchArgs &a) {
+    constexpr int R = kLongR, G = kLongG;
+    auto kernel = long_row_kernel<E, OP, P, R, G, VEC>;
+    int groups;
+    hipError_t e = cooperative_groups(kernel, R, G, M, a, &groups);
+    if (e != hipSuccess) return e;
+    const char *xp = static_cast<const char *>(x);
+    const char *wp = static_cast<const char *>(w);
+    char *yp = static_cast<char *>(y);
+    uint8_t *wsp = static_cast<uint8_t *>(ws);
+    int n = (int)N;
+    int spin = a.spin_limit;
+    void *args[] = {&xp, &wp, &yp, &rstd, &M, &n, &eps, &wsp, &groups, &spin};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(kernel), dim3(groups * G),
+                                      dim3(R), args, 0, a.stream);
+}
+
+template <class E, int OP>
+hipError_t dispatch(const Plan &p, const void *x, const void *w, void *y, float *rstd, int64_t M,
+                    int64_t N, float eps, void *ws, const LaunchArgs &a) {
+    if (p.vec) return launch_cfg<E, OP, kLongP, true>(x, w, y, rstd, M, N, eps, ws, a);
+    return launch_cfg<E, OP, kLongPElem, false>(x, w, y, rstd, M, N, eps, ws, a);
+}
+
+}  // namespace
+
+hipError_t launch_long_row(const Plan &p, int op, int dtype, const void *x, const void *w,
+                           void *y, float *rstd, int64_t M, int64_t N, float eps, void *ws,
+                           const LaunchArgs &a) {
+    if (op == kOpSoftmax)
+        return dtype == kF32 ? dispatch<F32, kLongSoftmax>(p, x, w, y, rstd, M, N, eps, ws, a)
+                             : dispatch<BF16, kLongSoftmax>(p, x, w, y, rstd, M, N, eps, ws, a);
+    return dtype == kF32 ? dispatch<F32, kLongRmsnorm>(p, x, w, y, rstd, M, N, eps, ws, a)
+                         : dispatch<BF16, kLongRmsnorm>(p, x, w, y, rstd, M, N, eps, ws, a);
+}
+
+}  // namespace rr

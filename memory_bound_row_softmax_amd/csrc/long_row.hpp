@@ -1,0 +1,136 @@
+// long_row.hpp -- softmax and RMSNorm forward for rows longer than the registers of
+// the split-row stream kernels can hold (more than P * R * G = 524288 elements).
+//
+// The QuACK article (无需CUDA代码，给H100加速33%-50%), section 内存吞吐量, names the
+// alternative to reducing a long row across a cluster: an online algorithm that reads
+// the row twice.  Here the G workgroups of a row group own every G-th tile of T = P * R
+// elements of the row:
+//   pass 1: stream the owned tiles, keeping a running (max, sum of exp) pair (softmax,
+//           the online-softmax rescaling) or the sum of squares (RMSNorm);
+//   merge:  reduce over the workgroup, then over the G workgroups through the
+//           workspace (grid_exchange.hpp);
+//   pass 2: read the owned tiles again and write y.
+// A workgroup's tiles were read a moment before, so the second read is served in large
+// part by the caches between the CUs and HBM (the 256 MB last-level cache holds the
+// few hundred KB each of the resident workgroups reads per row) rather than by HBM.
+// Each pass keeps the next tile's loads in flight while the current one is used.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "configs.hpp"
+#include "grid_exchange.hpp"
+#include "reduce.hpp"
+#include "row_io.hpp"
+#include "row_kernels.hpp"
+#include "vec_io.hpp"
+
+namespace rr {
+
+constexpr int kLongSoftmax = 0;
+constexpr int kLongRmsnorm = 1;
+
+// Walks tiles t = first, first + step, ... < tiles with two register buffers: the
+// next tile's loads are issued before the current tile is used.  `t` is the same
+// for the whole workgroup, so the branches are uniform.
+template <int P, class Load, class Use>
+__device__ __forceinline__ void walk_tiles(int first, int step, int tiles, Load load, Use use) {
+    float a[P], b[P];
+    int t = first;
+    if (t < tiles) load(a, t);
+    while (t < tiles) {
+        int tn = t + step;
+        if (tn < tiles) load(b, tn);
+        use(a, t);
+        t = tn;
+        if (t >= tiles) break;
+        tn = t + step;
+        if (tn < tiles) load(a, tn);
+        use(b, t);
+        t = tn;
+    }
+}
+
+template <class E, int OP, int P, int R, int G, bool VEC>
+__global__ void __launch_bounds__(R)
+    long_row_kernel(const char *x, const char *w, char *y, float *rstd, int64_t M, int N,
+                    float eps, uint8_t *ws, int groups, int spin_limit) {
+    static_assert(R >= 64 && G > 1, "whole waves, several workgroups per row");
+    constexpr int C = P / E::VPC;
+    constexpr int W = R / 64;
+    constexpr int T = P * R;  // elements per tile
+    __shared__ MaxSum red_ms[2][W];
+    __shared__ float red_q[2][W];
+    __shared__ float bcast[3];
+    RowCtx c{N, (int)threadIdx.x, 0, 0, true, nullptr, nullptr, bcast, GroupRef{}, spin_limit};
+    int group;
+    group_of_block<G>(groups, &group, &c.member);
+    c.g = group_ref<G>(ws, group);
+    if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
+    const int l = threadIdx.x;
+    const uint32_t rb = (uint32_t)N * E::BYTES;
+    const int tiles = (N + T - 1) / T;
+    const Buf wb = make_buf(w, rb);
+
+    for (int64_t row = group; row < M; row += groups) {
+        const RowView xv = stream_row_view(x, row, M, rb);
+        const RowView yv = stream_row_view(y, row, M, rb);
+        auto load = [&](float *v, int t) { load_part<E, C, R, VEC>(xv, t * C * R, l, v); };
+
+        // pass 1
+        MaxSum acc = {-INFINITY, 0.0f};
+        float q = 0.0f;
+        walk_tiles<P>(c.member, G, tiles, load, [&](float *v, int t) {
+            const int chunk0 = t * C * R;
+            if constexpr (OP == kLongSoftmax) {
+                if (!part_full<E, C, R>(chunk0, N)) mask_part<E, C, R>(chunk0, l, N, -INFINITY, v);
+                const float mnew = fmaxf(acc.m, tree_reduce<P>(v, OpMax{}));
+                const float mu = safe_max(mnew);
+#pragma unroll
+                for (int j = 0; j < P; ++j) v[j] = exp_shift(v[j], mu);
+                acc.s = acc.s * exp_shift(acc.m, mu) + tree_reduce<P>(v, OpSum{});
+                acc.m = mnew;
+            } else {
+                if (!part_full<E, C, R>(chunk0, N)) mask_part<E, C, R>(chunk0, l, N, 0.0f, v);
+                q += tree_sum_squares<P>(v);
+            }
+        });
+
+        // merge over the workgroup, then over the row group
+        float m_row = 0.0f, s_row = 0.0f, r = 0.0f;
+        if constexpr (OP == kLongSoftmax) {
+            acc = row_reduce<R>(acc, red_ms[c.it & 1], l, OpMerge{});
+            exchange_pairs<G>(c.g, c.member, c.it, acc.m, acc.s, c.spin_limit, c.bcast,
+                              MergeMaxSum{});
+            m_row = safe_max(c.bcast[0]);
+            s_row = __builtin_amdgcn_rcpf(c.bcast[1]);
+        } else {
+            q = row_reduce<R>(q, red_q[c.it & 1], l, OpSum{});
+            exchange_pairs<G>(c.g, c.member, c.it, q, 0.0f, c.spin_limit, c.bcast, MergeSum{});
+            r = __builtin_amdgcn_rsqf(c.bcast[0] / (float)N + eps);
+            if (rstd && c.member == 0 && l == 0) rstd[row] = r;
+        }
+
+        // pass 2
+        walk_tiles<P>(c.member, G, tiles, load, [&](float *v, int t) {
+            const int chunk0 = t * C * R;
+            const bool full = part_full<E, C, R>(chunk0, N);
+            if constexpr (OP == kLongSoftmax) {
+#pragma unroll
+                for (int j = 0; j < P; ++j) v[j] = exp_shift(v[j], m_row) * s_row;
+            } else {
+                float wv[P];
+                load_part<E, C, R, VEC, kReuseLoad>(RowView{wb, 0u}, chunk0, l, wv);
+#pragma unroll
+                for (int j = 0; j < P; ++j) v[j] = v[j] * wv[j] * r;
+            }
+            store_part<E, C, R, VEC>(yv, chunk0, l, N, true, full, v);
+        });
+        ++c.it;
+    }
+    if (c.it > 0) depart_group<G>(c.g);
+}
+
+}  // namespace rr

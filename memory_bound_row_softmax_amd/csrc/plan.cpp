@@ -303,6 +303,26 @@ PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *ou
     const char *kind = std::getenv("RR_FORCE_KIND");
     const bool force_stream = kind && std::strcmp(kind, "stream") == 0;
     const bool force_block = kind && std::strcmp(kind, "block") == 0;
+    const bool force_long = kind && std::strcmp(kind, "long") == 0;
+    const bool long_op = op == kOpSoftmax || op == kOpRmsnorm;
+    if (long_op && (force_long || (!fP && !fR && !fG && !force_stream && !force_block &&
+                                   !default_row(op, dtype, vec, N, &p)))) {
+        // past every on-chip plan: read the row twice
+        if (N > kLongMaxN) return kPlanUnsupported;
+        p = Plan{};
+        p.vec = vec;
+        p.stream = true;
+        p.path = kPathLong;
+        p.P = vec ? kLongP : kLongPElem;
+        p.R = kLongR;
+        p.G = kLongG;
+        p.max_n = kLongMaxN;
+        p.ws_bytes = grid_ws_bytes(kLongG, M);
+        p.block = kLongR;
+        p.rows_per_block = 1;
+        *out = p;
+        return kPlanOk;
+    }
     if (fP || fR || fG || force_stream || force_block) {
         p.stream = force_stream || (!force_block && fG > 1);
         p.P = fP ? fP : (p.stream ? 64 : 16);

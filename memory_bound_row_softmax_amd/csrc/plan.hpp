@@ -8,8 +8,9 @@
 namespace rr {
 
 // kPathRow: block kernel; kPathSplit: stream kernel with G > 1 (split rows);
-// kPathXent: cross-entropy; kPathStream: stream kernel with G = 1.
-enum PathKind { kPathRow = 0, kPathSplit = 1, kPathXent = 2, kPathStream = 3 };
+// kPathXent: cross-entropy; kPathStream: stream kernel with G = 1; kPathLong: rows
+// past the on-chip capacity, read twice (softmax and RMSNorm forward).
+enum PathKind { kPathRow = 0, kPathSplit = 1, kPathXent = 2, kPathStream = 3, kPathLong = 4 };
 // kOpXentGrad (cross-entropy forward fused with its gradient) runs the softmax
 // kernels with another epilogue and takes the softmax plan.
 // kOpSoftmaxBwd: softmax backward from the forward output (two input rows).
@@ -50,7 +51,7 @@ int rmsbwd_slices(int64_t parts, int64_t N);
 
 // Chooses the plan.  `vec` says whether the 128-bit path is usable for these
 // pointers.  Test-only overrides come from the environment: RR_FORCE_KIND
-// ("block" or "stream"), RR_FORCE_P, RR_FORCE_R and RR_FORCE_G (row ops), or
+// ("block", "stream" or "long"), RR_FORCE_P, RR_FORCE_R and RR_FORCE_G (row ops), or
 // RR_FORCE_P and RR_FORCE_R (cross-entropy); a forced configuration that is not
 // compiled, or too small for N, is unsupported.
 PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *out);

@@ -281,3 +281,72 @@ def test_stream_copy():
     rr.rr_stream_copy(a, b)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------- rows past on-chip capacity
+
+LONG = [(3, 524289), (2, 1 << 20), (2, 1_000_003), (1, 3_000_000)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N", LONG)
+def test_long_rows_read_twice(M, N, dtype):
+    code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
+    assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, M, N, code)["path"] == 4
+    say("long softmax", dtype, M, N)
+    parity_softmax(_x(M, N, dtype, sigma=3.0), dtype, f"long softmax {dtype} {M}x{N}")
+    say("long rmsnorm", dtype, M, N)
+    parity_rmsnorm(_x(M, N, dtype), _w(N, dtype), 1e-6, dtype, f"long rmsnorm {dtype} {M}x{N}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N", [(7, 1000), (33, 40000), (5, 16 * 16384 + 5), (70, 3)])
+def test_long_row_kernel_forced_at_short_rows(M, N, dtype):
+    """Tiles that do not fill a row group (members with no tile at all), ragged tails."""
+    with forced(kind="long"):
+        say("long forced softmax", dtype, M, N)
+        parity_softmax(_x(M, N, dtype, sigma=2.0), dtype, f"long forced softmax {M}x{N}")
+        say("long forced rmsnorm", dtype, M, N)
+        parity_rmsnorm(_x(M, N, dtype), _w(N, dtype), 1e-6, dtype, f"long forced rmsnorm {M}x{N}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_long_rows_unaligned(dtype):
+    M, N = 2, 600001
+    x_np = _x(M, N, dtype, sigma=2.0)
+    w_np = _w(N, dtype)
+    xs = to_dev(np.concatenate([np.zeros(1, x_np.dtype), x_np.ravel()]), dtype)[1:].view(M, N)
+    ys = torch.empty(M * N + 1, dtype=xs.dtype, device=DEV)[1:].view(M, N)
+    wt = torch.empty(N + 1, dtype=xs.dtype, device=DEV)[1:]
+    wt.copy_(to_dev(w_np, dtype))
+    code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
+    say("long unaligned softmax", dtype)
+    rr.rr_softmax_fwd(xs, ys, ws=rr.workspace(rr.RR_OP_SOFTMAX, M, N, code, DEV))
+    torch.cuda.synchronize()
+    check_out(from_dev(ys), oracle.softmax(x_np), dtype, "long unaligned softmax")
+    say("long unaligned rmsnorm", dtype)
+    rr.rr_rmsnorm_fwd(xs, wt, 1e-6, y=ys, ws=rr.workspace(rr.RR_OP_RMSNORM, M, N, code, DEV))
+    torch.cuda.synchronize()
+    check_out(from_dev(ys), oracle.rmsnorm(x_np, w_np, 1e-6), dtype, "long unaligned rmsnorm")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_long_rows_many_rows_deterministic(dtype):
+    M, N = 200, 600000
+    code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
+    x_np = _x(M, N, dtype, sigma=2.0)
+    x = to_dev(x_np, dtype)
+    ws = rr.workspace(rr.RR_OP_SOFTMAX, M, N, code, DEV)
+    outs = []
+    for i in range(3):
+        say("long rows repeat", i, dtype)
+        outs.append(rr.rr_softmax_fwd(x, ws=ws))
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero()) == 0
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    assert rr.rr_workspace_check(ws) == rr.RR_OK
+    rows = np.arange(0, M, 23)
+    check_out(from_dev(outs[0][torch.from_numpy(rows).to(DEV)]), oracle.softmax(x_np[rows]),
+              dtype, "long rows sampled")
+    s = outs[0].double().sum(dim=1)
+    assert float((s - 1).abs().max()) < (1e-4 if dtype == "f32" else 5e-2)

@@ -27,6 +27,10 @@ def test_row_plans_hold_the_row(op, dt, vec):
         else:
             p = rr.rr_plan_query(op, 16384, N, dt, vec)
         P, R, G = p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]
+        if p["path"] == 4:  # past every on-chip plan: the two-pass long-row kernel
+            assert op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM) and N > 262144
+            assert p["max_n"] == 1 << 28 and G == 16 and p["ws_bytes"] > 0
+            continue
         assert p["max_n"] == P * R * G >= N
         assert p["vectorized"] == int(vec)
         if p["path"] == 0:  # block kernel: a few rows per workgroup, one workgroup per row
@@ -42,8 +46,13 @@ def test_row_plans_hold_the_row(op, dt, vec):
             # a row is split only over as many workgroups as it needs
             assert G == 1 or (G // 2) * P * R < N
             assert p["ws_bytes"] == (256 + 1024 * (64 + 32 * G) if G > 1 else 0)
-    with pytest.raises(rr.RRError):
-        rr.rr_plan_query(op, 16, (1 << 20) + 1, dt, vec)
+    if op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):  # long rows: read twice, up to 2^28
+        assert rr.rr_plan_query(op, 16, (1 << 20) + 1, dt, vec)["path"] == 4
+        with pytest.raises(rr.RRError):
+            rr.rr_plan_query(op, 16, (1 << 28) + 1, dt, vec)
+    else:
+        with pytest.raises(rr.RRError):
+            rr.rr_plan_query(op, 16, (1 << 20) + 1, dt, vec)
 
 
 @pytest.mark.parametrize("dt", (rr.RR_F32, rr.RR_BF16))
@@ -154,3 +163,19 @@ def test_rmsnorm_bwd_plans(dt, vec):
     p = rr.rr_plan_query(rr.RR_OP_RMSNORM_BWD, 3, 4096, dt, vec)
     blocks = -(-3 // p["rows_per_block"])
     assert p["ws_bytes"] >= blocks * 4096 * 4 and p["ws_bytes"] < 16 * 4096 * 4
+
+
+def test_long_rows_take_the_two_pass_kernel(monkeypatch):
+    for op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
+        for dt in (rr.RR_F32, rr.RR_BF16):
+            on_chip = rr.rr_plan_query(op, 1000, 524288, dt)
+            assert on_chip["path"] == 1 and on_chip["max_n"] >= 524288
+            p = rr.rr_plan_query(op, 1000, 524289, dt)
+            assert p["path"] == 4 and p["lanes_per_row"] == 512 and p["groups_per_row"] == 16
+            assert p["ws_bytes"] == 256 + 1000 * (64 + 32 * 16)
+            assert rr.rr_plan_query(op, 10, 524289, dt, False)["vals_per_lane"] == 16
+    monkeypatch.setenv("RR_FORCE_KIND", "long")
+    assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 8, 1000, rr.RR_F32)["path"] == 4
+    # the other ops have no long-row kernel
+    with pytest.raises(rr.RRError):
+        rr.rr_plan_query(rr.RR_OP_SOFTMAX_BWD, 8, 1 << 20, rr.RR_F32)

@@ -113,7 +113,10 @@ constexpr int stream_depth(int op, int P, int R) {
 constexpr int kLongP = 32;
 constexpr int kLongPElem = 16;
 constexpr int kLongR = 512;
-constexpr int kLongG = 16;
+#ifndef RR_LONG_G
+#define RR_LONG_G 16
+#endif
+constexpr int kLongG = RR_LONG_G;
 constexpr long long kLongMaxN = 1ll << 28;
 
 // RMSNorm backward: the per-element path keeps P <= 16.

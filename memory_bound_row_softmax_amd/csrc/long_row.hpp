@@ -32,6 +32,14 @@ namespace rr {
 constexpr int kLongSoftmax = 0;
 constexpr int kLongRmsnorm = 1;
 
+// Cache policy of the first read of a tile: it is read again shortly, so it must
+// not carry the non-temporal hint of the other streams.  The second read is the
+// last use and streams.
+#ifndef RR_LONG_PASS1_POLICY
+#define RR_LONG_PASS1_POLICY 0
+#endif
+constexpr int kLongPass1Load = RR_LONG_PASS1_POLICY;
+
 // Walks tiles t = first, first + step, ... < tiles with two register buffers: the
 // next tile's loads are issued before the current tile is used.  `t` is the same
 // for the whole workgroup, so the branches are uniform.
@@ -77,12 +85,15 @@ __global__ void __launch_bounds__(R)
     for (int64_t row = group; row < M; row += groups) {
         const RowView xv = stream_row_view(x, row, M, rb);
         const RowView yv = stream_row_view(y, row, M, rb);
-        auto load = [&](float *v, int t) { load_part<E, C, R, VEC>(xv, t * C * R, l, v); };
+        auto load1 = [&](float *v, int t) {
+            load_part<E, C, R, VEC, kLongPass1Load>(xv, t * C * R, l, v);
+        };
+        auto load2 = [&](float *v, int t) { load_part<E, C, R, VEC>(xv, t * C * R, l, v); };
 
         // pass 1
         MaxSum acc = {-INFINITY, 0.0f};
         float q = 0.0f;
-        walk_tiles<P>(c.member, G, tiles, load, [&](float *v, int t) {
+        walk_tiles<P>(c.member, G, tiles, load1, [&](float *v, int t) {
             const int chunk0 = t * C * R;
             if constexpr (OP == kLongSoftmax) {
                 if (!part_full<E, C, R>(chunk0, N)) mask_part<E, C, R>(chunk0, l, N, -INFINITY, v);
@@ -114,7 +125,7 @@ __global__ void __launch_bounds__(R)
         }
 
         // pass 2
-        walk_tiles<P>(c.member, G, tiles, load, [&](float *v, int t) {
+        walk_tiles<P>(c.member, G, tiles, load2, [&](float *v, int t) {
             const int chunk0 = t * C * R;
             const bool full = part_full<E, C, R>(chunk0, N);
             if constexpr (OP == kLongSoftmax) {

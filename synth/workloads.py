@@ -71,8 +71,13 @@ def sweep():
     return out
 
 
+# Rows past the on-chip capacity (read twice): 1M-element rows.
+LONG = [Workload("softmax_f32_1024x1048576", "softmax", "f32", 1024, 1 << 20),
+        Workload("rmsnorm_bf16_2048x1048576", "rmsnorm", "bf16", 2048, 1 << 20)]
+
+
 def by_name(name: str) -> Workload:
-    for w in FIXED + BACKWARD + sweep():
+    for w in FIXED + BACKWARD + LONG + sweep():
         if w.name == name:
             return w
     raise KeyError(name)

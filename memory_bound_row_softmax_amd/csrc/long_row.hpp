@@ -40,25 +40,33 @@ constexpr int kLongRmsnorm = 1;
 #endif
 constexpr int kLongPass1Load = RR_LONG_PASS1_POLICY;
 
-// Walks tiles t = first, first + step, ... < tiles with two register buffers: the
-// next tile's loads are issued before the current tile is used.  `t` is the same
-// for the whole workgroup, so the branches are uniform.
+// Walks the tiles t = first, first + step, ... that lie in [0, tiles), with two
+// register buffers: the next tile's loads are issued before the current tile is
+// used.  `step` may be negative (the second pass walks backwards, so that it first
+// reads the tiles the first pass read last, the ones most likely still cached).
+// `t` is the same for the whole workgroup, so the branches are uniform.
 template <int P, class Load, class Use>
 __device__ __forceinline__ void walk_tiles(int first, int step, int tiles, Load load, Use use) {
+    auto in = [&](int t) { return t >= 0 && t < tiles; };
     float a[P], b[P];
     int t = first;
-    if (t < tiles) load(a, t);
-    while (t < tiles) {
+    if (in(t)) load(a, t);
+    while (in(t)) {
         int tn = t + step;
-        if (tn < tiles) load(b, tn);
+        if (in(tn)) load(b, tn);
         use(a, t);
         t = tn;
-        if (t >= tiles) break;
+        if (!in(t)) break;
         tn = t + step;
-        if (tn < tiles) load(a, tn);
+        if (in(tn)) load(a, tn);
         use(b, t);
         t = tn;
     }
+}
+
+// The last of the tiles first, first + step, ... below `tiles` (or `first` if none).
+__device__ __forceinline__ int last_tile(int first, int step, int tiles) {
+    return first < tiles ? first + ((tiles - 1 - first) / step) * step : first;
 }
 
 template <class E, int OP, int P, int R, int G, bool VEC>
@@ -124,8 +132,8 @@ __global__ void __launch_bounds__(R)
             if (rstd && c.member == 0 && l == 0) rstd[row] = r;
         }
 
-        // pass 2
-        walk_tiles<P>(c.member, G, tiles, load2, [&](float *v, int t) {
+        // pass 2, backwards
+        walk_tiles<P>(last_tile(c.member, G, tiles), -G, tiles, load2, [&](float *v, int t) {
             const int chunk0 = t * C * R;
             const bool full = part_full<E, C, R>(chunk0, N);
             if constexpr (OP == kLongSoftmax) {

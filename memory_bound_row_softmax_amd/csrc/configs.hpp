@@ -128,6 +128,24 @@ constexpr bool rmsbwd_config_enabled(bool vec, int P) { return vec || P <= 16; }
 constexpr int kBwdMaxWorkgroups = 1024;
 constexpr int kBwdReduceTarget = 512;  // workgroups of the first reduction pass
 
+// Split rows (G > 1) with the deferred exchange: a row's partial is published, the
+// next row reduced, and only then the wait for the peers' partials of the first
+// row (three row buffers instead of two).  Used where it measured faster on
+// MI355X: softmax fp32 with 64 values on 512 lanes (+5 % at 262144 elements) and
+// 16 values on 1024 lanes (+10-20 %).  Elsewhere the third buffer either does not
+// fit the registers or costs a workgroup per CU, which loses more than the
+// hidden exchange gains (-2 to -20 % for 32 values on 512 lanes, 64 on 256).
+#ifndef RR_SPLIT_DEFER
+#define RR_SPLIT_DEFER 1
+#endif
+constexpr bool kDeferredExchange = RR_SPLIT_DEFER != 0;
+
+constexpr bool defer_split(int op, int elem_bytes, bool vec, int P, int R) {
+    if (P == 64 && R == 512) return op == kCfgSoftmax && elem_bytes == 4;
+    if (P == 16 && R == 1024) return vec || op != kCfgXentGrad;
+    return false;
+}
+
 // Threads per workgroup and rows per workgroup for a lane-group width R (block
 // kernels; a stream kernel's workgroup is its R lanes).
 constexpr int block_threads_for(int R) { return R < 256 ? 256 : R; }
@@ -137,9 +155,10 @@ constexpr int rows_per_block_for(int R) { return block_threads_for(R) / R; }
 //   [0, 256)                 header; word 0 is the error word (non-zero: a wait timed out)
 //   256 + g * group_stride   record of row group g:
 //       +0                   departure counter (uint32)
-//       +64                  slots[2 parities][G][2] of uint64: (epoch << 32) | float bits
+//       +64                  slots[kSlotSets][G][2] of uint64: (epoch << 32) | float bits
 constexpr int kWsHeader = 256;
 constexpr int kMaxGroups = 1024;
-constexpr int group_stride_for(int G) { return 64 + 2 * G * 16; }
+constexpr int kSlotSets = 4;
+constexpr int group_stride_for(int G) { return 64 + kSlotSets * G * 16; }
 
 }  // namespace rr

@@ -12,9 +12,11 @@
 //    relaxed atomics.  The epoch (row iteration + 1) travels in the same word as the
 //    value, so a reader that sees the right epoch has the right value: no fences,
 //    no separate flag, no cache write-back or invalidate;
-//  * slots are double-buffered by iteration parity: a workgroup can only overwrite
-//    its parity-p slot two iterations later, after every peer has published the
-//    iteration in between, i.e. after every peer finished reading;
+//  * slots come in kSlotSets = 4 sets, used in turn by the row iterations.  A
+//    workgroup may publish iteration k before it waits for iteration k - 1 (the
+//    deferred exchange of the split-row kernels); it has then finished waiting for
+//    k - 2, so every peer has published k - 2, which a peer does only after it
+//    finished reading k - 4: the set of k - 4, which k overwrites, is free;
 //  * wave 0 polls the G slots (one lane per slot), then merges the partials in slot
 //    order, so every workgroup of the row computes the same bits;
 //  * each poll loop is bounded by `spin_limit`; a workgroup that gives up sets the
@@ -38,7 +40,7 @@ namespace rr {
 
 struct GroupRef {
     uint32_t *depart;  // departure counter
-    uint64_t *slots;   // [2][G][2]
+    uint64_t *slots;   // [kSlotSets][G][2]
     uint32_t *error;   // workspace error word
 };
 
@@ -60,22 +62,29 @@ __device__ __forceinline__ uint64_t atomic_get(const uint64_t *p) {
     return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Publishes (a, b) for member k at iteration `it`, waits for all G members and
-// leaves the G pairs merged in member order by `merge2` in bcast[0..1] (the same
-// bits for the whole workgroup).  Called by every thread; uses one barrier.
-// After a wait has timed out, `spin_limit` is lowered to 1 so that the rest of
-// the launch does not wait again.
-template <int G, class Merge>
-__device__ __forceinline__ void exchange_pairs(GroupRef g, int k, int it, float a, float b,
-                                               int &spin_limit, float *bcast, Merge merge2) {
-    const int tid = threadIdx.x;
-    const int par = it & 1;
-    const uint32_t epoch = (uint32_t)it + 1u;
-    uint64_t *slot = g.slots + (size_t)par * G * 2;
-    if (tid == 0) {
+// Publishes (a, b) for member k at iteration `it` (thread 0 writes; the values are
+// the same in every thread).
+template <int G>
+__device__ __forceinline__ void publish_pair(GroupRef g, int k, int it, float a, float b) {
+    if (threadIdx.x == 0) {
+        uint64_t *slot = g.slots + (size_t)(it & (kSlotSets - 1)) * G * 2;
+        const uint32_t epoch = (uint32_t)it + 1u;
         atomic_put(slot + 2 * k, tag(epoch, a));
         atomic_put(slot + 2 * k + 1, tag(epoch, b));
     }
+}
+
+// Waits until all G members have published iteration `it` and leaves the G pairs
+// merged in member order by `merge2` in bcast[0..1] (the same bits for the whole
+// workgroup).  Called by every thread; uses one barrier.  After a wait has timed
+// out, `spin_limit` is lowered to 1 so that the rest of the launch does not wait
+// again.
+template <int G, class Merge>
+__device__ __forceinline__ void wait_pairs(GroupRef g, int it, int &spin_limit, float *bcast,
+                                           Merge merge2) {
+    const int tid = threadIdx.x;
+    const uint32_t epoch = (uint32_t)it + 1u;
+    const uint64_t *slot = g.slots + (size_t)(it & (kSlotSets - 1)) * G * 2;
     if (tid < 64) {
         const int lane = tid;
         uint64_t wa = 0, wb = 0;
@@ -114,6 +123,14 @@ __device__ __forceinline__ void exchange_pairs(GroupRef g, int k, int it, float 
     if (bcast[2] != 0.0f) spin_limit = 1;
 }
 
+// Publish, then wait for the same iteration.
+template <int G, class Merge>
+__device__ __forceinline__ void exchange_pairs(GroupRef g, int k, int it, float a, float b,
+                                               int &spin_limit, float *bcast, Merge merge2) {
+    publish_pair<G>(g, k, it, a, b);
+    wait_pairs<G>(g, it, spin_limit, bcast, merge2);
+}
+
 // Called once per workgroup after its last row (only if it processed any row).
 template <int G>
 __device__ __forceinline__ void depart_group(GroupRef g) {
@@ -121,7 +138,7 @@ __device__ __forceinline__ void depart_group(GroupRef g) {
         uint32_t before =
             __hip_atomic_fetch_add(g.depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (before == (uint32_t)G - 1u) {
-            for (int i = 0; i < 2 * G * 2; ++i) atomic_put(g.slots + i, 0ull);
+            for (int i = 0; i < kSlotSets * G * 2; ++i) atomic_put(g.slots + i, 0ull);
             __hip_atomic_store(g.depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }

@@ -160,10 +160,10 @@ struct SoftmaxOut {
     __device__ __forceinline__ Epi epi(const float *, int64_t) const { return {}; }
 };
 
-// Passes 1-3 on a lane's loaded part v of the row, then the store.
-template <class E, int P, int R, int G, bool VEC, class Epi>
-__device__ __forceinline__ void softmax_finish(float *v, RowView yv, bool valid, RowCtx &c,
-                                               Epi &epi) {
+// Passes 1 and 2 on a lane's loaded part v of the row: the row max m (over this
+// workgroup's part), e = exp(x - m) in place and its sum s.
+template <class E, int P, int R, class Epi>
+__device__ __forceinline__ MaxSum softmax_local(float *v, RowCtx &c, Epi &epi) {
     constexpr int C = P / E::VPC;
     const int chunk0 = c.member * C * R;
     epi.template capture<E, C, R>(v, chunk0, c.l);
@@ -179,21 +179,37 @@ __device__ __forceinline__ void softmax_finish(float *v, RowView yv, bool valid,
     for (int j = 0; j < P; ++j) v[j] = exp_shift(v[j], mu);
     float s = tree_reduce<P>(v, OpSum{});
     s = row_reduce<R>(s, c.red_b, c.l, OpSum{});
+    return {m, s};
+}
 
-    // pass 3: normalise (a split row first merges the G partial (max, sum) pairs)
-    float scale, Mrow, Srow;
-    if constexpr (G == 1) {
-        scale = __builtin_amdgcn_rcpf(s);
-        Mrow = m;
-        Srow = s;
-    } else {
-        exchange_pairs<G>(c.g, c.member, c.it, m, s, c.spin_limit, c.bcast, MergeMaxSum{});
-        Mrow = c.bcast[0];
-        Srow = c.bcast[1];
-        scale = exp_shift(m, safe_max(Mrow)) * __builtin_amdgcn_rcpf(Srow);
-    }
+// Pass 3: normalise with the row's (M, S) (for a split row, merged over its G
+// workgroups; `loc` is this workgroup's own pair), then the store.
+template <class E, int P, int R, int G, bool VEC, class Epi>
+__device__ __forceinline__ void softmax_apply(float *v, RowView yv, bool valid, RowCtx &c,
+                                              Epi &epi, MaxSum loc, float Mrow, float Srow) {
+    constexpr int C = P / E::VPC;
+    const int chunk0 = c.member * C * R;
+    float scale;
+    if constexpr (G == 1)
+        scale = __builtin_amdgcn_rcpf(Srow);
+    else
+        scale = exp_shift(loc.m, safe_max(Mrow)) * __builtin_amdgcn_rcpf(Srow);
     epi.template apply<E, C, R>(v, scale, Mrow, Srow, chunk0, c, valid);
     store_part<E, C, R, VEC>(yv, chunk0, c.l, c.N, valid, c.full, v);
+}
+
+// Passes 1-3 on a lane's loaded part v of the row, then the store.
+template <class E, int P, int R, int G, bool VEC, class Epi>
+__device__ __forceinline__ void softmax_finish(float *v, RowView yv, bool valid, RowCtx &c,
+                                               Epi &epi) {
+    const MaxSum loc = softmax_local<E, P, R>(v, c, epi);
+    if constexpr (G == 1) {
+        softmax_apply<E, P, R, G, VEC>(v, yv, valid, c, epi, loc, loc.m, loc.s);
+    } else {
+        exchange_pairs<G>(c.g, c.member, c.it, loc.m, loc.s, c.spin_limit, c.bcast,
+                          MergeMaxSum{});
+        softmax_apply<E, P, R, G, VEC>(v, yv, valid, c, epi, loc, c.bcast[0], c.bcast[1]);
+    }
 }
 
 template <class E, int P, int R, bool VEC, class Out = SoftmaxOut>
@@ -238,22 +254,63 @@ __global__ void __launch_bounds__(R)
     c.full = part_full<E, C, R>(chunk0, N);
     const uint32_t rb = (uint32_t)N * E::BYTES;
 
-    // D register buffers: the loads of the next D - 1 rows are in flight while
-    // the current row is reduced, exchanged and written.  A row's per-row inputs
-    // (if the output policy has any) sit after its values and are loaded with it.
+    // Per-row inputs of the output policy (if any) sit after a row's values in its
+    // buffer and are loaded with it.
     constexpr int X = Out::kExtra;
-    float buf[D][P + X];
-    stream_rows<D>(
-        (int64_t)group, M, groups, buf,
-        [&](float *v, int64_t r) {
+    if constexpr (G > 1 && kDeferredExchange && defer_split(Out::kCfg, E::BYTES, VEC, P, R)) {
+        // Split rows, deferred exchange: three buffers.  Row k is reduced and its
+        // partial published before the workgroup waits for row k - 1's peers and
+        // writes row k - 1; the loads of row k + 1 are in flight meanwhile.  The
+        // exchange's latency is then hidden behind a whole row's reduction.
+        float buf[3][P + X];
+        typename Out::Epi epis[3];
+        MaxSum pend = {0.0f, 0.0f};  // this workgroup's (max, sum) of the row waiting
+        int64_t row = group;
+        auto load = [&](float *v, int64_t r) {
             load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
             if (r < M) out.stash(v + P, r);
-        },
-        [&](float *v, int64_t r) {
-            auto epi = out.epi(v + P, r);
-            softmax_finish<E, P, R, G, VEC>(v, stream_row_view(y, r, M, rb), true, c, epi);
+        };
+        load(buf[0], row);
+        load(buf[1], row + groups);
+        auto step = [&](auto Kc) -> bool {
+            constexpr int K = decltype(Kc)::value, KP = (K + 2) % 3;
+            const bool more = row < M;
+            MaxSum cur = {0.0f, 0.0f};
+            if (more) {
+                epis[K] = out.epi(buf[K] + P, row);
+                cur = softmax_local<E, P, R>(buf[K], c, epis[K]);
+                publish_pair<G>(c.g, c.member, c.it, cur.m, cur.s);
+            }
+            if (c.it > 0) {  // complete the previous row
+                wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeMaxSum{});
+                softmax_apply<E, P, R, G, VEC>(buf[KP], stream_row_view(y, row - groups, M, rb),
+                                               true, c, epis[KP], pend, c.bcast[0], c.bcast[1]);
+            }
+            pend = cur;
+            if (!more) return false;
+            load(buf[KP], row + 2 * (int64_t)groups);
             ++c.it;
-        });
+            row += groups;
+            return true;
+        };
+        while (stream_steps<0, 3>(step)) {
+        }
+    } else {
+        // D register buffers: the loads of the next D - 1 rows are in flight while
+        // the current row is reduced, exchanged and written.
+        float buf[D][P + X];
+        stream_rows<D>(
+            (int64_t)group, M, groups, buf,
+            [&](float *v, int64_t r) {
+                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
+                if (r < M) out.stash(v + P, r);
+            },
+            [&](float *v, int64_t r) {
+                auto epi = out.epi(v + P, r);
+                softmax_finish<E, P, R, G, VEC>(v, stream_row_view(y, r, M, rb), true, c, epi);
+                ++c.it;
+            });
+    }
     if constexpr (G > 1) {
         if (c.it > 0) depart_group<G>(c.g);
     }
@@ -296,26 +353,39 @@ struct WeightLds {
     }
 };
 
-template <class E, int P, int R, int G, bool VEC, class Weight>
-__device__ __forceinline__ void rmsnorm_finish(float *v, const Weight &w, RowView yv,
-                                               float *rstd_out, float eps, bool valid, RowCtx &c) {
+// Sum of squares of this workgroup's part of the row, and t = x * w in place.
+template <class E, int P, int R, class Weight>
+__device__ __forceinline__ float rmsnorm_local(float *v, const Weight &w, RowCtx &c) {
     constexpr int C = P / E::VPC;
     const int chunk0 = c.member * C * R;
     if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.N, 0.0f, v);
-
-    // sum of squares, then t = x * w in place; y = t * r once r is known
     float q = tree_sum_squares<P>(v);
     w.apply(v, c.l);
-    q = row_reduce<R>(q, c.one_reduction_slots(), c.l, OpSum{});
-    if constexpr (G > 1) {
-        exchange_pairs<G>(c.g, c.member, c.it, q, 0.0f, c.spin_limit, c.bcast, MergeSum{});
-        q = c.bcast[0];
-    }
-    const float r = __builtin_amdgcn_rsqf(q / (float)c.N + eps);
+    return row_reduce<R>(q, c.one_reduction_slots(), c.l, OpSum{});
+}
+
+// y = t * r with r = rsqrt(Q / N + eps) for the row's sum of squares Q, then the store.
+template <class E, int P, int R, bool VEC>
+__device__ __forceinline__ void rmsnorm_apply(float *v, float Q, RowView yv, float *rstd_out,
+                                              float eps, bool valid, const RowCtx &c) {
+    constexpr int C = P / E::VPC;
+    const int chunk0 = c.member * C * R;
+    const float r = __builtin_amdgcn_rsqf(Q / (float)c.N + eps);
 #pragma unroll
     for (int j = 0; j < P; ++j) v[j] *= r;
     store_part<E, C, R, VEC>(yv, chunk0, c.l, c.N, valid, c.full, v);
     if (rstd_out && valid && c.l == 0 && c.member == 0) *rstd_out = r;
+}
+
+template <class E, int P, int R, int G, bool VEC, class Weight>
+__device__ __forceinline__ void rmsnorm_finish(float *v, const Weight &w, RowView yv,
+                                               float *rstd_out, float eps, bool valid, RowCtx &c) {
+    float q = rmsnorm_local<E, P, R>(v, w, c);
+    if constexpr (G > 1) {
+        exchange_pairs<G>(c.g, c.member, c.it, q, 0.0f, c.spin_limit, c.bcast, MergeSum{});
+        q = c.bcast[0];
+    }
+    rmsnorm_apply<E, P, R, VEC>(v, q, yv, rstd_out, eps, valid, c);
 }
 
 template <class E, int P, int R, bool VEC>
@@ -372,17 +442,49 @@ __global__ void __launch_bounds__(R)
     }
     const WeightLds<P, R> wsrc{wslot};
 
-    float buf[D][P];
-    stream_rows<D>(
-        (int64_t)group, M, groups, buf,
-        [&](float *v, int64_t r) {
+    if constexpr (G > 1 && kDeferredExchange && defer_split(kCfgRmsnorm, E::BYTES, VEC, P, R)) {
+        // Split rows, deferred exchange (see the softmax stream kernel).
+        float buf[3][P];
+        int64_t row = group;
+        auto load = [&](float *v, int64_t r) {
             load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
-        },
-        [&](float *v, int64_t r) {
-            rmsnorm_finish<E, P, R, G, VEC>(v, wsrc, stream_row_view(y, r, M, rb),
-                                            rstd ? rstd + r : nullptr, eps, true, c);
+        };
+        load(buf[0], row);
+        load(buf[1], row + groups);
+        auto step = [&](auto Kc) -> bool {
+            constexpr int K = decltype(Kc)::value, KP = (K + 2) % 3;
+            const bool more = row < M;
+            if (more) {
+                const float q = rmsnorm_local<E, P, R>(buf[K], wsrc, c);
+                publish_pair<G>(c.g, c.member, c.it, q, 0.0f);
+            }
+            if (c.it > 0) {  // complete the previous row
+                wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeSum{});
+                const int64_t rp = row - groups;
+                rmsnorm_apply<E, P, R, VEC>(buf[KP], c.bcast[0], stream_row_view(y, rp, M, rb),
+                                            rstd ? rstd + rp : nullptr, eps, true, c);
+            }
+            if (!more) return false;
+            load(buf[KP], row + 2 * (int64_t)groups);
             ++c.it;
-        });
+            row += groups;
+            return true;
+        };
+        while (stream_steps<0, 3>(step)) {
+        }
+    } else {
+        float buf[D][P];
+        stream_rows<D>(
+            (int64_t)group, M, groups, buf,
+            [&](float *v, int64_t r) {
+                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
+            },
+            [&](float *v, int64_t r) {
+                rmsnorm_finish<E, P, R, G, VEC>(v, wsrc, stream_row_view(y, r, M, rb),
+                                                rstd ? rstd + r : nullptr, eps, true, c);
+                ++c.it;
+            });
+    }
     if constexpr (G > 1) {
         if (c.it > 0) depart_group<G>(c.g);
     }

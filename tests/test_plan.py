@@ -45,7 +45,7 @@ def test_row_plans_hold_the_row(op, dt, vec):
             assert p["block_threads"] == R and p["rows_per_block"] == 1
             # a row is split only over as many workgroups as it needs
             assert G == 1 or (G // 2) * P * R < N
-            assert p["ws_bytes"] == (256 + 1024 * (64 + 32 * G) if G > 1 else 0)
+            assert p["ws_bytes"] == (256 + 1024 * (64 + 64 * G) if G > 1 else 0)
     if op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):  # long rows: read twice, up to 2^28
         assert rr.rr_plan_query(op, 16, (1 << 20) + 1, dt, vec)["path"] == 4
         with pytest.raises(rr.RRError):
@@ -75,8 +75,8 @@ def test_workspace_scales_with_rows_up_to_the_group_cap():
     # the larger of the 128-bit and the per-element plans
     G = max(rr.rr_plan_query(rr.RR_OP_SOFTMAX, 3, N, rr.RR_F32, v)["groups_per_row"]
             for v in (True, False))
-    assert small == 256 + 3 * (64 + 32 * G)
-    assert big == 256 + 1024 * (64 + 32 * G)
+    assert small == 256 + 3 * (64 + 64 * G)
+    assert big == 256 + 1024 * (64 + 64 * G)
     assert rr.workspace_bytes(rr.RR_OP_SOFTMAX, 0, N, rr.RR_F32) == 0
     assert rr.workspace_bytes(rr.RR_OP_XENT, 8192, N, rr.RR_F32) == 0
 
@@ -95,7 +95,7 @@ def test_forced_configurations(monkeypatch):
     monkeypatch.setenv("RR_FORCE_G", "4")
     p = rr.rr_plan_query(rr.RR_OP_SOFTMAX, 50, 3000, rr.RR_F32)
     assert (p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"], p["path"]) == (64, 256, 4, 1)
-    assert p["ws_bytes"] == 256 + 50 * (64 + 32 * 4)
+    assert p["ws_bytes"] == 256 + 50 * (64 + 64 * 4)
     # too small for the row
     with pytest.raises(rr.RRError):
         rr.rr_plan_query(rr.RR_OP_SOFTMAX, 50, 70000, rr.RR_F32)
@@ -172,7 +172,7 @@ def test_long_rows_take_the_two_pass_kernel(monkeypatch):
             assert on_chip["path"] == 1 and on_chip["max_n"] >= 524288
             p = rr.rr_plan_query(op, 1000, 524289, dt)
             assert p["path"] == 4 and p["lanes_per_row"] == 512 and p["groups_per_row"] == 16
-            assert p["ws_bytes"] == 256 + 1000 * (64 + 32 * 16)
+            assert p["ws_bytes"] == 256 + 1000 * (64 + 64 * 16)
             assert rr.rr_plan_query(op, 10, 524289, dt, False)["vals_per_lane"] == 16
     monkeypatch.setenv("RR_FORCE_KIND", "long")
     assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 8, 1000, rr.RR_F32)["path"] == 4

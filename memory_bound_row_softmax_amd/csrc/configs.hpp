@@ -128,20 +128,25 @@ constexpr bool rmsbwd_config_enabled(bool vec, int P) { return vec || P <= 16; }
 constexpr int kBwdMaxWorkgroups = 1024;
 constexpr int kBwdReduceTarget = 512;  // workgroups of the first reduction pass
 
-// Split rows (G > 1) with the deferred exchange: a row's partial is published, the
-// next row reduced, and only then the wait for the peers' partials of the first
-// row (three row buffers instead of two).  Used where it measured faster on
-// MI355X: softmax fp32 with 64 values on 512 lanes (+5 % at 262144 elements) and
-// 16 values on 1024 lanes (+10-20 %).  Elsewhere the third buffer either does not
-// fit the registers or costs a workgroup per CU, which loses more than the
-// hidden exchange gains (-2 to -20 % for 32 values on 512 lanes, 64 on 256).
+// Split rows with the deferred exchange: a row's partial is published, the next
+// row reduced, and only then the wait for the peers' partials of the first row
+// (three row buffers instead of two; a row in flight is kept as raw chunks, half
+// the registers for bf16).  Used where it measured faster on MI355X: rows split
+// over 8 or more workgroups, softmax with 64 values on 512 lanes (+5-9 % at
+// 262144 elements) and 16 values on 1024 lanes (+10-20 %).  With 2 workgroups per
+// row the exchange is cheap and the deferral only delays the stores (bf16 softmax
+// at 65536 elements: -14 %); elsewhere the third buffer does not fit the
+// registers or costs a workgroup per CU (-2 to -20 % for 32 values on 512 lanes,
+// 64 on 256).
 #ifndef RR_SPLIT_DEFER
 #define RR_SPLIT_DEFER 1
 #endif
 constexpr bool kDeferredExchange = RR_SPLIT_DEFER != 0;
 
-constexpr bool defer_split(int op, int elem_bytes, bool vec, int P, int R) {
-    if (P == 64 && R == 512) return op == kCfgSoftmax && elem_bytes == 4;
+constexpr bool defer_split(int op, int elem_bytes, bool vec, int P, int R, int G) {
+    (void)elem_bytes;
+    if (G < 8) return false;
+    if (P == 64 && R == 512) return op == kCfgSoftmax;
     if (P == 16 && R == 1024) return vec || op != kCfgXentGrad;
     return false;
 }

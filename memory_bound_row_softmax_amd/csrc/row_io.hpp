@@ -55,6 +55,35 @@ __device__ __forceinline__ void load_part(RowView rv, int chunk0, int l, float *
     }
 }
 
+// The 128-bit loads of load_part without the conversion: the lane's chunks land as
+// raw 32-bit words in v[0 .. 4C), bit for bit (for bf16 that is half of v; the
+// rest is left unwritten, so a buffer in flight holds only P/2 live registers).
+// widen_part() later turns them into the P fp32 values load_part would give.
+template <class E, int C, int R, int POLICY = kStreamLoad>
+__device__ __forceinline__ void load_part_raw(RowView rv, int chunk0, int l, float *v) {
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        const u32x4 raw =
+            buf_load16<POLICY>(rv.buf, rv.base + (uint32_t)(chunk0 + i * R + l) * 16u);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[4 * i + q] = __uint_as_float(raw[q]);
+    }
+}
+
+// In place: the raw words of load_part_raw -> P fp32 values.  Word k holds
+// elements 2k and 2k + 1 (bf16), so going from the last element down never
+// overwrites a word that is still to be read.
+template <class E, int C>
+__device__ __forceinline__ void widen_part(float *v) {
+    if constexpr (E::BYTES == 2) {
+#pragma unroll
+        for (int j = C * E::VPC - 1; j >= 0; --j) {
+            const uint32_t w = __float_as_uint(v[j / 2]);
+            v[j] = __uint_as_float((j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        }
+    }
+}
+
 // Registers that hold no element of the row get `fill`.
 template <class E, int C, int R>
 __device__ __forceinline__ void mask_part(int chunk0, int l, int N, float fill, float *v) {

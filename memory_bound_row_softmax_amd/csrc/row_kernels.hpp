@@ -257,7 +257,7 @@ __global__ void __launch_bounds__(R)
     // Per-row inputs of the output policy (if any) sit after a row's values in its
     // buffer and are loaded with it.
     constexpr int X = Out::kExtra;
-    if constexpr (G > 1 && kDeferredExchange && defer_split(Out::kCfg, E::BYTES, VEC, P, R)) {
+    if constexpr (kDeferredExchange && defer_split(Out::kCfg, E::BYTES, VEC, P, R, G)) {
         // Split rows, deferred exchange: three buffers.  Row k is reduced and its
         // partial published before the workgroup waits for row k - 1's peers and
         // writes row k - 1; the loads of row k + 1 are in flight meanwhile.  The
@@ -266,8 +266,13 @@ __global__ void __launch_bounds__(R)
         typename Out::Epi epis[3];
         MaxSum pend = {0.0f, 0.0f};  // this workgroup's (max, sum) of the row waiting
         int64_t row = group;
+        // A row in flight is held as its raw 16-byte chunks (bf16: half the
+        // registers) and widened when it becomes the current row.
         auto load = [&](float *v, int64_t r) {
-            load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
+            if constexpr (VEC)
+                load_part_raw<E, C, R>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
+            else
+                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
             if (r < M) out.stash(v + P, r);
         };
         load(buf[0], row);
@@ -277,6 +282,7 @@ __global__ void __launch_bounds__(R)
             const bool more = row < M;
             MaxSum cur = {0.0f, 0.0f};
             if (more) {
+                if constexpr (VEC) widen_part<E, C>(buf[K]);
                 epis[K] = out.epi(buf[K] + P, row);
                 cur = softmax_local<E, P, R>(buf[K], c, epis[K]);
                 publish_pair<G>(c.g, c.member, c.it, cur.m, cur.s);
@@ -442,7 +448,7 @@ __global__ void __launch_bounds__(R)
     }
     const WeightLds<P, R> wsrc{wslot};
 
-    if constexpr (G > 1 && kDeferredExchange && defer_split(kCfgRmsnorm, E::BYTES, VEC, P, R)) {
+    if constexpr (kDeferredExchange && defer_split(kCfgRmsnorm, E::BYTES, VEC, P, R, G)) {
         // Split rows, deferred exchange (see the softmax stream kernel).
         float buf[3][P];
         int64_t row = group;

@@ -453,7 +453,10 @@ __global__ void __launch_bounds__(R)
         float buf[3][P];
         int64_t row = group;
         auto load = [&](float *v, int64_t r) {
-            load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
+            if constexpr (VEC)
+                load_part_raw<E, C, R>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
+            else
+                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
         };
         load(buf[0], row);
         load(buf[1], row + groups);
@@ -461,6 +464,7 @@ __global__ void __launch_bounds__(R)
             constexpr int K = decltype(Kc)::value, KP = (K + 2) % 3;
             const bool more = row < M;
             if (more) {
+                if constexpr (VEC) widen_part<E, C>(buf[K]);
                 const float q = rmsnorm_local<E, P, R>(buf[K], wsrc, c);
                 publish_pair<G>(c.g, c.member, c.it, q, 0.0f);
             }

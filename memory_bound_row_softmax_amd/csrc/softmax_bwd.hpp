@@ -25,22 +25,37 @@
 
 namespace rr {
 
+// The row's dot product c over this workgroup's part (a: y, b: dy).
+template <class E, int P, int R>
+__device__ __forceinline__ float softmax_bwd_local(float *a, float *b, RowCtx &c) {
+    constexpr int C = P / E::VPC;
+    const int chunk0 = c.member * C * R;
+    if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.N, 0.0f, a);
+    const float t = tree_dot<P>(a, b);
+    return row_reduce<R>(t, c.one_reduction_slots(), c.l, OpSum{});
+}
+
+// dx = y * (dy - c) into a, then the store.
+template <class E, int P, int R, bool VEC>
+__device__ __forceinline__ void softmax_bwd_apply(float *a, const float *b, float t,
+                                                  RowView dxv, bool valid, const RowCtx &c) {
+    constexpr int C = P / E::VPC;
+    const int chunk0 = c.member * C * R;
+#pragma unroll
+    for (int j = 0; j < P; ++j) a[j] = a[j] * (b[j] - t);
+    store_part<E, C, R, VEC>(dxv, chunk0, c.l, c.N, valid, c.full, a);
+}
+
 // a: the lane's part of y, b: of dy; a becomes dx.
 template <class E, int P, int R, int G, bool VEC>
 __device__ __forceinline__ void softmax_bwd_finish(float *a, float *b, RowView dxv, bool valid,
                                                    RowCtx &c) {
-    constexpr int C = P / E::VPC;
-    const int chunk0 = c.member * C * R;
-    if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.N, 0.0f, a);
-    float t = tree_dot<P>(a, b);
-    t = row_reduce<R>(t, c.one_reduction_slots(), c.l, OpSum{});
+    float t = softmax_bwd_local<E, P, R>(a, b, c);
     if constexpr (G > 1) {
         exchange_pairs<G>(c.g, c.member, c.it, t, 0.0f, c.spin_limit, c.bcast, MergeSum{});
         t = c.bcast[0];
     }
-#pragma unroll
-    for (int j = 0; j < P; ++j) a[j] = a[j] * (b[j] - t);
-    store_part<E, C, R, VEC>(dxv, chunk0, c.l, c.N, valid, c.full, a);
+    softmax_bwd_apply<E, P, R, VEC>(a, b, t, dxv, valid, c);
 }
 
 template <class E, int P, int R, bool VEC>
@@ -83,17 +98,61 @@ __global__ void __launch_bounds__(R)
     c.full = part_full<E, C, R>(chunk0, N);
     const uint32_t rb = (uint32_t)N * E::BYTES;
 
-    float buf[2][2 * P];
-    stream_rows<2>(
-        (int64_t)group, M, groups, buf,
-        [&](float *v, int64_t r) {
-            load_part<E, C, R, VEC>(stream_row_view(y, r, M, rb), chunk0, c.l, v);
-            load_part<E, C, R, VEC>(stream_row_view(dy, r, M, rb), chunk0, c.l, v + P);
-        },
-        [&](float *v, int64_t r) {
-            softmax_bwd_finish<E, P, R, G, VEC>(v, v + P, stream_row_view(dx, r, M, rb), true, c);
+    if constexpr (kDeferredExchange && defer_split(kCfgSoftmaxBwd, E::BYTES, VEC, P, R, G)) {
+        // Split rows, deferred exchange (see the softmax stream kernel): row k's
+        // partial dot product is published before the wait for row k - 1's; rows in
+        // flight are kept as raw chunks.
+        float buf[3][2 * P];
+        int64_t row = group;
+        auto load = [&](float *v, int64_t r) {
+            if constexpr (VEC) {
+                load_part_raw<E, C, R>(stream_row_view(y, r, M, rb), chunk0, c.l, v);
+                load_part_raw<E, C, R>(stream_row_view(dy, r, M, rb), chunk0, c.l, v + P);
+            } else {
+                load_part<E, C, R, VEC>(stream_row_view(y, r, M, rb), chunk0, c.l, v);
+                load_part<E, C, R, VEC>(stream_row_view(dy, r, M, rb), chunk0, c.l, v + P);
+            }
+        };
+        load(buf[0], row);
+        load(buf[1], row + groups);
+        auto step = [&](auto Kc) -> bool {
+            constexpr int K = decltype(Kc)::value, KP = (K + 2) % 3;
+            const bool more = row < M;
+            if (more) {
+                if constexpr (VEC) {
+                    widen_part<E, C>(buf[K]);
+                    widen_part<E, C>(buf[K] + P);
+                }
+                const float t = softmax_bwd_local<E, P, R>(buf[K], buf[K] + P, c);
+                publish_pair<G>(c.g, c.member, c.it, t, 0.0f);
+            }
+            if (c.it > 0) {  // complete the previous row
+                wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeSum{});
+                softmax_bwd_apply<E, P, R, VEC>(buf[KP], buf[KP] + P, c.bcast[0],
+                                                stream_row_view(dx, row - groups, M, rb), true, c);
+            }
+            if (!more) return false;
+            load(buf[KP], row + 2 * (int64_t)groups);
             ++c.it;
-        });
+            row += groups;
+            return true;
+        };
+        while (stream_steps<0, 3>(step)) {
+        }
+    } else {
+        float buf[2][2 * P];
+        stream_rows<2>(
+            (int64_t)group, M, groups, buf,
+            [&](float *v, int64_t r) {
+                load_part<E, C, R, VEC>(stream_row_view(y, r, M, rb), chunk0, c.l, v);
+                load_part<E, C, R, VEC>(stream_row_view(dy, r, M, rb), chunk0, c.l, v + P);
+            },
+            [&](float *v, int64_t r) {
+                softmax_bwd_finish<E, P, R, G, VEC>(v, v + P, stream_row_view(dx, r, M, rb), true,
+                                                    c);
+                ++c.it;
+            });
+    }
     if constexpr (G > 1) {
         if (c.it > 0) depart_group<G>(c.g);
     }

@@ -72,7 +72,11 @@ FORCED_ROW = [  # (kind, P, R, G, M, N): split rows at small N, empty / partial 
     ("stream", 32, 512, 1, 3, 16384), ("stream", 16, 1024, 8, 200, 100000),
     ("block", 16, 16, 1, 100, 256), ("block", 32, 128, 1, 31, 4000),
     ("block", 16, 1024, 1, 5, 16384), ("block", 8, 512, 1, 77, 3000),
-    ("block", 64, 1024, 1, 6, 65536)]
+    ("block", 64, 1024, 1, 6, 65536),
+    # deferred exchange (8 or more workgroups per row): many rows per row group, so
+    # the four slot sets are reused many times over
+    ("stream", 64, 512, 8, 333, 200000), ("stream", 16, 1024, 16, 150, 250000),
+    ("stream", 16, 1024, 8, 1000, 70000)]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -254,13 +258,15 @@ def test_split_rows_are_deterministic_and_leave_the_workspace_zero(dtype):
     assert float((s - 1).abs().max()) < (1e-4 if dtype == "f32" else 2e-2)
 
 
-def test_grid_wait_timeout_is_reported_not_hung():
+@pytest.mark.parametrize("N", [131072, 262144])
+def test_grid_wait_timeout_is_reported_not_hung(N):
     """A spin limit of one poll makes split-row workgroups give up at once: the
-    kernel must still finish, report the timeout, and leave the workspace clean."""
-    M, N = 64, 131072
+    kernel must still finish, report the timeout, and leave the workspace clean
+    (131072: the exchange inside a row's step; 262144: the deferred exchange)."""
+    M = 64
     x = to_dev(_x(M, N, "f32"), "f32")
     ws = rr.workspace(rr.RR_OP_SOFTMAX, M, N, rr.RR_F32, DEV)
-    say("forced grid timeout")
+    say("forced grid timeout", N)
     with forced(spin=1):
         rr.rr_softmax_fwd(x, ws=ws)
     st = rr.rr_workspace_check(ws)

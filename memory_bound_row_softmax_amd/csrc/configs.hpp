@@ -134,7 +134,9 @@ constexpr int kBwdReduceTarget = 512;  // workgroups of the first reduction pass
 // the registers for bf16).  Used where it measured faster on MI355X: rows split
 // over 8 or more workgroups, softmax with 64 values on 512 lanes (+5-9 % at
 // 262144 elements), 16 values on 1024 lanes (+10-20 %) and the softmax backward
-// with 32 values on 512 lanes (+11-24 % at 131072 and 262144 elements).  With 2 workgroups per
+// with 32 values on 512 lanes (+11-24 % at 131072 and 262144 elements), and
+// RMSNorm with 32 values on 512 lanes (fp32 at 262144 elements: 16 workgroups
+// per row deferred beat 8 with 64 values by 5 %).  With 2 workgroups per
 // row the exchange is cheap and the deferral only delays the stores (bf16 softmax
 // at 65536 elements: -14 %); elsewhere the third buffer does not fit the
 // registers or costs a workgroup per CU (-2 to -20 % for 32 values on 512 lanes,
@@ -148,6 +150,7 @@ constexpr bool defer_split(int op, int elem_bytes, bool vec, int P, int R, int G
     (void)elem_bytes;
     if (G < 8) return false;
     if (op == kCfgSoftmaxBwd) return vec && P == 32 && R == 512;
+    if (op == kCfgRmsnorm && P == 32 && R == 512) return true;
     if (P == 64 && R == 512) return op == kCfgSoftmax;
     if (P == 16 && R == 1024) return vec || op != kCfgXentGrad;
     return false;

@@ -125,7 +125,7 @@ static const Choice kTuned[4][2][8] = {
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 16, 256, 1}, {false, 64, 256, 1},
       {true, 32, 1024, 1}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8}}},
     {{{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 16, 1024, 1},
-      {true, 16, 1024, 2}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 64, 512, 8}},
+      {true, 16, 1024, 2}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 32, 512, 16}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {true, 32, 1024, 1},
       {false, 64, 512, 1}, {true, 32, 1024, 2}, {true, 64, 512, 4}, {true, 64, 512, 8}}},
     // softmax backward (y and dy both held: at most 32 values per lane in a stream kernel)

@@ -359,24 +359,26 @@ struct WeightLds {
     }
 };
 
-// Sum of squares of this workgroup's part of the row, and t = x * w in place.
-template <class E, int P, int R, class Weight>
-__device__ __forceinline__ float rmsnorm_local(float *v, const Weight &w, RowCtx &c) {
+// Sum of squares of this workgroup's part of the row.
+template <class E, int P, int R>
+__device__ __forceinline__ float rmsnorm_local(float *v, RowCtx &c) {
     constexpr int C = P / E::VPC;
     const int chunk0 = c.member * C * R;
     if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.N, 0.0f, v);
-    float q = tree_sum_squares<P>(v);
-    w.apply(v, c.l);
+    const float q = tree_sum_squares<P>(v);
     return row_reduce<R>(q, c.one_reduction_slots(), c.l, OpSum{});
 }
 
-// y = t * r with r = rsqrt(Q / N + eps) for the row's sum of squares Q, then the store.
-template <class E, int P, int R, bool VEC>
-__device__ __forceinline__ void rmsnorm_apply(float *v, float Q, RowView yv, float *rstd_out,
-                                              float eps, bool valid, const RowCtx &c) {
+// y = (x * w) * r with r = rsqrt(Q / N + eps) for the row's sum of squares Q, then
+// the store.
+template <class E, int P, int R, bool VEC, class Weight>
+__device__ __forceinline__ void rmsnorm_apply(float *v, const Weight &w, float Q, RowView yv,
+                                              float *rstd_out, float eps, bool valid,
+                                              const RowCtx &c) {
     constexpr int C = P / E::VPC;
     const int chunk0 = c.member * C * R;
     const float r = __builtin_amdgcn_rsqf(Q / (float)c.N + eps);
+    w.apply(v, c.l);
 #pragma unroll
     for (int j = 0; j < P; ++j) v[j] *= r;
     store_part<E, C, R, VEC>(yv, chunk0, c.l, c.N, valid, c.full, v);
@@ -386,12 +388,12 @@ __device__ __forceinline__ void rmsnorm_apply(float *v, float Q, RowView yv, flo
 template <class E, int P, int R, int G, bool VEC, class Weight>
 __device__ __forceinline__ void rmsnorm_finish(float *v, const Weight &w, RowView yv,
                                                float *rstd_out, float eps, bool valid, RowCtx &c) {
-    float q = rmsnorm_local<E, P, R>(v, w, c);
+    float q = rmsnorm_local<E, P, R>(v, c);
     if constexpr (G > 1) {
         exchange_pairs<G>(c.g, c.member, c.it, q, 0.0f, c.spin_limit, c.bcast, MergeSum{});
         q = c.bcast[0];
     }
-    rmsnorm_apply<E, P, R, VEC>(v, q, yv, rstd_out, eps, valid, c);
+    rmsnorm_apply<E, P, R, VEC>(v, w, q, yv, rstd_out, eps, valid, c);
 }
 
 template <class E, int P, int R, bool VEC>
@@ -465,13 +467,14 @@ __global__ void __launch_bounds__(R)
             const bool more = row < M;
             if (more) {
                 if constexpr (VEC) widen_part<E, C>(buf[K]);
-                const float q = rmsnorm_local<E, P, R>(buf[K], wsrc, c);
+                const float q = rmsnorm_local<E, P, R>(buf[K], c);
                 publish_pair<G>(c.g, c.member, c.it, q, 0.0f);
             }
             if (c.it > 0) {  // complete the previous row
                 wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeSum{});
                 const int64_t rp = row - groups;
-                rmsnorm_apply<E, P, R, VEC>(buf[KP], c.bcast[0], stream_row_view(y, rp, M, rb),
+                rmsnorm_apply<E, P, R, VEC>(buf[KP], wsrc, c.bcast[0],
+                                            stream_row_view(y, rp, M, rb),
                                             rstd ? rstd + rp : nullptr, eps, true, c);
             }
             if (!more) return false;

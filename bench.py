@@ -338,7 +338,7 @@ def main() -> int:
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--sweep", action="store_true",
                     help="run every fixed and sweep workload; one JSON line each to --out")
-    ap.add_argument("--out", default=os.path.join("gpurun_out", "bench_sweep.jsonl"))
+    ap.add_argument("--out", default="bench_sweep.jsonl")
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 31))
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -34,9 +34,11 @@
 #define RR_STREAM_CONFIGS(X)                                                                \
     X(16, 1024, 1) X(16, 1024, 2) X(16, 1024, 4) X(16, 1024, 8) X(16, 1024, 16)             \
     X(32, 512, 1) X(32, 512, 2) X(32, 512, 4) X(32, 512, 8) X(32, 512, 16)                  \
+    X(32, 512, 32) X(32, 512, 64)                                                           \
     X(32, 1024, 1) X(32, 1024, 2) X(32, 1024, 4) X(32, 1024, 8) X(32, 1024, 16)             \
     X(64, 256, 1) X(64, 256, 2) X(64, 256, 4) X(64, 256, 8) X(64, 256, 16)                  \
-    X(64, 512, 1) X(64, 512, 2) X(64, 512, 4) X(64, 512, 8) X(64, 512, 16)
+    X(64, 512, 1) X(64, 512, 2) X(64, 512, 4) X(64, 512, 8) X(64, 512, 16)                  \
+    X(64, 512, 32)
 
 // RMSNorm backward (persistent, see rmsnorm_bwd.hpp), named by (P, R, G): a lane
 // keeps x, dy (two rows in flight), its w slice and its dw partials, about 6P + 45
@@ -136,7 +138,8 @@ constexpr int kBwdReduceTarget = 512;  // workgroups of the first reduction pass
 // 262144 elements), 16 values on 1024 lanes (+10-20 %) and the softmax backward
 // with 32 values on 512 lanes (+11-24 % at 131072 and 262144 elements), and
 // RMSNorm with 32 values on 512 lanes (fp32 at 262144 elements: 16 workgroups
-// per row deferred beat 8 with 64 values by 5 %).  With 2 workgroups per
+// per row deferred beat 8 with 64 values by 5 %; at 1048576 elements 64 deferred
+// beat 32 with 64 values by 15-22 %).  With 2 workgroups per
 // row the exchange is cheap and the deferral only delays the stores (bf16 softmax
 // at 65536 elements: -14 %); elsewhere the third buffer does not fit the
 // registers or costs a workgroup per CU (-2 to -20 % for 32 values on 512 lanes,

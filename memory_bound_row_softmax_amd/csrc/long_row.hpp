@@ -1,5 +1,6 @@
 // long_row.hpp -- softmax and RMSNorm forward for rows longer than the registers of
-// the split-row stream kernels can hold (more than P * R * G = 524288 elements).
+// the split-row stream kernels can hold (more than P * R * G = 1048576 elements, or
+// 262144 on the per-element path).
 //
 // The QuACK article (无需CUDA代码，给H100加速33%-50%), section 内存吞吐量, names the
 // alternative to reducing a long row across a cluster: an online algorithm that reads

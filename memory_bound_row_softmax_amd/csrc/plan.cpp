@@ -117,28 +117,39 @@ struct Choice {
     bool stream;
     int P, R, G;
 };
-constexpr int kTunedN[8] = {256, 1024, 4096, 16384, 32768, 65536, 131072, 262144};
+constexpr int kTunedBuckets = 10;
+constexpr int64_t kTunedN[kTunedBuckets] = {256,   1024,   4096,   16384,  32768,
+                                            65536, 131072, 262144, 524288, 1048576};
 //   [op: softmax, rmsnorm, softmax backward, cross-entropy gradient][dtype: f32, bf16][N bucket]
-static const Choice kTuned[4][2][8] = {
+// (the two longest buckets were timed at 4096 and 2048 rows)
+static const Choice kTuned[4][2][kTunedBuckets] = {
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {true, 64, 512, 1},
-      {true, 16, 1024, 2}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8}},
+      {true, 16, 1024, 2}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8},
+      {true, 64, 512, 16}, {true, 64, 512, 32}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 16, 256, 1}, {false, 64, 256, 1},
-      {true, 32, 1024, 1}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8}}},
+      {true, 32, 1024, 1}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8},
+      {true, 64, 512, 16}, {true, 64, 512, 32}}},
     {{{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 16, 1024, 1},
-      {true, 16, 1024, 2}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 32, 512, 16}},
+      {true, 16, 1024, 2}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 32, 512, 16},
+      {true, 32, 512, 32}, {true, 32, 512, 64}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {true, 32, 1024, 1},
-      {false, 64, 512, 1}, {true, 32, 1024, 2}, {true, 64, 512, 4}, {true, 64, 512, 8}}},
+      {false, 64, 512, 1}, {true, 32, 1024, 2}, {true, 64, 512, 4}, {true, 64, 512, 8},
+      {true, 32, 512, 32}, {true, 32, 512, 64}}},
     // softmax backward (y and dy both held: at most 32 values per lane in a stream kernel)
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 16, 256, 1}, {false, 32, 1024, 1},
-      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16}},
+      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
+      {true, 32, 512, 32}, {true, 32, 512, 64}},
      {{false, 8, 32, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 16, 1024, 1},
-      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16}}},
+      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
+      {true, 32, 512, 32}, {true, 32, 512, 64}}},
     // cross-entropy forward fused with its gradient (the softmax kernels; block kernels
     // hold longer rows here than for the softmax)
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {true, 16, 1024, 1},
-      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 64, 512, 8}},
+      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 64, 512, 8},
+      {true, 64, 512, 16}, {true, 64, 512, 32}},
      {{false, 16, 16, 1}, {false, 64, 16, 1}, {false, 16, 256, 1}, {false, 32, 512, 1},
-      {false, 64, 512, 1}, {false, 64, 1024, 1}, {true, 64, 512, 4}, {true, 32, 1024, 8}}},
+      {false, 64, 512, 1}, {false, 64, 1024, 1}, {true, 64, 512, 4}, {true, 32, 1024, 8},
+      {true, 64, 512, 16}, {true, 64, 512, 32}}},
 };
 
 static bool try_choice(int op, int dtype, bool vec, int64_t N, Choice c, Plan *p) {
@@ -162,8 +173,8 @@ static bool default_row(int op, int dtype, bool vec, int64_t N, Plan *p) {
     const int o = op == kOpRmsnorm ? 1 : op == kOpSoftmaxBwd ? 2 : op == kOpXentGrad ? 3 : 0;
     const int d = dtype == kBf16 ? 1 : 0;
     int k = 0;
-    while (k < 7 && kTunedN[k] < N) ++k;
-    if (N <= kTunedN[7]) {
+    while (k < kTunedBuckets - 1 && kTunedN[k] < N) ++k;
+    if (N <= kTunedN[kTunedBuckets - 1]) {
         Choice c = kTuned[o][d][k];
         // A stream workgroup that would be less than half full: the block
         // choice of the bucket below, widened to the row.
@@ -175,10 +186,12 @@ static bool default_row(int op, int dtype, bool vec, int64_t N, Plan *p) {
             if (try_choice(op, dtype, vec, N, b, p)) return true;
         }
     }
-    // Past the table, or a configuration the per-element path does not have:
-    // the first stream configuration that holds the row with the fewest workgroups.
+    // A configuration the per-element path does not have: the first stream
+    // configuration that holds the row with the fewest workgroups.  The per-element
+    // path stops at 16 workgroups per row: its longer rows measured no faster on
+    // chip than in the two-pass kernel.
     static const int kStreamPR[5][2] = {{64, 512}, {32, 1024}, {64, 256}, {32, 512}, {16, 1024}};
-    for (int g = 1; g <= 16; g *= 2)
+    for (int g = 1; g <= (vec ? 64 : 16); g *= 2)
         for (int j = 0; j < 5; ++j)
             if (try_choice(op, dtype, vec, N, Choice{true, kStreamPR[j][0], kStreamPR[j][1], g}, p))
                 return true;

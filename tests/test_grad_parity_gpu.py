@@ -52,7 +52,7 @@ FORCED = [("stream", 64, 256, 2, 300, 20000), ("stream", 32, 512, 16, 97, 70000)
           ("stream", 16, 1024, 1, 700, 16000), ("stream", 32, 512, 1, 3, 16384),
           ("stream", 16, 1024, 8, 200, 100000), ("block", 16, 16, 1, 100, 256),
           ("block", 32, 128, 1, 31, 4000), ("block", 16, 1024, 1, 5, 16384),
-          ("block", 64, 1024, 1, 6, 65536)]
+          ("block", 64, 1024, 1, 6, 65536), ("stream", 64, 512, 32, 5, 1_000_000)]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -184,7 +184,8 @@ SMBWD_FORCED = [("stream", 32, 512, 2, 300, 20000), ("stream", 32, 512, 16, 97, 
                 ("stream", 16, 1024, 1, 700, 16000), ("stream", 16, 1024, 16, 9, 262144),
                 ("stream", 32, 512, 1, 3, 16384), ("block", 16, 16, 1, 100, 256),
                 ("block", 32, 128, 1, 31, 4000), ("block", 64, 512, 1, 5, 32768),
-                ("block", 32, 1024, 1, 6, 30000), ("block", 8, 64, 1, 70, 300)]
+                ("block", 32, 1024, 1, 6, 30000), ("block", 8, 64, 1, 70, 300),
+                ("stream", 32, 512, 32, 40, 500000), ("stream", 32, 512, 64, 3, 1 << 20)]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)

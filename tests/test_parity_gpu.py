@@ -291,18 +291,40 @@ def test_stream_copy():
 
 # ------------------------------------------------------------- rows past on-chip capacity
 
-LONG = [(3, 524289), (2, 1 << 20), (2, 1_000_003), (1, 3_000_000)]
+# Aligned rows up to 2^20 elements stay on chip (split over 32 or 64 workgroups);
+# rows that are not 16-byte aligned hold at most 16 values on 1024 lanes of 16
+# workgroups on chip (262144 elements) and go to the two-pass kernel past that.
+LONG = [(3, 524289), (2, 1 << 21), (2, 1_000_003), (1, 3_000_000)]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("M,N", LONG)
 def test_long_rows_read_twice(M, N, dtype):
     code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
-    assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, M, N, code)["path"] == 4
+    vec = N * (4 if dtype == "f32" else 2) % 16 == 0  # the 128-bit path needs 16-byte rows
+    assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, M, N, code, vec)["path"] == 4
     say("long softmax", dtype, M, N)
     parity_softmax(_x(M, N, dtype, sigma=3.0), dtype, f"long softmax {dtype} {M}x{N}")
     say("long rmsnorm", dtype, M, N)
     parity_rmsnorm(_x(M, N, dtype), _w(N, dtype), 1e-6, dtype, f"long rmsnorm {dtype} {M}x{N}")
+
+
+SPLIT_WIDE = [(3, 524288), (3, 524296), (2, 1 << 20), (5, 1_000_000), (40, 786432)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N", SPLIT_WIDE)
+def test_rows_split_over_32_or_64_workgroups(M, N, dtype):
+    """Aligned rows from 2^19 elements up: one read, 16 to 64 workgroups per row (40
+    rows give each row group several rows, so every exchange slot set is used)."""
+    code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
+    for op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
+        p = rr.rr_plan_query(op, M, N, code)
+        assert p["path"] == 1 and p["groups_per_row"] >= 16, p
+    say("split32 softmax", dtype, M, N)
+    parity_softmax(_x(M, N, dtype, sigma=3.0), dtype, f"split32 softmax {dtype} {M}x{N}")
+    say("split32 rmsnorm", dtype, M, N)
+    parity_rmsnorm(_x(M, N, dtype), _w(N, dtype), 1e-6, dtype, f"split32 rmsnorm {dtype} {M}x{N}")
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -336,19 +358,23 @@ def test_long_rows_unaligned(dtype):
     check_out(from_dev(ys), oracle.rmsnorm(x_np, w_np, 1e-6), dtype, "long unaligned rmsnorm")
 
 
+@pytest.mark.parametrize("kind", [None, "long"])
 @pytest.mark.parametrize("dtype", DTYPES)
-def test_long_rows_many_rows_deterministic(dtype):
+def test_long_rows_many_rows_deterministic(dtype, kind):
+    """Many rows of 600000 elements: split over 32 workgroups (default) or the
+    two-pass kernel (forced)."""
     M, N = 200, 600000
     code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
     x_np = _x(M, N, dtype, sigma=2.0)
     x = to_dev(x_np, dtype)
-    ws = rr.workspace(rr.RR_OP_SOFTMAX, M, N, code, DEV)
     outs = []
-    for i in range(3):
-        say("long rows repeat", i, dtype)
-        outs.append(rr.rr_softmax_fwd(x, ws=ws))
-        torch.cuda.synchronize()
-        assert int(ws.count_nonzero()) == 0
+    with forced(kind=kind):
+        ws = rr.workspace(rr.RR_OP_SOFTMAX, M, N, code, DEV)
+        for i in range(3):
+            say("long rows repeat", kind, i, dtype)
+            outs.append(rr.rr_softmax_fwd(x, ws=ws))
+            torch.cuda.synchronize()
+            assert int(ws.count_nonzero()) == 0
     assert all(torch.equal(outs[0], o) for o in outs[1:])
     assert rr.rr_workspace_check(ws) == rr.RR_OK
     rows = np.arange(0, M, 23)

@@ -168,14 +168,20 @@ def test_rmsnorm_bwd_plans(dt, vec):
 def test_long_rows_take_the_two_pass_kernel(monkeypatch):
     for op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
         for dt in (rr.RR_F32, rr.RR_BF16):
-            on_chip = rr.rr_plan_query(op, 1000, 524288, dt)
-            assert on_chip["path"] == 1 and on_chip["max_n"] >= 524288
-            p = rr.rr_plan_query(op, 1000, 524289, dt)
+            on_chip = rr.rr_plan_query(op, 1000, 1 << 20, dt)
+            G = on_chip["groups_per_row"]
+            assert on_chip["path"] == 1 and G in (32, 64)
+            assert on_chip["vals_per_lane"] * on_chip["lanes_per_row"] * G == 1 << 20
+            assert on_chip["ws_bytes"] == 256 + 1000 * (64 + 64 * G)
+            p = rr.rr_plan_query(op, 1000, (1 << 20) + 8, dt)
             assert p["path"] == 4 and p["lanes_per_row"] == 512 and p["groups_per_row"] == 16
             assert p["ws_bytes"] == 256 + 1000 * (64 + 64 * 16)
-            assert rr.rr_plan_query(op, 10, 524289, dt, False)["vals_per_lane"] == 16
+            # the per-element path holds 16 * 1024 * 16 elements on chip
+            assert rr.rr_plan_query(op, 10, 262144, dt, False)["path"] == 1
+            q = rr.rr_plan_query(op, 10, 262145, dt, False)
+            assert q["path"] == 4 and q["vals_per_lane"] == 16
     monkeypatch.setenv("RR_FORCE_KIND", "long")
     assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 8, 1000, rr.RR_F32)["path"] == 4
     # the other ops have no long-row kernel
     with pytest.raises(rr.RRError):
-        rr.rr_plan_query(rr.RR_OP_SOFTMAX_BWD, 8, 1 << 20, rr.RR_F32)
+        rr.rr_plan_query(rr.RR_OP_SOFTMAX_BWD, 8, (1 << 20) + 4, rr.RR_F32)

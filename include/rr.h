@@ -48,7 +48,8 @@ typedef enum {
                                     eps < 0 or not finite, partial overlap of x and y, N too
                                     large for an int32 label (cross-entropy) */
     RR_ERR_UNSUPPORTED = 2,      /* N above the largest row the on-chip plan can hold, or the
-                                    co-resident grid does not fit on the device */
+                                    workgroups that share a row do not fit on the device at
+                                    once */
     RR_ERR_WORKSPACE = 3,        /* ws is NULL or smaller than rr_workspace_bytes() */
     RR_ERR_HIP = 4,              /* a HIP call failed; see rr_last_hip_error() */
     RR_ERR_GRID_TIMEOUT = 5      /* reported by rr_workspace_check(): a split row waited for

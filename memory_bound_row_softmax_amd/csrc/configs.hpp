@@ -165,7 +165,8 @@ constexpr int block_threads_for(int R) { return R < 256 ? 256 : R; }
 constexpr int rows_per_block_for(int R) { return block_threads_for(R) / R; }
 
 // Split-row workspace layout (bytes):
-//   [0, 256)                 header; word 0 is the error word (non-zero: a wait timed out)
+//   [0, 256)                 header: word 0 is the error word (non-zero: a wait timed out),
+//                            words 1 and 2 the ticket and exit counters of a launch
 //   256 + g * group_stride   record of row group g:
 //       +0                   departure counter (uint32)
 //       +64                  slots[kSlotSets][G][2] of uint64: (epoch << 32) | float bits

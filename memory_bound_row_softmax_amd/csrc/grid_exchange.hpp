@@ -26,7 +26,17 @@
 //    the last one to leave zeroes the group's slots and the counter, so the
 //    workspace is all zero again for the next launch.
 //
-// Every workgroup of the grid must be resident at once (cooperative launch).
+// Membership by start order, not by block id.  An ordinary launch does not promise
+// that all of a grid's workgroups run at once, and a cooperative launch (which does)
+// cost 16-20 us more per launch on MI355X.  So each workgroup takes a ticket from a
+// counter in the workspace header when it starts, and ticket t makes it member
+// t % G of row group t / G.  Tickets are handed out in start order, so at any moment
+// every group but the one holding the latest ticket has all its members started:
+// those groups never wait on a workgroup that has not started, finish their rows
+// and exit, and the free slots then start the missing members of the last group.
+// The grid drains as long as G workgroups fit on the device at once (the planner
+// sizes the grid from the occupancy query, so all of it normally runs at once).
+// The last workgroup to leave the grid zeroes the ticket and exit counters.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -144,20 +154,40 @@ __device__ __forceinline__ void depart_group(GroupRef g) {
     }
 }
 
-// Which row group and member this workgroup is.  Consecutive block ids go to
-// different XCDs (round-robin dispatch), so members of one group are taken from
-// blocks with the same id modulo 8, which keeps a row's exchange inside one XCD
-// when the dispatcher behaves that way.  Correctness does not depend on it.
+// Header words of the workspace: the error word, then the ticket and exit counters.
+constexpr int kWsTicketWord = 1;
+constexpr int kWsExitWord = 2;
+
+// Which row group and member this workgroup is, from its ticket (see above).  The
+// grid is groups * G workgroups; the ticket is taken modulo that, so that a counter
+// left non-zero (a launch that never finished) still gives every (group, member)
+// exactly once.  Called by every thread; uses one barrier.
 template <int G>
-__device__ __forceinline__ void group_of_block(int groups, int *group, int *member) {
-    const int b = blockIdx.x;
-    if (groups % 8 == 0) {
-        const int xcd = b & 7, slot = b >> 3;
-        *group = xcd * (groups >> 3) + slot / G;
-        *member = slot % G;
-    } else {
-        *group = b / G;
-        *member = b % G;
+__device__ __forceinline__ void join_grid(uint8_t *ws, int groups, int *group, int *member) {
+    __shared__ int ticket;
+    if (threadIdx.x == 0) {
+        uint32_t *ctr = reinterpret_cast<uint32_t *>(ws) + kWsTicketWord;
+        const uint32_t t =
+            __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ticket = (int)(t % ((uint32_t)groups * (uint32_t)G));
+    }
+    __syncthreads();
+    *group = ticket / G;
+    *member = ticket % G;
+}
+
+// Called once by every workgroup of a split-row grid, as its last action.  The exit
+// count is incremented with release and acquire order, so the last workgroup's reset
+// of the ticket counter comes after every workgroup's ticket.
+__device__ __forceinline__ void leave_grid(uint8_t *ws) {
+    if (threadIdx.x == 0) {
+        uint32_t *h = reinterpret_cast<uint32_t *>(ws);
+        const uint32_t before = __hip_atomic_fetch_add(h + kWsExitWord, 1u, __ATOMIC_ACQ_REL,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+        if (before == gridDim.x - 1u) {
+            __hip_atomic_store(h + kWsTicketWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(h + kWsExitWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 

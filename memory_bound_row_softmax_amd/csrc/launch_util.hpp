@@ -10,19 +10,19 @@
 
 namespace rr {
 
-// Row groups of a cooperative (every block resident) launch with G blocks per row:
-// as many as fit on the device at once, at most kMaxGroups and at most M, and a
-// multiple of 8 when there are at least 8 (so each XCD gets whole groups).
+// Row groups of a persistent launch with G workgroups per row: as many as fit on
+// the device at once (so the whole grid normally runs at once), at most kMaxGroups
+// and at most M.  Split rows need G workgroups of the kernel to fit at once (their
+// members wait for each other; see grid_exchange.hpp).
 template <class K>
-hipError_t cooperative_groups(K kernel, int block, int G, int64_t M, const LaunchArgs &a,
-                              int *groups) {
+hipError_t resident_groups(K kernel, int block, int G, int64_t M, const LaunchArgs &a,
+                           int *groups) {
     int per_cu = 0;
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0);
     if (e != hipSuccess) return e;
     int64_t g = (int64_t)per_cu * a.num_cus / G;
     if (g > kMaxGroups) g = kMaxGroups;
     if (g > M) g = M;
-    if (g >= 8) g -= g % 8;
     if (g < 1) return hipErrorCooperativeLaunchTooLarge;
     *groups = (int)g;
     return hipSuccess;

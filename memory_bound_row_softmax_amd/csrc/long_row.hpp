@@ -83,7 +83,7 @@ __global__ void __launch_bounds__(R)
     __shared__ float bcast[3];
     RowCtx c{N, (int)threadIdx.x, 0, 0, true, nullptr, nullptr, bcast, GroupRef{}, spin_limit};
     int group;
-    group_of_block<G>(groups, &group, &c.member);
+    join_grid<G>(ws, groups, &group, &c.member);
     c.g = group_ref<G>(ws, group);
     if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
     const int l = threadIdx.x;
@@ -151,6 +151,7 @@ __global__ void __launch_bounds__(R)
         ++c.it;
     }
     if (c.it > 0) depart_group<G>(c.g);
+    leave_grid(ws);
 }
 
 }  // namespace rr

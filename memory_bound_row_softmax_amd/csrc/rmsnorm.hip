@@ -24,24 +24,13 @@ hipError_t launch_stream(const void *x, const void *w, void *y, float *rstd, int
                          int64_t N, float eps, void *ws, const LaunchArgs &a) {
     auto kernel = rmsnorm_stream_kernel<E, P, R, G, VEC>;
     int groups;
-    hipError_t e = cooperative_groups(kernel, R, G, M, a, &groups);
+    hipError_t e = resident_groups(kernel, R, G, M, a, &groups);
     if (e != hipSuccess) return e;
-    const char *xp = static_cast<const char *>(x);
-    const char *wp = static_cast<const char *>(w);
-    char *yp = static_cast<char *>(y);
-    uint8_t *wsp = static_cast<uint8_t *>(ws);
-    int n = (int)N;
-    int spin = a.spin_limit;
-    if constexpr (G == 1) {
-        // no workgroup waits for another: an ordinary launch
-        hipLaunchKernelGGL(kernel, dim3(groups), dim3(R), 0, a.stream, xp, wp, yp, rstd, M, n,
-                           eps, wsp, groups, spin);
-        return hipGetLastError();
-    } else {
-        void *args[] = {&xp, &wp, &yp, &rstd, &M, &n, &eps, &wsp, &groups, &spin};
-        return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(kernel),
-                                          dim3(groups * G), dim3(R), args, 0, a.stream);
-    }
+    hipLaunchKernelGGL(kernel, dim3(groups * G), dim3(R), 0, a.stream,
+                       static_cast<const char *>(x), static_cast<const char *>(w),
+                       static_cast<char *>(y), rstd, M, (int)N, eps, static_cast<uint8_t *>(ws),
+                       groups, a.spin_limit);
+    return hipGetLastError();
 }
 
 template <class E, bool VEC>

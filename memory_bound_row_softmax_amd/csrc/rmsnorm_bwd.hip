@@ -26,9 +26,9 @@ hipError_t launch_cfg(const Plan &p, const void *x, const void *w, const void *d
         if (g > p.max_parts) g = p.max_parts;
         groups = (int)g;
     } else {
-        hipError_t e = cooperative_groups(kernel, threads, G, M, a, &groups);
+        hipError_t e = resident_groups(kernel, threads, G, M, a, &groups);
         if (e != hipSuccess) return e;
-        if (groups > p.max_parts) groups = p.max_parts - p.max_parts % (p.max_parts >= 8 ? 8 : 1);
+        if (groups > p.max_parts) groups = p.max_parts;
     }
     *parts = groups;
     const char *xp = static_cast<const char *>(x);
@@ -38,15 +38,9 @@ hipError_t launch_cfg(const Plan &p, const void *x, const void *w, const void *d
     float *part = reinterpret_cast<float *>(ws + p.part_off);
     int n = (int)N;
     int spin = a.spin_limit;
-    if constexpr (G == 1) {
-        hipLaunchKernelGGL(kernel, dim3(groups), dim3(threads), 0, a.stream, xp, wp, dyp, rstd,
-                           dxp, part, M, n, ws, groups, spin);
-        return hipGetLastError();
-    } else {
-        void *args[] = {&xp, &wp, &dyp, &rstd, &dxp, &part, &M, &n, &ws, &groups, &spin};
-        return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(kernel),
-                                          dim3(groups * G), dim3(threads), args, 0, a.stream);
-    }
+    hipLaunchKernelGGL(kernel, dim3(groups * G), dim3(threads), 0, a.stream, xp, wp, dyp, rstd,
+                       dxp, part, M, n, ws, groups, spin);
+    return hipGetLastError();
 }
 
 template <class E, bool VEC>

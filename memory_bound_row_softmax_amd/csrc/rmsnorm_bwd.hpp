@@ -127,7 +127,7 @@ __global__ void __launch_bounds__(bwd_threads(R, G))
     RowCtx c{N, l, 0, 0, true, red[0] + sub * W, red[1] + sub * W, bcast, GroupRef{}, spin_limit};
     int group = blockIdx.x;
     if constexpr (G > 1) {
-        group_of_block<G>(groups, &group, &c.member);
+        join_grid<G>(ws, groups, &group, &c.member);
         c.g = group_ref<G>(ws, group);
         if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
     }
@@ -170,6 +170,7 @@ __global__ void __launch_bounds__(bwd_threads(R, G))
         });
     if constexpr (G > 1) {
         if (c.it > 0) depart_group<G>(c.g);
+        leave_grid(ws);
     }
 
     // One partial row per workgroup (its lane groups summed in order through LDS).

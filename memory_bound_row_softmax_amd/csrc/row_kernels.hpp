@@ -12,8 +12,8 @@
 // path.  Two kernel kinds per op (see configs.hpp): block kernels (G = 1, one
 // workgroup per few rows) and stream kernels (persistent, one row per workgroup
 // at a time, the next row's loads issued before the current row is reduced;
-// with G > 1 the grid is cooperative and the G workgroups of a row meet in the
-// workspace).
+// with G > 1 the G workgroups of a row meet in the workspace, grouped by the order
+// in which they start).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -246,7 +246,7 @@ __global__ void __launch_bounds__(R)
     RowCtx c{N, (int)threadIdx.x, 0, 0, true, red_max, red_sum, bcast, GroupRef{}, spin_limit};
     int group = blockIdx.x;
     if constexpr (G > 1) {
-        group_of_block<G>(groups, &group, &c.member);
+        join_grid<G>(ws, groups, &group, &c.member);
         c.g = group_ref<G>(ws, group);
         if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
     }
@@ -319,6 +319,7 @@ __global__ void __launch_bounds__(R)
     }
     if constexpr (G > 1) {
         if (c.it > 0) depart_group<G>(c.g);
+        leave_grid(ws);
     }
 }
 
@@ -431,7 +432,7 @@ __global__ void __launch_bounds__(R)
     RowCtx c{N, (int)threadIdx.x, 0, 0, true, red[0], red[1], bcast, GroupRef{}, spin_limit};
     int group = blockIdx.x;
     if constexpr (G > 1) {
-        group_of_block<G>(groups, &group, &c.member);
+        join_grid<G>(ws, groups, &group, &c.member);
         c.g = group_ref<G>(ws, group);
         if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
     }
@@ -500,6 +501,7 @@ __global__ void __launch_bounds__(R)
     }
     if constexpr (G > 1) {
         if (c.it > 0) depart_group<G>(c.g);
+        leave_grid(ws);
     }
 }
 

@@ -23,23 +23,13 @@ hipError_t launch_stream(const void *y, const void *dy, void *dx, int64_t M, int
                          const LaunchArgs &a) {
     auto kernel = softmax_bwd_stream_kernel<E, P, R, G, VEC>;
     int groups;
-    hipError_t e = cooperative_groups(kernel, R, G, M, a, &groups);
+    hipError_t e = resident_groups(kernel, R, G, M, a, &groups);
     if (e != hipSuccess) return e;
-    const char *yp = static_cast<const char *>(y);
-    const char *dyp = static_cast<const char *>(dy);
-    char *dxp = static_cast<char *>(dx);
-    uint8_t *wsp = static_cast<uint8_t *>(ws);
-    int n = (int)N;
-    int spin = a.spin_limit;
-    if constexpr (G == 1) {
-        hipLaunchKernelGGL(kernel, dim3(groups), dim3(R), 0, a.stream, yp, dyp, dxp, M, n, wsp,
-                           groups, spin);
-        return hipGetLastError();
-    } else {
-        void *args[] = {&yp, &dyp, &dxp, &M, &n, &wsp, &groups, &spin};
-        return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(kernel),
-                                          dim3(groups * G), dim3(R), args, 0, a.stream);
-    }
+    hipLaunchKernelGGL(kernel, dim3(groups * G), dim3(R), 0, a.stream,
+                       static_cast<const char *>(y), static_cast<const char *>(dy),
+                       static_cast<char *>(dx), M, (int)N, static_cast<uint8_t *>(ws), groups,
+                       a.spin_limit);
+    return hipGetLastError();
 }
 
 template <class E, bool VEC>

@@ -90,7 +90,7 @@ __global__ void __launch_bounds__(R)
     RowCtx c{N, (int)threadIdx.x, 0, 0, true, red[0], red[1], bcast, GroupRef{}, spin_limit};
     int group = blockIdx.x;
     if constexpr (G > 1) {
-        group_of_block<G>(groups, &group, &c.member);
+        join_grid<G>(ws, groups, &group, &c.member);
         c.g = group_ref<G>(ws, group);
         if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
     }
@@ -155,6 +155,7 @@ __global__ void __launch_bounds__(R)
     }
     if constexpr (G > 1) {
         if (c.it > 0) depart_group<G>(c.g);
+        leave_grid(ws);
     }
 }
 

@@ -25,24 +25,12 @@ hipError_t stream(const void *x, void *y, int64_t M, int64_t N, void *ws, const 
                   const LaunchArgs &a) {
     auto kernel = softmax_stream_kernel<E, P, R, G, VEC, Out>;
     int groups;
-    hipError_t e = cooperative_groups(kernel, R, G, M, a, &groups);
+    hipError_t e = resident_groups(kernel, R, G, M, a, &groups);
     if (e != hipSuccess) return e;
-    const char *xp = static_cast<const char *>(x);
-    char *yp = static_cast<char *>(y);
-    uint8_t *wsp = static_cast<uint8_t *>(ws);
-    int n = (int)N;
-    int spin = a.spin_limit;
-    Out o = out;
-    if constexpr (G == 1) {
-        // no workgroup waits for another: an ordinary launch
-        hipLaunchKernelGGL(kernel, dim3(groups), dim3(R), 0, a.stream, xp, yp, M, n, wsp, groups,
-                           spin, o);
-        return hipGetLastError();
-    } else {
-        void *args[] = {&xp, &yp, &M, &n, &wsp, &groups, &spin, &o};
-        return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(kernel),
-                                          dim3(groups * G), dim3(R), args, 0, a.stream);
-    }
+    hipLaunchKernelGGL(kernel, dim3(groups * G), dim3(R), 0, a.stream,
+                       static_cast<const char *>(x), static_cast<char *>(y), M, (int)N,
+                       static_cast<uint8_t *>(ws), groups, a.spin_limit, out);
+    return hipGetLastError();
 }
 
 template <class E, bool VEC, class Out>

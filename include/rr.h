@@ -177,7 +177,8 @@ typedef struct {
                            2: cross-entropy forward (streaming online max and sum),
                            3: persistent stream kernel, one workgroup per row */
     int vectorized;     /* 1: 128-bit path, 0: per-element path */
-    int vals_per_lane;  /* fp32 values each lane holds (row paths) or loads per step (streaming) */
+    int vals_per_lane;  /* values each lane holds (row paths: fp32 values, or 128 bf16 values
+                           kept packed by the bf16 RMSNorm) or loads per step (streaming) */
     int lanes_per_row;  /* lanes that share one row inside a workgroup */
     int groups_per_row; /* workgroups per row (1 except on path 1) */
     int block_threads;  /* threads per workgroup */

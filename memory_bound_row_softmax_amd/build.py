@@ -25,7 +25,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librr.so")
 
 SOURCES = ["api.cpp", "plan.cpp", "softmax.hip", "rmsnorm.hip", "xent.hip", "xent_grad.hip",
-           "softmax_bwd.hip", "rmsnorm_bwd.hip", "long_row.hip", "copy.hip"]
+           "softmax_bwd.hip", "rmsnorm_bwd.hip", "long_row.hip", "packed.hip", "copy.hip"]
 ARCH = "gfx950"
 
 

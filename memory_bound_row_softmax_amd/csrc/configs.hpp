@@ -40,6 +40,12 @@
     X(64, 512, 1) X(64, 512, 2) X(64, 512, 4) X(64, 512, 8) X(64, 512, 16)                  \
     X(64, 512, 32)
 
+// Packed bf16 RMSNorm stream kernels (128-bit path only, see packed_bf16.hpp),
+// named by (R, G): each lane keeps kPackedP = 128 bf16 values as 64 VGPRs of raw
+// chunks.  A plan names them with P = kPackedP.
+constexpr int kPackedP = 128;
+#define RR_PACKED_CONFIGS(X) X(512, 1) X(512, 2) X(512, 4) X(512, 8) X(512, 16)
+
 // RMSNorm backward (persistent, see rmsnorm_bwd.hpp), named by (P, R, G): a lane
 // keeps x, dy (two rows in flight), its w slice and its dw partials, about 6P + 45
 // VGPRs, so P <= 32 on up to 512 lanes and P = 8 on 1024 lanes.

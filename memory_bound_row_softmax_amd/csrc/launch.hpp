@@ -33,6 +33,8 @@ hipError_t launch_rmsnorm_bwd(const Plan &p, int dtype, const void *x, const voi
 hipError_t launch_long_row(const Plan &p, int op, int dtype, const void *x, const void *w,
                            void *y, float *rstd, int64_t M, int64_t N, float eps, void *ws,
                            const LaunchArgs &a);
+hipError_t launch_rmsnorm_packed(const Plan &p, const void *x, const void *w, void *y, float *rstd,
+                                 int64_t M, int64_t N, float eps, void *ws, const LaunchArgs &a);
 hipError_t launch_copy(const void *src, void *dst, size_t bytes, const LaunchArgs &a);
 
 }  // namespace rr

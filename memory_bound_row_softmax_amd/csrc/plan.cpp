@@ -41,6 +41,14 @@ bool block_config_ok(int op, int dtype, bool vec, int P, int R) {
 }
 
 bool stream_config_ok(int op, int dtype, bool vec, int P, int R, int G) {
+    if (P == kPackedP) {  // packed bf16: RMSNorm forward, 128-bit path
+        if (dtype != kBf16 || !vec || op != kOpRmsnorm) return false;
+#define RR_X(r, g) \
+    if (R == r && G == g) return true;
+        RR_PACKED_CONFIGS(RR_X)
+#undef RR_X
+        return false;
+    }
 #define RR_X(p, r, g)                    \
     if (P == p && R == r && G == g)      \
         return stream_config_enabled(cfg_op(op), elem_bytes(dtype), vec, p, r, g);
@@ -133,8 +141,8 @@ static const Choice kTuned[4][2][kTunedBuckets] = {
       {true, 16, 1024, 2}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 32, 512, 16},
       {true, 32, 512, 32}, {true, 32, 512, 64}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {true, 32, 1024, 1},
-      {false, 64, 512, 1}, {true, 32, 1024, 2}, {true, 64, 512, 4}, {true, 64, 512, 8},
-      {true, 32, 512, 32}, {true, 32, 512, 64}}},
+      {false, 64, 512, 1}, {true, 32, 1024, 2}, {true, 64, 512, 4}, {true, kPackedP, 512, 4},
+      {true, kPackedP, 512, 8}, {true, kPackedP, 512, 16}}},
     // softmax backward (y and dy both held: at most 32 values per lane in a stream kernel)
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 16, 256, 1}, {false, 32, 1024, 1},
       {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},

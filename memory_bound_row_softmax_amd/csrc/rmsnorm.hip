@@ -59,6 +59,8 @@ hipError_t dispatch(const Plan &p, const void *x, const void *w, void *y, float 
 hipError_t launch_rmsnorm(const Plan &p, int dtype, const void *x, const void *w, void *y,
                           float *rstd, int64_t M, int64_t N, float eps, void *ws,
                           const LaunchArgs &a) {
+    if (p.P == kPackedP)  // packed bf16 rows (packed.hip)
+        return launch_rmsnorm_packed(p, x, w, y, rstd, M, N, eps, ws, a);
     if (dtype == kF32)
         return p.vec ? dispatch<F32, true>(p, x, w, y, rstd, M, N, eps, ws, a)
                      : dispatch<F32, false>(p, x, w, y, rstd, M, N, eps, ws, a);

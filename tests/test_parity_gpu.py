@@ -100,6 +100,28 @@ def test_forced_row_plans(kind, P, R, G, M, N, dtype):
     assert ran > 0
 
 
+PACKED = [  # (G, M, N): packed bf16 RMSNorm (128 values per lane on 512 lanes)
+    (1, 300, 65536), (1, 700, 20000), (1, 3, 8), (2, 100, 131072), (2, 61, 65544),
+    (4, 90, 200000), (8, 40, 524288), (16, 7, 1000000), (16, 5, 300000), (16, 33, 1 << 20)]
+
+
+@pytest.mark.parametrize("G,M,N", PACKED)
+def test_packed_bf16_rmsnorm(G, M, N):
+    """bf16 rows kept as raw chunks: one workgroup up to 65536 elements, then split;
+    ragged rows, members with an empty part (300000 on 16), many rows per group."""
+    with forced(128, 512, G, kind="stream"):
+        p = rr.rr_plan_query(rr.RR_OP_RMSNORM, M, N, rr.RR_BF16)
+        assert p["vals_per_lane"] == 128 and p["groups_per_row"] == G
+        say("rmsnorm packed", G, M, N)
+        parity_rmsnorm(_x(M, N, "bf16", sigma=2.0), _w(N, "bf16"), 1e-6, "bf16",
+                       f"rmsnorm packed {G} {M}x{N}")
+        # only RMSNorm, only bf16, only on the 128-bit path
+        for args in ((rr.RR_OP_RMSNORM, M, N, rr.RR_F32), (rr.RR_OP_RMSNORM, M, N, rr.RR_BF16, False),
+                     (rr.RR_OP_SOFTMAX, M, N, rr.RR_BF16), (rr.RR_OP_XENT_GRAD, M, N, rr.RR_BF16)):
+            with pytest.raises(rr.RRError):
+                rr.rr_plan_query(*args)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("P,R", [(16, 16), (16, 1024), (32, 64), (32, 512)])
 def test_forced_xent_plans(P, R, dtype):
@@ -314,13 +336,15 @@ SPLIT_WIDE = [(3, 524288), (3, 524296), (2, 1 << 20), (5, 1_000_000), (40, 78643
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("M,N", SPLIT_WIDE)
-def test_rows_split_over_32_or_64_workgroups(M, N, dtype):
-    """Aligned rows from 2^19 elements up: one read, 16 to 64 workgroups per row (40
-    rows give each row group several rows, so every exchange slot set is used)."""
+def test_rows_split_over_many_workgroups(M, N, dtype):
+    """Aligned rows from 2^19 elements up: one read, 8 to 64 workgroups per row (bf16
+    RMSNorm packed, 8 or 16; 40 rows give each row group several rows, so every
+    exchange slot set is used)."""
     code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
     for op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
         p = rr.rr_plan_query(op, M, N, code)
-        assert p["path"] == 1 and p["groups_per_row"] >= 16, p
+        assert p["path"] == 1 and p["groups_per_row"] >= 8, p
+        assert p["vals_per_lane"] * p["lanes_per_row"] * p["groups_per_row"] >= N
     say("split32 softmax", dtype, M, N)
     parity_softmax(_x(M, N, dtype, sigma=3.0), dtype, f"split32 softmax {dtype} {M}x{N}")
     say("split32 rmsnorm", dtype, M, N)

@@ -131,10 +131,8 @@ constexpr long long kLongMaxN = 1ll << 28;
 constexpr bool rmsbwd_config_enabled(bool vec, int P) { return vec || P <= 16; }
 
 // RMSNorm backward partial rows: at most kBwdMaxWorkgroups / G row groups, each
-// writing one fp32 partial row of dw; the column reduction first adds them in
-// slices (about kBwdReduceTarget workgroups in all), then adds the slices.
+// writing one fp32 partial row of dw; one column reduction pass adds them.
 constexpr int kBwdMaxWorkgroups = 1024;
-constexpr int kBwdReduceTarget = 512;  // workgroups of the first reduction pass
 
 // Split rows with the deferred exchange: a row's partial is published, the next
 // row reduced, and only then the wait for the peers' partials of the first row

@@ -74,19 +74,6 @@ bool rmsbwd_config_ok(int dtype, bool vec, int P, int R, int G) {
     return false;
 }
 
-// About sqrt(parts) slices (both passes then read about sqrt(parts) rows per
-// thread), more when there are few column tiles, so that the first pass has
-// enough workgroups; at least 8 rows per slice.
-int rmsbwd_slices(int64_t parts, int64_t N) {
-    const int64_t tiles = (N + 1023) / 1024;  // 256 threads x 4 columns
-    int64_t s = 1;
-    while (s * s < parts) s *= 2;
-    while (s * tiles < kBwdReduceTarget / 4 && s * 16 <= parts) s *= 2;
-    if (s > parts / 8) s = parts / 8;
-    if (s < 1) s = 1;
-    return (int)s;
-}
-
 size_t grid_ws_bytes(int G, int64_t M) {
     int64_t groups = M < kMaxGroups ? M : kMaxGroups;
     if (groups < 1) groups = 1;
@@ -278,11 +265,9 @@ static PlanResult plan_rmsnorm_bwd(int dtype, int64_t M, int64_t N, bool vec, Pl
     if (parts > blocks) parts = blocks;
     if (parts < 1) parts = 1;
     p.max_parts = (int)parts;
-    p.slices = rmsbwd_slices(parts, N);
     const size_t exch = G > 1 ? align256(grid_ws_bytes(G, parts)) : 0;
     p.part_off = exch;
-    p.slice_off = p.part_off + align256((size_t)parts * (size_t)N * 4u);
-    p.ws_bytes = p.slice_off + (p.slices > 1 ? align256((size_t)p.slices * (size_t)N * 4u) : 0);
+    p.ws_bytes = p.part_off + align256((size_t)parts * (size_t)N * 4u);
     *out = p;
     return kPlanOk;
 }

@@ -28,10 +28,10 @@ enum PlanResult { kPlanOk = 0, kPlanUnsupported = 1, kPlanInvalid = 2 };
 
 struct Plan {
     int path = kPathRow;
-    // RMSNorm backward: byte offsets in the workspace of the dw partial rows and of
-    // the reduction slices, their counts at most, and the slices of the first pass.
-    size_t part_off = 0, slice_off = 0;
-    int max_parts = 0, slices = 0;
+    // RMSNorm backward: byte offset in the workspace of the dw partial rows, and
+    // their count at most.
+    size_t part_off = 0;
+    int max_parts = 0;
     bool stream = false;  // persistent, double-buffered stream kernel
     bool vec = true;
     int P = 0, R = 0, G = 1;
@@ -45,9 +45,6 @@ bool block_config_ok(int op, int dtype, bool vec, int P, int R);
 bool stream_config_ok(int op, int dtype, bool vec, int P, int R, int G);
 bool xent_config_exists(int P, int R);
 bool rmsbwd_config_ok(int dtype, bool vec, int P, int R, int G);
-
-// Slices of the first dw reduction pass for `parts` partial rows of N columns.
-int rmsbwd_slices(int64_t parts, int64_t N);
 
 // Chooses the plan.  `vec` says whether the 128-bit path is usable for these
 // pointers.  Test-only overrides come from the environment: RR_FORCE_KIND

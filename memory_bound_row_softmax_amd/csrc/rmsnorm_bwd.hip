@@ -56,32 +56,18 @@ hipError_t dispatch(const Plan &p, const void *x, const void *w, const void *dy,
     return hipErrorInvalidValue;
 }
 
-// dw = the sum of `parts` partial rows, in row order: first in slices (one pass
-// over all partial rows with enough workgroups to keep HBM busy), then the slices.
+// dw = the sum of `parts` partial rows (one pass, see rmsnorm_dw_reduce).
 hipError_t reduce_dw(const Plan &p, uint8_t *ws, int parts, int64_t N, float *dw,
                      const LaunchArgs &a) {
     const float *part = reinterpret_cast<const float *>(ws + p.part_off);
-    float *slice = reinterpret_cast<float *>(ws + p.slice_off);
-    const int n = (int)N;
-    const unsigned tiles = (unsigned)((N + 1023) / 1024);
-    const bool vec4 = N % 4 == 0;
-    auto pass = [&](const float *in, int rows, int per, int nslices, float *out) {
-        if (vec4)
-            hipLaunchKernelGGL(rmsnorm_dw_reduce<true>, dim3(tiles, (unsigned)nslices), dim3(256),
-                               0, a.stream, in, rows, per, n, out);
-        else
-            hipLaunchKernelGGL(rmsnorm_dw_reduce<false>, dim3(tiles, (unsigned)nslices), dim3(256),
-                               0, a.stream, in, rows, per, n, out);
-        return hipGetLastError();
-    };
-    int s = rmsbwd_slices(parts, N);
-    if (s > p.slices) s = p.slices;
-    if (s <= 1) return pass(part, parts, parts > 0 ? parts : 1, 1, dw);
-    const int per = (parts + s - 1) / s;
-    s = (parts + per - 1) / per;
-    hipError_t e = pass(part, parts, per, s, slice);
-    if (e != hipSuccess) return e;
-    return pass(slice, s, s, 1, dw);
+    const unsigned tiles = (unsigned)((N + 4 * kDwTileQuads - 1) / (4 * kDwTileQuads));
+    if (N % 4 == 0)
+        hipLaunchKernelGGL(rmsnorm_dw_reduce<true>, dim3(tiles), dim3(256), 0, a.stream, part,
+                           parts, (int)N, dw);
+    else
+        hipLaunchKernelGGL(rmsnorm_dw_reduce<false>, dim3(tiles), dim3(256), 0, a.stream, part,
+                           parts, (int)N, dw);
+    return hipGetLastError();
 }
 
 }  // namespace

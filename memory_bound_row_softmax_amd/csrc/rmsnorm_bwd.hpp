@@ -10,9 +10,9 @@
 // forward's shape: x and dy read once, dx written once.  dw is a reduction down the
 // columns, over all M rows: every persistent workgroup keeps the partial sums of its
 // columns in registers across the rows it processes, combines its lane groups
-// through LDS and writes one fp32 partial row to the workspace; two small passes
-// (rmsnorm_dw_reduce) then add the partial rows in a fixed order, so dw is the same
-// bits on every run.
+// through LDS and writes one fp32 partial row to the workspace; one small pass
+// (rmsnorm_dw_reduce) then adds the partial rows in a fixed order, so dw is the
+// same bits on every run.
 //
 // Kernel: a persistent grid; with G = 1 a workgroup holds rows_per_block_for(R)
 // rows at a time (R lanes each) and walks the row blocks group, group + groups,
@@ -196,54 +196,76 @@ __global__ void __launch_bounds__(bwd_threads(R, G))
     }
 }
 
-// dw partial sums: out[s][j] = sum of rows s * per .. min(rows, (s + 1) * per) - 1 of
-// `in` (rows x N fp32), added in row order.  One thread per 4 columns; `in` and
-// `out` are 16-byte aligned and N is a multiple of 4 when VEC4.  Eight rows are
-// loaded before they are added (still in row order), so eight loads are in flight.
+// dw = the sum of the `rows` partial rows of `in` (rows x N fp32), one pass.  A
+// workgroup owns a tile of kDwTileQuads * 4 columns; its thread (g, q) adds column
+// quad q of rows g, g + kDwRowGroups, ... in row order (eight loads in flight), and
+// the kDwRowGroups sums of a quad are then added pairwise through LDS.  The order
+// of the additions is fixed, so dw is the same bits on every run.  `in` is
+// 16-byte aligned and N is a multiple of 4 when VEC4.
+constexpr int kDwTileQuads = 8;
+constexpr int kDwRowGroups = 256 / kDwTileQuads;
+
 template <bool VEC4>
-__device__ __forceinline__ void dw_load4(const float *p, int col, int N, float *v) {
+__device__ __forceinline__ float4 dw_load4(const float *p, int col, int N) {
     if constexpr (VEC4) {
-        const float4 u = *reinterpret_cast<const float4 *>(p);
-        v[0] = u.x;
-        v[1] = u.y;
-        v[2] = u.z;
-        v[3] = u.w;
+        return *reinterpret_cast<const float4 *>(p);
     } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (col + e < N) ? p[e] : 0.0f;
+        return make_float4(col < N ? p[0] : 0.0f, col + 1 < N ? p[1] : 0.0f,
+                           col + 2 < N ? p[2] : 0.0f, col + 3 < N ? p[3] : 0.0f);
     }
 }
 
 template <bool VEC4>
-__global__ void __launch_bounds__(256)
-    rmsnorm_dw_reduce(const float *in, int rows, int per, int N, float *out) {
+__global__ void __launch_bounds__(256) rmsnorm_dw_reduce(const float *in, int rows, int N, float *dw) {
     constexpr int U = 8;
-    const int s = blockIdx.y;
-    const int col = (blockIdx.x * 256 + threadIdx.x) * 4;
-    if (col >= N) return;
-    const int r0 = s * per;
-    const int r1 = (r0 + per < rows) ? r0 + per : rows;
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    int r = r0;
-    for (; r + U <= r1; r += U) {
-        float v[U][4];
+    __shared__ float4 sums[kDwRowGroups][kDwTileQuads];
+    const int q = threadIdx.x % kDwTileQuads, g = threadIdx.x / kDwTileQuads;
+    const int col = (blockIdx.x * kDwTileQuads + q) * 4;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (col < N) {
+        int r = g;
+        for (; r + (U - 1) * kDwRowGroups < rows; r += U * kDwRowGroups) {
+            float4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) dw_load4<VEC4>(in + (int64_t)(r + u) * N + col, col, N, v[u]);
+            for (int u = 0; u < U; ++u)
+                v[u] = dw_load4<VEC4>(in + (int64_t)(r + u * kDwRowGroups) * N + col, col, N);
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] += v[u][e];
+            for (int u = 0; u < U; ++u) {
+                acc.x += v[u].x;
+                acc.y += v[u].y;
+                acc.z += v[u].z;
+                acc.w += v[u].w;
+            }
+        }
+        for (; r < rows; r += kDwRowGroups) {
+            const float4 v = dw_load4<VEC4>(in + (int64_t)r * N + col, col, N);
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
     }
-    for (; r < r1; ++r) {
-        float v[4];
-        dw_load4<VEC4>(in + (int64_t)r * N + col, col, N, v);
+    // the row groups' sums, added pairwise (a tree of log2(kDwRowGroups) levels)
+    sums[g][q] = acc;
+    __syncthreads();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += v[e];
+    for (int h = kDwRowGroups / 2; h >= 1; h /= 2) {
+        if (g < h) {
+            const float4 v = sums[g + h][q];
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+            sums[g][q] = acc;
+        }
+        __syncthreads();
     }
-    float *o = out + (int64_t)s * N + col;
+    if (g == 0 && col < N) {
+        const float o[4] = {acc.x, acc.y, acc.z, acc.w};  // dw need not be 16-byte aligned
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        if (col + e < N) o[e] = acc[e];
+        for (int e = 0; e < 4; ++e)
+            if (col + e < N) dw[col + e] = o[e];
+    }
 }
 
 }  // namespace rr

@@ -143,8 +143,7 @@ def test_workspace_covers_the_element_path():
 @pytest.mark.parametrize("vec", (True, False))
 def test_rmsnorm_bwd_plans(dt, vec):
     """Persistent kernels: one workgroup per row up to 16384 elements, then split;
-    the workspace holds the exchange area, one fp32 partial row per row group and
-    the reduction slices."""
+    the workspace holds the exchange area and one fp32 partial row per row group."""
     for N in NS:
         lim = 262144 if vec else 131072
         if N > lim:

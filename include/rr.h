@@ -26,9 +26,15 @@
  *    per-element path that gives the same results more slowly.
  *  - `ws` is a workspace that only rows split over several workgroups need:
  *    when rr_workspace_bytes(...) returns 0 it may be NULL.  Otherwise it
- *    must hold at least that many bytes, be zero-filled once when allocated,
- *    and must not be shared by launches that may run at the same time.  Every
- *    launch that completes normally leaves it zero-filled again.
+ *    must hold at least that many bytes, be 16-byte aligned, be zero-filled
+ *    once when allocated, and must not be shared by launches that may run at
+ *    the same time.  Every launch that completes normally leaves it zero-filled
+ *    again.
+ *  - The workgroups that share a row wait for each other.  They are grouped in
+ *    the order in which they start, so the launch completes whenever as many
+ *    of them as share a row fit on the device at once; each wait is bounded,
+ *    and a wait that gives up (for instance while other work holds the device)
+ *    is reported by rr_workspace_check().
  */
 #ifndef RR_H
 #define RR_H

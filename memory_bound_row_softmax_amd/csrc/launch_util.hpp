@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
 
 #include "configs.hpp"
 #include "launch.hpp"
@@ -21,6 +22,9 @@ hipError_t resident_groups(K kernel, int block, int G, int64_t M, const LaunchAr
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0);
     if (e != hipSuccess) return e;
     int64_t g = (int64_t)per_cu * a.num_cus / G;
+    // test override: a grid larger than fits at once (split rows must still drain)
+    const char *fg = std::getenv("RR_FORCE_GROUPS");
+    if (fg && *fg && std::atoi(fg) > 0) g = std::atoi(fg);
     if (g > kMaxGroups) g = kMaxGroups;
     if (g > M) g = M;
     if (g < 1) return hipErrorCooperativeLaunchTooLarge;

@@ -34,10 +34,10 @@ def from_dev(t: torch.Tensor) -> np.ndarray:
 
 
 @contextmanager
-def forced(P=None, R=None, G=None, spin=None, kind=None):
+def forced(P=None, R=None, G=None, spin=None, kind=None, groups=None):
     """Test-only plan overrides (read by the library at every call)."""
     keys = {"RR_FORCE_P": P, "RR_FORCE_R": R, "RR_FORCE_G": G, "RR_SPIN_LIMIT": spin,
-            "RR_FORCE_KIND": kind}
+            "RR_FORCE_KIND": kind, "RR_FORCE_GROUPS": groups}
     old = {k: os.environ.get(k) for k in keys}
     try:
         for k, v in keys.items():

@@ -320,6 +320,25 @@ def test_rmsnorm_bwd_unaligned(N, dtype):
     check_grad(dw.cpu().numpy(), ref_dw, sdw, "f32", "unaligned dw")
 
 
+@pytest.mark.parametrize("op", ["xent_grad", "softmax_bwd", "rmsnorm_bwd"])
+def test_split_backward_drains_when_the_grid_does_not_fit(op):
+    """Row groups forced far beyond what fits at once (members grouped by start
+    order, see the forward test of the same name)."""
+    M, N = 200, 262144 if op != "rmsnorm_bwd" else 65536
+    say("oversubscribed", op, M, N)
+    with forced(groups=M):
+        if op == "xent_grad":
+            x = synth.normal(M, N, sigma=2.0, dtype="f32")
+            parity_xent_grad(x, synth.labels(M, N), _dloss(M), "f32", "oversubscribed xent grad")
+        elif op == "softmax_bwd":
+            y, dy = softmax_bwd_inputs(M, N, "f32")
+            parity_softmax_bwd(y, dy, "f32", "oversubscribed softmax bwd")
+        else:
+            with forced(16, 512, 8, groups=M):
+                parity_rmsnorm_bwd(*rmsnorm_bwd_inputs(M, N, "f32"), "f32",
+                                   "oversubscribed rmsnorm bwd")
+
+
 def test_rmsnorm_bwd_no_rows_gives_zero_dw():
     say("rmsnorm bwd M = 0")
     dw = torch.full((777,), 5.0, device=DEV)

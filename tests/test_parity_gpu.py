@@ -302,6 +302,42 @@ def test_grid_wait_timeout_is_reported_not_hung(N):
     assert rr.rr_workspace_check(ws) == rr.RR_OK
 
 
+OVERSUBSCRIBED = [  # (op, dtype, M, N): row groups forced to M, far more than fit at once
+    ("softmax", "f32", 256, 200000),    # 8 workgroups per row, deferred exchange: 2048
+    ("softmax", "bf16", 64, 1 << 20),   # 32 per row: 2048
+    ("rmsnorm", "bf16", 256, 262144),   # packed, 4 per row: 1024 (one fits per CU)
+    ("rmsnorm", "f32", 96, 1 << 20),    # 64 per row: 6144
+    ("softmax", "f32", 64, 2_000_000),  # two-pass long rows, 16 per row: 1024
+]
+
+
+@pytest.mark.parametrize("op,dtype,M,N", OVERSUBSCRIBED)
+def test_split_rows_drain_when_the_grid_does_not_fit(op, dtype, M, N):
+    """Workgroups that share a row wait for each other, and an ordinary launch does
+    not promise that the whole grid runs at once.  Members are grouped by the order
+    in which they start, so a grid several times larger than the device holds must
+    still drain, with every row right and the workspace left clean."""
+    code = {"softmax": rr.RR_OP_SOFTMAX, "rmsnorm": rr.RR_OP_RMSNORM}[op]
+    dt = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
+    assert rr.rr_plan_query(code, M, N, dt)["groups_per_row"] > 1
+    x_np = _x(M, N, dtype, sigma=2.0)
+    x = to_dev(x_np, dtype)
+    ws = rr.workspace(code, M, N, dt, DEV)
+    say("oversubscribed", op, dtype, M, N)
+    with forced(groups=M):
+        if op == "softmax":
+            y = rr.rr_softmax_fwd(x, ws=ws)
+            ref = oracle.softmax(x_np)
+        else:
+            w_np = _w(N, dtype)
+            y = rr.rr_rmsnorm_fwd(x, to_dev(w_np, dtype), 1e-6, ws=ws)
+            ref = oracle.rmsnorm(x_np, w_np, 1e-6)
+        torch.cuda.synchronize()
+    assert rr.rr_workspace_check(ws) == rr.RR_OK
+    assert int(ws.count_nonzero()) == 0
+    check_out(from_dev(y), ref, dtype, f"oversubscribed {op} {dtype} {M}x{N}")
+
+
 def test_stream_copy():
     say("stream copy")
     a = torch.randn(1 << 20, device=DEV)

@@ -14,7 +14,8 @@
 // A workgroup's tiles were read a moment before, so the second read is served in large
 // part by the caches between the CUs and HBM (the 256 MB last-level cache holds the
 // few hundred KB each of the resident workgroups reads per row) rather than by HBM.
-// Each pass keeps the next tile's loads in flight while the current one is used.
+// Each pass keeps the next tile's loads in flight while the current one is used, and
+// the wait for the row group's partials overlaps the second pass's first loads.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -42,16 +43,20 @@ constexpr int kLongRmsnorm = 1;
 constexpr int kLongPass1Load = RR_LONG_PASS1_POLICY;
 
 // Walks the tiles t = first, first + step, ... that lie in [0, tiles), with two
-// register buffers: the next tile's loads are issued before the current tile is
-// used.  `step` may be negative (the second pass walks backwards, so that it first
-// reads the tiles the first pass read last, the ones most likely still cached).
-// `t` is the same for the whole workgroup, so the branches are uniform.
-template <int P, class Load, class Use>
-__device__ __forceinline__ void walk_tiles(int first, int step, int tiles, Load load, Use use) {
+// register buffers of B values: the next tile's loads are issued before the current
+// tile is used.  `step` may be negative (the second pass walks backwards, so that it
+// first reads the tiles the first pass read last, the ones most likely still cached).
+// `pre` runs once, after the first tile's loads are issued and before it is used (the
+// second pass waits there for the row group's merged partials, so the wait overlaps
+// the loads).  `t` is the same for the whole workgroup, so the branches are uniform.
+template <int B, class Load, class Use, class Pre>
+__device__ __forceinline__ void walk_tiles(int first, int step, int tiles, Load load, Use use,
+                                           Pre pre) {
     auto in = [&](int t) { return t >= 0 && t < tiles; };
-    float a[P], b[P];
+    float a[B], b[B];
     int t = first;
     if (in(t)) load(a, t);
+    pre();
     while (in(t)) {
         int tn = t + step;
         if (in(tn)) load(b, tn);
@@ -97,57 +102,74 @@ __global__ void __launch_bounds__(R)
         auto load1 = [&](float *v, int t) {
             load_part<E, C, R, VEC, kLongPass1Load>(xv, t * C * R, l, v);
         };
-        auto load2 = [&](float *v, int t) { load_part<E, C, R, VEC>(xv, t * C * R, l, v); };
 
         // pass 1
         MaxSum acc = {-INFINITY, 0.0f};
         float q = 0.0f;
-        walk_tiles<P>(c.member, G, tiles, load1, [&](float *v, int t) {
-            const int chunk0 = t * C * R;
-            if constexpr (OP == kLongSoftmax) {
-                if (!part_full<E, C, R>(chunk0, N)) mask_part<E, C, R>(chunk0, l, N, -INFINITY, v);
-                const float mnew = fmaxf(acc.m, tree_reduce<P>(v, OpMax{}));
-                const float mu = safe_max(mnew);
+        walk_tiles<P>(
+            c.member, G, tiles, load1,
+            [&](float *v, int t) {
+                const int chunk0 = t * C * R;
+                if constexpr (OP == kLongSoftmax) {
+                    if (!part_full<E, C, R>(chunk0, N))
+                        mask_part<E, C, R>(chunk0, l, N, -INFINITY, v);
+                    const float mnew = fmaxf(acc.m, tree_reduce<P>(v, OpMax{}));
+                    const float mu = safe_max(mnew);
 #pragma unroll
-                for (int j = 0; j < P; ++j) v[j] = exp_shift(v[j], mu);
-                acc.s = acc.s * exp_shift(acc.m, mu) + tree_reduce<P>(v, OpSum{});
-                acc.m = mnew;
-            } else {
-                if (!part_full<E, C, R>(chunk0, N)) mask_part<E, C, R>(chunk0, l, N, 0.0f, v);
-                q += tree_sum_squares<P>(v);
-            }
-        });
+                    for (int j = 0; j < P; ++j) v[j] = exp_shift(v[j], mu);
+                    acc.s = acc.s * exp_shift(acc.m, mu) + tree_reduce<P>(v, OpSum{});
+                    acc.m = mnew;
+                } else {
+                    if (!part_full<E, C, R>(chunk0, N)) mask_part<E, C, R>(chunk0, l, N, 0.0f, v);
+                    q += tree_sum_squares<P>(v);
+                }
+            },
+            [] {});
 
-        // merge over the workgroup, then over the row group
-        float m_row = 0.0f, s_row = 0.0f, r = 0.0f;
+        // merge over the workgroup and publish; the row group's merged partials are
+        // waited for once the second pass has its first tile's loads in flight
         if constexpr (OP == kLongSoftmax) {
             acc = row_reduce<R>(acc, red_ms[c.it & 1], l, OpMerge{});
-            exchange_pairs<G>(c.g, c.member, c.it, acc.m, acc.s, c.spin_limit, c.bcast,
-                              MergeMaxSum{});
-            m_row = safe_max(c.bcast[0]);
-            s_row = __builtin_amdgcn_rcpf(c.bcast[1]);
+            publish_pair<G>(c.g, c.member, c.it, acc.m, acc.s);
         } else {
             q = row_reduce<R>(q, red_q[c.it & 1], l, OpSum{});
-            exchange_pairs<G>(c.g, c.member, c.it, q, 0.0f, c.spin_limit, c.bcast, MergeSum{});
-            r = __builtin_amdgcn_rsqf(c.bcast[0] / (float)N + eps);
-            if (rstd && c.member == 0 && l == 0) rstd[row] = r;
+            publish_pair<G>(c.g, c.member, c.it, q, 0.0f);
         }
-
-        // pass 2, backwards
-        walk_tiles<P>(last_tile(c.member, G, tiles), -G, tiles, load2, [&](float *v, int t) {
-            const int chunk0 = t * C * R;
-            const bool full = part_full<E, C, R>(chunk0, N);
+        float m_row = 0.0f, s_row = 0.0f, r = 0.0f;
+        auto wait = [&] {
             if constexpr (OP == kLongSoftmax) {
-#pragma unroll
-                for (int j = 0; j < P; ++j) v[j] = exp_shift(v[j], m_row) * s_row;
+                wait_pairs<G>(c.g, c.it, c.spin_limit, c.bcast, MergeMaxSum{});
+                m_row = safe_max(c.bcast[0]);
+                s_row = __builtin_amdgcn_rcpf(c.bcast[1]);
             } else {
-                float wv[P];
-                load_part<E, C, R, VEC, kReuseLoad>(RowView{wb, 0u}, chunk0, l, wv);
-#pragma unroll
-                for (int j = 0; j < P; ++j) v[j] = v[j] * wv[j] * r;
+                wait_pairs<G>(c.g, c.it, c.spin_limit, c.bcast, MergeSum{});
+                r = __builtin_amdgcn_rsqf(c.bcast[0] / (float)N + eps);
+                if (rstd && c.member == 0 && l == 0) rstd[row] = r;
             }
-            store_part<E, C, R, VEC>(yv, chunk0, l, N, true, full, v);
-        });
+        };
+
+        // pass 2, backwards (RMSNorm: the tile of w is loaded with the tile of x)
+        constexpr int B2 = OP == kLongSoftmax ? P : 2 * P;
+        walk_tiles<B2>(
+            last_tile(c.member, G, tiles), -G, tiles,
+            [&](float *v, int t) {
+                load_part<E, C, R, VEC>(xv, t * C * R, l, v);
+                if constexpr (OP == kLongRmsnorm)
+                    load_part<E, C, R, VEC, kReuseLoad>(RowView{wb, 0u}, t * C * R, l, v + P);
+            },
+            [&](float *v, int t) {
+                const int chunk0 = t * C * R;
+                const bool full = part_full<E, C, R>(chunk0, N);
+                if constexpr (OP == kLongSoftmax) {
+#pragma unroll
+                    for (int j = 0; j < P; ++j) v[j] = exp_shift(v[j], m_row) * s_row;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < P; ++j) v[j] = v[j] * v[P + j] * r;
+                }
+                store_part<E, C, R, VEC>(yv, chunk0, l, N, true, full, v);
+            },
+            wait);
         ++c.it;
     }
     if (c.it > 0) depart_group<G>(c.g);

@@ -56,7 +56,8 @@ typedef enum {
     RR_ERR_UNSUPPORTED = 2,      /* N above the largest row the on-chip plan can hold, or the
                                     workgroups that share a row do not fit on the device at
                                     once */
-    RR_ERR_WORKSPACE = 3,        /* ws is NULL or smaller than rr_workspace_bytes() */
+    RR_ERR_WORKSPACE = 3,        /* ws is NULL, smaller than rr_workspace_bytes(), not
+                                    16-byte aligned, or shares a byte with an operand */
     RR_ERR_HIP = 4,              /* a HIP call failed; see rr_last_hip_error() */
     RR_ERR_GRID_TIMEOUT = 5      /* reported by rr_workspace_check(): a split row waited for
                                     its peer workgroups longer than the spin limit */

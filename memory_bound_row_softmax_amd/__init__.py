@@ -163,6 +163,24 @@ def _matrix(x):
     return x.shape[0], x.shape[1]
 
 
+def _like(t, ref, name):
+    """An output (or second input) the kernels address as ref's shape and dtype."""
+    if (t.shape != ref.shape or t.dtype != ref.dtype or not t.is_contiguous()
+            or t.device != ref.device):
+        raise ValueError(f"{name} must be a contiguous tensor of shape {tuple(ref.shape)}, "
+                         f"dtype {ref.dtype} on {ref.device}")
+    return t
+
+
+def _f32_vector(t, n, device, name):
+    """A contiguous fp32 vector of n elements on `device` (rstd, loss, lse, dloss, dw)."""
+    import torch
+
+    if t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name} must be a contiguous float32 [{n}] tensor on {device}")
+    return t
+
+
 def workspace_bytes(op: int, M: int, N: int, dt: int) -> int:
     return int(lib().rr_workspace_bytes(op, M, N, dt, -1))
 
@@ -178,14 +196,15 @@ def workspace(op: int, M: int, N: int, dt: int, device):
 def _ws_args(ws):
     if ws is None:
         return 0, 0
+    if not ws.is_contiguous() or not ws.is_cuda:
+        raise ValueError("the workspace must be a contiguous CUDA tensor")
     return ws.data_ptr(), ws.numel() * ws.element_size()
 
 
 def rr_softmax_fwd(x, y=None, ws=None, stream=None):
     """Row softmax of x [M, N] into y (new tensor if None; y may be x)."""
     M, N = _matrix(x)
-    if y is None:
-        y = _torch().empty_like(x)
+    y = _torch().empty_like(x) if y is None else _like(y, x, "y")
     dt = dtype_code(x)
     if ws is None:
         ws = workspace(RR_OP_SOFTMAX, M, N, dt, x.device)
@@ -198,10 +217,11 @@ def rr_softmax_fwd(x, y=None, ws=None, stream=None):
 def rr_rmsnorm_fwd(x, w, eps=1e-6, y=None, rstd=None, ws=None, stream=None):
     """RMSNorm of x [M, N] with weight w [N]; returns y (and fills rstd [M] if given)."""
     M, N = _matrix(x)
-    if w.dtype != x.dtype or w.numel() != N or not w.is_contiguous():
+    if w.dtype != x.dtype or w.numel() != N or not w.is_contiguous() or w.device != x.device:
         raise ValueError("weight must be a contiguous [N] tensor of the input's dtype")
-    if y is None:
-        y = _torch().empty_like(x)
+    y = _torch().empty_like(x) if y is None else _like(y, x, "y")
+    if rstd is not None:
+        _f32_vector(rstd, M, x.device, "rstd")
     dt = dtype_code(x)
     if ws is None:
         ws = workspace(RR_OP_RMSNORM, M, N, dt, x.device)
@@ -218,10 +238,12 @@ def rr_cross_entropy_fwd(logits, labels, loss=None, lse=None, ws=None, stream=No
     M, N = _matrix(logits)
     if labels.dtype != torch.int32 or labels.numel() != M or not labels.is_contiguous():
         raise ValueError("labels must be a contiguous int32 [M] tensor")
-    if loss is None:
-        loss = torch.empty(M, dtype=torch.float32, device=logits.device)
-    if lse is None:
-        lse = torch.empty(M, dtype=torch.float32, device=logits.device)
+    if labels.device != logits.device:
+        raise ValueError("labels must be on the logits' device")
+    loss = (torch.empty(M, dtype=torch.float32, device=logits.device) if loss is None
+            else _f32_vector(loss, M, logits.device, "loss"))
+    lse = (torch.empty(M, dtype=torch.float32, device=logits.device) if lse is None
+           else _f32_vector(lse, M, logits.device, "lse"))
     dt = dtype_code(logits)
     wp, wb = _ws_args(ws)
     _check(cross_entropy_fwd_raw(logits.data_ptr(), labels.data_ptr(), loss.data_ptr(),
@@ -239,14 +261,14 @@ def rr_cross_entropy_fwd_bwd(logits, labels, dloss, dlogits=None, loss=None, lse
     M, N = _matrix(logits)
     if labels.dtype != torch.int32 or labels.numel() != M or not labels.is_contiguous():
         raise ValueError("labels must be a contiguous int32 [M] tensor")
-    if dloss.dtype != torch.float32 or dloss.numel() != M or not dloss.is_contiguous():
-        raise ValueError("dloss must be a contiguous float32 [M] tensor")
-    if dlogits is None:
-        dlogits = torch.empty_like(logits)
-    if loss is None:
-        loss = torch.empty(M, dtype=torch.float32, device=logits.device)
-    if lse is None:
-        lse = torch.empty(M, dtype=torch.float32, device=logits.device)
+    if labels.device != logits.device:
+        raise ValueError("labels must be on the logits' device")
+    _f32_vector(dloss, M, logits.device, "dloss")
+    dlogits = torch.empty_like(logits) if dlogits is None else _like(dlogits, logits, "dlogits")
+    loss = (torch.empty(M, dtype=torch.float32, device=logits.device) if loss is None
+            else _f32_vector(loss, M, logits.device, "loss"))
+    lse = (torch.empty(M, dtype=torch.float32, device=logits.device) if lse is None
+           else _f32_vector(lse, M, logits.device, "lse"))
     dt = dtype_code(logits)
     if ws is None:
         ws = workspace(RR_OP_XENT_GRAD, M, N, dt, logits.device)
@@ -262,10 +284,8 @@ def rr_softmax_bwd(y, dy, dx=None, ws=None, stream=None):
     """Softmax backward from the forward output y [M, N] and the gradient dy [M, N]:
     dx = y * (dy - rowsum(y * dy)); dx may be y or dy itself."""
     M, N = _matrix(y)
-    if dy.shape != y.shape or dy.dtype != y.dtype or not dy.is_contiguous():
-        raise ValueError("dy must be a contiguous tensor of y's shape and dtype")
-    if dx is None:
-        dx = _torch().empty_like(y)
+    _like(dy, y, "dy")
+    dx = _torch().empty_like(y) if dx is None else _like(dx, y, "dx")
     dt = dtype_code(y)
     if ws is None:
         ws = workspace(RR_OP_SOFTMAX_BWD, M, N, dt, y.device)
@@ -282,16 +302,13 @@ def rr_rmsnorm_bwd(x, w, dy, rstd, dx=None, dw=None, ws=None, stream=None):
     M, N = x.shape if x.dim() == 2 else (None, None)
     if M is None or not x.is_contiguous() or not x.is_cuda:
         raise ValueError("expected a contiguous 2-D CUDA tensor [M, N]")
-    if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_contiguous():
-        raise ValueError("dy must be a contiguous tensor of x's shape and dtype")
-    if w.dtype != x.dtype or w.numel() != N or not w.is_contiguous():
+    _like(dy, x, "dy")
+    if w.dtype != x.dtype or w.numel() != N or not w.is_contiguous() or w.device != x.device:
         raise ValueError("weight must be a contiguous [N] tensor of the input's dtype")
-    if rstd.dtype != torch.float32 or rstd.numel() != M or not rstd.is_contiguous():
-        raise ValueError("rstd must be a contiguous float32 [M] tensor")
-    if dx is None:
-        dx = torch.empty_like(x)
-    if dw is None:
-        dw = torch.empty(N, dtype=torch.float32, device=x.device)
+    _f32_vector(rstd, M, x.device, "rstd")
+    dx = torch.empty_like(x) if dx is None else _like(dx, x, "dx")
+    dw = (torch.empty(N, dtype=torch.float32, device=x.device) if dw is None
+          else _f32_vector(dw, N, x.device, "dw"))
     dt = dtype_code(x)
     if ws is None:
         ws = workspace(RR_OP_RMSNORM_BWD, M, N, dt, x.device)
@@ -309,6 +326,10 @@ def rr_workspace_check(ws, stream=None) -> int:
 
 
 def rr_stream_copy(src, dst, stream=None):
+    """Copies src into dst (the same-run copy ceiling of the bench)."""
+    if not (src.is_contiguous() and dst.is_contiguous() and src.is_cuda and dst.is_cuda
+            and src.device == dst.device):
+        raise ValueError("src and dst must be contiguous CUDA tensors on one device")
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() < nbytes:
         raise ValueError("destination too small")

@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 
 #include "launch.hpp"
@@ -89,9 +90,20 @@ rr_status plan_status(rr::PlanResult r) {
     }
 }
 
-rr_status check_workspace(const rr::Plan &p, void *ws, size_t ws_bytes) {
+// A buffer of the call, for the workspace overlap check (p may be NULL).
+struct Region {
+    const void *p;
+    size_t n;
+};
+
+// The part of the workspace the plan uses must exist, be aligned and share no byte
+// with any operand of the call.
+rr_status check_workspace(const rr::Plan &p, void *ws, size_t ws_bytes,
+                          std::initializer_list<Region> operands) {
     if (p.ws_bytes == 0) return RR_OK;
     if (!ws || ws_bytes < p.ws_bytes || !aligned16(ws)) return RR_ERR_WORKSPACE;
+    for (const Region &r : operands)
+        if (r.p && overlap(ws, p.ws_bytes, r.p, r.n)) return RR_ERR_WORKSPACE;
     return RR_OK;
 }
 
@@ -119,7 +131,7 @@ rr_status rr_softmax_fwd(const void *x, void *y, int64_t M, int64_t N, rr_dtype 
     rr::Plan p;
     st = plan_status(rr::make_plan(rr::kOpSoftmax, dt, M, N, vec, &p));
     if (st != RR_OK) return st;
-    if ((st = check_workspace(p, ws, ws_bytes)) != RR_OK) return st;
+    if ((st = check_workspace(p, ws, ws_bytes, {{x, bytes}, {y, bytes}})) != RR_OK) return st;
     rr::LaunchArgs a;
     if ((st = launch_args(stream, &a)) != RR_OK) return st;
     if (p.path == rr::kPathLong)
@@ -142,7 +154,11 @@ rr_status rr_rmsnorm_fwd(const void *x, const void *w, void *y, float *rstd, int
     rr::Plan p;
     st = plan_status(rr::make_plan(rr::kOpRmsnorm, dt, M, N, vec, &p));
     if (st != RR_OK) return st;
-    if ((st = check_workspace(p, ws, ws_bytes)) != RR_OK) return st;
+    const size_t row_vec = (size_t)M * 4u;
+    if ((st = check_workspace(p, ws, ws_bytes,
+                              {{x, bytes}, {y, bytes}, {w, (size_t)N * elem_size(dt)},
+                               {rstd, row_vec}})) != RR_OK)
+        return st;
     rr::LaunchArgs a;
     if ((st = launch_args(stream, &a)) != RR_OK) return st;
     if (p.path == rr::kPathLong)
@@ -182,7 +198,11 @@ rr_status rr_cross_entropy_fwd_bwd(const void *logits, const int32_t *labels, co
     rr::Plan p;
     st = plan_status(rr::make_plan(rr::kOpXentGrad, dt, M, N, vec, &p));
     if (st != RR_OK) return st;
-    if ((st = check_workspace(p, ws, ws_bytes)) != RR_OK) return st;
+    const size_t row_vec = (size_t)M * 4u;
+    if ((st = check_workspace(p, ws, ws_bytes,
+                              {{logits, bytes}, {dlogits, bytes}, {labels, row_vec},
+                               {dloss, row_vec}, {loss, row_vec}, {lse, row_vec}})) != RR_OK)
+        return st;
     rr::LaunchArgs a;
     if ((st = launch_args(stream, &a)) != RR_OK) return st;
     return hip_status(rr::launch_xent_grad(p, dt, logits, labels, dloss, loss, lse, dlogits, M, N,
@@ -201,7 +221,8 @@ rr_status rr_softmax_bwd(const void *y, const void *dy, void *dx, int64_t M, int
     rr::Plan p;
     st = plan_status(rr::make_plan(rr::kOpSoftmaxBwd, dt, M, N, vec, &p));
     if (st != RR_OK) return st;
-    if ((st = check_workspace(p, ws, ws_bytes)) != RR_OK) return st;
+    if ((st = check_workspace(p, ws, ws_bytes, {{y, bytes}, {dy, bytes}, {dx, bytes}})) != RR_OK)
+        return st;
     rr::LaunchArgs a;
     if ((st = launch_args(stream, &a)) != RR_OK) return st;
     return hip_status(rr::launch_softmax_bwd(p, dt, y, dy, dx, M, N, ws, a));
@@ -226,7 +247,11 @@ rr_status rr_rmsnorm_bwd(const void *x, const void *w, const void *dy, const flo
     rr::Plan p;
     st = plan_status(rr::make_plan(rr::kOpRmsnormBwd, dt, M, N, vec, &p));
     if (st != RR_OK) return st;
-    if (M > 0 && (st = check_workspace(p, ws, ws_bytes)) != RR_OK) return st;
+    if (M > 0 && (st = check_workspace(p, ws, ws_bytes,
+                                       {{x, bytes}, {dy, bytes}, {dx, bytes},
+                                        {w, (size_t)N * elem_size(dt)}, {rstd, (size_t)M * 4u},
+                                        {dw, dw_bytes}})) != RR_OK)
+        return st;
     rr::LaunchArgs a;
     if ((st = launch_args(stream, &a)) != RR_OK) return st;
     return hip_status(rr::launch_rmsnorm_bwd(p, dt, x, w, dy, rstd, dx, dw, M, N, ws, a));
@@ -294,7 +319,9 @@ const char *rr_status_string(rr_status status) {
     case RR_OK: return "RR_OK";
     case RR_ERR_INVALID_ARGUMENT: return "RR_ERR_INVALID_ARGUMENT: invalid argument";
     case RR_ERR_UNSUPPORTED: return "RR_ERR_UNSUPPORTED: shape or grid not supported";
-    case RR_ERR_WORKSPACE: return "RR_ERR_WORKSPACE: workspace missing, too small or misaligned";
+    case RR_ERR_WORKSPACE:
+        return "RR_ERR_WORKSPACE: workspace missing, too small, misaligned or overlapping an "
+               "operand";
     case RR_ERR_HIP: return "RR_ERR_HIP: a HIP call failed (see rr_last_hip_error)";
     case RR_ERR_GRID_TIMEOUT: return "RR_ERR_GRID_TIMEOUT: a split row timed out waiting for peers";
     }

@@ -126,6 +126,13 @@ def test_missing_or_small_workspace():
     assert rr.softmax_fwd_raw(A, B, 64, N, rr.RR_F32) == rr.RR_ERR_WORKSPACE
     assert rr.softmax_fwd_raw(A, B, 64, N, rr.RR_F32, C, need - 1) == rr.RR_ERR_WORKSPACE
     assert rr.softmax_fwd_raw(A, B, 64, N, rr.RR_F32, C + 4, need) == rr.RR_ERR_WORKSPACE
+    # a workspace that shares bytes with an operand
+    assert rr.softmax_fwd_raw(A, B, 64, N, rr.RR_F32, B + 64 * N * 4 - 16, need) == \
+        rr.RR_ERR_WORKSPACE
+    assert rr.softmax_fwd_raw(A, B, 64, N, rr.RR_F32, A - need + 16, need) == rr.RR_ERR_WORKSPACE
+    need_b = rr.rr_plan_query(rr.RR_OP_SOFTMAX_BWD, 64, N, rr.RR_F32, True)["ws_bytes"]
+    assert need_b > 0
+    assert rr.softmax_bwd_raw(A, C, B, 64, N, rr.RR_F32, C + 1024, need_b) == rr.RR_ERR_WORKSPACE
 
 
 def test_plan_struct_layout_matches_header():

@@ -28,8 +28,10 @@
  *    when rr_workspace_bytes(...) returns 0 it may be NULL.  Otherwise it
  *    must hold at least that many bytes, be 16-byte aligned, be zero-filled
  *    once when allocated, and must not be shared by launches that may run at
- *    the same time.  Every launch that completes normally leaves it zero-filled
- *    again.
+ *    the same time.  Its first word is the error word rr_workspace_check()
+ *    reads.  Every launch that completes normally leaves it zero-filled again,
+ *    except for the dw partial rows of rr_rmsnorm_bwd (scratch that each call
+ *    rewrites).
  *  - The workgroups that share a row wait for each other.  They are grouped in
  *    the order in which they start, so the launch completes whenever as many
  *    of them as share a row fit on the device at once; each wait is bounded,
@@ -152,9 +154,9 @@ rr_status rr_softmax_bwd(const void *y, const void *dy, void *dx, int64_t M, int
  * through fp32 partial rows in the workspace (one per workgroup), added in a fixed
  * order, so repeated calls give the same bits.  dx may be x or dy itself (exact
  * aliasing); any other overlap among x, dy, dx and dw is rejected.  The workspace
- * (RR_OP_RMSNORM_BWD) is always needed when M > 0; only its first part (split rows)
- * must start zero-filled, as for the other calls.  N up to 262144 (131072 when the
- * rows are not 16-byte aligned).
+ * (RR_OP_RMSNORM_BWD) is always needed when M > 0; only its first part (the header
+ * and, for split rows, the exchange area) must start zero-filled, as for the other
+ * calls.  N up to 262144 (131072 when the rows are not 16-byte aligned).
  */
 rr_status rr_rmsnorm_bwd(const void *x, const void *w, const void *dy, const float *rstd,
                          void *dx, float *dw, int64_t M, int64_t N, rr_dtype dt, void *ws,

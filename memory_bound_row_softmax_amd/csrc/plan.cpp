@@ -265,7 +265,9 @@ static PlanResult plan_rmsnorm_bwd(int dtype, int64_t M, int64_t N, bool vec, Pl
     if (parts > blocks) parts = blocks;
     if (parts < 1) parts = 1;
     p.max_parts = (int)parts;
-    const size_t exch = G > 1 ? align256(grid_ws_bytes(G, parts)) : 0;
+    // the exchange area of split rows; with G == 1 the header alone, so that the
+    // first word of every workspace is the error word rr_workspace_check reads
+    const size_t exch = G > 1 ? align256(grid_ws_bytes(G, parts)) : (size_t)kWsHeader;
     p.part_off = exch;
     p.ws_bytes = p.part_off + align256((size_t)parts * (size_t)N * 4u);
     *out = p;

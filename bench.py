@@ -210,22 +210,37 @@ class Runner:
             dst = self.y[i]
         return self.rr.stream_copy_raw(src.data_ptr(), dst.data_ptr(), nbytes, self.sp)
 
-    def time(self, fn, steps: int, warmup: int):
+    def time(self, fn, steps: int, warmup: int, graph: bool = False):
         """Wall time of `steps` back-to-back launches, and the mean time per launch
-        from a pair of HIP events on the launch stream around the same region."""
+        from a pair of HIP events on the launch stream around the same region.
+        With `graph`, the `steps` launches are captured once in a HIP graph and the
+        timed region is one replay of it (no host launch cost between kernels)."""
         torch = self.torch
         with torch.cuda.stream(self.stream):
             for k in range(warmup):
                 st = fn(k)
                 if st != 0:
                     raise RuntimeError(f"launch failed: {self.rr.status_string(st)}")
+            g = None
+            if graph:
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=self.stream):
+                    for k in range(steps):
+                        st = fn(warmup + k)
+                        if st != 0:
+                            raise RuntimeError(f"capture failed: {self.rr.status_string(st)}")
+                g.replay()  # the first replay uploads the graph
             start = torch.cuda.Event(enable_timing=True)
             end = torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             start.record(self.stream)
-            for k in range(steps):
-                fn(warmup + k)
+            if graph:
+                g.replay()
+            else:
+                for k in range(steps):
+                    fn(warmup + k)
             end.record(self.stream)
             torch.cuda.synchronize()
             t1 = time.perf_counter()
@@ -285,11 +300,11 @@ def cpu_baseline(w, seconds: float):
 
 
 def measure(w, steps: int, warmup: int, min_rotation_bytes: float, with_cpu: bool,
-            cpu_seconds: float, host_rows=None):
+            cpu_seconds: float, host_rows=None, graph=False):
     r = Runner(w, min_rotation_bytes, host_rows=host_rows)
     nbytes = algorithmic_bytes(w)
-    wall, mean_ms = r.time(r.launch, steps, warmup)
-    copy_wall, copy_mean_ms = r.time(r.copy_launch, steps, warmup)
+    wall, mean_ms = r.time(r.launch, steps, warmup, graph)
+    copy_wall, copy_mean_ms = r.time(r.copy_launch, steps, warmup, graph)
     copy_bytes = 2 * r.x[0].numel() * r.x[0].element_size()
     achieved = nbytes / (mean_ms * 1e-3) / 1e9
     traffic, rec = traffic_for(w.name)
@@ -310,7 +325,7 @@ def measure(w, steps: int, warmup: int, min_rotation_bytes: float, with_cpu: boo
         "config": {"workload": w.name, "op": w.op, "io_dtype": w.dtype, "M": w.M, "N": w.N,
                    "plan": {k: r.plan[k] for k in ("path", "vals_per_lane", "lanes_per_row",
                                                     "groups_per_row", "block_threads")},
-                   "rotating_sets": r.sets},
+                   "rotating_sets": r.sets, "launch": "graph" if graph else "stream"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "launch_ms_mean": round(mean_ms, 5),
@@ -346,6 +361,9 @@ def main() -> int:
                     help="sweep only: rows generated on the host, repeated down the matrix")
     ap.add_argument("--only", default="",
                     help="sweep only: comma-separated substrings a workload name must contain")
+    ap.add_argument("--graph", action="store_true",
+                    help="time one replay of a HIP graph of the steps (kernel and copy) "
+                         "instead of launches from the host")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -369,7 +387,7 @@ def main() -> int:
             if w.name in done or (only and not all(t in w.name for t in only)):
                 continue
             line = measure(w, args.steps, args.warmup, args.rotate_bytes, False, 0,
-                           host_rows=args.sweep_host_rows)
+                           host_rows=args.sweep_host_rows, graph=args.graph)
             line["config"]["host_rows"] = args.sweep_host_rows
             with open(args.out, "a") as f:
                 f.write(json.dumps(line) + "\n")
@@ -379,7 +397,7 @@ def main() -> int:
         return 0
 
     line = measure(W.by_name(args.workload), args.steps, args.warmup, args.rotate_bytes,
-                   not args.no_cpu_baseline, args.cpu_seconds)
+                   not args.no_cpu_baseline, args.cpu_seconds, graph=args.graph)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -247,9 +247,13 @@ class Runner:
         return t1 - t0, start.elapsed_time(end) / steps
 
 
-def cpu_baseline(w, seconds: float):
+def cpu_baseline(w, seconds: float, max_threads: int = 16):
     """The oracle, single-threaded, on the first rows of the same workload (for a
-    backward pass, only the backward call is timed)."""
+    backward pass, only the backward call is timed); then the same oracle function
+    row-partitioned over the host's cores (one block of rows per thread; the C
+    oracle runs outside the interpreter lock).  Input generation is not timed."""
+    import concurrent.futures as cf
+
     import numpy as np
 
     import oracle
@@ -258,29 +262,31 @@ def cpu_baseline(w, seconds: float):
 
     per_row = algorithmic_bytes(w) / w.M
 
-    def run(rows):
-        x = W.x_rows(w, nrows=rows)
-        t0 = time.perf_counter()
+    def prepare(rows, row0=0):
+        """Inputs of the timed oracle call for rows row0 .. row0 + rows - 1."""
+        x = W.x_rows(w, nrows=rows, row0=row0)
         if w.op == "softmax":
-            oracle.softmax(x)
-        elif w.op == "rmsnorm":
-            oracle.rmsnorm(x, W.weight(w), w.eps)
-        elif w.op == "xent_grad":
-            oracle.cross_entropy_grad(x, W.label_rows(w, nrows=rows), W.dloss_rows(w, nrows=rows))
-        elif w.op == "softmax_bwd":
+            return (oracle.softmax, x)
+        if w.op == "rmsnorm":
+            return (oracle.rmsnorm, x, W.weight(w), w.eps)
+        if w.op == "xent_grad":
+            return (oracle.cross_entropy_grad, x, W.label_rows(w, nrows=rows, row0=row0),
+                    W.dloss_rows(w, nrows=rows, row0=row0))
+        if w.op == "softmax_bwd":
             y = oracle.softmax(x).astype(np.float32)
             y = y if w.dtype == "f32" else synth.f32_to_bf16(y)
-            dy = W.dy_rows(w, nrows=rows)
-            t0 = time.perf_counter()
-            oracle.softmax_backward(y, dy)
-        elif w.op == "rmsnorm_bwd":
+            return (oracle.softmax_backward, y, W.dy_rows(w, nrows=rows, row0=row0))
+        if w.op == "rmsnorm_bwd":
             wt = W.weight(w)
             _, r = oracle.rmsnorm(x, wt, w.eps, want_rstd=True)
-            dy = W.dy_rows(w, nrows=rows)
-            t0 = time.perf_counter()
-            oracle.rmsnorm_backward(x, wt, dy, r.astype(np.float32))
-        else:
-            oracle.cross_entropy(x, W.label_rows(w, nrows=rows))
+            return (oracle.rmsnorm_backward, x, wt, W.dy_rows(w, nrows=rows, row0=row0),
+                    r.astype(np.float32))
+        return (oracle.cross_entropy, x, W.label_rows(w, nrows=rows, row0=row0))
+
+    def run(rows):
+        call = prepare(rows)
+        t0 = time.perf_counter()
+        call[0](*call[1:])
         return time.perf_counter() - t0
 
     probe = max(1, min(w.M, (1 << 20) // w.N))
@@ -293,10 +299,32 @@ def cpu_baseline(w, seconds: float):
     total = 0.0
     for _ in range(passes):
         total += run(rows)
-    return {"value": round(per_row * rows * passes / total / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"first {rows} of {w.M} rows x {passes} pass(es), single-threaded "
-                      f"double-precision oracle, {total:.1f} s of CPU time"}
+    single = {"value": round(per_row * rows * passes / total / 1e9, 4), "unit": "GB/s",
+              "cores": 1, "kind": "oracle",
+              "sample": f"first {rows} of {w.M} rows x {passes} pass(es), single-threaded "
+                        f"double-precision oracle, {total:.1f} s of CPU time"}
+
+    # all cores: one contiguous block of rows per thread (at most 2^27 elements in
+    # all), rounds repeated to about half of `seconds`
+    threads = max(1, min(max_threads, os.cpu_count() or 1))
+    block = max(1, min(rows, w.M // threads, (1 << 27) // (w.N * threads)))
+    nblocks = min(threads, max(1, w.M // block))
+    calls = [prepare(block, row0=k * block) for k in range(nblocks)]
+    with cf.ThreadPoolExecutor(max_workers=nblocks) as ex:
+        def one_round():
+            t0 = time.perf_counter()
+            list(ex.map(lambda c: c[0](*c[1:]), calls))
+            return time.perf_counter() - t0
+
+        t_round = one_round()
+        rounds = max(1, int(0.5 * seconds / max(t_round, 1e-6)))
+        t_mt = sum(one_round() for _ in range(rounds))
+    single["all_cores"] = {
+        "value": round(per_row * block * nblocks * rounds / t_mt / 1e9, 4), "unit": "GB/s",
+        "cores": nblocks, "kind": "oracle",
+        "sample": f"{nblocks} blocks of {block} rows, one per thread, x {rounds} round(s), the "
+                  f"same oracle function, {t_mt:.1f} s wall"}
+    return single
 
 
 def measure(w, steps: int, warmup: int, min_rotation_bytes: float, with_cpu: bool,

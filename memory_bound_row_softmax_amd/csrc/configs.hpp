@@ -38,13 +38,13 @@
     X(32, 1024, 1) X(32, 1024, 2) X(32, 1024, 4) X(32, 1024, 8) X(32, 1024, 16)             \
     X(64, 256, 1) X(64, 256, 2) X(64, 256, 4) X(64, 256, 8) X(64, 256, 16)                  \
     X(64, 512, 1) X(64, 512, 2) X(64, 512, 4) X(64, 512, 8) X(64, 512, 16)                  \
-    X(64, 512, 32)
+    X(64, 512, 32) X(64, 512, 64)
 
 // Packed bf16 RMSNorm stream kernels (128-bit path only, see packed_bf16.hpp),
 // named by (R, G): each lane keeps kPackedP = 128 bf16 values as 64 VGPRs of raw
 // chunks.  A plan names them with P = kPackedP.
 constexpr int kPackedP = 128;
-#define RR_PACKED_CONFIGS(X) X(512, 1) X(512, 2) X(512, 4) X(512, 8) X(512, 16)
+#define RR_PACKED_CONFIGS(X) X(512, 1) X(512, 2) X(512, 4) X(512, 8) X(512, 16) X(512, 32)
 
 // RMSNorm backward (persistent, see rmsnorm_bwd.hpp), named by (P, R, G): a lane
 // keeps x, dy (two rows in flight), its w slice and its dw partials, about 6P + 45
@@ -116,15 +116,23 @@ constexpr int stream_depth(int op, int P, int R) {
 }
 
 // Two-pass long rows (softmax and RMSNorm forward past the split-row capacity):
-// tiles of kLongP * kLongR elements (kLongPElem on the per-element path), kLongG
-// workgroups per row, rows up to kLongMaxN elements (byte offsets stay 32-bit).
+// tiles of kLongP * kLongR elements (kLongPElem on the per-element path), G
+// workgroups per row (RMSNorm: kLongG; softmax: long_row_groups below), rows up to
+// kLongMaxN elements (byte offsets stay 32-bit).
 constexpr int kLongP = 32;
 constexpr int kLongPElem = 16;
 constexpr int kLongR = 512;
-#ifndef RR_LONG_G
-#define RR_LONG_G 16
-#endif
-constexpr int kLongG = RR_LONG_G;
+constexpr int kLongG = 16;
+// Softmax: as many workgroups per row (16, 32 or 64) as keep a workgroup's share
+// of the row at about 512 KiB or less.  On MI355X the two-read softmax ran fastest
+// that way (fp32 rows of 3M and 4M elements on 32, of 8M on 64, bf16 rows of 2M
+// and 4M on 16); RMSNorm measured within 3 % for 16, 32 and 64 and keeps 16.
+constexpr int long_row_groups(int op_softmax, long long row_bytes) {
+    if (!op_softmax) return kLongG;
+    int g = kLongG;
+    while (g < 64 && row_bytes > (long long)g * (512 << 10)) g *= 2;
+    return g;
+}
 constexpr long long kLongMaxN = 1ll << 28;
 
 // RMSNorm backward: the per-element path keeps P <= 16.

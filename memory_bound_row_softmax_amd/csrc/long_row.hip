@@ -6,10 +6,10 @@
 namespace rr {
 namespace {
 
-template <class E, int OP, int P, bool VEC>
+template <class E, int OP, int P, int G, bool VEC>
 hipError_t launch_cfg(const void *x, const void *w, void *y, float *rstd, int64_t M, int64_t N,
                       float eps, void *ws, const LaunchArgs &a) {
-    constexpr int R = kLongR, G = kLongG;
+    constexpr int R = kLongR;
     auto kernel = long_row_kernel<E, OP, P, R, G, VEC>;
     int groups;
     hipError_t e = resident_groups(kernel, R, G, M, a, &groups);
@@ -24,8 +24,18 @@ hipError_t launch_cfg(const void *x, const void *w, void *y, float *rstd, int64_
 template <class E, int OP>
 hipError_t dispatch(const Plan &p, const void *x, const void *w, void *y, float *rstd, int64_t M,
                     int64_t N, float eps, void *ws, const LaunchArgs &a) {
-    if (p.vec) return launch_cfg<E, OP, kLongP, true>(x, w, y, rstd, M, N, eps, ws, a);
-    return launch_cfg<E, OP, kLongPElem, false>(x, w, y, rstd, M, N, eps, ws, a);
+    // RMSNorm takes 16 workgroups per row; softmax 16, 32 or 64 (long_row_groups)
+    if constexpr (OP == kLongSoftmax) {
+        if (p.G == 32)
+            return p.vec ? launch_cfg<E, OP, kLongP, 32, true>(x, w, y, rstd, M, N, eps, ws, a)
+                         : launch_cfg<E, OP, kLongPElem, 32, false>(x, w, y, rstd, M, N, eps, ws, a);
+        if (p.G == 64)
+            return p.vec ? launch_cfg<E, OP, kLongP, 64, true>(x, w, y, rstd, M, N, eps, ws, a)
+                         : launch_cfg<E, OP, kLongPElem, 64, false>(x, w, y, rstd, M, N, eps, ws, a);
+    }
+    if (p.G != kLongG) return hipErrorInvalidValue;
+    if (p.vec) return launch_cfg<E, OP, kLongP, kLongG, true>(x, w, y, rstd, M, N, eps, ws, a);
+    return launch_cfg<E, OP, kLongPElem, kLongG, false>(x, w, y, rstd, M, N, eps, ws, a);
 }
 
 }  // namespace

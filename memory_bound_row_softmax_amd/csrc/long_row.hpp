@@ -1,6 +1,6 @@
-// long_row.hpp -- softmax and RMSNorm forward for rows longer than the registers of
-// the split-row stream kernels can hold (more than P * R * G = 1048576 elements, or
-// 262144 on the per-element path).
+// long_row.hpp -- softmax and RMSNorm forward for rows longer than the split-row
+// stream kernels hold in registers or run faster (more than 2097152 elements; bf16
+// softmax more than 1048576; the per-element path more than 262144).
 //
 // The QuACK article (无需CUDA代码，给H100加速33%-50%), section 内存吞吐量, names the
 // alternative to reducing a long row across a cluster: an online algorithm that reads

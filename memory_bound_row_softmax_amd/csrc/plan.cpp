@@ -112,39 +112,41 @@ struct Choice {
     bool stream;
     int P, R, G;
 };
-constexpr int kTunedBuckets = 10;
-constexpr int64_t kTunedN[kTunedBuckets] = {256,   1024,   4096,   16384,  32768,
-                                            65536, 131072, 262144, 524288, 1048576};
+constexpr int kTunedBuckets = 11;
+constexpr int64_t kTunedN[kTunedBuckets] = {256,    1024,   4096,   16384,   32768,  65536,
+                                            131072, 262144, 524288, 1048576, 2097152};
+// A choice with P = 0: no on-chip plan (softmax and RMSNorm then read the row twice).
+constexpr Choice kTwoReads = {false, 0, 0, 0};
 //   [op: softmax, rmsnorm, softmax backward, cross-entropy gradient][dtype: f32, bf16][N bucket]
-// (the two longest buckets were timed at 4096 and 2048 rows)
+// (the three longest buckets were timed at 4096, 2048 and 512-1024 rows)
 static const Choice kTuned[4][2][kTunedBuckets] = {
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {true, 64, 512, 1},
       {true, 16, 1024, 2}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8},
-      {true, 64, 512, 16}, {true, 64, 512, 32}},
+      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 16, 256, 1}, {false, 64, 256, 1},
       {true, 32, 1024, 1}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8},
-      {true, 64, 512, 16}, {true, 64, 512, 32}}},
+      {true, 64, 512, 16}, {true, 64, 512, 32}, kTwoReads}},
     {{{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 16, 1024, 1},
       {true, 16, 1024, 2}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 32, 512, 16},
-      {true, 32, 512, 32}, {true, 32, 512, 64}},
+      {true, 32, 512, 32}, {true, 32, 512, 64}, {true, 64, 512, 64}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {true, 32, 1024, 1},
       {false, 64, 512, 1}, {true, 32, 1024, 2}, {true, 64, 512, 4}, {true, kPackedP, 512, 4},
-      {true, kPackedP, 512, 8}, {true, kPackedP, 512, 16}}},
+      {true, kPackedP, 512, 8}, {true, kPackedP, 512, 16}, {true, kPackedP, 512, 32}}},
     // softmax backward (y and dy both held: at most 32 values per lane in a stream kernel)
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 16, 256, 1}, {false, 32, 1024, 1},
       {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
-      {true, 32, 512, 32}, {true, 32, 512, 64}},
+      {true, 32, 512, 32}, {true, 32, 512, 64}, kTwoReads},
      {{false, 8, 32, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 16, 1024, 1},
       {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
-      {true, 32, 512, 32}, {true, 32, 512, 64}}},
+      {true, 32, 512, 32}, {true, 32, 512, 64}, kTwoReads}},
     // cross-entropy forward fused with its gradient (the softmax kernels; block kernels
     // hold longer rows here than for the softmax)
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {true, 16, 1024, 1},
       {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 64, 512, 8},
-      {true, 64, 512, 16}, {true, 64, 512, 32}},
+      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}},
      {{false, 16, 16, 1}, {false, 64, 16, 1}, {false, 16, 256, 1}, {false, 32, 512, 1},
       {false, 64, 512, 1}, {false, 64, 1024, 1}, {true, 64, 512, 4}, {true, 32, 1024, 8},
-      {true, 64, 512, 16}, {true, 64, 512, 32}}},
+      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}}},
 };
 
 static bool try_choice(int op, int dtype, bool vec, int64_t N, Choice c, Plan *p) {
@@ -171,6 +173,7 @@ static bool default_row(int op, int dtype, bool vec, int64_t N, Plan *p) {
     while (k < kTunedBuckets - 1 && kTunedN[k] < N) ++k;
     if (N <= kTunedN[kTunedBuckets - 1]) {
         Choice c = kTuned[o][d][k];
+        if (c.P == 0) return false;  // no on-chip plan measured faster than two reads
         // A stream workgroup that would be less than half full: the block
         // choice of the bucket below, widened to the row.
         if (c.stream && k > 0 && 2 * N < (int64_t)c.P * c.R) c = kTuned[o][d][k - 1];
@@ -323,9 +326,9 @@ PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *ou
         p.path = kPathLong;
         p.P = vec ? kLongP : kLongPElem;
         p.R = kLongR;
-        p.G = kLongG;
+        p.G = long_row_groups(op == kOpSoftmax, N * (dtype == kBf16 ? 2 : 4));
         p.max_n = kLongMaxN;
-        p.ws_bytes = grid_ws_bytes(kLongG, M);
+        p.ws_bytes = grid_ws_bytes(p.G, M);
         p.block = kLongR;
         p.rows_per_block = 1;
         *out = p;

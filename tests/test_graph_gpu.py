@@ -28,7 +28,7 @@ def _inputs(seed, M, N, dtype):
     ("xent_grad", "f32", 50, 200000),   # fused gradient, deferred exchange
     ("softmax_bwd", "f32", 64, 131072),
     ("rmsnorm_bwd", "bf16", 512, 4096),  # persistent kernel + dw pass
-    ("softmax", "f32", 4, 2_000_000),   # two-pass long rows
+    ("softmax", "f32", 4, 3_000_000),   # two-pass long rows
 ])
 def test_captured_calls_replay_like_eager_ones(op, dtype, M, N):
     code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16

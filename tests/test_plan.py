@@ -47,12 +47,12 @@ def test_row_plans_hold_the_row(op, dt, vec):
             assert G == 1 or (G // 2) * P * R < N
             assert p["ws_bytes"] == (256 + 1024 * (64 + 64 * G) if G > 1 else 0)
     if op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):  # long rows: read twice, up to 2^28
-        assert rr.rr_plan_query(op, 16, (1 << 20) + 1, dt, vec)["path"] == 4
+        assert rr.rr_plan_query(op, 16, (1 << 21) + 1, dt, vec)["path"] == 4
         with pytest.raises(rr.RRError):
             rr.rr_plan_query(op, 16, (1 << 28) + 1, dt, vec)
     else:
         with pytest.raises(rr.RRError):
-            rr.rr_plan_query(op, 16, (1 << 20) + 1, dt, vec)
+            rr.rr_plan_query(op, 16, (1 << 21) + 1, dt, vec)
 
 
 @pytest.mark.parametrize("dt", (rr.RR_F32, rr.RR_BF16))
@@ -167,14 +167,26 @@ def test_rmsnorm_bwd_plans(dt, vec):
 def test_long_rows_take_the_two_pass_kernel(monkeypatch):
     for op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
         for dt in (rr.RR_F32, rr.RR_BF16):
-            on_chip = rr.rr_plan_query(op, 1000, 1 << 20, dt)
-            G = on_chip["groups_per_row"]
-            assert on_chip["path"] == 1 and G in (16, 32, 64)
-            assert on_chip["vals_per_lane"] * on_chip["lanes_per_row"] * G == 1 << 20
-            assert on_chip["ws_bytes"] == 256 + 1000 * (64 + 64 * G)
-            p = rr.rr_plan_query(op, 1000, (1 << 20) + 8, dt)
-            assert p["path"] == 4 and p["lanes_per_row"] == 512 and p["groups_per_row"] == 16
-            assert p["ws_bytes"] == 256 + 1000 * (64 + 64 * 16)
+            for n in (1 << 20, 1 << 21):
+                on_chip = rr.rr_plan_query(op, 1000, n, dt)
+                if op == rr.RR_OP_SOFTMAX and dt == rr.RR_BF16 and n > 1 << 20:
+                    # measured faster with two reads than on 64 workgroups
+                    assert on_chip["path"] == 4
+                    continue
+                G = on_chip["groups_per_row"]
+                assert on_chip["path"] == 1 and G in (16, 32, 64)
+                assert on_chip["vals_per_lane"] * on_chip["lanes_per_row"] * G == n
+                assert on_chip["ws_bytes"] == 256 + 1000 * (64 + 64 * G)
+            for n in ((1 << 21) + 8, 3_000_000, 1 << 23, 1 << 26):
+                p = rr.rr_plan_query(op, 1000, n, dt)
+                # RMSNorm: 16 workgroups per row; softmax: enough that a workgroup's
+                # share of the row is at most 512 KiB (16 to 64)
+                G = 16
+                if op == rr.RR_OP_SOFTMAX:
+                    while G < 64 and n * (4 if dt == rr.RR_F32 else 2) > G * 512 * 1024:
+                        G *= 2
+                assert p["path"] == 4 and p["lanes_per_row"] == 512 and p["groups_per_row"] == G
+                assert p["ws_bytes"] == 256 + 1000 * (64 + 64 * G)
             # the per-element path holds 16 * 1024 * 16 elements on chip
             assert rr.rr_plan_query(op, 10, 262144, dt, False)["path"] == 1
             q = rr.rr_plan_query(op, 10, 262145, dt, False)
@@ -184,3 +196,4 @@ def test_long_rows_take_the_two_pass_kernel(monkeypatch):
     # the other ops have no long-row kernel
     with pytest.raises(rr.RRError):
         rr.rr_plan_query(rr.RR_OP_SOFTMAX_BWD, 8, (1 << 20) + 4, rr.RR_F32)
+    # the per-element path keeps the two-pass kernel past 262144 elements

@@ -197,3 +197,18 @@ def test_long_rows_take_the_two_pass_kernel(monkeypatch):
     with pytest.raises(rr.RRError):
         rr.rr_plan_query(rr.RR_OP_SOFTMAX_BWD, 8, (1 << 20) + 4, rr.RR_F32)
     # the per-element path keeps the two-pass kernel past 262144 elements
+
+
+def test_few_rows_keep_a_row_on_one_workgroup():
+    """With few rows, a row one workgroup holds is not split (its exchange would not
+    be hidden behind other rows); with many rows the measured split plan stays."""
+    for op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
+        few = rr.rr_plan_query(op, 4096, 32768, rr.RR_F32)
+        assert few["path"] == 3 and few["groups_per_row"] == 1
+        assert few["vals_per_lane"] * few["lanes_per_row"] >= 32768
+        many = rr.rr_plan_query(op, 16384, 32768, rr.RR_F32)
+        assert many["groups_per_row"] == 2
+        # rows one workgroup cannot hold are split whatever M is
+        assert rr.rr_plan_query(op, 64, 65536, rr.RR_F32)["groups_per_row"] > 1
+        # the per-element path keeps its plan
+        assert rr.rr_plan_query(op, 64, 32768, rr.RR_F32, False)["vals_per_lane"] <= 16

@@ -38,13 +38,14 @@
     X(32, 1024, 1) X(32, 1024, 2) X(32, 1024, 4) X(32, 1024, 8) X(32, 1024, 16)             \
     X(64, 256, 1) X(64, 256, 2) X(64, 256, 4) X(64, 256, 8) X(64, 256, 16)                  \
     X(64, 512, 1) X(64, 512, 2) X(64, 512, 4) X(64, 512, 8) X(64, 512, 16)                  \
-    X(64, 512, 32) X(64, 512, 64)
+    X(64, 512, 32) X(64, 512, 64) X(64, 512, 128)
 
 // Packed bf16 RMSNorm stream kernels (128-bit path only, see packed_bf16.hpp),
 // named by (R, G): each lane keeps kPackedP = 128 bf16 values as 64 VGPRs of raw
 // chunks.  A plan names them with P = kPackedP.
 constexpr int kPackedP = 128;
-#define RR_PACKED_CONFIGS(X) X(512, 1) X(512, 2) X(512, 4) X(512, 8) X(512, 16) X(512, 32)
+#define RR_PACKED_CONFIGS(X) \
+    X(512, 1) X(512, 2) X(512, 4) X(512, 8) X(512, 16) X(512, 32) X(512, 64)
 
 // RMSNorm backward (persistent, see rmsnorm_bwd.hpp), named by (P, R, G): a lane
 // keeps x, dy (two rows in flight), its w slice and its dw partials, about 6P + 45
@@ -87,6 +88,8 @@ constexpr bool block_config_enabled(int op, int elem_bytes, bool vec, int P, int
     return true;
 }
 
+// Split rows take at most 128 workgroups per row (one wave polls the exchange slots,
+// two per lane).
 // Stream kernels hold two rows' worth of values per lane (about 2P + 40 VGPRs;
 // RMSNorm about 3P + 30, its weight slice coming back from LDS); the weight slice
 // of a workgroup lives in LDS as fp32 (4 * P * R bytes, at most 128 KiB).  The
@@ -96,6 +99,8 @@ constexpr bool block_config_enabled(int op, int elem_bytes, bool vec, int P, int
 // per row: fp32 with 32 values on 1024 lanes no longer fits in 128 VGPRs.
 constexpr bool stream_config_enabled(int op, int elem_bytes, bool vec, int P, int R, int G) {
     if (!vec && P > 16) return false;
+    // 128 workgroups per row (4194304 elements on chip): softmax and RMSNorm forward
+    if (G > 64 && op != kCfgSoftmax && op != kCfgRmsnorm) return false;
     if (op == kCfgXentGrad && elem_bytes == 4 && P == 32 && R == 1024) return false;
     // softmax backward keeps two rows (y, dy) per buffer: about 4P + 40 VGPRs
     if (op == kCfgSoftmaxBwd) return vec ? (R == 1024 ? P <= 16 : P <= 32) : P <= 16;

@@ -86,26 +86,35 @@ __device__ __forceinline__ void publish_pair(GroupRef g, int k, int it, float a,
 
 // Waits until all G members have published iteration `it` and leaves the G pairs
 // merged in member order by `merge2` in bcast[0..1] (the same bits for the whole
-// workgroup).  Called by every thread; uses one barrier.  After a wait has timed
-// out, `spin_limit` is lowered to 1 so that the rest of the launch does not wait
-// again.
+// workgroup).  Called by every thread; uses one barrier.  Lane l of wave 0 polls
+// the slots of members l and l + 64 (G <= 128).  After a wait has timed out,
+// `spin_limit` is lowered to 1 so that the rest of the launch does not wait again.
 template <int G, class Merge>
 __device__ __forceinline__ void wait_pairs(GroupRef g, int it, int &spin_limit, float *bcast,
                                            Merge merge2) {
+    static_assert(G >= 1 && G <= 128, "one wave polls at most two slots per lane");
+    constexpr int kPer = G > 64 ? 2 : 1;
     const int tid = threadIdx.x;
     const uint32_t epoch = (uint32_t)it + 1u;
     const uint64_t *slot = g.slots + (size_t)(it & (kSlotSets - 1)) * G * 2;
     if (tid < 64) {
         const int lane = tid;
-        uint64_t wa = 0, wb = 0;
+        uint64_t wa[kPer], wb[kPer];
+#pragma unroll
+        for (int s = 0; s < kPer; ++s) wa[s] = wb[s] = 0;
         bool all_in = false;
         int spins = 0;
         while (true) {
             bool mine = true;
-            if (lane < G) {
-                wa = atomic_get(slot + 2 * lane);
-                wb = atomic_get(slot + 2 * lane + 1);
-                mine = (uint32_t)(wa >> 32) == epoch && (uint32_t)(wb >> 32) == epoch;
+#pragma unroll
+            for (int s = 0; s < kPer; ++s) {
+                const int m = lane + 64 * s;
+                if (m < G) {
+                    wa[s] = atomic_get(slot + 2 * m);
+                    wb[s] = atomic_get(slot + 2 * m + 1);
+                    mine = mine && (uint32_t)(wa[s] >> 32) == epoch &&
+                           (uint32_t)(wb[s] >> 32) == epoch;
+                }
             }
             all_in = __all(mine);
             if (all_in || ++spins >= spin_limit) break;
@@ -114,15 +123,22 @@ __device__ __forceinline__ void wait_pairs(GroupRef g, int it, int &spin_limit, 
         if (!all_in && lane == 0)
             __hip_atomic_store(g.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (!all_in) bcast[2] = 1.0f;
-        float va = __uint_as_float((uint32_t)wa);
-        float vb = __uint_as_float((uint32_t)wb);
-        float acc_a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(va), 0));
-        float acc_b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vb), 0));
+        float acc_a = 0.0f, acc_b = 0.0f;
 #pragma unroll
-        for (int j = 1; j < G; ++j) {
-            float ja = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(va), j));
-            float jb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vb), j));
-            merge2(acc_a, acc_b, ja, jb);
+        for (int s = 0; s < kPer; ++s) {
+            const float va = __uint_as_float((uint32_t)wa[s]);
+            const float vb = __uint_as_float((uint32_t)wb[s]);
+#pragma unroll
+            for (int j = 0; j < 64 && j + 64 * s < G; ++j) {
+                const float ja = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(va), j));
+                const float jb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vb), j));
+                if (s == 0 && j == 0) {
+                    acc_a = ja;
+                    acc_b = jb;
+                } else {
+                    merge2(acc_a, acc_b, ja, jb);
+                }
+            }
         }
         if (lane == 0) {
             bcast[0] = acc_a;

@@ -1,5 +1,5 @@
 // long_row.hpp -- softmax and RMSNorm forward for rows longer than the split-row
-// stream kernels hold in registers or run faster (more than 2097152 elements; bf16
+// stream kernels hold in registers or run faster (more than 4194304 elements; bf16
 // softmax more than 1048576; the per-element path more than 262144).
 //
 // The QuACK article (无需CUDA代码，给H100加速33%-50%), section 内存吞吐量, names the

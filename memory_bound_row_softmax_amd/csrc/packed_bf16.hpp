@@ -59,8 +59,8 @@ __device__ __forceinline__ float tree_map(F f, Op op) {
     }
 }
 
-// Sum of squares of this workgroup's packed part (chunks past the row end were
-// read past the end of the row's buffer: zeros, which add nothing).
+// Sum of squares of this workgroup's packed part (chunks past the end of its part
+// were read past the end of its buffer: zeros, which add nothing).
 template <int R>
 __device__ __forceinline__ float rmsnorm_packed_local(const float *raw, RowCtx &c) {
     const float q = tree_map<kPackedP, 0>(
@@ -77,7 +77,7 @@ template <int R>
 __device__ __forceinline__ void rmsnorm_packed_apply(const float *raw, const u32x4 *wslot, float Q,
                                                      RowView yv, float *rstd_out, float eps,
                                                      const RowCtx &c) {
-    const int chunk0 = c.member * kPackedC * R;
+    const int chunk0 = c.chunk0;
     const float r = __builtin_amdgcn_rsqf(Q / (float)c.N + eps);
 #pragma unroll
     for (int i = 0; i < kPackedC; ++i) {
@@ -90,7 +90,7 @@ __device__ __forceinline__ void rmsnorm_packed_apply(const float *raw, const u32
             const float ww = __uint_as_float(wq[q]);
             o[q] = pack_bf16x2((bf16_lo(xw) * bf16_lo(ww)) * r, (bf16_hi(xw) * bf16_hi(ww)) * r);
         }
-        if (c.full || ch * 8 < c.N) buf_store16(yv.buf, yv.base + (uint32_t)ch * 16u, o);
+        if (c.full || ch * 8 < c.nend) buf_store16(yv.buf, yv.base + (uint32_t)ch * 16u, o);
     }
     if (rstd_out && c.l == 0 && c.member == 0) *rstd_out = r;
 }
@@ -111,9 +111,11 @@ __global__ void __launch_bounds__(R)
         c.g = group_ref<G>(ws, group);
         if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
     }
-    const int chunk0 = c.member * kPackedC * R;
-    c.full = part_full<BF16, kPackedC, R>(chunk0, N);
+    member_span<8, kPackedC * R, G>(c.member, N, &c.chunk0, &c.nend);
+    const int chunk0 = c.chunk0;
+    c.full = part_full<BF16, kPackedC, R>(chunk0, c.nend);
     const uint32_t rb = (uint32_t)N * 2u;
+    const uint32_t vb = (uint32_t)c.nend * 2u;  // this member's part ends here
 
     // This workgroup's slice of w, packed, once; each lane later reads back only
     // the slots it wrote, so no barrier is needed.
@@ -128,7 +130,7 @@ __global__ void __launch_bounds__(R)
     stream_rows<2>(
         (int64_t)group, M, groups, buf,
         [&](float *v, int64_t r) {
-            load_part_raw<BF16, kPackedC, R>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
+            load_part_raw<BF16, kPackedC, R>(stream_row_view(x, r, M, rb, vb), chunk0, c.l, v);
         },
         [&](float *v, int64_t r) {
             float q = rmsnorm_packed_local<R>(v, c);
@@ -136,7 +138,7 @@ __global__ void __launch_bounds__(R)
                 exchange_pairs<G>(c.g, c.member, c.it, q, 0.0f, c.spin_limit, c.bcast, MergeSum{});
                 q = c.bcast[0];
             }
-            rmsnorm_packed_apply<R>(v, wslot, q, stream_row_view(y, r, M, rb),
+            rmsnorm_packed_apply<R>(v, wslot, q, stream_row_view(y, r, M, rb, vb),
                                     rstd ? rstd + r : nullptr, eps, c);
             ++c.it;
         });

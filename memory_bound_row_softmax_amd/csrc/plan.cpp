@@ -112,41 +112,43 @@ struct Choice {
     bool stream;
     int P, R, G;
 };
-constexpr int kTunedBuckets = 11;
+constexpr int kTunedBuckets = 12;
 constexpr int64_t kTunedN[kTunedBuckets] = {256,    1024,   4096,   16384,   32768,  65536,
-                                            131072, 262144, 524288, 1048576, 2097152};
+                                            131072, 262144, 524288, 1048576, 2097152,
+                                            4194304};
 // A choice with P = 0: no on-chip plan (softmax and RMSNorm then read the row twice).
 constexpr Choice kTwoReads = {false, 0, 0, 0};
 //   [op: softmax, rmsnorm, softmax backward, cross-entropy gradient][dtype: f32, bf16][N bucket]
-// (the three longest buckets were timed at 4096, 2048 and 512-1024 rows)
+// (the four longest buckets were timed at 4096, 2048, 512-1024 and 256-512 rows)
 static const Choice kTuned[4][2][kTunedBuckets] = {
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {true, 64, 512, 1},
       {true, 16, 1024, 2}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8},
-      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}},
+      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, {true, 64, 512, 128}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 16, 256, 1}, {false, 64, 256, 1},
       {true, 32, 1024, 1}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8},
-      {true, 64, 512, 16}, {true, 64, 512, 32}, kTwoReads}},
+      {true, 64, 512, 16}, {true, 64, 512, 32}, kTwoReads, kTwoReads}},
     {{{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 16, 1024, 1},
       {true, 16, 1024, 2}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 32, 512, 16},
-      {true, 32, 512, 32}, {true, 32, 512, 64}, {true, 64, 512, 64}},
+      {true, 32, 512, 32}, {true, 32, 512, 64}, {true, 64, 512, 64}, {true, 64, 512, 128}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {true, 32, 1024, 1},
       {false, 64, 512, 1}, {true, 32, 1024, 2}, {true, 64, 512, 4}, {true, kPackedP, 512, 4},
-      {true, kPackedP, 512, 8}, {true, kPackedP, 512, 16}, {true, kPackedP, 512, 32}}},
+      {true, kPackedP, 512, 8}, {true, kPackedP, 512, 16}, {true, kPackedP, 512, 32},
+      {true, kPackedP, 512, 64}}},
     // softmax backward (y and dy both held: at most 32 values per lane in a stream kernel)
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 16, 256, 1}, {false, 32, 1024, 1},
       {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
-      {true, 32, 512, 32}, {true, 32, 512, 64}, kTwoReads},
+      {true, 32, 512, 32}, {true, 32, 512, 64}, kTwoReads, kTwoReads},
      {{false, 8, 32, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 16, 1024, 1},
       {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
-      {true, 32, 512, 32}, {true, 32, 512, 64}, kTwoReads}},
+      {true, 32, 512, 32}, {true, 32, 512, 64}, kTwoReads, kTwoReads}},
     // cross-entropy forward fused with its gradient (the softmax kernels; block kernels
     // hold longer rows here than for the softmax)
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {true, 16, 1024, 1},
       {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 64, 512, 8},
-      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}},
+      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads},
      {{false, 16, 16, 1}, {false, 64, 16, 1}, {false, 16, 256, 1}, {false, 32, 512, 1},
       {false, 64, 512, 1}, {false, 64, 1024, 1}, {true, 64, 512, 4}, {true, 32, 1024, 8},
-      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}}},
+      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads}},
 };
 
 static bool try_choice(int op, int dtype, bool vec, int64_t N, Choice c, Plan *p) {
@@ -182,6 +184,13 @@ static bool default_row(int op, int dtype, bool vec, int64_t M, int64_t N, Plan 
     if (N <= kTunedN[kTunedBuckets - 1]) {
         Choice c = kTuned[o][d][k];
         if (c.P == 0) return false;  // no on-chip plan measured faster than two reads
+        // Softmax rows on 128 workgroups (2M to 4M elements) measured faster than
+        // two reads only when they fill at least 9/10 of the plan: fp32 rows of
+        // 3.5M, 3.67M, 3.9M and 4M elements ran at 0.94, 0.97, 1.03 and 1.10 times
+        // the two-read rate.  RMSNorm gained at every fill measured (1.14-1.36).
+        if (op == kOpSoftmax && c.stream && c.G == 128 &&
+            10 * N < 9 * (int64_t)c.P * c.R * c.G)
+            return false;
         if (c.stream && c.G > 1 && M <= kFewRows &&
             try_choice(op, dtype, vec, N, Choice{true, 32, 1024, 1}, p))
             return true;

@@ -32,6 +32,32 @@ __device__ __forceinline__ bool part_full(int chunk0, int N) {
     return (int64_t)(chunk0 + C * R) * E::VPC <= (int64_t)N;
 }
 
+// The part of a row that member `member` of the G workgroups of a split row holds:
+// chunks [chunk0, chunk0 + S) with S = ceil(row chunks / G) rounded up to whole
+// waves (64 chunks), so the G workgroups get equal shares even when the row does
+// not fill the configuration; `nend` is the end of that part in elements (at most
+// N; at or below chunk0 * VPC when the member holds nothing).  A lane still owns
+// chunks chunk0 + i * R + l (i < C); those at or past `nend` belong to the next
+// member and are masked, and the member's buffer resources end at `nend`, so they
+// are neither read nor written.  With G = 1: the whole row.
+template <int VPC, int CR, int G>
+__device__ __forceinline__ void member_span(int member, int N, int *chunk0, int *nend) {
+    if constexpr (G == 1) {
+        *chunk0 = 0;
+        *nend = N;
+    } else {
+        static_assert(CR % 64 == 0, "a member's part is whole waves");
+        const int total = (N + VPC - 1) / VPC;
+        int span = (total + G - 1) / G;
+        span = (span + 63) & ~63;
+        if (span > CR) span = CR;  // N beyond P * R * G: never planned
+        const int c0 = member * span;
+        const int64_t end = (int64_t)(c0 + span) * VPC;
+        *chunk0 = c0;
+        *nend = (int)(end < (int64_t)N ? end : (int64_t)N);
+    }
+}
+
 // POLICY: kStreamLoad for data read once, kReuseLoad for data read by every row.
 template <class E, int C, int R, bool VEC, int POLICY = kStreamLoad>
 __device__ __forceinline__ void load_part(RowView rv, int chunk0, int l, float *v) {

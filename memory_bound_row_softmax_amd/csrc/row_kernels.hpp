@@ -65,6 +65,14 @@ __device__ __forceinline__ RowView stream_row_view(const char *base, int64_t row
     return {make_buf(base + (ok ? row : 0) * row_bytes, ok ? row_bytes : 0u), 0u};
 }
 
+// The same, with the buffer ending `span_bytes` into the row (the end of a split
+// row member's part, see member_span).
+__device__ __forceinline__ RowView stream_row_view(const char *base, int64_t row, int64_t M,
+                                                   uint32_t row_bytes, uint32_t span_bytes) {
+    const bool ok = row < M;
+    return {make_buf(base + (ok ? row : 0) * row_bytes, ok ? span_bytes : 0u), 0u};
+}
+
 // Row loop of the stream kernels with D register buffers.  Rows group,
 // group + groups, ... < M are processed in order; buffer k % D holds the k-th of
 // them.  Before row k is finished, the loads of row k + D - 1 are issued, so
@@ -111,6 +119,8 @@ struct RowCtx {
     float *bcast;   // LDS: merged split-row partials [0..1], "a wait timed out" flag [2]
     GroupRef g;
     int spin_limit;
+    int chunk0 = 0;  // first chunk of this workgroup's part of the row (member_span)
+    int nend = N;    // end of that part, in elements
 
     // Slots for a row body with a single reduction.  A slot array may be written
     // again only after a later barrier (waves_combine), so a persistent kernel
@@ -147,7 +157,7 @@ struct SoftmaxOut {
     static constexpr int kExtra = 0;
     struct Epi {
         template <class E, int C, int R>
-        __device__ __forceinline__ void capture(const float *, int, int) {}
+        __device__ __forceinline__ void capture(const float *, int, int, int) {}
         template <class E, int C, int R>
         __device__ __forceinline__ void apply(float *v, float scale, float, float, int,
                                               const RowCtx &, bool) {
@@ -165,9 +175,9 @@ struct SoftmaxOut {
 template <class E, int P, int R, class Epi>
 __device__ __forceinline__ MaxSum softmax_local(float *v, RowCtx &c, Epi &epi) {
     constexpr int C = P / E::VPC;
-    const int chunk0 = c.member * C * R;
-    epi.template capture<E, C, R>(v, chunk0, c.l);
-    if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.N, -INFINITY, v);
+    const int chunk0 = c.chunk0;
+    epi.template capture<E, C, R>(v, chunk0, c.l, c.nend);
+    if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.nend, -INFINITY, v);
 
     // pass 1: row max
     float m = tree_reduce<P>(v, OpMax{});
@@ -188,14 +198,14 @@ template <class E, int P, int R, int G, bool VEC, class Epi>
 __device__ __forceinline__ void softmax_apply(float *v, RowView yv, bool valid, RowCtx &c,
                                               Epi &epi, MaxSum loc, float Mrow, float Srow) {
     constexpr int C = P / E::VPC;
-    const int chunk0 = c.member * C * R;
+    const int chunk0 = c.chunk0;
     float scale;
     if constexpr (G == 1)
         scale = __builtin_amdgcn_rcpf(Srow);
     else
         scale = exp_shift(loc.m, safe_max(Mrow)) * __builtin_amdgcn_rcpf(Srow);
     epi.template apply<E, C, R>(v, scale, Mrow, Srow, chunk0, c, valid);
-    store_part<E, C, R, VEC>(yv, chunk0, c.l, c.N, valid, c.full, v);
+    store_part<E, C, R, VEC>(yv, chunk0, c.l, c.nend, valid, c.full, v);
 }
 
 // Passes 1-3 on a lane's loaded part v of the row, then the store.
@@ -250,9 +260,11 @@ __global__ void __launch_bounds__(R)
         c.g = group_ref<G>(ws, group);
         if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
     }
-    const int chunk0 = c.member * C * R;
-    c.full = part_full<E, C, R>(chunk0, N);
+    member_span<E::VPC, C * R, G>(c.member, N, &c.chunk0, &c.nend);
+    const int chunk0 = c.chunk0;
+    c.full = part_full<E, C, R>(chunk0, c.nend);
     const uint32_t rb = (uint32_t)N * E::BYTES;
+    const uint32_t vb = (uint32_t)c.nend * E::BYTES;  // this member's part ends here
 
     // Per-row inputs of the output policy (if any) sit after a row's values in its
     // buffer and are loaded with it.
@@ -270,9 +282,9 @@ __global__ void __launch_bounds__(R)
         // registers) and widened when it becomes the current row.
         auto load = [&](float *v, int64_t r) {
             if constexpr (VEC)
-                load_part_raw<E, C, R>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
+                load_part_raw<E, C, R>(stream_row_view(x, r, M, rb, vb), chunk0, c.l, v);
             else
-                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
+                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb, vb), chunk0, c.l, v);
             if (r < M) out.stash(v + P, r);
         };
         load(buf[0], row);
@@ -289,7 +301,7 @@ __global__ void __launch_bounds__(R)
             }
             if (c.it > 0) {  // complete the previous row
                 wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeMaxSum{});
-                softmax_apply<E, P, R, G, VEC>(buf[KP], stream_row_view(y, row - groups, M, rb),
+                softmax_apply<E, P, R, G, VEC>(buf[KP], stream_row_view(y, row - groups, M, rb, vb),
                                                true, c, epis[KP], pend, c.bcast[0], c.bcast[1]);
             }
             pend = cur;
@@ -308,12 +320,12 @@ __global__ void __launch_bounds__(R)
         stream_rows<D>(
             (int64_t)group, M, groups, buf,
             [&](float *v, int64_t r) {
-                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
+                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb, vb), chunk0, c.l, v);
                 if (r < M) out.stash(v + P, r);
             },
             [&](float *v, int64_t r) {
                 auto epi = out.epi(v + P, r);
-                softmax_finish<E, P, R, G, VEC>(v, stream_row_view(y, r, M, rb), true, c, epi);
+                softmax_finish<E, P, R, G, VEC>(v, stream_row_view(y, r, M, rb, vb), true, c, epi);
                 ++c.it;
             });
     }
@@ -364,8 +376,8 @@ struct WeightLds {
 template <class E, int P, int R>
 __device__ __forceinline__ float rmsnorm_local(float *v, RowCtx &c) {
     constexpr int C = P / E::VPC;
-    const int chunk0 = c.member * C * R;
-    if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.N, 0.0f, v);
+    const int chunk0 = c.chunk0;
+    if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.nend, 0.0f, v);
     const float q = tree_sum_squares<P>(v);
     return row_reduce<R>(q, c.one_reduction_slots(), c.l, OpSum{});
 }
@@ -377,12 +389,12 @@ __device__ __forceinline__ void rmsnorm_apply(float *v, const Weight &w, float Q
                                               float *rstd_out, float eps, bool valid,
                                               const RowCtx &c) {
     constexpr int C = P / E::VPC;
-    const int chunk0 = c.member * C * R;
+    const int chunk0 = c.chunk0;
     const float r = __builtin_amdgcn_rsqf(Q / (float)c.N + eps);
     w.apply(v, c.l);
 #pragma unroll
     for (int j = 0; j < P; ++j) v[j] *= r;
-    store_part<E, C, R, VEC>(yv, chunk0, c.l, c.N, valid, c.full, v);
+    store_part<E, C, R, VEC>(yv, chunk0, c.l, c.nend, valid, c.full, v);
     if (rstd_out && valid && c.l == 0 && c.member == 0) *rstd_out = r;
 }
 
@@ -436,9 +448,11 @@ __global__ void __launch_bounds__(R)
         c.g = group_ref<G>(ws, group);
         if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
     }
-    const int chunk0 = c.member * C * R;
-    c.full = part_full<E, C, R>(chunk0, N);
+    member_span<E::VPC, C * R, G>(c.member, N, &c.chunk0, &c.nend);
+    const int chunk0 = c.chunk0;
+    c.full = part_full<E, C, R>(chunk0, c.nend);
     const uint32_t rb = (uint32_t)N * E::BYTES;
+    const uint32_t vb = (uint32_t)c.nend * E::BYTES;  // this member's part ends here
 
     // This workgroup's slice of w, once; each lane later reads back only the
     // slots it wrote, so no barrier is needed.
@@ -457,9 +471,9 @@ __global__ void __launch_bounds__(R)
         int64_t row = group;
         auto load = [&](float *v, int64_t r) {
             if constexpr (VEC)
-                load_part_raw<E, C, R>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
+                load_part_raw<E, C, R>(stream_row_view(x, r, M, rb, vb), chunk0, c.l, v);
             else
-                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
+                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb, vb), chunk0, c.l, v);
         };
         load(buf[0], row);
         load(buf[1], row + groups);
@@ -475,7 +489,7 @@ __global__ void __launch_bounds__(R)
                 wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeSum{});
                 const int64_t rp = row - groups;
                 rmsnorm_apply<E, P, R, VEC>(buf[KP], wsrc, c.bcast[0],
-                                            stream_row_view(y, rp, M, rb),
+                                            stream_row_view(y, rp, M, rb, vb),
                                             rstd ? rstd + rp : nullptr, eps, true, c);
             }
             if (!more) return false;
@@ -491,10 +505,10 @@ __global__ void __launch_bounds__(R)
         stream_rows<D>(
             (int64_t)group, M, groups, buf,
             [&](float *v, int64_t r) {
-                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), chunk0, c.l, v);
+                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb, vb), chunk0, c.l, v);
             },
             [&](float *v, int64_t r) {
-                rmsnorm_finish<E, P, R, G, VEC>(v, wsrc, stream_row_view(y, r, M, rb),
+                rmsnorm_finish<E, P, R, G, VEC>(v, wsrc, stream_row_view(y, r, M, rb, vb),
                                                 rstd ? rstd + r : nullptr, eps, true, c);
                 ++c.it;
             });

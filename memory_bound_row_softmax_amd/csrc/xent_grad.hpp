@@ -44,14 +44,14 @@ struct XentGradOut {
         // index: "pick one of these registers" turned into an address would move
         // the whole row out of registers.
         template <class E, int C, int R>
-        __device__ __forceinline__ void capture(const float *v, int chunk0, int l) {
+        __device__ __forceinline__ void capture(const float *v, int chunk0, int l, int nend) {
             constexpr int VPC = E::VPC;
             uint32_t bits = 0;
             bool found = false;
 #pragma unroll
             for (int i = 0; i < C; ++i) {
                 const int d = label - (chunk0 + i * R + l) * VPC;
-                if ((unsigned)d < (unsigned)VPC) {
+                if ((unsigned)d < (unsigned)VPC && label < nend) {
 #pragma unroll
                     for (int e = 0; e < VPC; ++e)
                         bits |= __float_as_uint(v[i * VPC + e]) & (0u - (uint32_t)(d == e));

@@ -71,16 +71,18 @@ def sweep():
     return out
 
 
-# The longest rows held on chip (one read, 16 to 64 workgroups per row): 1M and 2M
-# elements.
+# The longest rows held on chip (one read, 16 to 128 workgroups per row): 1M, 2M
+# and 4M elements.
 WIDE = [Workload("softmax_f32_1024x1048576", "softmax", "f32", 1024, 1 << 20),
         Workload("rmsnorm_bf16_2048x1048576", "rmsnorm", "bf16", 2048, 1 << 20),
         Workload("softmax_f32_512x2097152", "softmax", "f32", 512, 1 << 21),
-        Workload("rmsnorm_bf16_1024x2097152", "rmsnorm", "bf16", 1024, 1 << 21)]
-
-# Rows past the on-chip capacity (read twice): 4M-element rows.
-LONG = [Workload("softmax_f32_256x4194304", "softmax", "f32", 256, 1 << 22),
+        Workload("rmsnorm_bf16_1024x2097152", "rmsnorm", "bf16", 1024, 1 << 21),
+        Workload("softmax_f32_256x4194304", "softmax", "f32", 256, 1 << 22),
         Workload("rmsnorm_bf16_512x4194304", "rmsnorm", "bf16", 512, 1 << 22)]
+
+# Rows past the on-chip capacity (read twice): 8M-element rows.
+LONG = [Workload("softmax_f32_128x8388608", "softmax", "f32", 128, 1 << 23),
+        Workload("rmsnorm_bf16_256x8388608", "rmsnorm", "bf16", 256, 1 << 23)]
 
 
 def by_name(name: str) -> Workload:

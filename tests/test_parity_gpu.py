@@ -76,7 +76,10 @@ FORCED_ROW = [  # (kind, P, R, G, M, N): split rows at small N, empty / partial 
     # deferred exchange (8 or more workgroups per row): many rows per row group, so
     # the four slot sets are reused many times over
     ("stream", 64, 512, 8, 333, 200000), ("stream", 16, 1024, 16, 150, 250000),
-    ("stream", 16, 1024, 8, 1000, 70000)]
+    ("stream", 16, 1024, 8, 1000, 70000),
+    # 128 workgroups per row: most members hold nothing of a short row; 10 rows per
+    # row group
+    ("stream", 64, 512, 128, 20, 100000)]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -102,7 +105,8 @@ def test_forced_row_plans(kind, P, R, G, M, N, dtype):
 
 PACKED = [  # (G, M, N): packed bf16 RMSNorm (128 values per lane on 512 lanes)
     (1, 300, 65536), (1, 700, 20000), (1, 3, 8), (2, 100, 131072), (2, 61, 65544),
-    (4, 90, 200000), (8, 40, 524288), (16, 7, 1000000), (16, 5, 300000), (16, 33, 1 << 20)]
+    (4, 90, 200000), (8, 40, 524288), (16, 7, 1000000), (16, 5, 300000), (16, 33, 1 << 20),
+    (64, 5, 1 << 22), (64, 9, 3_000_000)]
 
 
 @pytest.mark.parametrize("G,M,N", PACKED)
@@ -307,7 +311,10 @@ OVERSUBSCRIBED = [  # (op, dtype, M, N): row groups forced to M, far more than f
     ("softmax", "bf16", 64, 1 << 20),   # 32 per row: 2048
     ("rmsnorm", "bf16", 256, 262144),   # packed, 4 per row: 1024 (one fits per CU)
     ("rmsnorm", "f32", 96, 1 << 20),    # 64 per row: 6144
-    ("softmax", "f32", 64, 3_000_000),  # two-pass long rows, 16 per row: 1024
+    ("softmax", "f32", 64, 3_000_000),  # two-pass long rows, 32 per row: 2048
+    ("rmsnorm", "f32", 3, 3_000_000),   # 128 per row: 384, of which 256 fit at once
+    ("softmax", "f32", 4, 1 << 22),     # 128 per row: 512
+    ("softmax", "f32", 16, 5_000_000),  # two-pass long rows, 64 per row: 1024
 ]
 
 
@@ -349,12 +356,12 @@ def test_stream_copy():
 
 # ------------------------------------------------------------- rows past on-chip capacity
 
-# Aligned rows up to 2^21 elements stay on chip (split over up to 64 workgroups);
-# rows that are not 16-byte aligned hold at most 16 values on 1024 lanes of 16
-# workgroups on chip (262144 elements) and go to the two-pass kernel past that.  The
-# two-pass softmax splits fp32 rows of 3M elements over 32 workgroups and of 8M
-# over 64.
-LONG = [(3, 524289), (2, (1 << 21) + 8), (2, 1_000_003), (1, 3_000_000), (2, 1 << 23)]
+# Aligned rows up to 2^22 elements stay on chip (split over up to 128 workgroups;
+# bf16 softmax up to 2^20); rows that are not 16-byte aligned hold at most 16 values
+# on 1024 lanes of 16 workgroups on chip (262144 elements) and go to the two-pass
+# kernel past that.  The two-pass softmax splits fp32 rows of 5M elements over 64
+# workgroups and of 8M over 64.
+LONG = [(3, 524289), (2, (1 << 22) + 8), (2, 1_000_003), (1, 5_000_000), (2, 1 << 23)]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -370,20 +377,24 @@ def test_long_rows_read_twice(M, N, dtype):
 
 
 SPLIT_WIDE = [(3, 524288), (3, 524296), (2, 1 << 20), (5, 1_000_000), (40, 786432),
-              (2, 1 << 21), (24, 1_500_000)]
+              (2, 1 << 21), (24, 1_500_000), (2, (1 << 21) + 8), (1, 3_000_000), (3, 1 << 22),
+              (9, 3_500_000), (5, 3_800_000)]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("M,N", SPLIT_WIDE)
 def test_rows_split_over_many_workgroups(M, N, dtype):
-    """Aligned rows from 2^19 to 2^21 elements: one read, 8 to 64 workgroups per row
-    (bf16 RMSNorm packed, 8 to 32; 40 rows give each row group several rows, so every
-    exchange slot set is used)."""
+    """Aligned rows from 2^19 to 2^22 elements: one read, 8 to 128 workgroups per row
+    (bf16 RMSNorm packed, 8 to 64; 40 rows, or 9 rows on two row groups of 128, give
+    each row group several rows, so every exchange slot set is used)."""
     code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
     for op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
         p = rr.rr_plan_query(op, M, N, code)
         if op == rr.RR_OP_SOFTMAX and dtype == "bf16" and N > 1 << 20:
             assert p["path"] == 4  # bf16 softmax past 1M elements: two reads measured faster
+            continue
+        if op == rr.RR_OP_SOFTMAX and 1 << 21 < N and 10 * N < 9 * (1 << 22):
+            assert p["path"] == 4  # fp32 softmax on 128 workgroups: only from 9/10 full
             continue
         assert p["path"] == 1 and p["groups_per_row"] >= 8, p
         assert p["vals_per_lane"] * p["lanes_per_row"] * p["groups_per_row"] >= N

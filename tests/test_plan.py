@@ -47,12 +47,37 @@ def test_row_plans_hold_the_row(op, dt, vec):
             assert G == 1 or (G // 2) * P * R < N
             assert p["ws_bytes"] == (256 + 1024 * (64 + 64 * G) if G > 1 else 0)
     if op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):  # long rows: read twice, up to 2^28
-        assert rr.rr_plan_query(op, 16, (1 << 21) + 1, dt, vec)["path"] == 4
+        assert rr.rr_plan_query(op, 16, (1 << 22) + 1, dt, vec)["path"] == 4
         with pytest.raises(rr.RRError):
             rr.rr_plan_query(op, 16, (1 << 28) + 1, dt, vec)
     else:
         with pytest.raises(rr.RRError):
             rr.rr_plan_query(op, 16, (1 << 21) + 1, dt, vec)
+
+
+def test_rows_up_to_4m_elements_stay_on_chip():
+    """Aligned rows of 2^21 to 2^22 elements are split over 128 workgroups (64 values
+    on 512 lanes; bf16 RMSNorm packed, 64 workgroups of 128 values) and read once;
+    fp32 softmax only from 9/10 of 2^22 elements, bf16 softmax past 2^20 elements and
+    the per-element path past 2^18 read twice."""
+    for N in ((1 << 21) + 1, 3_000_000, 3_774_874, 1 << 22):
+        for op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
+            p = rr.rr_plan_query(op, 256, N, rr.RR_F32)
+            if op == rr.RR_OP_SOFTMAX and 10 * N < 9 * (1 << 22):
+                # softmax on 128 workgroups only when the row fills 9/10 of them
+                assert p["path"] == 4, (N, p)
+                continue
+            assert (p["path"], p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]) == \
+                (1, 64, 512, 128), (op, N, p)
+            assert p["ws_bytes"] == 256 + 256 * (64 + 64 * 128)
+        p = rr.rr_plan_query(rr.RR_OP_RMSNORM, 256, N, rr.RR_BF16)
+        assert (p["path"], p["vals_per_lane"], p["groups_per_row"]) == (1, 128, 64), (N, p)
+        assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 256, N, rr.RR_BF16)["path"] == 4
+        for op in (rr.RR_OP_XENT_GRAD, rr.RR_OP_SOFTMAX_BWD):
+            with pytest.raises(rr.RRError):
+                rr.rr_plan_query(op, 256, N, rr.RR_F32)
+    for dt in (rr.RR_F32, rr.RR_BF16):
+        assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 256, 1 << 22, dt, False)["path"] == 4
 
 
 @pytest.mark.parametrize("dt", (rr.RR_F32, rr.RR_BF16))
@@ -167,17 +192,17 @@ def test_rmsnorm_bwd_plans(dt, vec):
 def test_long_rows_take_the_two_pass_kernel(monkeypatch):
     for op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
         for dt in (rr.RR_F32, rr.RR_BF16):
-            for n in (1 << 20, 1 << 21):
+            for n in (1 << 20, 1 << 21, 1 << 22):
                 on_chip = rr.rr_plan_query(op, 1000, n, dt)
                 if op == rr.RR_OP_SOFTMAX and dt == rr.RR_BF16 and n > 1 << 20:
                     # measured faster with two reads than on 64 workgroups
                     assert on_chip["path"] == 4
                     continue
                 G = on_chip["groups_per_row"]
-                assert on_chip["path"] == 1 and G in (16, 32, 64)
+                assert on_chip["path"] == 1 and G in (16, 32, 64, 128)
                 assert on_chip["vals_per_lane"] * on_chip["lanes_per_row"] * G == n
                 assert on_chip["ws_bytes"] == 256 + 1000 * (64 + 64 * G)
-            for n in ((1 << 21) + 8, 3_000_000, 1 << 23, 1 << 26):
+            for n in ((1 << 22) + 8, 5_000_000, 1 << 23, 1 << 26):
                 p = rr.rr_plan_query(op, 1000, n, dt)
                 # RMSNorm: 16 workgroups per row; softmax: enough that a workgroup's
                 # share of the row is at most 512 KiB (16 to 64)

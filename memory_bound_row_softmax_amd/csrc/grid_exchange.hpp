@@ -34,8 +34,13 @@
 // every group but the one holding the latest ticket has all its members started:
 // those groups never wait on a workgroup that has not started, finish their rows
 // and exit, and the free slots then start the missing members of the last group.
-// The grid drains as long as G workgroups fit on the device at once (the planner
-// sizes the grid from the occupancy query, so all of it normally runs at once).
+// The planner sizes the grid from the occupancy query, so all of it normally runs
+// at once.  A grid larger than that (other work holding slots, or a test override)
+// still drains when one XCD can hold G workgroups of the kernel at once: a
+// workgroup runs on the XCD its block id names (block id mod 8), so near the end
+// of the grid the only workgroups left to start may all belong to one XCD, and a
+// partial group must not be able to fill that XCD's slots by itself.  Past that,
+// the bounded wait ends a wait that cannot be met.
 // The last workgroup to leave the grid zeroes the ticket and exit counters.
 #pragma once
 

@@ -22,7 +22,8 @@ hipError_t resident_groups(K kernel, int block, int G, int64_t M, const LaunchAr
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0);
     if (e != hipSuccess) return e;
     int64_t g = (int64_t)per_cu * a.num_cus / G;
-    // test override: a grid larger than fits at once (split rows must still drain)
+    // test override: a grid larger than fits at once (split rows must still drain
+    // when one XCD holds G workgroups)
     const char *fg = std::getenv("RR_FORCE_GROUPS");
     if (fg && *fg && std::atoi(fg) > 0) g = std::atoi(fg);
     if (g > kMaxGroups) g = kMaxGroups;

@@ -39,12 +39,13 @@ namespace rr {
 // Rows past M read 0 (past the end of the buffer) and are never written.
 template <int R>
 __device__ __forceinline__ RowView rows_view(const char *base, int64_t M, int64_t blk, int sub,
-                                             uint32_t row_bytes) {
+                                             uint32_t row_bytes, uint32_t span_bytes) {
     constexpr int RPB = rows_per_block_for(R);
     const int64_t first = blk * RPB;
     if (first >= M) return {make_buf(base, 0u), 0u};
     if constexpr (R >= 64) {
-        if constexpr (RPB == 1) return {make_buf(base + first * row_bytes, row_bytes), 0u};
+        // one row per workgroup: the buffer ends with this member's part (member_span)
+        if constexpr (RPB == 1) return {make_buf(base + first * row_bytes, span_bytes), 0u};
         int64_t row = first + sub;
         const bool ok = row < M;
         return {make_buf(base + (ok ? row : 0) * row_bytes, ok ? row_bytes : 0u), 0u};
@@ -86,10 +87,10 @@ __device__ __forceinline__ void rmsnorm_bwd_finish(float *a, float *b, float r,
                                                    const WeightLds<P, R> &wsrc, float *acc,
                                                    RowView dxv, bool valid, RowCtx &c) {
     constexpr int C = P / E::VPC;
-    const int chunk0 = c.member * C * R;
+    const int chunk0 = c.chunk0;
     if (!c.full) {
-        mask_part<E, C, R>(chunk0, c.l, c.N, 0.0f, a);
-        mask_part<E, C, R>(chunk0, c.l, c.N, 0.0f, b);
+        mask_part<E, C, R>(chunk0, c.l, c.nend, 0.0f, a);
+        mask_part<E, C, R>(chunk0, c.l, c.nend, 0.0f, b);
     }
     // dw partial first (before b is overwritten): dy * x * r
 #pragma unroll
@@ -105,7 +106,7 @@ __device__ __forceinline__ void rmsnorm_bwd_finish(float *a, float *b, float r,
     const float k = r * r * t / (float)c.N;
 #pragma unroll
     for (int j = 0; j < P; ++j) a[j] = r * (b[j] - a[j] * k);
-    store_part<E, C, R, VEC>(dxv, chunk0, c.l, c.N, valid, c.full, a);
+    store_part<E, C, R, VEC>(dxv, chunk0, c.l, c.nend, valid, c.full, a);
 }
 
 constexpr int bwd_threads(int R, int G) { return G == 1 ? block_threads_for(R) : R; }
@@ -131,9 +132,11 @@ __global__ void __launch_bounds__(bwd_threads(R, G))
         c.g = group_ref<G>(ws, group);
         if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
     }
-    const int chunk0 = c.member * C * R;
-    c.full = part_full<E, C, R>(chunk0, N);
+    member_span<E::VPC, C * R, G>(c.member, N, &c.chunk0, &c.nend);
+    const int chunk0 = c.chunk0;
+    c.full = part_full<E, C, R>(chunk0, c.nend);
     const uint32_t rb = (uint32_t)N * E::BYTES;
+    const uint32_t vb = (uint32_t)c.nend * E::BYTES;  // this member's part ends here
     const int64_t nblk = (M + RPB - 1) / RPB;
 
     // The workgroup's slice of w, once, decoded to fp32 in LDS (the lane groups of a
@@ -157,15 +160,15 @@ __global__ void __launch_bounds__(bwd_threads(R, G))
     stream_rows<2>(
         (int64_t)group, nblk, groups, buf,
         [&](float *v, int64_t blk) {
-            load_part<E, C, R, VEC>(rows_view<R>(x, M, blk, sub, rb), chunk0, l, v);
-            load_part<E, C, R, VEC>(rows_view<R>(dy, M, blk, sub, rb), chunk0, l, v + P);
+            load_part<E, C, R, VEC>(rows_view<R>(x, M, blk, sub, rb, vb), chunk0, l, v);
+            load_part<E, C, R, VEC>(rows_view<R>(dy, M, blk, sub, rb, vb), chunk0, l, v + P);
             const int64_t row = blk * RPB + sub;
             v[2 * P] = (blk < nblk) ? rstd[row < M ? row : M - 1] : 0.0f;
         },
         [&](float *v, int64_t blk) {
             const int64_t row = blk * RPB + sub;
             rmsnorm_bwd_finish<E, P, R, G, VEC>(v, v + P, v[2 * P], wsrc, acc,
-                                                rows_view<R>(dx, M, blk, sub, rb), row < M, c);
+                                                rows_view<R>(dx, M, blk, sub, rb, vb), row < M, c);
             ++c.it;
         });
     if constexpr (G > 1) {
@@ -192,7 +195,7 @@ __global__ void __launch_bounds__(bwd_threads(R, G))
     }
     if (sub == 0) {
         const Buf pb = make_buf(partial + (int64_t)group * N, (uint32_t)N * 4u);
-        store_part_f32<E, C, R>(pb, chunk0, l, N, acc);
+        store_part_f32<E, C, R>(pb, chunk0, l, c.nend, acc);  // this member's columns only
     }
 }
 

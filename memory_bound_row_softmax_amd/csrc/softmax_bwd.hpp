@@ -29,8 +29,8 @@ namespace rr {
 template <class E, int P, int R>
 __device__ __forceinline__ float softmax_bwd_local(float *a, float *b, RowCtx &c) {
     constexpr int C = P / E::VPC;
-    const int chunk0 = c.member * C * R;
-    if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.N, 0.0f, a);
+    const int chunk0 = c.chunk0;
+    if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.nend, 0.0f, a);
     const float t = tree_dot<P>(a, b);
     return row_reduce<R>(t, c.one_reduction_slots(), c.l, OpSum{});
 }
@@ -40,10 +40,10 @@ template <class E, int P, int R, bool VEC>
 __device__ __forceinline__ void softmax_bwd_apply(float *a, const float *b, float t,
                                                   RowView dxv, bool valid, const RowCtx &c) {
     constexpr int C = P / E::VPC;
-    const int chunk0 = c.member * C * R;
+    const int chunk0 = c.chunk0;
 #pragma unroll
     for (int j = 0; j < P; ++j) a[j] = a[j] * (b[j] - t);
-    store_part<E, C, R, VEC>(dxv, chunk0, c.l, c.N, valid, c.full, a);
+    store_part<E, C, R, VEC>(dxv, chunk0, c.l, c.nend, valid, c.full, a);
 }
 
 // a: the lane's part of y, b: of dy; a becomes dx.
@@ -94,9 +94,11 @@ __global__ void __launch_bounds__(R)
         c.g = group_ref<G>(ws, group);
         if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
     }
-    const int chunk0 = c.member * C * R;
-    c.full = part_full<E, C, R>(chunk0, N);
+    member_span<E::VPC, C * R, G>(c.member, N, &c.chunk0, &c.nend);
+    const int chunk0 = c.chunk0;
+    c.full = part_full<E, C, R>(chunk0, c.nend);
     const uint32_t rb = (uint32_t)N * E::BYTES;
+    const uint32_t vb = (uint32_t)c.nend * E::BYTES;  // this member's part ends here
 
     if constexpr (kDeferredExchange && defer_split(kCfgSoftmaxBwd, E::BYTES, VEC, P, R, G)) {
         // Split rows, deferred exchange (see the softmax stream kernel): row k's
@@ -106,11 +108,11 @@ __global__ void __launch_bounds__(R)
         int64_t row = group;
         auto load = [&](float *v, int64_t r) {
             if constexpr (VEC) {
-                load_part_raw<E, C, R>(stream_row_view(y, r, M, rb), chunk0, c.l, v);
-                load_part_raw<E, C, R>(stream_row_view(dy, r, M, rb), chunk0, c.l, v + P);
+                load_part_raw<E, C, R>(stream_row_view(y, r, M, rb, vb), chunk0, c.l, v);
+                load_part_raw<E, C, R>(stream_row_view(dy, r, M, rb, vb), chunk0, c.l, v + P);
             } else {
-                load_part<E, C, R, VEC>(stream_row_view(y, r, M, rb), chunk0, c.l, v);
-                load_part<E, C, R, VEC>(stream_row_view(dy, r, M, rb), chunk0, c.l, v + P);
+                load_part<E, C, R, VEC>(stream_row_view(y, r, M, rb, vb), chunk0, c.l, v);
+                load_part<E, C, R, VEC>(stream_row_view(dy, r, M, rb, vb), chunk0, c.l, v + P);
             }
         };
         load(buf[0], row);
@@ -129,7 +131,7 @@ __global__ void __launch_bounds__(R)
             if (c.it > 0) {  // complete the previous row
                 wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeSum{});
                 softmax_bwd_apply<E, P, R, VEC>(buf[KP], buf[KP] + P, c.bcast[0],
-                                                stream_row_view(dx, row - groups, M, rb), true, c);
+                                                stream_row_view(dx, row - groups, M, rb, vb), true, c);
             }
             if (!more) return false;
             load(buf[KP], row + 2 * (int64_t)groups);
@@ -144,11 +146,11 @@ __global__ void __launch_bounds__(R)
         stream_rows<2>(
             (int64_t)group, M, groups, buf,
             [&](float *v, int64_t r) {
-                load_part<E, C, R, VEC>(stream_row_view(y, r, M, rb), chunk0, c.l, v);
-                load_part<E, C, R, VEC>(stream_row_view(dy, r, M, rb), chunk0, c.l, v + P);
+                load_part<E, C, R, VEC>(stream_row_view(y, r, M, rb, vb), chunk0, c.l, v);
+                load_part<E, C, R, VEC>(stream_row_view(dy, r, M, rb, vb), chunk0, c.l, v + P);
             },
             [&](float *v, int64_t r) {
-                softmax_bwd_finish<E, P, R, G, VEC>(v, v + P, stream_row_view(dx, r, M, rb), true,
+                softmax_bwd_finish<E, P, R, G, VEC>(v, v + P, stream_row_view(dx, r, M, rb, vb), true,
                                                     c);
                 ++c.it;
             });

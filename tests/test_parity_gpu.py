@@ -307,14 +307,15 @@ def test_grid_wait_timeout_is_reported_not_hung(N):
 
 
 OVERSUBSCRIBED = [  # (op, dtype, M, N): row groups forced to M, far more than fit at once
+    # Workgroups are bound to an XCD by block id (8 XCDs of 32 CUs), so a forced
+    # grid is sure to drain only when one XCD holds G of them at once: every case
+    # here has G <= 32 at one workgroup per CU (64 with two).
     ("softmax", "f32", 256, 200000),    # 8 workgroups per row, deferred exchange: 2048
     ("softmax", "bf16", 64, 1 << 20),   # 32 per row: 2048
     ("rmsnorm", "bf16", 256, 262144),   # packed, 4 per row: 1024 (one fits per CU)
-    ("rmsnorm", "f32", 96, 1 << 20),    # 64 per row: 6144
-    ("softmax", "f32", 64, 3_000_000),  # two-pass long rows, 32 per row: 2048
-    ("rmsnorm", "f32", 3, 3_000_000),   # 128 per row: 384, of which 256 fit at once
-    ("softmax", "f32", 4, 1 << 22),     # 128 per row: 512
-    ("softmax", "f32", 16, 5_000_000),  # two-pass long rows, 64 per row: 1024
+    ("rmsnorm", "f32", 96, 1 << 19),    # 32 per row: 3072
+    ("softmax", "f32", 64, 3_000_000),  # two-pass long rows, 32 per row: 2048 (two per CU)
+    ("softmax", "f32", 16, 5_000_000),  # two-pass long rows, 64 per row: 1024 (two per CU)
 ]
 
 
@@ -323,7 +324,8 @@ def test_split_rows_drain_when_the_grid_does_not_fit(op, dtype, M, N):
     """Workgroups that share a row wait for each other, and an ordinary launch does
     not promise that the whole grid runs at once.  Members are grouped by the order
     in which they start, so a grid several times larger than the device holds must
-    still drain, with every row right and the workspace left clean."""
+    still drain, with every row right and the workspace left clean, as long as one
+    XCD can hold a row's G workgroups at once."""
     code = {"softmax": rr.RR_OP_SOFTMAX, "rmsnorm": rr.RR_OP_RMSNORM}[op]
     dt = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
     assert rr.rr_plan_query(code, M, N, dt)["groups_per_row"] > 1

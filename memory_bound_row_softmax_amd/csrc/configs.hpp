@@ -38,7 +38,8 @@
     X(32, 1024, 1) X(32, 1024, 2) X(32, 1024, 4) X(32, 1024, 8) X(32, 1024, 16)             \
     X(64, 256, 1) X(64, 256, 2) X(64, 256, 4) X(64, 256, 8) X(64, 256, 16)                  \
     X(64, 512, 1) X(64, 512, 2) X(64, 512, 4) X(64, 512, 8) X(64, 512, 16)                  \
-    X(64, 512, 32) X(64, 512, 64) X(64, 512, 128)
+    X(64, 512, 32) X(64, 512, 64) X(64, 512, 128)                                           \
+    X(64, 512, 3) X(64, 512, 5) X(64, 512, 6)
 
 // Packed bf16 RMSNorm stream kernels (128-bit path only, see packed_bf16.hpp),
 // named by (R, G): each lane keeps kPackedP = 128 bf16 values as 64 VGPRs of raw
@@ -101,6 +102,12 @@ constexpr bool stream_config_enabled(int op, int elem_bytes, bool vec, int P, in
     if (!vec && P > 16) return false;
     // 128 workgroups per row (4194304 elements on chip): softmax and RMSNorm forward
     if (G > 64 && op != kCfgSoftmax && op != kCfgRmsnorm) return false;
+    // Workgroups per row that are not a power of two: bf16 softmax and cross-entropy
+    // gradient rows on 64 values x 512 lanes take exactly as many as the row needs
+    // (the planner), so that every register holds an element of the row.
+    if ((G & (G - 1)) != 0)
+        return vec && elem_bytes == 2 && P == 64 && R == 512 &&
+               (op == kCfgSoftmax || op == kCfgXentGrad);
     if (op == kCfgXentGrad && elem_bytes == 4 && P == 32 && R == 1024) return false;
     // softmax backward keeps two rows (y, dy) per buffer: about 4P + 40 VGPRs
     if (op == kCfgSoftmaxBwd) return vec ? (R == 1024 ? P <= 16 : P <= 32) : P <= 16;

@@ -151,6 +151,23 @@ static const Choice kTuned[4][2][kTunedBuckets] = {
       {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads}},
 };
 
+// bf16 softmax and cross-entropy gradient rows split over 64 values x 512 lanes take
+// exactly as many workgroups as the row needs when that is 3, 5 or 6 (compiled
+// besides the powers of two) instead of the next power of two.  A lane runs every
+// register through the exponential whether or not it holds an element, and at two
+// bytes per element that work shows.  Measured on MI355X (bf16 softmax, 16384 rows):
+// 151936 elements 5548 GB/s on 5 workgroups against 4105 on 8, 70000 5089 on 3
+// against 4129 on 4, 180000 5261 on 6 against 4713 on 8; the gradient at 70000 and
+// 90000 elements +25 % and +11 % on 3.  Seven lost to eight (4892 against 5119 at
+// 200000 elements), which defer the exchange (configs.hpp), so 7 is not compiled.
+static void exact_groups(int op, int dtype, bool vec, int64_t N, Plan *p) {
+    if (!p->stream || p->G <= 2 || dtype != kBf16 || !vec || p->P != 64 || p->R != 512 ||
+        (op != kOpSoftmax && op != kOpXentGrad))
+        return;
+    const int64_t need = (N + 64 * 512 - 1) / (64 * 512);
+    if (need < p->G && stream_config_ok(op, dtype, vec, 64, 512, (int)need)) p->G = (int)need;
+}
+
 static bool try_choice(int op, int dtype, bool vec, int64_t N, Choice c, Plan *p) {
     if (c.stream) {
         while (c.G > 1 && (int64_t)c.P * c.R * (c.G / 2) >= N) c.G /= 2;
@@ -197,7 +214,10 @@ static bool default_row(int op, int dtype, bool vec, int64_t M, int64_t N, Plan 
         // A stream workgroup that would be less than half full: the block
         // choice of the bucket below, widened to the row.
         if (c.stream && k > 0 && 2 * N < (int64_t)c.P * c.R) c = kTuned[o][d][k - 1];
-        if (try_choice(op, dtype, vec, N, c, p)) return true;
+        if (try_choice(op, dtype, vec, N, c, p)) {
+            exact_groups(op, dtype, vec, N, p);
+            return true;
+        }
         // a block choice the per-element path does not have: fewer values per lane
         for (Choice b = c; !b.stream && b.P > 8;) {
             b.P /= 2;

@@ -47,6 +47,17 @@ def test_xent_grad(M, N, dtype):
     parity_xent_grad(x, synth.labels(M, N), _dloss(M), dtype, f"xent grad {dtype} {M}x{N}")
 
 
+@pytest.mark.parametrize("N", [70000, 90000])
+def test_xent_grad_bf16_on_three_workgroups(N):
+    """bf16 rows of 65537 to 98304 elements: split over exactly 3 workgroups."""
+    M = 50
+    p = rr.rr_plan_query(rr.RR_OP_XENT_GRAD, 16384, N, rr.RR_BF16)
+    assert (p["path"], p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]) == (1, 64, 512, 3)
+    say("xent grad G=3", M, N)
+    x = synth.normal(M, N, sigma=2.0, dtype="bf16")
+    parity_xent_grad(x, synth.labels(M, N), _dloss(M), "bf16", f"xent grad bf16 G=3 {M}x{N}")
+
+
 FORCED = [("stream", 64, 256, 2, 300, 20000), ("stream", 32, 512, 16, 97, 70000),
           ("stream", 64, 512, 2, 50, 65536), ("stream", 64, 512, 16, 9, 500000),
           ("stream", 16, 1024, 1, 700, 16000), ("stream", 32, 512, 1, 3, 16384),

@@ -103,6 +103,22 @@ def test_forced_row_plans(kind, P, R, G, M, N, dtype):
     assert ran > 0
 
 
+EXACT_GROUPS = [(3, 70000), (5, 151936), (6, 180000)]
+
+
+@pytest.mark.parametrize("G,N", EXACT_GROUPS)
+def test_bf16_softmax_takes_exactly_the_workgroups_a_row_needs(G, N):
+    """bf16 rows on 64 values x 512 lanes are split over ceil(N / 32768) workgroups,
+    also when that is 3, 5 or 6, with 40 rows so that each row group has several."""
+    M = 40
+    p = rr.rr_plan_query(rr.RR_OP_SOFTMAX, 16384, N, rr.RR_BF16)
+    assert (p["path"], p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]) == (1, 64, 512, G)
+    say("softmax exact groups", G, M, N)
+    with forced(groups=2):  # two row groups: 20 rows each, every slot set reused
+        parity_softmax(_x(M, N, "bf16", sigma=2.0), "bf16", f"softmax bf16 G={G} {M}x{N}")
+    parity_softmax(_x(M, N, "bf16", sigma=2.0), "bf16", f"softmax bf16 G={G} {M}x{N}")
+
+
 PACKED = [  # (G, M, N): packed bf16 RMSNorm (128 values per lane on 512 lanes)
     (1, 300, 65536), (1, 700, 20000), (1, 3, 8), (2, 100, 131072), (2, 61, 65544),
     (4, 90, 200000), (8, 40, 524288), (16, 7, 1000000), (16, 5, 300000), (16, 33, 1 << 20),

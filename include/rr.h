@@ -33,10 +33,12 @@
  *    except for the dw partial rows of rr_rmsnorm_bwd (scratch that each call
  *    rewrites).
  *  - The workgroups that share a row wait for each other.  They are grouped in
- *    the order in which they start, so the launch completes whenever as many
- *    of them as share a row fit on the device at once; each wait is bounded,
- *    and a wait that gives up (for instance while other work holds the device)
- *    is reported by rr_workspace_check().
+ *    the order in which they start, and the grid is sized so that all of it
+ *    fits on an idle device at once.  When it does not all run at once (other
+ *    work holding the device), the launch still completes if one XCD can hold
+ *    as many of them as share a row (a workgroup runs on the XCD its block id
+ *    names).  Each wait is bounded, and a wait that gives up is reported by
+ *    rr_workspace_check().
  */
 #ifndef RR_H
 #define RR_H

@@ -298,6 +298,10 @@ __global__ void __launch_bounds__(R)
                 epis[K] = out.epi(buf[K] + P, row);
                 cur = softmax_local<E, P, R>(buf[K], c, epis[K]);
                 publish_pair<G>(c.g, c.member, c.it, cur.m, cur.s);
+            } else {
+                // no reduction (and its barriers) in this step: every wave has read
+                // the previous row's merged pair before wave 0 writes the next one
+                __syncthreads();
             }
             if (c.it > 0) {  // complete the previous row
                 wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeMaxSum{});
@@ -484,6 +488,8 @@ __global__ void __launch_bounds__(R)
                 if constexpr (VEC) widen_part<E, C>(buf[K]);
                 const float q = rmsnorm_local<E, P, R>(buf[K], c);
                 publish_pair<G>(c.g, c.member, c.it, q, 0.0f);
+            } else {
+                __syncthreads();  // as in the softmax kernel: the merged sum is read
             }
             if (c.it > 0) {  // complete the previous row
                 wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeSum{});

@@ -127,6 +127,8 @@ __global__ void __launch_bounds__(R)
                 }
                 const float t = softmax_bwd_local<E, P, R>(buf[K], buf[K] + P, c);
                 publish_pair<G>(c.g, c.member, c.it, t, 0.0f);
+            } else {
+                __syncthreads();  // as in the softmax kernel: the merged c is read
             }
             if (c.it > 0) {  // complete the previous row
                 wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeSum{});

@@ -292,7 +292,9 @@ def test_rmsnorm_bwd(M, N, dtype):
 
 RMS_FORCED = [(8, 16, 1, 300, 100), (8, 1024, 1, 40, 8000), (16, 64, 1, 777, 1000),
               (32, 128, 1, 65, 4000), (16, 512, 2, 300, 9000), (16, 512, 16, 5, 100000),
-              (32, 512, 2, 600, 20000), (32, 512, 8, 50, 131072), (32, 512, 16, 3, 200000)]
+              (32, 512, 2, 600, 20000), (32, 512, 8, 50, 131072), (32, 512, 16, 3, 200000),
+              # 8 and 16 workgroups per row with many rows per row group, ragged shares
+              (16, 512, 8, 300, 60000), (16, 512, 16, 100, 131072), (16, 512, 16, 77, 70001)]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)

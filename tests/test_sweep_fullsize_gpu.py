@@ -73,3 +73,60 @@ def test_sweep_point_at_full_size(w):
         for r0 in range(0, w.M, step):
             s = y[r0:r0 + step].double().sum(dim=1)
             assert float((s - 1.0).abs().max()) < (1e-4 if w.dtype == "f32" else 2e-2), r0
+
+
+# Rows whose length is not a power of two, at full size with the bench's plan: a
+# 151936-entry vocabulary (softmax) and 200000-wide rows (RMSNorm).  The members of
+# a split row hold equal shares (softmax fp32 on 8 workgroups, bf16 on exactly 5;
+# RMSNorm fp32 on 16, bf16 packed on 4).
+UNEVEN = [W.Workload("softmax_f32_16384x151936", "softmax", "f32", 16384, 151936),
+          W.Workload("softmax_bf16_16384x151936", "softmax", "bf16", 16384, 151936),
+          W.Workload("rmsnorm_f32_16384x200000", "rmsnorm", "f32", 16384, 200000),
+          W.Workload("rmsnorm_bf16_16384x200000", "rmsnorm", "bf16", 16384, 200000)]
+UNEVEN_G = {"softmax_f32": 8, "softmax_bf16": 5, "rmsnorm_f32": 16, "rmsnorm_bf16": 4}
+
+
+@pytest.mark.parametrize("w", UNEVEN, ids=lambda w: w.name)
+def test_uneven_rows_at_full_size(w):
+    code = rr.RR_F32 if w.dtype == "f32" else rr.RR_BF16
+    op = rr.RR_OP_SOFTMAX if w.op == "softmax" else rr.RR_OP_RMSNORM
+    p = rr.rr_plan_query(op, w.M, w.N, code)
+    assert p["path"] == 1 and p["groups_per_row"] == UNEVEN_G[f"{w.op}_{w.dtype}"], p
+    say("uneven full size", w.name)
+    x_np = W.x_rows(w, nrows=HOST_ROWS)
+    x = to_dev(x_np, w.dtype).repeat(w.M // HOST_ROWS, 1)
+    rows = _rows(w.M)
+    rows_t = torch.from_numpy(rows).to(DEV)
+    src = x_np[rows % HOST_ROWS]
+    ws = rr.workspace(op, w.M, w.N, code, DEV)
+    if w.op == "softmax":
+        y = rr.rr_softmax_fwd(x, ws=ws)
+        ref = oracle.softmax(src)
+    else:
+        w_np = W.weight(w)
+        y = rr.rr_rmsnorm_fwd(x, to_dev(w_np, w.dtype), w.eps, ws=ws)
+        ref = oracle.rmsnorm(src, w_np, w.eps)
+    torch.cuda.synchronize()
+    assert rr.rr_workspace_check(ws) == rr.RR_OK
+    assert int(ws.count_nonzero()) == 0
+    check_out(from_dev(y[rows_t]), ref, w.dtype, w.name)
+    # Every row against the oracle's result for its host row (rows repeat every
+    # HOST_ROWS), on the device: fp32 within 1e-5 relative, bf16 within one ulp.
+    if w.op == "softmax":
+        full = oracle.softmax(x_np)
+    else:
+        full = oracle.rmsnorm(x_np, w_np, w.eps)
+    ref_t = torch.from_numpy(np.ascontiguousarray(full, dtype=np.float64)).to(DEV)
+    if w.dtype == "f32":
+        tol = 1e-5 * ref_t.abs()
+    else:
+        expo = torch.floor(torch.log2(ref_t.abs().clamp_min(2.0 ** -126))).to(torch.int32)
+        tol = torch.ldexp(torch.ones_like(ref_t), expo - 7)
+    tol = torch.maximum(tol, torch.full_like(tol, 2.0 ** -126))
+    worst_rep = 0.0
+    for r0 in range(0, w.M, HOST_ROWS):
+        blk = y[r0:r0 + HOST_ROWS].double()
+        err = (blk - ref_t).abs()
+        assert bool((err <= tol).all()), (r0, float((err / tol).max()))
+        worst_rep = max(worst_rep, float((blk - y[:HOST_ROWS].double()).abs().max()))
+    say("largest difference between repeats of a row:", worst_rep)

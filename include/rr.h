@@ -158,7 +158,7 @@ rr_status rr_softmax_bwd(const void *y, const void *dy, void *dx, int64_t M, int
  * aliasing); any other overlap among x, dy, dx and dw is rejected.  The workspace
  * (RR_OP_RMSNORM_BWD) is always needed when M > 0; only its first part (the header
  * and, for split rows, the exchange area) must start zero-filled, as for the other
- * calls.  N up to 262144 (131072 when the rows are not 16-byte aligned).
+ * calls.  N up to 262144.
  */
 rr_status rr_rmsnorm_bwd(const void *x, const void *w, const void *dy, const float *rstd,
                          void *dx, float *dw, int64_t M, int64_t N, rr_dtype dt, void *ws,

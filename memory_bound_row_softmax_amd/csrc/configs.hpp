@@ -55,7 +55,7 @@ constexpr int kPackedP = 128;
     X(8, 16, 1) X(8, 32, 1) X(8, 64, 1) X(8, 128, 1) X(8, 256, 1) X(8, 512, 1) X(8, 1024, 1)  \
     X(16, 16, 1) X(16, 32, 1) X(16, 64, 1) X(16, 128, 1) X(16, 256, 1) X(16, 512, 1)          \
     X(32, 16, 1) X(32, 32, 1) X(32, 64, 1) X(32, 128, 1) X(32, 256, 1) X(32, 512, 1)          \
-    X(16, 512, 2) X(16, 512, 4) X(16, 512, 8) X(16, 512, 16)                                  \
+    X(16, 512, 2) X(16, 512, 4) X(16, 512, 8) X(16, 512, 16) X(16, 512, 32)                   \
     X(32, 512, 2) X(32, 512, 4) X(32, 512, 8) X(32, 512, 16)
 
 #define RR_XENT_CONFIGS(X)                                                                  \

@@ -289,7 +289,7 @@ static PlanResult plan_rmsnorm_bwd(int dtype, int64_t M, int64_t N, bool vec, Pl
         } else {
             while (G > 1 && (int64_t)P * R * (G / 2) >= N) G /= 2;
         }
-        while ((int64_t)P * R * G < N && G < 16) G *= 2;  // past the table
+        while ((int64_t)P * R * G < N && G < 32) G *= 2;  // past the table
     }
     if (!rmsbwd_config_ok(dtype, vec, P, R, G)) return kPlanUnsupported;
     Plan p;

@@ -316,7 +316,7 @@ def test_rmsnorm_bwd_in_place(inplace, dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("N", [64, 1000, 4096, 40000, 131072])
+@pytest.mark.parametrize("N", [64, 1000, 4096, 40000, 131072, 200001, 262144])
 def test_rmsnorm_bwd_unaligned(N, dtype):
     M = 6
     x_np, w_np, dy_np, r_np = rmsnorm_bwd_inputs(M, N, dtype)

@@ -184,7 +184,7 @@ def test_rmsnorm_bwd_plans(dt, vec):
     """Persistent kernels: one workgroup per row up to 16384 elements, then split;
     the workspace holds the exchange area and one fp32 partial row per row group."""
     for N in NS:
-        lim = 262144 if vec else 131072
+        lim = 262144
         if N > lim:
             with pytest.raises(rr.RRError):
                 rr.rr_plan_query(rr.RR_OP_RMSNORM_BWD, 16384, N, dt, vec)

@@ -411,7 +411,7 @@ def main() -> int:
                 except (ValueError, KeyError):
                     pass
         only = [t for t in args.only.split(",") if t]
-        for w in W.FIXED + W.sweep() + W.BACKWARD + W.WIDE + W.LONG:
+        for w in W.FIXED + W.sweep() + W.BACKWARD + W.WIDE + W.LONG + W.UNEVEN:
             if w.name in done or (only and not all(t in w.name for t in only)):
                 continue
             line = measure(w, args.steps, args.warmup, args.rotate_bytes, False, 0,

@@ -85,8 +85,16 @@ LONG = [Workload("softmax_f32_128x8388608", "softmax", "f32", 128, 1 << 23),
         Workload("rmsnorm_bf16_256x8388608", "rmsnorm", "bf16", 256, 1 << 23)]
 
 
+# Rows whose length is not a power of two: a 151936-entry vocabulary (softmax) and
+# 200000-wide rows (RMSNorm), split into equal shares.
+UNEVEN = [Workload("softmax_f32_16384x151936", "softmax", "f32", 16384, 151936),
+          Workload("softmax_bf16_16384x151936", "softmax", "bf16", 16384, 151936),
+          Workload("rmsnorm_f32_16384x200000", "rmsnorm", "f32", 16384, 200000),
+          Workload("rmsnorm_bf16_16384x200000", "rmsnorm", "bf16", 16384, 200000)]
+
+
 def by_name(name: str) -> Workload:
-    for w in FIXED + BACKWARD + WIDE + LONG + sweep():
+    for w in FIXED + BACKWARD + WIDE + LONG + UNEVEN + sweep():
         if w.name == name:
             return w
     raise KeyError(name)

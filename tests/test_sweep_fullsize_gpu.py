@@ -79,10 +79,7 @@ def test_sweep_point_at_full_size(w):
 # 151936-entry vocabulary (softmax) and 200000-wide rows (RMSNorm).  The members of
 # a split row hold equal shares (softmax fp32 on 8 workgroups, bf16 on exactly 5;
 # RMSNorm fp32 on 16, bf16 packed on 4).
-UNEVEN = [W.Workload("softmax_f32_16384x151936", "softmax", "f32", 16384, 151936),
-          W.Workload("softmax_bf16_16384x151936", "softmax", "bf16", 16384, 151936),
-          W.Workload("rmsnorm_f32_16384x200000", "rmsnorm", "f32", 16384, 200000),
-          W.Workload("rmsnorm_bf16_16384x200000", "rmsnorm", "bf16", 16384, 200000)]
+UNEVEN = W.UNEVEN
 UNEVEN_G = {"softmax_f32": 8, "softmax_bf16": 5, "rmsnorm_f32": 16, "rmsnorm_bf16": 4}
 
 

@@ -112,42 +112,43 @@ struct Choice {
     bool stream;
     int P, R, G;
 };
-constexpr int kTunedBuckets = 12;
-constexpr int64_t kTunedN[kTunedBuckets] = {256,    1024,   4096,   16384,   32768,  65536,
-                                            131072, 262144, 524288, 1048576, 2097152,
-                                            4194304};
+constexpr int kTunedBuckets = 13;
+constexpr int64_t kTunedN[kTunedBuckets] = {256,    1024,   4096,   8192,    16384,   32768,  65536,
+                                            131072, 262144, 524288, 1048576, 2097152, 4194304};
 // A choice with P = 0: no on-chip plan (softmax and RMSNorm then read the row twice).
 constexpr Choice kTwoReads = {false, 0, 0, 0};
 //   [op: softmax, rmsnorm, softmax backward, cross-entropy gradient][dtype: f32, bf16][N bucket]
-// (the four longest buckets were timed at 4096, 2048, 512-1024 and 256-512 rows)
+// (the four longest buckets were timed at 4096, 2048, 512-1024 and 256-512 rows; the
+// 8192 bucket was added later: the interpolated plans ran 3-37 % slower there)
 static const Choice kTuned[4][2][kTunedBuckets] = {
-    {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {true, 64, 512, 1},
+    {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 64, 128, 1},
+      {true, 64, 512, 1},
       {true, 16, 1024, 2}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8},
       {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, {true, 64, 512, 128}},
-     {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 16, 256, 1}, {false, 64, 256, 1},
-      {true, 32, 1024, 1}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8},
+     {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 16, 256, 1}, {false, 16, 512, 1},
+      {false, 64, 256, 1}, {true, 32, 1024, 1}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8},
       {true, 64, 512, 16}, {true, 64, 512, 32}, kTwoReads, kTwoReads}},
-    {{{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 16, 1024, 1},
-      {true, 16, 1024, 2}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 32, 512, 16},
+    {{{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 64, 128, 1},
+      {false, 16, 1024, 1}, {true, 16, 1024, 2}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 32, 512, 16},
       {true, 32, 512, 32}, {true, 32, 512, 64}, {true, 64, 512, 64}, {true, 64, 512, 128}},
-     {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {true, 32, 1024, 1},
-      {false, 64, 512, 1}, {true, 32, 1024, 2}, {true, 64, 512, 4}, {true, kPackedP, 512, 4},
+     {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 16, 512, 1},
+      {true, 32, 1024, 1}, {false, 64, 512, 1}, {true, 32, 1024, 2}, {true, 64, 512, 4}, {true, kPackedP, 512, 4},
       {true, kPackedP, 512, 8}, {true, kPackedP, 512, 16}, {true, kPackedP, 512, 32},
       {true, kPackedP, 512, 64}}},
     // softmax backward (y and dy both held: at most 32 values per lane in a stream kernel)
-    {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 16, 256, 1}, {false, 32, 1024, 1},
-      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
+    {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 16, 256, 1}, {false, 32, 256, 1},
+      {false, 32, 1024, 1}, {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
       {true, 32, 512, 32}, {true, 32, 512, 64}, kTwoReads, kTwoReads},
-     {{false, 8, 32, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 16, 1024, 1},
-      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
+     {{false, 8, 32, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 16, 512, 1},
+      {false, 16, 1024, 1}, {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
       {true, 32, 512, 32}, {true, 32, 512, 64}, kTwoReads, kTwoReads}},
     // cross-entropy forward fused with its gradient (the softmax kernels; block kernels
     // hold longer rows here than for the softmax)
-    {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {true, 16, 1024, 1},
-      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 64, 512, 8},
+    {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 32, 256, 1},
+      {true, 16, 1024, 1}, {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 64, 512, 8},
       {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads},
-     {{false, 16, 16, 1}, {false, 64, 16, 1}, {false, 16, 256, 1}, {false, 32, 512, 1},
-      {false, 64, 512, 1}, {false, 64, 1024, 1}, {true, 64, 512, 4}, {true, 32, 1024, 8},
+     {{false, 16, 16, 1}, {false, 64, 16, 1}, {false, 16, 256, 1}, {false, 32, 256, 1},
+      {false, 32, 512, 1}, {false, 64, 512, 1}, {false, 64, 1024, 1}, {true, 64, 512, 4}, {true, 32, 1024, 8},
       {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads}},
 };
 
@@ -258,6 +259,7 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 struct BwdChoice {
     int P, R, G;
 };
+constexpr int64_t kTunedBwdN[8] = {256, 1024, 4096, 16384, 32768, 65536, 131072, 262144};
 static const BwdChoice kTunedRmsBwd[2][8] = {
     {{8, 32, 1}, {16, 64, 1}, {16, 256, 1}, {16, 512, 2}, {16, 512, 4}, {32, 512, 4},
      {32, 512, 8}, {32, 512, 16}},
@@ -274,7 +276,7 @@ static PlanResult plan_rmsnorm_bwd(int dtype, int64_t M, int64_t N, bool vec, Pl
         G = fG ? fG : 1;
     } else {
         int k = 0;
-        while (k < 7 && kTunedN[k] < N) ++k;
+        while (k < 7 && kTunedBwdN[k] < N) ++k;
         BwdChoice c = kTunedRmsBwd[dtype == kBf16 ? 1 : 0][k];
         if (!vec && c.P > 16) {  // the per-element path keeps P <= 16: twice the lanes
             c.P = 16;

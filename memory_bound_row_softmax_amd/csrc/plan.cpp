@@ -112,43 +112,53 @@ struct Choice {
     bool stream;
     int P, R, G;
 };
-constexpr int kTunedBuckets = 13;
-constexpr int64_t kTunedN[kTunedBuckets] = {256,    1024,   4096,   8192,    16384,   32768,  65536,
-                                            131072, 262144, 524288, 1048576, 2097152, 4194304};
+constexpr int kTunedBuckets = 16;
+constexpr int64_t kTunedN[kTunedBuckets] = {256,    1024,   4096,    5120,    6144,    8192,
+                                            12288,  16384,  32768,   65536,   131072,  262144,
+                                            524288, 1048576, 2097152, 4194304};
 // A choice with P = 0: no on-chip plan (softmax and RMSNorm then read the row twice).
 constexpr Choice kTwoReads = {false, 0, 0, 0};
 //   [op: softmax, rmsnorm, softmax backward, cross-entropy gradient][dtype: f32, bf16][N bucket]
 // (the four longest buckets were timed at 4096, 2048, 512-1024 and 256-512 rows; the
-// 8192 bucket was added later: the interpolated plans ran 3-37 % slower there)
+// 5120, 6144, 8192 and 12288 buckets were added later, where the plans interpolated
+// from their neighbours ran 3-37 % slower; at 5120, 6144 and 12288 the softmax and
+// RMSNorm were timed, at 12288 also the fp32 cross-entropy gradient, and the other
+// entries there are the ones those lengths used before)
 static const Choice kTuned[4][2][kTunedBuckets] = {
-    {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 64, 128, 1},
-      {true, 64, 512, 1},
+    {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 32, 256, 1},
+      {false, 32, 256, 1}, {false, 64, 128, 1}, {false, 64, 256, 1}, {true, 64, 512, 1},
       {true, 16, 1024, 2}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8},
       {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, {true, 64, 512, 128}},
-     {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 16, 256, 1}, {false, 16, 512, 1},
-      {false, 64, 256, 1}, {true, 32, 1024, 1}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8},
+     {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 16, 256, 1}, {false, 32, 256, 1},
+      {false, 32, 256, 1}, {false, 16, 512, 1}, {false, 64, 256, 1}, {false, 64, 256, 1},
+      {true, 32, 1024, 1}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8},
       {true, 64, 512, 16}, {true, 64, 512, 32}, kTwoReads, kTwoReads}},
-    {{{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 64, 128, 1},
-      {false, 16, 1024, 1}, {true, 16, 1024, 2}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 32, 512, 16},
+    {{{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 16, 512, 1},
+      {false, 32, 256, 1}, {false, 64, 128, 1}, {false, 16, 1024, 1}, {false, 16, 1024, 1},
+      {true, 16, 1024, 2}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 32, 512, 16},
       {true, 32, 512, 32}, {true, 32, 512, 64}, {true, 64, 512, 64}, {true, 64, 512, 128}},
-     {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 16, 512, 1},
-      {true, 32, 1024, 1}, {false, 64, 512, 1}, {true, 32, 1024, 2}, {true, 64, 512, 4}, {true, kPackedP, 512, 4},
-      {true, kPackedP, 512, 8}, {true, kPackedP, 512, 16}, {true, kPackedP, 512, 32},
-      {true, kPackedP, 512, 64}}},
+     {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 32, 256, 1},
+      {false, 32, 256, 1}, {false, 16, 512, 1}, {false, 64, 256, 1}, {true, 32, 1024, 1},
+      {false, 64, 512, 1}, {true, 32, 1024, 2}, {true, 64, 512, 4}, {true, kPackedP, 512, 4},
+      {true, kPackedP, 512, 8}, {true, kPackedP, 512, 16}, {true, kPackedP, 512, 32}, {true, kPackedP, 512, 64}}},
     // softmax backward (y and dy both held: at most 32 values per lane in a stream kernel)
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 16, 256, 1}, {false, 32, 256, 1},
-      {false, 32, 1024, 1}, {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
+      {false, 32, 256, 1}, {false, 32, 256, 1}, {false, 32, 1024, 1}, {false, 32, 1024, 1},
+      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
       {true, 32, 512, 32}, {true, 32, 512, 64}, kTwoReads, kTwoReads},
      {{false, 8, 32, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 16, 512, 1},
-      {false, 16, 1024, 1}, {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
+      {false, 16, 512, 1}, {false, 16, 512, 1}, {false, 16, 1024, 1}, {false, 16, 1024, 1},
+      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
       {true, 32, 512, 32}, {true, 32, 512, 64}, kTwoReads, kTwoReads}},
     // cross-entropy forward fused with its gradient (the softmax kernels; block kernels
     // hold longer rows here than for the softmax)
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 32, 256, 1},
-      {true, 16, 1024, 1}, {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 64, 512, 8},
+      {false, 32, 256, 1}, {false, 32, 256, 1}, {false, 16, 1024, 1}, {true, 16, 1024, 1},
+      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 64, 512, 8},
       {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads},
      {{false, 16, 16, 1}, {false, 64, 16, 1}, {false, 16, 256, 1}, {false, 32, 256, 1},
-      {false, 32, 512, 1}, {false, 64, 512, 1}, {false, 64, 1024, 1}, {true, 64, 512, 4}, {true, 32, 1024, 8},
+      {false, 32, 256, 1}, {false, 32, 256, 1}, {false, 32, 512, 1}, {false, 32, 512, 1},
+      {false, 64, 512, 1}, {false, 64, 1024, 1}, {true, 64, 512, 4}, {true, 32, 1024, 8},
       {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads}},
 };
 

@@ -23,7 +23,9 @@
  *  - M == 0 is a no-op returning RR_OK.
  *  - 16-byte aligned pointers with (N * element size) % 16 == 0 take the
  *    vectorised path (128-bit loads and stores); anything else takes a
- *    per-element path that gives the same results more slowly.
+ *    per-element path that gives the same results more slowly (it still moves
+ *    whole 16-byte chunks at element-aligned addresses, and only each row's last
+ *    partial chunk element by element).
  *  - `ws` is a workspace that only rows split over several workgroups need:
  *    when rr_workspace_bytes(...) returns 0 it may be NULL.  Otherwise it
  *    must hold at least that many bytes, be 16-byte aligned, be zero-filled

@@ -155,7 +155,7 @@ __global__ void __launch_bounds__(R)
             [&](float *v, int t) {
                 load_part<E, C, R, VEC>(xv, t * C * R, l, v);
                 if constexpr (OP == kLongRmsnorm)
-                    load_part<E, C, R, VEC, kReuseLoad>(RowView{wb, 0u}, t * C * R, l, v + P);
+                    load_part<E, C, R, VEC, kReuseLoad>(RowView{wb, 0u, rb}, t * C * R, l, v + P);
             },
             [&](float *v, int t) {
                 const int chunk0 = t * C * R;

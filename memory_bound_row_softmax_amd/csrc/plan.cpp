@@ -122,7 +122,7 @@ constexpr Choice kTwoReads = {false, 0, 0, 0};
 // (the four longest buckets were timed at 4096, 2048, 512-1024 and 256-512 rows; the
 // 5120, 6144, 8192 and 12288 buckets were added later, where the plans interpolated
 // from their neighbours ran 3-37 % slower; at 5120, 6144 and 12288 the softmax and
-// RMSNorm were timed, at 12288 also the fp32 cross-entropy gradient, and the other
+// RMSNorm were timed, at 12288 also the cross-entropy gradient, and the other
 // entries there are the ones those lengths used before)
 static const Choice kTuned[4][2][kTunedBuckets] = {
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 32, 256, 1},
@@ -157,7 +157,7 @@ static const Choice kTuned[4][2][kTunedBuckets] = {
       {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 64, 512, 8},
       {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads},
      {{false, 16, 16, 1}, {false, 64, 16, 1}, {false, 16, 256, 1}, {false, 32, 256, 1},
-      {false, 32, 256, 1}, {false, 32, 256, 1}, {false, 32, 512, 1}, {false, 32, 512, 1},
+      {false, 32, 256, 1}, {false, 32, 256, 1}, {false, 64, 256, 1}, {false, 32, 512, 1},
       {false, 64, 512, 1}, {false, 64, 1024, 1}, {true, 64, 512, 4}, {true, 32, 1024, 8},
       {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads}},
 };
@@ -269,12 +269,19 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 struct BwdChoice {
     int P, R, G;
 };
-constexpr int64_t kTunedBwdN[8] = {256, 1024, 4096, 16384, 32768, 65536, 131072, 262144};
-static const BwdChoice kTunedRmsBwd[2][8] = {
-    {{8, 32, 1}, {16, 64, 1}, {16, 256, 1}, {16, 512, 2}, {16, 512, 4}, {32, 512, 4},
-     {32, 512, 8}, {32, 512, 16}},
-    {{16, 16, 1}, {16, 64, 1}, {32, 128, 1}, {32, 512, 1}, {32, 512, 2}, {32, 512, 4},
-     {32, 512, 8}, {32, 512, 16}},
+// (the 5120, 8192 and 12288 buckets were added later, where the plans interpolated
+// from their neighbours ran up to 23 % slower: bf16 at 5120 elements 3958 -> 4881 GB/s,
+// fp32 at 12288 5379 -> 5753)
+constexpr int kTunedBwdBuckets = 11;
+constexpr int64_t kTunedBwdN[kTunedBwdBuckets] = {256,   1024,  4096,  5120,   8192,  12288,
+                                                  16384, 32768, 65536, 131072, 262144};
+constexpr bool kBwdAlignedOnly[kTunedBwdBuckets] = {false, false, false, true,  true, true,
+                                                    false, false, false, false, false};
+static const BwdChoice kTunedRmsBwd[2][kTunedBwdBuckets] = {
+    {{8, 32, 1}, {16, 64, 1}, {16, 256, 1}, {32, 256, 1}, {16, 512, 1}, {32, 512, 1},
+     {16, 512, 2}, {16, 512, 4}, {32, 512, 4}, {32, 512, 8}, {32, 512, 16}},
+    {{16, 16, 1}, {16, 64, 1}, {32, 128, 1}, {8, 1024, 1}, {16, 512, 1}, {32, 512, 1},
+     {32, 512, 1}, {32, 512, 2}, {32, 512, 4}, {32, 512, 8}, {32, 512, 16}},
 };
 
 static PlanResult plan_rmsnorm_bwd(int dtype, int64_t M, int64_t N, bool vec, Plan *out) {
@@ -286,7 +293,10 @@ static PlanResult plan_rmsnorm_bwd(int dtype, int64_t M, int64_t N, bool vec, Pl
         G = fG ? fG : 1;
     } else {
         int k = 0;
-        while (k < 7 && kTunedBwdN[k] < N) ++k;
+        // The 5120, 8192 and 12288 buckets were measured on the 128-bit path only;
+        // rows on the per-element path keep the plans of the buckets around them.
+        while (k < kTunedBwdBuckets - 1 && (kTunedBwdN[k] < N || (!vec && kBwdAlignedOnly[k])))
+            ++k;
         BwdChoice c = kTunedRmsBwd[dtype == kBf16 ? 1 : 0][k];
         if (!vec && c.P > 16) {  // the per-element path keeps P <= 16: twice the lanes
             c.P = 16;

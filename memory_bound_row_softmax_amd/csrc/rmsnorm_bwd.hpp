@@ -42,17 +42,19 @@ __device__ __forceinline__ RowView rows_view(const char *base, int64_t M, int64_
                                              uint32_t row_bytes, uint32_t span_bytes) {
     constexpr int RPB = rows_per_block_for(R);
     const int64_t first = blk * RPB;
-    if (first >= M) return {make_buf(base, 0u), 0u};
+    if (first >= M) return {make_buf(base, 0u), 0u, 0u};
     if constexpr (R >= 64) {
         // one row per workgroup: the buffer ends with this member's part (member_span)
-        if constexpr (RPB == 1) return {make_buf(base + first * row_bytes, span_bytes), 0u};
+        if constexpr (RPB == 1)
+            return {make_buf(base + first * row_bytes, span_bytes), 0u, span_bytes};
         int64_t row = first + sub;
         const bool ok = row < M;
-        return {make_buf(base + (ok ? row : 0) * row_bytes, ok ? row_bytes : 0u), 0u};
+        return {make_buf(base + (ok ? row : 0) * row_bytes, ok ? row_bytes : 0u), 0u, row_bytes};
     } else {
         const int64_t left = M - first;
         const uint32_t nrows = (uint32_t)(left < RPB ? left : RPB);
-        return {make_buf(base + first * row_bytes, nrows * row_bytes), (uint32_t)sub * row_bytes};
+        return {make_buf(base + first * row_bytes, nrows * row_bytes), (uint32_t)sub * row_bytes,
+                (uint32_t)(sub + 1) * row_bytes};
     }
 }
 
@@ -144,7 +146,7 @@ __global__ void __launch_bounds__(bwd_threads(R, G))
     __shared__ float4 wslot[(P / 4) * R];
     if (sub == 0) {
         float t[P];
-        load_part<E, C, R, VEC, kReuseLoad>(RowView{make_buf(w, rb), 0u}, chunk0, l, t);
+        load_part<E, C, R, VEC, kReuseLoad>(RowView{make_buf(w, rb), 0u, rb}, chunk0, l, t);
 #pragma unroll
         for (int q = 0; q < P / 4; ++q)
             wslot[q * R + l] = make_float4(t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]);

@@ -49,11 +49,12 @@ __device__ __forceinline__ RowView block_row_view(const char *base, int64_t M, i
     if constexpr (R >= 64) {
         int64_t row = first + sub;
         if (row >= M) row = M - 1;
-        return {make_buf(base + row * row_bytes, row_bytes), 0u};
+        return {make_buf(base + row * row_bytes, row_bytes), 0u, row_bytes};
     } else {
         const int64_t left = M - first;
         const uint32_t nrows = (uint32_t)(left < RPB ? left : RPB);
-        return {make_buf(base + first * row_bytes, nrows * row_bytes), (uint32_t)sub * row_bytes};
+        return {make_buf(base + first * row_bytes, nrows * row_bytes), (uint32_t)sub * row_bytes,
+                (uint32_t)(sub + 1) * row_bytes};
     }
 }
 
@@ -62,7 +63,7 @@ __device__ __forceinline__ RowView block_row_view(const char *base, int64_t M, i
 __device__ __forceinline__ RowView stream_row_view(const char *base, int64_t row, int64_t M,
                                                    uint32_t row_bytes) {
     const bool ok = row < M;
-    return {make_buf(base + (ok ? row : 0) * row_bytes, ok ? row_bytes : 0u), 0u};
+    return {make_buf(base + (ok ? row : 0) * row_bytes, ok ? row_bytes : 0u), 0u, row_bytes};
 }
 
 // The same, with the buffer ending `span_bytes` into the row (the end of a split
@@ -70,7 +71,7 @@ __device__ __forceinline__ RowView stream_row_view(const char *base, int64_t row
 __device__ __forceinline__ RowView stream_row_view(const char *base, int64_t row, int64_t M,
                                                    uint32_t row_bytes, uint32_t span_bytes) {
     const bool ok = row < M;
-    return {make_buf(base + (ok ? row : 0) * row_bytes, ok ? span_bytes : 0u), 0u};
+    return {make_buf(base + (ok ? row : 0) * row_bytes, ok ? span_bytes : 0u), 0u, span_bytes};
 }
 
 // Row loop of the stream kernels with D register buffers.  Rows group,
@@ -430,7 +431,7 @@ __global__ void __launch_bounds__(block_threads_for(R))
     float v[P];
     load_part<E, C, R, VEC>(block_row_view<R>(x, M, sub, row_bytes), 0, c.l, v);
     float wv[P];
-    load_part<E, C, R, VEC, kReuseLoad>(RowView{make_buf(w, row_bytes), 0u}, 0, c.l, wv);
+    load_part<E, C, R, VEC, kReuseLoad>(RowView{make_buf(w, row_bytes), 0u, row_bytes}, 0, c.l, wv);
     rmsnorm_finish<E, P, R, 1, VEC>(v, WeightRegs<P>{wv}, block_row_view<R>(y, M, sub, row_bytes),
                                     rstd ? rstd + row : nullptr, eps, valid, c);
 }
@@ -462,7 +463,7 @@ __global__ void __launch_bounds__(R)
     // slots it wrote, so no barrier is needed.
     {
         float t[P];
-        load_part<E, C, R, VEC, kReuseLoad>(RowView{make_buf(w, rb), 0u}, chunk0, c.l, t);
+        load_part<E, C, R, VEC, kReuseLoad>(RowView{make_buf(w, rb), 0u, rb}, chunk0, c.l, t);
 #pragma unroll
         for (int q = 0; q < P / 4; ++q)
             wslot[q * R + c.l] = make_float4(t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]);

@@ -314,6 +314,7 @@ static PlanResult plan_rmsnorm_bwd(int dtype, int64_t M, int64_t N, bool vec, Pl
         while ((int64_t)P * R * G < N && G < 32) G *= 2;  // past the table
     }
     if (!rmsbwd_config_ok(dtype, vec, P, R, G)) return kPlanUnsupported;
+    if (!vec && R >= 64 && dtype == kBf16 && N < 8) return kPlanUnsupported;
     Plan p;
     p.vec = vec;
     p.stream = true;
@@ -382,6 +383,7 @@ PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *ou
                                    !default_row(op, dtype, vec, M, N, &p)))) {
         // past every on-chip plan: read the row twice
         if (N > kLongMaxN) return kPlanUnsupported;
+        if (!vec && dtype == kBf16 && N < 8) return kPlanUnsupported;  // see below
         p = Plan{};
         p.vec = vec;
         p.stream = true;
@@ -410,6 +412,9 @@ PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *ou
     const int P = p.P, R = p.R, G = p.G;
     p.max_n = (int64_t)P * R * G;
     if (N > p.max_n) return kPlanUnsupported;
+    // Unaligned bf16 rows shorter than 16 bytes are read element by element, which
+    // only lane groups of fewer than 64 lanes compile.
+    if (!vec && R >= 64 && dtype == kBf16 && N < 8) return kPlanUnsupported;
     p.path = !p.stream ? kPathRow : (G > 1 ? kPathSplit : kPathStream);
     p.ws_bytes = G > 1 ? grid_ws_bytes(G, M) : 0;
     if (p.stream) {

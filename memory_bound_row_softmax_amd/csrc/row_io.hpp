@@ -3,7 +3,9 @@
 // Lane l of a group of R lanes owns chunks chunk0 + i * R + l for i = 0..C-1
 // (chunk = 16 bytes).  For a fixed i the R lanes touch R consecutive chunks, so
 // each load instruction of a wave covers contiguous memory (1 KiB when R >= 64).
-// All C loads are issued before any value is used and none sits behind a branch.
+// All C loads are issued before any value is used and none sits behind a branch
+// (except on the per-element path of unaligned fp32 rows, whose values need no
+// conversion after the load).
 //
 // A RowView is a buffer resource plus the byte offset of the row inside it: one
 // row per resource when a row has at least one whole wave (the resource is then
@@ -61,6 +63,21 @@ __device__ __forceinline__ void member_span(int member, int N, int *chunk0, int 
     }
 }
 
+// A buffer offset past every resource: loads there return 0 and touch no memory.
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+
+// The 16 bytes of `c` moved down by `s` bytes (s < 16), zeros shifted in at the
+// top: byte j of the result is byte j + s of c.  Written as one 128-bit shift,
+// which the backend expands into shifts and selects; a select in the source whose
+// operand is a loaded value would be turned into a branch around that use, and the
+// wait for the load would then sit inside the branch.
+__device__ __forceinline__ u32x4 shift_down_bytes(u32x4 c, uint32_t s) {
+    using u128 = unsigned __int128;
+    const u128 w = ((u128)c[0] | ((u128)c[1] << 32) | ((u128)c[2] << 64) | ((u128)c[3] << 96)) >>
+                   (8u * s);
+    return u32x4{(uint32_t)w, (uint32_t)(w >> 32), (uint32_t)(w >> 64), (uint32_t)(w >> 96)};
+}
+
 // POLICY: kStreamLoad for data read once, kReuseLoad for data read by every row.
 template <class E, int C, int R, bool VEC, int POLICY = kStreamLoad>
 __device__ __forceinline__ void load_part(RowView rv, int chunk0, int l, float *v) {
@@ -72,11 +89,12 @@ __device__ __forceinline__ void load_part(RowView rv, int chunk0, int l, float *
             raw[i] = buf_load16<POLICY>(rv.buf, rv.base + (uint32_t)(chunk0 + i * R + l) * 16u);
 #pragma unroll
         for (int i = 0; i < C; ++i) decode<E>(raw[i], v + i * VPC);
-    } else {
-        // Rows that are not 16-byte aligned: a chunk that lies wholly inside the row
-        // is still one 16-byte load (buffer instructions take element-aligned
-        // offsets on gfx950; measured at 93-95 % of the aligned rate), and only the
-        // chunk that holds the row's end is read element by element.
+    } else if constexpr (E::BYTES == 4) {
+        // fp32 rows that are not 16-byte aligned: a chunk that lies wholly inside the
+        // row is one 16-byte load at an element-aligned offset (buffer instructions
+        // take those on gfx950; measured at 93-95 % of the aligned rate), and the
+        // chunk that holds the row's end is read element by element.  The branch
+        // costs nothing here, since an fp32 chunk needs no conversion after the load.
 #pragma unroll
         for (int i = 0; i < C; ++i) {
             const uint32_t first = (uint32_t)(chunk0 + i * R + l) * VPC;
@@ -88,6 +106,42 @@ __device__ __forceinline__ void load_part(RowView rv, int chunk0, int l, float *
                 for (int e = 0; e < VPC; ++e)
                     v[i * VPC + e] = buf_load_elem<E, POLICY>(rv.buf, byte0 + e * E::BYTES);
             }
+        }
+    } else if (R >= 64 || __builtin_amdgcn_readfirstlane(rv.end - rv.base) >= 16u) {
+        // bf16 rows that are not 16-byte aligned.  Widening bf16 to fp32 is ALU work
+        // on the loaded words; behind a per-lane branch it would make the wave wait
+        // for the load inside the branch, before the next loads are issued.  So each
+        // chunk is one 16-byte load at an element-aligned offset with no branch: the
+        // range check zeroes every dword that crosses the end of a resource, so the
+        // chunk that holds the row's end reads the 16 bytes that end at `end`, and
+        // its elements are shifted into place after the load; chunks wholly past the
+        // end read 0.  The loads of a part then stay in flight together, as in the
+        // aligned path.  This needs rows of at least 16 bytes: plans with whole waves
+        // per row (R >= 64) are only made for those, and smaller lane groups test it
+        // (end - base is one row there, the same in every lane).
+        u32x4 raw[C];
+        uint32_t sh[C];
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const uint32_t first = (uint32_t)(chunk0 + i * R + l) * VPC;
+            const uint32_t byte0 = rv.base + first * E::BYTES;
+            const bool past = byte0 >= rv.end;
+            const bool tail = byte0 + 16u > rv.end;
+            const uint32_t off = past ? kOutOfRange : (tail ? rv.end - 16u : byte0);
+            sh[i] = (tail && !past) ? byte0 - off : 0u;
+            raw[i] = buf_load16<POLICY>(rv.buf, off);
+        }
+#pragma unroll
+        for (int i = 0; i < C; ++i) decode<E>(shift_down_bytes(raw[i], sh[i]), v + i * VPC);
+    } else {
+        // bf16 rows shorter than 16 bytes: element by element
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const uint32_t first = (uint32_t)(chunk0 + i * R + l) * VPC;
+            const uint32_t byte0 = rv.base + first * E::BYTES;
+#pragma unroll
+            for (int e = 0; e < VPC; ++e)
+                v[i * VPC + e] = buf_load_elem<E, POLICY>(rv.buf, byte0 + e * E::BYTES);
         }
     }
 }

@@ -423,7 +423,7 @@ def test_rows_split_over_many_workgroups(M, N, dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("M,N", [(7, 1000), (33, 40000), (5, 16 * 16384 + 5), (70, 3)])
+@pytest.mark.parametrize("M,N", [(7, 1000), (33, 40000), (5, 16 * 16384 + 5), (70, 9)])
 def test_long_row_kernel_forced_at_short_rows(M, N, dtype):
     """Tiles that do not fill a row group (members with no tile at all), ragged tails."""
     with forced(kind="long"):

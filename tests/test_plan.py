@@ -160,6 +160,30 @@ def test_forced_configurations(monkeypatch):
     assert (p["vals_per_lane"], p["lanes_per_row"]) == (16, 64)
 
 
+def test_short_unaligned_rows_take_small_lane_groups(monkeypatch):
+    """Unaligned bf16 rows shorter than 16 bytes are read element by element, which
+    only lane groups of fewer than 64 lanes compile: default plans use those (for
+    fp32 too), and forced bf16 plans with whole waves per row are refused."""
+    ops = (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM, rr.RR_OP_XENT, rr.RR_OP_XENT_GRAD,
+           rr.RR_OP_SOFTMAX_BWD, rr.RR_OP_RMSNORM_BWD)
+    for dt, size in ((rr.RR_F32, 4), (rr.RR_BF16, 2)):
+        for N in range(1, 16 // size):
+            for op in ops:
+                p = rr.rr_plan_query(op, 100, N, dt, False)
+                assert p["lanes_per_row"] < 64, (op, N, dt, p)
+    monkeypatch.setenv("RR_FORCE_KIND", "long")
+    with pytest.raises(rr.RRError):
+        rr.rr_plan_query(rr.RR_OP_SOFTMAX, 70, 7, rr.RR_BF16, False)
+    assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 70, 9, rr.RR_BF16, False)["path"] == 4
+    assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 70, 3, rr.RR_F32, False)["path"] == 4
+    monkeypatch.setenv("RR_FORCE_KIND", "stream")
+    monkeypatch.setenv("RR_FORCE_P", "16")
+    monkeypatch.setenv("RR_FORCE_R", "1024")
+    with pytest.raises(rr.RRError):
+        rr.rr_plan_query(rr.RR_OP_RMSNORM, 70, 7, rr.RR_BF16, False)
+    assert rr.rr_plan_query(rr.RR_OP_RMSNORM, 70, 9, rr.RR_BF16, False)["lanes_per_row"] == 1024
+
+
 def test_invalid_plan_arguments():
     for args in ((rr.RR_OP_SOFTMAX, -1, 10, rr.RR_F32), (rr.RR_OP_SOFTMAX, 4, 0, rr.RR_F32),
                  (7, 4, 10, rr.RR_F32), (rr.RR_OP_SOFTMAX, 4, 10, 3),

@@ -94,12 +94,17 @@ constexpr bool block_config_enabled(int op, int elem_bytes, bool vec, int P, int
 // Stream kernels hold two rows' worth of values per lane (about 2P + 40 VGPRs;
 // RMSNorm about 3P + 30, its weight slice coming back from LDS); the weight slice
 // of a workgroup lives in LDS as fp32 (4 * P * R bytes, at most 128 KiB).  The
-// per-element path keeps P <= 16.  RMSNorm fp32 with 32 values on 1024 lanes
-// would need scratch when the row is split.
+// per-element path keeps P <= 16 (one exception below).  RMSNorm fp32 with 32
+// values on 1024 lanes would need scratch when the row is split.
 // The cross-entropy gradient epilogue keeps the label, dloss and the label's logit
 // per row: fp32 with 32 values on 1024 lanes no longer fits in 128 VGPRs.
 constexpr bool stream_config_enabled(int op, int elem_bytes, bool vec, int P, int R, int G) {
-    if (!vec && P > 16) return false;
+    // The per-element path keeps P <= 16, except unaligned bf16 softmax and RMSNorm
+    // rows split over 2 to 8 workgroups: 32 values on 512 lanes (the planner uses
+    // them up to 81920 elements).
+    if (!vec && P > 16)
+        return elem_bytes == 2 && P == 32 && R == 512 && G >= 2 && G <= 8 &&
+               (op == kCfgSoftmax || op == kCfgRmsnorm);
     // 128 workgroups per row (4194304 elements on chip): softmax and RMSNorm forward
     if (G > 64 && op != kCfgSoftmax && op != kCfgRmsnorm) return false;
     // Workgroups per row that are not a power of two: bf16 softmax and cross-entropy

@@ -179,8 +179,16 @@ static void exact_groups(int op, int dtype, bool vec, int64_t N, Plan *p) {
     if (need < p->G && stream_config_ok(op, dtype, vec, 64, 512, (int)need)) p->G = (int)need;
 }
 
+// Unaligned bf16 softmax and RMSNorm rows split over 2 to 8 workgroups take 32
+// values on 512 lanes up to this many elements, 16 values on 1024 lanes beyond
+// (same box, GB/s, 8192 rows, 16 -> 32 values: softmax 32001 3171 -> 3647, 50257
+// 2691 -> 3554, 65537 2466 -> 2714, 100001 (RMSNorm) 3599 -> 3493, 151935 2582 ->
+// 2506; RMSNorm 50257 3149 -> 3718).
+constexpr int64_t kElemWideMaxN = 81920;
+
 static bool try_choice(int op, int dtype, bool vec, int64_t N, Choice c, Plan *p) {
     if (c.stream) {
+        if (!vec && c.P > 16 && N > kElemWideMaxN) return false;
         while (c.G > 1 && (int64_t)c.P * c.R * (c.G / 2) >= N) c.G /= 2;
         if ((int64_t)c.P * c.R * c.G < N || !stream_config_ok(op, dtype, vec, c.P, c.R, c.G))
             return false;

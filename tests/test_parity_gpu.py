@@ -153,6 +153,33 @@ def test_forced_xent_plans(P, R, dtype):
 
 # ------------------------------------------------------------- layouts
 
+@pytest.mark.parametrize("N", [16385, 20001, 50257, 65537, 81919, 81921])
+def test_unaligned_bf16_split_rows_wide_lanes(N):
+    """Unaligned bf16 softmax and RMSNorm rows of 16385 to 81920 elements: 32 values on
+    512 lanes over 2 to 8 workgroups (16 on 1024 past that), with a base one element
+    past a 16-byte boundary and 40 rows, so row groups take several rows."""
+    M = 40
+    for code in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
+        p = rr.rr_plan_query(code, M, N, rr.RR_BF16, False)
+        wide = N <= 81920
+        assert (p["vals_per_lane"], p["lanes_per_row"]) == ((32, 512) if wide else (16, 1024))
+        assert 2 <= p["groups_per_row"] <= (8 if wide else 16)
+    x_np = _x(M, N, "bf16", sigma=2.0)
+    w_np = _w(N, "bf16")
+    xs = to_dev(np.concatenate([np.zeros(1, x_np.dtype), x_np.ravel()]), "bf16")[1:].view(M, N)
+    ys = torch.empty(M * N + 1, dtype=xs.dtype, device=DEV)[1:].view(M, N)
+    wt = torch.empty(N + 1, dtype=xs.dtype, device=DEV)[1:]
+    wt.copy_(to_dev(w_np, "bf16"))
+    say("unaligned wide softmax", N)
+    rr.rr_softmax_fwd(xs, ys, ws=rr.workspace(rr.RR_OP_SOFTMAX, M, N, rr.RR_BF16, DEV))
+    torch.cuda.synchronize()
+    check_out(from_dev(ys), oracle.softmax(x_np), "bf16", f"unaligned wide softmax {N}")
+    say("unaligned wide rmsnorm", N)
+    rr.rr_rmsnorm_fwd(xs, wt, 1e-6, y=ys, ws=rr.workspace(rr.RR_OP_RMSNORM, M, N, rr.RR_BF16, DEV))
+    torch.cuda.synchronize()
+    check_out(from_dev(ys), oracle.rmsnorm(x_np, w_np, 1e-6), "bf16", f"unaligned wide rmsnorm {N}")
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("N", [64, 1000, 4096, 40000, 131072])
 def test_unaligned_rows_take_the_element_path(N, dtype):

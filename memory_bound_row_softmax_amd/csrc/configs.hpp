@@ -152,8 +152,11 @@ constexpr int long_row_groups(int op_softmax, long long row_bytes) {
 }
 constexpr long long kLongMaxN = 1ll << 28;
 
-// RMSNorm backward: the per-element path keeps P <= 16.
-constexpr bool rmsbwd_config_enabled(bool vec, int P) { return vec || P <= 16; }
+// RMSNorm backward: the per-element path keeps P <= 16 for fp32; bf16 (whose
+// per-element loads take no branch) has 32 values per lane as well.
+constexpr bool rmsbwd_config_enabled(bool vec, int P, int elem_bytes) {
+    return vec || P <= 16 || (elem_bytes == 2 && P <= 32);
+}
 
 // RMSNorm backward partial rows: at most kBwdMaxWorkgroups / G row groups, each
 // writing one fp32 partial row of dw; one column reduction pass adds them.

@@ -66,9 +66,8 @@ bool xent_config_exists(int P, int R) {
 }
 
 bool rmsbwd_config_ok(int dtype, bool vec, int P, int R, int G) {
-    (void)dtype;
 #define RR_X(p, r, g) \
-    if (P == p && R == r && G == g) return rmsbwd_config_enabled(vec, p);
+    if (P == p && R == r && G == g) return rmsbwd_config_enabled(vec, p, elem_bytes(dtype));
     RR_RMSBWD_CONFIGS(RR_X)
 #undef RR_X
     return false;
@@ -301,12 +300,17 @@ static PlanResult plan_rmsnorm_bwd(int dtype, int64_t M, int64_t N, bool vec, Pl
         G = fG ? fG : 1;
     } else {
         int k = 0;
-        // The 5120, 8192 and 12288 buckets were measured on the 128-bit path only;
+        // The 5120, 8192 and 12288 buckets were measured on the 128-bit path; fp32
         // rows on the per-element path keep the plans of the buckets around them.
-        while (k < kTunedBwdBuckets - 1 && (kTunedBwdN[k] < N || (!vec && kBwdAlignedOnly[k])))
+        // Unaligned bf16 rows, whose loads take no branch, use every bucket and the
+        // table's 32 values per lane (16384 rows, GB/s, from 16 values: x2047 3124
+        // -> 3582, x4095 3302 -> 3792, x10001 2506 -> 3431, x65537 1519 -> 2480,
+        // x131071 2485 -> 3759, x262143 2398 -> 3431).
+        while (k < kTunedBwdBuckets - 1 &&
+               (kTunedBwdN[k] < N || (!vec && dtype != kBf16 && kBwdAlignedOnly[k])))
             ++k;
         BwdChoice c = kTunedRmsBwd[dtype == kBf16 ? 1 : 0][k];
-        if (!vec && c.P > 16) {  // the per-element path keeps P <= 16: twice the lanes
+        if (!vec && c.P > 16 && dtype != kBf16) {  // fp32 per-element: P <= 16, twice the lanes
             c.P = 16;
             if (c.G == 1 && c.R < 512) c.R *= 2; else c.G *= 2;
         }

@@ -48,7 +48,7 @@ hipError_t dispatch(const Plan &p, const void *x, const void *w, const void *dy,
                     const float *rstd, void *dx, int64_t M, int64_t N, uint8_t *ws, int *parts,
                     const LaunchArgs &a) {
 #define RR_X(P_, R_, G_)                                                                 \
-    if constexpr (rmsbwd_config_enabled(VEC, P_))                                        \
+    if constexpr (rmsbwd_config_enabled(VEC, P_, E::BYTES))                              \
         if (p.P == P_ && p.R == R_ && p.G == G_)                                         \
             return launch_cfg<E, P_, R_, G_, VEC>(p, x, w, dy, rstd, dx, M, N, ws, parts, a);
     RR_RMSBWD_CONFIGS(RR_X)

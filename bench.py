@@ -36,7 +36,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "effective HBM GB/s (1 read+1 write) and % of MI355X peak, per op/N/dtype"
 HBM_PEAK_GBPS = 8000.0
-DEFAULT_WORKLOAD = "rmsnorm_bf16_16384x4096"
+# The largest fixed workload, and the shape the pages quote their headline on ([QuACK]
+# section NCU 性能分析（Softmax 内核）: fp32 softmax, 16K rows of 131K, 3.01 TB/s on H100).
+DEFAULT_WORKLOAD = "softmax_f32_16384x131072_spiky"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = os.path.join(ROOT, "memory_bound_row_softmax_amd", "csrc")
 
@@ -210,11 +212,22 @@ class Runner:
             dst = self.y[i]
         return self.rr.stream_copy_raw(src.data_ptr(), dst.data_ptr(), nbytes, self.sp)
 
+    def check_workspace(self):
+        """Fails if a split row of the timed launches gave up waiting for its peer
+        workgroups (its rows would then be NaN, and the launch faster than a real one)."""
+        if self.ws is None:
+            return
+        st = self.rr.rr_workspace_check(self.ws, stream=self.sp)
+        if st != 0:
+            raise RuntimeError(f"workspace check failed: {self.rr.status_string(st)}")
+
     def time(self, fn, steps: int, warmup: int, graph: bool = False):
         """Wall time of `steps` back-to-back launches, and the mean time per launch
         from a pair of HIP events on the launch stream around the same region.
         With `graph`, the `steps` launches are captured once in a HIP graph and the
-        timed region is one replay of it (no host launch cost between kernels)."""
+        timed region is one replay of it (no host launch cost between kernels).
+        Every launch's status is checked (after the timed region, so that the check
+        adds nothing between launches), and so is the workspace's error word."""
         torch = self.torch
         with torch.cuda.stream(self.stream):
             for k in range(warmup):
@@ -236,14 +249,18 @@ class Runner:
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             start.record(self.stream)
+            bad = 0
             if graph:
                 g.replay()
             else:
                 for k in range(steps):
-                    fn(warmup + k)
+                    bad |= fn(warmup + k)
             end.record(self.stream)
             torch.cuda.synchronize()
             t1 = time.perf_counter()
+        if bad != 0:
+            raise RuntimeError(f"a timed launch failed: {self.rr.status_string(bad)}")
+        self.check_workspace()
         return t1 - t0, start.elapsed_time(end) / steps
 
 

@@ -39,8 +39,10 @@
  *    fits on an idle device at once.  When it does not all run at once (other
  *    work holding the device), the launch still completes if one XCD can hold
  *    as many of them as share a row (a workgroup runs on the XCD its block id
- *    names).  Each wait is bounded, and a wait that gives up is reported by
- *    rr_workspace_check().
+ *    names).  Each wait is bounded (about a second).  A workgroup whose wait gives up
+ *    writes NaN in place of its share of that row (and of every later row whose wait
+ *    also fails) and sets the workspace's error word, which rr_workspace_check()
+ *    reports: a launch never ends with wrong values that are not NaN.
  */
 #ifndef RR_H
 #define RR_H
@@ -209,6 +211,31 @@ rr_status rr_plan_query(rr_op op, int64_t M, int64_t N, rr_dtype dt, int vectori
  * operators; a measurement aid.
  */
 rr_status rr_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
+
+/*
+ * Test-only: forces plan and launch choices for every later call in the process, so
+ * that tests reach each kernel path at sizes the oracle checks in seconds (a split row
+ * at N = 3000, a grid several times larger than the device holds, a wait that gives
+ * up).  Not for production use: a forced plan may be slow or unsupported, and a forced
+ * spin limit makes split rows time out (their rows are then NaN and
+ * rr_workspace_check() reports RR_ERR_GRID_TIMEOUT).  Nothing else in the library
+ * reads these values, and no environment variable changes any plan.  NULL (or all
+ * fields zero) restores the defaults.  Returns RR_ERR_INVALID_ARGUMENT for a negative
+ * field (other than spin_limit = -1) or an unknown kind.  Process-wide; not meant to be
+ * changed while calls run on other threads.
+ */
+typedef struct {
+    int kind;            /* 0: the planner's choice, 1: block kernel, 2: stream kernel,
+                            3: the two-read long-row kernel (softmax and RMSNorm forward) */
+    int vals_per_lane;   /* P of the plan (0: the planner's choice) */
+    int lanes_per_row;   /* R of the plan (0: the planner's choice) */
+    int groups_per_row;  /* G of the plan (0: the planner's choice) */
+    int resident_groups; /* row groups of a persistent grid (0: as many as fit at once) */
+    int spin_limit;      /* polls per split-row wait (0: the default of 2^20, about a
+                            second); -1: every wait gives up at once */
+} rr_test_overrides;
+
+rr_status rr_set_test_overrides(const rr_test_overrides *overrides);
 
 const char *rr_status_string(rr_status status);
 

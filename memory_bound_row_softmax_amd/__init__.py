@@ -31,8 +31,8 @@ RR_F32, RR_BF16 = 0, 1
 
 EXPORTS = ("rr_softmax_fwd", "rr_rmsnorm_fwd", "rr_cross_entropy_fwd",
            "rr_cross_entropy_fwd_bwd", "rr_softmax_bwd", "rr_rmsnorm_bwd", "rr_workspace_bytes",
-           "rr_workspace_check", "rr_plan_query", "rr_stream_copy", "rr_status_string",
-           "rr_last_hip_error")
+           "rr_workspace_check", "rr_plan_query", "rr_stream_copy", "rr_set_test_overrides",
+           "rr_status_string", "rr_last_hip_error")
 
 
 class RRError(RuntimeError):
@@ -47,6 +47,12 @@ class PlanInfo(ctypes.Structure):
                 ("groups_per_row", ctypes.c_int), ("block_threads", ctypes.c_int),
                 ("rows_per_block", ctypes.c_int), ("max_n", ctypes.c_int64),
                 ("ws_bytes", ctypes.c_size_t)]
+
+
+class TestOverrides(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int), ("vals_per_lane", ctypes.c_int),
+                ("lanes_per_row", ctypes.c_int), ("groups_per_row", ctypes.c_int),
+                ("resident_groups", ctypes.c_int), ("spin_limit", ctypes.c_int)]
 
 
 _lock = threading.Lock()
@@ -76,13 +82,14 @@ def lib():
             L.rr_workspace_check.argtypes = [vp, sz, vp]
             L.rr_plan_query.argtypes = [ci, i64, i64, ci, ci, ctypes.POINTER(PlanInfo)]
             L.rr_stream_copy.argtypes = [vp, vp, sz, vp]
+            L.rr_set_test_overrides.argtypes = [ctypes.POINTER(TestOverrides)]
             L.rr_status_string.argtypes = [ci]
             L.rr_status_string.restype = ctypes.c_char_p
             L.rr_last_hip_error.argtypes = []
             for f in (L.rr_softmax_fwd, L.rr_rmsnorm_fwd, L.rr_cross_entropy_fwd,
                       L.rr_cross_entropy_fwd_bwd, L.rr_softmax_bwd, L.rr_rmsnorm_bwd,
                       L.rr_workspace_check, L.rr_plan_query, L.rr_stream_copy,
-                      L.rr_last_hip_error):
+                      L.rr_set_test_overrides, L.rr_last_hip_error):
                 f.restype = st
             _lib = L
     return _lib
@@ -151,10 +158,42 @@ def dtype_code(t) -> int:
     raise TypeError(f"librr takes float32 or bfloat16 tensors, got {t.dtype}")
 
 
+def _handle(stream) -> int:
+    """A raw stream handle from a torch stream or an integer handle."""
+    return int(getattr(stream, "cuda_stream", stream))
+
+
 def _stream(t, stream):
     if stream is not None:
-        return int(stream)
+        return _handle(stream)
     return _torch().cuda.current_stream(t.device).cuda_stream
+
+
+class _on_stream:
+    """Makes the launch stream current while a call allocates its outputs and
+    workspace, so that they are allocated (and the workspace zero-filled) in that
+    stream's order: the zero fill then precedes the kernel, and the caching allocator
+    does not hand the memory to other work before the kernel is done with it.
+    Yields the raw handle of the launch stream."""
+
+    def __init__(self, device, stream):
+        self.device, self.stream, self.ctx = device, stream, None
+
+    def __enter__(self) -> int:
+        torch = _torch()
+        cur = torch.cuda.current_stream(self.device)
+        if self.stream is None or _handle(self.stream) == cur.cuda_stream:
+            return cur.cuda_stream
+        ext = (self.stream if isinstance(self.stream, torch.cuda.Stream)
+               else torch.cuda.ExternalStream(_handle(self.stream), device=self.device))
+        self.ctx = torch.cuda.stream(ext)
+        self.ctx.__enter__()
+        return ext.cuda_stream
+
+    def __exit__(self, *exc):
+        if self.ctx is not None:
+            self.ctx.__exit__(*exc)
+        return False
 
 
 def _matrix(x):
@@ -204,13 +243,14 @@ def _ws_args(ws):
 def rr_softmax_fwd(x, y=None, ws=None, stream=None):
     """Row softmax of x [M, N] into y (new tensor if None; y may be x)."""
     M, N = _matrix(x)
-    y = _torch().empty_like(x) if y is None else _like(y, x, "y")
     dt = dtype_code(x)
-    if ws is None:
-        ws = workspace(RR_OP_SOFTMAX, M, N, dt, x.device)
-    wp, wb = _ws_args(ws)
-    _check(softmax_fwd_raw(x.data_ptr(), y.data_ptr(), M, N, dt, wp, wb, _stream(x, stream)),
-           "rr_softmax_fwd")
+    with _on_stream(x.device, stream) as sp:
+        y = _torch().empty_like(x) if y is None else _like(y, x, "y")
+        if ws is None:
+            ws = workspace(RR_OP_SOFTMAX, M, N, dt, x.device)
+        wp, wb = _ws_args(ws)
+        _check(softmax_fwd_raw(x.data_ptr(), y.data_ptr(), M, N, dt, wp, wb, sp),
+               "rr_softmax_fwd")
     return y
 
 
@@ -219,16 +259,17 @@ def rr_rmsnorm_fwd(x, w, eps=1e-6, y=None, rstd=None, ws=None, stream=None):
     M, N = _matrix(x)
     if w.dtype != x.dtype or w.numel() != N or not w.is_contiguous() or w.device != x.device:
         raise ValueError("weight must be a contiguous [N] tensor of the input's dtype")
-    y = _torch().empty_like(x) if y is None else _like(y, x, "y")
     if rstd is not None:
         _f32_vector(rstd, M, x.device, "rstd")
     dt = dtype_code(x)
-    if ws is None:
-        ws = workspace(RR_OP_RMSNORM, M, N, dt, x.device)
-    wp, wb = _ws_args(ws)
-    _check(rmsnorm_fwd_raw(x.data_ptr(), w.data_ptr(), y.data_ptr(),
-                           rstd.data_ptr() if rstd is not None else 0, M, N, dt, float(eps), wp,
-                           wb, _stream(x, stream)), "rr_rmsnorm_fwd")
+    with _on_stream(x.device, stream) as sp:
+        y = _torch().empty_like(x) if y is None else _like(y, x, "y")
+        if ws is None:
+            ws = workspace(RR_OP_RMSNORM, M, N, dt, x.device)
+        wp, wb = _ws_args(ws)
+        _check(rmsnorm_fwd_raw(x.data_ptr(), w.data_ptr(), y.data_ptr(),
+                               rstd.data_ptr() if rstd is not None else 0, M, N, dt, float(eps),
+                               wp, wb, sp), "rr_rmsnorm_fwd")
     return y
 
 
@@ -240,15 +281,16 @@ def rr_cross_entropy_fwd(logits, labels, loss=None, lse=None, ws=None, stream=No
         raise ValueError("labels must be a contiguous int32 [M] tensor")
     if labels.device != logits.device:
         raise ValueError("labels must be on the logits' device")
-    loss = (torch.empty(M, dtype=torch.float32, device=logits.device) if loss is None
-            else _f32_vector(loss, M, logits.device, "loss"))
-    lse = (torch.empty(M, dtype=torch.float32, device=logits.device) if lse is None
-           else _f32_vector(lse, M, logits.device, "lse"))
     dt = dtype_code(logits)
-    wp, wb = _ws_args(ws)
-    _check(cross_entropy_fwd_raw(logits.data_ptr(), labels.data_ptr(), loss.data_ptr(),
-                                 lse.data_ptr(), M, N, dt, wp, wb, _stream(logits, stream)),
-           "rr_cross_entropy_fwd")
+    with _on_stream(logits.device, stream) as sp:
+        loss = (torch.empty(M, dtype=torch.float32, device=logits.device) if loss is None
+                else _f32_vector(loss, M, logits.device, "loss"))
+        lse = (torch.empty(M, dtype=torch.float32, device=logits.device) if lse is None
+               else _f32_vector(lse, M, logits.device, "lse"))
+        wp, wb = _ws_args(ws)
+        _check(cross_entropy_fwd_raw(logits.data_ptr(), labels.data_ptr(), loss.data_ptr(),
+                                     lse.data_ptr(), M, N, dt, wp, wb, sp),
+               "rr_cross_entropy_fwd")
     return loss, lse
 
 
@@ -264,19 +306,20 @@ def rr_cross_entropy_fwd_bwd(logits, labels, dloss, dlogits=None, loss=None, lse
     if labels.device != logits.device:
         raise ValueError("labels must be on the logits' device")
     _f32_vector(dloss, M, logits.device, "dloss")
-    dlogits = torch.empty_like(logits) if dlogits is None else _like(dlogits, logits, "dlogits")
-    loss = (torch.empty(M, dtype=torch.float32, device=logits.device) if loss is None
-            else _f32_vector(loss, M, logits.device, "loss"))
-    lse = (torch.empty(M, dtype=torch.float32, device=logits.device) if lse is None
-           else _f32_vector(lse, M, logits.device, "lse"))
     dt = dtype_code(logits)
-    if ws is None:
-        ws = workspace(RR_OP_XENT_GRAD, M, N, dt, logits.device)
-    wp, wb = _ws_args(ws)
-    _check(cross_entropy_fwd_bwd_raw(logits.data_ptr(), labels.data_ptr(), dloss.data_ptr(),
-                                     loss.data_ptr(), lse.data_ptr(), dlogits.data_ptr(), M, N,
-                                     dt, wp, wb, _stream(logits, stream)),
-           "rr_cross_entropy_fwd_bwd")
+    with _on_stream(logits.device, stream) as sp:
+        dlogits = (torch.empty_like(logits) if dlogits is None
+                   else _like(dlogits, logits, "dlogits"))
+        loss = (torch.empty(M, dtype=torch.float32, device=logits.device) if loss is None
+                else _f32_vector(loss, M, logits.device, "loss"))
+        lse = (torch.empty(M, dtype=torch.float32, device=logits.device) if lse is None
+               else _f32_vector(lse, M, logits.device, "lse"))
+        if ws is None:
+            ws = workspace(RR_OP_XENT_GRAD, M, N, dt, logits.device)
+        wp, wb = _ws_args(ws)
+        _check(cross_entropy_fwd_bwd_raw(logits.data_ptr(), labels.data_ptr(), dloss.data_ptr(),
+                                         loss.data_ptr(), lse.data_ptr(), dlogits.data_ptr(), M,
+                                         N, dt, wp, wb, sp), "rr_cross_entropy_fwd_bwd")
     return loss, lse, dlogits
 
 
@@ -285,13 +328,14 @@ def rr_softmax_bwd(y, dy, dx=None, ws=None, stream=None):
     dx = y * (dy - rowsum(y * dy)); dx may be y or dy itself."""
     M, N = _matrix(y)
     _like(dy, y, "dy")
-    dx = _torch().empty_like(y) if dx is None else _like(dx, y, "dx")
     dt = dtype_code(y)
-    if ws is None:
-        ws = workspace(RR_OP_SOFTMAX_BWD, M, N, dt, y.device)
-    wp, wb = _ws_args(ws)
-    _check(softmax_bwd_raw(y.data_ptr(), dy.data_ptr(), dx.data_ptr(), M, N, dt, wp, wb,
-                           _stream(y, stream)), "rr_softmax_bwd")
+    with _on_stream(y.device, stream) as sp:
+        dx = _torch().empty_like(y) if dx is None else _like(dx, y, "dx")
+        if ws is None:
+            ws = workspace(RR_OP_SOFTMAX_BWD, M, N, dt, y.device)
+        wp, wb = _ws_args(ws)
+        _check(softmax_bwd_raw(y.data_ptr(), dy.data_ptr(), dx.data_ptr(), M, N, dt, wp, wb, sp),
+               "rr_softmax_bwd")
     return dx
 
 
@@ -306,23 +350,40 @@ def rr_rmsnorm_bwd(x, w, dy, rstd, dx=None, dw=None, ws=None, stream=None):
     if w.dtype != x.dtype or w.numel() != N or not w.is_contiguous() or w.device != x.device:
         raise ValueError("weight must be a contiguous [N] tensor of the input's dtype")
     _f32_vector(rstd, M, x.device, "rstd")
-    dx = torch.empty_like(x) if dx is None else _like(dx, x, "dx")
-    dw = (torch.empty(N, dtype=torch.float32, device=x.device) if dw is None
-          else _f32_vector(dw, N, x.device, "dw"))
     dt = dtype_code(x)
-    if ws is None:
-        ws = workspace(RR_OP_RMSNORM_BWD, M, N, dt, x.device)
-    wp, wb = _ws_args(ws)
-    _check(rmsnorm_bwd_raw(x.data_ptr(), w.data_ptr(), dy.data_ptr(), rstd.data_ptr(),
-                           dx.data_ptr(), dw.data_ptr(), M, N, dt, wp, wb, _stream(x, stream)),
-           "rr_rmsnorm_bwd")
+    with _on_stream(x.device, stream) as sp:
+        dx = torch.empty_like(x) if dx is None else _like(dx, x, "dx")
+        dw = (torch.empty(N, dtype=torch.float32, device=x.device) if dw is None
+              else _f32_vector(dw, N, x.device, "dw"))
+        if ws is None:
+            ws = workspace(RR_OP_RMSNORM_BWD, M, N, dt, x.device)
+        wp, wb = _ws_args(ws)
+        _check(rmsnorm_bwd_raw(x.data_ptr(), w.data_ptr(), dy.data_ptr(), rstd.data_ptr(),
+                               dx.data_ptr(), dw.data_ptr(), M, N, dt, wp, wb, sp),
+               "rr_rmsnorm_bwd")
     return dx, dw
 
 
 def rr_workspace_check(ws, stream=None) -> int:
-    """Synchronises the stream and returns (and clears) the workspace's status."""
+    """Synchronises the stream and returns (and clears) the workspace's status:
+    RR_OK, or RR_ERR_GRID_TIMEOUT if a split row of a launch that used `ws` gave up
+    waiting for its peer workgroups (that row's outputs are then NaN).  The ops above
+    do not call it themselves (it synchronises); a caller that passes its own `ws`
+    checks it when it synchronises anyway."""
     wp, wb = _ws_args(ws)
     return lib().rr_workspace_check(wp, wb, _stream(ws, stream))
+
+
+_KINDS = {None: 0, "block": 1, "stream": 2, "long": 3}
+
+
+def set_test_overrides(kind=None, P=None, R=None, G=None, groups=None, spin=None):
+    """Test-only: forces the plan (kernel kind, P, R, G), the row groups of a persistent
+    grid and the bound of each split-row wait (spin = -1: every wait gives up) for every
+    later call in the process; with no arguments, restores the defaults.  See
+    rr_set_test_overrides in include/rr.h."""
+    o = TestOverrides(_KINDS[kind], P or 0, R or 0, G or 0, groups or 0, spin or 0)
+    _check(lib().rr_set_test_overrides(ctypes.byref(o)), "rr_set_test_overrides")
 
 
 def rr_stream_copy(src, dst, stream=None):

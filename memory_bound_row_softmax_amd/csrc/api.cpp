@@ -5,7 +5,6 @@
 
 #include <atomic>
 #include <cstdint>
-#include <cstdlib>
 #include <cstring>
 #include <initializer_list>
 #include <mutex>
@@ -34,14 +33,8 @@ int device_cus(int dev, hipError_t *err) {
     return c;
 }
 
-int spin_limit() {
-    const char *s = std::getenv("RR_SPIN_LIMIT");
-    if (s && *s) {
-        long v = std::strtol(s, nullptr, 10);
-        if (v >= 1 && v <= 0x7FFFFFFF) return (int)v;
-    }
-    return 1 << 20;
-}
+// Polls of each split-row wait before it gives up (about a second on MI355X).
+constexpr int kSpinLimit = 1 << 20;
 
 rr_status hip_status(hipError_t e) {
     if (e == hipSuccess) return RR_OK;
@@ -113,7 +106,9 @@ rr_status launch_args(hipStream_t stream, rr::LaunchArgs *a) {
     if (e != hipSuccess) return hip_status(e);
     const int cus = device_cus(dev, &e);
     if (e != hipSuccess) return hip_status(e);
-    *a = rr::LaunchArgs{stream, cus, spin_limit()};
+    const rr::TestOverrides ov = rr::test_overrides();
+    *a = rr::LaunchArgs{stream, cus, ov.spin != 0 ? (ov.spin < 0 ? 0 : ov.spin) : kSpinLimit,
+                        ov.groups > 0 ? ov.groups : 0};
     return RR_OK;
 }
 
@@ -312,6 +307,23 @@ rr_status rr_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t s
     rr_status st = launch_args(stream, &a);
     if (st != RR_OK) return st;
     return hip_status(rr::launch_copy(src, dst, bytes, a));
+}
+
+rr_status rr_set_test_overrides(const rr_test_overrides *o) {
+    rr::TestOverrides t;
+    if (o) {
+        if (o->kind < 0 || o->kind > 3 || o->vals_per_lane < 0 || o->lanes_per_row < 0 ||
+            o->groups_per_row < 0 || o->resident_groups < 0 || o->spin_limit < -1)
+            return RR_ERR_INVALID_ARGUMENT;
+        t.kind = o->kind;
+        t.P = o->vals_per_lane;
+        t.R = o->lanes_per_row;
+        t.G = o->groups_per_row;
+        t.groups = o->resident_groups;
+        t.spin = o->spin_limit;
+    }
+    rr::set_test_overrides(t);
+    return RR_OK;
 }
 
 const char *rr_status_string(rr_status status) {

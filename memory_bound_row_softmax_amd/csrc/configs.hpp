@@ -181,9 +181,12 @@ constexpr int kBwdMaxWorkgroups = 1024;
 #endif
 constexpr bool kDeferredExchange = RR_SPLIT_DEFER != 0;
 
+#ifndef RR_DEFER_MIN_G
+#define RR_DEFER_MIN_G 8
+#endif
 constexpr bool defer_split(int op, int elem_bytes, bool vec, int P, int R, int G) {
     (void)elem_bytes;
-    if (G < 8) return false;
+    if (G < RR_DEFER_MIN_G) return false;
     if (op == kCfgSoftmaxBwd) return vec && P == 32 && R == 512;
     if (op == kCfgRmsnorm && P == 32 && R == 512) return true;
     if (P == 64 && R == 512) return op == kCfgSoftmax;

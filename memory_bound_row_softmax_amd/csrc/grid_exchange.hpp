@@ -20,8 +20,10 @@
 //  * wave 0 polls the G slots (one lane per slot), then merges the partials in slot
 //    order, so every workgroup of the row computes the same bits;
 //  * each poll loop is bounded by `spin_limit`; a workgroup that gives up sets the
-//    workspace error word and carries on (its outputs are then not valid), so a
-//    kernel always finishes;
+//    workspace error word, takes NaN as the row's merged result (so its share of the
+//    row is written as NaN, never as a wrong number) and carries on, so a kernel
+//    always finishes.  Later waits of that workgroup poll once: a row whose peers
+//    have all published is still exact, any other row is NaN;
 //  * after its last row every workgroup increments the group's departure counter;
 //    the last one to leave zeroes the group's slots and the counter, so the
 //    workspace is all zero again for the next launch.
@@ -92,8 +94,11 @@ __device__ __forceinline__ void publish_pair(GroupRef g, int k, int it, float a,
 // Waits until all G members have published iteration `it` and leaves the G pairs
 // merged in member order by `merge2` in bcast[0..1] (the same bits for the whole
 // workgroup).  Called by every thread; uses one barrier.  Lane l of wave 0 polls
-// the slots of members l and l + 64 (G <= 128).  After a wait has timed out,
-// `spin_limit` is lowered to 1 so that the rest of the launch does not wait again.
+// the slots of members l and l + 64 (G <= 128).  A wait that gives up (after
+// `spin_limit` polls; at once if spin_limit <= 0) leaves NaN in bcast[0..1], which
+// every op's epilogue carries into each value it writes for the row, and lowers
+// `spin_limit` to 1 so that the rest of the launch does not wait long again (a limit
+// of 0, which only a test sets, stays 0: every wait of the launch gives up).
 template <int G, class Merge>
 __device__ __forceinline__ void wait_pairs(GroupRef g, int it, int &spin_limit, float *bcast,
                                            Merge merge2) {
@@ -125,9 +130,11 @@ __device__ __forceinline__ void wait_pairs(GroupRef g, int it, int &spin_limit, 
             if (all_in || ++spins >= spin_limit) break;
             __builtin_amdgcn_s_sleep(1);
         }
-        if (!all_in && lane == 0)
+        all_in = all_in && spin_limit > 0;
+        if (!all_in && lane == 0) {
             __hip_atomic_store(g.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (!all_in) bcast[2] = 1.0f;
+            bcast[2] = 1.0f;
+        }
         float acc_a = 0.0f, acc_b = 0.0f;
 #pragma unroll
         for (int s = 0; s < kPer; ++s) {
@@ -146,12 +153,12 @@ __device__ __forceinline__ void wait_pairs(GroupRef g, int it, int &spin_limit, 
             }
         }
         if (lane == 0) {
-            bcast[0] = acc_a;
-            bcast[1] = acc_b;
+            bcast[0] = all_in ? acc_a : __builtin_nanf("");
+            bcast[1] = all_in ? acc_b : __builtin_nanf("");
         }
     }
     __syncthreads();
-    if (bcast[2] != 0.0f) spin_limit = 1;
+    if (bcast[2] != 0.0f && spin_limit > 1) spin_limit = 1;
 }
 
 // Publish, then wait for the same iteration.

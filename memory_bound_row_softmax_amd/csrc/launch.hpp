@@ -12,7 +12,8 @@ namespace rr {
 struct LaunchArgs {
     hipStream_t stream;
     int num_cus;     // compute units of the current device
-    int spin_limit;  // bound on each grid-exchange wait (polls)
+    int spin_limit;     // bound on each grid-exchange wait (polls); <= 0: a wait gives up at once
+    int forced_groups;  // row groups of a persistent grid (0: from the occupancy query)
 };
 
 hipError_t launch_softmax(const Plan &p, int dtype, const void *x, void *y, int64_t M, int64_t N,

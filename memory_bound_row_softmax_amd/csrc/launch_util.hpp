@@ -4,7 +4,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <cstdlib>
 
 #include "configs.hpp"
 #include "launch.hpp"
@@ -22,10 +21,9 @@ hipError_t resident_groups(K kernel, int block, int G, int64_t M, const LaunchAr
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0);
     if (e != hipSuccess) return e;
     int64_t g = (int64_t)per_cu * a.num_cus / G;
-    // test override: a grid larger than fits at once (split rows must still drain
-    // when one XCD holds G workgroups)
-    const char *fg = std::getenv("RR_FORCE_GROUPS");
-    if (fg && *fg && std::atoi(fg) > 0) g = std::atoi(fg);
+    // test override (rr_set_test_overrides): a grid larger than fits at once (split
+    // rows must still drain when one XCD holds G workgroups)
+    if (a.forced_groups > 0) g = a.forced_groups;
     if (g > kMaxGroups) g = kMaxGroups;
     if (g > M) g = M;
     if (g < 1) return hipErrorCooperativeLaunchTooLarge;

@@ -90,7 +90,8 @@ __device__ __forceinline__ void rmsnorm_packed_apply(const float *raw, const u32
             const float ww = __uint_as_float(wq[q]);
             o[q] = pack_bf16x2((bf16_lo(xw) * bf16_lo(ww)) * r, (bf16_hi(xw) * bf16_hi(ww)) * r);
         }
-        if (c.full || ch * 8 < c.nend) buf_store16(yv.buf, yv.base + (uint32_t)ch * 16u, o);
+        // yv ends where this member's part ends: the range check drops chunks past it
+        buf_store16(yv.buf, yv.base + (uint32_t)ch * 16u, o);
     }
     if (rstd_out && c.l == 0 && c.member == 0) *rstd_out = r;
 }

@@ -15,12 +15,41 @@
 //     running (max, sum) instead of holding it.
 #include "plan.hpp"
 
-#include <cstdlib>
-#include <cstring>
+#include <atomic>
 
 #include "configs.hpp"
 
 namespace rr {
+
+// The test overrides.  Each field is read with one relaxed load per call; `active`
+// lets a call that sees no override skip the rest.
+namespace {
+std::atomic<bool> g_active{false};
+std::atomic<int> g_kind{0}, g_P{0}, g_R{0}, g_G{0}, g_groups{0}, g_spin{0};
+}  // namespace
+
+void set_test_overrides(const TestOverrides &o) {
+    g_kind.store(o.kind, std::memory_order_relaxed);
+    g_P.store(o.P, std::memory_order_relaxed);
+    g_R.store(o.R, std::memory_order_relaxed);
+    g_G.store(o.G, std::memory_order_relaxed);
+    g_groups.store(o.groups, std::memory_order_relaxed);
+    g_spin.store(o.spin, std::memory_order_relaxed);
+    const bool any = o.kind || o.P || o.R || o.G || o.groups || o.spin;
+    g_active.store(any, std::memory_order_release);
+}
+
+TestOverrides test_overrides() {
+    TestOverrides o;
+    if (!g_active.load(std::memory_order_acquire)) return o;
+    o.kind = g_kind.load(std::memory_order_relaxed);
+    o.P = g_P.load(std::memory_order_relaxed);
+    o.R = g_R.load(std::memory_order_relaxed);
+    o.G = g_G.load(std::memory_order_relaxed);
+    o.groups = g_groups.load(std::memory_order_relaxed);
+    o.spin = g_spin.load(std::memory_order_relaxed);
+    return o;
+}
 
 static int cfg_op(int op) {
     switch (op) {
@@ -83,12 +112,6 @@ static int64_t next_pow2(int64_t v) {
     int64_t p = 1;
     while (p < v) p <<= 1;
     return p;
-}
-
-static int env_int(const char *name) {
-    const char *s = std::getenv(name);
-    if (!s || !*s) return 0;
-    return std::atoi(s);
 }
 
 static void fill_geometry(Plan *p) {
@@ -292,7 +315,8 @@ static const BwdChoice kTunedRmsBwd[2][kTunedBwdBuckets] = {
 };
 
 static PlanResult plan_rmsnorm_bwd(int dtype, int64_t M, int64_t N, bool vec, Plan *out) {
-    const int fP = env_int("RR_FORCE_P"), fR = env_int("RR_FORCE_R"), fG = env_int("RR_FORCE_G");
+    const TestOverrides ov = test_overrides();
+    const int fP = ov.P, fR = ov.R, fG = ov.G;
     int P, R, G = 1;
     if (fP || fR || fG) {
         P = fP ? fP : 16;
@@ -366,7 +390,8 @@ PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *ou
     if (N < 1) N = 1;  // M == 0: any plan will do, nothing is launched
     Plan p;
     p.vec = vec;
-    const int fP = env_int("RR_FORCE_P"), fR = env_int("RR_FORCE_R"), fG = env_int("RR_FORCE_G");
+    const TestOverrides ov = test_overrides();
+    const int fP = ov.P, fR = ov.R, fG = ov.G;
 
     if (op == kOpXent) {
         if (N > INT32_MAX) return kPlanInvalid;
@@ -386,10 +411,9 @@ PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *ou
         return kPlanOk;
     }
 
-    const char *kind = std::getenv("RR_FORCE_KIND");
-    const bool force_stream = kind && std::strcmp(kind, "stream") == 0;
-    const bool force_block = kind && std::strcmp(kind, "block") == 0;
-    const bool force_long = kind && std::strcmp(kind, "long") == 0;
+    const bool force_stream = ov.kind == kForceStream;
+    const bool force_block = ov.kind == kForceBlock;
+    const bool force_long = ov.kind == kForceLong;
     const bool long_op = op == kOpSoftmax || op == kOpRmsnorm;
     if (long_op && (force_long || (!fP && !fR && !fG && !force_stream && !force_block &&
                                    !default_row(op, dtype, vec, M, N, &p)))) {

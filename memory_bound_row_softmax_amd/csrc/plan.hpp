@@ -46,11 +46,23 @@ bool stream_config_ok(int op, int dtype, bool vec, int P, int R, int G);
 bool xent_config_exists(int P, int R);
 bool rmsbwd_config_ok(int dtype, bool vec, int P, int R, int G);
 
+// Test-only overrides, set through rr_set_test_overrides() and nowhere else (all
+// zero unless a test sets them): the kernel kind, P, R and G of the plan, the row
+// groups of a persistent grid and the bound of each split-row wait.
+enum ForcedKind { kForceNone = 0, kForceBlock = 1, kForceStream = 2, kForceLong = 3 };
+struct TestOverrides {
+    int kind = kForceNone;
+    int P = 0, R = 0, G = 0;  // 0: not forced
+    int groups = 0;           // 0: as many row groups as fit on the device
+    int spin = 0;             // 0: the default bound; -1: every wait gives up at once
+};
+void set_test_overrides(const TestOverrides &o);
+TestOverrides test_overrides();
+
 // Chooses the plan.  `vec` says whether the 128-bit path is usable for these
-// pointers.  Test-only overrides come from the environment: RR_FORCE_KIND
-// ("block", "stream" or "long"), RR_FORCE_P, RR_FORCE_R and RR_FORCE_G (row ops), or
-// RR_FORCE_P and RR_FORCE_R (cross-entropy); a forced configuration that is not
-// compiled, or too small for N, is unsupported.
+// pointers.  Under test overrides (kind, P, R, G for the row ops; P, R for
+// cross-entropy) a forced configuration that is not compiled, or too small for N,
+// is unsupported.
 PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *out);
 
 // Workspace bytes of the grid path for G workgroups per row and M rows.

@@ -1,7 +1,5 @@
 // rmsnorm_bwd.hip -- instantiates the RMSNorm backward kernels of the configuration
 // menu and launches the one the plan names, then the dw column reduction.
-#include <cstdlib>
-
 #include "launch_util.hpp"
 #include "rmsnorm_bwd.hpp"
 
@@ -20,9 +18,8 @@ hipError_t launch_cfg(const Plan &p, const void *x, const void *w, const void *d
         // percent of two or four), at most one per row block and at most the
         // workspace's partial rows
         int64_t g = a.num_cus;
-        // test and tuning override of the number of persistent workgroups
-        const char *fg = std::getenv("RR_FORCE_GROUPS");
-        if (fg && *fg && std::atoi(fg) > 0) g = std::atoi(fg);
+        // test override of the number of persistent workgroups (rr_set_test_overrides)
+        if (a.forced_groups > 0) g = a.forced_groups;
         if (g > p.max_parts) g = p.max_parts;
         groups = (int)g;
     } else {

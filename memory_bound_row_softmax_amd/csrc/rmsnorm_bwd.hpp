@@ -12,7 +12,10 @@
 // columns in registers across the rows it processes, combines its lane groups
 // through LDS and writes one fp32 partial row to the workspace; one small pass
 // (rmsnorm_dw_reduce) then adds the partial rows in a fixed order, so dw is the
-// same bits on every run.
+// same bits on every run.  A workgroup's running sums over its M / 256 rows do not
+// round once per row (DwAcc below), so the error of dw does not grow with M: the
+// steps after them (the fp32 partial row, the lane-group combine and the reduce
+// pass) round a bounded number of times.
 //
 // Kernel: a persistent grid; with G = 1 a workgroup holds rows_per_block_for(R)
 // rows at a time (R lanes each) and walks the row blocks group, group + groups,
@@ -83,20 +86,70 @@ __device__ __forceinline__ void store_part_f32(Buf b, int chunk0, int l, int N, 
     }
 }
 
+// The dw running sums of a lane's P columns.  Each term dy * x * r is formed in fp32.
+// Wide: the sums are fp64 registers, so adding a term rounds at 2^-53 and n terms
+// stay within n * 2^-53 of the exact sum of the fp32 terms.  Compensated (for the
+// kernels whose registers cannot hold P more): fp32 sums with Kahan compensation,
+// the compensation terms in LDS (P * T floats); the sum of n terms is then within
+// about 2^-23 of the exact sum, whatever n is.
+template <int P, bool WIDE>
+struct DwAcc;
+
+template <int P>
+struct DwAcc<P, true> {
+    double s[P];
+    __device__ __forceinline__ void init(float *) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) s[j] = 0.0;
+    }
+    __device__ __forceinline__ void add(int j, float t) { s[j] += (double)t; }
+    __device__ __forceinline__ float get(int j) const { return (float)s[j]; }
+};
+
+template <int P>
+struct DwAcc<P, false> {
+    float s[P];
+    float *comp;  // this thread's compensation terms: comp[j * T]
+    int stride;
+    __device__ __forceinline__ void init(float *c) {
+        comp = c;
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            s[j] = 0.0f;
+            comp[j * stride] = 0.0f;
+        }
+    }
+    __device__ __forceinline__ void add(int j, float t) {
+        const float y = t - comp[j * stride];
+        const float n = s[j] + y;
+        comp[j * stride] = (n - s[j]) - y;
+        s[j] = n;
+    }
+    __device__ __forceinline__ float get(int j) const { return s[j]; }
+};
+
+// fp64 sums need P more registers than fp32 ones; the fp32 kernels with 32 values on
+// 512 lanes (1 workgroup per CU, 256 registers a lane, already 240 in use) take the
+// compensated sums instead.
+template <class E, int P, int R>
+constexpr bool dw_wide() {
+    return !(E::BYTES == 4 && P == 32 && R >= 512);
+}
+
 // a: x, b: dy of the lane's part of a row (b is reused); wsrc: w; acc: dw partials.
-template <class E, int P, int R, int G, bool VEC>
+template <class E, int P, int R, int G, bool VEC, class Acc>
 __device__ __forceinline__ void rmsnorm_bwd_finish(float *a, float *b, float r,
-                                                   const WeightLds<P, R> &wsrc, float *acc,
+                                                   const WeightLds<P, R> &wsrc, Acc &acc,
                                                    RowView dxv, bool valid, RowCtx &c) {
     constexpr int C = P / E::VPC;
     const int chunk0 = c.chunk0;
     if (!c.full) {
-        mask_part<E, C, R>(chunk0, c.l, c.nend, 0.0f, a);
-        mask_part<E, C, R>(chunk0, c.l, c.nend, 0.0f, b);
+        mask_part<E, C, R, true>(chunk0, c.l, c.nend, 0.0f, a);
+        mask_part<E, C, R, true>(chunk0, c.l, c.nend, 0.0f, b);
     }
     // dw partial first (before b is overwritten): dy * x * r
 #pragma unroll
-    for (int j = 0; j < P; ++j) acc[j] += (b[j] * a[j]) * r;
+    for (int j = 0; j < P; ++j) acc.add(j, (b[j] * a[j]) * r);
     // b <- w * dy, then c = sum (w dy) x
     wsrc.apply(b, c.l);
     float t = tree_dot<P>(b, a);
@@ -108,7 +161,7 @@ __device__ __forceinline__ void rmsnorm_bwd_finish(float *a, float *b, float r,
     const float k = r * r * t / (float)c.N;
 #pragma unroll
     for (int j = 0; j < P; ++j) a[j] = r * (b[j] - a[j] * k);
-    store_part<E, C, R, VEC>(dxv, chunk0, c.l, c.nend, valid, c.full, a);
+    store_part<E, C, R, VEC, true>(dxv, chunk0, c.l, c.nend, valid, c.full, a);
 }
 
 constexpr int bwd_threads(int R, int G) { return G == 1 ? block_threads_for(R) : R; }
@@ -153,9 +206,11 @@ __global__ void __launch_bounds__(bwd_threads(R, G))
     }
     if constexpr (RPB > 1) __syncthreads();
     const WeightLds<P, R> wsrc{wslot};
-    float acc[P];
-#pragma unroll
-    for (int j = 0; j < P; ++j) acc[j] = 0.0f;
+    constexpr bool kWide = dw_wide<E, P, R>();
+    __shared__ float dw_comp[kWide ? 1 : P * T];
+    DwAcc<P, kWide> acc;
+    if constexpr (!kWide) acc.stride = T;
+    acc.init(dw_comp + threadIdx.x);  // each thread reads back only what it wrote
 
     // buffer: x (P), dy (P), r (1)
     float buf[2][2 * P + 1];
@@ -178,12 +233,16 @@ __global__ void __launch_bounds__(bwd_threads(R, G))
         leave_grid(ws);
     }
 
-    // One partial row per workgroup (its lane groups summed in order through LDS).
+    // One partial row per workgroup (its lane groups summed in order through LDS,
+    // in fp32).
+    float part[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) part[j] = acc.get(j);
     if constexpr (RPB > 1) {
         __shared__ float comb[T * P];
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < P; ++j) comb[j * T + threadIdx.x] = acc[j];
+        for (int j = 0; j < P; ++j) comb[j * T + threadIdx.x] = part[j];
         __syncthreads();
         if (sub == 0) {
 #pragma unroll
@@ -191,13 +250,13 @@ __global__ void __launch_bounds__(bwd_threads(R, G))
                 float s = comb[j * T + l];
 #pragma unroll
                 for (int q = 1; q < RPB; ++q) s += comb[j * T + q * R + l];
-                acc[j] = s;
+                part[j] = s;
             }
         }
     }
     if (sub == 0) {
         const Buf pb = make_buf(partial + (int64_t)group * N, (uint32_t)N * 4u);
-        store_part_f32<E, C, R>(pb, chunk0, l, c.nend, acc);  // this member's columns only
+        store_part_f32<E, C, R>(pb, chunk0, l, c.nend, part);  // this member's columns only
     }
 }
 

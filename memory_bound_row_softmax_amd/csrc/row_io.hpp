@@ -176,28 +176,62 @@ __device__ __forceinline__ void widen_part(float *v) {
 }
 
 // Registers that hold no element of the row get `fill`.
-template <class E, int C, int R>
+// OPAQUE (persistent kernels, whose row loop keeps chunk0 and N fixed): the lane's
+// count of elements left in the row passes through an empty asm statement, so that
+// the comparisons stay inside the row loop, where they run only for a part that is
+// not full.  Left to itself, the compiler hoists all P comparisons out of the loop,
+// and their P lane masks and element indices stay live in registers for every row
+// (116 spilled scalar registers and some 15 vector registers in the 64-value fp32
+// stream kernel).
+template <class E, int C, int R, bool OPAQUE = false>
 __device__ __forceinline__ void mask_part(int chunk0, int l, int N, float fill, float *v) {
     constexpr int VPC = E::VPC;
+    if constexpr (OPAQUE) {
+        int left = N - (chunk0 + l) * VPC;  // negative or zero: nothing of the row
+        asm volatile("" : "+v"(left));
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const int first = (chunk0 + i * R + l) * VPC;
+        for (int i = 0; i < C; ++i) {
 #pragma unroll
-        for (int e = 0; e < VPC; ++e)
-            if (first + e >= N) v[i * VPC + e] = fill;
+            for (int e = 0; e < VPC; ++e)
+                if (i * R * VPC + e >= left) v[i * VPC + e] = fill;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int first = (chunk0 + i * R + l) * VPC;
+#pragma unroll
+            for (int e = 0; e < VPC; ++e)
+                if (first + e >= N) v[i * VPC + e] = fill;
+        }
     }
 }
 
-template <class E, int C, int R, bool VEC>
+// BOUNDED: the buffer resource holds only this row (or this split-row member's part)
+// and ends where it ends, as in the persistent kernels; the hardware's range check
+// then drops the stores of chunks past it, and whole waves per row store every chunk
+// with no predicate.  Left to a per-chunk predicate in a row loop, the compiler hoists
+// the chunks' comparisons out of the loop and keeps their lane masks live (spilled
+// scalar registers).  Otherwise (block kernels, whose lane groups of fewer than 64
+// lanes share one buffer across rows) each chunk is stored only if it lies in the row.
+template <class E, int C, int R, bool VEC, bool BOUNDED = false>
 __device__ __forceinline__ void store_part(RowView rv, int chunk0, int l, int N, bool valid,
                                            bool full, const float *v) {
     constexpr int VPC = E::VPC;
     if constexpr (VEC) {
+        if constexpr (BOUNDED && R >= 64) {
+            if (valid) {
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
-            const int c = chunk0 + i * R + l;
-            if (valid && (full || c * VPC < N))
-                buf_store16(rv.buf, rv.base + (uint32_t)c * 16u, encode<E>(v + i * VPC));
+                for (int i = 0; i < C; ++i)
+                    buf_store16(rv.buf, rv.base + (uint32_t)(chunk0 + i * R + l) * 16u,
+                                encode<E>(v + i * VPC));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < C; ++i) {
+                const int c = chunk0 + i * R + l;
+                if (valid && (full || c * VPC < N))
+                    buf_store16(rv.buf, rv.base + (uint32_t)c * 16u, encode<E>(v + i * VPC));
+            }
         }
     } else {
         // As for the loads: whole chunks inside the row (and inside [0, N), the end of

@@ -173,12 +173,12 @@ struct SoftmaxOut {
 
 // Passes 1 and 2 on a lane's loaded part v of the row: the row max m (over this
 // workgroup's part), e = exp(x - m) in place and its sum s.
-template <class E, int P, int R, class Epi>
+template <class E, int P, int R, bool STREAM, class Epi>
 __device__ __forceinline__ MaxSum softmax_local(float *v, RowCtx &c, Epi &epi) {
     constexpr int C = P / E::VPC;
     const int chunk0 = c.chunk0;
     epi.template capture<E, C, R>(v, chunk0, c.l, c.nend);
-    if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.nend, -INFINITY, v);
+    if (!c.full) mask_part<E, C, R, STREAM>(chunk0, c.l, c.nend, -INFINITY, v);
 
     // pass 1: row max
     float m = tree_reduce<P>(v, OpMax{});
@@ -194,8 +194,10 @@ __device__ __forceinline__ MaxSum softmax_local(float *v, RowCtx &c, Epi &epi) {
 }
 
 // Pass 3: normalise with the row's (M, S) (for a split row, merged over its G
-// workgroups; `loc` is this workgroup's own pair), then the store.
-template <class E, int P, int R, int G, bool VEC, class Epi>
+// workgroups; `loc` is this workgroup's own pair), then the store.  STREAM: called
+// from a persistent kernel's row loop (row buffers that end with the part, masks
+// kept inside the loop; see store_part and mask_part).
+template <class E, int P, int R, int G, bool VEC, bool STREAM, class Epi>
 __device__ __forceinline__ void softmax_apply(float *v, RowView yv, bool valid, RowCtx &c,
                                               Epi &epi, MaxSum loc, float Mrow, float Srow) {
     constexpr int C = P / E::VPC;
@@ -206,20 +208,20 @@ __device__ __forceinline__ void softmax_apply(float *v, RowView yv, bool valid, 
     else
         scale = exp_shift(loc.m, safe_max(Mrow)) * __builtin_amdgcn_rcpf(Srow);
     epi.template apply<E, C, R>(v, scale, Mrow, Srow, chunk0, c, valid);
-    store_part<E, C, R, VEC>(yv, chunk0, c.l, c.nend, valid, c.full, v);
+    store_part<E, C, R, VEC, STREAM>(yv, chunk0, c.l, c.nend, valid, c.full, v);
 }
 
 // Passes 1-3 on a lane's loaded part v of the row, then the store.
-template <class E, int P, int R, int G, bool VEC, class Epi>
+template <class E, int P, int R, int G, bool VEC, bool STREAM, class Epi>
 __device__ __forceinline__ void softmax_finish(float *v, RowView yv, bool valid, RowCtx &c,
                                                Epi &epi) {
-    const MaxSum loc = softmax_local<E, P, R>(v, c, epi);
+    const MaxSum loc = softmax_local<E, P, R, STREAM>(v, c, epi);
     if constexpr (G == 1) {
-        softmax_apply<E, P, R, G, VEC>(v, yv, valid, c, epi, loc, loc.m, loc.s);
+        softmax_apply<E, P, R, G, VEC, STREAM>(v, yv, valid, c, epi, loc, loc.m, loc.s);
     } else {
         exchange_pairs<G>(c.g, c.member, c.it, loc.m, loc.s, c.spin_limit, c.bcast,
                           MergeMaxSum{});
-        softmax_apply<E, P, R, G, VEC>(v, yv, valid, c, epi, loc, c.bcast[0], c.bcast[1]);
+        softmax_apply<E, P, R, G, VEC, STREAM>(v, yv, valid, c, epi, loc, c.bcast[0], c.bcast[1]);
     }
 }
 
@@ -240,7 +242,8 @@ __global__ void __launch_bounds__(block_threads_for(R))
     float v[P];
     load_part<E, C, R, VEC>(block_row_view<R>(x, M, sub, row_bytes), 0, c.l, v);
     auto epi = out.row(valid ? row : M - 1);
-    softmax_finish<E, P, R, 1, VEC>(v, block_row_view<R>(y, M, sub, row_bytes), valid, c, epi);
+    softmax_finish<E, P, R, 1, VEC, false>(v, block_row_view<R>(y, M, sub, row_bytes), valid, c,
+                                           epi);
 }
 
 template <class E, int P, int R, int G, bool VEC, class Out = SoftmaxOut,
@@ -297,7 +300,7 @@ __global__ void __launch_bounds__(R)
             if (more) {
                 if constexpr (VEC) widen_part<E, C>(buf[K]);
                 epis[K] = out.epi(buf[K] + P, row);
-                cur = softmax_local<E, P, R>(buf[K], c, epis[K]);
+                cur = softmax_local<E, P, R, true>(buf[K], c, epis[K]);
                 publish_pair<G>(c.g, c.member, c.it, cur.m, cur.s);
             } else {
                 // no reduction (and its barriers) in this step: every wave has read
@@ -306,7 +309,7 @@ __global__ void __launch_bounds__(R)
             }
             if (c.it > 0) {  // complete the previous row
                 wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeMaxSum{});
-                softmax_apply<E, P, R, G, VEC>(buf[KP], stream_row_view(y, row - groups, M, rb, vb),
+                softmax_apply<E, P, R, G, VEC, true>(buf[KP], stream_row_view(y, row - groups, M, rb, vb),
                                                true, c, epis[KP], pend, c.bcast[0], c.bcast[1]);
             }
             pend = cur;
@@ -330,7 +333,8 @@ __global__ void __launch_bounds__(R)
             },
             [&](float *v, int64_t r) {
                 auto epi = out.epi(v + P, r);
-                softmax_finish<E, P, R, G, VEC>(v, stream_row_view(y, r, M, rb, vb), true, c, epi);
+                softmax_finish<E, P, R, G, VEC, true>(v, stream_row_view(y, r, M, rb, vb), true, c,
+                                                      epi);
                 ++c.it;
             });
     }
@@ -378,18 +382,18 @@ struct WeightLds {
 };
 
 // Sum of squares of this workgroup's part of the row.
-template <class E, int P, int R>
+template <class E, int P, int R, bool STREAM>
 __device__ __forceinline__ float rmsnorm_local(float *v, RowCtx &c) {
     constexpr int C = P / E::VPC;
     const int chunk0 = c.chunk0;
-    if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.nend, 0.0f, v);
+    if (!c.full) mask_part<E, C, R, STREAM>(chunk0, c.l, c.nend, 0.0f, v);
     const float q = tree_sum_squares<P>(v);
     return row_reduce<R>(q, c.one_reduction_slots(), c.l, OpSum{});
 }
 
 // y = (x * w) * r with r = rsqrt(Q / N + eps) for the row's sum of squares Q, then
 // the store.
-template <class E, int P, int R, bool VEC, class Weight>
+template <class E, int P, int R, bool VEC, bool STREAM, class Weight>
 __device__ __forceinline__ void rmsnorm_apply(float *v, const Weight &w, float Q, RowView yv,
                                               float *rstd_out, float eps, bool valid,
                                               const RowCtx &c) {
@@ -399,19 +403,19 @@ __device__ __forceinline__ void rmsnorm_apply(float *v, const Weight &w, float Q
     w.apply(v, c.l);
 #pragma unroll
     for (int j = 0; j < P; ++j) v[j] *= r;
-    store_part<E, C, R, VEC>(yv, chunk0, c.l, c.nend, valid, c.full, v);
+    store_part<E, C, R, VEC, STREAM>(yv, chunk0, c.l, c.nend, valid, c.full, v);
     if (rstd_out && valid && c.l == 0 && c.member == 0) *rstd_out = r;
 }
 
-template <class E, int P, int R, int G, bool VEC, class Weight>
+template <class E, int P, int R, int G, bool VEC, bool STREAM, class Weight>
 __device__ __forceinline__ void rmsnorm_finish(float *v, const Weight &w, RowView yv,
                                                float *rstd_out, float eps, bool valid, RowCtx &c) {
-    float q = rmsnorm_local<E, P, R>(v, c);
+    float q = rmsnorm_local<E, P, R, STREAM>(v, c);
     if constexpr (G > 1) {
         exchange_pairs<G>(c.g, c.member, c.it, q, 0.0f, c.spin_limit, c.bcast, MergeSum{});
         q = c.bcast[0];
     }
-    rmsnorm_apply<E, P, R, VEC>(v, w, q, yv, rstd_out, eps, valid, c);
+    rmsnorm_apply<E, P, R, VEC, STREAM>(v, w, q, yv, rstd_out, eps, valid, c);
 }
 
 template <class E, int P, int R, bool VEC>
@@ -432,7 +436,7 @@ __global__ void __launch_bounds__(block_threads_for(R))
     load_part<E, C, R, VEC>(block_row_view<R>(x, M, sub, row_bytes), 0, c.l, v);
     float wv[P];
     load_part<E, C, R, VEC, kReuseLoad>(RowView{make_buf(w, row_bytes), 0u, row_bytes}, 0, c.l, wv);
-    rmsnorm_finish<E, P, R, 1, VEC>(v, WeightRegs<P>{wv}, block_row_view<R>(y, M, sub, row_bytes),
+    rmsnorm_finish<E, P, R, 1, VEC, false>(v, WeightRegs<P>{wv}, block_row_view<R>(y, M, sub, row_bytes),
                                     rstd ? rstd + row : nullptr, eps, valid, c);
 }
 
@@ -487,7 +491,7 @@ __global__ void __launch_bounds__(R)
             const bool more = row < M;
             if (more) {
                 if constexpr (VEC) widen_part<E, C>(buf[K]);
-                const float q = rmsnorm_local<E, P, R>(buf[K], c);
+                const float q = rmsnorm_local<E, P, R, true>(buf[K], c);
                 publish_pair<G>(c.g, c.member, c.it, q, 0.0f);
             } else {
                 __syncthreads();  // as in the softmax kernel: the merged sum is read
@@ -495,7 +499,7 @@ __global__ void __launch_bounds__(R)
             if (c.it > 0) {  // complete the previous row
                 wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeSum{});
                 const int64_t rp = row - groups;
-                rmsnorm_apply<E, P, R, VEC>(buf[KP], wsrc, c.bcast[0],
+                rmsnorm_apply<E, P, R, VEC, true>(buf[KP], wsrc, c.bcast[0],
                                             stream_row_view(y, rp, M, rb, vb),
                                             rstd ? rstd + rp : nullptr, eps, true, c);
             }
@@ -515,7 +519,7 @@ __global__ void __launch_bounds__(R)
                 load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb, vb), chunk0, c.l, v);
             },
             [&](float *v, int64_t r) {
-                rmsnorm_finish<E, P, R, G, VEC>(v, wsrc, stream_row_view(y, r, M, rb, vb),
+                rmsnorm_finish<E, P, R, G, VEC, true>(v, wsrc, stream_row_view(y, r, M, rb, vb),
                                                 rstd ? rstd + r : nullptr, eps, true, c);
                 ++c.it;
             });

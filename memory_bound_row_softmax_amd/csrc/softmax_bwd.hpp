@@ -25,37 +25,44 @@
 
 namespace rr {
 
-// The row's dot product c over this workgroup's part (a: y, b: dy).
-template <class E, int P, int R>
+// The row's dot product c over this workgroup's part (a: y, b: dy).  Registers past
+// the row are zeroed in both operands where lane groups of fewer than 64 lanes share
+// one buffer resource: there they hold the next row's values, and an Inf or NaN in
+// them must not reach this row's sum through 0 * Inf.  (With a buffer per row or per
+// split-row part, loads past its end return 0.)
+template <class E, int P, int R, bool STREAM>
 __device__ __forceinline__ float softmax_bwd_local(float *a, float *b, RowCtx &c) {
     constexpr int C = P / E::VPC;
     const int chunk0 = c.chunk0;
-    if (!c.full) mask_part<E, C, R>(chunk0, c.l, c.nend, 0.0f, a);
+    if (!c.full) {
+        mask_part<E, C, R, STREAM>(chunk0, c.l, c.nend, 0.0f, a);
+        if constexpr (R < 64) mask_part<E, C, R, STREAM>(chunk0, c.l, c.nend, 0.0f, b);
+    }
     const float t = tree_dot<P>(a, b);
     return row_reduce<R>(t, c.one_reduction_slots(), c.l, OpSum{});
 }
 
 // dx = y * (dy - c) into a, then the store.
-template <class E, int P, int R, bool VEC>
+template <class E, int P, int R, bool VEC, bool STREAM>
 __device__ __forceinline__ void softmax_bwd_apply(float *a, const float *b, float t,
                                                   RowView dxv, bool valid, const RowCtx &c) {
     constexpr int C = P / E::VPC;
     const int chunk0 = c.chunk0;
 #pragma unroll
     for (int j = 0; j < P; ++j) a[j] = a[j] * (b[j] - t);
-    store_part<E, C, R, VEC>(dxv, chunk0, c.l, c.nend, valid, c.full, a);
+    store_part<E, C, R, VEC, STREAM>(dxv, chunk0, c.l, c.nend, valid, c.full, a);
 }
 
 // a: the lane's part of y, b: of dy; a becomes dx.
-template <class E, int P, int R, int G, bool VEC>
+template <class E, int P, int R, int G, bool VEC, bool STREAM>
 __device__ __forceinline__ void softmax_bwd_finish(float *a, float *b, RowView dxv, bool valid,
                                                    RowCtx &c) {
-    float t = softmax_bwd_local<E, P, R>(a, b, c);
+    float t = softmax_bwd_local<E, P, R, STREAM>(a, b, c);
     if constexpr (G > 1) {
         exchange_pairs<G>(c.g, c.member, c.it, t, 0.0f, c.spin_limit, c.bcast, MergeSum{});
         t = c.bcast[0];
     }
-    softmax_bwd_apply<E, P, R, VEC>(a, b, t, dxv, valid, c);
+    softmax_bwd_apply<E, P, R, VEC, STREAM>(a, b, t, dxv, valid, c);
 }
 
 template <class E, int P, int R, bool VEC>
@@ -73,7 +80,8 @@ __global__ void __launch_bounds__(block_threads_for(R))
     float a[P], b[P];
     load_part<E, C, R, VEC>(block_row_view<R>(y, M, sub, row_bytes), 0, c.l, a);
     load_part<E, C, R, VEC>(block_row_view<R>(dy, M, sub, row_bytes), 0, c.l, b);
-    softmax_bwd_finish<E, P, R, 1, VEC>(a, b, block_row_view<R>(dx, M, sub, row_bytes), valid, c);
+    softmax_bwd_finish<E, P, R, 1, VEC, false>(a, b, block_row_view<R>(dx, M, sub, row_bytes), valid,
+                                               c);
 }
 
 // Persistent stream kernel: each buffer holds a row of y (first P values) and of
@@ -125,14 +133,14 @@ __global__ void __launch_bounds__(R)
                     widen_part<E, C>(buf[K]);
                     widen_part<E, C>(buf[K] + P);
                 }
-                const float t = softmax_bwd_local<E, P, R>(buf[K], buf[K] + P, c);
+                const float t = softmax_bwd_local<E, P, R, true>(buf[K], buf[K] + P, c);
                 publish_pair<G>(c.g, c.member, c.it, t, 0.0f);
             } else {
                 __syncthreads();  // as in the softmax kernel: the merged c is read
             }
             if (c.it > 0) {  // complete the previous row
                 wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeSum{});
-                softmax_bwd_apply<E, P, R, VEC>(buf[KP], buf[KP] + P, c.bcast[0],
+                softmax_bwd_apply<E, P, R, VEC, true>(buf[KP], buf[KP] + P, c.bcast[0],
                                                 stream_row_view(dx, row - groups, M, rb, vb), true, c);
             }
             if (!more) return false;
@@ -152,7 +160,7 @@ __global__ void __launch_bounds__(R)
                 load_part<E, C, R, VEC>(stream_row_view(dy, r, M, rb, vb), chunk0, c.l, v + P);
             },
             [&](float *v, int64_t r) {
-                softmax_bwd_finish<E, P, R, G, VEC>(v, v + P, stream_row_view(dx, r, M, rb, vb), true,
+                softmax_bwd_finish<E, P, R, G, VEC, true>(v, v + P, stream_row_view(dx, r, M, rb, vb), true,
                                                     c);
                 ++c.it;
             });

@@ -2,7 +2,6 @@
 through the C ABI, bring the outputs back, and compare them with the oracle."""
 from __future__ import annotations
 
-import os
 import sys
 from contextlib import contextmanager
 
@@ -21,6 +20,21 @@ def say(*a):
     print("[gpu]", *a, file=sys.stderr, flush=True)
 
 
+def record(config: str, stats, **extra):
+    """Prints one accuracy line for a configuration, and appends it as JSON to the
+    file RR_PARITY_LOG names (if set); conftest.py turns that file into a table."""
+    import json
+    import os
+
+    d = {"config": config, **stats.as_dict(), **extra}
+    print("[parity]", json.dumps(d), file=sys.stderr, flush=True)
+    path = os.environ.get("RR_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(d) + "\n")
+    return stats
+
+
 def to_dev(a: np.ndarray, dtype: str) -> torch.Tensor:
     if dtype == "f32":
         return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
@@ -35,23 +49,12 @@ def from_dev(t: torch.Tensor) -> np.ndarray:
 
 @contextmanager
 def forced(P=None, R=None, G=None, spin=None, kind=None, groups=None):
-    """Test-only plan overrides (read by the library at every call)."""
-    keys = {"RR_FORCE_P": P, "RR_FORCE_R": R, "RR_FORCE_G": G, "RR_SPIN_LIMIT": spin,
-            "RR_FORCE_KIND": kind, "RR_FORCE_GROUPS": groups}
-    old = {k: os.environ.get(k) for k in keys}
+    """Test-only plan and launch overrides (rr_set_test_overrides), restored after."""
+    rr.set_test_overrides(kind=kind, P=P, R=R, G=G, groups=groups, spin=spin)
     try:
-        for k, v in keys.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = str(v)
         yield
     finally:
-        for k, v in old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
+        rr.set_test_overrides()
 
 
 def check_out(got: np.ndarray, ref: np.ndarray, dtype: str, what: str):

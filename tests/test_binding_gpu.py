@@ -62,3 +62,35 @@ def test_good_outputs_are_accepted():
     torch.cuda.synchronize()
     assert torch.allclose(y.sum(dim=1), torch.ones(M, device=DEV), atol=1e-5)
     assert bool((rstd > 0).all())
+
+
+def test_calls_on_a_stream_that_is_not_current():
+    """Outputs and the workspace the binding allocates are made in the launch
+    stream's order (so the zero fill precedes the kernel, and the memory is not handed
+    to other work while the kernel runs): split rows on a side stream, while the
+    current stream is busy, give the right rows and a clean status."""
+    import numpy as np
+
+    import oracle
+    import synth
+    from _gpu import from_dev
+
+    side = torch.cuda.Stream(device=DEV)
+    Mx, Nx = 48, 131072
+    assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, Mx, Nx, rr.RR_F32)["ws_bytes"] > 0
+    x_np = synth.normal(Mx, Nx, sigma=2.0)
+    x = torch.from_numpy(x_np).to(DEV)
+    torch.cuda.synchronize()
+    busy = torch.randn(4096, 4096, device=DEV)
+    for _ in range(4):
+        busy = busy @ busy  # keeps the current stream busy meanwhile
+        busy /= busy.norm()
+    outs = [rr.rr_softmax_fwd(x, stream=side) for _ in range(3)]
+    outs.append(rr.rr_softmax_fwd(x, stream=side.cuda_stream))  # raw handle
+    side.synchronize()
+    torch.cuda.synchronize()
+    ref = oracle.softmax(x_np[:8])
+    for y in outs:
+        got = from_dev(y)
+        assert np.all(np.abs(got[:8] - ref) <= 1e-5 * ref + 1e-37)
+        assert torch.equal(y, outs[0])

@@ -29,6 +29,9 @@ from _verify import check_f32, check_grad
 
 pytestmark = pytest.mark.gpu
 
+# launches of a determinism test, each compared with the first bit for bit
+REPEATS = 20
+
 DTYPES = ("f32", "bf16")
 SHAPES = [(256, 1024), (64, 1), (64, 3), (70, 255), (33, 257), (37, 1000), (16, 4095),
           (16, 4096), (9, 4097), (8, 16384), (5, 20000), (4, 65536), (3, 65537), (3, 131072),
@@ -150,7 +153,7 @@ def test_xent_grad_split_rows_are_deterministic(dtype):
     g = torch.from_numpy(_dloss(M)).to(DEV)
     ws = rr.workspace(rr.RR_OP_XENT_GRAD, M, N, code, DEV)
     outs = []
-    for i in range(3):
+    for i in range(REPEATS):
         say("xent grad split-row repeat", i, dtype)
         outs.append(rr.rr_cross_entropy_fwd_bwd(x, lab, g, ws=ws))
         torch.cuda.synchronize()
@@ -256,6 +259,36 @@ def test_softmax_bwd_special_rows(dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("N", [200, 13])
+def test_softmax_bwd_rows_do_not_see_the_next_rows_values(N, dtype):
+    """Block kernels whose lane groups hold less than a wave share one buffer across
+    the rows of a block, so the registers past a row's end hold the next row's
+    values.  An Inf or NaN in the next row's dy must not reach this row's dot product
+    (0 * Inf): every row without one is finite and matches the oracle."""
+    code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
+    M = 64
+    assert rr.rr_plan_query(rr.RR_OP_SOFTMAX_BWD, M, N, code)["lanes_per_row"] < 64
+    y, dy = softmax_bwd_inputs(M, N, dtype)
+    bad = np.arange(1, M, 4)  # the first element of every fourth row
+    inf = np.float32(np.inf) if dtype == "f32" else np.uint16(0x7F80)
+    nan = np.float32(np.nan) if dtype == "f32" else np.uint16(0x7FC0)
+    dy = dy.copy()
+    dy[bad[0::2], 0] = inf
+    dy[bad[1::2], 0] = nan
+    say("softmax bwd next-row Inf/NaN", dtype, M, N)
+    dx = from_dev(rr.rr_softmax_bwd(to_dev(y, dtype), to_dev(dy, dtype)))
+    torch.cuda.synchronize()
+    good = np.setdiff1d(np.arange(M), bad)
+    ref = oracle.softmax_backward(y[good], dy[good])
+    got = dx[good]
+    got64 = got.astype(np.float64) if dtype == "f32" else \
+        (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.isfinite(got64).all(), "a row picked up its neighbour's Inf or NaN"
+    check_grad(got, ref, softmax_bwd_scale(y[good], dy[good], dtype), dtype,
+               f"softmax bwd rows next to Inf/NaN {dtype} {M}x{N}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_softmax_bwd_split_rows_are_deterministic(dtype):
     M, N = 200, 262144
     code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
@@ -264,7 +297,7 @@ def test_softmax_bwd_split_rows_are_deterministic(dtype):
     y, dy = to_dev(y_np, dtype), to_dev(dy_np, dtype)
     ws = rr.workspace(rr.RR_OP_SOFTMAX_BWD, M, N, code, DEV)
     outs = []
-    for i in range(3):
+    for i in range(REPEATS):
         say("softmax bwd split-row repeat", i, dtype)
         outs.append(rr.rr_softmax_bwd(y, dy, ws=ws))
         torch.cuda.synchronize()
@@ -371,7 +404,7 @@ def test_rmsnorm_bwd_is_deterministic(dtype):
         r = torch.from_numpy(r_np).to(DEV)
         ws = rr.workspace(rr.RR_OP_RMSNORM_BWD, M, N, code, DEV)
         outs = []
-        for i in range(3):
+        for i in range(REPEATS):
             say("rmsnorm bwd repeat", i, dtype, M, N)
             outs.append(rr.rr_rmsnorm_bwd(x, w, dy, r, ws=ws))
             torch.cuda.synchronize()

@@ -23,6 +23,9 @@ from _verify import check_f32
 
 pytestmark = pytest.mark.gpu
 
+# launches of a determinism test, each compared with the first bit for bit
+REPEATS = 20
+
 DTYPES = ("f32", "bf16")
 # (M, N): every plan bucket, ragged tails, a few rows past a block boundary
 SHAPES = [(256, 1024), (64, 1), (64, 3), (70, 255), (64, 256), (33, 257), (37, 1000), (16, 2048),
@@ -314,7 +317,7 @@ def test_split_rows_are_deterministic_and_leave_the_workspace_zero(dtype):
     x = to_dev(_x(M, N, dtype, sigma=2.0), dtype)
     ws = rr.workspace(rr.RR_OP_SOFTMAX, M, N, code, DEV)
     outs = []
-    for i in range(3):
+    for i in range(REPEATS):
         say("split-row repeat", i, dtype)
         y = rr.rr_softmax_fwd(x, ws=ws)
         torch.cuda.synchronize()
@@ -327,26 +330,128 @@ def test_split_rows_are_deterministic_and_leave_the_workspace_zero(dtype):
     assert float((s - 1).abs().max()) < (1e-4 if dtype == "f32" else 2e-2)
 
 
-@pytest.mark.parametrize("N", [131072, 262144])
-def test_grid_wait_timeout_is_reported_not_hung(N):
-    """A spin limit of one poll makes split-row workgroups give up at once: the
-    kernel must still finish, report the timeout, and leave the workspace clean
-    (131072: the exchange inside a row's step; 262144: the deferred exchange)."""
-    M = 64
-    x = to_dev(_x(M, N, "f32"), "f32")
-    ws = rr.workspace(rr.RR_OP_SOFTMAX, M, N, rr.RR_F32, DEV)
-    say("forced grid timeout", N)
-    with forced(spin=1):
-        rr.rr_softmax_fwd(x, ws=ws)
+# Split-row calls for the timeout tests: (name, op, dtype, M, N, forced kind).  Each
+# takes a plan whose rows are split over several workgroups (or read twice by the
+# long-row kernel), with the exchange inside a row's step and deferred.
+TIMEOUT_CASES = [
+    ("softmax f32 G4", "softmax", "f32", 64, 131072, None),
+    ("softmax f32 G8 deferred", "softmax", "f32", 64, 262144, None),
+    ("softmax bf16 G4", "softmax", "bf16", 64, 262144, None),
+    ("rmsnorm f32 G16 deferred", "rmsnorm", "f32", 64, 262144, None),
+    ("rmsnorm bf16 packed G4", "rmsnorm", "bf16", 64, 262144, None),
+    ("xent_grad f32 G4", "xent_grad", "f32", 64, 131072, None),
+    ("softmax_bwd f32 G8 deferred", "softmax_bwd", "f32", 64, 262144, None),
+    ("rmsnorm_bwd f32 G4", "rmsnorm_bwd", "f32", 64, 65536, None),
+    ("long-row softmax", "softmax", "f32", 48, 70000, "long"),
+    ("long-row rmsnorm", "rmsnorm", "bf16", 48, 70000, "long"),
+]
+
+_OP_CODES = {"softmax": rr.RR_OP_SOFTMAX, "rmsnorm": rr.RR_OP_RMSNORM,
+             "xent_grad": rr.RR_OP_XENT_GRAD, "softmax_bwd": rr.RR_OP_SOFTMAX_BWD,
+             "rmsnorm_bwd": rr.RR_OP_RMSNORM_BWD}
+
+
+def _split_call(op, dtype, M, N, kind):
+    """Inputs and a launcher for one split-row call; the launcher returns the row
+    outputs as float64 arrays ([M, N] matrices and [M] vectors) and dw (or None)."""
+    code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
+    with forced(kind=kind):
+        plan = rr.rr_plan_query(_OP_CODES[op], M, N, code)
+    assert plan["path"] in (1, 4), plan
+    x_np = _x(M, N, dtype, sigma=2.0)
+    x = to_dev(x_np, dtype)
+    ws = rr.workspace(_OP_CODES[op], M, N, code, DEV)
+    w = to_dev(_w(N, dtype), dtype)
+    dy = to_dev(synth.normal(M, N, dtype=dtype, stream=synth.STREAM_DY), dtype)
+    lab = torch.from_numpy(synth.labels(M, N)).to(DEV)
+    g = torch.full((M,), 0.5, dtype=torch.float32, device=DEV)
+    rstd = torch.empty(M, dtype=torch.float32, device=DEV)
+    rr.rr_rmsnorm_fwd(x, w, 1e-6, rstd=rstd)
+    yfwd = rr.rr_softmax_fwd(x)
+    torch.cuda.synchronize()
+
+    def run(spin=None):
+        with forced(kind=kind, spin=spin):
+            if op == "softmax":
+                outs, dw = [rr.rr_softmax_fwd(x, ws=ws)], None
+            elif op == "rmsnorm":
+                r = torch.empty(M, dtype=torch.float32, device=DEV)
+                outs, dw = [rr.rr_rmsnorm_fwd(x, w, 1e-6, rstd=r, ws=ws), r], None
+            elif op == "xent_grad":
+                loss, lse, dx = rr.rr_cross_entropy_fwd_bwd(x, lab, g, ws=ws)
+                outs, dw = [dx, loss, lse], None
+            elif op == "softmax_bwd":
+                outs, dw = [rr.rr_softmax_bwd(yfwd, dy, ws=ws)], None
+            else:
+                dx, dw = rr.rr_rmsnorm_bwd(x, w, dy, rstd, ws=ws)
+                outs = [dx]
+        torch.cuda.synchronize()
+        return [o.double().cpu().numpy() for o in outs], dw
+
+    return ws, run
+
+
+def _exchange_area(ws, op, dtype, M, N):
+    """The part of a workspace that must be zero between launches: all of it, except
+    for the RMSNorm backward's dw partial rows at its end (scratch every call rewrites:
+    at most min(row blocks, 1024 / G) rows of N fp32, 256-byte aligned)."""
+    if op != "rmsnorm_bwd":
+        return ws
+    code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
+    p = rr.rr_plan_query(rr.RR_OP_RMSNORM_BWD, M, N, code)
+    blocks = -(-M // p["rows_per_block"])
+    parts = min(blocks, 1024 // p["groups_per_row"])
+    part_bytes = -(-parts * N * 4 // 256) * 256
+    return ws[:ws.numel() - part_bytes]
+
+
+@pytest.mark.parametrize("name,op,dtype,M,N,kind", TIMEOUT_CASES)
+def test_forced_timeout_gives_nan_rows_and_is_reported(name, op, dtype, M, N, kind):
+    """With every split-row wait forced to give up at once (spin limit -1, set from
+    the host), the kernel must still finish, write NaN for every value of every split
+    row (never a wrong number), report RR_ERR_GRID_TIMEOUT and leave the workspace
+    clean; a normal call afterwards gives the same bits as a call before."""
+    ws, run = _split_call(op, dtype, M, N, kind)
+    say("reference call", name)
+    ref, ref_dw = run()
+    assert rr.rr_workspace_check(ws) == rr.RR_OK
+    say("forced timeout", name)
+    outs, dw = run(spin=-1)
+    assert rr.rr_workspace_check(ws) == rr.RR_ERR_GRID_TIMEOUT
+    # error word cleared by the check, slots by the kernel
+    assert int(_exchange_area(ws, op, dtype, M, N).count_nonzero()) == 0
+    for o in outs:
+        assert np.isnan(o).all(), f"{name}: a timed-out split row holds a non-NaN value"
+    if dw is not None:  # dw does not depend on the exchange
+        assert torch.equal(dw, ref_dw)
+    say("after timeout", name)
+    again, _ = run()
+    assert rr.rr_workspace_check(ws) == rr.RR_OK
+    for a, b in zip(again, ref):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("name,op,dtype,M,N,kind", TIMEOUT_CASES[:2] + TIMEOUT_CASES[5:8])
+def test_one_poll_waits_never_give_silent_garbage(name, op, dtype, M, N, kind):
+    """With a spin limit of one poll, some waits may give up and others succeed.
+    Every row must then be either exactly the normal result or hold NaN, and a row
+    with NaN must come with RR_ERR_GRID_TIMEOUT."""
+    ws, run = _split_call(op, dtype, M, N, kind)
+    say("reference call", name)
+    ref, _ = run()
+    say("one-poll waits", name)
+    outs, _ = run(spin=1)
     st = rr.rr_workspace_check(ws)
     assert st in (rr.RR_OK, rr.RR_ERR_GRID_TIMEOUT)
-    assert int(ws.count_nonzero()) == 0  # error word cleared by the check, slots by the kernel
-    # a normal launch afterwards is correct again
-    say("after timeout")
-    y = rr.rr_softmax_fwd(x, ws=ws)
-    torch.cuda.synchronize()
-    check_f32(y[:4].cpu().numpy(), oracle.softmax(from_dev(x)[:4]), "after timeout")
-    assert rr.rr_workspace_check(ws) == rr.RR_OK
+    assert int(_exchange_area(ws, op, dtype, M, N).count_nonzero()) == 0
+    any_nan = False
+    for o, r in zip(outs, ref):
+        rows_nan = np.isnan(o).reshape(M, -1).any(axis=1)
+        any_nan |= bool(rows_nan.any())
+        ok = rows_nan | (o == r).reshape(M, -1).all(axis=1)
+        assert ok.all(), f"{name}: rows {np.flatnonzero(~ok)[:5]} differ without NaN"
+    if any_nan:
+        assert st == rr.RR_ERR_GRID_TIMEOUT
 
 
 OVERSUBSCRIBED = [  # (op, dtype, M, N): row groups forced to M, far more than fit at once
@@ -492,7 +597,7 @@ def test_long_rows_many_rows_deterministic(dtype, kind):
     outs = []
     with forced(kind=kind):
         ws = rr.workspace(rr.RR_OP_SOFTMAX, M, N, code, DEV)
-        for i in range(3):
+        for i in range(REPEATS):
             say("long rows repeat", kind, i, dtype)
             outs.append(rr.rr_softmax_fwd(x, ws=ws))
             torch.cuda.synchronize()

@@ -2,8 +2,6 @@
 a compiled configuration that holds the row, the grid path appears only past
 one workgroup's capacity, workspace sizes follow the documented layout, and the
 test-only overrides reach every path."""
-import os
-
 import pytest
 
 import memory_bound_row_softmax_amd as rr
@@ -128,10 +126,10 @@ def test_cross_entropy_streams(dt):
         assert p["vals_per_lane"] in (16, 32) and 16 <= p["lanes_per_row"] <= (512 if dt else 256)
 
 
-def test_forced_configurations(monkeypatch):
-    monkeypatch.setenv("RR_FORCE_P", "64")
-    monkeypatch.setenv("RR_FORCE_R", "256")
-    monkeypatch.setenv("RR_FORCE_G", "4")
+def test_forced_configurations(overrides):
+    overrides.set(P=64)
+    overrides.set(R=256)
+    overrides.set(G=4)
     p = rr.rr_plan_query(rr.RR_OP_SOFTMAX, 50, 3000, rr.RR_F32)
     assert (p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"], p["path"]) == (64, 256, 4, 1)
     assert p["ws_bytes"] == 256 + 50 * (64 + 64 * 4)
@@ -139,28 +137,28 @@ def test_forced_configurations(monkeypatch):
     with pytest.raises(rr.RRError):
         rr.rr_plan_query(rr.RR_OP_SOFTMAX, 50, 70000, rr.RR_F32)
     # a stream kernel with one workgroup per row
-    monkeypatch.setenv("RR_FORCE_KIND", "stream")
-    monkeypatch.setenv("RR_FORCE_G", "1")
+    overrides.set(kind="stream")
+    overrides.set(G=1)
     p = rr.rr_plan_query(rr.RR_OP_RMSNORM, 50, 3000, rr.RR_BF16)
     assert (p["path"], p["groups_per_row"], p["block_threads"], p["ws_bytes"]) == (3, 1, 256, 0)
     # not compiled for RMSNorm (would not fit in registers): 64 values x 1024 lanes
-    monkeypatch.setenv("RR_FORCE_KIND", "block")
-    monkeypatch.setenv("RR_FORCE_R", "1024")
+    overrides.set(kind="block")
+    overrides.set(R=1024)
     with pytest.raises(rr.RRError):
         rr.rr_plan_query(rr.RR_OP_RMSNORM, 50, 3000, rr.RR_F32)
     # no block kernel splits a row
-    monkeypatch.setenv("RR_FORCE_G", "2")
+    overrides.set(G=2)
     with pytest.raises(rr.RRError):
         rr.rr_plan_query(rr.RR_OP_SOFTMAX, 50, 3000, rr.RR_F32)
-    monkeypatch.delenv("RR_FORCE_KIND")
-    monkeypatch.delenv("RR_FORCE_G")
-    monkeypatch.setenv("RR_FORCE_P", "16")
-    monkeypatch.setenv("RR_FORCE_R", "64")
+    overrides.set(kind=None)
+    overrides.set(G=None)
+    overrides.set(P=16)
+    overrides.set(R=64)
     p = rr.rr_plan_query(rr.RR_OP_XENT, 50, 3000, rr.RR_F32)
     assert (p["vals_per_lane"], p["lanes_per_row"]) == (16, 64)
 
 
-def test_short_unaligned_rows_take_small_lane_groups(monkeypatch):
+def test_short_unaligned_rows_take_small_lane_groups(overrides):
     """Unaligned bf16 rows shorter than 16 bytes are read element by element, which
     only lane groups of fewer than 64 lanes compile: default plans use those (for
     fp32 too), and forced bf16 plans with whole waves per row are refused."""
@@ -171,14 +169,14 @@ def test_short_unaligned_rows_take_small_lane_groups(monkeypatch):
             for op in ops:
                 p = rr.rr_plan_query(op, 100, N, dt, False)
                 assert p["lanes_per_row"] < 64, (op, N, dt, p)
-    monkeypatch.setenv("RR_FORCE_KIND", "long")
+    overrides.set(kind="long")
     with pytest.raises(rr.RRError):
         rr.rr_plan_query(rr.RR_OP_SOFTMAX, 70, 7, rr.RR_BF16, False)
     assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 70, 9, rr.RR_BF16, False)["path"] == 4
     assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 70, 3, rr.RR_F32, False)["path"] == 4
-    monkeypatch.setenv("RR_FORCE_KIND", "stream")
-    monkeypatch.setenv("RR_FORCE_P", "16")
-    monkeypatch.setenv("RR_FORCE_R", "1024")
+    overrides.set(kind="stream")
+    overrides.set(P=16)
+    overrides.set(R=1024)
     with pytest.raises(rr.RRError):
         rr.rr_plan_query(rr.RR_OP_RMSNORM, 70, 7, rr.RR_BF16, False)
     assert rr.rr_plan_query(rr.RR_OP_RMSNORM, 70, 9, rr.RR_BF16, False)["lanes_per_row"] == 1024
@@ -244,7 +242,7 @@ def test_rmsnorm_bwd_plans(dt, vec):
     assert p["ws_bytes"] >= blocks * 4096 * 4 and p["ws_bytes"] < 16 * 4096 * 4
 
 
-def test_long_rows_take_the_two_pass_kernel(monkeypatch):
+def test_long_rows_take_the_two_pass_kernel(overrides):
     for op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
         for dt in (rr.RR_F32, rr.RR_BF16):
             for n in (1 << 20, 1 << 21, 1 << 22):
@@ -271,7 +269,7 @@ def test_long_rows_take_the_two_pass_kernel(monkeypatch):
             assert rr.rr_plan_query(op, 10, 262144, dt, False)["path"] == 1
             q = rr.rr_plan_query(op, 10, 262145, dt, False)
             assert q["path"] == 4 and q["vals_per_lane"] == 16
-    monkeypatch.setenv("RR_FORCE_KIND", "long")
+    overrides.set(kind="long")
     assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 8, 1000, rr.RR_F32)["path"] == 4
     # the other ops have no long-row kernel
     with pytest.raises(rr.RRError):

@@ -15,11 +15,13 @@ Printed: one JSON line with
              per launch (null if the kernel sources changed since the counters were
              taken)
   cpu_baseline  the double-precision CPU oracle on a bounded sample of the same workload
-  copy_ceiling  a 128-bit streaming copy of the same bytes in the same run
+  copy_ceiling  a 128-bit streaming copy of the same bytes in the same run, and beside it
+             a read-only stream of the input bytes and a write-only stream of the output
+             bytes (the kernel's reads and writes each at the rate HBM gives them alone)
 Algorithmic bytes: softmax M*N*(s_in + s_out); RMSNorm M*N*(s_in + s_out) + N*s;
 cross-entropy M*N*s + 12*M (labels in, loss and lse out).
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--sweep]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--sweep] [--ceiling]
 """
 from __future__ import annotations
 
@@ -177,6 +179,7 @@ class Runner:
         if w.op in ("softmax_bwd", "rmsnorm_bwd"):
             self.dyp = [t.data_ptr() for t in self.dy]
         self.copy_dst = None
+        self.sink = None
 
     def launch(self, k: int) -> int:
         w, rr, i = self.w, self.rr, k % self.sets
@@ -199,6 +202,20 @@ class Runner:
                                                 self.wsp, self.wsb, self.sp)
         return rr.cross_entropy_fwd_raw(self.xp[i], self.labp, self.lp[i], self.ep[i], w.M, w.N,
                                         self.dt, self.wsp, self.wsb, self.sp)
+
+    def read_launch(self, k: int) -> int:
+        src = self.x[k % self.sets]
+        nbytes = src.numel() * src.element_size()
+        if self.sink is None:
+            self.sink = self.torch.empty(self.rr.stream_read_sink_bytes(nbytes) // 4,
+                                         dtype=self.torch.int32, device=self.dev)
+        return self.rr.stream_read_raw(src.data_ptr(), nbytes, self.sink.data_ptr(),
+                                       self.sink.numel() * 4, self.sp)
+
+    def write_launch(self, k: int) -> int:
+        dst = self.y[k % self.sets] if self.w.op != "xent" else self.x[k % self.sets]
+        return self.rr.stream_fill_raw(dst.data_ptr(), dst.numel() * dst.element_size(), k,
+                                       self.sp)
 
     def copy_launch(self, k: int) -> int:
         i = k % self.sets
@@ -350,6 +367,13 @@ def measure(w, steps: int, warmup: int, min_rotation_bytes: float, with_cpu: boo
     nbytes = algorithmic_bytes(w)
     wall, mean_ms = r.time(r.launch, steps, warmup, graph)
     copy_wall, copy_mean_ms = r.time(r.copy_launch, steps, warmup, graph)
+    _, read_mean_ms = r.time(r.read_launch, steps, warmup, graph)
+    in_bytes = r.x[0].numel() * r.x[0].element_size()
+    out_bytes = in_bytes if w.op != "xent" else in_bytes  # xent: the fill writes x's size
+    if w.op != "xent":
+        _, write_mean_ms = r.time(r.write_launch, steps, warmup, graph)
+    else:
+        write_mean_ms = None  # cross-entropy writes 12 bytes per row
     copy_bytes = 2 * r.x[0].numel() * r.x[0].element_size()
     achieved = nbytes / (mean_ms * 1e-3) / 1e9
     traffic, rec = traffic_for(w.name)
@@ -377,7 +401,10 @@ def measure(w, steps: int, warmup: int, min_rotation_bytes: float, with_cpu: boo
                      "algorithmic_bytes": nbytes},
         "copy_ceiling": {"value": round(copy_gbps, 2), "unit": "GB/s",
                          "frac": round(copy_gbps / HBM_PEAK_GBPS, 4),
-                         "kernel_vs_copy": round(achieved / copy_gbps, 4)},
+                         "kernel_vs_copy": round(achieved / copy_gbps, 4),
+                         "read_only": round(in_bytes / (read_mean_ms * 1e-3) / 1e9, 2),
+                         "write_only": (round(out_bytes / (write_mean_ms * 1e-3) / 1e9, 2)
+                                        if write_mean_ms else None)},
     }
     if rec is not None:
         line["roofline"]["traffic_source"] = rec.get("summary")
@@ -388,6 +415,59 @@ def measure(w, steps: int, warmup: int, min_rotation_bytes: float, with_cpu: boo
 
     torch.cuda.empty_cache()
     return line
+
+
+def ceiling(steps: int, out=None) -> int:
+    """HBM ceilings of this GPU: the library's 128-bit copy (one read and one write per
+    byte), read-only and write-only streams, each timed over `steps` launches with HIP
+    events, on footprints from 256 MiB to 16 GiB each way (sets rotate up to 4 GiB so
+    that launches read cold data)."""
+    import torch
+
+    import memory_bound_row_softmax_amd as rr
+
+    dev = "cuda:0"
+    stream = torch.cuda.Stream(device=dev)
+    sp = stream.cuda_stream
+    for size in (256 << 20, 1 << 30, 4 << 30, 16 << 30):
+        sets = max(1, (4 << 30) // (2 * size))
+        bufs = [(torch.empty(size, dtype=torch.uint8, device=dev),
+                 torch.empty(size, dtype=torch.uint8, device=dev)) for _ in range(sets)]
+        for a, b in bufs:
+            a.fill_(0x5A)
+        sink = torch.empty(rr.stream_read_sink_bytes(size) // 4, dtype=torch.int32, device=dev)
+        kinds = {
+            "copy": (2, lambda k: rr.stream_copy_raw(bufs[k % sets][0].data_ptr(),
+                                                     bufs[k % sets][1].data_ptr(), size, sp)),
+            "read": (1, lambda k: rr.stream_read_raw(bufs[k % sets][0].data_ptr(), size,
+                                                     sink.data_ptr(), sink.numel() * 4, sp)),
+            "write": (1, lambda k: rr.stream_fill_raw(bufs[k % sets][1].data_ptr(), size, k, sp)),
+        }
+        line = {"bytes_each_way": size, "unit": "GB/s"}
+        with torch.cuda.stream(stream):
+            for name, (ways, fn) in kinds.items():
+                for k in range(3):
+                    if fn(k) != 0:
+                        raise RuntimeError(f"{name} launch failed")
+                start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                start.record(stream)
+                bad = 0
+                for k in range(steps):
+                    bad |= fn(k)
+                end.record(stream)
+                torch.cuda.synchronize()
+                if bad:
+                    raise RuntimeError(f"{name} launch failed")
+                ms = start.elapsed_time(end) / steps
+                line[name] = round(ways * size / (ms * 1e-3) / 1e9, 1)
+        print(json.dumps(line), flush=True)
+        if out:
+            with open(out, "a") as f:
+                f.write(json.dumps(line) + "\n")
+        del bufs, sink
+        torch.cuda.empty_cache()
+    return 0
 
 
 def main() -> int:
@@ -406,6 +486,9 @@ def main() -> int:
                     help="sweep only: rows generated on the host, repeated down the matrix")
     ap.add_argument("--only", default="",
                     help="sweep only: comma-separated substrings a workload name must contain")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="time the copy, read-only and write-only streams at 256 MiB, 1 GiB, "
+                         "4 GiB and 16 GiB (one JSON line each)")
     ap.add_argument("--graph", action="store_true",
                     help="time one replay of a HIP graph of the steps (kernel and copy) "
                          "instead of launches from the host")
@@ -418,6 +501,8 @@ def main() -> int:
 
     from synth import workloads as W
 
+    if args.ceiling:
+        return ceiling(args.steps, args.out if args.out != "bench_sweep.jsonl" else None)
     if args.sweep:
         os.makedirs(os.path.dirname(args.out) or ".", exist_ok=True)
         done = set()

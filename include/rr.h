@@ -206,11 +206,27 @@ rr_status rr_plan_query(rr_op op, int64_t M, int64_t N, rr_dtype dt, int vectori
                         rr_plan_info *out);
 
 /*
- * 128-bit streaming copy of `bytes` bytes (a multiple of 16, 16-byte aligned pointers):
- * the same-run HBM ceiling the three kernels are compared with.  Not one of the pages'
- * operators; a measurement aid.
+ * Streaming ceilings, measured in the same run as the kernels they are compared with
+ * ([QuACK] sections NCU 性能分析（Softmax 内核） and 内存吞吐量 report each kernel's DRAM
+ * throughput as a share of what the memory delivers).  Not operators of the pages;
+ * measurement aids.  Each moves every byte once, 16 bytes per lane per access, with
+ * the row kernels' non-temporal cache policies, and assigns the blocks of every
+ * 128 KiB region to the eight XCDs so that each XCD's accesses share address bits
+ * 12..14 (the mapping measured fastest for one read plus one write per byte).
+ * `bytes` is a multiple of 16 and the data pointers are 16-byte aligned; otherwise
+ * RR_ERR_INVALID_ARGUMENT.  Stream-ordered like the operators.
+ *
+ * rr_stream_copy: copies src to dst (no overlap; one read and one write per byte).
+ * rr_stream_read: reads src and writes one 32-bit XOR checksum per 16 KiB to `sink`
+ *   (4-byte aligned, at least rr_stream_read_sink_bytes(bytes) bytes, no overlap
+ *   with src), so the reads cannot be dropped.
+ * rr_stream_fill: writes the 32-bit `value` over dst (one write per byte).
  */
 rr_status rr_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
+size_t rr_stream_read_sink_bytes(size_t bytes);
+rr_status rr_stream_read(const void *src, size_t bytes, void *sink, size_t sink_bytes,
+                         hipStream_t stream);
+rr_status rr_stream_fill(void *dst, size_t bytes, uint32_t value, hipStream_t stream);
 
 /*
  * Test-only: forces plan and launch choices for every later call in the process, so

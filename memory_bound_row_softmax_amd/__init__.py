@@ -31,7 +31,8 @@ RR_F32, RR_BF16 = 0, 1
 
 EXPORTS = ("rr_softmax_fwd", "rr_rmsnorm_fwd", "rr_cross_entropy_fwd",
            "rr_cross_entropy_fwd_bwd", "rr_softmax_bwd", "rr_rmsnorm_bwd", "rr_workspace_bytes",
-           "rr_workspace_check", "rr_plan_query", "rr_stream_copy", "rr_set_test_overrides",
+           "rr_workspace_check", "rr_plan_query", "rr_stream_copy", "rr_stream_read_sink_bytes",
+           "rr_stream_read", "rr_stream_fill", "rr_set_test_overrides",
            "rr_status_string", "rr_last_hip_error")
 
 
@@ -60,13 +61,24 @@ _lib = None
 
 
 def lib():
-    """The loaded librr (raises if it is not built)."""
+    """The loaded librr (raises if it is not built).
+
+    PyTorch, when it is installed, is imported first.  Its HIP runtime then serves
+    librr too: both carry the soname libamdhip64.so.7, so the dynamic linker resolves
+    librr's dependency to the copy already loaded.  Loaded the other way round, librr
+    would bring in the system's runtime and torch would still load its own (it names
+    the file libamdhip64.so), and torch's memory and streams would reach kernels
+    launched through the other runtime."""
     global _lib
     with _lock:
         if _lib is None:
             if not os.path.exists(LIB_PATH):
                 raise RuntimeError(f"{LIB_PATH} is not built; run "
                                    "`python -m memory_bound_row_softmax_amd.build`")
+            try:
+                import torch  # noqa: F401  (see above)
+            except ImportError:
+                pass
             L = ctypes.CDLL(LIB_PATH)
             vp, i64, sz, ci, st = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t,
                                    ctypes.c_int, ctypes.c_int)
@@ -82,6 +94,10 @@ def lib():
             L.rr_workspace_check.argtypes = [vp, sz, vp]
             L.rr_plan_query.argtypes = [ci, i64, i64, ci, ci, ctypes.POINTER(PlanInfo)]
             L.rr_stream_copy.argtypes = [vp, vp, sz, vp]
+            L.rr_stream_read_sink_bytes.argtypes = [sz]
+            L.rr_stream_read_sink_bytes.restype = sz
+            L.rr_stream_read.argtypes = [vp, sz, vp, sz, vp]
+            L.rr_stream_fill.argtypes = [vp, sz, ctypes.c_uint32, vp]
             L.rr_set_test_overrides.argtypes = [ctypes.POINTER(TestOverrides)]
             L.rr_status_string.argtypes = [ci]
             L.rr_status_string.restype = ctypes.c_char_p
@@ -89,7 +105,8 @@ def lib():
             for f in (L.rr_softmax_fwd, L.rr_rmsnorm_fwd, L.rr_cross_entropy_fwd,
                       L.rr_cross_entropy_fwd_bwd, L.rr_softmax_bwd, L.rr_rmsnorm_bwd,
                       L.rr_workspace_check, L.rr_plan_query, L.rr_stream_copy,
-                      L.rr_set_test_overrides, L.rr_last_hip_error):
+                      L.rr_stream_read, L.rr_stream_fill, L.rr_set_test_overrides,
+                      L.rr_last_hip_error):
                 f.restype = st
             _lib = L
     return _lib
@@ -139,6 +156,18 @@ def rmsnorm_bwd_raw(x, w, dy, rstd, dx, dw, M, N, dt, ws=0, ws_bytes=0, stream=0
 
 def stream_copy_raw(src, dst, nbytes, stream=0) -> int:
     return lib().rr_stream_copy(src, dst, nbytes, stream or None)
+
+
+def stream_read_sink_bytes(nbytes) -> int:
+    return int(lib().rr_stream_read_sink_bytes(nbytes))
+
+
+def stream_read_raw(src, nbytes, sink, sink_bytes, stream=0) -> int:
+    return lib().rr_stream_read(src, nbytes, sink, sink_bytes, stream or None)
+
+
+def stream_fill_raw(dst, nbytes, value, stream=0) -> int:
+    return lib().rr_stream_fill(dst, nbytes, value & 0xFFFFFFFF, stream or None)
 
 
 # --------------------------------------------------------------- torch tensors

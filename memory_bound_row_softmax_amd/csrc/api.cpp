@@ -326,6 +326,31 @@ rr_status rr_set_test_overrides(const rr_test_overrides *o) {
     return RR_OK;
 }
 
+size_t rr_stream_read_sink_bytes(size_t bytes) { return rr::stream_read_sink_bytes(bytes); }
+
+rr_status rr_stream_read(const void *src, size_t bytes, void *sink, size_t sink_bytes,
+                         hipStream_t stream) {
+    if (!src || !sink || bytes % 16 != 0 || !aligned16(src) ||
+        (reinterpret_cast<uintptr_t>(sink) & 3u) != 0)
+        return RR_ERR_INVALID_ARGUMENT;
+    if (bytes == 0) return RR_OK;
+    const size_t need = rr::stream_read_sink_bytes(bytes);
+    if (sink_bytes < need || overlap(src, bytes, sink, need)) return RR_ERR_INVALID_ARGUMENT;
+    rr::LaunchArgs a;
+    rr_status st = launch_args(stream, &a);
+    if (st != RR_OK) return st;
+    return hip_status(rr::launch_read(src, bytes, static_cast<uint32_t *>(sink), a));
+}
+
+rr_status rr_stream_fill(void *dst, size_t bytes, uint32_t value, hipStream_t stream) {
+    if (!dst || bytes % 16 != 0 || !aligned16(dst)) return RR_ERR_INVALID_ARGUMENT;
+    if (bytes == 0) return RR_OK;
+    rr::LaunchArgs a;
+    rr_status st = launch_args(stream, &a);
+    if (st != RR_OK) return st;
+    return hip_status(rr::launch_fill(dst, bytes, value, a));
+}
+
 const char *rr_status_string(rr_status status) {
     switch (status) {
     case RR_OK: return "RR_OK";

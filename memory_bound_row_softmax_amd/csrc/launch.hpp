@@ -37,5 +37,9 @@ hipError_t launch_long_row(const Plan &p, int op, int dtype, const void *x, cons
 hipError_t launch_rmsnorm_packed(const Plan &p, const void *x, const void *w, void *y, float *rstd,
                                  int64_t M, int64_t N, float eps, void *ws, const LaunchArgs &a);
 hipError_t launch_copy(const void *src, void *dst, size_t bytes, const LaunchArgs &a);
+hipError_t launch_read(const void *src, size_t bytes, uint32_t *sink, const LaunchArgs &a);
+hipError_t launch_fill(void *dst, size_t bytes, uint32_t value, const LaunchArgs &a);
+// Bytes of the per-block checksums launch_read writes for `bytes` of input.
+size_t stream_read_sink_bytes(size_t bytes);
 
 }  // namespace rr

@@ -357,10 +357,10 @@ def _split_call(op, dtype, M, N, kind):
     code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
     with forced(kind=kind):
         plan = rr.rr_plan_query(_OP_CODES[op], M, N, code)
+        ws = rr.workspace(_OP_CODES[op], M, N, code, DEV)
     assert plan["path"] in (1, 4), plan
     x_np = _x(M, N, dtype, sigma=2.0)
     x = to_dev(x_np, dtype)
-    ws = rr.workspace(_OP_CODES[op], M, N, code, DEV)
     w = to_dev(_w(N, dtype), dtype)
     dy = to_dev(synth.normal(M, N, dtype=dtype, stream=synth.STREAM_DY), dtype)
     lab = torch.from_numpy(synth.labels(M, N)).to(DEV)
@@ -393,16 +393,20 @@ def _split_call(op, dtype, M, N, kind):
 
 def _exchange_area(ws, op, dtype, M, N):
     """The part of a workspace that must be zero between launches: all of it, except
-    for the RMSNorm backward's dw partial rows at its end (scratch every call rewrites:
-    at most min(row blocks, 1024 / G) rows of N fp32, 256-byte aligned)."""
+    for the RMSNorm backward's dw partial rows (scratch every call rewrites), which
+    follow the header and the exchange area of its 128-bit plan: 256 bytes, then for
+    split rows min(parts, 1024) records of 64 + 64 G bytes, parts = min(row blocks,
+    1024 / G), rounded up to 256 bytes."""
     if op != "rmsnorm_bwd":
         return ws
     code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
     p = rr.rr_plan_query(rr.RR_OP_RMSNORM_BWD, M, N, code)
-    blocks = -(-M // p["rows_per_block"])
-    parts = min(blocks, 1024 // p["groups_per_row"])
-    part_bytes = -(-parts * N * 4 // 256) * 256
-    return ws[:ws.numel() - part_bytes]
+    G = p["groups_per_row"]
+    if G == 1:
+        return ws[:256]
+    parts = min(-(-M // p["rows_per_block"]), 1024 // G)
+    exch = 256 + min(parts, 1024) * (64 + 64 * G)
+    return ws[:-(-exch // 256) * 256]
 
 
 @pytest.mark.parametrize("name,op,dtype,M,N,kind", TIMEOUT_CASES)
@@ -495,7 +499,39 @@ def test_split_rows_drain_when_the_grid_does_not_fit(op, dtype, M, N):
     check_out(from_dev(y), ref, dtype, f"oversubscribed {op} {dtype} {M}x{N}")
 
 
-def test_stream_copy():
+@pytest.mark.parametrize("nbytes", [16, 1024 + 16, 3 * 131072 + 4096 + 32, 1 << 22,
+                                    (1 << 32) + 48])
+def test_streams(nbytes):
+    """The copy, read and fill streams (the bench's ceilings) move exactly `nbytes`,
+    including a partial last region and offsets past 32 bits: the copy is exact and
+    leaves the bytes after it alone, the read's checksums XOR to the data's, and the
+    fill writes the pattern and nothing after it."""
+    say("streams", nbytes)
+    n32 = nbytes // 4
+    a = torch.randint(-2**31, 2**31 - 1, (n32 + 64,), dtype=torch.int32, device=DEV)
+    b = torch.zeros_like(a)
+    sp = torch.cuda.current_stream().cuda_stream
+    assert rr.stream_copy_raw(a.data_ptr(), b.data_ptr(), nbytes, sp) == rr.RR_OK
+    sink = torch.zeros(rr.stream_read_sink_bytes(nbytes) // 4, dtype=torch.int32, device=DEV)
+    assert rr.stream_read_raw(a.data_ptr(), nbytes, sink.data_ptr(), sink.numel() * 4, sp) == 0
+    c = torch.zeros_like(a)
+    assert rr.stream_fill_raw(c.data_ptr(), nbytes, 0x1234ABCD, sp) == rr.RR_OK
+    torch.cuda.synchronize()
+    assert torch.equal(a[:n32], b[:n32]) and int(b[n32:].count_nonzero()) == 0
+    def xor_all(t):
+        t = t.to(torch.int64) & 0xFFFFFFFF
+        while t.numel() > 1:
+            if t.numel() % 2:
+                t = torch.cat([t, torch.zeros(1, dtype=t.dtype, device=t.device)])
+            t = t[0::2] ^ t[1::2]
+        return int(t[0])
+    assert xor_all(sink) == xor_all(a[:n32])
+    assert bool((c[:n32] == 0x1234ABCD).all()) and int(c[n32:].count_nonzero()) == 0
+    del a, b, c
+    torch.cuda.empty_cache()
+
+
+def test_stream_copy_binding():
     say("stream copy")
     a = torch.randn(1 << 20, device=DEV)
     b = torch.empty_like(a)

@@ -93,6 +93,24 @@ rr_status rr_softmax_fwd(const void *x, void *y, int64_t M, int64_t N, rr_dtype 
                          size_t ws_bytes, hipStream_t stream);
 
 /*
+ * rr_softmax_fwd without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): rows split over several workgroups use a buffer the library holds on
+ * each GPU, a device array of RR_STATIC_SCRATCH_BYTES (8 MiB + 256 KiB, enough for
+ * every softmax plan) kept until the process ends.  The call allocates nothing; its
+ * first call on a device looks the array's address up with hipGetSymbolAddress (not
+ * an allocation).  Same arguments, results, plans and kernels as rr_softmax_fwd (the
+ * same bits).  Calls on one GPU share the array: calls that may overlap on one GPU
+ * (other streams, other threads) race and must not be made.  A wait that gives up is
+ * seen as NaN rows (there is no workspace to check).  Returns RR_ERR_WORKSPACE if a
+ * plan would need more than the array holds (no softmax plan does), RR_ERR_HIP if the
+ * address lookup fails; otherwise as rr_softmax_fwd.
+ */
+#define RR_STATIC_SCRATCH_BYTES (8388608u + 262144u)
+rr_status rr_softmax_fwd_static(const void *x, void *y, int64_t M, int64_t N, rr_dtype dt,
+                                hipStream_t stream);
+
+/*
  * RMSNorm forward, per row i:  r_i = 1 / sqrt(sum_j x_ij^2 / N + eps),  y_ij = x_ij * r_i * w_j.
  * [QuACK] section 让内存密集型内核达到"光速" (RMSNorm among the three kernels) and
  * 总结 (RMSNorm's layout, loads/stores and reduction helpers reused for softmax).

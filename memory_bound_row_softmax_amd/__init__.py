@@ -29,7 +29,7 @@ RR_F32, RR_BF16 = 0, 1
 (RR_OP_SOFTMAX, RR_OP_RMSNORM, RR_OP_XENT, RR_OP_XENT_GRAD, RR_OP_SOFTMAX_BWD,
  RR_OP_RMSNORM_BWD) = 0, 1, 2, 3, 4, 5
 
-EXPORTS = ("rr_softmax_fwd", "rr_rmsnorm_fwd", "rr_cross_entropy_fwd",
+EXPORTS = ("rr_softmax_fwd", "rr_softmax_fwd_static", "rr_rmsnorm_fwd", "rr_cross_entropy_fwd",
            "rr_cross_entropy_fwd_bwd", "rr_softmax_bwd", "rr_rmsnorm_bwd", "rr_workspace_bytes",
            "rr_workspace_check", "rr_plan_query", "rr_stream_copy", "rr_stream_read_sink_bytes",
            "rr_stream_read", "rr_stream_fill", "rr_set_test_overrides",
@@ -83,6 +83,7 @@ def lib():
             vp, i64, sz, ci, st = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t,
                                    ctypes.c_int, ctypes.c_int)
             L.rr_softmax_fwd.argtypes = [vp, vp, i64, i64, ci, vp, sz, vp]
+            L.rr_softmax_fwd_static.argtypes = [vp, vp, i64, i64, ci, vp]
             L.rr_rmsnorm_fwd.argtypes = [vp, vp, vp, vp, i64, i64, ci, ctypes.c_float, vp, sz, vp]
             L.rr_cross_entropy_fwd.argtypes = [vp, vp, vp, vp, i64, i64, ci, vp, sz, vp]
             L.rr_cross_entropy_fwd_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, ci, vp, sz,
@@ -102,7 +103,7 @@ def lib():
             L.rr_status_string.argtypes = [ci]
             L.rr_status_string.restype = ctypes.c_char_p
             L.rr_last_hip_error.argtypes = []
-            for f in (L.rr_softmax_fwd, L.rr_rmsnorm_fwd, L.rr_cross_entropy_fwd,
+            for f in (L.rr_softmax_fwd, L.rr_softmax_fwd_static, L.rr_rmsnorm_fwd, L.rr_cross_entropy_fwd,
                       L.rr_cross_entropy_fwd_bwd, L.rr_softmax_bwd, L.rr_rmsnorm_bwd,
                       L.rr_workspace_check, L.rr_plan_query, L.rr_stream_copy,
                       L.rr_stream_read, L.rr_stream_fill, L.rr_set_test_overrides,
@@ -127,6 +128,11 @@ def _check(status: int, what: str):
 
 def softmax_fwd_raw(x, y, M, N, dt, ws=0, ws_bytes=0, stream=0) -> int:
     return lib().rr_softmax_fwd(x, y, M, N, dt, ws or None, ws_bytes, stream or None)
+
+
+def softmax_fwd_static_raw(x, y, M, N, dt, stream=0) -> int:
+    """rr_softmax_fwd_static: the split-row workspace is the library's own."""
+    return lib().rr_softmax_fwd_static(x, y, M, N, dt, stream or None)
 
 
 def rmsnorm_fwd_raw(x, w, y, rstd, M, N, dt, eps, ws=0, ws_bytes=0, stream=0) -> int:

@@ -112,12 +112,12 @@ rr_status launch_args(hipStream_t stream, rr::LaunchArgs *a) {
     return RR_OK;
 }
 
-}  // namespace
+static_assert(RR_STATIC_SCRATCH_BYTES == rr::kStaticScratchBytes,
+              "the header states the size of the library-held workspace");
 
-extern "C" {
-
-rr_status rr_softmax_fwd(const void *x, void *y, int64_t M, int64_t N, rr_dtype dt, void *ws,
-                         size_t ws_bytes, hipStream_t stream) {
+// rr_softmax_fwd, with the caller's workspace or (static_ws) the library's own.
+rr_status softmax_fwd(const void *x, void *y, int64_t M, int64_t N, rr_dtype dt, void *ws,
+                      size_t ws_bytes, bool static_ws, hipStream_t stream) {
     size_t bytes = 0;
     rr_status st = check_matrix(M, N, dt, &bytes);
     if (st != RR_OK || M == 0) return st;
@@ -126,6 +126,18 @@ rr_status rr_softmax_fwd(const void *x, void *y, int64_t M, int64_t N, rr_dtype 
     rr::Plan p;
     st = plan_status(rr::make_plan(rr::kOpSoftmax, dt, M, N, vec, &p));
     if (st != RR_OK) return st;
+    if (static_ws) {
+        if (p.ws_bytes > rr::kStaticScratchBytes) return RR_ERR_WORKSPACE;
+        ws = nullptr;
+        ws_bytes = 0;
+        if (p.ws_bytes > 0) {
+            int dev = 0;
+            hipError_t e = hipGetDevice(&dev);
+            if (e == hipSuccess) e = rr::static_scratch(dev, &ws);
+            if (e != hipSuccess) return hip_status(e);
+            ws_bytes = rr::kStaticScratchBytes;
+        }
+    }
     if ((st = check_workspace(p, ws, ws_bytes, {{x, bytes}, {y, bytes}})) != RR_OK) return st;
     rr::LaunchArgs a;
     if ((st = launch_args(stream, &a)) != RR_OK) return st;
@@ -133,6 +145,20 @@ rr_status rr_softmax_fwd(const void *x, void *y, int64_t M, int64_t N, rr_dtype 
         return hip_status(rr::launch_long_row(p, rr::kOpSoftmax, dt, x, nullptr, y, nullptr, M, N,
                                               0.0f, ws, a));
     return hip_status(rr::launch_softmax(p, dt, x, y, M, N, ws, a));
+}
+
+}  // namespace
+
+extern "C" {
+
+rr_status rr_softmax_fwd(const void *x, void *y, int64_t M, int64_t N, rr_dtype dt, void *ws,
+                         size_t ws_bytes, hipStream_t stream) {
+    return softmax_fwd(x, y, M, N, dt, ws, ws_bytes, false, stream);
+}
+
+rr_status rr_softmax_fwd_static(const void *x, void *y, int64_t M, int64_t N, rr_dtype dt,
+                                hipStream_t stream) {
+    return softmax_fwd(x, y, M, N, dt, nullptr, 0, true, stream);
 }
 
 rr_status rr_rmsnorm_fwd(const void *x, const void *w, void *y, float *rstd, int64_t M,

@@ -37,6 +37,13 @@ hipError_t launch_long_row(const Plan &p, int op, int dtype, const void *x, cons
 hipError_t launch_rmsnorm_packed(const Plan &p, const void *x, const void *w, void *y, float *rstd,
                                  int64_t M, int64_t N, float eps, void *ws, const LaunchArgs &a);
 hipError_t launch_copy(const void *src, void *dst, size_t bytes, const LaunchArgs &a);
+
+// Bytes of the library-held softmax workspace on each GPU (rr_softmax_fwd_static): the
+// largest a softmax plan needs, 256 + 1024 * (64 + 64 * 128) = 8454400, rounded up.
+constexpr size_t kStaticScratchBytes = (size_t)(8u << 20) + (256u << 10);
+// Its device address on device `dev`, which must be the current device (found with
+// hipGetSymbolAddress on the first call for each device, then kept).
+hipError_t static_scratch(int dev, void **ptr);
 hipError_t launch_read(const void *src, size_t bytes, uint32_t *sink, const LaunchArgs &a);
 hipError_t launch_fill(void *dst, size_t bytes, uint32_t value, const LaunchArgs &a);
 // Bytes of the per-block checksums launch_read writes for `bytes` of input.

@@ -161,12 +161,18 @@ class Runner:
               "xent_grad": rr.RR_OP_XENT_GRAD, "softmax_bwd": rr.RR_OP_SOFTMAX_BWD,
               "rmsnorm_bwd": rr.RR_OP_RMSNORM_BWD}[w.op]
         self.op = op
-        self.ws = rr.workspace(op, w.M, w.N, self.dt, device)
+        # The workspace is zero-filled on the launch stream, and everything above is
+        # finished before the first launch: a kernel that started before the fill
+        # (on another stream) would find stale counters and slots, and have them
+        # zeroed under it while its workgroups wait for each other.
+        self.stream = torch.cuda.Stream(device=device)
+        self.sp = self.stream.cuda_stream
+        with torch.cuda.stream(self.stream):
+            self.ws = rr.workspace(op, w.M, w.N, self.dt, device)
+        torch.cuda.synchronize()
         self.wsp = self.ws.data_ptr() if self.ws is not None else 0
         self.wsb = self.ws.numel() if self.ws is not None else 0
         self.plan = rr.rr_plan_query(op, w.M, w.N, self.dt)
-        self.stream = torch.cuda.Stream(device=device)
-        self.sp = self.stream.cuda_stream
         self.xp = [t.data_ptr() for t in self.x]
         if has_rows:
             self.lp, self.ep = [t.data_ptr() for t in self.loss], [t.data_ptr() for t in self.lse]

@@ -34,12 +34,12 @@
  *    reads.  Every launch that completes normally leaves it zero-filled again,
  *    except for the dw partial rows of rr_rmsnorm_bwd (scratch that each call
  *    rewrites).
- *  - The workgroups that share a row wait for each other.  They are grouped in
- *    the order in which they start, and the grid is sized so that all of it
- *    fits on an idle device at once.  When it does not all run at once (other
- *    work holding the device), the launch still completes if one XCD can hold
- *    as many of them as share a row (a workgroup runs on the XCD its block id
- *    names).  Each wait is bounded (about a second).  A workgroup whose wait gives up
+ *  - The workgroups that share a row wait for each other.  The G workgroups of
+ *    a row group are G consecutive block ids, and the grid is sized so that all
+ *    of it fits on an idle device at once.  When it does not all run at once
+ *    (other work holding the device), the launch still completes if each XCD can
+ *    hold ceil(G / 8) of them (block b runs on XCD b mod 8, and each XCD starts
+ *    its blocks in id order).  Each wait is bounded (about a second).  A workgroup whose wait gives up
  *    writes NaN in place of its share of that row (and of every later row whose wait
  *    also fails) and sets the workspace's error word, which rr_workspace_check()
  *    reports: a launch never ends with wrong values that are not NaN.

@@ -194,14 +194,40 @@ constexpr bool defer_split(int op, int elem_bytes, bool vec, int P, int R, int G
     return false;
 }
 
+// Granule, in 16-byte chunks, in which the chunks of a row split over G workgroups
+// are dealt to them (row_io.hpp, lane_of); one workgroup holds S = C * R chunks of a
+// row (C per lane).  Chosen by measurement on MI355X: softmax forward over 16384
+// rows, GB/s averaged over six byte offsets between input and output (the spread
+// over offsets reaches 10 %), against one contiguous part per workgroup:
+//   G = 2:  512 chunks (8 KiB) +1 %
+//   G = 4:  4 KiB +5 % (bf16, S = 4096); fp32 softmax (S = 8192) 8 KiB +1 % (4 KiB: -2 %)
+//   G = 8:  4 KiB +2 to +6 %
+//   G = 5, 16, 32, 64: a contiguous part per workgroup was best (4 KiB: -6 to -8 %)
+// RMSNorm, the softmax backward and the cross-entropy gradient at G = 4 measured best
+// with 4 KiB (+5 to +13 %).
+constexpr int split_granule(int op, int C, int R, int G) {
+    const int S = C * R;
+#ifdef RR_SPLIT_GRANULE
+    int K = RR_SPLIT_GRANULE == 0 ? S : RR_SPLIT_GRANULE;  // tuning builds; 0: contiguous
+#else
+    int K = S;
+    if (G == 2) K = 512;
+    if (G == 4) K = (op == kCfgSoftmax && S >= 8192) ? 512 : 256;
+    if (G == 8) K = 256;
+#endif
+    if (K >= S) return S;
+    if (K > R && C % (K / R) != 0) return S;
+    return K;
+}
+
 // Threads per workgroup and rows per workgroup for a lane-group width R (block
 // kernels; a stream kernel's workgroup is its R lanes).
 constexpr int block_threads_for(int R) { return R < 256 ? 256 : R; }
 constexpr int rows_per_block_for(int R) { return block_threads_for(R) / R; }
 
 // Split-row workspace layout (bytes):
-//   [0, 256)                 header: word 0 is the error word (non-zero: a wait timed out),
-//                            words 1 and 2 the ticket and exit counters of a launch
+//   [0, 256)                 header: word 0 is the error word (non-zero: a wait timed
+//                            out), the rest unused
 //   256 + g * group_stride   record of row group g:
 //       +0                   departure counter (uint32)
 //       +64                  slots[kSlotSets][G][2] of uint64: (epoch << 32) | float bits

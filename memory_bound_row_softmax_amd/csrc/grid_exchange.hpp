@@ -28,22 +28,16 @@
 //    the last one to leave zeroes the group's slots and the counter, so the
 //    workspace is all zero again for the next launch.
 //
-// Membership by start order, not by block id.  An ordinary launch does not promise
-// that all of a grid's workgroups run at once, and a cooperative launch (which does)
-// cost 16-20 us more per launch on MI355X.  So each workgroup takes a ticket from a
-// counter in the workspace header when it starts, and ticket t makes it member
-// t % G of row group t / G.  Tickets are handed out in start order, so at any moment
-// every group but the one holding the latest ticket has all its members started:
-// those groups never wait on a workgroup that has not started, finish their rows
-// and exit, and the free slots then start the missing members of the last group.
-// The planner sizes the grid from the occupancy query, so all of it normally runs
-// at once.  A grid larger than that (other work holding slots, or a test override)
-// still drains when one XCD can hold G workgroups of the kernel at once: a
-// workgroup runs on the XCD its block id names (block id mod 8), so near the end
-// of the grid the only workgroups left to start may all belong to one XCD, and a
-// partial group must not be able to fill that XCD's slots by itself.  Past that,
-// the bounded wait ends a wait that cannot be met.
-// The last workgroup to leave the grid zeroes the ticket and exit counters.
+// Membership by block id.  Row group g is the G consecutive blocks gG .. gG + G - 1,
+// and block b is member b % G.  Blocks go to the eight XCDs in turn (block b to XCD
+// b mod 8), and each XCD starts its blocks in the order of their ids; so the members
+// of every group that has not finished are either running or next in line on their
+// XCD, and a grid larger than the device holds at once (other work holding slots, or
+// a test override) still drains when each XCD can hold ceil(G / 8) workgroups of the
+// kernel: the lowest unfinished group's members on an XCD come right after the
+// blocks of finished groups there.  The planner sizes the grid from the occupancy
+// query, so normally all of it runs at once.  Past that, the bounded wait ends a wait
+// that cannot be met.  Which chunks of a row each member holds: row_io.hpp, lane_of.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -182,41 +176,11 @@ __device__ __forceinline__ void depart_group(GroupRef g) {
     }
 }
 
-// Header words of the workspace: the error word, then the ticket and exit counters.
-constexpr int kWsTicketWord = 1;
-constexpr int kWsExitWord = 2;
-
-// Which row group and member this workgroup is, from its ticket (see above).  The
-// grid is groups * G workgroups; the ticket is taken modulo that, so that a counter
-// left non-zero (a launch that never finished) still gives every (group, member)
-// exactly once.  Called by every thread; uses one barrier.
+// Which row group and member this workgroup is (see the membership note above).
 template <int G>
-__device__ __forceinline__ void join_grid(uint8_t *ws, int groups, int *group, int *member) {
-    __shared__ int ticket;
-    if (threadIdx.x == 0) {
-        uint32_t *ctr = reinterpret_cast<uint32_t *>(ws) + kWsTicketWord;
-        const uint32_t t =
-            __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        ticket = (int)(t % ((uint32_t)groups * (uint32_t)G));
-    }
-    __syncthreads();
-    *group = ticket / G;
-    *member = ticket % G;
-}
-
-// Called once by every workgroup of a split-row grid, as its last action.  The exit
-// count is incremented with release and acquire order, so the last workgroup's reset
-// of the ticket counter comes after every workgroup's ticket.
-__device__ __forceinline__ void leave_grid(uint8_t *ws) {
-    if (threadIdx.x == 0) {
-        uint32_t *h = reinterpret_cast<uint32_t *>(ws);
-        const uint32_t before = __hip_atomic_fetch_add(h + kWsExitWord, 1u, __ATOMIC_ACQ_REL,
-                                                       __HIP_MEMORY_SCOPE_AGENT);
-        if (before == gridDim.x - 1u) {
-            __hip_atomic_store(h + kWsTicketWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(h + kWsExitWord, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+__device__ __forceinline__ void member_of(int *group, int *member) {
+    *group = (int)(blockIdx.x / G);
+    *member = (int)(blockIdx.x % G);
 }
 
 }  // namespace rr

@@ -88,7 +88,7 @@ __global__ void __launch_bounds__(R)
     __shared__ float bcast[3];
     RowCtx c{N, (int)threadIdx.x, 0, 0, true, nullptr, nullptr, bcast, GroupRef{}, spin_limit};
     int group;
-    join_grid<G>(ws, groups, &group, &c.member);
+    member_of<G>(&group, &c.member);
     c.g = group_ref<G>(ws, group);
     if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
     const int l = threadIdx.x;
@@ -99,8 +99,9 @@ __global__ void __launch_bounds__(R)
     for (int64_t row = group; row < M; row += groups) {
         const RowView xv = stream_row_view(x, row, M, rb);
         const RowView yv = stream_row_view(y, row, M, rb);
+        auto tile = [&](int t) { return Lane{t * C * R + l, R}; };  // lane l's chunks of tile t
         auto load1 = [&](float *v, int t) {
-            load_part<E, C, R, VEC, kLongPass1Load>(xv, t * C * R, l, v);
+            load_part<E, C, R, VEC, kLongPass1Load>(xv, tile(t), v);
         };
 
         // pass 1
@@ -109,10 +110,9 @@ __global__ void __launch_bounds__(R)
         walk_tiles<P>(
             c.member, G, tiles, load1,
             [&](float *v, int t) {
-                const int chunk0 = t * C * R;
+                const bool full = part_full_at<E, C, R>(t * C * R, N);
                 if constexpr (OP == kLongSoftmax) {
-                    if (!part_full<E, C, R>(chunk0, N))
-                        mask_part<E, C, R>(chunk0, l, N, -INFINITY, v);
+                    if (!full) mask_part<E, C, R>(tile(t), N, -INFINITY, v);
                     const float mnew = fmaxf(acc.m, tree_reduce<P>(v, OpMax{}));
                     const float mu = safe_max(mnew);
 #pragma unroll
@@ -120,7 +120,7 @@ __global__ void __launch_bounds__(R)
                     acc.s = acc.s * exp_shift(acc.m, mu) + tree_reduce<P>(v, OpSum{});
                     acc.m = mnew;
                 } else {
-                    if (!part_full<E, C, R>(chunk0, N)) mask_part<E, C, R>(chunk0, l, N, 0.0f, v);
+                    if (!full) mask_part<E, C, R>(tile(t), N, 0.0f, v);
                     q += tree_sum_squares<P>(v);
                 }
             },
@@ -153,13 +153,12 @@ __global__ void __launch_bounds__(R)
         walk_tiles<B2>(
             last_tile(c.member, G, tiles), -G, tiles,
             [&](float *v, int t) {
-                load_part<E, C, R, VEC>(xv, t * C * R, l, v);
+                load_part<E, C, R, VEC>(xv, tile(t), v);
                 if constexpr (OP == kLongRmsnorm)
-                    load_part<E, C, R, VEC, kReuseLoad>(RowView{wb, 0u, rb}, t * C * R, l, v + P);
+                    load_part<E, C, R, VEC, kReuseLoad>(RowView{wb, 0u, rb}, tile(t), v + P);
             },
             [&](float *v, int t) {
-                const int chunk0 = t * C * R;
-                const bool full = part_full<E, C, R>(chunk0, N);
+                const bool full = part_full_at<E, C, R>(t * C * R, N);
                 if constexpr (OP == kLongSoftmax) {
 #pragma unroll
                     for (int j = 0; j < P; ++j) v[j] = exp_shift(v[j], m_row) * s_row;
@@ -167,13 +166,12 @@ __global__ void __launch_bounds__(R)
 #pragma unroll
                     for (int j = 0; j < P; ++j) v[j] = v[j] * v[P + j] * r;
                 }
-                store_part<E, C, R, VEC>(yv, chunk0, l, N, true, full, v);
+                store_part<E, C, R, VEC>(yv, tile(t), N, true, full, v);
             },
             wait);
         ++c.it;
     }
     if (c.it > 0) depart_group<G>(c.g);
-    leave_grid(ws);
 }
 
 }  // namespace rr

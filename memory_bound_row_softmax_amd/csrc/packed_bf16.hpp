@@ -59,7 +59,7 @@ __device__ __forceinline__ float tree_map(F f, Op op) {
     }
 }
 
-// Sum of squares of this workgroup's packed part (chunks past the end of its part
+// Sum of squares of this workgroup's packed part (chunks past the end of the row
 // were read past the end of its buffer: zeros, which add nothing).
 template <int R>
 __device__ __forceinline__ float rmsnorm_packed_local(const float *raw, RowCtx &c) {
@@ -77,11 +77,10 @@ template <int R>
 __device__ __forceinline__ void rmsnorm_packed_apply(const float *raw, const u32x4 *wslot, float Q,
                                                      RowView yv, float *rstd_out, float eps,
                                                      const RowCtx &c) {
-    const int chunk0 = c.chunk0;
     const float r = __builtin_amdgcn_rsqf(Q / (float)c.N + eps);
 #pragma unroll
     for (int i = 0; i < kPackedC; ++i) {
-        const int ch = chunk0 + i * R + c.l;
+        const int ch = c.ln.chunk(i);
         const u32x4 wq = wslot[i * R + c.l];
         u32x4 o;
 #pragma unroll
@@ -90,7 +89,7 @@ __device__ __forceinline__ void rmsnorm_packed_apply(const float *raw, const u32
             const float ww = __uint_as_float(wq[q]);
             o[q] = pack_bf16x2((bf16_lo(xw) * bf16_lo(ww)) * r, (bf16_hi(xw) * bf16_hi(ww)) * r);
         }
-        // yv ends where this member's part ends: the range check drops chunks past it
+        // yv ends where the row ends: the range check drops chunks past it
         buf_store16(yv.buf, yv.base + (uint32_t)ch * 16u, o);
     }
     if (rstd_out && c.l == 0 && c.member == 0) *rstd_out = r;
@@ -108,15 +107,12 @@ __global__ void __launch_bounds__(R)
     RowCtx c{N, (int)threadIdx.x, 0, 0, true, red[0], red[1], bcast, GroupRef{}, spin_limit};
     int group = blockIdx.x;
     if constexpr (G > 1) {
-        join_grid<G>(ws, groups, &group, &c.member);
+        member_of<G>(&group, &c.member);
         c.g = group_ref<G>(ws, group);
         if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
     }
-    member_span<8, kPackedC * R, G>(c.member, N, &c.chunk0, &c.nend);
-    const int chunk0 = c.chunk0;
-    c.full = part_full<BF16, kPackedC, R>(chunk0, c.nend);
+    c.ln = lane_of<kCfgRmsnorm, BF16, kPackedC, R, G>(c.member, c.l);
     const uint32_t rb = (uint32_t)N * 2u;
-    const uint32_t vb = (uint32_t)c.nend * 2u;  // this member's part ends here
 
     // This workgroup's slice of w, packed, once; each lane later reads back only
     // the slots it wrote, so no barrier is needed.
@@ -124,14 +120,15 @@ __global__ void __launch_bounds__(R)
         const Buf wb = make_buf(w, rb);
 #pragma unroll
         for (int i = 0; i < kPackedC; ++i)
-            wslot[i * R + c.l] = buf_load16<kReuseLoad>(wb, (uint32_t)(chunk0 + i * R + c.l) * 16u);
+            wslot[i * R + c.l] =
+                buf_load16<kReuseLoad>(wb, (uint32_t)(c.ln.chunk(i)) * 16u);
     }
 
     float buf[2][kPackedW];
     stream_rows<2>(
         (int64_t)group, M, groups, buf,
         [&](float *v, int64_t r) {
-            load_part_raw<BF16, kPackedC, R>(stream_row_view(x, r, M, rb, vb), chunk0, c.l, v);
+            load_part_raw<BF16, kPackedC, R>(stream_row_view(x, r, M, rb), c.ln, v);
         },
         [&](float *v, int64_t r) {
             float q = rmsnorm_packed_local<R>(v, c);
@@ -139,13 +136,12 @@ __global__ void __launch_bounds__(R)
                 exchange_pairs<G>(c.g, c.member, c.it, q, 0.0f, c.spin_limit, c.bcast, MergeSum{});
                 q = c.bcast[0];
             }
-            rmsnorm_packed_apply<R>(v, wslot, q, stream_row_view(y, r, M, rb, vb),
+            rmsnorm_packed_apply<R>(v, wslot, q, stream_row_view(y, r, M, rb),
                                     rstd ? rstd + r : nullptr, eps, c);
             ++c.it;
         });
     if constexpr (G > 1) {
         if (c.it > 0) depart_group<G>(c.g);
-        leave_grid(ws);
     }
 }
 

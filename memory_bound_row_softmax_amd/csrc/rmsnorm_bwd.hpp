@@ -42,14 +42,14 @@ namespace rr {
 // Rows past M read 0 (past the end of the buffer) and are never written.
 template <int R>
 __device__ __forceinline__ RowView rows_view(const char *base, int64_t M, int64_t blk, int sub,
-                                             uint32_t row_bytes, uint32_t span_bytes) {
+                                             uint32_t row_bytes) {
     constexpr int RPB = rows_per_block_for(R);
     const int64_t first = blk * RPB;
     if (first >= M) return {make_buf(base, 0u), 0u, 0u};
     if constexpr (R >= 64) {
-        // one row per workgroup: the buffer ends with this member's part (member_span)
+        // the buffer holds only this row: the range check drops what lies past its end
         if constexpr (RPB == 1)
-            return {make_buf(base + first * row_bytes, span_bytes), 0u, span_bytes};
+            return {make_buf(base + first * row_bytes, row_bytes), 0u, row_bytes};
         int64_t row = first + sub;
         const bool ok = row < M;
         return {make_buf(base + (ok ? row : 0) * row_bytes, ok ? row_bytes : 0u), 0u, row_bytes};
@@ -63,11 +63,11 @@ __device__ __forceinline__ RowView rows_view(const char *base, int64_t M, int64_
 
 // Stores P fp32 values of a lane (the element layout of E) into an fp32 row.
 template <class E, int C, int R>
-__device__ __forceinline__ void store_part_f32(Buf b, int chunk0, int l, int N, const float *v) {
+__device__ __forceinline__ void store_part_f32(Buf b, Lane ln, int N, const float *v) {
     constexpr int VPC = E::VPC;
 #pragma unroll
     for (int i = 0; i < C; ++i) {
-        const int first = (chunk0 + i * R + l) * VPC;
+        const int first = ln.chunk(i) * VPC;
 #pragma unroll
         for (int q = 0; q < VPC / 4; ++q) {
             const int e0 = first + 4 * q;
@@ -128,12 +128,13 @@ struct DwAcc<P, false> {
     __device__ __forceinline__ float get(int j) const { return s[j]; }
 };
 
-// fp64 sums need P more registers than fp32 ones; the fp32 kernels with 32 values on
-// 512 lanes (1 workgroup per CU, 256 registers a lane, already 240 in use) take the
-// compensated sums instead.
-template <class E, int P, int R>
+// fp64 sums need P more registers than fp32 ones; the kernels with 32 values on 512
+// lanes (1 workgroup per CU, 256 registers a lane) whose other registers already fill
+// most of that budget take the compensated sums instead: fp32 rows, and bf16 rows
+// on the per-element path.
+template <class E, int P, int R, bool VEC>
 constexpr bool dw_wide() {
-    return !(E::BYTES == 4 && P == 32 && R >= 512);
+    return !(P == 32 && R >= 512 && (E::BYTES == 4 || !VEC));
 }
 
 // a: x, b: dy of the lane's part of a row (b is reused); wsrc: w; acc: dw partials.
@@ -142,10 +143,9 @@ __device__ __forceinline__ void rmsnorm_bwd_finish(float *a, float *b, float r,
                                                    const WeightLds<P, R> &wsrc, Acc &acc,
                                                    RowView dxv, bool valid, RowCtx &c) {
     constexpr int C = P / E::VPC;
-    const int chunk0 = c.chunk0;
     if (!c.full) {
-        mask_part<E, C, R, true>(chunk0, c.l, c.nend, 0.0f, a);
-        mask_part<E, C, R, true>(chunk0, c.l, c.nend, 0.0f, b);
+        mask_part<E, C, R, true>(c.ln, c.N, 0.0f, a);
+        mask_part<E, C, R, true>(c.ln, c.N, 0.0f, b);
     }
     // dw partial first (before b is overwritten): dy * x * r
 #pragma unroll
@@ -161,7 +161,7 @@ __device__ __forceinline__ void rmsnorm_bwd_finish(float *a, float *b, float r,
     const float k = r * r * t / (float)c.N;
 #pragma unroll
     for (int j = 0; j < P; ++j) a[j] = r * (b[j] - a[j] * k);
-    store_part<E, C, R, VEC, true>(dxv, chunk0, c.l, c.nend, valid, c.full, a);
+    store_part<E, C, R, VEC, true>(dxv, c.ln, c.N, valid, c.full, a);
 }
 
 constexpr int bwd_threads(int R, int G) { return G == 1 ? block_threads_for(R) : R; }
@@ -183,15 +183,13 @@ __global__ void __launch_bounds__(bwd_threads(R, G))
     RowCtx c{N, l, 0, 0, true, red[0] + sub * W, red[1] + sub * W, bcast, GroupRef{}, spin_limit};
     int group = blockIdx.x;
     if constexpr (G > 1) {
-        join_grid<G>(ws, groups, &group, &c.member);
+        member_of<G>(&group, &c.member);
         c.g = group_ref<G>(ws, group);
         if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
     }
-    member_span<E::VPC, C * R, G>(c.member, N, &c.chunk0, &c.nend);
-    const int chunk0 = c.chunk0;
-    c.full = part_full<E, C, R>(chunk0, c.nend);
+    c.ln = lane_of<kCfgRmsnorm, E, C, R, G>(c.member, l);
+    c.full = part_full<kCfgRmsnorm, E, C, R, G>(c.member, N);
     const uint32_t rb = (uint32_t)N * E::BYTES;
-    const uint32_t vb = (uint32_t)c.nend * E::BYTES;  // this member's part ends here
     const int64_t nblk = (M + RPB - 1) / RPB;
 
     // The workgroup's slice of w, once, decoded to fp32 in LDS (the lane groups of a
@@ -199,14 +197,14 @@ __global__ void __launch_bounds__(bwd_threads(R, G))
     __shared__ float4 wslot[(P / 4) * R];
     if (sub == 0) {
         float t[P];
-        load_part<E, C, R, VEC, kReuseLoad>(RowView{make_buf(w, rb), 0u, rb}, chunk0, l, t);
+        load_part<E, C, R, VEC, kReuseLoad>(RowView{make_buf(w, rb), 0u, rb}, c.ln, t);
 #pragma unroll
         for (int q = 0; q < P / 4; ++q)
             wslot[q * R + l] = make_float4(t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]);
     }
     if constexpr (RPB > 1) __syncthreads();
     const WeightLds<P, R> wsrc{wslot};
-    constexpr bool kWide = dw_wide<E, P, R>();
+    constexpr bool kWide = dw_wide<E, P, R, VEC>();
     __shared__ float dw_comp[kWide ? 1 : P * T];
     DwAcc<P, kWide> acc;
     if constexpr (!kWide) acc.stride = T;
@@ -217,20 +215,19 @@ __global__ void __launch_bounds__(bwd_threads(R, G))
     stream_rows<2>(
         (int64_t)group, nblk, groups, buf,
         [&](float *v, int64_t blk) {
-            load_part<E, C, R, VEC>(rows_view<R>(x, M, blk, sub, rb, vb), chunk0, l, v);
-            load_part<E, C, R, VEC>(rows_view<R>(dy, M, blk, sub, rb, vb), chunk0, l, v + P);
+            load_part<E, C, R, VEC>(rows_view<R>(x, M, blk, sub, rb), c.ln, v);
+            load_part<E, C, R, VEC>(rows_view<R>(dy, M, blk, sub, rb), c.ln, v + P);
             const int64_t row = blk * RPB + sub;
             v[2 * P] = (blk < nblk) ? rstd[row < M ? row : M - 1] : 0.0f;
         },
         [&](float *v, int64_t blk) {
             const int64_t row = blk * RPB + sub;
             rmsnorm_bwd_finish<E, P, R, G, VEC>(v, v + P, v[2 * P], wsrc, acc,
-                                                rows_view<R>(dx, M, blk, sub, rb, vb), row < M, c);
+                                                rows_view<R>(dx, M, blk, sub, rb), row < M, c);
             ++c.it;
         });
     if constexpr (G > 1) {
         if (c.it > 0) depart_group<G>(c.g);
-        leave_grid(ws);
     }
 
     // One partial row per workgroup (its lane groups summed in order through LDS,
@@ -256,7 +253,7 @@ __global__ void __launch_bounds__(bwd_threads(R, G))
     }
     if (sub == 0) {
         const Buf pb = make_buf(partial + (int64_t)group * N, (uint32_t)N * 4u);
-        store_part_f32<E, C, R>(pb, chunk0, l, c.nend, part);  // this member's columns only
+        store_part_f32<E, C, R>(pb, c.ln, N, part);  // this member's columns only
     }
 }
 

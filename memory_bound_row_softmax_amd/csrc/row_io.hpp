@@ -1,11 +1,12 @@
 // row_io.hpp -- a lane's share of a row: which chunks it owns, loads, masks, stores.
 //
-// Lane l of a group of R lanes owns chunks chunk0 + i * R + l for i = 0..C-1
-// (chunk = 16 bytes).  For a fixed i the R lanes touch R consecutive chunks, so
-// each load instruction of a wave covers contiguous memory (1 KiB when R >= 64).
-// All C loads are issued before any value is used and none sits behind a branch
-// (except on the per-element path of unaligned fp32 rows, whose values need no
-// conversion after the load).
+// A lane owns C chunks of its row (chunk = 16 bytes): chunk i is ln.chunk(i) (a
+// Lane).  A whole row on a group of R lanes: lane l owns chunks l + i * R, so for a
+// fixed i the R lanes touch R consecutive chunks and each load instruction of a
+// wave covers contiguous memory (1 KiB when R >= 64).  A row split over G
+// workgroups: see lane_of.  All C loads are issued before any value is used
+// and none sits behind a branch (except on the per-element path of unaligned fp32
+// rows, whose values need no conversion after the load).
 //
 // A RowView is a buffer resource plus the byte offset of the row inside it: one
 // row per resource when a row has at least one whole wave (the resource is then
@@ -19,6 +20,7 @@
 
 #include <cstdint>
 
+#include "configs.hpp"
 #include "vec_io.hpp"
 
 namespace rr {
@@ -26,41 +28,63 @@ namespace rr {
 struct RowView {
     Buf buf;
     uint32_t base;     // byte offset of the row inside buf
-    uint32_t end = 0;  // byte offset inside buf where the row (or a split row's share)
-                       // ends; 0 if not known (the per-element path then reads and
-                       // writes element by element throughout)
+    uint32_t end = 0;  // byte offset inside buf where the row ends; 0 if not known
+                       // (the per-element path then reads and writes element by
+                       // element throughout)
 };
 
-// Whether every element owned by lanes chunk0 .. chunk0 + C * R - 1 lies in the row.
-template <class E, int C, int R>
-__device__ __forceinline__ bool part_full(int chunk0, int N) {
-    return (int64_t)(chunk0 + C * R) * E::VPC <= (int64_t)N;
+// Where a lane's chunks lie in its row: chunk i is first + off(i).  The lane's
+// chunks come in rounds of q (one granule of a split row, see lane_of): off(i) =
+// (i / q) * stride + (i % q) * step.  With q = 1 that is first + i * stride.
+struct Lane {
+    int first;
+    int stride;
+    int step = 0;
+    int q = 1;
+    __device__ __forceinline__ int off(int i) const { return (i / q) * stride + (i % q) * step; }
+    __device__ __forceinline__ int chunk(int i) const { return first + off(i); }
+};
+
+// The layout of lane l of workgroup `member` of the G workgroups that share a row,
+// for kernel family OP (configs.hpp).  G == 1: the whole row, lane l owns chunks l +
+// i * R.  G > 1: the row is cut into granules of K chunks (configs.hpp,
+// split_granule), member m owns the granules j with j % G == m, and its chunk k = i *
+// R + l (granule k / K of its own, place k % K in it) is chunk ((k / K) * G + m) * K
+// + k % K of the row.  For each i the R lanes still read R consecutive chunks.  With
+// K = C * R each member holds one contiguous part of the row.  With small granules
+// the G members get equal shares of any row (to one granule), and for G = 8 each
+// XCD's share of every row is one class of 4 KiB granules (address bits 12..14), as
+// in the copy that MI355X ran fastest (copy.hip).
+template <int OP, class E, int C, int R, int G>
+__device__ __forceinline__ Lane lane_of(int member, int l) {
+    if constexpr (G == 1) {
+        return {l, R};
+    } else {
+        constexpr int K = split_granule(OP, C, R, G);
+        if constexpr (K <= R) {
+            static_assert(R % K == 0, "a granule divides the lanes' chunks of one round");
+            return {((l / K) * G + member) * K + l % K, R * G};
+        } else {
+            static_assert(K % R == 0 && C % (K / R) == 0, "a lane's chunks fill whole granules");
+            return {member * K + l, G * K, R, K / R};
+        }
+    }
 }
 
-// The part of a row that member `member` of the G workgroups of a split row holds:
-// chunks [chunk0, chunk0 + S) with S = ceil(row chunks / G) rounded up to whole
-// waves (64 chunks), so the G workgroups get equal shares even when the row does
-// not fill the configuration; `nend` is the end of that part in elements (at most
-// N; at or below chunk0 * VPC when the member holds nothing).  A lane still owns
-// chunks chunk0 + i * R + l (i < C); those at or past `nend` belong to the next
-// member and are masked, and the member's buffer resources end at `nend`, so they
-// are neither read nor written.  With G = 1: the whole row.
-template <int VPC, int CR, int G>
-__device__ __forceinline__ void member_span(int member, int N, int *chunk0, int *nend) {
-    if constexpr (G == 1) {
-        *chunk0 = 0;
-        *nend = N;
-    } else {
-        static_assert(CR % 64 == 0, "a member's part is whole waves");
-        const int total = (N + VPC - 1) / VPC;
-        int span = (total + G - 1) / G;
-        span = (span + 63) & ~63;
-        if (span > CR) span = CR;  // N beyond P * R * G: never planned
-        const int c0 = member * span;
-        const int64_t end = (int64_t)(c0 + span) * VPC;
-        *chunk0 = c0;
-        *nend = (int)(end < (int64_t)N ? end : (int64_t)N);
-    }
+// Whether every chunk that member `member` of a row's G workgroups owns (C chunks
+// in each of its lanes, layout of lane_of) lies wholly inside a row of N elements:
+// whether the last chunk of its last lane does.
+template <int OP, class E, int C, int R, int G>
+__device__ __forceinline__ bool part_full(int member, int N) {
+    return ((int64_t)lane_of<OP, E, C, R, G>(member, R - 1).chunk(C - 1) + 1) * E::VPC <=
+           (int64_t)N;
+}
+
+// The same for a lane group that holds chunks chunk0 + i * R + l of a row (block
+// kernels, one tile of a long row).
+template <class E, int C, int R>
+__device__ __forceinline__ bool part_full_at(int chunk0, int N) {
+    return (int64_t)(chunk0 + C * R) * E::VPC <= (int64_t)N;
 }
 
 // A buffer offset past every resource: loads there return 0 and touch no memory.
@@ -78,15 +102,27 @@ __device__ __forceinline__ u32x4 shift_down_bytes(u32x4 c, uint32_t s) {
     return u32x4{(uint32_t)w, (uint32_t)(w >> 32), (uint32_t)(w >> 64), (uint32_t)(w >> 96)};
 }
 
+// The lane's first chunk, as a value the compiler cannot trace back to how it was
+// computed.  The predicated stores of the block kernels take their addresses from
+// it, so that the addresses of a part are formed where they are used: otherwise the
+// compiler keeps the C addresses of the loads live in registers until the stores
+// that reuse them (up to 40 more registers a lane).  The persistent kernels keep
+// their addresses from row to row anyway, and there the stores go out back to back.
+__device__ __forceinline__ int fresh_first(Lane ln) {
+    int f = ln.first;
+    asm volatile("" : "+v"(f));
+    return f;
+}
+
 // POLICY: kStreamLoad for data read once, kReuseLoad for data read by every row.
 template <class E, int C, int R, bool VEC, int POLICY = kStreamLoad>
-__device__ __forceinline__ void load_part(RowView rv, int chunk0, int l, float *v) {
+__device__ __forceinline__ void load_part(RowView rv, Lane ln, float *v) {
     constexpr int VPC = E::VPC;
     if constexpr (VEC) {
         u32x4 raw[C];
 #pragma unroll
         for (int i = 0; i < C; ++i)
-            raw[i] = buf_load16<POLICY>(rv.buf, rv.base + (uint32_t)(chunk0 + i * R + l) * 16u);
+            raw[i] = buf_load16<POLICY>(rv.buf, rv.base + (uint32_t)ln.chunk(i) * 16u);
 #pragma unroll
         for (int i = 0; i < C; ++i) decode<E>(raw[i], v + i * VPC);
     } else if constexpr (E::BYTES == 4) {
@@ -97,7 +133,7 @@ __device__ __forceinline__ void load_part(RowView rv, int chunk0, int l, float *
         // costs nothing here, since an fp32 chunk needs no conversion after the load.
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            const uint32_t first = (uint32_t)(chunk0 + i * R + l) * VPC;
+            const uint32_t first = (uint32_t)ln.chunk(i) * VPC;
             const uint32_t byte0 = rv.base + first * E::BYTES;
             if (byte0 + 16u <= rv.end) {
                 decode<E>(buf_load16<POLICY>(rv.buf, byte0), v + i * VPC);
@@ -123,7 +159,7 @@ __device__ __forceinline__ void load_part(RowView rv, int chunk0, int l, float *
         uint32_t sh[C];
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            const uint32_t first = (uint32_t)(chunk0 + i * R + l) * VPC;
+            const uint32_t first = (uint32_t)ln.chunk(i) * VPC;
             const uint32_t byte0 = rv.base + first * E::BYTES;
             const bool past = byte0 >= rv.end;
             const bool tail = byte0 + 16u > rv.end;
@@ -137,7 +173,7 @@ __device__ __forceinline__ void load_part(RowView rv, int chunk0, int l, float *
         // bf16 rows shorter than 16 bytes: element by element
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            const uint32_t first = (uint32_t)(chunk0 + i * R + l) * VPC;
+            const uint32_t first = (uint32_t)ln.chunk(i) * VPC;
             const uint32_t byte0 = rv.base + first * E::BYTES;
 #pragma unroll
             for (int e = 0; e < VPC; ++e)
@@ -151,11 +187,11 @@ __device__ __forceinline__ void load_part(RowView rv, int chunk0, int l, float *
 // rest is left unwritten, so a buffer in flight holds only P/2 live registers).
 // widen_part() later turns them into the P fp32 values load_part would give.
 template <class E, int C, int R, int POLICY = kStreamLoad>
-__device__ __forceinline__ void load_part_raw(RowView rv, int chunk0, int l, float *v) {
+__device__ __forceinline__ void load_part_raw(RowView rv, Lane ln, float *v) {
 #pragma unroll
     for (int i = 0; i < C; ++i) {
         const u32x4 raw =
-            buf_load16<POLICY>(rv.buf, rv.base + (uint32_t)(chunk0 + i * R + l) * 16u);
+            buf_load16<POLICY>(rv.buf, rv.base + (uint32_t)ln.chunk(i) * 16u);
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[4 * i + q] = __uint_as_float(raw[q]);
     }
@@ -176,7 +212,7 @@ __device__ __forceinline__ void widen_part(float *v) {
 }
 
 // Registers that hold no element of the row get `fill`.
-// OPAQUE (persistent kernels, whose row loop keeps chunk0 and N fixed): the lane's
+// OPAQUE (persistent kernels, whose row loop keeps the layout and N fixed): the lane's
 // count of elements left in the row passes through an empty asm statement, so that
 // the comparisons stay inside the row loop, where they run only for a part that is
 // not full.  Left to itself, the compiler hoists all P comparisons out of the loop,
@@ -184,37 +220,30 @@ __device__ __forceinline__ void widen_part(float *v) {
 // (116 spilled scalar registers and some 15 vector registers in the 64-value fp32
 // stream kernel).
 template <class E, int C, int R, bool OPAQUE = false>
-__device__ __forceinline__ void mask_part(int chunk0, int l, int N, float fill, float *v) {
+__device__ __forceinline__ void mask_part(Lane ln, int N, float fill, float *v) {
     constexpr int VPC = E::VPC;
-    if constexpr (OPAQUE) {
-        int left = N - (chunk0 + l) * VPC;  // negative or zero: nothing of the row
-        asm volatile("" : "+v"(left));
+    int left = N - ln.first * VPC;  // negative or zero: nothing of the row
+    if constexpr (OPAQUE) asm volatile("" : "+v"(left));
+    // Compared with the lane's count of elements left, so that one register holds
+    // what the comparisons need (an element index per chunk would be shared with
+    // the loads' addresses and stay live until here).
 #pragma unroll
-        for (int i = 0; i < C; ++i) {
+    for (int i = 0; i < C; ++i) {
 #pragma unroll
-            for (int e = 0; e < VPC; ++e)
-                if (i * R * VPC + e >= left) v[i * VPC + e] = fill;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-            const int first = (chunk0 + i * R + l) * VPC;
-#pragma unroll
-            for (int e = 0; e < VPC; ++e)
-                if (first + e >= N) v[i * VPC + e] = fill;
-        }
+        for (int e = 0; e < VPC; ++e)
+            if (ln.off(i) * VPC + e >= left) v[i * VPC + e] = fill;
     }
 }
 
-// BOUNDED: the buffer resource holds only this row (or this split-row member's part)
-// and ends where it ends, as in the persistent kernels; the hardware's range check
+// BOUNDED: the buffer resource holds only this row and ends where it ends, as in the
+// persistent kernels; the hardware's range check
 // then drops the stores of chunks past it, and whole waves per row store every chunk
 // with no predicate.  Left to a per-chunk predicate in a row loop, the compiler hoists
 // the chunks' comparisons out of the loop and keeps their lane masks live (spilled
 // scalar registers).  Otherwise (block kernels, whose lane groups of fewer than 64
 // lanes share one buffer across rows) each chunk is stored only if it lies in the row.
 template <class E, int C, int R, bool VEC, bool BOUNDED = false>
-__device__ __forceinline__ void store_part(RowView rv, int chunk0, int l, int N, bool valid,
+__device__ __forceinline__ void store_part(RowView rv, Lane ln, int N, bool valid,
                                            bool full, const float *v) {
     constexpr int VPC = E::VPC;
     if constexpr (VEC) {
@@ -222,23 +251,25 @@ __device__ __forceinline__ void store_part(RowView rv, int chunk0, int l, int N,
             if (valid) {
 #pragma unroll
                 for (int i = 0; i < C; ++i)
-                    buf_store16(rv.buf, rv.base + (uint32_t)(chunk0 + i * R + l) * 16u,
+                    buf_store16(rv.buf, rv.base + (uint32_t)ln.chunk(i) * 16u,
                                 encode<E>(v + i * VPC));
             }
         } else {
+            const int f = fresh_first(ln);
+            const int left = N - ln.first * VPC;  // as in mask_part
 #pragma unroll
             for (int i = 0; i < C; ++i) {
-                const int c = chunk0 + i * R + l;
-                if (valid && (full || c * VPC < N))
-                    buf_store16(rv.buf, rv.base + (uint32_t)c * 16u, encode<E>(v + i * VPC));
+                if (valid && (full || ln.off(i) * VPC < left))
+                    buf_store16(rv.buf, rv.base + (uint32_t)(f + ln.off(i)) * 16u,
+                                encode<E>(v + i * VPC));
             }
         }
     } else {
-        // As for the loads: whole chunks inside the row (and inside [0, N), the end of
-        // this workgroup's part) are one 16-byte store, the rest element by element.
+        // As for the loads: whole chunks inside the row are one 16-byte store, the rest
+        // element by element.
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            const int first = (chunk0 + i * R + l) * VPC;
+            const int first = ln.chunk(i) * VPC;
             const uint32_t byte0 = rv.base + (uint32_t)first * E::BYTES;
             if (byte0 + 16u <= rv.end && first + VPC <= N) {
                 if (valid) buf_store16(rv.buf, byte0, encode<E>(v + i * VPC));

@@ -12,8 +12,8 @@
 // path.  Two kernel kinds per op (see configs.hpp): block kernels (G = 1, one
 // workgroup per few rows) and stream kernels (persistent, one row per workgroup
 // at a time, the next row's loads issued before the current row is reduced;
-// with G > 1 the G workgroups of a row meet in the workspace, grouped by the order
-// in which they start).
+// with G > 1 the G consecutive blocks of a row group meet in the workspace, each
+// holding an interleaved share of the row: row_io.hpp, lane_of).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -66,14 +66,6 @@ __device__ __forceinline__ RowView stream_row_view(const char *base, int64_t row
     return {make_buf(base + (ok ? row : 0) * row_bytes, ok ? row_bytes : 0u), 0u, row_bytes};
 }
 
-// The same, with the buffer ending `span_bytes` into the row (the end of a split
-// row member's part, see member_span).
-__device__ __forceinline__ RowView stream_row_view(const char *base, int64_t row, int64_t M,
-                                                   uint32_t row_bytes, uint32_t span_bytes) {
-    const bool ok = row < M;
-    return {make_buf(base + (ok ? row : 0) * row_bytes, ok ? span_bytes : 0u), 0u, span_bytes};
-}
-
 // Row loop of the stream kernels with D register buffers.  Rows group,
 // group + groups, ... < M are processed in order; buffer k % D holds the k-th of
 // them.  Before row k is finished, the loads of row k + D - 1 are issued, so
@@ -120,8 +112,7 @@ struct RowCtx {
     float *bcast;   // LDS: merged split-row partials [0..1], "a wait timed out" flag [2]
     GroupRef g;
     int spin_limit;
-    int chunk0 = 0;  // first chunk of this workgroup's part of the row (member_span)
-    int nend = N;    // end of that part, in elements
+    Lane ln = {0, 0};  // where this lane's chunks lie in the row (lane_of)
 
     // Slots for a row body with a single reduction.  A slot array may be written
     // again only after a later barrier (waves_combine), so a persistent kernel
@@ -145,8 +136,8 @@ struct MergeMaxSum {
 // What a softmax kernel writes for a row, given e_j = exp(x_j - mu) in registers
 // and the factor `scale` that turns e_j into the softmax p_j.  An output policy
 // `Out` (a kernel argument) hands out one Epi per row:
-//   capture<E, C, R>(v, chunk0, l)  sees the lane's raw values before the exp;
-//   apply<E, C, R>(v, scale, M, S, chunk0, ctx, valid)  turns e into the values
+//   capture<E, C, R>(v, ln, N)      sees the lane's raw values before the exp;
+//   apply<E, C, R>(v, scale, M, S, ctx, valid)  turns e into the values
 //                                   to store and writes any per-row outputs
 //                                   (M, S: the row's max and sum of exp(x - M)).
 // A stream kernel keeps kExtra more registers per row buffer for the row's own
@@ -158,9 +149,9 @@ struct SoftmaxOut {
     static constexpr int kExtra = 0;
     struct Epi {
         template <class E, int C, int R>
-        __device__ __forceinline__ void capture(const float *, int, int, int) {}
+        __device__ __forceinline__ void capture(const float *, Lane, int) {}
         template <class E, int C, int R>
-        __device__ __forceinline__ void apply(float *v, float scale, float, float, int,
+        __device__ __forceinline__ void apply(float *v, float scale, float, float,
                                               const RowCtx &, bool) {
 #pragma unroll
             for (int j = 0; j < C * E::VPC; ++j) v[j] *= scale;
@@ -176,9 +167,8 @@ struct SoftmaxOut {
 template <class E, int P, int R, bool STREAM, class Epi>
 __device__ __forceinline__ MaxSum softmax_local(float *v, RowCtx &c, Epi &epi) {
     constexpr int C = P / E::VPC;
-    const int chunk0 = c.chunk0;
-    epi.template capture<E, C, R>(v, chunk0, c.l, c.nend);
-    if (!c.full) mask_part<E, C, R, STREAM>(chunk0, c.l, c.nend, -INFINITY, v);
+    epi.template capture<E, C, R>(v, c.ln, c.N);
+    if (!c.full) mask_part<E, C, R, STREAM>(c.ln, c.N, -INFINITY, v);
 
     // pass 1: row max
     float m = tree_reduce<P>(v, OpMax{});
@@ -195,20 +185,19 @@ __device__ __forceinline__ MaxSum softmax_local(float *v, RowCtx &c, Epi &epi) {
 
 // Pass 3: normalise with the row's (M, S) (for a split row, merged over its G
 // workgroups; `loc` is this workgroup's own pair), then the store.  STREAM: called
-// from a persistent kernel's row loop (row buffers that end with the part, masks
+// from a persistent kernel's row loop (row buffers that end with the row, masks
 // kept inside the loop; see store_part and mask_part).
 template <class E, int P, int R, int G, bool VEC, bool STREAM, class Epi>
 __device__ __forceinline__ void softmax_apply(float *v, RowView yv, bool valid, RowCtx &c,
                                               Epi &epi, MaxSum loc, float Mrow, float Srow) {
     constexpr int C = P / E::VPC;
-    const int chunk0 = c.chunk0;
     float scale;
     if constexpr (G == 1)
         scale = __builtin_amdgcn_rcpf(Srow);
     else
         scale = exp_shift(loc.m, safe_max(Mrow)) * __builtin_amdgcn_rcpf(Srow);
-    epi.template apply<E, C, R>(v, scale, Mrow, Srow, chunk0, c, valid);
-    store_part<E, C, R, VEC, STREAM>(yv, chunk0, c.l, c.nend, valid, c.full, v);
+    epi.template apply<E, C, R>(v, scale, Mrow, Srow, c, valid);
+    store_part<E, C, R, VEC, STREAM>(yv, c.ln, c.N, valid, c.full, v);
 }
 
 // Passes 1-3 on a lane's loaded part v of the row, then the store.
@@ -235,12 +224,13 @@ __global__ void __launch_bounds__(block_threads_for(R))
     __shared__ float red_sum[RPB * W];
     const int sub = lane_group<R>();
     const uint32_t row_bytes = (uint32_t)N * E::BYTES;
-    RowCtx c{N, (int)(threadIdx.x % R), 0, 0, part_full<E, C, R>(0, N), red_max + sub * W,
-             red_sum + sub * W, nullptr, GroupRef{}, 0};
+    RowCtx c{N, (int)(threadIdx.x % R), 0, 0, part_full<Out::kCfg, E, C, R, 1>(0, N),
+             red_max + sub * W, red_sum + sub * W, nullptr, GroupRef{}, 0};
+    c.ln = lane_of<Out::kCfg, E, C, R, 1>(0, c.l);
     const int64_t row = (int64_t)blockIdx.x * RPB + sub;
     const bool valid = row < M;
     float v[P];
-    load_part<E, C, R, VEC>(block_row_view<R>(x, M, sub, row_bytes), 0, c.l, v);
+    load_part<E, C, R, VEC>(block_row_view<R>(x, M, sub, row_bytes), c.ln, v);
     auto epi = out.row(valid ? row : M - 1);
     softmax_finish<E, P, R, 1, VEC, false>(v, block_row_view<R>(y, M, sub, row_bytes), valid, c,
                                            epi);
@@ -260,15 +250,13 @@ __global__ void __launch_bounds__(R)
     RowCtx c{N, (int)threadIdx.x, 0, 0, true, red_max, red_sum, bcast, GroupRef{}, spin_limit};
     int group = blockIdx.x;
     if constexpr (G > 1) {
-        join_grid<G>(ws, groups, &group, &c.member);
+        member_of<G>(&group, &c.member);
         c.g = group_ref<G>(ws, group);
         if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
     }
-    member_span<E::VPC, C * R, G>(c.member, N, &c.chunk0, &c.nend);
-    const int chunk0 = c.chunk0;
-    c.full = part_full<E, C, R>(chunk0, c.nend);
+    c.ln = lane_of<Out::kCfg, E, C, R, G>(c.member, (int)threadIdx.x);
+    c.full = part_full<Out::kCfg, E, C, R, G>(c.member, N);
     const uint32_t rb = (uint32_t)N * E::BYTES;
-    const uint32_t vb = (uint32_t)c.nend * E::BYTES;  // this member's part ends here
 
     // Per-row inputs of the output policy (if any) sit after a row's values in its
     // buffer and are loaded with it.
@@ -286,9 +274,9 @@ __global__ void __launch_bounds__(R)
         // registers) and widened when it becomes the current row.
         auto load = [&](float *v, int64_t r) {
             if constexpr (VEC)
-                load_part_raw<E, C, R>(stream_row_view(x, r, M, rb, vb), chunk0, c.l, v);
+                load_part_raw<E, C, R>(stream_row_view(x, r, M, rb), c.ln, v);
             else
-                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb, vb), chunk0, c.l, v);
+                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), c.ln, v);
             if (r < M) out.stash(v + P, r);
         };
         load(buf[0], row);
@@ -309,7 +297,7 @@ __global__ void __launch_bounds__(R)
             }
             if (c.it > 0) {  // complete the previous row
                 wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeMaxSum{});
-                softmax_apply<E, P, R, G, VEC, true>(buf[KP], stream_row_view(y, row - groups, M, rb, vb),
+                softmax_apply<E, P, R, G, VEC, true>(buf[KP], stream_row_view(y, row - groups, M, rb),
                                                true, c, epis[KP], pend, c.bcast[0], c.bcast[1]);
             }
             pend = cur;
@@ -328,19 +316,18 @@ __global__ void __launch_bounds__(R)
         stream_rows<D>(
             (int64_t)group, M, groups, buf,
             [&](float *v, int64_t r) {
-                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb, vb), chunk0, c.l, v);
+                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), c.ln, v);
                 if (r < M) out.stash(v + P, r);
             },
             [&](float *v, int64_t r) {
                 auto epi = out.epi(v + P, r);
-                softmax_finish<E, P, R, G, VEC, true>(v, stream_row_view(y, r, M, rb, vb), true, c,
+                softmax_finish<E, P, R, G, VEC, true>(v, stream_row_view(y, r, M, rb), true, c,
                                                       epi);
                 ++c.it;
             });
     }
     if constexpr (G > 1) {
         if (c.it > 0) depart_group<G>(c.g);
-        leave_grid(ws);
     }
 }
 
@@ -385,8 +372,7 @@ struct WeightLds {
 template <class E, int P, int R, bool STREAM>
 __device__ __forceinline__ float rmsnorm_local(float *v, RowCtx &c) {
     constexpr int C = P / E::VPC;
-    const int chunk0 = c.chunk0;
-    if (!c.full) mask_part<E, C, R, STREAM>(chunk0, c.l, c.nend, 0.0f, v);
+    if (!c.full) mask_part<E, C, R, STREAM>(c.ln, c.N, 0.0f, v);
     const float q = tree_sum_squares<P>(v);
     return row_reduce<R>(q, c.one_reduction_slots(), c.l, OpSum{});
 }
@@ -398,12 +384,11 @@ __device__ __forceinline__ void rmsnorm_apply(float *v, const Weight &w, float Q
                                               float *rstd_out, float eps, bool valid,
                                               const RowCtx &c) {
     constexpr int C = P / E::VPC;
-    const int chunk0 = c.chunk0;
     const float r = __builtin_amdgcn_rsqf(Q / (float)c.N + eps);
     w.apply(v, c.l);
 #pragma unroll
     for (int j = 0; j < P; ++j) v[j] *= r;
-    store_part<E, C, R, VEC, STREAM>(yv, chunk0, c.l, c.nend, valid, c.full, v);
+    store_part<E, C, R, VEC, STREAM>(yv, c.ln, c.N, valid, c.full, v);
     if (rstd_out && valid && c.l == 0 && c.member == 0) *rstd_out = r;
 }
 
@@ -428,14 +413,15 @@ __global__ void __launch_bounds__(block_threads_for(R))
     __shared__ float red[RPB * W];
     const int sub = lane_group<R>();
     const uint32_t row_bytes = (uint32_t)N * E::BYTES;
-    RowCtx c{N, (int)(threadIdx.x % R), 0, 0, part_full<E, C, R>(0, N), red + sub * W, nullptr,
-             nullptr, GroupRef{}, 0};
+    RowCtx c{N, (int)(threadIdx.x % R), 0, 0, part_full<kCfgRmsnorm, E, C, R, 1>(0, N),
+             red + sub * W, nullptr, nullptr, GroupRef{}, 0};
     const int64_t row = (int64_t)blockIdx.x * RPB + sub;
     const bool valid = row < M;
     float v[P];
-    load_part<E, C, R, VEC>(block_row_view<R>(x, M, sub, row_bytes), 0, c.l, v);
+    c.ln = lane_of<kCfgRmsnorm, E, C, R, 1>(0, c.l);
+    load_part<E, C, R, VEC>(block_row_view<R>(x, M, sub, row_bytes), c.ln, v);
     float wv[P];
-    load_part<E, C, R, VEC, kReuseLoad>(RowView{make_buf(w, row_bytes), 0u, row_bytes}, 0, c.l, wv);
+    load_part<E, C, R, VEC, kReuseLoad>(RowView{make_buf(w, row_bytes), 0u, row_bytes}, c.ln, wv);
     rmsnorm_finish<E, P, R, 1, VEC, false>(v, WeightRegs<P>{wv}, block_row_view<R>(y, M, sub, row_bytes),
                                     rstd ? rstd + row : nullptr, eps, valid, c);
 }
@@ -453,21 +439,19 @@ __global__ void __launch_bounds__(R)
     RowCtx c{N, (int)threadIdx.x, 0, 0, true, red[0], red[1], bcast, GroupRef{}, spin_limit};
     int group = blockIdx.x;
     if constexpr (G > 1) {
-        join_grid<G>(ws, groups, &group, &c.member);
+        member_of<G>(&group, &c.member);
         c.g = group_ref<G>(ws, group);
         if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
     }
-    member_span<E::VPC, C * R, G>(c.member, N, &c.chunk0, &c.nend);
-    const int chunk0 = c.chunk0;
-    c.full = part_full<E, C, R>(chunk0, c.nend);
+    c.ln = lane_of<kCfgRmsnorm, E, C, R, G>(c.member, (int)threadIdx.x);
+    c.full = part_full<kCfgRmsnorm, E, C, R, G>(c.member, N);
     const uint32_t rb = (uint32_t)N * E::BYTES;
-    const uint32_t vb = (uint32_t)c.nend * E::BYTES;  // this member's part ends here
 
     // This workgroup's slice of w, once; each lane later reads back only the
     // slots it wrote, so no barrier is needed.
     {
         float t[P];
-        load_part<E, C, R, VEC, kReuseLoad>(RowView{make_buf(w, rb), 0u, rb}, chunk0, c.l, t);
+        load_part<E, C, R, VEC, kReuseLoad>(RowView{make_buf(w, rb), 0u, rb}, c.ln, t);
 #pragma unroll
         for (int q = 0; q < P / 4; ++q)
             wslot[q * R + c.l] = make_float4(t[4 * q], t[4 * q + 1], t[4 * q + 2], t[4 * q + 3]);
@@ -480,9 +464,9 @@ __global__ void __launch_bounds__(R)
         int64_t row = group;
         auto load = [&](float *v, int64_t r) {
             if constexpr (VEC)
-                load_part_raw<E, C, R>(stream_row_view(x, r, M, rb, vb), chunk0, c.l, v);
+                load_part_raw<E, C, R>(stream_row_view(x, r, M, rb), c.ln, v);
             else
-                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb, vb), chunk0, c.l, v);
+                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), c.ln, v);
         };
         load(buf[0], row);
         load(buf[1], row + groups);
@@ -500,7 +484,7 @@ __global__ void __launch_bounds__(R)
                 wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeSum{});
                 const int64_t rp = row - groups;
                 rmsnorm_apply<E, P, R, VEC, true>(buf[KP], wsrc, c.bcast[0],
-                                            stream_row_view(y, rp, M, rb, vb),
+                                            stream_row_view(y, rp, M, rb),
                                             rstd ? rstd + rp : nullptr, eps, true, c);
             }
             if (!more) return false;
@@ -516,17 +500,16 @@ __global__ void __launch_bounds__(R)
         stream_rows<D>(
             (int64_t)group, M, groups, buf,
             [&](float *v, int64_t r) {
-                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb, vb), chunk0, c.l, v);
+                load_part<E, C, R, VEC>(stream_row_view(x, r, M, rb), c.ln, v);
             },
             [&](float *v, int64_t r) {
-                rmsnorm_finish<E, P, R, G, VEC, true>(v, wsrc, stream_row_view(y, r, M, rb, vb),
+                rmsnorm_finish<E, P, R, G, VEC, true>(v, wsrc, stream_row_view(y, r, M, rb),
                                                 rstd ? rstd + r : nullptr, eps, true, c);
                 ++c.it;
             });
     }
     if constexpr (G > 1) {
         if (c.it > 0) depart_group<G>(c.g);
-        leave_grid(ws);
     }
 }
 

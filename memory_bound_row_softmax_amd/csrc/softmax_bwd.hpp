@@ -33,10 +33,9 @@ namespace rr {
 template <class E, int P, int R, bool STREAM>
 __device__ __forceinline__ float softmax_bwd_local(float *a, float *b, RowCtx &c) {
     constexpr int C = P / E::VPC;
-    const int chunk0 = c.chunk0;
     if (!c.full) {
-        mask_part<E, C, R, STREAM>(chunk0, c.l, c.nend, 0.0f, a);
-        if constexpr (R < 64) mask_part<E, C, R, STREAM>(chunk0, c.l, c.nend, 0.0f, b);
+        mask_part<E, C, R, STREAM>(c.ln, c.N, 0.0f, a);
+        if constexpr (R < 64) mask_part<E, C, R, STREAM>(c.ln, c.N, 0.0f, b);
     }
     const float t = tree_dot<P>(a, b);
     return row_reduce<R>(t, c.one_reduction_slots(), c.l, OpSum{});
@@ -47,10 +46,9 @@ template <class E, int P, int R, bool VEC, bool STREAM>
 __device__ __forceinline__ void softmax_bwd_apply(float *a, const float *b, float t,
                                                   RowView dxv, bool valid, const RowCtx &c) {
     constexpr int C = P / E::VPC;
-    const int chunk0 = c.chunk0;
 #pragma unroll
     for (int j = 0; j < P; ++j) a[j] = a[j] * (b[j] - t);
-    store_part<E, C, R, VEC, STREAM>(dxv, chunk0, c.l, c.nend, valid, c.full, a);
+    store_part<E, C, R, VEC, STREAM>(dxv, c.ln, c.N, valid, c.full, a);
 }
 
 // a: the lane's part of y, b: of dy; a becomes dx.
@@ -74,12 +72,13 @@ __global__ void __launch_bounds__(block_threads_for(R))
     __shared__ float red[RPB * W];
     const int sub = lane_group<R>();
     const uint32_t row_bytes = (uint32_t)N * E::BYTES;
-    RowCtx c{N, (int)(threadIdx.x % R), 0, 0, part_full<E, C, R>(0, N), red + sub * W, nullptr,
-             nullptr, GroupRef{}, 0};
+    RowCtx c{N, (int)(threadIdx.x % R), 0, 0, part_full<kCfgSoftmaxBwd, E, C, R, 1>(0, N),
+             red + sub * W, nullptr, nullptr, GroupRef{}, 0};
     const bool valid = (int64_t)blockIdx.x * RPB + sub < M;
     float a[P], b[P];
-    load_part<E, C, R, VEC>(block_row_view<R>(y, M, sub, row_bytes), 0, c.l, a);
-    load_part<E, C, R, VEC>(block_row_view<R>(dy, M, sub, row_bytes), 0, c.l, b);
+    c.ln = lane_of<kCfgSoftmaxBwd, E, C, R, 1>(0, c.l);
+    load_part<E, C, R, VEC>(block_row_view<R>(y, M, sub, row_bytes), c.ln, a);
+    load_part<E, C, R, VEC>(block_row_view<R>(dy, M, sub, row_bytes), c.ln, b);
     softmax_bwd_finish<E, P, R, 1, VEC, false>(a, b, block_row_view<R>(dx, M, sub, row_bytes), valid,
                                                c);
 }
@@ -98,15 +97,13 @@ __global__ void __launch_bounds__(R)
     RowCtx c{N, (int)threadIdx.x, 0, 0, true, red[0], red[1], bcast, GroupRef{}, spin_limit};
     int group = blockIdx.x;
     if constexpr (G > 1) {
-        join_grid<G>(ws, groups, &group, &c.member);
+        member_of<G>(&group, &c.member);
         c.g = group_ref<G>(ws, group);
         if (threadIdx.x == 0) bcast[2] = 0.0f;  // read only after later barriers
     }
-    member_span<E::VPC, C * R, G>(c.member, N, &c.chunk0, &c.nend);
-    const int chunk0 = c.chunk0;
-    c.full = part_full<E, C, R>(chunk0, c.nend);
+    c.ln = lane_of<kCfgSoftmaxBwd, E, C, R, G>(c.member, (int)threadIdx.x);
+    c.full = part_full<kCfgSoftmaxBwd, E, C, R, G>(c.member, N);
     const uint32_t rb = (uint32_t)N * E::BYTES;
-    const uint32_t vb = (uint32_t)c.nend * E::BYTES;  // this member's part ends here
 
     if constexpr (kDeferredExchange && defer_split(kCfgSoftmaxBwd, E::BYTES, VEC, P, R, G)) {
         // Split rows, deferred exchange (see the softmax stream kernel): row k's
@@ -116,11 +113,11 @@ __global__ void __launch_bounds__(R)
         int64_t row = group;
         auto load = [&](float *v, int64_t r) {
             if constexpr (VEC) {
-                load_part_raw<E, C, R>(stream_row_view(y, r, M, rb, vb), chunk0, c.l, v);
-                load_part_raw<E, C, R>(stream_row_view(dy, r, M, rb, vb), chunk0, c.l, v + P);
+                load_part_raw<E, C, R>(stream_row_view(y, r, M, rb), c.ln, v);
+                load_part_raw<E, C, R>(stream_row_view(dy, r, M, rb), c.ln, v + P);
             } else {
-                load_part<E, C, R, VEC>(stream_row_view(y, r, M, rb, vb), chunk0, c.l, v);
-                load_part<E, C, R, VEC>(stream_row_view(dy, r, M, rb, vb), chunk0, c.l, v + P);
+                load_part<E, C, R, VEC>(stream_row_view(y, r, M, rb), c.ln, v);
+                load_part<E, C, R, VEC>(stream_row_view(dy, r, M, rb), c.ln, v + P);
             }
         };
         load(buf[0], row);
@@ -141,7 +138,7 @@ __global__ void __launch_bounds__(R)
             if (c.it > 0) {  // complete the previous row
                 wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeSum{});
                 softmax_bwd_apply<E, P, R, VEC, true>(buf[KP], buf[KP] + P, c.bcast[0],
-                                                stream_row_view(dx, row - groups, M, rb, vb), true, c);
+                                                stream_row_view(dx, row - groups, M, rb), true, c);
             }
             if (!more) return false;
             load(buf[KP], row + 2 * (int64_t)groups);
@@ -156,18 +153,17 @@ __global__ void __launch_bounds__(R)
         stream_rows<2>(
             (int64_t)group, M, groups, buf,
             [&](float *v, int64_t r) {
-                load_part<E, C, R, VEC>(stream_row_view(y, r, M, rb, vb), chunk0, c.l, v);
-                load_part<E, C, R, VEC>(stream_row_view(dy, r, M, rb, vb), chunk0, c.l, v + P);
+                load_part<E, C, R, VEC>(stream_row_view(y, r, M, rb), c.ln, v);
+                load_part<E, C, R, VEC>(stream_row_view(dy, r, M, rb), c.ln, v + P);
             },
             [&](float *v, int64_t r) {
-                softmax_bwd_finish<E, P, R, G, VEC, true>(v, v + P, stream_row_view(dx, r, M, rb, vb), true,
+                softmax_bwd_finish<E, P, R, G, VEC, true>(v, v + P, stream_row_view(dx, r, M, rb), true,
                                                     c);
                 ++c.it;
             });
     }
     if constexpr (G > 1) {
         if (c.it > 0) depart_group<G>(c.g);
-        leave_grid(ws);
     }
 }
 

@@ -44,14 +44,14 @@ struct XentGradOut {
         // index: "pick one of these registers" turned into an address would move
         // the whole row out of registers.
         template <class E, int C, int R>
-        __device__ __forceinline__ void capture(const float *v, int chunk0, int l, int nend) {
+        __device__ __forceinline__ void capture(const float *v, Lane ln, int N) {
             constexpr int VPC = E::VPC;
             uint32_t bits = 0;
             bool found = false;
 #pragma unroll
             for (int i = 0; i < C; ++i) {
-                const int d = label - (chunk0 + i * R + l) * VPC;
-                if ((unsigned)d < (unsigned)VPC && label < nend) {
+                const int d = label - ln.chunk(i) * VPC;
+                if ((unsigned)d < (unsigned)VPC && label < N) {
 #pragma unroll
                     for (int e = 0; e < VPC; ++e)
                         bits |= __float_as_uint(v[i * VPC + e]) & (0u - (uint32_t)(d == e));
@@ -64,7 +64,7 @@ struct XentGradOut {
 
         template <class E, int C, int R>
         __device__ __forceinline__ void apply(float *v, float scale, float Mrow, float Srow,
-                                              int chunk0, const RowCtx &c, bool valid) {
+                                              const RowCtx &c, bool valid) {
             constexpr int VPC = E::VPC;
             const bool ok = label >= 0 && label < c.N;
             const float ge = ok ? g : __builtin_nanf("");
@@ -74,7 +74,7 @@ struct XentGradOut {
             if (has) {
 #pragma unroll
                 for (int i = 0; i < C; ++i) {
-                    const int d = label - (chunk0 + i * R + c.l) * VPC;
+                    const int d = label - (c.ln.chunk(i)) * VPC;
                     if ((unsigned)d < (unsigned)VPC) {
 #pragma unroll
                         for (int e = 0; e < VPC; ++e) v[i * VPC + e] -= (d == e) ? ge : 0.0f;

@@ -46,13 +46,13 @@ __global__ void __launch_bounds__(block_threads_for(R))
     bool has_label = false;
     for (int k = 0; k < steps; ++k) {
         float v[P];
-        const int chunk0 = k * step;
-        load_part<E, C, R, VEC>(xv, chunk0, l, v);
-        if (!part_full<E, C, R>(chunk0, N)) mask_part<E, C, R>(chunk0, l, N, -INFINITY, v);
+        const Lane ln = {k * step + l, R};
+        load_part<E, C, R, VEC>(xv, ln, v);
+        if (!part_full_at<E, C, R>(k * step, N)) mask_part<E, C, R>(ln, N, -INFINITY, v);
         // keep row[label] if this lane loaded it
 #pragma unroll
         for (int i = 0; i < C; ++i) {
-            const int d = label - (chunk0 + i * R + l) * VPC;
+            const int d = label - ln.chunk(i) * VPC;
             if ((unsigned)d < (unsigned)VPC) {
 #pragma unroll
                 for (int e = 0; e < VPC; ++e)

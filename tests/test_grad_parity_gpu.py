@@ -368,8 +368,8 @@ def test_rmsnorm_bwd_unaligned(N, dtype):
 
 @pytest.mark.parametrize("op", ["xent_grad", "softmax_bwd", "rmsnorm_bwd"])
 def test_split_backward_drains_when_the_grid_does_not_fit(op):
-    """Row groups forced far beyond what fits at once (members grouped by start
-    order, see the forward test of the same name)."""
+    """Row groups forced far beyond what fits at once (row groups are consecutive
+    block ids, see the forward test of the same name)."""
     M, N = 200, 262144 if op != "rmsnorm_bwd" else 65536
     say("oversubscribed", op, M, N)
     with forced(groups=M):

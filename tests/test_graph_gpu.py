@@ -1,7 +1,7 @@
 """The library's calls can be captured in a HIP graph and replayed.
 
 The kernels allocate nothing, record no memset (the split-row workspace is left
-zero by every launch that completes, tickets and exchange slots included), and
+zero by every launch that completes, exchange slots included), and
 launch with ordinary kernel nodes, so a captured call replays like an eager one.
 Each replay here is compared with the eager result, with eager work (new inputs
 copied in) between the replays, as HIP graphs that record memset nodes have given

@@ -459,13 +459,15 @@ def test_one_poll_waits_never_give_silent_garbage(name, op, dtype, M, N, kind):
 
 
 OVERSUBSCRIBED = [  # (op, dtype, M, N): row groups forced to M, far more than fit at once
-    # Workgroups are bound to an XCD by block id (8 XCDs of 32 CUs), so a forced
-    # grid is sure to drain only when one XCD holds G of them at once: every case
-    # here has G <= 32 at one workgroup per CU (64 with two).
+    # A row group is G consecutive block ids, spread over the 8 XCDs (block b on
+    # XCD b mod 8), so a forced grid drains when each XCD (32 CUs) holds ceil(G / 8)
+    # workgroups at once.
     ("softmax", "f32", 256, 200000),    # 8 workgroups per row, deferred exchange: 2048
     ("softmax", "bf16", 64, 1 << 20),   # 32 per row: 2048
     ("rmsnorm", "bf16", 256, 262144),   # packed, 4 per row: 1024 (one fits per CU)
     ("rmsnorm", "f32", 96, 1 << 19),    # 32 per row: 3072
+    ("softmax", "f32", 64, 2_000_000),  # 64 per row: 4096
+    ("softmax", "f32", 32, 4_000_000),  # 128 per row: 4096
     ("softmax", "f32", 64, 3_000_000),  # two-pass long rows, 32 per row: 2048 (two per CU)
     ("softmax", "f32", 16, 5_000_000),  # two-pass long rows, 64 per row: 1024 (two per CU)
 ]
@@ -474,10 +476,10 @@ OVERSUBSCRIBED = [  # (op, dtype, M, N): row groups forced to M, far more than f
 @pytest.mark.parametrize("op,dtype,M,N", OVERSUBSCRIBED)
 def test_split_rows_drain_when_the_grid_does_not_fit(op, dtype, M, N):
     """Workgroups that share a row wait for each other, and an ordinary launch does
-    not promise that the whole grid runs at once.  Members are grouped by the order
-    in which they start, so a grid several times larger than the device holds must
-    still drain, with every row right and the workspace left clean, as long as one
-    XCD can hold a row's G workgroups at once."""
+    not promise that the whole grid runs at once.  A row group is G consecutive
+    block ids and each XCD starts its blocks in id order, so a grid several times
+    larger than the device holds must still drain, with every row right and the
+    workspace left clean, as long as each XCD can hold ceil(G / 8) of them."""
     code = {"softmax": rr.RR_OP_SOFTMAX, "rmsnorm": rr.RR_OP_RMSNORM}[op]
     dt = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
     assert rr.rr_plan_query(code, M, N, dt)["groups_per_row"] > 1

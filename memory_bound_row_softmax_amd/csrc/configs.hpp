@@ -69,6 +69,7 @@ constexpr int kCfgSoftmax = 0;
 constexpr int kCfgRmsnorm = 1;
 constexpr int kCfgXentGrad = 2;  // softmax kernels with the cross-entropy gradient epilogue
 constexpr int kCfgSoftmaxBwd = 3;
+constexpr int kCfgRmsnormBwd = 4;  // register budgets only (stream_waves)
 
 // Which block configurations are compiled for (op, element bytes, vectorised
 // path).  Excluded are those that would need more than the 128 VGPRs a lane of a
@@ -202,7 +203,10 @@ constexpr bool defer_split(int op, int elem_bytes, bool vec, int P, int R, int G
 //   G = 2:  512 chunks (8 KiB) +1 %
 //   G = 4:  4 KiB +5 % (bf16, S = 4096); fp32 softmax (S = 8192) 8 KiB +1 % (4 KiB: -2 %)
 //   G = 8:  4 KiB +2 to +6 %
-//   G = 5, 16, 32, 64: a contiguous part per workgroup was best (4 KiB: -6 to -8 %)
+//   G = 16: a contiguous part per workgroup for S = 8192 (fp32, 64 x 512: 4 KiB -7 %);
+//           4 KiB for S = 4096 (softmax backward 32 x 512: +12 % bf16, +1 % fp32;
+//           cross-entropy gradient 64 x 256: +5 %)
+//   G = 5, 32, 64: a contiguous part per workgroup was best (4 KiB: -4 to -8 %)
 // RMSNorm, the softmax backward and the cross-entropy gradient at G = 4 measured best
 // with 4 KiB (+5 to +13 %).
 constexpr int split_granule(int op, int C, int R, int G) {
@@ -214,10 +218,25 @@ constexpr int split_granule(int op, int C, int R, int G) {
     if (G == 2) K = 512;
     if (G == 4) K = (op == kCfgSoftmax && S >= 8192) ? 512 : 256;
     if (G == 8) K = 256;
+    if (G == 16 && S <= 4096) K = 256;
 #endif
     if (K >= S) return S;
     if (K > R && C % (K / R) != 0) return S;
     return K;
+}
+
+// Waves per SIMD a persistent kernel is compiled for, as a register budget: with 4,
+// a lane has at most 128 VGPRs and a CU holds two 512-lane workgroups, twice the
+// bytes in flight of one.  Listed are the 512-lane kernels that fit that budget
+// without spilling; 1 leaves the budget to the compiler.  bf16 softmax at G = 2..5
+// measured +3 to +7 % (16384 rows of 65536 to 151936 elements).
+constexpr int stream_waves(int op, int elem_bytes, bool vec, int P, int R, int G) {
+    if (R != 512 || elem_bytes != 2) return 1;
+    if (op == kCfgSoftmax && vec && P == 64 && G >= 2 && G <= 5) return 4;
+    if (op == kCfgRmsnorm && !vec && P == 32 && (G == 2 || G == 4)) return 4;
+    if (op == kCfgSoftmaxBwd && vec && P == 32 && G == 2) return 4;
+    if (op == kCfgRmsnormBwd && !vec && P == 16 && G == 1) return 4;
+    return 1;
 }
 
 // Threads per workgroup and rows per workgroup for a lane-group width R (block

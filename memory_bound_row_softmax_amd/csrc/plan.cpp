@@ -129,7 +129,16 @@ static void fill_geometry(Plan *p) {
 // kernels, whose second register buffer keeps the next row's loads in flight
 // while a row is reduced, with as few workgroups per row as fit (each extra one
 // joins the exchange).  Differences between the top few configurations are a
-// few percent.
+// few percent.  The softmax and RMSNorm forward entries from 32768 to 1048576
+// elements were measured again after the split rows took granule-interleaved
+// shares (configs.hpp, split_granule) and bf16 kernels two workgroups per CU
+// (stream_waves): GB/s averaged over six byte offsets between input and output,
+// since a single placement can be off by up to 10 %.  64 values on 256 lanes then
+// led from 32768 to 131072 elements (fp32 softmax at 131072: 6460 against 6015 GB/s
+// for 64 x 512 on 4 workgroups, whose rate also swung from 5628 to 6240 with the
+// offset), and the fp32 RMSNorm at 262144 took 64 x 512 on 8 (6626 against 5774).
+// The softmax backward and the cross-entropy gradient were measured the same way
+// (the gradient's bf16 rows of 131072: 5373 against 4478 GB/s).
 struct Choice {
     bool stream;
     int P, R, G;
@@ -149,39 +158,39 @@ constexpr Choice kTwoReads = {false, 0, 0, 0};
 static const Choice kTuned[4][2][kTunedBuckets] = {
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 32, 256, 1},
       {false, 32, 256, 1}, {false, 64, 128, 1}, {false, 64, 256, 1}, {true, 64, 512, 1},
-      {true, 16, 1024, 2}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8},
+      {true, 64, 256, 2}, {true, 64, 256, 4}, {true, 64, 256, 8}, {true, 64, 512, 8},
       {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, {true, 64, 512, 128}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 16, 256, 1}, {false, 32, 256, 1},
       {false, 32, 256, 1}, {false, 16, 512, 1}, {false, 64, 256, 1}, {false, 64, 256, 1},
-      {true, 32, 1024, 1}, {true, 64, 512, 2}, {true, 64, 512, 4}, {true, 64, 512, 8},
+      {true, 32, 1024, 1}, {true, 32, 512, 4}, {true, 64, 256, 8}, {true, 64, 512, 8},
       {true, 64, 512, 16}, {true, 64, 512, 32}, kTwoReads, kTwoReads}},
     {{{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 16, 512, 1},
       {false, 32, 256, 1}, {false, 64, 128, 1}, {false, 16, 1024, 1}, {false, 16, 1024, 1},
-      {true, 16, 1024, 2}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 32, 512, 16},
-      {true, 32, 512, 32}, {true, 32, 512, 64}, {true, 64, 512, 64}, {true, 64, 512, 128}},
+      {true, 64, 256, 2}, {true, 64, 256, 4}, {true, 64, 256, 8}, {true, 64, 512, 8},
+      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, {true, 64, 512, 128}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 32, 256, 1},
       {false, 32, 256, 1}, {false, 16, 512, 1}, {false, 64, 256, 1}, {true, 32, 1024, 1},
-      {false, 64, 512, 1}, {true, 32, 1024, 2}, {true, 64, 512, 4}, {true, kPackedP, 512, 4},
+      {true, 32, 512, 2}, {true, 32, 512, 4}, {true, 64, 256, 8}, {true, kPackedP, 512, 4},
       {true, kPackedP, 512, 8}, {true, kPackedP, 512, 16}, {true, kPackedP, 512, 32}, {true, kPackedP, 512, 64}}},
     // softmax backward (y and dy both held: at most 32 values per lane in a stream kernel)
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 16, 256, 1}, {false, 32, 256, 1},
       {false, 32, 256, 1}, {false, 32, 256, 1}, {false, 32, 1024, 1}, {false, 32, 1024, 1},
-      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
+      {true, 16, 1024, 2}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 16, 1024, 16},
       {true, 32, 512, 32}, {true, 32, 512, 64}, kTwoReads, kTwoReads},
      {{false, 8, 32, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 16, 512, 1},
       {false, 16, 512, 1}, {false, 16, 512, 1}, {false, 16, 1024, 1}, {false, 16, 1024, 1},
-      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
+      {true, 32, 512, 2}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
       {true, 32, 512, 32}, {true, 32, 512, 64}, kTwoReads, kTwoReads}},
     // cross-entropy forward fused with its gradient (the softmax kernels; block kernels
     // hold longer rows here than for the softmax)
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 32, 256, 1},
       {false, 32, 256, 1}, {false, 32, 256, 1}, {false, 16, 1024, 1}, {true, 16, 1024, 1},
-      {false, 32, 1024, 1}, {true, 32, 512, 4}, {true, 64, 512, 4}, {true, 64, 512, 8},
+      {true, 64, 256, 2}, {true, 64, 256, 4}, {true, 64, 256, 8}, {true, 64, 256, 16},
       {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads},
      {{false, 16, 16, 1}, {false, 64, 16, 1}, {false, 16, 256, 1}, {false, 32, 256, 1},
       {false, 32, 256, 1}, {false, 32, 256, 1}, {false, 64, 256, 1}, {false, 32, 512, 1},
-      {false, 64, 512, 1}, {false, 64, 1024, 1}, {true, 64, 512, 4}, {true, 32, 1024, 8},
-      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads}},
+      {false, 64, 512, 1}, {false, 64, 1024, 1}, {true, 64, 256, 8}, {true, 32, 1024, 8},
+      {true, 32, 1024, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads}},
 };
 
 // bf16 softmax and cross-entropy gradient rows split over 64 values x 512 lanes take
@@ -193,12 +202,20 @@ static const Choice kTuned[4][2][kTunedBuckets] = {
 // against 4129 on 4, 180000 5261 on 6 against 4713 on 8; the gradient at 70000 and
 // 90000 elements +25 % and +11 % on 3.  Seven lost to eight (4892 against 5119 at
 // 200000 elements), which defer the exchange (configs.hpp), so 7 is not compiled.
+// These plans replace whatever the table chose for the row (64 values on 256 lanes
+// at 70000 elements, after the re-measurement above: 4890 GB/s against 5177 on
+// 64 x 512 x 3, offset-averaged); a row that needs 4 keeps the table's plan.
 static void exact_groups(int op, int dtype, bool vec, int64_t N, Plan *p) {
-    if (!p->stream || p->G <= 2 || dtype != kBf16 || !vec || p->P != 64 || p->R != 512 ||
+    if (!p->stream || p->G <= 2 || dtype != kBf16 || !vec ||
         (op != kOpSoftmax && op != kOpXentGrad))
         return;
     const int64_t need = (N + 64 * 512 - 1) / (64 * 512);
-    if (need < p->G && stream_config_ok(op, dtype, vec, 64, 512, (int)need)) p->G = (int)need;
+    if ((need == 3 || need == 5 || need == 6) &&
+        stream_config_ok(op, dtype, vec, 64, 512, (int)need)) {
+        p->P = 64;
+        p->R = 512;
+        p->G = (int)need;
+    }
 }
 
 // Unaligned bf16 softmax and RMSNorm rows split over 2 to 8 workgroups take 32

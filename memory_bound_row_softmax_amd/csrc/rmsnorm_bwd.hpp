@@ -168,6 +168,7 @@ constexpr int bwd_threads(int R, int G) { return G == 1 ? block_threads_for(R) :
 
 template <class E, int P, int R, int G, bool VEC>
 __global__ void __launch_bounds__(bwd_threads(R, G))
+    __attribute__((amdgpu_waves_per_eu(stream_waves(kCfgRmsnormBwd, E::BYTES, VEC, P, R, G))))
     rmsnorm_bwd_kernel(const char *x, const char *w, const char *dy, const float *rstd, char *dx,
                        float *partial, int64_t M, int N, uint8_t *ws, int groups,
                        int spin_limit) {

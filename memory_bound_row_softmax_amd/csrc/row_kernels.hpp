@@ -239,6 +239,7 @@ __global__ void __launch_bounds__(block_threads_for(R))
 template <class E, int P, int R, int G, bool VEC, class Out = SoftmaxOut,
           int D = stream_depth(kCfgSoftmax, P, R)>
 __global__ void __launch_bounds__(R)
+    __attribute__((amdgpu_waves_per_eu(stream_waves(Out::kCfg, E::BYTES, VEC, P, R, G))))
     softmax_stream_kernel(const char *x, char *y, int64_t M, int N, uint8_t *ws, int groups,
                           int spin_limit, Out out) {
     static_assert(R >= 64, "one row per workgroup");
@@ -428,6 +429,7 @@ __global__ void __launch_bounds__(block_threads_for(R))
 
 template <class E, int P, int R, int G, bool VEC, int D = stream_depth(kCfgRmsnorm, P, R)>
 __global__ void __launch_bounds__(R)
+    __attribute__((amdgpu_waves_per_eu(stream_waves(kCfgRmsnorm, E::BYTES, VEC, P, R, G))))
     rmsnorm_stream_kernel(const char *x, const char *w, char *y, float *rstd, int64_t M, int N,
                           float eps, uint8_t *ws, int groups, int spin_limit) {
     static_assert(R >= 64, "one row per workgroup");

@@ -87,6 +87,7 @@ __global__ void __launch_bounds__(block_threads_for(R))
 // dy (next P), the next row's loads in flight while the current one is finished.
 template <class E, int P, int R, int G, bool VEC>
 __global__ void __launch_bounds__(R)
+    __attribute__((amdgpu_waves_per_eu(stream_waves(kCfgSoftmaxBwd, E::BYTES, VEC, P, R, G))))
     softmax_bwd_stream_kernel(const char *y, const char *dy, char *dx, int64_t M, int N,
                               uint8_t *ws, int groups, int spin_limit) {
     static_assert(R >= 64, "one row per workgroup");

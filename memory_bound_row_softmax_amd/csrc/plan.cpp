@@ -138,7 +138,10 @@ static void fill_geometry(Plan *p) {
 // for 64 x 512 on 4 workgroups, whose rate also swung from 5628 to 6240 with the
 // offset), and the fp32 RMSNorm at 262144 took 64 x 512 on 8 (6626 against 5774).
 // The softmax backward and the cross-entropy gradient were measured the same way
-// (the gradient's bf16 rows of 131072: 5373 against 4478 GB/s).
+// (the gradient's bf16 rows of 131072: 5373 against 4478 GB/s), and the fp32 softmax
+// and RMSNorm at 16384 took 16 values on a 1024-lane stream workgroup (6188 against
+// 5490 GB/s for 64 x 512, whose lanes were half empty; RMSNorm 6340 against 5953 for
+// the 16 x 1024 block kernel).
 struct Choice {
     bool stream;
     int P, R, G;
@@ -157,7 +160,7 @@ constexpr Choice kTwoReads = {false, 0, 0, 0};
 // entries there are the ones those lengths used before)
 static const Choice kTuned[4][2][kTunedBuckets] = {
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 32, 256, 1},
-      {false, 32, 256, 1}, {false, 64, 128, 1}, {false, 64, 256, 1}, {true, 64, 512, 1},
+      {false, 32, 256, 1}, {false, 64, 128, 1}, {false, 64, 256, 1}, {true, 16, 1024, 1},
       {true, 64, 256, 2}, {true, 64, 256, 4}, {true, 64, 256, 8}, {true, 64, 512, 8},
       {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, {true, 64, 512, 128}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 16, 256, 1}, {false, 32, 256, 1},
@@ -165,7 +168,7 @@ static const Choice kTuned[4][2][kTunedBuckets] = {
       {true, 32, 1024, 1}, {true, 32, 512, 4}, {true, 64, 256, 8}, {true, 64, 512, 8},
       {true, 64, 512, 16}, {true, 64, 512, 32}, kTwoReads, kTwoReads}},
     {{{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 16, 512, 1},
-      {false, 32, 256, 1}, {false, 64, 128, 1}, {false, 16, 1024, 1}, {false, 16, 1024, 1},
+      {false, 32, 256, 1}, {false, 64, 128, 1}, {false, 16, 1024, 1}, {true, 16, 1024, 1},
       {true, 64, 256, 2}, {true, 64, 256, 4}, {true, 64, 256, 8}, {true, 64, 512, 8},
       {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, {true, 64, 512, 128}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 32, 256, 1},
@@ -318,7 +321,8 @@ struct BwdChoice {
 };
 // (the 5120, 8192 and 12288 buckets were added later, where the plans interpolated
 // from their neighbours ran up to 23 % slower: bf16 at 5120 elements 3958 -> 4881 GB/s,
-// fp32 at 12288 5379 -> 5753)
+// fp32 at 12288 5379 -> 5753; after the split layout changed, bf16 at 32768 and 65536
+// took 16 values on 4 and 8 workgroups: 5604 -> 6050 and 5744 -> 6009, offset-averaged)
 constexpr int kTunedBwdBuckets = 11;
 constexpr int64_t kTunedBwdN[kTunedBwdBuckets] = {256,   1024,  4096,  5120,   8192,  12288,
                                                   16384, 32768, 65536, 131072, 262144};
@@ -328,7 +332,7 @@ static const BwdChoice kTunedRmsBwd[2][kTunedBwdBuckets] = {
     {{8, 32, 1}, {16, 64, 1}, {16, 256, 1}, {32, 256, 1}, {16, 512, 1}, {32, 512, 1},
      {16, 512, 2}, {16, 512, 4}, {32, 512, 4}, {32, 512, 8}, {32, 512, 16}},
     {{16, 16, 1}, {16, 64, 1}, {32, 128, 1}, {8, 1024, 1}, {16, 512, 1}, {32, 512, 1},
-     {32, 512, 1}, {32, 512, 2}, {32, 512, 4}, {32, 512, 8}, {32, 512, 16}},
+     {32, 512, 1}, {16, 512, 4}, {16, 512, 8}, {32, 512, 8}, {32, 512, 16}},
 };
 
 static PlanResult plan_rmsnorm_bwd(int dtype, int64_t M, int64_t N, bool vec, Plan *out) {

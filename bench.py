@@ -48,7 +48,7 @@ KERNEL_SOURCES = os.path.join(ROOT, "memory_bound_row_softmax_amd", "csrc")
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for name in sorted(os.listdir(KERNEL_SOURCES)):
-        if name.endswith((".hip", ".hpp")):
+        if name.endswith((".hip", ".hpp", ".cpp")):  # kernels and the planner that picks them
             with open(os.path.join(KERNEL_SOURCES, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]

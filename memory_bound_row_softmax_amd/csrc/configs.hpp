@@ -109,11 +109,12 @@ constexpr bool stream_config_enabled(int op, int elem_bytes, bool vec, int P, in
     // 128 workgroups per row (4194304 elements on chip): softmax and RMSNorm forward
     if (G > 64 && op != kCfgSoftmax && op != kCfgRmsnorm) return false;
     // Workgroups per row that are not a power of two: bf16 softmax and cross-entropy
-    // gradient rows on 64 values x 512 lanes take exactly as many as the row needs
-    // (the planner), so that every register holds an element of the row.
+    // gradient rows, and fp32 softmax rows, on 64 values x 512 lanes take exactly as
+    // many as the row needs (the planner), so that most registers hold an element.
     if ((G & (G - 1)) != 0)
-        return vec && elem_bytes == 2 && P == 64 && R == 512 &&
-               (op == kCfgSoftmax || op == kCfgXentGrad);
+        return vec && P == 64 && R == 512 &&
+               ((elem_bytes == 2 && (op == kCfgSoftmax || op == kCfgXentGrad)) ||
+                (elem_bytes == 4 && op == kCfgSoftmax));
     if (op == kCfgXentGrad && elem_bytes == 4 && P == 32 && R == 1024) return false;
     // softmax backward keeps two rows (y, dy) per buffer: about 4P + 40 VGPRs
     if (op == kCfgSoftmaxBwd) return vec ? (R == 1024 ? P <= 16 : P <= 32) : P <= 16;

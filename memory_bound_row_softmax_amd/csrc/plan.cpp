@@ -208,12 +208,17 @@ static const Choice kTuned[4][2][kTunedBuckets] = {
 // These plans replace whatever the table chose for the row (64 values on 256 lanes
 // at 70000 elements, after the re-measurement above: 4890 GB/s against 5177 on
 // 64 x 512 x 3, offset-averaged); a row that needs 4 keeps the table's plan.
+// fp32 softmax rows take 5 or 6 the same way (offset-averaged GB/s, exact against the
+// table: 151936 elements 6155 on 5 against 5472 on 8, 163840 6134 against 5873,
+// 180000 6189 on 6 against 5778); on 3 they gained at 70000 elements (+2 %) but lost
+// at 98304 (-5 %), so fp32 keeps the table there.
 static void exact_groups(int op, int dtype, bool vec, int64_t N, Plan *p) {
-    if (!p->stream || p->G <= 2 || dtype != kBf16 || !vec ||
-        (op != kOpSoftmax && op != kOpXentGrad))
-        return;
+    if (!p->stream || p->G <= 2 || !vec) return;
+    const bool bf16 = dtype == kBf16 && (op == kOpSoftmax || op == kOpXentGrad);
+    const bool f32 = dtype != kBf16 && op == kOpSoftmax;
+    if (!bf16 && !f32) return;
     const int64_t need = (N + 64 * 512 - 1) / (64 * 512);
-    if ((need == 3 || need == 5 || need == 6) &&
+    if (((bf16 && need == 3) || need == 5 || need == 6) &&
         stream_config_ok(op, dtype, vec, 64, 512, (int)need)) {
         p->P = 64;
         p->R = 512;

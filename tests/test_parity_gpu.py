@@ -122,6 +122,21 @@ def test_bf16_softmax_takes_exactly_the_workgroups_a_row_needs(G, N):
     parity_softmax(_x(M, N, "bf16", sigma=2.0), "bf16", f"softmax bf16 G={G} {M}x{N}")
 
 
+@pytest.mark.parametrize("G,N", EXACT_GROUPS)
+def test_fp32_softmax_exact_groups(G, N):
+    """fp32 rows on 64 values x 512 lanes split over 3, 5 or 6 workgroups (the planner
+    picks 5 and 6; 3 is forced), one contiguous part per workgroup, the last shorter."""
+    M = 40
+    if G != 3:
+        p = rr.rr_plan_query(rr.RR_OP_SOFTMAX, 16384, N, rr.RR_F32)
+        assert (p["path"], p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]) == (1, 64, 512, G)
+    say("softmax fp32 exact groups", G, M, N)
+    with forced(64, 512, G, kind="stream", groups=2):
+        parity_softmax(_x(M, N, "f32", sigma=2.0), "f32", f"softmax f32 G={G} {M}x{N}")
+    with forced(64, 512, G, kind="stream"):
+        parity_softmax(_x(M, N, "f32", sigma=2.0), "f32", f"softmax f32 G={G} {M}x{N}")
+
+
 PACKED = [  # (G, M, N): packed bf16 RMSNorm (128 values per lane on 512 lanes)
     (1, 300, 65536), (1, 700, 20000), (1, 3, 8), (2, 100, 131072), (2, 61, 65544),
     (4, 90, 200000), (8, 40, 524288), (16, 7, 1000000), (16, 5, 300000), (16, 33, 1 << 20),

@@ -86,9 +86,13 @@ __device__ __forceinline__ void publish_pair(GroupRef g, int k, int it, float a,
 }
 
 // Waits until all G members have published iteration `it` and leaves the G pairs
-// merged in member order by `merge2` in bcast[0..1] (the same bits for the whole
-// workgroup).  Called by every thread; uses one barrier.  Lane l of wave 0 polls
-// the slots of members l and l + 64 (G <= 128).  A wait that gives up (after
+// merged in bcast[0..1] (the same bits for the whole workgroup, and in every member:
+// the merge order is fixed).  Called by every thread; uses one barrier.  Lane l of
+// wave 0 polls the slots of members l and l + 64 (G <= 128), merges its two, and
+// the wave merges its lanes' pairs with the butterfly of reduce.hpp (`Merge::lanes`;
+// lanes with no member hold the empty pair), log2 G steps on every lane at once.
+// Merging one member after the other from lane 0 instead kept all G pairs in
+// registers at once (12 more VGPRs at G = 16).  A wait that gives up (after
 // `spin_limit` polls; at once if spin_limit <= 0) leaves NaN in bcast[0..1], which
 // every op's epilogue carries into each value it writes for the row, and lowers
 // `spin_limit` to 1 so that the rest of the launch does not wait long again (a limit
@@ -129,23 +133,19 @@ __device__ __forceinline__ void wait_pairs(GroupRef g, int it, int &spin_limit, 
             __hip_atomic_store(g.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             bcast[2] = 1.0f;
         }
-        float acc_a = 0.0f, acc_b = 0.0f;
-#pragma unroll
-        for (int s = 0; s < kPer; ++s) {
-            const float va = __uint_as_float((uint32_t)wa[s]);
-            const float vb = __uint_as_float((uint32_t)wb[s]);
-#pragma unroll
-            for (int j = 0; j < 64 && j + 64 * s < G; ++j) {
-                const float ja = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(va), j));
-                const float jb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(vb), j));
-                if (s == 0 && j == 0) {
-                    acc_a = ja;
-                    acc_b = jb;
-                } else {
-                    merge2(acc_a, acc_b, ja, jb);
-                }
-            }
+        float acc_a = Merge::kEmptyA, acc_b = Merge::kEmptyB;
+        if (lane < G) {
+            acc_a = __uint_as_float((uint32_t)wa[0]);
+            acc_b = __uint_as_float((uint32_t)wb[0]);
         }
+        if constexpr (kPer == 2) {
+            if (lane + 64 < G)
+                merge2(acc_a, acc_b, __uint_as_float((uint32_t)wa[1]),
+                       __uint_as_float((uint32_t)wb[1]));
+        }
+        constexpr int W = G >= 64 ? 64 : G > 32 ? 64 : G > 16 ? 32 : G > 8 ? 16 : G > 4 ? 8
+                                                                              : G > 2 ? 4 : 2;
+        Merge::template lanes<W>(acc_a, acc_b);
         if (lane == 0) {
             bcast[0] = all_in ? acc_a : __builtin_nanf("");
             bcast[1] = all_in ? acc_b : __builtin_nanf("");

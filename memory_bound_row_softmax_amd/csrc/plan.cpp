@@ -192,7 +192,7 @@ static const Choice kTuned[4][2][kTunedBuckets] = {
       {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads},
      {{false, 16, 16, 1}, {false, 64, 16, 1}, {false, 16, 256, 1}, {false, 32, 256, 1},
       {false, 32, 256, 1}, {false, 32, 256, 1}, {false, 64, 256, 1}, {false, 32, 512, 1},
-      {false, 64, 512, 1}, {false, 64, 1024, 1}, {true, 64, 256, 8}, {true, 32, 1024, 8},
+      {false, 64, 512, 1}, {false, 64, 1024, 1}, {true, 64, 256, 8}, {true, 64, 256, 16},
       {true, 32, 1024, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads}},
 };
 
@@ -204,7 +204,8 @@ static const Choice kTuned[4][2][kTunedBuckets] = {
 // 151936 elements 5548 GB/s on 5 workgroups against 4105 on 8, 70000 5089 on 3
 // against 4129 on 4, 180000 5261 on 6 against 4713 on 8; the gradient at 70000 and
 // 90000 elements +25 % and +11 % on 3.  Seven lost to eight (4892 against 5119 at
-// 200000 elements), which defer the exchange (configs.hpp), so 7 is not compiled.
+// 200000 elements), which then deferred the exchange, so 7 is not compiled; eight
+// now run two workgroups per CU without the deferral (5791 GB/s at 200000).
 // These plans replace whatever the table chose for the row (64 values on 256 lanes
 // at 70000 elements, after the re-measurement above: 4890 GB/s against 5177 on
 // 64 x 512 x 3, offset-averaged); a row that needs 4 keeps the table's plan.

@@ -125,9 +125,18 @@ struct RowCtx {
 
 // ---------------------------------------------------------------- softmax
 
+// Merges of the split-row partials (grid_exchange.hpp): two pairs, or the pairs of
+// W lanes by a butterfly; kEmpty* is the pair of a lane with no member.
 struct MergeMaxSum {
+    static constexpr float kEmptyA = -__builtin_inff(), kEmptyB = 0.0f;
     __device__ __forceinline__ void operator()(float &m, float &s, float mj, float sj) const {
         MaxSum r = merge(MaxSum{m, s}, MaxSum{mj, sj});
+        m = r.m;
+        s = r.s;
+    }
+    template <int W>
+    __device__ __forceinline__ static void lanes(float &m, float &s) {
+        MaxSum r = lanes_reduce<W>(MaxSum{m, s}, OpMerge{});
         m = r.m;
         s = r.s;
     }
@@ -335,8 +344,14 @@ __global__ void __launch_bounds__(R)
 // ---------------------------------------------------------------- RMSNorm
 
 struct MergeSum {
+    static constexpr float kEmptyA = 0.0f, kEmptyB = 0.0f;
     __device__ __forceinline__ void operator()(float &q, float &unused, float qj, float) const {
         q = q + qj;
+        unused = 0.0f;
+    }
+    template <int W>
+    __device__ __forceinline__ static void lanes(float &q, float &unused) {
+        q = lanes_reduce<W>(q, OpSum{});
         unused = 0.0f;
     }
 };

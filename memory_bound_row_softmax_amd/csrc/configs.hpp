@@ -187,13 +187,15 @@ constexpr bool kDeferredExchange = RR_SPLIT_DEFER != 0;
 #define RR_DEFER_MIN_G 8
 #endif
 constexpr bool defer_split(int op, int elem_bytes, bool vec, int P, int R, int G) {
-    (void)elem_bytes;
     if (G < RR_DEFER_MIN_G) return false;
     if (op == kCfgSoftmaxBwd) return vec && P == 32 && R == 512;
     if (op == kCfgRmsnorm && P == 32 && R == 512) return true;
-    // bf16 softmax on 8: two non-deferred workgroups per CU beat one deferred
-    // (stream_waves; 262144 elements: 6246 against 5849 GB/s, offset-averaged)
-    if (P == 64 && R == 512 && elem_bytes == 2 && G == 8 && op == kCfgSoftmax) return false;
+    // bf16 softmax on 8 and 16: two non-deferred workgroups per CU beat one deferred
+    // (stream_waves; offset-averaged GB/s: 262144 elements on 8 6246 against 5849,
+    // 524288 on 16 5746 against 5577, 400000 on 16 5299 against 4594; on 32 they
+    // lost, 5443 against 5715 at 1048576)
+    if (P == 64 && R == 512 && elem_bytes == 2 && (G == 8 || G == 16) && op == kCfgSoftmax)
+        return false;
     if (P == 64 && R == 512) return op == kCfgSoftmax;
     if (P == 16 && R == 1024) return vec || op != kCfgXentGrad;
     return false;
@@ -233,11 +235,11 @@ constexpr int split_granule(int op, int C, int R, int G) {
 // a lane has at most 128 VGPRs and a CU holds two 512-lane workgroups, twice the
 // bytes in flight of one.  Listed are the 512-lane kernels that fit that budget
 // without spilling; 1 leaves the budget to the compiler.  bf16 softmax at G = 2..5
-// measured +3 to +7 % (16384 rows of 65536 to 151936 elements), at G = 8 (without
-// the deferred exchange, which does not fit) +7 % at 262144 and +23 % at 200000.
+// measured +3 to +7 % (16384 rows of 65536 to 151936 elements), at G = 8 and 16
+// (without the deferred exchange, which does not fit) +3 to +23 % (defer_split).
 constexpr int stream_waves(int op, int elem_bytes, bool vec, int P, int R, int G) {
     if (R != 512 || elem_bytes != 2) return 1;
-    if (op == kCfgSoftmax && vec && P == 64 && G >= 2 && G <= 8) return 4;
+    if (op == kCfgSoftmax && vec && P == 64 && G >= 2 && G <= 16) return 4;
     if (op == kCfgRmsnorm && !vec && P == 32 && (G == 2 || G == 4)) return 4;
     if (op == kCfgSoftmaxBwd && vec && P == 32 && G == 2) return 4;
     if (op == kCfgRmsnormBwd && !vec && P == 16 && G == 1) return 4;

@@ -306,11 +306,32 @@ static bool default_row(int op, int dtype, bool vec, int64_t M, int64_t N, Plan 
 // Cross-entropy: 16 values per lane for short rows, else 32; as many lanes as the
 // row needs, up to 256 lanes (512 for bf16 rows of 32768 or more, which then
 // still take two or more steps): 32 KiB of the row per step, which measured best
-// for long rows.
-static void default_xent(int dtype, int64_t N, int *P, int *R) {
+// for long f32 rows.  bf16 rows of 1025 to 32767 elements take two or more steps
+// of the lane count that pads the row least (ties to more lanes, at most eight
+// steps, since narrow lane groups reduce more often, and no narrower than keeps
+// two 256-lane workgroups per CU of a 256-CU device busy): a row streamed in steps
+// overlaps the next step's loads with the reduction of the last, and the lanes
+// past the row's end cost about as much as real ones.  Measured on MI355X (GB/s
+// averaged over output offsets; "one step": the next power of two above N / 32
+// lanes, the choice for f32):
+//   N                      1100  1500  2048  3000  4096  5000  6000  8192 12000 20000 24577
+//   16384 rows  one step   2439  3310  5461  4079  5905  3702  4366  6162  5200  6017  4625
+//               this       2993  4003  5447  5347  6133  5518  5999  6562  6297  6341  5556
+//    4096 rows  one step   1613  2099  3731  3067  4589  3046  3640  5071  4562  5329  4104
+//               this       1518  2131  3635  3442  5033  4182  4769  5603  5488  5908  4726
+static void default_xent(int dtype, int64_t M, int64_t N, int *P, int *R) {
     *P = N <= 512 ? 16 : 32;
-    int64_t r = next_pow2((N + *P - 1) / *P);
     const int64_t rmax = (dtype == kBf16 && N >= 32768) ? 512 : 256;
+    int64_t r = next_pow2((N + *P - 1) / *P);
+    if (dtype == kBf16 && N > 1024 && N < 32768) {
+        int64_t c0 = 16;
+        while (c0 < rmax && M * c0 < 2 * 256 * 256) c0 *= 2;
+        int64_t best_cap = INT64_MAX;
+        for (int64_t c = c0; c <= rmax && c * *P < N; c *= 2) {
+            const int64_t step = c * *P, steps = (N + step - 1) / step;
+            if (steps <= 8 && steps * step <= best_cap) { best_cap = steps * step; r = c; }
+        }
+    }
     if (r < 16) r = 16;
     if (r > rmax) r = rmax;
     *R = (int)r;
@@ -423,7 +444,7 @@ PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *ou
     if (op == kOpXent) {
         if (N > INT32_MAX) return kPlanInvalid;
         int P, R;
-        default_xent(dtype, N, &P, &R);
+        default_xent(dtype, M, N, &P, &R);
         if (fP) P = fP;
         if (fR) R = fR;
         if (!xent_config_exists(P, R)) return kPlanUnsupported;

@@ -133,6 +133,9 @@ def test_cross_entropy_streams(dt):
         p = rr.rr_plan_query(rr.RR_OP_XENT, 8192, N, dt)
         assert p["path"] == 2 and p["groups_per_row"] == 1 and p["ws_bytes"] == 0
         assert p["vals_per_lane"] in (16, 32) and 16 <= p["lanes_per_row"] <= (512 if dt else 256)
+    # bf16 rows of 1025..32767 elements take the least padding in two to eight steps; f32 one
+    for N, lanes in ((2048, 64 >> dt), (3000, 128 >> (2 * dt)), (4096, 128 >> dt), (8192, 256 >> dt), (16384, 256)):
+        assert rr.rr_plan_query(rr.RR_OP_XENT, 8192, N, dt)["lanes_per_row"] == lanes, N
 
 
 def test_forced_configurations(overrides):

@@ -39,7 +39,9 @@
     X(64, 256, 1) X(64, 256, 2) X(64, 256, 4) X(64, 256, 8) X(64, 256, 16)                  \
     X(64, 512, 1) X(64, 512, 2) X(64, 512, 4) X(64, 512, 8) X(64, 512, 16)                  \
     X(64, 512, 32) X(64, 512, 64) X(64, 512, 128)                                           \
-    X(64, 512, 3) X(64, 512, 5) X(64, 512, 6)
+    X(64, 512, 3) X(64, 512, 5) X(64, 512, 6)                                           \
+    X(64, 256, 3) X(64, 256, 5) X(64, 256, 6) X(64, 256, 7) X(64, 256, 9) X(64, 256, 10)   \
+    X(64, 256, 11) X(64, 256, 12) X(64, 256, 13) X(64, 256, 14) X(64, 256, 15)
 
 // Packed bf16 RMSNorm stream kernels (128-bit path only, see packed_bf16.hpp),
 // named by (R, G): each lane keeps kPackedP = 128 bf16 values as 64 VGPRs of raw
@@ -109,12 +111,15 @@ constexpr bool stream_config_enabled(int op, int elem_bytes, bool vec, int P, in
     // 128 workgroups per row (4194304 elements on chip): softmax and RMSNorm forward
     if (G > 64 && op != kCfgSoftmax && op != kCfgRmsnorm) return false;
     // Workgroups per row that are not a power of two: bf16 softmax and cross-entropy
-    // gradient rows, and fp32 softmax rows, on 64 values x 512 lanes take exactly as
-    // many as the row needs (the planner), so that most registers hold an element.
-    if ((G & (G - 1)) != 0)
+    // gradient rows, and fp32 softmax rows, on 64 values x 512 lanes, and bf16
+    // cross-entropy gradient rows on 64 values x 256 lanes, take exactly as many as
+    // the row needs (the planner), so that most registers hold an element.
+    if ((G & (G - 1)) != 0) {
+        if (R == 256) return vec && P == 64 && elem_bytes == 2 && op == kCfgXentGrad;
         return vec && P == 64 && R == 512 &&
                ((elem_bytes == 2 && (op == kCfgSoftmax || op == kCfgXentGrad)) ||
                 (elem_bytes == 4 && op == kCfgSoftmax));
+    }
     if (op == kCfgXentGrad && elem_bytes == 4 && P == 32 && R == 1024) return false;
     // softmax backward keeps two rows (y, dy) per buffer: about 4P + 40 VGPRs
     if (op == kCfgSoftmaxBwd) return vec ? (R == 1024 ? P <= 16 : P <= 32) : P <= 16;
@@ -237,7 +242,11 @@ constexpr int split_granule(int op, int C, int R, int G) {
 // without spilling; 1 leaves the budget to the compiler.  bf16 softmax at G = 2..5
 // measured +3 to +7 % (16384 rows of 65536 to 151936 elements), at G = 8 and 16
 // (without the deferred exchange, which does not fit) +3 to +23 % (defer_split).
+// The bf16 cross-entropy gradient on 64 values x 256 lanes (G >= 3) fits it too:
+// four workgroups per CU instead of three, +2 to +11 % at 8 and 16 workgroups
+// (16384 rows of 131072 to 262144 elements; 151936 on 16: 3990 -> 4415 GB/s).
 constexpr int stream_waves(int op, int elem_bytes, bool vec, int P, int R, int G) {
+    if (op == kCfgXentGrad && elem_bytes == 2 && vec && P == 64 && R == 256 && G >= 3) return 4;
     if (R != 512 || elem_bytes != 2) return 1;
     if (op == kCfgSoftmax && vec && P == 64 && G >= 2 && G <= 16) return 4;
     if (op == kCfgRmsnorm && !vec && P == 32 && (G == 2 || G == 4)) return 4;

@@ -196,26 +196,55 @@ static const Choice kTuned[4][2][kTunedBuckets] = {
       {true, 32, 1024, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads}},
 };
 
-// bf16 softmax and cross-entropy gradient rows split over 64 values x 512 lanes take
-// exactly as many workgroups as the row needs when that is 3, 5 or 6 (compiled
-// besides the powers of two) instead of the next power of two.  A lane runs every
-// register through the exponential whether or not it holds an element, and at two
-// bytes per element that work shows.  Measured on MI355X (bf16 softmax, 16384 rows):
-// 151936 elements 5548 GB/s on 5 workgroups against 4105 on 8, 70000 5089 on 3
-// against 4129 on 4, 180000 5261 on 6 against 4713 on 8; the gradient at 70000 and
-// 90000 elements +25 % and +11 % on 3.  Seven lost to eight (4892 against 5119 at
-// 200000 elements), which then deferred the exchange, so 7 is not compiled; eight
-// now run two workgroups per CU without the deferral (5791 GB/s at 200000).
-// These plans replace whatever the table chose for the row (64 values on 256 lanes
-// at 70000 elements, after the re-measurement above: 4890 GB/s against 5177 on
-// 64 x 512 x 3, offset-averaged); a row that needs 4 keeps the table's plan.
+// Up to this many rows, a row that one workgroup of the stream kernels holds is
+// not split: a persistent row group then has only a few rows, so the split row's
+// exchange is no longer hidden behind the next rows' loads.  Measured on MI355X
+// for fp32 rows of 32768 elements (softmax, M = 512 .. 4096): 5.67-5.92 TB/s on
+// one workgroup of 32 values x 1024 lanes against 3.60-5.53 split over two; at
+// 8192 rows and more the table's split plan is as fast or faster.
+constexpr int64_t kFewRows = 4096;
+
+// bf16 softmax rows split over 64 values x 512 lanes take exactly as many
+// workgroups as the row needs when that is 3, 5 or 6 (compiled besides the powers
+// of two) instead of the next power of two.  A lane runs every register through the
+// exponential whether or not it holds an element, and at two bytes per element that
+// work shows.  Measured on MI355X (bf16 softmax, 16384 rows): 151936 elements 5548
+// GB/s on 5 workgroups against 4105 on 8, 70000 5089 on 3 against 4129 on 4, 180000
+// 5261 on 6 against 4713 on 8.  Seven lost to eight (4892 against 5119 at 200000
+// elements), which then deferred the exchange, so 7 is not compiled; eight now run
+// two workgroups per CU without the deferral (5791 GB/s at 200000).  These plans
+// replace whatever the table chose for the row (64 values on 256 lanes at 70000
+// elements, after the re-measurement above: 4890 GB/s against 5177 on 64 x 512 x 3,
+// offset-averaged); a row that needs 4 keeps the table's plan.
 // fp32 softmax rows take 5 or 6 the same way (offset-averaged GB/s, exact against the
 // table: 151936 elements 6155 on 5 against 5472 on 8, 163840 6134 against 5873,
 // 180000 6189 on 6 against 5778); on 3 they gained at 70000 elements (+2 %) but lost
 // at 98304 (-5 %), so fp32 keeps the table there.
+// The bf16 cross-entropy gradient, whose 64 x 512 kernels need more than 128 VGPRs
+// (one workgroup per CU), takes 64 values x 256 lanes on exactly ceil(N / 16384)
+// workgroups from 3 to 16 (every count compiled; four workgroups per CU) for rows of
+// 32769 to 262144 elements, whatever the table chose.  Offset-averaged GB/s, 16384
+// rows, the previous plan -> this one: 40000 elements (block 64 x 1024) 4377 ->
+// 5293 (on 3), 65536 (block) 5515 -> 6104 (4), 70000 (64 x 512 x 3) 3501 -> 5232
+// (5), 100000 (64 x 256 x 8) 4240 -> 5369 (7), 151936 (64 x 512 x 5) 4073 -> 5450
+// (10), 200000 (64 x 256 x 16) 3936 -> 5337 (13).  With few rows the split row
+// still won over the block kernel (512 rows: 40000 elements 3730 -> 4880, 65536
+// 5180 -> 5600; 256 rows of 151936: 3620 on 64 x 512 x 5 -> 5100).
 static void exact_groups(int op, int dtype, bool vec, int64_t N, Plan *p) {
-    if (!p->stream || p->G <= 2 || !vec) return;
-    const bool bf16 = dtype == kBf16 && (op == kOpSoftmax || op == kOpXentGrad);
+    if (!vec) return;
+    if (op == kOpXentGrad && dtype == kBf16) {
+        const int64_t need = (N + 64 * 256 - 1) / (64 * 256);
+        if (need >= 3 && need <= 16 &&
+            stream_config_ok(op, dtype, vec, 64, 256, (int)need)) {
+            p->stream = true;
+            p->P = 64;
+            p->R = 256;
+            p->G = (int)need;
+        }
+        return;
+    }
+    if (!p->stream || p->G <= 2) return;
+    const bool bf16 = dtype == kBf16 && op == kOpSoftmax;
     const bool f32 = dtype != kBf16 && op == kOpSoftmax;
     if (!bf16 && !f32) return;
     const int64_t need = (N + 64 * 512 - 1) / (64 * 512);
@@ -252,13 +281,6 @@ static bool try_choice(int op, int dtype, bool vec, int64_t N, Choice c, Plan *p
     return true;
 }
 
-// Up to this many rows, a row that one workgroup of the stream kernels holds is
-// not split: a persistent row group then has only a few rows, so the split row's
-// exchange is no longer hidden behind the next rows' loads.  Measured on MI355X
-// for fp32 rows of 32768 elements (softmax, M = 512 .. 4096): 5.67-5.92 TB/s on
-// one workgroup of 32 values x 1024 lanes against 3.60-5.53 split over two; at
-// 8192 rows and more the table's split plan is as fast or faster.
-constexpr int64_t kFewRows = 4096;
 
 static bool default_row(int op, int dtype, bool vec, int64_t M, int64_t N, Plan *p) {
     const int o = op == kOpRmsnorm ? 1 : op == kOpSoftmaxBwd ? 2 : op == kOpXentGrad ? 3 : 0;

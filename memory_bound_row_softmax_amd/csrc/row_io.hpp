@@ -71,6 +71,33 @@ __device__ __forceinline__ Lane lane_of(int member, int l) {
     }
 }
 
+// The inverse of lane_of: the member, lane and register chunk i (of C) whose part
+// holds chunk k >= 0 of the row; i >= C when k lies past every lane's part.  The
+// divisors are compile-time constants.
+template <int OP, class E, int C, int R, int G>
+__device__ __forceinline__ void chunk_owner(int k, int &member, int &l, int &i) {
+    if constexpr (G == 1) {
+        member = 0;
+        l = k % R;
+        i = k / R;
+    } else {
+        constexpr int K = split_granule(OP, C, R, G);
+        if constexpr (K <= R) {
+            // chunk(i) = gi * K + k % K + i * R * G with gi = (l / K) * G + member
+            const int rem = k % (R * G), gi = rem / K;
+            member = gi % G;
+            l = (gi / G) * K + rem % K;
+            i = k / (R * G);
+        } else {
+            // chunk(i) = member * K + (i % q) * R + l + (i / q) * G * K, q = K / R
+            const int rem = k % (G * K), in = rem % K;
+            member = rem / K;
+            l = in % R;
+            i = (k / (G * K)) * (K / R) + in / R;
+        }
+    }
+}
+
 // Whether every chunk that member `member` of a row's G workgroups owns (C chunks
 // in each of its lanes, layout of lane_of) lies wholly inside a row of N elements:
 // whether the last chunk of its last lane does.

@@ -145,10 +145,12 @@ struct MergeMaxSum {
 // What a softmax kernel writes for a row, given e_j = exp(x_j - mu) in registers
 // and the factor `scale` that turns e_j into the softmax p_j.  An output policy
 // `Out` (a kernel argument) hands out one Epi per row:
-//   capture<E, C, R>(v, ln, N)      sees the lane's raw values before the exp;
-//   apply<E, C, R>(v, scale, M, S, ctx, valid)  turns e into the values
-//                                   to store and writes any per-row outputs
-//                                   (M, S: the row's max and sum of exp(x - M)).
+//   capture<E, C, R, G, STREAM>(v, ctx)  sees the lane's raw values before the exp;
+//   apply<E, C, R, STREAM>(v, scale, mu, M, S, ctx, valid)  turns e = exp(x - mu)
+//                                   into the values to store and writes any
+//                                   per-row outputs (M, S: the row's max and sum
+//                                   of exp(x - M));
+//   fixup<E, R, STREAM>(yv, valid)  runs after the lane's stores of the row.
 // A stream kernel keeps kExtra more registers per row buffer for the row's own
 // inputs: stash(extra, r) fills them when the row's loads are issued (so they
 // arrive with the row), and epi(extra, r) builds the Epi when the row is
@@ -157,14 +159,16 @@ struct SoftmaxOut {
     static constexpr int kCfg = kCfgSoftmax;  // configuration menu predicates
     static constexpr int kExtra = 0;
     struct Epi {
-        template <class E, int C, int R>
-        __device__ __forceinline__ void capture(const float *, Lane, int) {}
-        template <class E, int C, int R>
-        __device__ __forceinline__ void apply(float *v, float scale, float, float,
+        template <class E, int C, int R, int G, bool STREAM>
+        __device__ __forceinline__ void capture(const float *, const RowCtx &) {}
+        template <class E, int C, int R, bool STREAM>
+        __device__ __forceinline__ void apply(float *v, float scale, float, float, float,
                                               const RowCtx &, bool) {
 #pragma unroll
             for (int j = 0; j < C * E::VPC; ++j) v[j] *= scale;
         }
+        template <class E, int R, bool STREAM>
+        __device__ __forceinline__ void fixup(RowView, bool) {}
     };
     __device__ __forceinline__ Epi row(int64_t) const { return {}; }
     __device__ __forceinline__ void stash(float *, int64_t) const {}
@@ -173,10 +177,10 @@ struct SoftmaxOut {
 
 // Passes 1 and 2 on a lane's loaded part v of the row: the row max m (over this
 // workgroup's part), e = exp(x - m) in place and its sum s.
-template <class E, int P, int R, bool STREAM, class Epi>
+template <class E, int P, int R, int G, bool STREAM, class Epi>
 __device__ __forceinline__ MaxSum softmax_local(float *v, RowCtx &c, Epi &epi) {
     constexpr int C = P / E::VPC;
-    epi.template capture<E, C, R>(v, c.ln, c.N);
+    epi.template capture<E, C, R, G, STREAM>(v, c);
     if (!c.full) mask_part<E, C, R, STREAM>(c.ln, c.N, -INFINITY, v);
 
     // pass 1: row max
@@ -205,15 +209,16 @@ __device__ __forceinline__ void softmax_apply(float *v, RowView yv, bool valid, 
         scale = __builtin_amdgcn_rcpf(Srow);
     else
         scale = exp_shift(loc.m, safe_max(Mrow)) * __builtin_amdgcn_rcpf(Srow);
-    epi.template apply<E, C, R>(v, scale, Mrow, Srow, c, valid);
+    epi.template apply<E, C, R, STREAM>(v, scale, safe_max(loc.m), Mrow, Srow, c, valid);
     store_part<E, C, R, VEC, STREAM>(yv, c.ln, c.N, valid, c.full, v);
+    epi.template fixup<E, R, STREAM>(yv, valid);
 }
 
 // Passes 1-3 on a lane's loaded part v of the row, then the store.
 template <class E, int P, int R, int G, bool VEC, bool STREAM, class Epi>
 __device__ __forceinline__ void softmax_finish(float *v, RowView yv, bool valid, RowCtx &c,
                                                Epi &epi) {
-    const MaxSum loc = softmax_local<E, P, R, STREAM>(v, c, epi);
+    const MaxSum loc = softmax_local<E, P, R, G, STREAM>(v, c, epi);
     if constexpr (G == 1) {
         softmax_apply<E, P, R, G, VEC, STREAM>(v, yv, valid, c, epi, loc, loc.m, loc.s);
     } else {
@@ -298,7 +303,7 @@ __global__ void __launch_bounds__(R)
             if (more) {
                 if constexpr (VEC) widen_part<E, C>(buf[K]);
                 epis[K] = out.epi(buf[K] + P, row);
-                cur = softmax_local<E, P, R, true>(buf[K], c, epis[K]);
+                cur = softmax_local<E, P, R, G, true>(buf[K], c, epis[K]);
                 publish_pair<G>(c.g, c.member, c.it, cur.m, cur.s);
             } else {
                 // no reduction (and its barriers) in this step: every wave has read

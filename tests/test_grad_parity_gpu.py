@@ -50,15 +50,19 @@ def test_xent_grad(M, N, dtype):
     parity_xent_grad(x, synth.labels(M, N), _dloss(M), dtype, f"xent grad {dtype} {M}x{N}")
 
 
-@pytest.mark.parametrize("N", [70000, 90000])
-def test_xent_grad_bf16_on_three_workgroups(N):
-    """bf16 rows of 65537 to 98304 elements: split over exactly 3 workgroups."""
+@pytest.mark.parametrize("N,G", [(40000, 3), (70000, 5), (90000, 6), (100000, 7),
+                                 (140000, 9), (151936, 10), (180000, 11), (196608, 12),
+                                 (200000, 13), (220000, 14), (240000, 15)])
+def test_xent_grad_bf16_exact_groups(N, G):
+    """bf16 rows of 32769 to 262144 elements: split over exactly ceil(N / 16384)
+    workgroups of 64 values x 256 lanes (the plan at 16384 rows; 50 rows run)."""
     M = 50
     p = rr.rr_plan_query(rr.RR_OP_XENT_GRAD, 16384, N, rr.RR_BF16)
-    assert (p["path"], p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]) == (1, 64, 512, 3)
-    say("xent grad G=3", M, N)
+    assert (p["path"], p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]) == (1, 64, 256, G)
+    say("xent grad exact groups", G, M, N)
     x = synth.normal(M, N, sigma=2.0, dtype="bf16")
-    parity_xent_grad(x, synth.labels(M, N), _dloss(M), "bf16", f"xent grad bf16 G=3 {M}x{N}")
+    with forced(64, 256, G, kind="stream"):
+        parity_xent_grad(x, synth.labels(M, N), _dloss(M), "bf16", f"xent grad bf16 G={G} {M}x{N}")
 
 
 FORCED = [("stream", 64, 256, 2, 300, 20000), ("stream", 32, 512, 16, 97, 70000),
@@ -66,7 +70,12 @@ FORCED = [("stream", 64, 256, 2, 300, 20000), ("stream", 32, 512, 16, 97, 70000)
           ("stream", 16, 1024, 1, 700, 16000), ("stream", 32, 512, 1, 3, 16384),
           ("stream", 16, 1024, 8, 200, 100000), ("block", 16, 16, 1, 100, 256),
           ("block", 32, 128, 1, 31, 4000), ("block", 16, 1024, 1, 5, 16384),
-          ("block", 64, 1024, 1, 6, 65536), ("stream", 64, 512, 32, 5, 1_000_000)]
+          ("block", 64, 1024, 1, 6, 65536), ("stream", 64, 512, 32, 5, 1_000_000),
+          # bf16 on 64 x 256 lanes rewrites the label's element after the row's
+          # stores: 1, 2, 4, 8, 10 and 16 workgroups, labels in every member
+          ("stream", 64, 256, 1, 400, 16000), ("stream", 64, 256, 4, 120, 60000),
+          ("stream", 64, 256, 8, 80, 131072), ("stream", 64, 256, 10, 60, 151936),
+          ("stream", 64, 256, 16, 40, 250000), ("stream", 32, 512, 2, 200, 30000)]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)

@@ -122,6 +122,15 @@ def test_bf16_softmax_takes_exactly_the_workgroups_a_row_needs(G, N):
     parity_softmax(_x(M, N, "bf16", sigma=2.0), "bf16", f"softmax bf16 G={G} {M}x{N}")
 
 
+@pytest.mark.parametrize("M,N", [(40, 151936), (30, 140000), (25, 163840)])
+def test_bf16_softmax_on_ten_workgroups_of_64x256(M, N):
+    """bf16 rows split over 10 workgroups of 64 values x 256 lanes: the last member
+    partly or wholly empty, or every member full."""
+    say("softmax bf16 64x256x10", M, N)
+    with forced(64, 256, 10, kind="stream"):
+        parity_softmax(_x(M, N, "bf16", sigma=2.0), "bf16", f"softmax bf16 64,256,10 {M}x{N}")
+
+
 @pytest.mark.parametrize("G,N", EXACT_GROUPS)
 def test_fp32_softmax_exact_groups(G, N):
     """fp32 rows on 64 values x 512 lanes split over 3, 5 or 6 workgroups (the planner

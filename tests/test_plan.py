@@ -79,10 +79,11 @@ def test_rows_up_to_4m_elements_stay_on_chip():
 
 
 def test_bf16_softmax_rows_take_exactly_the_workgroups_they_need():
-    """bf16 softmax (and cross-entropy gradient) rows that need 3, 5 or 6 workgroups
-    of 64 values x 512 lanes get exactly that many (seven take eight, four keep the
-    table's 64 x 256 x 8); fp32 softmax rows that need 5 or 6 too; other fp32 rows
-    and forced plans keep powers of two."""
+    """bf16 softmax rows that need 3, 5 or 6 workgroups of 64 values x 512 lanes get
+    exactly that many (seven take eight, four keep the table's 64 x 256 x 8); fp32
+    softmax rows that need 5 or 6 too; bf16 cross-entropy gradient rows of 32769 to
+    262144 elements take exactly ceil(N / 16384) workgroups of 64 x 256; other fp32
+    rows and forced plans keep powers of two."""
     for N, (P, R, G) in ((70000, (64, 512, 3)), (100000, (64, 256, 8)), (151936, (64, 512, 5)),
                          (180000, (64, 512, 6)), (200000, (64, 512, 8)), (262144, (64, 512, 8))):
         p = rr.rr_plan_query(rr.RR_OP_SOFTMAX, 16384, N, rr.RR_BF16)
@@ -96,7 +97,20 @@ def test_bf16_softmax_rows_take_exactly_the_workgroups_they_need():
             assert f32["groups_per_row"] in (2, 4, 8), (N, f32)
         # the fp32 cross-entropy gradient keeps powers of two
         assert rr.rr_plan_query(rr.RR_OP_XENT_GRAD, 8192, N, rr.RR_F32)["groups_per_row"] in (2, 4, 8, 16)
-    assert rr.rr_plan_query(rr.RR_OP_XENT_GRAD, 16384, 90000, rr.RR_BF16)["groups_per_row"] == 3
+    for N, G in ((32768, None), (32769, 3), (49152, 3), (65536, 4), (70000, 5), (90000, 6),
+                 (100000, 7), (131072, 8), (151936, 10), (180000, 11), (200000, 13),
+                 (262144, 16), (262145, None)):
+        p = rr.rr_plan_query(rr.RR_OP_XENT_GRAD, 16384, N, rr.RR_BF16)
+        if G is None:
+            assert (p["lanes_per_row"], p["groups_per_row"]) != (256, (N + 16383) // 16384), (N, p)
+        else:
+            assert (p["path"], p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]) == \
+                (1, 64, 256, G), (N, p)
+            assert p["ws_bytes"] == 256 + 1024 * (64 + 64 * G)
+    # also with few rows
+    for M, N, G in ((512, 40000, 3), (4096, 65536, 4), (256, 151936, 10)):
+        p = rr.rr_plan_query(rr.RR_OP_XENT_GRAD, M, N, rr.RR_BF16)
+        assert (p["path"], p["lanes_per_row"], p["groups_per_row"]) == (1, 256, G), (M, N, p)
     # the per-element path has no such plans
     assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 16384, 151935, rr.RR_BF16, False)["groups_per_row"] in (4, 8, 16)
 

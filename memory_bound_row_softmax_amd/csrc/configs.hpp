@@ -102,12 +102,13 @@ constexpr bool block_config_enabled(int op, int elem_bytes, bool vec, int P, int
 // The cross-entropy gradient epilogue keeps the label, dloss and the label's logit
 // per row: fp32 with 32 values on 1024 lanes no longer fits in 128 VGPRs.
 constexpr bool stream_config_enabled(int op, int elem_bytes, bool vec, int P, int R, int G) {
-    // The per-element path keeps P <= 16, except unaligned bf16 softmax and RMSNorm
-    // rows split over 2 to 8 workgroups: 32 values on 512 lanes (the planner uses
-    // them up to 81920 elements).
+    // The per-element path keeps P <= 16, except unaligned bf16 softmax, RMSNorm and
+    // cross-entropy gradient rows split over 2 to 8 workgroups: 32 values on 512
+    // lanes (the planner uses them up to 81920 elements; the gradient at 8192 x
+    // 50257 ran at 2363 GB/s on a 64 x 1024 block kernel, 3536 on 32 x 512 x 4).
     if (!vec && P > 16)
         return elem_bytes == 2 && P == 32 && R == 512 && G >= 2 && G <= 8 &&
-               (op == kCfgSoftmax || op == kCfgRmsnorm);
+               (op == kCfgSoftmax || op == kCfgRmsnorm || op == kCfgXentGrad);
     // 128 workgroups per row (4194304 elements on chip): softmax and RMSNorm forward
     if (G > 64 && op != kCfgSoftmax && op != kCfgRmsnorm) return false;
     // Workgroups per row that are not a power of two: bf16 softmax and cross-entropy

@@ -18,8 +18,8 @@ import memory_bound_row_softmax_amd as rr
 import oracle
 import synth
 from _gpu import (DEV, check_out, forced, from_dev, parity_rmsnorm, parity_softmax,
-                  parity_xent, run_softmax, say, to_dev)
-from _verify import check_f32
+                  parity_xent, run_softmax, say, to_dev, xent_grad_scale)
+from _verify import check_f32, check_grad
 
 pytestmark = pytest.mark.gpu
 
@@ -122,15 +122,6 @@ def test_bf16_softmax_takes_exactly_the_workgroups_a_row_needs(G, N):
     parity_softmax(_x(M, N, "bf16", sigma=2.0), "bf16", f"softmax bf16 G={G} {M}x{N}")
 
 
-@pytest.mark.parametrize("M,N", [(40, 151936), (30, 140000), (25, 163840)])
-def test_bf16_softmax_on_ten_workgroups_of_64x256(M, N):
-    """bf16 rows split over 10 workgroups of 64 values x 256 lanes: the last member
-    partly or wholly empty, or every member full."""
-    say("softmax bf16 64x256x10", M, N)
-    with forced(64, 256, 10, kind="stream"):
-        parity_softmax(_x(M, N, "bf16", sigma=2.0), "bf16", f"softmax bf16 64,256,10 {M}x{N}")
-
-
 @pytest.mark.parametrize("G,N", EXACT_GROUPS)
 def test_fp32_softmax_exact_groups(G, N):
     """fp32 rows on 64 values x 512 lanes split over 3, 5 or 6 workgroups (the planner
@@ -184,11 +175,14 @@ def test_forced_xent_plans(P, R, dtype):
 def test_unaligned_bf16_split_rows_wide_lanes(N):
     """Unaligned bf16 softmax and RMSNorm rows of 16385 to 81920 elements: 32 values on
     512 lanes over 2 to 8 workgroups (16 on 1024 past that), with a base one element
-    past a 16-byte boundary and 40 rows, so row groups take several rows."""
+    past a 16-byte boundary and 40 rows, so row groups take several rows.  The
+    cross-entropy gradient takes them past 32768 elements."""
     M = 40
-    for code in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
+    wide = N <= 81920
+    for code in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM, rr.RR_OP_XENT_GRAD):
         p = rr.rr_plan_query(code, M, N, rr.RR_BF16, False)
-        wide = N <= 81920
+        if code == rr.RR_OP_XENT_GRAD and N <= 32768:
+            continue  # the table's block kernels
         assert (p["vals_per_lane"], p["lanes_per_row"]) == ((32, 512) if wide else (16, 1024))
         assert 2 <= p["groups_per_row"] <= (8 if wide else 16)
     x_np = _x(M, N, "bf16", sigma=2.0)
@@ -205,6 +199,17 @@ def test_unaligned_bf16_split_rows_wide_lanes(N):
     rr.rr_rmsnorm_fwd(xs, wt, 1e-6, y=ys, ws=rr.workspace(rr.RR_OP_RMSNORM, M, N, rr.RR_BF16, DEV))
     torch.cuda.synchronize()
     check_out(from_dev(ys), oracle.rmsnorm(x_np, w_np, 1e-6), "bf16", f"unaligned wide rmsnorm {N}")
+    say("unaligned wide xent grad", N)
+    lab = synth.labels(M, N)
+    g = synth.uniform(1, M, lo=0.5, hi=1.5, stream=synth.STREAM_DLOSS)[0]
+    loss, lse, dx = rr.rr_cross_entropy_fwd_bwd(xs, torch.from_numpy(lab).to(DEV),
+                                                torch.from_numpy(g).to(DEV), dlogits=ys)
+    torch.cuda.synchronize()
+    ref_loss, ref_lse, ref_dx = oracle.cross_entropy_grad(x_np, lab, g)
+    check_f32(loss.cpu().numpy(), ref_loss, f"unaligned wide xent grad loss {N}")
+    check_f32(lse.cpu().numpy(), ref_lse, f"unaligned wide xent grad lse {N}")
+    check_grad(from_dev(dx), ref_dx, xent_grad_scale(x_np, lab, g), "bf16",
+               f"unaligned wide xent grad dx {N}")
 
 
 @pytest.mark.parametrize("dtype", DTYPES)

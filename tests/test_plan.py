@@ -210,8 +210,9 @@ def test_short_unaligned_rows_take_small_lane_groups(overrides):
 
 def test_unaligned_bf16_split_rows_take_wide_lanes():
     """Unaligned bf16 softmax and RMSNorm rows split over 2 to 8 workgroups take 32
-    values on 512 lanes up to 81920 elements; other ops, fp32 and longer rows keep
-    16 values per lane on the per-element path."""
+    values on 512 lanes up to 81920 elements, and cross-entropy gradient rows past
+    32768 elements; other ops, fp32 and longer rows keep 16 values per lane on the
+    per-element path."""
     for op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
         for N in (16385, 32001, 50257, 65537, 81920):
             p = rr.rr_plan_query(op, 8192, N, rr.RR_BF16, False)
@@ -221,7 +222,12 @@ def test_unaligned_bf16_split_rows_take_wide_lanes():
             assert rr.rr_plan_query(op, 8192, N, rr.RR_BF16, False)["vals_per_lane"] == 16
         for N in (32001, 50257):
             assert rr.rr_plan_query(op, 8192, N, rr.RR_F32, False)["vals_per_lane"] <= 16
-    assert rr.rr_plan_query(rr.RR_OP_XENT_GRAD, 8192, 50257, rr.RR_BF16, False)["vals_per_lane"] == 16
+    for N in (32769, 50257, 81920):
+        p = rr.rr_plan_query(rr.RR_OP_XENT_GRAD, 8192, N, rr.RR_BF16, False)
+        assert (p["vals_per_lane"], p["lanes_per_row"]) == (32, 512), (N, p)
+        assert 2 <= p["groups_per_row"] <= 8
+    assert rr.rr_plan_query(rr.RR_OP_XENT_GRAD, 8192, 100001, rr.RR_BF16, False)["vals_per_lane"] == 16
+    assert rr.rr_plan_query(rr.RR_OP_SOFTMAX_BWD, 8192, 50257, rr.RR_BF16, False)["vals_per_lane"] <= 16
 
 
 def test_invalid_plan_arguments():

@@ -212,6 +212,42 @@ def test_unaligned_bf16_split_rows_wide_lanes(N):
                f"unaligned wide xent grad dx {N}")
 
 
+UNALIGNED_ROWS = [  # (kind, P, R, G, N): aligned tensors whose row length is not a
+    # multiple of 16 bytes, so the rows start at every offset modulo 16 bytes
+    ("block", 16, 512, 1, 5001), ("block", 32, 256, 1, 8191), ("stream", 16, 1024, 1, 16001),
+    ("stream", 16, 1024, 2, 30001), ("stream", 32, 512, 4, 50257),
+    ("stream", 16, 1024, 8, 120001), ("stream", 16, 1024, 16, 250001),
+    ("stream", 16, 1024, 1, 16383), ("stream", 16, 1024, 1, 16381)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("kind,P,R,G,N", UNALIGNED_ROWS)
+def test_rows_at_every_offset(kind, P, R, G, N, dtype):
+    """Softmax and the cross-entropy gradient on 37 rows that start at every offset
+    modulo 16 bytes, on forced per-element plans, element by element against the
+    oracle."""
+    M = 37
+    code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
+    with forced(P, R, G, kind=kind):
+        try:
+            rr.rr_plan_query(rr.RR_OP_SOFTMAX, M, N, code, False)
+        except rr.RRError:
+            pytest.skip("not compiled for this dtype")
+        say("rows at every offset", kind, P, R, G, dtype, M, N)
+        x_np = _x(M, N, dtype, sigma=2.0)
+        parity_softmax(x_np, dtype, f"offset rows softmax {kind} {P},{R},{G} {N}")
+        lab = synth.labels(M, N)
+        g = synth.uniform(1, M, lo=0.5, hi=1.5, stream=synth.STREAM_DLOSS)[0]
+        loss, lse, dx = rr.rr_cross_entropy_fwd_bwd(to_dev(x_np, dtype), torch.from_numpy(lab).to(DEV),
+                                                    torch.from_numpy(g).to(DEV))
+        torch.cuda.synchronize()
+        ref_loss, ref_lse, ref_dx = oracle.cross_entropy_grad(x_np, lab, g)
+        check_f32(loss.cpu().numpy(), ref_loss, f"offset rows xent grad loss {N}")
+        check_f32(lse.cpu().numpy(), ref_lse, f"offset rows xent grad lse {N}")
+        check_grad(from_dev(dx), ref_dx, xent_grad_scale(x_np, lab, g), dtype,
+                   f"offset rows xent grad dx {kind} {P},{R},{G} {N}")
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("N", [64, 1000, 4096, 40000, 131072])
 def test_unaligned_rows_take_the_element_path(N, dtype):

@@ -43,13 +43,16 @@ SOFTMAX_SPIKY = Workload("softmax_f32_16384x131072_spiky", "softmax", "f32", 163
 FIXED = [SOFTMAX_SMALL, RMSNORM_MAIN, XENT_VOCAB, SOFTMAX_SPIKY]
 
 # Backward passes (training): the cross-entropy forward fused with its gradient
-# on the vocab-like shape above and on a bf16 32K vocabulary (per-row upstream
+# on the vocab-like shape above, on a bf16 32K vocabulary and on a bf16 151936-entry
+# vocabulary (a row that does not fill a power of two of workgroups; per-row upstream
 # gradients dloss ~ U(0.5, 1.5)); the softmax backward from the softmax of
 # x ~ N(0, sigma=2) with dy ~ N(0, 1); the RMSNorm backward at the forward's
 # shape and a wider fp32 one, x and w as for the forward, dy ~ N(0, 1), rstd from
 # the forward.
 BACKWARD = [Workload("xentgrad_f32_8192x131072", "xent_grad", "f32", 8192, 131072, sigma=2.0),
             Workload("xentgrad_bf16_16384x32768", "xent_grad", "bf16", 16384, 32768, sigma=2.0),
+            Workload("xentgrad_bf16_16384x151936", "xent_grad", "bf16", 16384, 151936,
+                     sigma=2.0),
             Workload("softmaxbwd_f32_16384x4096", "softmax_bwd", "f32", 16384, 4096, sigma=2.0),
             Workload("softmaxbwd_bf16_16384x32768", "softmax_bwd", "bf16", 16384, 32768,
                      sigma=2.0),

@@ -38,7 +38,7 @@
     X(32, 1024, 1) X(32, 1024, 2) X(32, 1024, 4) X(32, 1024, 8) X(32, 1024, 16)             \
     X(64, 256, 1) X(64, 256, 2) X(64, 256, 4) X(64, 256, 8) X(64, 256, 16)                  \
     X(64, 512, 1) X(64, 512, 2) X(64, 512, 4) X(64, 512, 8) X(64, 512, 16)                  \
-    X(64, 512, 32) X(64, 512, 64) X(64, 512, 128)                                           \
+    X(64, 512, 32) X(64, 512, 64) X(64, 512, 128) X(64, 512, 256)                           \
     X(64, 512, 3) X(64, 512, 5) X(64, 512, 6)                                           \
     X(64, 256, 3) X(64, 256, 5) X(64, 256, 6) X(64, 256, 7) X(64, 256, 9) X(64, 256, 10)   \
     X(64, 256, 11) X(64, 256, 12) X(64, 256, 13) X(64, 256, 14) X(64, 256, 15)
@@ -48,7 +48,7 @@
 // chunks.  A plan names them with P = kPackedP.
 constexpr int kPackedP = 128;
 #define RR_PACKED_CONFIGS(X) \
-    X(512, 1) X(512, 2) X(512, 4) X(512, 8) X(512, 16) X(512, 32) X(512, 64)
+    X(512, 1) X(512, 2) X(512, 4) X(512, 8) X(512, 16) X(512, 32) X(512, 64) X(512, 128)
 
 // RMSNorm backward (persistent, see rmsnorm_bwd.hpp), named by (P, R, G): a lane
 // keeps x, dy (two rows in flight), its w slice and its dw partials, about 6P + 45
@@ -269,6 +269,10 @@ constexpr int rows_per_block_for(int R) { return block_threads_for(R) / R; }
 //       +64                  slots[kSlotSets][G][2] of uint64: (epoch << 32) | float bits
 constexpr int kWsHeader = 256;
 constexpr int kMaxGroups = 1024;
+// Row groups at most, per G: kMaxGroups, and for G = 256 half of it, so that no split
+// plan's workspace passes 256 + 1024 * group_stride_for(128) bytes (a grid of rows
+// on 256 workgroups each has only a few row groups on a 256-CU device).
+constexpr int max_groups_for(int G) { return G <= 128 ? kMaxGroups : kMaxGroups * 128 / G; }
 constexpr int kSlotSets = 4;
 constexpr int group_stride_for(int G) { return 64 + kSlotSets * G * 16; }
 

@@ -88,7 +88,8 @@ __device__ __forceinline__ void publish_pair(GroupRef g, int k, int it, float a,
 // Waits until all G members have published iteration `it` and leaves the G pairs
 // merged in bcast[0..1] (the same bits for the whole workgroup, and in every member:
 // the merge order is fixed).  Called by every thread; uses one barrier.  Lane l of
-// wave 0 polls the slots of members l and l + 64 (G <= 128), merges its two, and
+// wave 0 polls the slots of members l, l + 64, l + 128 and l + 192 (those below G),
+// merges them in that order, and
 // the wave merges its lanes' pairs with the butterfly of reduce.hpp (`Merge::lanes`;
 // lanes with no member hold the empty pair), log2 G steps on every lane at once.
 // Merging one member after the other from lane 0 instead kept all G pairs in
@@ -100,8 +101,8 @@ __device__ __forceinline__ void publish_pair(GroupRef g, int k, int it, float a,
 template <int G, class Merge>
 __device__ __forceinline__ void wait_pairs(GroupRef g, int it, int &spin_limit, float *bcast,
                                            Merge merge2) {
-    static_assert(G >= 1 && G <= 128, "one wave polls at most two slots per lane");
-    constexpr int kPer = G > 64 ? 2 : 1;
+    static_assert(G >= 1 && G <= 256, "one wave polls at most four slots per lane");
+    constexpr int kPer = (G + 63) / 64;
     const int tid = threadIdx.x;
     const uint32_t epoch = (uint32_t)it + 1u;
     const uint64_t *slot = g.slots + (size_t)(it & (kSlotSets - 1)) * G * 2;
@@ -138,10 +139,11 @@ __device__ __forceinline__ void wait_pairs(GroupRef g, int it, int &spin_limit, 
             acc_a = __uint_as_float((uint32_t)wa[0]);
             acc_b = __uint_as_float((uint32_t)wb[0]);
         }
-        if constexpr (kPer == 2) {
-            if (lane + 64 < G)
-                merge2(acc_a, acc_b, __uint_as_float((uint32_t)wa[1]),
-                       __uint_as_float((uint32_t)wb[1]));
+#pragma unroll
+        for (int s = 1; s < kPer; ++s) {
+            if (lane + 64 * s < G)
+                merge2(acc_a, acc_b, __uint_as_float((uint32_t)wa[s]),
+                       __uint_as_float((uint32_t)wb[s]));
         }
         constexpr int W = G >= 64 ? 64 : G > 32 ? 64 : G > 16 ? 32 : G > 8 ? 16 : G > 4 ? 8
                                                                               : G > 2 ? 4 : 2;

@@ -39,7 +39,8 @@ hipError_t launch_rmsnorm_packed(const Plan &p, const void *x, const void *w, vo
 hipError_t launch_copy(const void *src, void *dst, size_t bytes, const LaunchArgs &a);
 
 // Bytes of the library-held softmax workspace on each GPU (rr_softmax_fwd_static): the
-// largest a softmax plan needs, 256 + 1024 * (64 + 64 * 128) = 8454400, rounded up.
+// largest a softmax plan needs, 256 + 1024 * (64 + 64 * 128) = 8454400 (on 256
+// workgroups per row at most 512 row groups: 8421632), rounded up.
 constexpr size_t kStaticScratchBytes = (size_t)(8u << 20) + (256u << 10);
 // Its device address on device `dev`, which must be the current device (found with
 // hipGetSymbolAddress on the first call for each device, then kept).

@@ -11,8 +11,8 @@
 namespace rr {
 
 // Row groups of a persistent launch with G workgroups per row: as many as fit on
-// the device at once (so the whole grid normally runs at once), at most kMaxGroups
-// and at most M.  Split rows need G workgroups of the kernel to fit at once (their
+// the device at once (so the whole grid normally runs at once), at most
+// max_groups_for(G) and at most M.  Split rows need G workgroups of the kernel to fit at once (their
 // members wait for each other; see grid_exchange.hpp).
 template <class K>
 hipError_t resident_groups(K kernel, int block, int G, int64_t M, const LaunchArgs &a,
@@ -24,7 +24,7 @@ hipError_t resident_groups(K kernel, int block, int G, int64_t M, const LaunchAr
     // test override (rr_set_test_overrides): a grid larger than fits at once (split
     // rows must still drain when one XCD holds G workgroups)
     if (a.forced_groups > 0) g = a.forced_groups;
-    if (g > kMaxGroups) g = kMaxGroups;
+    if (g > max_groups_for(G)) g = max_groups_for(G);
     if (g > M) g = M;
     if (g < 1) return hipErrorCooperativeLaunchTooLarge;
     *groups = (int)g;

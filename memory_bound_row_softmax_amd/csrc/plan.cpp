@@ -103,7 +103,7 @@ bool rmsbwd_config_ok(int dtype, bool vec, int P, int R, int G) {
 }
 
 size_t grid_ws_bytes(int G, int64_t M) {
-    int64_t groups = M < kMaxGroups ? M : kMaxGroups;
+    int64_t groups = M < max_groups_for(G) ? M : max_groups_for(G);
     if (groups < 1) groups = 1;
     return (size_t)kWsHeader + (size_t)groups * (size_t)group_stride_for(G);
 }
@@ -146,10 +146,10 @@ struct Choice {
     bool stream;
     int P, R, G;
 };
-constexpr int kTunedBuckets = 16;
-constexpr int64_t kTunedN[kTunedBuckets] = {256,    1024,   4096,    5120,    6144,    8192,
-                                            12288,  16384,  32768,   65536,   131072,  262144,
-                                            524288, 1048576, 2097152, 4194304};
+constexpr int kTunedBuckets = 17;
+constexpr int64_t kTunedN[kTunedBuckets] = {256,    1024,    4096,    5120,    6144,   8192,
+                                            12288,  16384,   32768,   65536,   131072, 262144,
+                                            524288, 1048576, 2097152, 4194304, 8388608};
 // A choice with P = 0: no on-chip plan (softmax and RMSNorm then read the row twice).
 constexpr Choice kTwoReads = {false, 0, 0, 0};
 //   [op: softmax, rmsnorm, softmax backward, cross-entropy gradient][dtype: f32, bf16][N bucket]
@@ -162,38 +162,42 @@ static const Choice kTuned[4][2][kTunedBuckets] = {
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 32, 256, 1},
       {false, 32, 256, 1}, {false, 64, 128, 1}, {false, 64, 256, 1}, {true, 16, 1024, 1},
       {true, 64, 256, 2}, {true, 64, 256, 4}, {true, 64, 256, 8}, {true, 64, 512, 8},
-      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, {true, 64, 512, 128}},
+      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, {true, 64, 512, 128},
+      {true, 64, 512, 256}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 16, 256, 1}, {false, 32, 256, 1},
       {false, 32, 256, 1}, {false, 16, 512, 1}, {false, 64, 256, 1}, {false, 64, 256, 1},
       {true, 32, 1024, 1}, {true, 32, 512, 4}, {true, 64, 256, 8}, {true, 64, 512, 8},
-      {true, 64, 512, 16}, {true, 64, 512, 32}, kTwoReads, kTwoReads}},
+      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, {true, 64, 512, 128},
+      {true, 64, 512, 256}}},
     {{{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 16, 512, 1},
       {false, 32, 256, 1}, {false, 64, 128, 1}, {false, 16, 1024, 1}, {true, 16, 1024, 1},
       {true, 64, 256, 2}, {true, 64, 256, 4}, {true, 64, 256, 8}, {true, 64, 512, 8},
-      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, {true, 64, 512, 128}},
+      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, {true, 64, 512, 128},
+      {true, 64, 512, 256}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 32, 256, 1},
       {false, 32, 256, 1}, {false, 16, 512, 1}, {false, 64, 256, 1}, {true, 16, 1024, 1},
       {true, 32, 512, 2}, {true, 32, 512, 4}, {true, 64, 256, 8}, {true, kPackedP, 512, 4},
-      {true, kPackedP, 512, 8}, {true, kPackedP, 512, 16}, {true, kPackedP, 512, 32}, {true, kPackedP, 512, 64}}},
+      {true, kPackedP, 512, 8}, {true, kPackedP, 512, 16}, {true, kPackedP, 512, 32}, {true, kPackedP, 512, 64},
+      {true, kPackedP, 512, 128}}},
     // softmax backward (y and dy both held: at most 32 values per lane in a stream kernel)
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 16, 256, 1}, {false, 32, 256, 1},
       {false, 32, 256, 1}, {false, 32, 256, 1}, {false, 32, 1024, 1}, {false, 32, 1024, 1},
       {true, 16, 1024, 2}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 16, 1024, 16},
-      {true, 32, 512, 32}, {true, 32, 512, 64}, kTwoReads, kTwoReads},
+      {true, 32, 512, 32}, {true, 32, 512, 64}, kTwoReads, kTwoReads, kTwoReads},
      {{false, 8, 32, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 16, 512, 1},
       {false, 16, 512, 1}, {false, 16, 512, 1}, {false, 16, 1024, 1}, {false, 16, 1024, 1},
       {true, 32, 512, 2}, {true, 32, 512, 4}, {true, 32, 512, 8}, {true, 32, 512, 16},
-      {true, 32, 512, 32}, {true, 32, 512, 64}, kTwoReads, kTwoReads}},
+      {true, 32, 512, 32}, {true, 32, 512, 64}, kTwoReads, kTwoReads, kTwoReads}},
     // cross-entropy forward fused with its gradient (the softmax kernels; block kernels
     // hold longer rows here than for the softmax)
     {{{false, 16, 16, 1}, {false, 8, 128, 1}, {false, 8, 512, 1}, {false, 32, 256, 1},
       {false, 32, 256, 1}, {false, 32, 256, 1}, {false, 16, 1024, 1}, {true, 16, 1024, 1},
       {true, 64, 256, 2}, {true, 64, 256, 4}, {true, 64, 256, 8}, {true, 64, 256, 16},
-      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads},
+      {true, 64, 512, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads, kTwoReads},
      {{false, 16, 16, 1}, {false, 64, 16, 1}, {false, 16, 256, 1}, {false, 32, 256, 1},
       {false, 32, 256, 1}, {false, 32, 256, 1}, {false, 64, 256, 1}, {false, 32, 512, 1},
       {false, 64, 512, 1}, {false, 64, 1024, 1}, {true, 64, 256, 8}, {true, 64, 256, 16},
-      {true, 32, 1024, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads}},
+      {true, 32, 1024, 16}, {true, 64, 512, 32}, {true, 64, 512, 64}, kTwoReads, kTwoReads}},
 };
 
 // Up to this many rows, a row that one workgroup of the stream kernels holds is
@@ -294,7 +298,18 @@ static bool default_row(int op, int dtype, bool vec, int64_t M, int64_t N, Plan 
         // two reads only when they fill at least 9/10 of the plan: fp32 rows of
         // 3.5M, 3.67M, 3.9M and 4M elements ran at 0.94, 0.97, 1.03 and 1.10 times
         // the two-read rate.  RMSNorm gained at every fill measured (1.14-1.36).
-        if (op == kOpSoftmax && c.stream && c.G == 128 &&
+        // Rows of 4M to 8M elements, on a workgroup of every CU (256, or 128 packed
+        // bf16 RMSNorm workgroups), the same: offset-averaged GB/s, two reads -> on
+        // chip, full rows (8388608): softmax fp32 4567 -> 6181, bf16 4646 -> 5528,
+        // RMSNorm fp32 3499 -> 4622, bf16 4388 -> 5170; at 9/10 (softmax fp32
+        // 7.6M) 4544 -> 6126; at 0.72 (6M) only the fp32 softmax and bf16 RMSNorm
+        // still gained (4608 -> 5593, 4493 -> 4590), the bf16 softmax and fp32
+        // RMSNorm lost (4673 -> 4024, 4289 -> 4192); at 0.54 all four lost.  bf16
+        // softmax rows of 1M to 2M elements on 64 workgroups likewise (1.5M: 4635 ->
+        // 4285; 2M: 4911 -> 5550; 0.91 of 128 workgroups, 3.8M: 4735 -> 4876).
+        if (c.stream &&
+            ((op == kOpSoftmax && (c.G == 128 || (dtype == kBf16 && c.G == 64))) ||
+             k == kTunedBuckets - 1) &&
             10 * N < 9 * (int64_t)c.P * c.R * c.G)
             return false;
         if (c.stream && c.G > 1 && M <= kFewRows &&

@@ -140,7 +140,7 @@ def test_fp32_softmax_exact_groups(G, N):
 PACKED = [  # (G, M, N): packed bf16 RMSNorm (128 values per lane on 512 lanes)
     (1, 300, 65536), (1, 700, 20000), (1, 3, 8), (2, 100, 131072), (2, 61, 65544),
     (4, 90, 200000), (8, 40, 524288), (16, 7, 1000000), (16, 5, 300000), (16, 33, 1 << 20),
-    (64, 5, 1 << 22), (64, 9, 3_000_000)]
+    (64, 5, 1 << 22), (64, 9, 3_000_000), (128, 3, 1 << 23), (128, 4, 6_000_000)]
 
 
 @pytest.mark.parametrize("G,M,N", PACKED)
@@ -609,12 +609,13 @@ def test_stream_copy_binding():
 
 # ------------------------------------------------------------- rows past on-chip capacity
 
-# Aligned rows up to 2^22 elements stay on chip (split over up to 128 workgroups;
-# bf16 softmax up to 2^20); rows that are not 16-byte aligned hold at most 16 values
-# on 1024 lanes of 16 workgroups on chip (262144 elements) and go to the two-pass
-# kernel past that.  The two-pass softmax splits fp32 rows of 5M elements over 64
-# workgroups and of 8M over 64.
-LONG = [(3, 524289), (2, (1 << 22) + 8), (2, 1_000_003), (1, 5_000_000), (2, 1 << 23)]
+# Aligned rows up to 2^23 elements stay on chip (split over up to 256 workgroups;
+# rows that fill less than 9/10 of the largest plan, and softmax rows below 9/10 of
+# 128 workgroups, read twice); rows that are not 16-byte aligned hold at most 16
+# values on 1024 lanes of 16 workgroups on chip (262144 elements) and go to the
+# two-pass kernel past that.  The two-pass softmax splits fp32 rows of 5M elements
+# over 64 workgroups and of 8M over 64.
+LONG = [(3, 524289), (2, (1 << 22) + 8), (2, 1_000_003), (1, 5_000_000), (2, (1 << 23) + 8)]
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -629,6 +630,24 @@ def test_long_rows_read_twice(M, N, dtype):
     parity_rmsnorm(_x(M, N, dtype), _w(N, dtype), 1e-6, dtype, f"long rmsnorm {dtype} {M}x{N}")
 
 
+ON_256 = [(3, 1 << 23), (2, 8_000_000), (3, 5_000_000), (4, 8_388_600)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N", ON_256)
+def test_rows_on_256_workgroups(M, N, dtype):
+    """Rows of 5M to 8M elements on 64 values x 512 lanes x 256 workgroups (forced):
+    one row group of every CU, the rows one after another through it (every slot set
+    used), members past a short row's end holding nothing."""
+    for op, run in (("softmax", lambda: parity_softmax(_x(M, N, dtype, sigma=3.0), dtype,
+                                                       f"256 softmax {dtype} {M}x{N}")),
+                    ("rmsnorm", lambda: parity_rmsnorm(_x(M, N, dtype), _w(N, dtype), 1e-6, dtype,
+                                                       f"256 rmsnorm {dtype} {M}x{N}"))):
+        with forced(64, 512, 256, kind="stream"):
+            say("256 workgroups", op, dtype, M, N)
+            run()
+
+
 SPLIT_WIDE = [(3, 524288), (3, 524296), (2, 1 << 20), (5, 1_000_000), (40, 786432),
               (2, 1 << 21), (24, 1_500_000), (2, (1 << 21) + 8), (1, 3_000_000), (3, 1 << 22),
               (9, 3_500_000), (5, 3_800_000)]
@@ -639,15 +658,17 @@ SPLIT_WIDE = [(3, 524288), (3, 524296), (2, 1 << 20), (5, 1_000_000), (40, 78643
 def test_rows_split_over_many_workgroups(M, N, dtype):
     """Aligned rows from 2^19 to 2^22 elements: one read, 8 to 128 workgroups per row
     (bf16 RMSNorm packed, 8 to 64; 40 rows, or 9 rows on two row groups of 128, give
-    each row group several rows, so every exchange slot set is used)."""
+    each row group several rows, so every exchange slot set is used); softmax rows
+    that fill less than 9/10 of 128 workgroups (bf16: of 64) read twice."""
     code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
     for op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
         p = rr.rr_plan_query(op, M, N, code)
-        if op == rr.RR_OP_SOFTMAX and dtype == "bf16" and N > 1 << 20:
-            assert p["path"] == 4  # bf16 softmax past 1M elements: two reads measured faster
-            continue
         if op == rr.RR_OP_SOFTMAX and 1 << 21 < N and 10 * N < 9 * (1 << 22):
-            assert p["path"] == 4  # fp32 softmax on 128 workgroups: only from 9/10 full
+            assert p["path"] == 4  # softmax on 128 workgroups: only from 9/10 full
+            continue
+        if (op == rr.RR_OP_SOFTMAX and dtype == "bf16" and 1 << 20 < N <= 1 << 21
+                and 10 * N < 9 * (1 << 21)):
+            assert p["path"] == 4  # bf16 softmax on 64 workgroups: only from 9/10 full
             continue
         assert p["path"] == 1 and p["groups_per_row"] >= 8, p
         assert p["vals_per_lane"] * p["lanes_per_row"] * p["groups_per_row"] >= N

@@ -53,29 +53,40 @@ def test_row_plans_hold_the_row(op, dt, vec):
             rr.rr_plan_query(op, 16, (1 << 21) + 1, dt, vec)
 
 
-def test_rows_up_to_4m_elements_stay_on_chip():
+def test_rows_up_to_8m_elements_stay_on_chip():
     """Aligned rows of 2^21 to 2^22 elements are split over 128 workgroups (64 values
-    on 512 lanes; bf16 RMSNorm packed, 64 workgroups of 128 values) and read once;
-    fp32 softmax only from 9/10 of 2^22 elements, bf16 softmax past 2^20 elements and
-    the per-element path past 2^18 read twice."""
-    for N in ((1 << 21) + 1, 3_000_000, 3_774_874, 1 << 22):
-        for op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
-            p = rr.rr_plan_query(op, 256, N, rr.RR_F32)
-            if op == rr.RR_OP_SOFTMAX and 10 * N < 9 * (1 << 22):
-                # softmax on 128 workgroups only when the row fills 9/10 of them
-                assert p["path"] == 4, (N, p)
-                continue
-            assert (p["path"], p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]) == \
-                (1, 64, 512, 128), (op, N, p)
-            assert p["ws_bytes"] == 256 + 256 * (64 + 64 * 128)
-        p = rr.rr_plan_query(rr.RR_OP_RMSNORM, 256, N, rr.RR_BF16)
-        assert (p["path"], p["vals_per_lane"], p["groups_per_row"]) == (1, 128, 64), (N, p)
-        assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 256, N, rr.RR_BF16)["path"] == 4
+    on 512 lanes; bf16 RMSNorm packed, 64 workgroups of 128 values), rows of 2^22 to
+    2^23 over 256 (packed bf16 RMSNorm: 128), and read once; softmax on 128 and every
+    op on the largest plan only from 9/10 full; the per-element path past 2^18 reads
+    twice."""
+    def cap_ok(N, cap):
+        return 10 * N >= 9 * cap
+    for N in ((1 << 21) + 1, 3_000_000, 3_774_874, 1 << 22, (1 << 22) + 1, 6_000_000,
+              7_549_747, 7_549_748, 1 << 23):
+        big = N > 1 << 22
+        G = 256 if big else 128
+        for dt in (rr.RR_F32, rr.RR_BF16):
+            for op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
+                p = rr.rr_plan_query(op, 256, N, dt)
+                packed = op == rr.RR_OP_RMSNORM and dt == rr.RR_BF16
+                g = G // 2 if packed else G
+                vals = 128 if packed else 64
+                if (big or op == rr.RR_OP_SOFTMAX) and not cap_ok(N, vals * 512 * g):
+                    assert p["path"] == 4, (op, dt, N, p)
+                    continue
+                assert (p["path"], p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]) == \
+                    (1, vals, 512, g), (op, dt, N, p)
+                assert p["ws_bytes"] == 256 + 256 * (64 + 64 * g)
         for op in (rr.RR_OP_XENT_GRAD, rr.RR_OP_SOFTMAX_BWD):
             with pytest.raises(rr.RRError):
                 rr.rr_plan_query(op, 256, N, rr.RR_F32)
     for dt in (rr.RR_F32, rr.RR_BF16):
         assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 256, 1 << 22, dt, False)["path"] == 4
+        assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 256, (1 << 23) + 1, dt)["path"] == 4
+    # bf16 softmax on 64 workgroups only from 9/10 full; fp32 at any fill
+    assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 256, 1_500_000, rr.RR_BF16)["path"] == 4
+    assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 256, 1_900_000, rr.RR_BF16)["groups_per_row"] == 64
+    assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 256, 1_500_000, rr.RR_F32)["groups_per_row"] == 64
 
 
 def test_bf16_softmax_rows_take_exactly_the_workgroups_they_need():
@@ -277,17 +288,13 @@ def test_rmsnorm_bwd_plans(dt, vec):
 def test_long_rows_take_the_two_pass_kernel(overrides):
     for op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):
         for dt in (rr.RR_F32, rr.RR_BF16):
-            for n in (1 << 20, 1 << 21, 1 << 22):
+            for n in (1 << 20, 1 << 21, 1 << 22, 1 << 23):
                 on_chip = rr.rr_plan_query(op, 1000, n, dt)
-                if op == rr.RR_OP_SOFTMAX and dt == rr.RR_BF16 and n > 1 << 20:
-                    # measured faster with two reads than on 64 workgroups
-                    assert on_chip["path"] == 4
-                    continue
                 G = on_chip["groups_per_row"]
-                assert on_chip["path"] == 1 and G in (16, 32, 64, 128)
+                assert on_chip["path"] == 1 and G in (16, 32, 64, 128, 256)
                 assert on_chip["vals_per_lane"] * on_chip["lanes_per_row"] * G == n
-                assert on_chip["ws_bytes"] == 256 + 1000 * (64 + 64 * G)
-            for n in ((1 << 22) + 8, 5_000_000, 1 << 23, 1 << 26):
+                assert on_chip["ws_bytes"] == 256 + min(1000, 512 if G > 128 else 1024) * (64 + 64 * G)
+            for n in ((1 << 22) + 8, 5_000_000, (1 << 23) + 8, 1 << 26):
                 p = rr.rr_plan_query(op, 1000, n, dt)
                 # RMSNorm: 16 workgroups per row; softmax: enough that a workgroup's
                 # share of the row is at most 512 KiB (16 to 64)
@@ -322,3 +329,15 @@ def test_few_rows_keep_a_row_on_one_workgroup():
         assert rr.rr_plan_query(op, 64, 65536, rr.RR_F32)["groups_per_row"] > 1
         # the per-element path keeps its plan
         assert rr.rr_plan_query(op, 64, 32768, rr.RR_F32, False)["vals_per_lane"] <= 16
+
+
+def test_every_softmax_plan_fits_the_static_workspace():
+    """rr_softmax_fwd_static exchanges through a library array of 8 MiB + 256 KiB per
+    GPU: every on-chip softmax plan's workspace fits it, at any number of rows (the
+    row groups are capped per G)."""
+    limit = (8 << 20) + (256 << 10)
+    for dt in (rr.RR_F32, rr.RR_BF16):
+        for N in (65536, 1 << 20, 1 << 21, 1 << 22, 1 << 23):
+            for M in (1, 300, 1 << 20):
+                p = rr.rr_plan_query(rr.RR_OP_SOFTMAX, M, N, dt)
+                assert p["ws_bytes"] <= limit, (dt, N, M, p)

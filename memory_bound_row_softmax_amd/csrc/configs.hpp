@@ -45,10 +45,16 @@
 
 // Packed bf16 RMSNorm stream kernels (128-bit path only, see packed_bf16.hpp),
 // named by (R, G): each lane keeps kPackedP = 128 bf16 values as 64 VGPRs of raw
-// chunks.  A plan names them with P = kPackedP.
+// chunks.  A plan names them with P = kPackedP.  256 lanes on 8 workgroups (two per
+// CU) serve rows of 131073 to 262144 elements: offset-averaged GB/s against 512
+// lanes on 4, 16384 x 262144 6034 -> 6402 (and 5769-6439 -> 6383-6430 over the
+// offsets), 8192 and 32768 rows +1.5 and +2.4 %, 200000 elements +1.3 %, 160000 and
+// 180000 within 1 %; at 16384 to 65536 elements 128 or 256 lanes lost 5-14 % to the
+// unpacked kernels, and at 524288 and 1048576 256 lanes lost 5-6 % to 512.
 constexpr int kPackedP = 128;
 #define RR_PACKED_CONFIGS(X) \
-    X(512, 1) X(512, 2) X(512, 4) X(512, 8) X(512, 16) X(512, 32) X(512, 64) X(512, 128)
+    X(512, 1) X(512, 2) X(512, 4) X(512, 8) X(512, 16) X(512, 32) X(512, 64) X(512, 128) \
+    X(256, 8)
 
 // RMSNorm backward (persistent, see rmsnorm_bwd.hpp), named by (P, R, G): a lane
 // keeps x, dy (two rows in flight), its w slice and its dw partials, about 6P + 45

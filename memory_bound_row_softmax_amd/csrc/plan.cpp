@@ -176,7 +176,7 @@ static const Choice kTuned[4][2][kTunedBuckets] = {
       {true, 64, 512, 256}},
      {{false, 16, 16, 1}, {false, 16, 64, 1}, {false, 8, 512, 1}, {false, 32, 256, 1},
       {false, 32, 256, 1}, {false, 16, 512, 1}, {false, 64, 256, 1}, {true, 16, 1024, 1},
-      {true, 32, 512, 2}, {true, 32, 512, 4}, {true, 64, 256, 8}, {true, kPackedP, 512, 4},
+      {true, 32, 512, 2}, {true, 32, 512, 4}, {true, 64, 256, 8}, {true, kPackedP, 256, 8},
       {true, kPackedP, 512, 8}, {true, kPackedP, 512, 16}, {true, kPackedP, 512, 32}, {true, kPackedP, 512, 64},
       {true, kPackedP, 512, 128}}},
     // softmax backward (y and dy both held: at most 32 values per lane in a stream kernel)

@@ -160,6 +160,19 @@ def test_packed_bf16_rmsnorm(G, M, N):
                 rr.rr_plan_query(*args)
 
 
+@pytest.mark.parametrize("M,N", [(300, 262144), (77, 200000), (40, 131080), (9, 65536)])
+def test_packed_bf16_rmsnorm_on_256_lanes(M, N):
+    """Packed bf16 RMSNorm on 8 workgroups of 256 lanes (the plan from 131073 to 262144
+    elements): full, ragged and short rows (members with an empty part)."""
+    if N > 131072:
+        p = rr.rr_plan_query(rr.RR_OP_RMSNORM, 16384, N, rr.RR_BF16)
+        assert (p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]) == (128, 256, 8), p
+    with forced(128, 256, 8, kind="stream"):
+        say("rmsnorm packed 256x8", M, N)
+        parity_rmsnorm(_x(M, N, "bf16", sigma=2.0), _w(N, "bf16"), 1e-6, "bf16",
+                       f"rmsnorm packed 256x8 {M}x{N}")
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("P,R", [(16, 16), (16, 1024), (32, 64), (32, 512)])
 def test_forced_xent_plans(P, R, dtype):

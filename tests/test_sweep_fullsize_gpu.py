@@ -80,10 +80,10 @@ def test_sweep_point_at_full_size(w):
 # Rows whose length is not a power of two, at full size with the bench's plan: a
 # 151936-entry vocabulary (softmax) and 200000-wide rows (RMSNorm).  The members of
 # a split row hold interleaved 4 KiB granules (RMSNorm fp32 on 8 workgroups and bf16
-# packed on 4) or one contiguous part each (softmax fp32 and bf16 on exactly 5, the
+# packed on 8 of 256 lanes) or one contiguous part each (softmax fp32 and bf16 on exactly 5, the
 # last part shorter).
 UNEVEN = W.UNEVEN
-UNEVEN_G = {"softmax_f32": 5, "softmax_bf16": 5, "rmsnorm_f32": 8, "rmsnorm_bf16": 4}
+UNEVEN_G = {"softmax_f32": 5, "softmax_bf16": 5, "rmsnorm_f32": 8, "rmsnorm_bf16": 8}
 
 
 @pytest.mark.parametrize("w", UNEVEN, ids=lambda w: w.name)

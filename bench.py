@@ -501,8 +501,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(rows shard across GPUs with no exchange; see the design notes)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path "
+              "(rows would shard across GPUs with no exchange between them)", file=sys.stderr)
         return 2
 
     from synth import workloads as W

@@ -3,7 +3,8 @@ several workgroups exchange through a device array the library holds on each GPU
 against rr_softmax_fwd with a workspace the caller allocates: the same bits, called
 through the C ABI, on two calls in a row (the second with a smaller input, so the
 array holds the first call's leftovers), for split rows (the exchange inside a row's
-step, and deferred), rows read twice, and a plan that needs no workspace."""
+step, and deferred, up to 256 workgroups per row), rows read twice, and a plan that
+needs no workspace."""
 import pytest
 import torch
 
@@ -18,6 +19,7 @@ PAIRS = [
     ((64, 262144), (16, 70000)),      # 8 then 4 workgroups per row (deferred, then not)
     ((200, 131072), (7, 131072)),     # 4 per row, fewer rows
     ((8, 5_000_000), (3, 3_000_000)),  # rows read twice (64 then 32 per row)
+    ((3, 8_388_608), (2, 8_000_000)),  # 256 workgroups per row, one on every CU
     ((256, 1024), (100, 1000)),       # no workspace at all
 ]
 
@@ -43,7 +45,8 @@ def _one(dtype, M, N):
 @pytest.mark.parametrize("pair", PAIRS, ids=lambda p: f"{p[0][0]}x{p[0][1]}")
 def test_no_alloc_softmax_matches_caller_workspace(pair, dtype):
     if dtype == "bf16" and pair[0][1] == 5_000_000:
-        pair = ((8, 2_500_000), (3, 1_500_000))  # bf16 rows past 1M elements read twice
+        # bf16 rows that fill less than 9/10 of 64 or 128 workgroups read twice
+        pair = ((8, 2_500_000), (3, 1_500_000))
     for M, N in pair:
         say("no-alloc softmax", dtype, M, N)
         _one(dtype, M, N)

@@ -51,10 +51,19 @@
 // offsets), 8192 and 32768 rows +1.5 and +2.4 %, 200000 elements +1.3 %, 160000 and
 // 180000 within 1 %; at 16384 to 65536 elements 128 or 256 lanes lost 5-14 % to the
 // unpacked kernels, and at 524288 and 1048576 256 lanes lost 5-6 % to 512.
+// 512 lanes on 256 workgroups (one on every CU) hold rows of up to 16M elements.
 constexpr int kPackedP = 128;
 #define RR_PACKED_CONFIGS(X) \
     X(512, 1) X(512, 2) X(512, 4) X(512, 8) X(512, 16) X(512, 32) X(512, 64) X(512, 128) \
-    X(256, 8)
+    X(512, 256) X(256, 8)
+
+// The packed kernels defer the exchange (three buffers, 254 VGPRs) from 16
+// workgroups per row.  Offset-averaged GB/s, bf16 RMSNorm, waiting at once ->
+// deferred: 1048576 elements on 16 6041 -> 6075-6135, 2097152 on 32 5748 -> 6259-6295,
+// 4194304 on 64 5307 -> 6099-6116, 8388608 on 128 5245 -> 6078-6127, 3000000 on 64
+// 4754 -> 5410-5428; on 8 it lost 4 % (524288 elements 6555 -> 6288; 262144 on 8 of
+// 256 lanes 6443 -> 6193).
+constexpr int kPackedDeferMinG = 16;
 
 // RMSNorm backward (persistent, see rmsnorm_bwd.hpp), named by (P, R, G): a lane
 // keeps x, dy (two rows in flight), its w slice and its dw partials, about 6P + 45
@@ -202,6 +211,11 @@ constexpr bool defer_split(int op, int elem_bytes, bool vec, int P, int R, int G
     if (G < RR_DEFER_MIN_G) return false;
     if (op == kCfgSoftmaxBwd) return vec && P == 32 && R == 512;
     if (op == kCfgRmsnorm && P == 32 && R == 512) return true;
+    // fp32 RMSNorm with 64 values (offset-averaged GB/s, waiting at once -> deferred):
+    // 524288 elements on 16 6006 -> 6348, 1048576 on 32 5785 -> 6483, 2097152 on 64
+    // 5250 -> 6253, 4194304 on 128 5187 -> 6341, 8388608 on 256 4684 -> 6224; on 8
+    // it lost 1-3 % (200000 6144 -> 6013, 262144 6615 -> 6472)
+    if (op == kCfgRmsnorm && P == 64 && R == 512) return G >= 16;
     // bf16 softmax on 8 and 16: two non-deferred workgroups per CU beat one deferred
     // (stream_waves; offset-averaged GB/s: 262144 elements on 8 6246 against 5849,
     // 524288 on 16 5746 against 5577, 400000 on 16 5299 against 4594; on 32 they

@@ -124,6 +124,43 @@ __global__ void __launch_bounds__(R)
                 buf_load16<kReuseLoad>(wb, (uint32_t)(c.ln.chunk(i)) * 16u);
     }
 
+    if constexpr (kDeferredExchange && G >= kPackedDeferMinG) {
+        // Split rows, deferred exchange (as in the other stream kernels): row k is
+        // reduced and published before the workgroup waits for row k - 1's peers
+        // and writes row k - 1, with the loads of row k + 1 in flight meanwhile.
+        float buf[3][kPackedW];
+        int64_t row = group;
+        auto load = [&](float *v, int64_t r) {
+            load_part_raw<BF16, kPackedC, R>(stream_row_view(x, r, M, rb), c.ln, v);
+        };
+        load(buf[0], row);
+        load(buf[1], row + groups);
+        auto step = [&](auto Kc) -> bool {
+            constexpr int K = decltype(Kc)::value, KP = (K + 2) % 3;
+            const bool more = row < M;
+            if (more) {
+                const float q = rmsnorm_packed_local<R>(buf[K], c);
+                publish_pair<G>(c.g, c.member, c.it, q, 0.0f);
+            } else {
+                // no reduction (and its barriers) in this step: every wave has read
+                // the previous row's merged sum before wave 0 writes the next one
+                __syncthreads();
+            }
+            if (c.it > 0) {  // complete the previous row
+                wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeSum{});
+                const int64_t rp = row - groups;
+                rmsnorm_packed_apply<R>(buf[KP], wslot, c.bcast[0], stream_row_view(y, rp, M, rb),
+                                        rstd ? rstd + rp : nullptr, eps, c);
+            }
+            if (!more) return false;
+            load(buf[KP], row + 2 * (int64_t)groups);
+            ++c.it;
+            row += groups;
+            return true;
+        };
+        while (stream_steps<0, 3>(step)) {
+        }
+    } else {
     float buf[2][kPackedW];
     stream_rows<2>(
         (int64_t)group, M, groups, buf,
@@ -140,6 +177,7 @@ __global__ void __launch_bounds__(R)
                                     rstd ? rstd + r : nullptr, eps, c);
             ++c.it;
         });
+    }
     if constexpr (G > 1) {
         if (c.it > 0) depart_group<G>(c.g);
     }

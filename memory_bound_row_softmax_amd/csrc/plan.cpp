@@ -301,15 +301,19 @@ static bool default_row(int op, int dtype, bool vec, int64_t M, int64_t N, Plan 
         // Rows of 4M to 8M elements, on a workgroup of every CU (256, or 128 packed
         // bf16 RMSNorm workgroups), the same: offset-averaged GB/s, two reads -> on
         // chip, full rows (8388608): softmax fp32 4567 -> 6181, bf16 4646 -> 5528,
-        // RMSNorm fp32 3499 -> 4622, bf16 4388 -> 5170; at 9/10 (softmax fp32
-        // 7.6M) 4544 -> 6126; at 0.72 (6M) only the fp32 softmax and bf16 RMSNorm
-        // still gained (4608 -> 5593, 4493 -> 4590), the bf16 softmax and fp32
-        // RMSNorm lost (4673 -> 4024, 4289 -> 4192); at 0.54 all four lost.  bf16
+        // RMSNorm fp32 3499 -> 4622, bf16 4388 -> 5170 (before the RMSNorm deferred
+        // its exchange; now 6224 and 6078-6127); at 9/10 (softmax fp32 7.6M) 4544
+        // -> 6126; at 0.72 (6M) the fp32 softmax gained (4608 -> 5593) and the bf16
+        // softmax lost (4673 -> 4024); at 0.54 both lost.  bf16
         // softmax rows of 1M to 2M elements on 64 workgroups likewise (1.5M: 4635 ->
         // 4285; 2M: 4911 -> 5550; 0.91 of 128 workgroups, 3.8M: 4735 -> 4876).
-        if (c.stream &&
-            ((op == kOpSoftmax && (c.G == 128 || (dtype == kBf16 && c.G == 64))) ||
-             k == kTunedBuckets - 1) &&
+        // The RMSNorm, since it defers the exchange from 16 workgroups, gains at
+        // every fill measured and is exempt: fp32 on 256 workgroups, 6M 4380 ->
+        // 5422-5465, 4.5M 4307 -> 4652-4660; packed bf16 on 128, 6M 4473 -> 5374,
+        // 4.5M 4141 -> 4680; on 64, 2.2M 4481 -> 4683.  (The softmax backward and
+        // the cross-entropy gradient have no plan there.)
+        if (c.stream && op == kOpSoftmax &&
+            (c.G == 128 || (dtype == kBf16 && c.G == 64) || k == kTunedBuckets - 1) &&
             10 * N < 9 * (int64_t)c.P * c.R * c.G)
             return false;
         if (c.stream && c.G > 1 && M <= kFewRows &&
@@ -328,6 +332,12 @@ static bool default_row(int op, int dtype, bool vec, int64_t M, int64_t N, Plan 
             if (try_choice(op, dtype, vec, N, b, p)) return true;
         }
     }
+    // Packed bf16 RMSNorm rows past the table: 256 workgroups of 128 values x 512
+    // lanes, one on every CU, hold up to 16M elements, at any fill (offset-averaged
+    // GB/s, two reads -> on chip: 16777216 elements 3724 -> 5890, 15M 3809 -> 5628,
+    // 12M 3927 -> 5256, 9M 4042 -> 4609).
+    if (op == kOpRmsnorm && dtype == kBf16 && vec && N > kTunedN[kTunedBuckets - 1])
+        return try_choice(op, dtype, vec, N, Choice{true, kPackedP, 512, 256}, p);
     // A configuration the per-element path does not have: the first stream
     // configuration that holds the row with the fewest workgroups.  The per-element
     // path stops at 16 workgroups per row: its longer rows measured no faster on

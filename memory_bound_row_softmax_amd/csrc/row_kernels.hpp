@@ -389,6 +389,11 @@ struct WeightLds {
     }
 };
 
+// No weight (already applied).
+struct WeightNone {
+    __device__ __forceinline__ void apply(float *, int) const {}
+};
+
 // Sum of squares of this workgroup's part of the row.
 template <class E, int P, int R, bool STREAM>
 __device__ __forceinline__ float rmsnorm_local(float *v, RowCtx &c) {
@@ -499,13 +504,14 @@ __global__ void __launch_bounds__(R)
                 if constexpr (VEC) widen_part<E, C>(buf[K]);
                 const float q = rmsnorm_local<E, P, R, true>(buf[K], c);
                 publish_pair<G>(c.g, c.member, c.it, q, 0.0f);
+                wsrc.apply(buf[K], c.l);
             } else {
                 __syncthreads();  // as in the softmax kernel: the merged sum is read
             }
             if (c.it > 0) {  // complete the previous row
                 wait_pairs<G>(c.g, c.it - 1, c.spin_limit, c.bcast, MergeSum{});
                 const int64_t rp = row - groups;
-                rmsnorm_apply<E, P, R, VEC, true>(buf[KP], wsrc, c.bcast[0],
+                rmsnorm_apply<E, P, R, VEC, true>(buf[KP], WeightNone{}, c.bcast[0],
                                             stream_row_view(y, rp, M, rb),
                                             rstd ? rstd + rp : nullptr, eps, true, c);
             }

@@ -75,7 +75,7 @@ def sweep():
 
 
 # The longest rows held on chip (one read, 16 to 256 workgroups per row): 1M, 2M,
-# 4M and 8M elements.
+# 4M and 8M elements, and 16M for the packed bf16 RMSNorm.
 WIDE = [Workload("softmax_f32_1024x1048576", "softmax", "f32", 1024, 1 << 20),
         Workload("rmsnorm_bf16_2048x1048576", "rmsnorm", "bf16", 2048, 1 << 20),
         Workload("softmax_f32_512x2097152", "softmax", "f32", 512, 1 << 21),
@@ -83,11 +83,14 @@ WIDE = [Workload("softmax_f32_1024x1048576", "softmax", "f32", 1024, 1 << 20),
         Workload("softmax_f32_256x4194304", "softmax", "f32", 256, 1 << 22),
         Workload("rmsnorm_bf16_512x4194304", "rmsnorm", "bf16", 512, 1 << 22),
         Workload("softmax_f32_128x8388608", "softmax", "f32", 128, 1 << 23),
-        Workload("rmsnorm_bf16_256x8388608", "rmsnorm", "bf16", 256, 1 << 23)]
-
-# Rows past the on-chip capacity (read twice): 16M-element rows.
-LONG = [Workload("softmax_f32_64x16777216", "softmax", "f32", 64, 1 << 24),
+        Workload("rmsnorm_bf16_256x8388608", "rmsnorm", "bf16", 256, 1 << 23),
+        Workload("rmsnorm_f32_256x8388608", "rmsnorm", "f32", 256, 1 << 23),
         Workload("rmsnorm_bf16_128x16777216", "rmsnorm", "bf16", 128, 1 << 24)]
+
+# Rows past the on-chip capacity (read twice): 16M-element fp32 rows and 32M-element
+# bf16 rows.
+LONG = [Workload("softmax_f32_64x16777216", "softmax", "f32", 64, 1 << 24),
+        Workload("rmsnorm_bf16_64x33554432", "rmsnorm", "bf16", 64, 1 << 25)]
 
 
 # Rows whose length is not a power of two: a 151936-entry vocabulary (softmax) and

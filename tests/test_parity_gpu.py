@@ -140,7 +140,8 @@ def test_fp32_softmax_exact_groups(G, N):
 PACKED = [  # (G, M, N): packed bf16 RMSNorm (128 values per lane on 512 lanes)
     (1, 300, 65536), (1, 700, 20000), (1, 3, 8), (2, 100, 131072), (2, 61, 65544),
     (4, 90, 200000), (8, 40, 524288), (16, 7, 1000000), (16, 5, 300000), (16, 33, 1 << 20),
-    (64, 5, 1 << 22), (64, 9, 3_000_000), (128, 3, 1 << 23), (128, 4, 6_000_000)]
+    (64, 5, 1 << 22), (64, 9, 3_000_000), (128, 3, 1 << 23), (128, 4, 6_000_000),
+    (256, 2, 1 << 24), (256, 3, 15_000_000)]
 
 
 @pytest.mark.parametrize("G,M,N", PACKED)
@@ -158,6 +159,22 @@ def test_packed_bf16_rmsnorm(G, M, N):
                      (rr.RR_OP_SOFTMAX, M, N, rr.RR_BF16), (rr.RR_OP_XENT_GRAD, M, N, rr.RR_BF16)):
             with pytest.raises(rr.RRError):
                 rr.rr_plan_query(*args)
+
+
+@pytest.mark.parametrize("dtype,P,G,N", [("f32", 64, 16, 524288), ("f32", 64, 32, 1_000_000),
+                                         ("f32", 64, 64, 2_097_152), ("bf16", 128, 16, 1_000_000),
+                                         ("bf16", 128, 32, 2_000_000)])
+def test_rmsnorm_deferred_many_rows_per_group(dtype, P, G, N):
+    """RMSNorm rows on 512 lanes defer the exchange from 16 workgroups (64 fp32 values,
+    or 128 packed bf16 ones): two row groups give each of them many rows, so every
+    exchange slot set is reused; ragged rows leave the last members' parts short."""
+    M = 11
+    with forced(P, 512, G, kind="stream", groups=2):
+        p = rr.rr_plan_query(rr.RR_OP_RMSNORM, M, N, rr.RR_F32 if dtype == "f32" else rr.RR_BF16)
+        assert (p["vals_per_lane"], p["groups_per_row"]) == (P, G)
+        say("rmsnorm deferred", dtype, P, G, M, N)
+        parity_rmsnorm(_x(M, N, dtype, sigma=2.0), _w(N, dtype), 1e-6, dtype,
+                       f"rmsnorm deferred {dtype} {G} {M}x{N}")
 
 
 @pytest.mark.parametrize("M,N", [(300, 262144), (77, 200000), (40, 131080), (9, 65536)])
@@ -624,10 +641,12 @@ def test_stream_copy_binding():
 
 # Aligned rows up to 2^23 elements stay on chip (split over up to 256 workgroups;
 # rows that fill less than 9/10 of the largest plan, and softmax rows below 9/10 of
-# 128 workgroups, read twice); rows that are not 16-byte aligned hold at most 16
-# values on 1024 lanes of 16 workgroups on chip (262144 elements) and go to the
-# two-pass kernel past that.  The two-pass softmax splits fp32 rows of 5M elements
-# over 64 workgroups and of 8M over 64.
+# 128 workgroups, read twice; aligned RMSNorm rows stay on chip at any fill, up to
+# 2^23 elements and packed bf16 ones to 2^24, so their two-pass kernel is forced
+# here); rows that are not 16-byte
+# aligned hold at most 16 values on 1024 lanes of 16 workgroups on chip (262144
+# elements) and go to the two-pass kernel past that.  The two-pass softmax splits
+# fp32 rows of 5M elements over 64 workgroups and of 8M over 64.
 LONG = [(3, 524289), (2, (1 << 22) + 8), (2, 1_000_003), (1, 5_000_000), (2, (1 << 23) + 8)]
 
 
@@ -639,8 +658,12 @@ def test_long_rows_read_twice(M, N, dtype):
     assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, M, N, code, vec)["path"] == 4
     say("long softmax", dtype, M, N)
     parity_softmax(_x(M, N, dtype, sigma=3.0), dtype, f"long softmax {dtype} {M}x{N}")
+    on_chip = vec and 262144 < N <= 1 << (24 if dtype == "bf16" else 23)
+    assert (rr.rr_plan_query(rr.RR_OP_RMSNORM, M, N, code, vec)["path"] == 4) != on_chip
     say("long rmsnorm", dtype, M, N)
-    parity_rmsnorm(_x(M, N, dtype), _w(N, dtype), 1e-6, dtype, f"long rmsnorm {dtype} {M}x{N}")
+    with forced(kind="long" if on_chip else None):
+        assert rr.rr_plan_query(rr.RR_OP_RMSNORM, M, N, code, vec)["path"] == 4
+        parity_rmsnorm(_x(M, N, dtype), _w(N, dtype), 1e-6, dtype, f"long rmsnorm {dtype} {M}x{N}")
 
 
 ON_256 = [(3, 1 << 23), (2, 8_000_000), (3, 5_000_000), (4, 8_388_600)]

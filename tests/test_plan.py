@@ -45,7 +45,14 @@ def test_row_plans_hold_the_row(op, dt, vec):
             assert G == 1 or (G // 2) * P * R < N
             assert p["ws_bytes"] == (256 + 1024 * (64 + 64 * G) if G > 1 else 0)
     if op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM):  # long rows: read twice, up to 2^28
-        assert rr.rr_plan_query(op, 16, (1 << 22) + 1, dt, vec)["path"] == 4
+        q = rr.rr_plan_query(op, 16, (1 << 22) + 1, dt, vec)
+        if op == rr.RR_OP_RMSNORM and vec:  # on chip at any fill, to 2^23 (packed bf16 2^24)
+            cap = 1 << (24 if dt == rr.RR_BF16 else 23)
+            assert q["path"] == 1 and q["vals_per_lane"] == (128 if dt == rr.RR_BF16 else 64)
+            assert rr.rr_plan_query(op, 16, cap, dt, vec)["path"] == 1
+            assert rr.rr_plan_query(op, 16, cap + 1, dt, vec)["path"] == 4
+        else:
+            assert q["path"] == 4
         with pytest.raises(rr.RRError):
             rr.rr_plan_query(op, 16, (1 << 28) + 1, dt, vec)
     else:
@@ -56,9 +63,9 @@ def test_row_plans_hold_the_row(op, dt, vec):
 def test_rows_up_to_8m_elements_stay_on_chip():
     """Aligned rows of 2^21 to 2^22 elements are split over 128 workgroups (64 values
     on 512 lanes; bf16 RMSNorm packed, 64 workgroups of 128 values), rows of 2^22 to
-    2^23 over 256 (packed bf16 RMSNorm: 128), and read once; softmax on 128 and every
-    op on the largest plan only from 9/10 full; the per-element path past 2^18 reads
-    twice."""
+    2^23 over 256 (packed bf16 RMSNorm: 128), and read once; the softmax on 128 and
+    on 256 only from 9/10 full, the RMSNorm at any fill; the per-element path past
+    2^18 reads twice."""
     def cap_ok(N, cap):
         return 10 * N >= 9 * cap
     for N in ((1 << 21) + 1, 3_000_000, 3_774_874, 1 << 22, (1 << 22) + 1, 6_000_000,
@@ -71,7 +78,7 @@ def test_rows_up_to_8m_elements_stay_on_chip():
                 packed = op == rr.RR_OP_RMSNORM and dt == rr.RR_BF16
                 g = G // 2 if packed else G
                 vals = 128 if packed else 64
-                if (big or op == rr.RR_OP_SOFTMAX) and not cap_ok(N, vals * 512 * g):
+                if op == rr.RR_OP_SOFTMAX and not cap_ok(N, vals * 512 * g):
                     assert p["path"] == 4, (op, dt, N, p)
                     continue
                 assert (p["path"], p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]) == \
@@ -294,8 +301,11 @@ def test_long_rows_take_the_two_pass_kernel(overrides):
                 assert on_chip["path"] == 1 and G in (16, 32, 64, 128, 256)
                 assert on_chip["vals_per_lane"] * on_chip["lanes_per_row"] * G == n
                 assert on_chip["ws_bytes"] == 256 + min(1000, 512 if G > 128 else 1024) * (64 + 64 * G)
-            for n in ((1 << 22) + 8, 5_000_000, (1 << 23) + 8, 1 << 26):
+            for n in ((1 << 22) + 8, 5_000_000, (1 << 23) + 8, (1 << 24) + 8, 1 << 26):
                 p = rr.rr_plan_query(op, 1000, n, dt)
+                if op == rr.RR_OP_RMSNORM and n <= 1 << (24 if dt == rr.RR_BF16 else 23):
+                    assert p["path"] == 1  # on chip at any fill
+                    continue
                 # RMSNorm: 16 workgroups per row; softmax: enough that a workgroup's
                 # share of the row is at most 512 KiB (16 to 64)
                 G = 16
@@ -314,6 +324,28 @@ def test_long_rows_take_the_two_pass_kernel(overrides):
     with pytest.raises(rr.RRError):
         rr.rr_plan_query(rr.RR_OP_SOFTMAX_BWD, 8, (1 << 20) + 4, rr.RR_F32)
     # the per-element path keeps the two-pass kernel past 262144 elements
+
+
+def test_packed_bf16_rmsnorm_stays_on_chip_to_16m_elements():
+    """Aligned bf16 RMSNorm rows keep the packed plans at any fill: 128 workgroups up
+    to 2^23 elements, 256 (one on every CU) up to 2^24, then the two-pass kernel; the
+    per-element path and fp32 take the two-pass kernel past 2^23."""
+    for N, G in ((2_200_000, 64), (4_500_000, 128), (6_000_000, 128), (1 << 23, 128),
+                 ((1 << 23) + 8, 256), (9_000_000, 256), (15_000_000, 256), (1 << 24, 256)):
+        p = rr.rr_plan_query(rr.RR_OP_RMSNORM, 128, N, rr.RR_BF16)
+        assert (p["path"], p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]) == \
+            (1, 128, 512, G), (N, p)
+        assert p["ws_bytes"] == 256 + 128 * (64 + 64 * G)
+    for M in (1, 300, 1 << 20):  # row groups capped per G: the workspace stays small
+        assert rr.rr_plan_query(rr.RR_OP_RMSNORM, M, 1 << 24, rr.RR_BF16)["ws_bytes"] <= \
+            (8 << 20) + (256 << 10)
+    assert rr.rr_plan_query(rr.RR_OP_RMSNORM, 128, (1 << 24) + 8, rr.RR_BF16)["path"] == 4
+    assert rr.rr_plan_query(rr.RR_OP_RMSNORM, 128, (1 << 23) + 8, rr.RR_F32)["path"] == 4
+    assert rr.rr_plan_query(rr.RR_OP_RMSNORM, 128, (1 << 23) + 8, rr.RR_BF16, False)["path"] == 4
+    # fp32 RMSNorm rows on 256 workgroups at any fill
+    assert rr.rr_plan_query(rr.RR_OP_RMSNORM, 128, 4_500_000, rr.RR_F32)["groups_per_row"] == 256
+    # the softmax keeps the fill rule on its largest plan
+    assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 128, 6_000_000, rr.RR_F32)["path"] == 4
 
 
 def test_few_rows_keep_a_row_on_one_workgroup():

@@ -432,13 +432,15 @@ TIMEOUT_CASES = [
     ("softmax f32 G4", "softmax", "f32", 64, 131072, None),
     ("softmax f32 G8 deferred", "softmax", "f32", 64, 262144, None),
     ("softmax bf16 G4", "softmax", "bf16", 64, 262144, None),
-    ("rmsnorm f32 G16 deferred", "rmsnorm", "f32", 64, 262144, None),
+    ("rmsnorm f32 G8", "rmsnorm", "f32", 64, 262144, None),
     ("rmsnorm bf16 packed G4", "rmsnorm", "bf16", 64, 262144, None),
     ("xent_grad f32 G4", "xent_grad", "f32", 64, 131072, None),
     ("softmax_bwd f32 G8 deferred", "softmax_bwd", "f32", 64, 262144, None),
     ("rmsnorm_bwd f32 G4", "rmsnorm_bwd", "f32", 64, 65536, None),
     ("long-row softmax", "softmax", "f32", 48, 70000, "long"),
     ("long-row rmsnorm", "rmsnorm", "bf16", 48, 70000, "long"),
+    ("rmsnorm f32 G16 deferred", "rmsnorm", "f32", 64, 524288, None),
+    ("rmsnorm bf16 packed G16 deferred", "rmsnorm", "bf16", 64, 1 << 20, None),
 ]
 
 _OP_CODES = {"softmax": rr.RR_OP_SOFTMAX, "rmsnorm": rr.RR_OP_RMSNORM,
@@ -530,7 +532,7 @@ def test_forced_timeout_gives_nan_rows_and_is_reported(name, op, dtype, M, N, ki
         assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("name,op,dtype,M,N,kind", TIMEOUT_CASES[:2] + TIMEOUT_CASES[5:8])
+@pytest.mark.parametrize("name,op,dtype,M,N,kind", TIMEOUT_CASES[:2] + TIMEOUT_CASES[5:8] + TIMEOUT_CASES[10:])
 def test_one_poll_waits_never_give_silent_garbage(name, op, dtype, M, N, kind):
     """With a spin limit of one poll, some waits may give up and others succeed.
     Every row must then be either exactly the normal result or hold NaN, and a row

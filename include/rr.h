@@ -161,6 +161,9 @@ rr_status rr_cross_entropy_fwd_bwd(const void *logits, const int32_t *labels, co
  * dy are each read once and dx written once.  dx may be y or dy itself (exact aliasing);
  * any other overlap among the three is rejected.  Arithmetic in fp32.  Rows of more than
  * 32768 elements are split over workgroups and need a workspace (RR_OP_SOFTMAX_BWD).
+ * Rows past the on-chip plans (more than 1048576 elements, or 262144 when y, dy or dx
+ * is not 16-byte aligned), up to 2^28 elements, take a two-read kernel: c_i is summed
+ * over a first read of y and dy, and dx is written from a second read.
  */
 rr_status rr_softmax_bwd(const void *y, const void *dy, void *dx, int64_t M, int64_t N,
                          rr_dtype dt, void *ws, size_t ws_bytes, hipStream_t stream);
@@ -208,7 +211,10 @@ typedef struct {
                            1: persistent stream kernel with each row split over
                               `groups_per_row` workgroups (split rows, workspace),
                            2: cross-entropy forward (streaming online max and sum),
-                           3: persistent stream kernel, one workgroup per row */
+                           3: persistent stream kernel, one workgroup per row,
+                           4: two-read long-row kernel (softmax and RMSNorm forward,
+                              softmax backward), `groups_per_row` workgroups per row
+                              (workspace) */
     int vectorized;     /* 1: 128-bit path, 0: per-element path */
     int vals_per_lane;  /* values each lane holds (row paths: fp32 values, or 128 bf16 values
                            kept packed by the bf16 RMSNorm) or loads per step (streaming) */
@@ -260,7 +266,8 @@ rr_status rr_stream_fill(void *dst, size_t bytes, uint32_t value, hipStream_t st
  */
 typedef struct {
     int kind;            /* 0: the planner's choice, 1: block kernel, 2: stream kernel,
-                            3: the two-read long-row kernel (softmax and RMSNorm forward) */
+                            3: the two-read long-row kernel (softmax and RMSNorm forward,
+                               softmax backward) */
     int vals_per_lane;   /* P of the plan (0: the planner's choice) */
     int lanes_per_row;   /* R of the plan (0: the planner's choice) */
     int groups_per_row;  /* G of the plan (0: the planner's choice) */

@@ -246,6 +246,9 @@ rr_status rr_softmax_bwd(const void *y, const void *dy, void *dx, int64_t M, int
         return st;
     rr::LaunchArgs a;
     if ((st = launch_args(stream, &a)) != RR_OK) return st;
+    if (p.path == rr::kPathLong)
+        return hip_status(rr::launch_long_row(p, rr::kOpSoftmaxBwd, dt, y, dy, dx, nullptr, M, N,
+                                              0.0f, ws, a));
     return hip_status(rr::launch_softmax_bwd(p, dt, y, dy, dx, M, N, ws, a));
 }
 

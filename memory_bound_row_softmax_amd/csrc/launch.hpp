@@ -31,6 +31,8 @@ hipError_t launch_softmax_bwd(const Plan &p, int dtype, const void *y, const voi
 hipError_t launch_rmsnorm_bwd(const Plan &p, int dtype, const void *x, const void *w,
                               const void *dy, const float *rstd, void *dx, float *dw, int64_t M,
                               int64_t N, void *ws, const LaunchArgs &a);
+// op kOpSoftmax or kOpRmsnorm: x, w (RMSNorm), y, rstd (RMSNorm, may be NULL);
+// kOpSoftmaxBwd: x = the forward's y, w = dy (M x N), y = dx.
 hipError_t launch_long_row(const Plan &p, int op, int dtype, const void *x, const void *w,
                            void *y, float *rstd, int64_t M, int64_t N, float eps, void *ws,
                            const LaunchArgs &a);

@@ -1,5 +1,6 @@
 // long_row.hip -- instantiates the two-pass long-row kernels (softmax and RMSNorm
-// forward past the on-chip capacity) and launches the one the plan names.
+// forward and the softmax backward past the on-chip capacity) and launches the one
+// the plan names.
 #include "launch_util.hpp"
 #include "long_row.hpp"
 
@@ -24,8 +25,9 @@ hipError_t launch_cfg(const void *x, const void *w, void *y, float *rstd, int64_
 template <class E, int OP>
 hipError_t dispatch(const Plan &p, const void *x, const void *w, void *y, float *rstd, int64_t M,
                     int64_t N, float eps, void *ws, const LaunchArgs &a) {
-    // RMSNorm takes 16 workgroups per row; softmax 16, 32 or 64 (long_row_groups)
-    if constexpr (OP == kLongSoftmax) {
+    // RMSNorm takes 16 workgroups per row; the softmax and its backward 16, 32 or 64
+    // (long_row_groups)
+    if constexpr (OP != kLongRmsnorm) {
         if (p.G == 32)
             return p.vec ? launch_cfg<E, OP, kLongP, 32, true>(x, w, y, rstd, M, N, eps, ws, a)
                          : launch_cfg<E, OP, kLongPElem, 32, false>(x, w, y, rstd, M, N, eps, ws, a);
@@ -46,6 +48,10 @@ hipError_t launch_long_row(const Plan &p, int op, int dtype, const void *x, cons
     if (op == kOpSoftmax)
         return dtype == kF32 ? dispatch<F32, kLongSoftmax>(p, x, w, y, rstd, M, N, eps, ws, a)
                              : dispatch<BF16, kLongSoftmax>(p, x, w, y, rstd, M, N, eps, ws, a);
+    if (op == kOpSoftmaxBwd)
+        return dtype == kF32 ? dispatch<F32, kLongSoftmaxBwd>(p, x, w, y, rstd, M, N, eps, ws, a)
+                             : dispatch<BF16, kLongSoftmaxBwd>(p, x, w, y, rstd, M, N, eps, ws, a);
+    if (op != kOpRmsnorm) return hipErrorInvalidValue;
     return dtype == kF32 ? dispatch<F32, kLongRmsnorm>(p, x, w, y, rstd, M, N, eps, ws, a)
                          : dispatch<BF16, kLongRmsnorm>(p, x, w, y, rstd, M, N, eps, ws, a);
 }

@@ -1,16 +1,16 @@
-// long_row.hpp -- softmax and RMSNorm forward for rows longer than the split-row
-// stream kernels hold in registers or run faster (more than 4194304 elements; bf16
-// softmax more than 1048576; the per-element path more than 262144).
+// long_row.hpp -- softmax and RMSNorm forward, and the softmax backward, for rows
+// longer than the split-row stream kernels hold in registers or run faster.
 //
 // The QuACK article (无需CUDA代码，给H100加速33%-50%), section 内存吞吐量, names the
 // alternative to reducing a long row across a cluster: an online algorithm that reads
 // the row twice.  Here the G workgroups of a row group own every G-th tile of T = P * R
 // elements of the row:
 //   pass 1: stream the owned tiles, keeping a running (max, sum of exp) pair (softmax,
-//           the online-softmax rescaling) or the sum of squares (RMSNorm);
+//           the online-softmax rescaling), the sum of squares (RMSNorm) or the dot
+//           product of y and dy (softmax backward);
 //   merge:  reduce over the workgroup, then over the G workgroups through the
 //           workspace (grid_exchange.hpp);
-//   pass 2: read the owned tiles again and write y.
+//   pass 2: read the owned tiles again and write y (dx).
 // A workgroup's tiles were read a moment before, so the second read is served in large
 // part by the caches between the CUs and HBM (the 256 MB last-level cache holds the
 // few hundred KB each of the resident workgroups reads per row) rather than by HBM.
@@ -33,6 +33,7 @@ namespace rr {
 
 constexpr int kLongSoftmax = 0;
 constexpr int kLongRmsnorm = 1;
+constexpr int kLongSoftmaxBwd = 2;  // x: y of the forward, w: dy (M x N), y: dx
 
 // Cache policy of the first read of a tile: it is read again shortly, so it must
 // not carry the non-temporal hint of the other streams.  The second read is the
@@ -100,18 +101,29 @@ __global__ void __launch_bounds__(R)
         const RowView xv = stream_row_view(x, row, M, rb);
         const RowView yv = stream_row_view(y, row, M, rb);
         auto tile = [&](int t) { return Lane{t * C * R + l, R}; };  // lane l's chunks of tile t
+        // dy's row (softmax backward; the other ops do not use it)
+        const RowView dv = OP == kLongSoftmaxBwd ? stream_row_view(w, row, M, rb) : xv;
         auto load1 = [&](float *v, int t) {
             load_part<E, C, R, VEC, kLongPass1Load>(xv, tile(t), v);
+            if constexpr (OP == kLongSoftmaxBwd)
+                load_part<E, C, R, VEC, kLongPass1Load>(dv, tile(t), v + P);
         };
 
         // pass 1
         MaxSum acc = {-INFINITY, 0.0f};
         float q = 0.0f;
-        walk_tiles<P>(
+        constexpr int B1 = OP == kLongSoftmaxBwd ? 2 * P : P;
+        walk_tiles<B1>(
             c.member, G, tiles, load1,
             [&](float *v, int t) {
                 const bool full = part_full_at<E, C, R>(t * C * R, N);
-                if constexpr (OP == kLongSoftmax) {
+                if constexpr (OP == kLongSoftmaxBwd) {
+                    if (!full) {  // both operands: padding adds nothing to the dot product
+                        mask_part<E, C, R>(tile(t), N, 0.0f, v);
+                        mask_part<E, C, R>(tile(t), N, 0.0f, v + P);
+                    }
+                    q += tree_dot<P>(v, v + P);
+                } else if constexpr (OP == kLongSoftmax) {
                     if (!full) mask_part<E, C, R>(tile(t), N, -INFINITY, v);
                     const float mnew = fmaxf(acc.m, tree_reduce<P>(v, OpMax{}));
                     const float mu = safe_max(mnew);
@@ -137,7 +149,10 @@ __global__ void __launch_bounds__(R)
         }
         float m_row = 0.0f, s_row = 0.0f, r = 0.0f;
         auto wait = [&] {
-            if constexpr (OP == kLongSoftmax) {
+            if constexpr (OP == kLongSoftmaxBwd) {
+                wait_pairs<G>(c.g, c.it, c.spin_limit, c.bcast, MergeSum{});
+                r = c.bcast[0];  // the row's sum of y * dy
+            } else if constexpr (OP == kLongSoftmax) {
                 wait_pairs<G>(c.g, c.it, c.spin_limit, c.bcast, MergeMaxSum{});
                 m_row = safe_max(c.bcast[0]);
                 s_row = __builtin_amdgcn_rcpf(c.bcast[1]);
@@ -148,7 +163,8 @@ __global__ void __launch_bounds__(R)
             }
         };
 
-        // pass 2, backwards (RMSNorm: the tile of w is loaded with the tile of x)
+        // pass 2, backwards (RMSNorm: the tile of w is loaded with the tile of x;
+        // softmax backward: the tile of dy with the tile of y)
         constexpr int B2 = OP == kLongSoftmax ? P : 2 * P;
         walk_tiles<B2>(
             last_tile(c.member, G, tiles), -G, tiles,
@@ -156,10 +172,14 @@ __global__ void __launch_bounds__(R)
                 load_part<E, C, R, VEC>(xv, tile(t), v);
                 if constexpr (OP == kLongRmsnorm)
                     load_part<E, C, R, VEC, kReuseLoad>(RowView{wb, 0u, rb}, tile(t), v + P);
+                if constexpr (OP == kLongSoftmaxBwd) load_part<E, C, R, VEC>(dv, tile(t), v + P);
             },
             [&](float *v, int t) {
                 const bool full = part_full_at<E, C, R>(t * C * R, N);
-                if constexpr (OP == kLongSoftmax) {
+                if constexpr (OP == kLongSoftmaxBwd) {
+#pragma unroll
+                    for (int j = 0; j < P; ++j) v[j] = v[j] * (v[P + j] - r);
+                } else if constexpr (OP == kLongSoftmax) {
 #pragma unroll
                     for (int j = 0; j < P; ++j) v[j] = exp_shift(v[j], m_row) * s_row;
                 } else {

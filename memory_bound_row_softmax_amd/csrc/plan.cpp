@@ -509,7 +509,7 @@ PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *ou
     const bool force_stream = ov.kind == kForceStream;
     const bool force_block = ov.kind == kForceBlock;
     const bool force_long = ov.kind == kForceLong;
-    const bool long_op = op == kOpSoftmax || op == kOpRmsnorm;
+    const bool long_op = op == kOpSoftmax || op == kOpRmsnorm || op == kOpSoftmaxBwd;
     if (long_op && (force_long || (!fP && !fR && !fG && !force_stream && !force_block &&
                                    !default_row(op, dtype, vec, M, N, &p)))) {
         // past every on-chip plan: read the row twice
@@ -521,7 +521,9 @@ PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *ou
         p.path = kPathLong;
         p.P = vec ? kLongP : kLongPElem;
         p.R = kLongR;
-        p.G = long_row_groups(op == kOpSoftmax, N * (dtype == kBf16 ? 2 : 4));
+        // the softmax backward reads two rows (y and dy) per pass
+        p.G = long_row_groups(op != kOpRmsnorm,
+                              (op == kOpSoftmaxBwd ? 2 : 1) * N * (dtype == kBf16 ? 2 : 4));
         p.max_n = kLongMaxN;
         p.ws_bytes = grid_ws_bytes(p.G, M);
         p.block = kLongR;

@@ -114,8 +114,12 @@ def test_too_long_rows_are_unsupported():
     assert rr.softmax_fwd_raw(A, B, 2, (1 << 28) + 4, rr.RR_F32) == rr.RR_ERR_UNSUPPORTED
     # (a longer row than the on-chip plans hold, without a workspace)
     assert rr.softmax_fwd_raw(A, B, 2, (1 << 19) + 4, rr.RR_F32) == rr.RR_ERR_WORKSPACE
-    # the backward kernels hold the row on chip: 64 workgroups x 512 lanes x 32 values
-    assert rr.softmax_bwd_raw(A, C, B, 2, (1 << 20) + 4, rr.RR_F32) == rr.RR_ERR_UNSUPPORTED
+    # the softmax backward reads y and dy twice past the on-chip plans, up to 2^28
+    assert rr.softmax_bwd_raw(A, C, B, 2, (1 << 20) + 4, rr.RR_F32) == rr.RR_ERR_WORKSPACE
+    assert rr.softmax_bwd_raw(A, C, B, 2, (1 << 28) + 4, rr.RR_F32) == rr.RR_ERR_UNSUPPORTED
+    # the cross-entropy gradient holds the row on chip: 64 workgroups x 512 lanes x 64 values
+    assert rr.cross_entropy_fwd_bwd_raw(A, C, C + 4096, C + 8192, C + 12288, B, 2, (1 << 21) + 4,
+                                        rr.RR_F32) == rr.RR_ERR_UNSUPPORTED
 
 
 @needs_no_gpu

@@ -225,6 +225,32 @@ def test_softmax_bwd_forced_plans(kind, P, R, G, M, N, dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N", [(2, (1 << 20) + 8), (1, 3_000_000), (3, 1_500_016)])
+def test_softmax_bwd_long_rows(M, N, dtype):
+    """Rows past the on-chip plans: the two-read kernel (y and dy summed over a first
+    read, dx written from a second), 16 to 64 workgroups per row, ragged last tiles."""
+    code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
+    assert rr.rr_plan_query(rr.RR_OP_SOFTMAX_BWD, M, N, code)["path"] == 4
+    say("softmax bwd long", dtype, M, N)
+    y, dy = softmax_bwd_inputs(M, N, dtype)
+    parity_softmax_bwd(y, dy, dtype, f"softmax bwd long {dtype} {M}x{N}")
+    for inplace in ("y", "dy"):  # dx over y or dy: each tile is read before it is written
+        say("softmax bwd long in place", inplace, dtype, M, N)
+        parity_softmax_bwd(y, dy, dtype, f"softmax bwd long in place {inplace}", inplace=inplace)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N", [(7, 1000), (33, 40000), (5, 16 * 16384 + 5), (70, 9)])
+def test_softmax_bwd_long_row_kernel_forced_at_short_rows(M, N, dtype):
+    """The two-read kernel forced on short rows: tiles that do not fill a row group
+    (members with no tile at all), ragged tails, rows of fewer than 16 bytes."""
+    with forced(kind="long"):
+        say("softmax bwd long forced", dtype, M, N)
+        y, dy = softmax_bwd_inputs(M, N, dtype)
+        parity_softmax_bwd(y, dy, dtype, f"softmax bwd long forced {dtype} {M}x{N}")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("inplace", ["y", "dy"])
 def test_softmax_bwd_in_place(inplace, dtype):
     for M, N in ((64, 1024), (8, 131072)):
@@ -234,7 +260,7 @@ def test_softmax_bwd_in_place(inplace, dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("N", [64, 1000, 4096, 40000, 131072])
+@pytest.mark.parametrize("N", [64, 1000, 4096, 40000, 131072, 300001])
 def test_softmax_bwd_unaligned(N, dtype):
     M = 6
     y_np, dy_np = softmax_bwd_inputs(M, N, dtype)

@@ -504,6 +504,9 @@ __global__ void __launch_bounds__(R)
                 if constexpr (VEC) widen_part<E, C>(buf[K]);
                 const float q = rmsnorm_local<E, P, R, true>(buf[K], c);
                 publish_pair<G>(c.g, c.member, c.it, q, 0.0f);
+                // x * w now rather than at the store: the store step then reads no
+                // weight from LDS while three rows are live, which with 64 fp32
+                // values per lane would not fit the registers; (x * w) * r as before
                 wsrc.apply(buf[K], c.l);
             } else {
                 __syncthreads();  // as in the softmax kernel: the merged sum is read

@@ -145,8 +145,11 @@ rr_status rr_cross_entropy_fwd(const void *logits, const int32_t *labels, float 
  * loss: fp32[M]; lse: fp32[M] or NULL; dlogits: M x N of type dt (bf16: round to
  * nearest even).  dlogits == logits (exact aliasing) is allowed; any other overlap is
  * rejected.  A label outside [0, N) gives loss_i = NaN and a NaN row of dlogits (lse_i
- * is still written); it is never used as an address.  Same plans, limits and workspace
- * as rr_softmax_fwd (query with RR_OP_XENT_GRAD).  N must fit int32 and M be below 2^30.
+ * is still written); it is never used as an address.  Plans and workspace are queried
+ * with RR_OP_XENT_GRAD.  Rows past the on-chip plans (more than 2097152 elements, or
+ * 262144 when logits or dlogits is not 16-byte aligned), up to 2^28 elements, take a
+ * two-read kernel: the row's max and sum over a first read, dlogits from a second.
+ * N must fit int32 and M be below 2^30.
  */
 rr_status rr_cross_entropy_fwd_bwd(const void *logits, const int32_t *labels, const float *dloss,
                                    float *loss, float *lse, void *dlogits, int64_t M, int64_t N,
@@ -213,8 +216,8 @@ typedef struct {
                            2: cross-entropy forward (streaming online max and sum),
                            3: persistent stream kernel, one workgroup per row,
                            4: two-read long-row kernel (softmax and RMSNorm forward,
-                              softmax backward), `groups_per_row` workgroups per row
-                              (workspace) */
+                              softmax backward, cross-entropy gradient), `groups_per_row`
+                              workgroups per row (workspace) */
     int vectorized;     /* 1: 128-bit path, 0: per-element path */
     int vals_per_lane;  /* values each lane holds (row paths: fp32 values, or 128 bf16 values
                            kept packed by the bf16 RMSNorm) or loads per step (streaming) */
@@ -267,7 +270,7 @@ rr_status rr_stream_fill(void *dst, size_t bytes, uint32_t value, hipStream_t st
 typedef struct {
     int kind;            /* 0: the planner's choice, 1: block kernel, 2: stream kernel,
                             3: the two-read long-row kernel (softmax and RMSNorm forward,
-                               softmax backward) */
+                               softmax backward, cross-entropy gradient) */
     int vals_per_lane;   /* P of the plan (0: the planner's choice) */
     int lanes_per_row;   /* R of the plan (0: the planner's choice) */
     int groups_per_row;  /* G of the plan (0: the planner's choice) */

@@ -226,6 +226,9 @@ rr_status rr_cross_entropy_fwd_bwd(const void *logits, const int32_t *labels, co
         return st;
     rr::LaunchArgs a;
     if ((st = launch_args(stream, &a)) != RR_OK) return st;
+    if (p.path == rr::kPathLong)
+        return hip_status(rr::launch_long_row(p, rr::kOpXentGrad, dt, logits, nullptr, dlogits, lse,
+                                              M, N, 0.0f, ws, a, {labels, dloss, loss}));
     return hip_status(rr::launch_xent_grad(p, dt, logits, labels, dloss, loss, lse, dlogits, M, N,
                                            ws, a));
 }

@@ -31,11 +31,20 @@ hipError_t launch_softmax_bwd(const Plan &p, int dtype, const void *y, const voi
 hipError_t launch_rmsnorm_bwd(const Plan &p, int dtype, const void *x, const void *w,
                               const void *dy, const float *rstd, void *dx, float *dw, int64_t M,
                               int64_t N, void *ws, const LaunchArgs &a);
+// Per-row inputs and outputs of the cross-entropy gradient on the long-row kernel
+// (unused by the other ops).
+struct XentRows {
+    const int32_t *labels = nullptr;
+    const float *dloss = nullptr;
+    float *loss = nullptr;
+};
+
 // op kOpSoftmax or kOpRmsnorm: x, w (RMSNorm), y, rstd (RMSNorm, may be NULL);
-// kOpSoftmaxBwd: x = the forward's y, w = dy (M x N), y = dx.
+// kOpSoftmaxBwd: x = the forward's y, w = dy (M x N), y = dx;
+// kOpXentGrad: x = logits, y = dlogits, rstd = lse (may be NULL), and xr.
 hipError_t launch_long_row(const Plan &p, int op, int dtype, const void *x, const void *w,
                            void *y, float *rstd, int64_t M, int64_t N, float eps, void *ws,
-                           const LaunchArgs &a);
+                           const LaunchArgs &a, XentRows xr = {});
 hipError_t launch_rmsnorm_packed(const Plan &p, const void *x, const void *w, void *y, float *rstd,
                                  int64_t M, int64_t N, float eps, void *ws, const LaunchArgs &a);
 hipError_t launch_copy(const void *src, void *dst, size_t bytes, const LaunchArgs &a);

@@ -509,7 +509,8 @@ PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *ou
     const bool force_stream = ov.kind == kForceStream;
     const bool force_block = ov.kind == kForceBlock;
     const bool force_long = ov.kind == kForceLong;
-    const bool long_op = op == kOpSoftmax || op == kOpRmsnorm || op == kOpSoftmaxBwd;
+    const bool long_op =
+        op == kOpSoftmax || op == kOpRmsnorm || op == kOpSoftmaxBwd || op == kOpXentGrad;
     if (long_op && (force_long || (!fP && !fR && !fG && !force_stream && !force_block &&
                                    !default_row(op, dtype, vec, M, N, &p)))) {
         // past every on-chip plan: read the row twice

@@ -88,10 +88,12 @@ WIDE = [Workload("softmax_f32_1024x1048576", "softmax", "f32", 1024, 1 << 20),
         Workload("rmsnorm_bf16_128x16777216", "rmsnorm", "bf16", 128, 1 << 24)]
 
 # Rows past the on-chip capacity (read twice): 16M-element fp32 rows and 32M-element
-# bf16 rows, and the softmax backward's 16M-element fp32 rows.
+# bf16 rows, the softmax backward's 16M-element fp32 rows and the cross-entropy
+# gradient's 16M-element bf16 rows.
 LONG = [Workload("softmax_f32_64x16777216", "softmax", "f32", 64, 1 << 24),
         Workload("rmsnorm_bf16_64x33554432", "rmsnorm", "bf16", 64, 1 << 25),
-        Workload("softmaxbwd_f32_64x16777216", "softmax_bwd", "f32", 64, 1 << 24, sigma=2.0)]
+        Workload("softmaxbwd_f32_64x16777216", "softmax_bwd", "f32", 64, 1 << 24, sigma=2.0),
+        Workload("xentgrad_bf16_64x16777216", "xent_grad", "bf16", 64, 1 << 24, sigma=2.0)]
 
 
 # Rows whose length is not a power of two: a 151936-entry vocabulary (softmax) and

@@ -117,8 +117,10 @@ def test_too_long_rows_are_unsupported():
     # the softmax backward reads y and dy twice past the on-chip plans, up to 2^28
     assert rr.softmax_bwd_raw(A, C, B, 2, (1 << 20) + 4, rr.RR_F32) == rr.RR_ERR_WORKSPACE
     assert rr.softmax_bwd_raw(A, C, B, 2, (1 << 28) + 4, rr.RR_F32) == rr.RR_ERR_UNSUPPORTED
-    # the cross-entropy gradient holds the row on chip: 64 workgroups x 512 lanes x 64 values
+    # and so does the cross-entropy gradient
     assert rr.cross_entropy_fwd_bwd_raw(A, C, C + 4096, C + 8192, C + 12288, B, 2, (1 << 21) + 4,
+                                        rr.RR_F32) == rr.RR_ERR_WORKSPACE
+    assert rr.cross_entropy_fwd_bwd_raw(A, C, C + 4096, C + 8192, C + 12288, B, 2, (1 << 28) + 4,
                                         rr.RR_F32) == rr.RR_ERR_UNSUPPORTED
 
 

@@ -100,7 +100,40 @@ def test_xent_grad_in_place(M, N, dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("N", [64, 1000, 4096, 40000, 131072])
+@pytest.mark.parametrize("M,N", [(2, (1 << 21) + 8), (1, 3_000_000)])
+def test_xent_grad_long_rows(M, N, dtype):
+    """Rows past the on-chip plans: the two-read kernel (the row's max and sum over a
+    first read, dlogits from a second), also in place (x[label] is read before any
+    workgroup of the row writes)."""
+    code = rr.RR_F32 if dtype == "f32" else rr.RR_BF16
+    assert rr.rr_plan_query(rr.RR_OP_XENT_GRAD, M, N, code)["path"] == 4
+    x = synth.normal(M, N, sigma=2.0, dtype=dtype)
+    for inplace in (False, True):
+        say("xent grad long", dtype, M, N, inplace)
+        parity_xent_grad(x, synth.labels(M, N), _dloss(M), dtype,
+                         f"xent grad long {dtype} {M}x{N}", inplace=inplace)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("M,N", [(7, 1000), (33, 40000), (5, 16 * 16384 + 5), (70, 9)])
+def test_xent_grad_long_row_kernel_forced_at_short_rows(M, N, dtype):
+    """The two-read kernel forced on short rows: members with no tile, ragged tails,
+    labels in every position of a tile; invalid labels and constant rows."""
+    with forced(kind="long"):
+        say("xent grad long forced", dtype, M, N)
+        x = synth.normal(M, N, sigma=2.0, dtype=dtype)
+        parity_xent_grad(x, synth.labels(M, N), _dloss(M), dtype, f"xent grad long forced {M}x{N}")
+        if N == 1000:
+            lab = np.array([0, -1, N, N - 1, 1 << 30, 7, -(1 << 30)], dtype=np.int32)
+            parity_xent_grad(x, lab, _dloss(M), dtype, "xent grad long forced, invalid labels")
+            c = np.full((4, 4096), 2.5, dtype=np.float32)
+            c = c if dtype == "f32" else synth.f32_to_bf16(c)
+            parity_xent_grad(c, np.array([0, 5, 4095, 17], np.int32), _dloss(4), dtype,
+                             "xent grad long forced, constant rows")
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("N", [64, 1000, 4096, 40000, 131072, 300001])
 def test_xent_grad_unaligned(N, dtype):
     M = 6
     x_np = synth.normal(M, N, sigma=2.0, dtype=dtype)

@@ -442,6 +442,7 @@ TIMEOUT_CASES = [
     ("rmsnorm f32 G16 deferred", "rmsnorm", "f32", 64, 524288, None),
     ("rmsnorm bf16 packed G16 deferred", "rmsnorm", "bf16", 64, 1 << 20, None),
     ("long-row softmax_bwd", "softmax_bwd", "f32", 48, 70000, "long"),
+    ("long-row xent_grad", "xent_grad", "bf16", 48, 70000, "long"),
 ]
 
 _OP_CODES = {"softmax": rr.RR_OP_SOFTMAX, "rmsnorm": rr.RR_OP_RMSNORM,

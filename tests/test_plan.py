@@ -26,7 +26,7 @@ def test_row_plans_hold_the_row(op, dt, vec):
             p = rr.rr_plan_query(op, 16384, N, dt, vec)
         P, R, G = p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]
         if p["path"] == 4:  # past every on-chip plan: the two-pass long-row kernel
-            assert op in (rr.RR_OP_SOFTMAX, rr.RR_OP_RMSNORM, rr.RR_OP_SOFTMAX_BWD) and N > 262144
+            assert N > 262144
             assert p["max_n"] == 1 << 28 and G in (16, 32, 64) and p["ws_bytes"] > 0
             continue
         assert p["max_n"] == P * R * G >= N
@@ -55,13 +55,10 @@ def test_row_plans_hold_the_row(op, dt, vec):
             assert q["path"] == 4
         with pytest.raises(rr.RRError):
             rr.rr_plan_query(op, 16, (1 << 28) + 1, dt, vec)
-    elif op == rr.RR_OP_SOFTMAX_BWD:  # read twice past 2^20 (unaligned: 262144), to 2^28
+    else:  # backward ops: read twice past the on-chip plans, up to 2^28
         assert rr.rr_plan_query(op, 16, (1 << 21) + 1, dt, vec)["path"] == 4
         with pytest.raises(rr.RRError):
             rr.rr_plan_query(op, 16, (1 << 28) + 1, dt, vec)
-    else:
-        with pytest.raises(rr.RRError):
-            rr.rr_plan_query(op, 16, (1 << 21) + 1, dt, vec)
 
 
 def test_rows_up_to_8m_elements_stay_on_chip():
@@ -88,10 +85,9 @@ def test_rows_up_to_8m_elements_stay_on_chip():
                 assert (p["path"], p["vals_per_lane"], p["lanes_per_row"], p["groups_per_row"]) == \
                     (1, vals, 512, g), (op, dt, N, p)
                 assert p["ws_bytes"] == 256 + 256 * (64 + 64 * g)
-        with pytest.raises(rr.RRError):
-            rr.rr_plan_query(rr.RR_OP_XENT_GRAD, 256, N, rr.RR_F32)
-        # the softmax backward reads y and dy twice past 2^20 elements
-        assert rr.rr_plan_query(rr.RR_OP_SOFTMAX_BWD, 256, N, rr.RR_F32)["path"] == 4
+        # the backward ops read their rows twice past their on-chip plans
+        for op in (rr.RR_OP_XENT_GRAD, rr.RR_OP_SOFTMAX_BWD):
+            assert rr.rr_plan_query(op, 256, N, rr.RR_F32)["path"] == 4
     for dt in (rr.RR_F32, rr.RR_BF16):
         assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 256, 1 << 22, dt, False)["path"] == 4
         assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 256, (1 << 23) + 1, dt)["path"] == 4
@@ -326,12 +322,28 @@ def test_long_rows_take_the_two_pass_kernel(overrides):
     overrides.set(kind="long")
     assert rr.rr_plan_query(rr.RR_OP_SOFTMAX, 8, 1000, rr.RR_F32)["path"] == 4
     assert rr.rr_plan_query(rr.RR_OP_SOFTMAX_BWD, 8, 1000, rr.RR_F32)["path"] == 4
-    # the cross-entropy gradient has no long-row kernel (the cross-entropy forward
-    # streams any row in its own kernel)
-    with pytest.raises(rr.RRError):
-        rr.rr_plan_query(rr.RR_OP_XENT_GRAD, 8, (1 << 21) + 4, rr.RR_F32)
+    assert rr.rr_plan_query(rr.RR_OP_XENT_GRAD, 8, 1000, rr.RR_F32)["path"] == 4
+    # the cross-entropy forward streams any row in its own kernel
     assert rr.rr_plan_query(rr.RR_OP_XENT, 8, (1 << 21) + 4, rr.RR_F32)["path"] == 2
     # the per-element path keeps the two-pass kernel past 262144 elements
+
+
+def test_cross_entropy_gradient_long_rows_take_the_two_pass_kernel():
+    """Cross-entropy gradient rows past the on-chip plans (2^21 elements on the 128-bit
+    path, 262144 on the per-element path) read the logits twice, up to 2^28 elements,
+    on 16 to 64 workgroups per row (the softmax's rule)."""
+    for dt, size in ((rr.RR_F32, 4), (rr.RR_BF16, 2)):
+        assert rr.rr_plan_query(rr.RR_OP_XENT_GRAD, 64, 1 << 21, dt)["path"] == 1
+        assert rr.rr_plan_query(rr.RR_OP_XENT_GRAD, 64, 262144, dt, False)["path"] == 1
+        for vec, N in ((True, (1 << 21) + 8), (True, 3_000_000), (True, 1 << 28),
+                       (False, 262145), (False, 1_000_003)):
+            p = rr.rr_plan_query(rr.RR_OP_XENT_GRAD, 64, N, dt, vec)
+            G = 16
+            while G < 64 and N * size > G * 512 * 1024:
+                G *= 2
+            assert (p["path"], p["lanes_per_row"], p["groups_per_row"]) == (4, 512, G), (N, p)
+        with pytest.raises(rr.RRError):
+            rr.rr_plan_query(rr.RR_OP_XENT_GRAD, 64, (1 << 28) + 1, dt)
 
 
 def test_softmax_backward_long_rows_take_the_two_pass_kernel():

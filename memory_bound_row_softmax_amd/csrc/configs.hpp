@@ -155,20 +155,21 @@ constexpr int stream_depth(int op, int P, int R) {
     return (RR_STREAM_DEPTH > 2 && fits) ? RR_STREAM_DEPTH : 2;
 }
 
-// Two-pass long rows (softmax and RMSNorm forward past the split-row capacity):
-// tiles of kLongP * kLongR elements (kLongPElem on the per-element path), G
-// workgroups per row (RMSNorm: kLongG; softmax: long_row_groups below), rows up to
-// kLongMaxN elements (byte offsets stay 32-bit).
+// Two-pass long rows (past the split-row capacity): tiles of kLongP * kLongR elements
+// (kLongPElem on the per-element path), G workgroups per row (long_row_groups
+// below), rows up to kLongMaxN elements (byte offsets stay 32-bit).
 constexpr int kLongP = 32;
 constexpr int kLongPElem = 16;
 constexpr int kLongR = 512;
 constexpr int kLongG = 16;
-// Softmax: as many workgroups per row (16, 32 or 64) as keep a workgroup's share
-// of the row at about 512 KiB or less.  On MI355X the two-read softmax ran fastest
-// that way (fp32 rows of 3M and 4M elements on 32, of 8M on 64, bf16 rows of 2M
-// and 4M on 16); RMSNorm measured within 3 % for 16, 32 and 64 and keeps 16.
-constexpr int long_row_groups(int op_softmax, long long row_bytes) {
-    if (!op_softmax) return kLongG;
+// As many workgroups per row (16, 32 or 64) as keep a workgroup's share of the row
+// (of y and dy for the softmax backward) at about 512 KiB or less.  On MI355X the
+// two-read softmax ran fastest that way (fp32 rows of 3M and 4M elements on 32, of
+// 8M on 64, bf16 rows of 2M and 4M on 16).  RMSNorm measured within 3 % for 16, 32
+// and 64 at 4M and 8M elements, and 64 won on longer rows (offset-averaged GB/s, 16
+// -> 64: bf16 32M elements 3450 -> 3767, 64M 3185 -> 3558; fp32 16M 3486 -> 4116,
+// 9M 4090 -> 4252).
+constexpr int long_row_groups(long long row_bytes) {
     int g = kLongG;
     while (g < 64 && row_bytes > (long long)g * (512 << 10)) g *= 2;
     return g;

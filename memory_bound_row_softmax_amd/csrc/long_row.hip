@@ -25,8 +25,8 @@ hipError_t launch_cfg(const void *x, const void *w, void *y, float *rstd, int64_
 template <class E, int OP>
 hipError_t dispatch(const Plan &p, const void *x, const void *w, void *y, float *rstd, int64_t M,
                     int64_t N, float eps, void *ws, const LaunchArgs &a, XentRows xr) {
-    // RMSNorm takes 16 workgroups per row; the other ops 16, 32 or 64 (long_row_groups)
-    if constexpr (OP != kLongRmsnorm) {
+    // 16, 32 or 64 workgroups per row (long_row_groups)
+    {
         if (p.G == 32)
             return p.vec ? launch_cfg<E, OP, kLongP, 32, true>(x, w, y, rstd, M, N, eps, ws, a, xr)
                          : launch_cfg<E, OP, kLongPElem, 32, false>(x, w, y, rstd, M, N, eps, ws, a, xr);

@@ -523,8 +523,7 @@ PlanResult make_plan(int op, int dtype, int64_t M, int64_t N, bool vec, Plan *ou
         p.P = vec ? kLongP : kLongPElem;
         p.R = kLongR;
         // the softmax backward reads two rows (y and dy) per pass
-        p.G = long_row_groups(op != kOpRmsnorm,
-                              (op == kOpSoftmaxBwd ? 2 : 1) * N * (dtype == kBf16 ? 2 : 4));
+        p.G = long_row_groups((op == kOpSoftmaxBwd ? 2 : 1) * N * (dtype == kBf16 ? 2 : 4));
         p.max_n = kLongMaxN;
         p.ws_bytes = grid_ws_bytes(p.G, M);
         p.block = kLongR;

@@ -307,12 +307,11 @@ def test_long_rows_take_the_two_pass_kernel(overrides):
                 if op == rr.RR_OP_RMSNORM and n <= 1 << (24 if dt == rr.RR_BF16 else 23):
                     assert p["path"] == 1  # on chip at any fill
                     continue
-                # RMSNorm: 16 workgroups per row; softmax: enough that a workgroup's
-                # share of the row is at most 512 KiB (16 to 64)
+                # enough workgroups that a workgroup's share of the row is at most
+                # 512 KiB (16 to 64)
                 G = 16
-                if op == rr.RR_OP_SOFTMAX:
-                    while G < 64 and n * (4 if dt == rr.RR_F32 else 2) > G * 512 * 1024:
-                        G *= 2
+                while G < 64 and n * (4 if dt == rr.RR_F32 else 2) > G * 512 * 1024:
+                    G *= 2
                 assert p["path"] == 4 and p["lanes_per_row"] == 512 and p["groups_per_row"] == G
                 assert p["ws_bytes"] == 256 + 1000 * (64 + 64 * G)
             # the per-element path holds 16 * 1024 * 16 elements on chip
